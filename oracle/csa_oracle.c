@@ -1,0 +1,463 @@
+/*
+ * csa_oracle.c -- plain, slow CPU oracle for the compressed sparse attention
+ * (CSA) / heavily compressed attention (HCA) path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  It is loaded by tests/, by the smoke check and by
+ * the CPU-baseline leg of the benchmark; the GPU library never links, includes
+ * or calls it, and it shares no source with the GPU library.
+ *
+ * Everything is computed in IEEE double with plain loops, in the order the
+ * method states its steps.  The only parallelism is an OpenMP loop over
+ * independent rows (a batch element, a query token or a compressed entry).
+ * Inputs are read in their stored formats (fp32, bf16 bits, OCP e4m3 codes)
+ * and decoded by this file's own routines.
+ *
+ * Sources (web pages on DeepSeek-V4 hybrid attention):
+ *  - "DeepSeek V4 CSA + CP migration to HP" (gitcode hyper-parallel issue 4),
+ *    section 3.2: the compressor is linear_wkv + linear_wgate with a softmax
+ *    over an overlapping window and an absolute position embedding `ape`;
+ *    ratio 4 overlaps, ratio 128 does not.
+ *  - "DS-V4 analysis" (edward-lyz), sections 1.2-1.5: m tokens -> one entry,
+ *    each entry looks at 2m adjacent positions; indexer scores -> top-k ->
+ *    attend to the k entries plus a sliding window of raw KV; HCA is dense
+ *    over all compressed entries.
+ *  - notion copy of the same, section 1.1: attention with 1/sqrt(head_dim)
+ *    scale; MQA (one shared KV head).
+ *  - chenxutan article, section 3.2 (mean-pool special case, entry count
+ *    seq_len // m, simplified indexer einsum + topk) and section 5.2 (window
+ *    rule: token i sees [max(0, i - W + 1), i]).
+ *
+ * Parity status per function (see the tests under tests/):
+ *  - orc_compress: the uniform-gate / no-overlap case is pinned to the
+ *    mean-pool closed form; the non-uniform overlapping gate form is the
+ *    plainest reading of section 3.2 of the migration page and is otherwise
+ *    "parity unpinned" by the pages.
+ *  - orc_indexer_topk: the score formula (sum over heads of w * ReLU(q.k)) is
+ *    the published Lightning Indexer form; the pages print only its one-head
+ *    special case, so the multi-head form is "parity unpinned"; the top-k
+ *    order is pinned against a library sort.
+ *  - orc_sparse_attn / orc_hca_dense_attn: pinned to a library scaled
+ *    dot-product attention with an explicit mask.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_E4M3 = 2 };
+
+/* ---- number formats ---------------------------------------------------- */
+
+/* bfloat16: the upper 16 bits of an IEEE binary32 value. */
+double orc_bf16_decode(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* OCP FP8 E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; largest finite magnitude 1.75 * 2^8 = 448;
+ * exponent field 0 encodes subnormals m/8 * 2^-6. */
+double orc_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, mant = c & 7;
+  double v;
+  if (e == 15 && mant == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)mant / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)mant / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Round half to even of a non-negative double to an integer value. */
+static double rne(double r) {
+  double f = floor(r);
+  double d = r - f;
+  if (d > 0.5) return f + 1.0;
+  if (d < 0.5) return f;
+  return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+/* Encode a double as e4m3 with round-to-nearest-even; magnitudes beyond the
+ * largest finite value saturate to +-448 (the saturating conversion). */
+uint8_t orc_e4m3_encode(double v) {
+  uint8_t sign = signbit(v) ? 0x80 : 0;
+  double a = fabs(v), q, r;
+  int ex, e;
+  if (isnan(v)) return 0x7f;
+  if (a == 0) return sign;
+  frexp(a, &ex);
+  e = ex - 1;            /* a lies in [2^e, 2^(e+1)) */
+  if (e < -6) e = -6;    /* subnormals share the binade-(-6) spacing 2^-9 */
+  q = ldexp(1.0, e - 3); /* spacing of the 3-bit mantissa in this binade */
+  r = rne(a / q) * q;    /* a / q is exact: q is a power of two */
+  if (r > 448.0) return sign | 0x7e;
+  if (r == 0) return sign;
+  frexp(r, &ex);
+  e = ex - 1;
+  if (e < -6) return sign | (uint8_t)(r / ldexp(1.0, -9));
+  return sign | (uint8_t)(((e + 7) << 3) | (int)((r / ldexp(1.0, e) - 1.0) * 8.0));
+}
+
+/* bf16 round-to-nearest-even of a double (rounded to binary32 first). */
+uint16_t orc_bf16_encode(double v) {
+  float f = (float)v;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static double ld(const void* p, size_t i, int dt) {
+  switch (dt) {
+    case ODT_F32: return (double)((const float*)p)[i];
+    case ODT_BF16: return orc_bf16_decode(((const uint16_t*)p)[i]);
+    default: return orc_e4m3_decode(((const uint8_t*)p)[i]);
+  }
+}
+
+/* Per-row e4m3 quantisation as the compressor's fp8 store defines it:
+ * scale s = amax / 448 (s = 1 for an all-zero row), code = e4m3(v / s). */
+void orc_quant_rows_e4m3(int rows, int cols, const double* in, uint8_t* codes,
+                         double* scales) {
+  for (int r = 0; r < rows; ++r) {
+    double amax = 0, s;
+    for (int c = 0; c < cols; ++c) amax = fmax(amax, fabs(in[(size_t)r * cols + c]));
+    s = amax > 0 ? amax / 448.0 : 1.0;
+    scales[r] = s;
+    for (int c = 0; c < cols; ++c)
+      codes[(size_t)r * cols + c] = orc_e4m3_encode(in[(size_t)r * cols + c] / s);
+  }
+}
+
+/* ---- compressor ---------------------------------------------------------
+ * Token j (absolute position) has a projected value P_j = W_kv x_j and gate
+ * logits G_j = W_gate x_j, both of width E (weights stored [E, d_model]).  Compressed entry i pools the
+ * window of tokens [m (i - o), m (i + 1)) (o = 1: the previous block and its
+ * own block, 2m tokens; o = 0: its own m tokens), restricted to j >= 0:
+ *     a_{j,e} = softmax over the window of (G_{j,e} + ape[j - m (i - o), e])
+ *     C_{i,e} = sum_j a_{j,e} P_{j,e}.
+ * Entry i exists once its last token m (i + 1) - 1 has been seen.  A call
+ * processes tokens [pos0, pos0 + L) of each sequence; the previous
+ * (1 + o) m - 1 tokens come from state_in (P then G per token, in position
+ * order; absent tokens carry P = 0, G = -inf, which gives them zero weight).
+ * state_out receives the same record for the last (1 + o) m - 1 tokens.
+ * Output rows are written (double, before any storage rounding) for every
+ * entry completed in the call with i < Nc_cap; written[b, i] flags them. */
+int orc_compress(int B, int L, int d_model, int E, int m, int overlap,
+                 const int64_t* pos0, const void* x, const void* w_kv,
+                 const void* w_gate, int in_dt, const double* ape,
+                 const double* state_in, double* state_out, int Nc_cap,
+                 double* out, uint8_t* written) {
+  const int Sw = (1 + overlap) * m, ns = Sw - 1;
+  if (B < 0 || L < 0 || m < 1 || E < 1 || d_model < 1) return 1;
+  for (int b = 0; b < B; ++b) {
+    const int64_t p0 = pos0[b];
+    const int64_t base = p0 - ns; /* position of token-table row 0 */
+    const int ntok = ns + L;
+    double* P = (double*)calloc((size_t)ntok * E, sizeof(double));
+    double* G = (double*)malloc((size_t)ntok * E * sizeof(double));
+    for (size_t k = 0; k < (size_t)ntok * E; ++k) G[k] = -INFINITY;
+    /* carried tokens */
+    for (int s = 0; s < ns; ++s) {
+      int64_t pos = base + s;
+      if (pos < 0 || !state_in) continue;
+      for (int e = 0; e < E; ++e) {
+        P[(size_t)s * E + e] = state_in[(((size_t)b * ns + s) * 2 + 0) * E + e];
+        G[(size_t)s * E + e] = state_in[(((size_t)b * ns + s) * 2 + 1) * E + e];
+      }
+    }
+    /* projections of the new tokens */
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < L; ++t) {
+      for (int e = 0; e < E; ++e) {
+        double pk = 0, gk = 0;
+        for (int k = 0; k < d_model; ++k) {
+          double xv = ld(x, ((size_t)b * L + t) * d_model + k, in_dt);
+          pk += xv * ld(w_kv, (size_t)e * d_model + k, in_dt);
+          gk += xv * ld(w_gate, (size_t)e * d_model + k, in_dt);
+        }
+        P[(size_t)(ns + t) * E + e] = pk;
+        G[(size_t)(ns + t) * E + e] = gk;
+      }
+    }
+    /* entries completed by this chunk */
+    {
+      int64_t i_lo = (p0 + 1 + m - 1) / m - 1; /* smallest i with m(i+1)-1 >= p0 */
+      int64_t i_hi = (p0 + L) / m - 1;         /* largest i with m(i+1)-1 < p0+L */
+      if (i_lo < 0) i_lo = 0;
+#pragma omp parallel for schedule(static)
+      for (int64_t i = i_lo; i <= i_hi; ++i) {
+        int64_t first = (int64_t)m * (i - overlap);
+        int64_t last = (int64_t)m * (i + 1) - 1;
+        if (i >= Nc_cap) continue;
+        for (int e = 0; e < E; ++e) {
+          double mx = -INFINITY, den = 0, num = 0;
+          for (int64_t j = first; j <= last; ++j) {
+            double z;
+            if (j < 0) continue;
+            z = G[(size_t)(j - base) * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+            if (z > mx) mx = z;
+          }
+          for (int64_t j = first; j <= last; ++j) {
+            double z, w;
+            if (j < 0) continue;
+            z = G[(size_t)(j - base) * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+            if (z == -INFINITY) continue;
+            w = exp(z - mx);
+            den += w;
+            num += w * P[(size_t)(j - base) * E + e];
+          }
+          out[((size_t)b * Nc_cap + i) * E + e] = num / den;
+        }
+        if (written) written[(size_t)b * Nc_cap + i] = 1;
+      }
+    }
+    /* carried state for the next call */
+    if (state_out) {
+      for (int s = 0; s < ns; ++s) {
+        int64_t pos = p0 + L - ns + s;
+        int64_t row = pos - base;
+        for (int e = 0; e < E; ++e) {
+          double pv = 0, gv = -INFINITY;
+          if (pos >= 0) {
+            pv = P[(size_t)row * E + e];
+            gv = G[(size_t)row * E + e];
+          }
+          state_out[(((size_t)b * ns + s) * 2 + 0) * E + e] = pv;
+          state_out[(((size_t)b * ns + s) * 2 + 1) * E + e] = gv;
+        }
+      }
+    }
+    free(P);
+    free(G);
+  }
+  return 0;
+}
+
+/* ---- visibility -----------------------------------------------------------
+ * A query at absolute position t sees compressed entry i iff the entry's last
+ * token m (i + 1) - 1 is at or before t; at most n_cmp entries exist. */
+static int64_t n_visible(int64_t t, int64_t n_cmp, int m, int64_t cap) {
+  int64_t n = (t + 1) / m;
+  if (t < 0) n = 0;
+  if (n > n_cmp) n = n_cmp;
+  if (n > cap) n = cap;
+  if (n < 0) n = 0;
+  return n;
+}
+
+/* ---- Lightning Indexer score + top-k --------------------------------------
+ * score(t, j) = sum_h w[t,h] * ReLU(sq[t,h] * sk[j] * sum_e q[t,h,e] k[j,e])
+ * over the visible entries j < n_vis(t) (sq = sk = 1 unless e4m3).
+ * Selection: the first min(topk, n_vis) entries under the order
+ * (score descending, index ascending), written in ascending index order and
+ * padded with -1.  sel_score receives the selected scores aligned with
+ * idx_out (NaN in padded slots); kth receives the score of the last selected
+ * entry in selection order (NaN if none); all_scores (optional) every score,
+ * NaN for invisible entries. */
+typedef struct {
+  double s;
+  int32_t j;
+} scored;
+
+static int by_score_desc_index_asc(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+static int by_int_asc(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+int orc_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
+                     const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
+                     const float* q_scale, const float* w_idx, const void* k_idx,
+                     const float* k_scale, int qk_dt, int32_t* idx_out,
+                     double* sel_score, double* kth, double* all_scores) {
+  if (B < 0 || T < 0 || H_I < 1 || d_I < 1 || m < 1 || topk < 0) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+    int b = (int)(bt / T), t = (int)(bt % T);
+    int64_t pos = q_pos[b] + t;
+    int64_t nv = n_visible(pos, n_cmp[b], m, Nc_cap);
+    int nsel = (int)(nv < topk ? nv : topk);
+    scored* row = (scored*)malloc(sizeof(scored) * (nv > 0 ? nv : 1));
+    int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (nsel > 0 ? nsel : 1));
+    for (int64_t j = 0; j < nv; ++j) {
+      double sk = (qk_dt == ODT_E4M3) ? (double)k_scale[(size_t)b * Nc_cap + j] : 1.0;
+      double s = 0;
+      for (int h = 0; h < H_I; ++h) {
+        size_t qrow = (((size_t)b * T + t) * H_I + h);
+        double sq = (qk_dt == ODT_E4M3) ? (double)q_scale[qrow] : 1.0;
+        double dot = 0, v;
+        for (int e = 0; e < d_I; ++e)
+          dot += ld(q_idx, qrow * d_I + e, qk_dt) *
+                 ld(k_idx, ((size_t)b * Nc_cap + j) * d_I + e, qk_dt);
+        v = sq * sk * dot;
+        s += (double)w_idx[qrow] * (v > 0 ? v : 0.0);
+      }
+      row[j].s = s;
+      row[j].j = (int32_t)j;
+      if (all_scores) all_scores[((size_t)b * T + t) * Nc_cap + j] = s;
+    }
+    if (all_scores)
+      for (int64_t j = nv; j < Nc_cap; ++j) all_scores[((size_t)b * T + t) * Nc_cap + j] = NAN;
+    qsort(row, (size_t)nv, sizeof(scored), by_score_desc_index_asc);
+    for (int k = 0; k < nsel; ++k) sel[k] = row[k].j;
+    if (kth) kth[(size_t)b * T + t] = nsel > 0 ? row[nsel - 1].s : NAN;
+    qsort(sel, (size_t)nsel, sizeof(int32_t), by_int_asc);
+    for (int k = 0; k < topk; ++k) {
+      size_t o = ((size_t)b * T + t) * topk + k;
+      idx_out[o] = k < nsel ? sel[k] : -1;
+      if (sel_score) {
+        double sv = NAN;
+        if (k < nsel) {
+          /* recover the score of sel[k] from the sorted row */
+          for (int q = 0; q < nsel; ++q)
+            if (row[q].j == sel[k]) { sv = row[q].s; break; }
+        }
+        sel_score[o] = sv;
+      }
+    }
+    free(row);
+    free(sel);
+  }
+  return 0;
+}
+
+/* ---- attention ------------------------------------------------------------
+ * MQA: all H query heads share one KV head; a KV row is [K | V] of width 2D.
+ * For query token t (absolute position pos) and head h, the attended key set
+ * J is the union of the compressed rows named by idx (entries outside
+ * [0, Nc_cap) are skipped) and the raw tokens j in [max(0, pos - W + 1), pos]
+ * whose row r = j - raw_base lies in [0, R_cap).  One softmax runs over J:
+ *     l_j = scale * q . K_j,  out = sum_j softmax(l)_j V_j,
+ *     lse = log sum_j exp(l_j)   (natural log).
+ * An empty J gives out = 0 and lse = -inf. */
+static void attend_row(int D, double scale, const void* q, size_t qoff, int dt,
+                       const void* const* rows_src, const size_t* rows_off, int n,
+                       double* o, double* lse) {
+  double mx = -INFINITY, den = 0;
+  double* l = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
+  for (int d = 0; d < D; ++d) o[d] = 0;
+  for (int r = 0; r < n; ++r) {
+    double dot = 0;
+    for (int d = 0; d < D; ++d) dot += ld(q, qoff + d, dt) * ld(rows_src[r], rows_off[r] + d, dt);
+    l[r] = scale * dot;
+    if (l[r] > mx) mx = l[r];
+  }
+  for (int r = 0; r < n; ++r) {
+    double p = exp(l[r] - mx);
+    den += p;
+    for (int d = 0; d < D; ++d) o[d] += p * ld(rows_src[r], rows_off[r] + D + d, dt);
+  }
+  if (n > 0) {
+    for (int d = 0; d < D; ++d) o[d] /= den;
+    *lse = mx + log(den);
+  } else {
+    *lse = -INFINITY;
+  }
+  free(l);
+}
+
+int orc_sparse_attn(int B, int T, int H, int D, int topk, int window, double scale,
+                    const int64_t* q_pos, const void* q, const void* kv_cmp, int Nc_cap,
+                    const int32_t* idx, const void* kv_raw, int R_cap,
+                    const int64_t* raw_base, int dt, double* out, double* lse) {
+  if (B < 0 || T < 0 || H < 1 || D < 1 || topk < 0 || window < 0) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+    int b = (int)(bt / T), t = (int)(bt % T);
+    int64_t pos = q_pos[b] + t;
+    int cap = topk + window;
+    const void** src = (const void**)malloc(sizeof(void*) * (cap > 0 ? cap : 1));
+    size_t* off = (size_t*)malloc(sizeof(size_t) * (cap > 0 ? cap : 1));
+    int n = 0;
+    for (int k = 0; k < topk; ++k) {
+      int32_t j = idx[((size_t)b * T + t) * topk + k];
+      if (j < 0 || j >= Nc_cap) continue;
+      src[n] = kv_cmp;
+      off[n++] = ((size_t)b * Nc_cap + j) * 2 * D;
+    }
+    if (window > 0) {
+      int64_t lo = pos - window + 1;
+      if (lo < 0) lo = 0;
+      for (int64_t j = lo; j <= pos; ++j) {
+        int64_t r = j - raw_base[b];
+        if (r < 0 || r >= R_cap) continue;
+        src[n] = kv_raw;
+        off[n++] = ((size_t)b * R_cap + (size_t)r) * 2 * D;
+      }
+    }
+    for (int h = 0; h < H; ++h) {
+      size_t row = ((size_t)b * T + t) * H + h;
+      double l;
+      attend_row(D, scale, q, row * D, dt, src, off, n, out + row * D, &l);
+      if (lse) lse[row] = l;
+    }
+    free(src);
+    free(off);
+  }
+  return 0;
+}
+
+/* HCA: the compressed part of the key set is every visible entry
+ * [0, n_vis(pos)), n_vis as for the indexer; the window part is as above. */
+int orc_hca_dense_attn(int B, int T, int H, int D, int m, int window, double scale,
+                       const int64_t* q_pos, const int32_t* n_cmp, const void* q,
+                       const void* kv_cmp, int Nc_cap, const void* kv_raw, int R_cap,
+                       const int64_t* raw_base, int dt, double* out, double* lse) {
+  if (B < 0 || T < 0 || H < 1 || D < 1 || m < 1 || window < 0) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+    int b = (int)(bt / T), t = (int)(bt % T);
+    int64_t pos = q_pos[b] + t;
+    int64_t nv = n_visible(pos, n_cmp[b], m, Nc_cap);
+    int64_t cap = nv + window;
+    const void** src = (const void**)malloc(sizeof(void*) * (cap > 0 ? cap : 1));
+    size_t* off = (size_t*)malloc(sizeof(size_t) * (cap > 0 ? cap : 1));
+    int n = 0;
+    for (int64_t j = 0; j < nv; ++j) {
+      src[n] = kv_cmp;
+      off[n++] = ((size_t)b * Nc_cap + j) * 2 * D;
+    }
+    if (window > 0) {
+      int64_t lo = pos - window + 1;
+      if (lo < 0) lo = 0;
+      for (int64_t j = lo; j <= pos; ++j) {
+        int64_t r = j - raw_base[b];
+        if (r < 0 || r >= R_cap) continue;
+        src[n] = kv_raw;
+        off[n++] = ((size_t)b * R_cap + (size_t)r) * 2 * D;
+      }
+    }
+    for (int h = 0; h < H; ++h) {
+      size_t row = ((size_t)b * T + t) * H + h;
+      double l;
+      attend_row(D, scale, q, row * D, dt, src, off, n, out + row * D, &l);
+      if (lse) lse[row] = l;
+    }
+    free(src);
+    free(off);
+  }
+  return 0;
+}
+
+/* Number of threads an OpenMP parallel region will use (for reporting). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,219 @@
+"""ctypes wrapper around the plain CPU oracle in ``csa_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
+the CPU-baseline leg of the benchmark.  The GPU product path never imports it.
+
+Arrays are passed in their stored formats: fp32 as ``float32``, bf16 as the
+``uint16`` bit pattern, OCP e4m3 as the ``uint8`` code.  Results come back as
+``float64`` arrays (values before any storage rounding).
+
+Citations follow the C file: the migration page's section 3.2 (compressor),
+the DS-V4 analysis sections 1.2-1.5 (pipeline, overlap, HCA, SWA), the
+article's sections 3.2 and 5.2 (mean-pool special case, entry count, window).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "csa_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+DT_F32, DT_BF16, DT_E4M3 = 0, 1, 2
+
+
+def build() -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math)."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                           "-o", tmp, SRC, "-lm"])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        L = C.CDLL(LIB)
+        vp, i32, i64p, dp = C.c_void_p, C.c_int, C.c_void_p, C.c_void_p
+        L.orc_compress.argtypes = [i32] * 6 + [i64p, vp, vp, vp, i32, dp, dp, dp, i32, dp, vp]
+        L.orc_indexer_topk.argtypes = [i32] * 7 + [i64p, vp, vp, vp, vp, vp, vp, i32, vp, dp, dp, dp]
+        L.orc_sparse_attn.argtypes = [i32] * 6 + [C.c_double, i64p, vp, vp, i32, vp, vp, i32, i64p, i32, dp, dp]
+        L.orc_hca_dense_attn.argtypes = [i32] * 6 + [C.c_double, i64p, vp, vp, vp, i32, vp, i32, i64p, i32, dp, dp]
+        for f in (L.orc_compress, L.orc_indexer_topk, L.orc_sparse_attn, L.orc_hca_dense_attn):
+            f.restype = C.c_int
+        L.orc_e4m3_encode.argtypes = [C.c_double]
+        L.orc_e4m3_encode.restype = C.c_uint8
+        L.orc_e4m3_decode.argtypes = [C.c_uint8]
+        L.orc_e4m3_decode.restype = C.c_double
+        L.orc_bf16_encode.argtypes = [C.c_double]
+        L.orc_bf16_encode.restype = C.c_uint16
+        L.orc_bf16_decode.argtypes = [C.c_uint16]
+        L.orc_bf16_decode.restype = C.c_double
+        L.orc_quant_rows_e4m3.argtypes = [i32, i32, dp, vp, dp]
+        L.orc_quant_rows_e4m3.restype = None
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype=dtype))
+    return a
+
+
+def _dt(a):
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.uint16:
+        return DT_BF16
+    if a.dtype == np.uint8:
+        return DT_E4M3
+    raise TypeError("stored format must be float32, uint16 (bf16) or uint8 (e4m3): %s" % a.dtype)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(float(v))
+
+
+def e4m3_decode(c: int) -> float:
+    return lib().orc_e4m3_decode(int(c))
+
+
+def bf16_encode(v: float) -> int:
+    return lib().orc_bf16_encode(float(v))
+
+
+def bf16_decode(h: int) -> float:
+    return lib().orc_bf16_decode(int(h))
+
+
+def quant_rows_e4m3(x):
+    """Per-row e4m3 quantisation (scale = amax / 448): returns (codes, scales)."""
+    x = _c(x, np.float64)
+    rows, cols = x.reshape(-1, x.shape[-1]).shape
+    codes = np.zeros(x.shape, np.uint8)
+    scales = np.zeros(x.shape[:-1], np.float64)
+    lib().orc_quant_rows_e4m3(rows, cols, _p(x), _p(codes), _p(scales))
+    return codes, scales
+
+
+def compress(x, w_kv, w_gate, m, overlap, pos0, Nc_cap, ape=None, state_in=None,
+             want_state=True):
+    """Gated overlapping compressor.
+
+    x [B, L, d_model], w_kv / w_gate [E, d_model] (same stored format);
+    ape [(1+o) m, E] float; state_in [B, (1+o) m - 1, 2, E] float or None.
+    Returns (out [B, Nc_cap, E] float64 with NaN in unwritten rows,
+    written [B, Nc_cap] bool, state_out or None).
+    """
+    x, w_kv, w_gate = _c(x), _c(w_kv), _c(w_gate)
+    B, L, d_model = x.shape
+    E = w_kv.shape[0]
+    dt = _dt(x)
+    assert _dt(w_kv) == dt and _dt(w_gate) == dt
+    ns = (1 + overlap) * m - 1
+    pos0 = _c(np.broadcast_to(np.asarray(pos0, np.int64), (B,)), np.int64)
+    ape = _c(ape, np.float64)
+    state_in = _c(state_in, np.float64)
+    state_out = np.zeros((B, ns, 2, E), np.float64) if want_state else None
+    out = np.full((B, Nc_cap, E), np.nan, np.float64)
+    written = np.zeros((B, Nc_cap), np.uint8)
+    rc = lib().orc_compress(B, L, d_model, E, m, overlap, _p(pos0), _p(x), _p(w_kv),
+                            _p(w_gate), dt, _p(ape), _p(state_in), _p(state_out),
+                            Nc_cap, _p(out), _p(written))
+    assert rc == 0
+    return out, written.astype(bool), state_out
+
+
+def indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None,
+                 k_scale=None, want_all=False):
+    """Lightning-indexer scores + per-row top-k.
+
+    q_idx [B, T, H_I, d_I], w_idx [B, T, H_I] fp32, k_idx [B, Nc_cap, d_I];
+    e4m3 inputs need q_scale [B, T, H_I] and k_scale [B, Nc_cap].
+    Returns (idx [B, T, topk] int32 ascending with -1 pads, sel_score, kth,
+    all_scores or None).
+    """
+    q_idx, k_idx = _c(q_idx), _c(k_idx)
+    w_idx = _c(w_idx, np.float32)
+    B, T, H_I, d_I = q_idx.shape
+    Nc_cap = k_idx.shape[1]
+    dt = _dt(q_idx)
+    assert _dt(k_idx) == dt
+    if dt == DT_E4M3:
+        q_scale, k_scale = _c(q_scale, np.float32), _c(k_scale, np.float32)
+    else:
+        q_scale = k_scale = None
+    q_pos = _c(np.broadcast_to(np.asarray(q_pos, np.int64), (B,)), np.int64)
+    n_cmp = _c(np.broadcast_to(np.asarray(n_cmp, np.int32), (B,)), np.int32)
+    idx = np.zeros((B, T, topk), np.int32)
+    sel = np.zeros((B, T, topk), np.float64)
+    kth = np.zeros((B, T), np.float64)
+    alls = np.zeros((B, T, Nc_cap), np.float64) if want_all else None
+    rc = lib().orc_indexer_topk(B, T, H_I, d_I, Nc_cap, m, topk, _p(q_pos), _p(n_cmp),
+                                _p(q_idx), _p(q_scale), _p(w_idx), _p(k_idx), _p(k_scale),
+                                dt, _p(idx), _p(sel), _p(kth), _p(alls))
+    assert rc == 0
+    return idx, sel, kth, alls
+
+
+def sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None):
+    """CSA attention: joint softmax over the selected compressed rows and the
+    raw sliding window.  q [B, T, H, D], kv_cmp [B, Nc_cap, 2D],
+    idx [B, T, topk], kv_raw [B, R_cap, 2D].  Returns (out, lse) float64."""
+    q, kv_cmp, kv_raw = _c(q), _c(kv_cmp), _c(kv_raw)
+    idx = _c(idx, np.int32)
+    B, T, H, D = q.shape
+    dt = _dt(q)
+    assert _dt(kv_cmp) == dt and _dt(kv_raw) == dt
+    topk = idx.shape[2]
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    q_pos = _c(np.broadcast_to(np.asarray(q_pos, np.int64), (B,)), np.int64)
+    raw_base = _c(np.broadcast_to(np.asarray(raw_base, np.int64), (B,)), np.int64)
+    out = np.zeros((B, T, H, D), np.float64)
+    lse = np.zeros((B, T, H), np.float64)
+    rc = lib().orc_sparse_attn(B, T, H, D, topk, window, scale, _p(q_pos), _p(q), _p(kv_cmp),
+                               kv_cmp.shape[1], _p(idx), _p(kv_raw), kv_raw.shape[1],
+                               _p(raw_base), dt, _p(out), _p(lse))
+    assert rc == 0
+    return out, lse
+
+
+def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=None):
+    """HCA attention: every visible compressed entry plus the raw window."""
+    q, kv_cmp, kv_raw = _c(q), _c(kv_cmp), _c(kv_raw)
+    B, T, H, D = q.shape
+    dt = _dt(q)
+    assert _dt(kv_cmp) == dt and _dt(kv_raw) == dt
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    q_pos = _c(np.broadcast_to(np.asarray(q_pos, np.int64), (B,)), np.int64)
+    n_cmp = _c(np.broadcast_to(np.asarray(n_cmp, np.int32), (B,)), np.int32)
+    raw_base = _c(np.broadcast_to(np.asarray(raw_base, np.int64), (B,)), np.int64)
+    out = np.zeros((B, T, H, D), np.float64)
+    lse = np.zeros((B, T, H), np.float64)
+    rc = lib().orc_hca_dense_attn(B, T, H, D, m, window, scale, _p(q_pos), _p(n_cmp), _p(q),
+                                  _p(kv_cmp), kv_cmp.shape[1], _p(kv_raw), kv_raw.shape[1],
+                                  _p(raw_base), dt, _p(out), _p(lse))
+    assert rc == 0
+    return out, lse

@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test names the passage it follows.  The pages are: the hyper-parallel
+migration issue (compressor section 3.2), the DS-V4 analysis and its Notion
+copy (sections 1.1-1.5), and the chenxutan article (sections 3.2, 4.1, 5.2).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from tests import brute
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = brute.decode_bits(codes)
+    ours = np.array([orc.e4m3_decode(c) for c in codes])
+    both_nan = np.isnan(ref) & np.isnan(ours)
+    assert np.all(both_nan | (ref == ours))
+    assert orc.e4m3_decode(0x7E) == 448.0 and orc.e4m3_decode(0x01) == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_rne():
+    r = rng(1)
+    vals = np.concatenate([
+        r.normal(0, 1, 4000) * np.exp2(r.integers(-12, 9, 4000)),
+        # exact midpoints between neighbours: ties must go to even
+        np.array([orc.e4m3_decode(c) for c in range(0, 0x7E)]) * 0.5
+        + np.array([orc.e4m3_decode(c + 1) for c in range(0, 0x7E)]) * 0.5,
+        [0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -11, 447.9, -447.9],
+    ]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = np.array([orc.e4m3_encode(float(v)) for v in vals], np.uint8)
+    assert np.array_equal(ref, ours)
+
+
+def test_e4m3_encode_saturates():
+    # values past the largest finite e4m3 magnitude clamp to +-448
+    for v in (449.0, 463.9, 464.0, 1000.0, 1e30):
+        assert orc.e4m3_encode(v) == 0x7E
+        assert orc.e4m3_encode(-v) == 0xFE
+
+
+def test_bf16_encode_matches_torch():
+    r = rng(2)
+    vals = np.concatenate([r.normal(0, 1, 5000) * np.exp2(r.integers(-30, 30, 5000)),
+                           [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0]]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = np.array([orc.bf16_encode(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(ref, ours)
+
+
+# ---------------------------------------------------------------- compressor
+
+def test_compress_worked_example():
+    g = json.load(open(os.path.join(GOLD, "compress_worked_example.json")))
+    S = g["seq_len"]
+    j = np.arange(S, dtype=np.float64)
+    x = np.stack([j + 1, np.log(j + 1)], axis=1)[None].astype(np.float32)   # [1, S, 2]
+    w_kv = np.array([[1.0, 0.0]], np.float32)      # P_j = x_j[0]
+    w_gate = np.array([[0.0, 1.0]], np.float32)    # G_j = x_j[1]
+    out, written, _ = orc.compress(x, w_kv, w_gate, g["m"], g["overlap"], 0, S // g["m"])
+    assert written.all()
+    np.testing.assert_allclose(out[0, :, 0], g["expected"], rtol=1e-6)
+
+
+@pytest.mark.parametrize("overlap", [0, 1])
+@pytest.mark.parametrize("m", [1, 4, 5])
+def test_compress_uniform_gates_reduce_to_mean_pool(m, overlap):
+    # chenxutan section 3.2: C[i] = W . mean(K[m i : m (i + 1)]); with the
+    # overlap the window is the previous block plus the own block (2m tokens;
+    # entry 0 has only its own block).  Uniform gates: W_gate = 0, ape = 0.
+    r = rng(10 + m + overlap)
+    S, dm, E = 7 * m + 3, 9, 6
+    x = r.normal(0, 1, (2, S, dm)).astype(np.float32)
+    w_kv = r.normal(0, 1, (E, dm)).astype(np.float32)
+    w_gate = np.zeros((E, dm), np.float32)
+    out, written, _ = orc.compress(x, w_kv, w_gate, m, overlap, 0, S // m + 2)
+    n = S // m
+    assert written[:, :n].all() and not written[:, n:].any()
+    xd = x.astype(np.float64)
+    for i in range(n):
+        lo = max(0, m * (i - overlap))
+        mean = xd[:, lo:m * (i + 1)].mean(axis=1)            # pool first ...
+        np.testing.assert_allclose(out[:, i], mean @ w_kv.T.astype(np.float64), rtol=1e-9, atol=1e-12)
+
+
+def test_compress_partition_of_unity():
+    # constant P_j with arbitrary gates and ape: every entry equals P.
+    r = rng(3)
+    m, o, S, E = 4, 1, 40, 5
+    x = np.zeros((1, S, 4), np.float32)
+    x[0, :, 0] = 1.0                                # drives P (constant)
+    x[0, :, 1:] = r.normal(0, 1, (S, 3))            # drives G (varies)
+    w_kv = np.zeros((E, 4), np.float32)
+    w_kv[:, 0] = r.normal(0, 1, E)
+    w_gate = np.zeros((E, 4), np.float32)
+    w_gate[:, 1:] = r.normal(0, 2, (E, 3))
+    ape = r.normal(0, 1, ((1 + o) * m, E))
+    out, written, _ = orc.compress(x, w_kv, w_gate, m, o, 0, S // m, ape=ape)
+    np.testing.assert_allclose(out[0], np.broadcast_to(w_kv[:, 0], out[0].shape), rtol=1e-12)
+
+
+def test_compress_ape_shift_invariance_and_effect():
+    r = rng(4)
+    m, o, S, dm, E = 4, 1, 33, 6, 7
+    x = r.normal(0, 1, (1, S, dm)).astype(np.float32)
+    w_kv, w_gate = (r.normal(0, 1, (E, dm)).astype(np.float32) for _ in range(2))
+    ape = r.normal(0, 1, ((1 + o) * m, E))
+    a, _, _ = orc.compress(x, w_kv, w_gate, m, o, 0, S // m, ape=ape)
+    b, _, _ = orc.compress(x, w_kv, w_gate, m, o, 0, S // m, ape=ape + r.normal(0, 3, (1, E)))
+    c, _, _ = orc.compress(x, w_kv, w_gate, m, o, 0, S // m, ape=None)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    assert np.abs(a - c).max() > 1e-3
+
+
+def test_compress_entry_counts_printed_by_pages():
+    g = json.load(open(os.path.join(GOLD, "entry_counts.json")))
+    for case in g["cases"]:
+        S, m = case["seq_len"], case["m"]
+        x = np.ones((1, S, 1), np.float32)
+        w = np.ones((1, 1), np.float32)
+        _, written, _ = orc.compress(x, w, w, m, 1 if m == 4 else 0, 0, S, want_state=False)
+        assert int(written.sum()) == case["entries"], case["cite"]
+
+
+@pytest.mark.parametrize("m,o", [(4, 1), (4, 0), (3, 1), (1, 0), (16, 0)])
+def test_compress_streaming_and_chunked_equal_one_shot(m, o):
+    r = rng(5 + m)
+    B, S, dm, E = 2, 61, 8, 5
+    x = r.normal(0, 1, (B, S, dm)).astype(np.float32)
+    w_kv, w_gate = (r.normal(0, 1, (E, dm)).astype(np.float32) for _ in range(2))
+    ape = r.normal(0, 1, ((1 + o) * m, E))
+    Nc = S // m
+    ref, wr, st_ref = orc.compress(x, w_kv, w_gate, m, o, 0, Nc, ape=ape)
+    for cuts in ([1] * S, [7, 1, 1, 13, 2, 37], [S]):
+        out = np.full_like(ref, np.nan)
+        st, p = None, 0
+        for L in cuts:
+            o_c, w_c, st = orc.compress(x[:, p:p + L], w_kv, w_gate, m, o, p, Nc, ape=ape, state_in=st)
+            out[w_c] = o_c[w_c]
+            p += L
+        assert p == S
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(st, st_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_compress_never_reads_future_tokens():
+    r = rng(6)
+    m, o, S, dm, E = 4, 1, 40, 5, 3
+    x = r.normal(0, 1, (1, S, dm)).astype(np.float32)
+    w_kv, w_gate = (r.normal(0, 1, (E, dm)).astype(np.float32) for _ in range(2))
+    ref, _, _ = orc.compress(x, w_kv, w_gate, m, o, 0, S // m)
+    cut = 22                                    # tokens >= 22 poisoned
+    xp = x.copy()
+    xp[0, cut:] = np.nan
+    out, _, _ = orc.compress(xp, w_kv, w_gate, m, o, 0, S // m)
+    ok = (m * (np.arange(S // m) + 1) - 1) < cut  # entries whose last token < cut
+    assert np.array_equal(out[0, ok], ref[0, ok])
+    assert np.isnan(out[0, ~ok]).all()
+
+
+# ---------------------------------------------------------------- indexer
+
+def _n_vis(pos, n_cmp, m, cap):
+    return max(0, min(n_cmp, (pos + 1) // m, cap))
+
+
+def test_indexer_single_head_reduces_to_einsum_topk():
+    # chenxutan section 3.2: score = einsum('bqd,bkd->bqk'), then torch.topk.
+    # One head, w = 1 and positive q, k make the ReLU and head sum vanish.
+    r = rng(7)
+    B, T, d, Nc, m, k = 2, 9, 16, 40, 4, 6
+    q = np.abs(r.normal(0, 1, (B, T, 1, d))).astype(np.float32)
+    kk = np.abs(r.normal(0, 1, (B, Nc, d))).astype(np.float32)
+    w = np.ones((B, T, 1), np.float32)
+    q_pos = 4 * Nc                               # every entry visible
+    idx, _, _, _ = orc.indexer_topk(q, w, kk, m, k, q_pos, Nc)
+    s = torch.einsum("bqd,bkd->bqk", torch.from_numpy(q[:, :, 0].astype(np.float64)),
+                     torch.from_numpy(kk.astype(np.float64)))
+    ref = torch.topk(s, k, dim=-1).indices.sort(dim=-1).values.numpy()
+    assert np.array_equal(idx, ref)
+
+
+def test_indexer_heads_sum_weighted_relu():
+    # Structure of the multi-head score: linear in w; a head whose dot
+    # products are all negative contributes nothing whatever its weight.
+    r = rng(8)
+    B, T, H, d, Nc, m = 1, 5, 3, 8, 20, 4
+    kk = np.abs(r.normal(0, 1, (B, Nc, d))).astype(np.float32)
+    q = r.normal(0, 1, (B, T, H, d)).astype(np.float32)
+    q[:, :, 1] = -np.abs(q[:, :, 1])             # head 1: all dots < 0
+    q[:, :, 0] = np.abs(q[:, :, 0])              # head 0: all dots > 0
+    w1 = r.normal(0, 1, (B, T, H)).astype(np.float32)
+    w2 = r.normal(0, 1, (B, T, H)).astype(np.float32)
+    kw = dict(m=m, topk=4, q_pos=200, n_cmp=Nc, want_all=True)
+    s1 = orc.indexer_topk(q, w1, kk, **kw)[3]
+    s2 = orc.indexer_topk(q, w2, kk, **kw)[3]
+    s12 = orc.indexer_topk(q, w1 + w2, kk, **kw)[3]
+    np.testing.assert_allclose(s12, s1 + s2, rtol=1e-5, atol=1e-6)
+    w3 = w1.copy()
+    w3[:, :, 1] = 1e6
+    np.testing.assert_array_equal(orc.indexer_topk(q, w3, kk, **kw)[3], s1)
+    # head 0 alone: w0 * sum_e q k (positive), so its sign follows w0
+    w4 = np.zeros_like(w1)
+    w4[:, :, 0] = -1.0
+    s4 = orc.indexer_topk(q, w4, kk, **kw)[3]
+    dots = np.einsum("btd,bnd->btn", q[:, :, 0].astype(np.float64), kk.astype(np.float64))
+    np.testing.assert_allclose(s4, -dots, rtol=1e-12)
+
+
+def test_indexer_selection_order_matches_lexsort_and_causality():
+    r = rng(9)
+    B, T, H, d, Nc, m, k = 2, 23, 4, 8, 30, 4, 5
+    q = r.normal(0, 1, (B, T, H, d)).astype(np.float32)
+    kk = r.normal(0, 1, (B, Nc, d)).astype(np.float32)
+    w = r.normal(0, 1, (B, T, H)).astype(np.float32)
+    q_pos = np.array([0, 50])
+    n_cmp = np.array([Nc, 17])
+    idx, sel, kth, alls = orc.indexer_topk(q, w, kk, m, k, q_pos, n_cmp, want_all=True)
+    for b in range(B):
+        for t in range(T):
+            nv = _n_vis(q_pos[b] + t, n_cmp[b], m, Nc)
+            assert np.isnan(alls[b, t, nv:]).all()
+            ref = brute.select_lexsort(alls[b, t, :nv], min(k, nv))
+            got = idx[b, t][idx[b, t] >= 0]
+            assert np.array_equal(got, ref)
+            assert (idx[b, t, len(ref):] == -1).all()
+            assert (got < nv).all()
+    # poisoning every invisible key row changes nothing
+    kp = kk.copy()
+    for b in range(B):
+        kp[b, _n_vis(q_pos[b] + T - 1, n_cmp[b], m, Nc):] = np.nan
+    idx2 = orc.indexer_topk(q, w, kp, m, k, q_pos, n_cmp)[0]
+    assert np.array_equal(idx, idx2)
+
+
+def test_indexer_ties_go_to_lower_index():
+    r = rng(11)
+    B, T, H, d, Nc, m, k = 1, 3, 2, 8, 24, 4, 7
+    row = r.normal(0, 1, d)
+    kk = np.tile(row, (B, Nc, 1)).astype(np.float32)            # all keys equal
+    q = r.normal(0, 1, (B, T, H, d)).astype(np.float32)
+    w = np.abs(r.normal(0, 1, (B, T, H))).astype(np.float32)
+    idx = orc.indexer_topk(q, w, kk, m, k, 100, Nc)[0]
+    assert np.array_equal(idx[0], np.tile(np.arange(k), (T, 1)))
+    # duplicates of the best row among distinct rows: lower copy wins ties
+    kk2 = r.normal(0, 1, (B, Nc, d)).astype(np.float32)
+    kk2[0, 20] = kk2[0, 3]
+    kk2[0, 11] = kk2[0, 3]
+    qq = np.tile(kk2[0, 3], (B, 1, 1, 1)).astype(np.float32)    # q = key 3: best dot
+    idx2 = orc.indexer_topk(qq, np.ones((1, 1, 1), np.float32), kk2, m, 2, 100, Nc)[0]
+    assert np.array_equal(idx2[0, 0], [3, 11])
+
+
+def test_indexer_e4m3_scales_fold_into_score():
+    # with e4m3 storage the score uses sq * sk * dot(codes); by positive
+    # homogeneity of ReLU it equals the score of the dequantised values.
+    r = rng(12)
+    B, T, H, d, Nc, m, k = 1, 4, 3, 16, 32, 4, 6
+    qf = r.normal(0, 1, (B, T, H, d))
+    kf = r.normal(0, 1, (B, Nc, d))
+    qc, qs = orc.quant_rows_e4m3(qf)
+    kc, ks = orc.quant_rows_e4m3(kf)
+    w = r.normal(0, 1, (B, T, H)).astype(np.float32)
+    qs32, ks32 = qs.astype(np.float32), ks.astype(np.float32)
+    a = orc.indexer_topk(qc, w, kc, m, k, 200, Nc, q_scale=qs32, k_scale=ks32, want_all=True)
+    qd = (brute.decode_bits(qc) * qs32[..., None].astype(np.float64))
+    kd = (brute.decode_bits(kc) * ks32[..., None].astype(np.float64))
+    s_ref = np.einsum("bth,bthn->btn", w.astype(np.float64),
+                      np.maximum(np.einsum("bthd,bnd->bthn", qd, kd), 0))
+    np.testing.assert_allclose(a[3], s_ref, rtol=1e-9, atol=1e-9)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_case(seed, B=2, T=9, H=4, D=16, Nc=12, R=20, topk=5, window=6, dt=np.float32):
+    r = rng(seed)
+    q = r.normal(0, 1, (B, T, H, D)).astype(dt)
+    kv_cmp = r.normal(0, 1, (B, Nc, 2 * D)).astype(dt)
+    kv_raw = r.normal(0, 1, (B, R, 2 * D)).astype(dt)
+    idx = np.full((B, T, topk), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = r.integers(0, topk + 1)
+            idx[b, t, :n] = np.sort(r.choice(Nc, n, replace=False))
+    return q, kv_cmp, kv_raw, idx
+
+
+def test_sparse_attn_matches_sdpa_with_mask():
+    q, kv_cmp, kv_raw, idx = _attn_case(20)
+    B, T, H, D = q.shape
+    Nc, R, W = kv_cmp.shape[1], kv_raw.shape[1], 6
+    q_pos = np.array([14, 3])
+    raw_base = np.array([5, 0])
+    out, lse = orc.sparse_attn(q, kv_cmp, idx, kv_raw, W, q_pos, raw_base)
+    for b in range(B):
+        mask = brute.csa_mask(T, q_pos[b], idx[b], Nc, R, raw_base[b], W)
+        rows = np.concatenate([kv_cmp[b], kv_raw[b]]).astype(np.float64)
+        ro, rl = brute.sdpa_masked(q[b], rows[:, :D], rows[:, D:], mask, 1 / math.sqrt(D))
+        np.testing.assert_allclose(out[b], ro, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=1e-10, atol=1e-12)
+
+
+def test_sparse_attn_window_only_is_causal_attention():
+    # topk = 0 and W >= S: full causal attention over the raw KV (the ratio-0
+    # sliding-window layer with a window covering everything).
+    r = rng(21)
+    B, S, H, D = 1, 17, 3, 8
+    q = r.normal(0, 1, (B, S, H, D)).astype(np.float32)
+    kv = r.normal(0, 1, (B, S, 2 * D)).astype(np.float32)
+    out, _ = orc.sparse_attn(q, kv[:, :1], np.zeros((B, S, 0), np.int32), kv, S + 5, 0, 0)
+    qt = torch.from_numpy(q[0].astype(np.float64)).permute(1, 0, 2)
+    k = torch.from_numpy(kv[0, :, :D].astype(np.float64)).expand(H, -1, -1)
+    v = torch.from_numpy(kv[0, :, D:].astype(np.float64)).expand(H, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, k, v, is_causal=True)
+    np.testing.assert_allclose(out[0], ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_sparse_attn_empty_set_and_permutation_and_convexity():
+    q, kv_cmp, kv_raw, idx = _attn_case(22, window=0)
+    idx[0, 0] = -1
+    out, lse = orc.sparse_attn(q, kv_cmp, idx, kv_raw, 0, 10, 0)
+    assert (out[0, 0] == 0).all() and np.isneginf(lse[0, 0]).all()
+    r = rng(23)
+    perm = idx[..., r.permutation(idx.shape[-1])]
+    out2, _ = orc.sparse_attn(q, kv_cmp, perm, kv_raw, 0, 10, 0)
+    np.testing.assert_allclose(out, out2, rtol=1e-12, atol=1e-14)
+    D = q.shape[-1]
+    for b in range(q.shape[0]):
+        for t in range(q.shape[1]):
+            sel = idx[b, t][idx[b, t] >= 0]
+            if sel.size == 0:
+                continue
+            V = kv_cmp[b, sel, D:].astype(np.float64)
+            assert (out[b, t] <= V.max(0) + 1e-12).all() and (out[b, t] >= V.min(0) - 1e-12).all()
+
+
+def test_hca_matches_sdpa_and_equals_csa_with_all_visible_selected():
+    r = rng(24)
+    B, T, H, D, m, Nc, W = 2, 12, 3, 8, 4, 9, 5
+    q = r.normal(0, 1, (B, T, H, D)).astype(np.float32)
+    kv_cmp = r.normal(0, 1, (B, Nc, 2 * D)).astype(np.float32)
+    R = 30
+    kv_raw = r.normal(0, 1, (B, R, 2 * D)).astype(np.float32)
+    q_pos = np.array([20, 2])
+    n_cmp = np.array([Nc, 3])
+    raw_base = np.array([2, 0])
+    out, lse = orc.hca_dense_attn(q, kv_cmp, kv_raw, m, W, q_pos, n_cmp, raw_base)
+    topk = Nc
+    idx = np.full((B, T, topk), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            nv = _n_vis(q_pos[b] + t, n_cmp[b], m, Nc)
+            idx[b, t, :nv] = np.arange(nv)
+    out2, lse2 = orc.sparse_attn(q, kv_cmp, idx, kv_raw, W, q_pos, raw_base)
+    np.testing.assert_allclose(out, out2, rtol=1e-12, atol=1e-14)
+    for b in range(B):
+        mask = brute.csa_mask(T, q_pos[b], [list(range(_n_vis(q_pos[b] + t, n_cmp[b], m, Nc)))
+                                            for t in range(T)], Nc, R, raw_base[b], W)
+        rows = np.concatenate([kv_cmp[b], kv_raw[b]]).astype(np.float64)
+        ro, rl = brute.sdpa_masked(q[b], rows[:, :D], rows[:, D:], mask, 1 / math.sqrt(D))
+        np.testing.assert_allclose(out[b], ro, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl, rtol=1e-10, atol=1e-12)
+
+
+def test_pipeline_reduces_to_textbook_causal_attention():
+    # m = 1, no overlap (each entry is one token's projected K|V), k >= S and
+    # no window: CSA is standard causal attention softmax(Q K^T / sqrt(D)) V
+    # with K|V = W_kv x (Notion copy section 1.1; chenxutan section 1.1).
+    r = rng(25)
+    B, S, dm, H, D, HI, dI = 1, 14, 12, 3, 8, 2, 4
+    x = r.normal(0, 1, (B, S, dm)).astype(np.float32)
+    w_kv = r.normal(0, 0.3, (2 * D, dm)).astype(np.float32)
+    w_gate = r.normal(0, 0.3, (2 * D, dm)).astype(np.float32)
+    kvc, wr, _ = orc.compress(x, w_kv, w_gate, 1, 0, 0, S)
+    assert wr.all()
+    kvc32 = kvc.astype(np.float32)          # exact enough: compared at 1e-6 below
+    q_idx = r.normal(0, 1, (B, S, HI, dI)).astype(np.float32)
+    w_idx = r.normal(0, 1, (B, S, HI)).astype(np.float32)
+    k_idx = r.normal(0, 1, (B, S, dI)).astype(np.float32)
+    idx = orc.indexer_topk(q_idx, w_idx, k_idx, 1, S, 0, S)[0]
+    q = r.normal(0, 1, (B, S, H, D)).astype(np.float32)
+    out, _ = orc.sparse_attn(q, kvc32, idx, kvc32[:, :1], 0, 0, 0)
+    kv = x[0].astype(np.float64) @ w_kv.T.astype(np.float64)
+    qt = torch.from_numpy(q[0].astype(np.float64)).permute(1, 0, 2)
+    k = torch.from_numpy(kv[:, :D]).expand(H, -1, -1)
+    v = torch.from_numpy(kv[:, D:]).expand(H, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, k, v, is_causal=True)
+    np.testing.assert_allclose(out[0], ref.permute(1, 0, 2).numpy(), rtol=1e-5, atol=1e-6)
+
+
+def test_attention_never_reads_outside_visible_set():
+    q, kv_cmp, kv_raw, idx = _attn_case(26, R=40, window=4)
+    B, T, H, D = q.shape
+    q_pos, raw_base = np.array([10, 30]), np.array([0, 15])
+    ref, _ = orc.sparse_attn(q, kv_cmp, idx, kv_raw, 4, q_pos, raw_base)
+    kc, kr = kv_cmp.copy(), kv_raw.copy()
+    for b in range(B):
+        used = set(idx[b][idx[b] >= 0].tolist())
+        for j in range(kc.shape[1]):
+            if j not in used:
+                kc[b, j] = np.nan
+        lo = max(0, q_pos[b] - 4 + 1) - raw_base[b]
+        hi = q_pos[b] + T - 1 - raw_base[b]
+        kr[b, :max(lo, 0)] = np.nan
+        kr[b, hi + 1:] = np.nan
+    out, _ = orc.sparse_attn(q, kc, idx, kr, 4, q_pos, raw_base)
+    assert np.array_equal(out, ref)
+
+
+def test_compress_ape_slot_orientation():
+    # ape row s biases window slot s, slot 0 being the oldest token of the
+    # window [m (i - o), m (i + 1)): a dominant bias on slot s makes entry i
+    # the projected value of token m (i - o) + s.
+    r = rng(13)
+    m, o, S, dm, E = 4, 1, 32, 5, 3
+    x = r.normal(0, 1, (1, S, dm)).astype(np.float32)
+    w_kv, w_gate = (r.normal(0, 0.1, (E, dm)).astype(np.float32) for _ in range(2))
+    P = x[0].astype(np.float64) @ w_kv.T.astype(np.float64)
+    for s in range((1 + o) * m):
+        ape = np.zeros(((1 + o) * m, E))
+        ape[s] = 60.0
+        out, _, _ = orc.compress(x, w_kv, w_gate, m, o, 0, S // m, ape=ape)
+        for i in range(1, S // m):
+            np.testing.assert_allclose(out[0, i], P[m * (i - o) + s], rtol=1e-9, atol=1e-12)
