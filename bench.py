@@ -1,0 +1,453 @@
+"""Benchmark of the compressed sparse attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  * csa_prefill_8k_bf16 (default, the line's `value`): compress (main and
+    indexer) -> indexer top-k -> sparse attention for 8192 tokens;
+  * csa_decode_128k_b32 (reported in the same line under "decode_128k"):
+    indexer top-k -> sparse attention for 32 sequences at 131072 tokens of
+    context, caches resident in HBM;
+  * --workload selects any of the five workloads instead.
+Timing uses HIP events on the stream the library launches on.  Decode steps
+run with the L2 and the 256 MB last-level cache flushed (a 1 GiB write)
+before each step, outside the timed events, so cache-resident reuse across
+steps does not pass for HBM bandwidth.
+
+The CPU baseline times the oracle (test infrastructure under oracle/) on a
+bounded sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import compressed_sparse_attention_overlapped_amd as csa  # noqa: E402
+from compressed_sparse_attention_overlapped_amd import inputs as gen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+DEV = "cuda"
+
+
+def i64(v):
+    return torch.tensor(np.asarray(v, np.int64).reshape(-1), dtype=torch.int64, device=DEV)
+
+
+def i32(v):
+    return torch.tensor(np.asarray(v, np.int32).reshape(-1), dtype=torch.int32, device=DEV)
+
+
+def n_vis(t, ncmp, m):
+    return min(ncmp, (t + 1) // m)
+
+
+# ---------------------------------------------------------------- work counts
+
+def csa_counts(w: gen.Workload, q_pos0: int, T: int, ncmp: int):
+    """(indexer pairs, attention key visits) summed over query rows."""
+    t = np.arange(q_pos0, q_pos0 + T, dtype=np.int64)
+    nv = np.minimum(ncmp, (t + 1) // w.m)
+    pairs = int(nv.sum())
+    visits = int(np.minimum(w.topk, nv).sum() + np.minimum(w.window, t + 1).sum())
+    return pairs, visits
+
+
+def hca_visits(w: gen.Workload, q_pos0: int):
+    t = np.arange(q_pos0, q_pos0 + w.T, dtype=np.int64)
+    nv = np.minimum(w.n_cmp, (t + 1) // w.m)
+    return int(nv.sum() + np.minimum(w.window, t + 1).sum())
+
+
+# ---------------------------------------------------------------- timing
+
+class Timer:
+    """Per-stage HIP-event timing of one step on the current stream."""
+
+    def __init__(self, names):
+        self.names = names
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+
+    def mark(self, i):
+        self.ev[i].record()
+
+    def stage_ms(self):
+        return [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(len(self.names))]
+
+
+def flush_caches(buf):
+    buf.fill_(1.0)       # 1 GiB write: evicts L2 and the last-level cache
+
+
+def run_steps(step_fn, names, steps, warmup, flush):
+    buf = torch.empty(1 << 28, dtype=torch.float32, device=DEV) if flush else None
+    for _ in range(warmup):
+        if flush:
+            flush_caches(buf)
+        step_fn(Timer(names))
+    torch.cuda.synchronize()
+    timers = []
+    wall0 = time.perf_counter()
+    for _ in range(steps):
+        if flush:
+            flush_caches(buf)
+        tm = Timer(names)
+        step_fn(tm)
+        timers.append(tm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([tm.stage_ms() for tm in timers])          # steps x stages
+    step_ms = per.sum(axis=1)
+    return {
+        "step_ms_mean": float(step_ms.mean()),
+        "step_ms_median": float(np.median(step_ms)),
+        "step_ms_p90": float(np.percentile(step_ms, 90)),
+        "stage_ms": {n: float(per[:, i].mean()) for i, n in enumerate(names)},
+        "wall_s": wall,
+    }
+
+
+# ---------------------------------------------------------------- workloads
+
+def setup_prefill(w):
+    inp = gen.prefill_inputs(w, device=DEV)
+    B, S = w.B, w.T
+    dt = gen.torch_dtype(w.dt)
+    st = dict(inp)
+    st["kv_cmp"] = torch.empty(B, w.n_cmp, 2 * w.D, device=DEV, dtype=dt)
+    st["k_idx"] = torch.empty(B, w.n_cmp, w.d_I, device=DEV, dtype=dt)
+    st["pos0"] = i64([0] * B)
+    st["ncmp"] = i32([w.n_cmp] * B)
+    st["raw_base"] = i64([0] * B)
+    st["idx"] = torch.empty(B, S, w.topk, dtype=torch.int32, device=DEV)
+    st["out"] = torch.empty(B, S, w.H, w.D, device=DEV, dtype=dt)
+    st["ws_c1"] = torch.empty(max(1, csa.csa_compress_workspace_size(B, S, w.d_model, 2 * w.D, w.m, w.overlap, dt)), dtype=torch.uint8, device=DEV)
+    st["ws_c2"] = torch.empty(max(1, csa.csa_compress_workspace_size(B, S, w.d_model, w.d_I, w.m, w.overlap, dt)), dtype=torch.uint8, device=DEV)
+    st["ws_i"] = torch.empty(max(1, csa.csa_indexer_topk_workspace_size(B, S, w.H_I, w.d_I, w.n_cmp, w.topk, dt)), dtype=torch.uint8, device=DEV)
+    st["ws_a"] = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(B, S, w.H, w.D, w.topk, w.window)), dtype=torch.uint8, device=DEV)
+    return st
+
+
+def step_prefill(w, st):
+    def fn(tm):
+        tm.mark(0)
+        csa.csa_compress(st["x"], st["w_kv"], st["w_gate"], st["pos0"], w.m, w.overlap,
+                         st["kv_cmp"], workspace=st["ws_c1"])
+        csa.csa_compress(st["x"], st["w_ikv"], st["w_igate"], st["pos0"], w.m, w.overlap,
+                         st["k_idx"], workspace=st["ws_c2"])
+        tm.mark(1)
+        csa.csa_indexer_topk(st["q_idx"], st["w_idx"], st["k_idx"], w.m, w.topk, st["pos0"],
+                             st["ncmp"], q_scale=st["q_scale"], idx_out=st["idx"],
+                             workspace=st["ws_i"])
+        tm.mark(2)
+        csa.csa_sparse_attn(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"], w.window, st["pos0"],
+                            st["raw_base"], out=st["out"], workspace=st["ws_a"])
+        tm.mark(3)
+    return fn, ["compress", "indexer_topk", "sparse_attn"]
+
+
+def setup_decode(w):
+    stream = w.d_model > 0
+    # the streaming step emits the last entry itself
+    inp = gen.decode_inputs(w, device=DEV)
+    B = w.B
+    st = dict(inp)
+    T = w.ctx
+    st["q_pos"] = i64([T - 1] * B)
+    st["ncmp"] = i32([w.n_cmp] * B)
+    st["raw_base"] = i64([T - w.window] * B)
+    st["idx"] = torch.empty(B, 1, w.topk, dtype=torch.int32, device=DEV)
+    st["out"] = torch.empty(B, 1, w.H, w.D, device=DEV, dtype=torch.bfloat16)
+    st["ws_i"] = torch.empty(max(1, csa.csa_indexer_topk_workspace_size(B, 1, w.H_I, w.d_I, w.n_cmp, w.topk, torch.float8_e4m3fn)), dtype=torch.uint8, device=DEV)
+    st["ws_a"] = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(B, 1, w.H, w.D, w.topk, w.window)), dtype=torch.uint8, device=DEV)
+    if stream:
+        ns = 2 * w.m - 1
+        for k, E in (("main", 2 * w.D), ("idx", w.d_I)):
+            st["s0_" + k] = torch.empty(B, ns, 2, E, device=DEV)
+            st["s1_" + k] = torch.empty(B, ns, 2, E, device=DEV)
+            st["ws_" + k] = torch.empty(max(1, csa.csa_compress_workspace_size(B, w.tail, w.d_model, E, w.m, w.overlap, torch.bfloat16)), dtype=torch.uint8, device=DEV)
+        # untimed: stream the 7-token tail (positions T-8 .. T-2) into the state
+        p_tail = i64([T - 1 - w.tail] * B)
+        csa.csa_compress(st["x_tail"], st["w_kv"], st["w_gate"], p_tail, w.m, w.overlap,
+                         st["kv_cmp"], state_out=st["s0_main"], workspace=st["ws_main"])
+        csa.csa_compress(st["x_tail"], st["w_ikv"], st["w_igate"], p_tail, w.m, w.overlap,
+                         st["k_idx"], out_scale=st["k_scale"], state_out=st["s0_idx"],
+                         workspace=st["ws_idx"])
+        torch.cuda.synchronize()
+    return st
+
+
+def step_decode(w, st):
+    stream = w.d_model > 0
+
+    def fn(tm):
+        tm.mark(0)
+        i = 0
+        if stream:
+            csa.csa_compress(st["x_new"], st["w_kv"], st["w_gate"], st["q_pos"], w.m, w.overlap,
+                             st["kv_cmp"], state_in=st["s0_main"], state_out=st["s1_main"],
+                             workspace=st["ws_main"])
+            csa.csa_compress(st["x_new"], st["w_ikv"], st["w_igate"], st["q_pos"], w.m, w.overlap,
+                             st["k_idx"], out_scale=st["k_scale"], state_in=st["s0_idx"],
+                             state_out=st["s1_idx"], workspace=st["ws_idx"])
+            i += 1
+            tm.mark(i)
+        csa.csa_indexer_topk(st["q_idx"], st["w_idx"], st["k_idx"], w.m, w.topk, st["q_pos"],
+                             st["ncmp"], q_scale=st["q_scale"], k_scale=st["k_scale"],
+                             idx_out=st["idx"], workspace=st["ws_i"])
+        i += 1
+        tm.mark(i)
+        csa.csa_sparse_attn(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"], w.window, st["q_pos"],
+                            st["raw_base"], out=st["out"], workspace=st["ws_a"])
+        i += 1
+        tm.mark(i)
+    names = (["compress"] if stream else []) + ["indexer_topk", "sparse_attn"]
+    return fn, names
+
+
+def setup_hca(w):
+    st = gen.hca_inputs(w, device=DEV)
+    q0 = w.ctx - w.T
+    st["q_pos"] = i64([q0] * w.B)
+    st["ncmp"] = i32([w.n_cmp] * w.B)
+    st["raw_base"] = i64([q0 - w.window + 1] * w.B)
+    st["out"] = torch.empty_like(st["q"])
+    st["ws"] = torch.empty(max(1, csa.hca_dense_attn_workspace_size(w.B, w.T, w.H, w.D, w.n_cmp, w.window)), dtype=torch.uint8, device=DEV)
+    return st
+
+
+def step_hca(w, st):
+    def fn(tm):
+        tm.mark(0)
+        csa.hca_dense_attn(st["q"], st["kv_cmp"], st["kv_raw"], w.m, w.window, st["q_pos"],
+                           st["ncmp"], st["raw_base"], out=st["out"], workspace=st["ws"])
+        tm.mark(1)
+    return fn, ["hca_dense_attn"]
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, budget_s=12.0):
+    """Time the oracle on a bounded sample of the workload on the host cores."""
+    from oracle import oracle as orc
+    cores = orc.num_threads()
+    rng = np.random.default_rng(0)
+    if w.kind == "csa_prefill":
+        # sample query tokens spread over the sequence; per token the oracle
+        # runs its share of the compressor (one entry per m tokens, both
+        # compressors), the indexer row and the attention row
+        d = gen.Draw(w.seed + 999)
+        dm, S = w.d_model, w.T
+        x = gen.host_bits(gen.store(d.normal(1, 2 * w.m, dm), w.dt))
+        wk, wg = (gen.host_bits(t) for t in gen.compressor_weights(d, dm, 2 * w.D, w.dt))
+        wik, wig = (gen.host_bits(t) for t in gen.compressor_weights(d, dm, w.d_I, w.dt))
+        kv_cmp = gen.host_bits(gen.store(d.normal(1, w.n_cmp, 2 * w.D), w.dt))
+        kv_raw = gen.host_bits(gen.store(d.normal(1, S, 2 * w.D), w.dt))
+        k_idx = gen.host_bits(gen.store(d.normal(1, w.n_cmp, w.d_I), w.idx_dt))
+        n_tok = 0
+        t_comp = t_idx = t_att = 0.0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            tt = int(rng.integers(0, S))
+            q_idx = gen.host_bits(gen.store(d.normal(1, 1, w.H_I, w.d_I), w.idx_dt))
+            w_idx = d.normal(1, 1, w.H_I).numpy()
+            q = gen.host_bits(gen.store(d.normal(1, 1, w.H, w.D), w.dt))
+            a = time.perf_counter()
+            if n_tok % w.m == 0:       # one entry of each compressor per m tokens
+                orc.compress(x, wk, wg, w.m, w.overlap, 0, 2, want_state=False)
+                orc.compress(x, wik, wig, w.m, w.overlap, 0, 2, want_state=False)
+            b = time.perf_counter()
+            idx = orc.indexer_topk(q_idx, w_idx, k_idx, w.m, w.topk, tt, w.n_cmp)[0]
+            c = time.perf_counter()
+            orc.sparse_attn(q, kv_cmp, idx, kv_raw, w.window, tt, 0)
+            e = time.perf_counter()
+            t_comp += b - a
+            t_idx += c - b
+            t_att += e - c
+            n_tok += 1
+        tot = t_comp + t_idx + t_att
+        return {"value": n_tok / tot, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "sample": "%d query tokens at uniformly drawn positions of the 8192-token "
+                          "prefill, each with its indexer row and attention row, plus one "
+                          "compressed entry of each compressor per %d tokens" % (n_tok, w.m)}
+    if w.kind == "csa_decode":
+        d = gen.Draw(w.seed + 999)
+        Bs = 2
+        k_idx, k_scale = gen.indexer_keys(d, Bs, w.n_cmp, w.d_I, w.idx_dt)
+        q_idx, q_scale, w_idx = gen.indexer_query(d, Bs, 1, w.H_I, w.d_I, w.idx_dt)
+        kv_cmp = gen.host_bits(gen.store(d.normal(Bs, min(w.n_cmp, 65536), 2 * w.D), w.dt))
+        kv_raw = gen.host_bits(gen.store(d.normal(Bs, w.window, 2 * w.D), w.dt))
+        q = gen.host_bits(gen.store(d.normal(Bs, 1, w.H, w.D), w.dt))
+        kb, ks = gen.host_bits(k_idx), gen.host_bits(k_scale)
+        qb, qs, wb = gen.host_bits(q_idx), gen.host_bits(q_scale), w_idx.numpy()
+        n_q, tot = 0, 0.0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            a = time.perf_counter()
+            idx = orc.indexer_topk(qb, wb, kb, w.m, w.topk, w.ctx - 1, w.n_cmp, q_scale=qs,
+                                   k_scale=ks)[0]
+            idx = np.where(idx >= kv_cmp.shape[1], idx % kv_cmp.shape[1], idx)
+            orc.sparse_attn(q, kv_cmp, idx, kv_raw, w.window, w.ctx - 1, w.ctx - w.window)
+            tot += time.perf_counter() - a
+            n_q += Bs
+        return {"value": n_q / tot, "unit": "queries/s", "cores": cores, "kind": "oracle",
+                "sample": "%d decode queries (indexer over all %d entries + top-%d + "
+                          "attention over %d keys), %d sequences per oracle call"
+                          % (n_q, w.n_cmp, w.topk, w.topk + w.window, Bs)}
+    if w.kind == "hca_prefill":
+        d = gen.Draw(w.seed + 999)
+        kv_cmp = gen.host_bits(gen.store(d.normal(1, w.n_cmp, 2 * w.D), w.dt))
+        kv_raw = gen.host_bits(gen.store(d.normal(1, w.T + w.window - 1, 2 * w.D), w.dt))
+        q0 = w.ctx - w.T
+        n_tok, tot = 0, 0.0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            Ts = 16
+            t = int(rng.integers(0, w.T - Ts))
+            q = gen.host_bits(gen.store(d.normal(1, Ts, w.H, w.D), w.dt))
+            a = time.perf_counter()
+            orc.hca_dense_attn(q, kv_cmp, kv_raw, w.m, w.window, q0 + t, w.n_cmp, q0 - w.window + 1)
+            tot += time.perf_counter() - a
+            n_tok += Ts
+        return {"value": n_tok / tot, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "sample": "%d query tokens of the 4096-token chunk (16 per oracle call)" % n_tok}
+    return None
+
+
+# ---------------------------------------------------------------- driver
+
+def measure(name, steps, warmup, with_cpu):
+    w = gen.WORKLOADS[name]
+    if w.kind == "csa_prefill":
+        st = setup_prefill(w)
+        fn, names = step_prefill(w, st)
+        flush = False
+        pairs, visits = csa_counts(w, 0, w.T, w.n_cmp)
+        attn_flops = visits * w.H * w.D * 4
+        idx_flops = pairs * w.H_I * w.d_I * 2
+        comp_flops = 2 * w.B * w.T * w.d_model * 2 * (2 * w.D + w.d_I)
+        unit_items, unit = w.B * w.T, "tokens/s"
+    elif w.kind == "csa_decode":
+        st = setup_decode(w)
+        fn, names = step_decode(w, st)
+        flush = True
+        unit_items, unit = w.B, "queries/s"
+    else:
+        st = setup_hca(w)
+        fn, names = step_hca(w, st)
+        flush = False
+        unit_items, unit = w.B * w.T, "tokens/s"
+    r = run_steps(fn, names, steps, warmup, flush)
+    step_s = r["step_ms_mean"] / 1e3
+    res = {"workload": name, "value": unit_items / step_s, "unit": unit,
+           "ms_per_step": r["step_ms_mean"], "ms_median": r["step_ms_median"],
+           "ms_p90": r["step_ms_p90"], "stage_ms": r["stage_ms"]}
+    sm = r["stage_ms"]
+    if w.kind == "csa_prefill":
+        if w.dt == gen.BF16:
+            ach = attn_flops / (sm["sparse_attn"] / 1e3) / 1e12
+            res["roofline"] = {"bound": "mfma", "kernel": "attn_bf16_kernel",
+                               "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        else:
+            ach = attn_flops / (sm["sparse_attn"] / 1e3) / 1e12
+            res["roofline"] = {"bound": "alu", "kernel": "attn_f32_kernel", "achieved": ach,
+                               "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": ach / FP32_VECTOR_PEAK_TFLOPS, "traffic": None}
+        res["work"] = {"attn_gflop": attn_flops / 1e9, "indexer_gflop": idx_flops / 1e9,
+                       "compress_gflop": comp_flops / 1e9,
+                       "indexer_plus_attn_mfma_frac": (attn_flops + idx_flops)
+                       / ((sm["sparse_attn"] + sm["indexer_topk"]) / 1e3) / 1e12
+                       / MFMA_BF16_PEAK_TFLOPS}
+    elif w.kind == "csa_decode":
+        B, Nc = w.B, w.n_cmp
+        key_bytes = B * Nc * (w.d_I + 4)
+        gather = B * (w.topk + w.window) * 4 * w.D
+        small = B * (2 * w.H * w.D * 2 + 2 * w.topk * 4 + w.H_I * w.d_I + w.H_I * 8)
+        total = key_bytes + gather + small
+        if w.d_model:
+            total += 2 * (2 * w.D + w.d_I) * w.d_model * 2       # compressor weights (bf16)
+            total += B * (w.d_model * 2 + 2 * 7 * 2 * (2 * w.D + w.d_I) * 4)
+        ach = key_bytes / (sm["indexer_topk"] / 1e3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": "indexer_topk (score_fp8_kernel + select)",
+                           "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": None}
+        res["work"] = {"step_bytes": total, "indexer_key_bytes": key_bytes,
+                       "attn_gather_bytes": gather,
+                       "step_hbm_frac": total / step_s / 1e9 / HBM_PEAK_GBS,
+                       "attn_gbs": gather / (sm["sparse_attn"] / 1e3) / 1e9}
+    else:
+        visits = hca_visits(w, w.ctx - w.T)
+        flops = visits * w.H * w.D * 4
+        ach = flops / step_s / 1e12
+        res["roofline"] = {"bound": "mfma", "kernel": "attn_bf16_kernel (dense)", "achieved": ach,
+                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        res["work"] = {"attn_gflop": flops / 1e9}
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(w)
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="default")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the path shards by sequence across "
+              "GPUs by design, but no multi-GPU run is implemented); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    csa.lib()
+    if args.workload == "all":
+        for name in gen.WORKLOADS:
+            r = measure(name, args.steps, args.warmup, not args.no_cpu)
+            print(json.dumps(r), flush=True)
+        return
+    if args.workload != "default":
+        print(json.dumps(measure(args.workload, args.steps, args.warmup, not args.no_cpu)), flush=True)
+        return
+    prim = measure("csa_prefill_8k_bf16", args.steps, args.warmup, not args.no_cpu)
+    dec = measure("csa_decode_128k_b32", args.steps, args.warmup, not args.no_cpu)
+    line = {
+        "metric": "CSA prefill tokens/s + decode queries/s at 128K ctx; % of HBM/MFMA peak",
+        "value": prim["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "csa_prefill_8k_bf16", "batch": 1, "seq_len": 8192,
+                   "d_model": 4096, "m": 4, "overlap": 1, "heads": 64, "head_dim": 128,
+                   "indexer": "16x64 bf16", "topk": 512, "window": 512, "parallelism": "none"},
+        "roofline": prim["roofline"],
+        "cpu_baseline": prim.get("cpu_baseline"),
+        "stage_ms": prim["stage_ms"], "work": prim["work"],
+        "decode_128k": {k: dec[k] for k in ("value", "unit", "ms_per_step", "ms_median", "ms_p90",
+                                             "stage_ms", "roofline", "work")}
+        | {"cpu_baseline": dec.get("cpu_baseline"), "workload": "csa_decode_128k_b32",
+           "cache": "L2 + last-level cache flushed before every step"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+// C ABI of libcsa: argument validation, workspace sizing and dispatch to the
+// gfx950 kernels.  Every check runs on the host before any launch; nothing is
+// allocated and nothing synchronises.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+csa_status_t fail(csa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+csa_status_t ok() {
+  g_err[0] = 0;
+  return CSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+csa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(csa_status_t s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_E_ARG: return "invalid argument";
+    case CSA_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case CSA_E_WORKSPACE: return "workspace too small";
+    case CSA_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* csa_last_error(void) { return g_err; }
+
+size_t csa_compress_workspace_size(int B, int L, int d_model, int E, int m, int overlap,
+                                   csa_dtype_t in_dt) {
+  if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0) return 0;
+  return csa_host::compress_ws_bytes(B, L, d_model, E, m, overlap, in_dt);
+}
+
+csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap,
+                          const int64_t* pos0, const void* x, const void* w_kv,
+                          const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                          const float* state_in, float* state_out, void* out, float* out_scale,
+                          csa_dtype_t out_dt, int Nc_cap, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0 || Nc_cap < 0)
+    return fail(CSA_E_ARG, "csa_compress: B, L, d_model, E must be > 0 and Nc_cap >= 0");
+  if (m < 1) return fail(CSA_E_ARG, "csa_compress: m must be >= 1 (got %d)", m);
+  if (overlap != 0 && overlap != 1) return fail(CSA_E_ARG, "csa_compress: overlap must be 0 or 1");
+  if (!pos0 || !x || !w_kv || !w_gate || !out)
+    return fail(CSA_E_ARG, "csa_compress: pos0, x, w_kv, w_gate and out are required");
+  if (state_in && state_in == state_out)
+    return fail(CSA_E_ARG, "csa_compress: state_out must not alias state_in");
+  if (in_dt != CSA_DT_F32 && in_dt != CSA_DT_BF16)
+    return fail(CSA_E_UNSUPPORTED, "csa_compress: in_dt must be F32 or BF16");
+  if (out_dt != CSA_DT_F32 && out_dt != CSA_DT_BF16 && out_dt != CSA_DT_FP8E4M3)
+    return fail(CSA_E_ARG, "csa_compress: bad out_dt %d", (int)out_dt);
+  if (out_dt == CSA_DT_FP8E4M3 && !out_scale)
+    return fail(CSA_E_ARG, "csa_compress: fp8 output needs out_scale");
+  if (E > 1024) return fail(CSA_E_UNSUPPORTED, "csa_compress: E > 1024");
+  if (in_dt == CSA_DT_BF16 && (d_model % 32 != 0 || !aligned16(x) || !aligned16(w_kv) ||
+                               !aligned16(w_gate)))
+    return fail(CSA_E_UNSUPPORTED,
+                "csa_compress: bf16 needs d_model %% 32 == 0 and 16-byte aligned x and weights");
+  const size_t need = csa_host::compress_ws_bytes(B, L, d_model, E, m, overlap, in_dt);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "csa_compress: workspace %zu < %zu bytes", ws_bytes, need);
+  csa_host::CompressArgs a{B, L, d_model, E, m, overlap, Nc_cap, pos0, x, w_kv, w_gate, in_dt,
+                           out_dt, ape, state_in, state_out, out, out_scale, workspace};
+  return hip_status(csa_host::launch_compress(a, stream), "csa_compress launch");
+}
+
+size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_cap, int topk,
+                                       csa_dtype_t qk_dt) {
+  if (B <= 0 || T <= 0 || Nc_cap <= 0) return 0;
+  return csa_host::indexer_ws_bytes(B, T, H_I, d_I, Nc_cap, topk, qk_dt);
+}
+
+csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
+                              const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
+                              const float* q_scale, const float* w_idx, const void* k_idx,
+                              const float* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
+                              float* score_out, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (B <= 0 || T <= 0 || H_I <= 0 || d_I <= 0 || Nc_cap < 0 || topk < 0)
+    return fail(CSA_E_ARG, "csa_indexer_topk: B, T, H_I, d_I must be > 0; Nc_cap, topk >= 0");
+  if (m < 1) return fail(CSA_E_ARG, "csa_indexer_topk: m must be >= 1");
+  if (topk == 0) return ok();  // nothing to select, nothing to write
+  if (!q_pos || !n_cmp || !q_idx || !w_idx || !idx_out || (Nc_cap > 0 && !k_idx))
+    return fail(CSA_E_ARG, "csa_indexer_topk: missing required pointer");
+  if (qk_dt == CSA_DT_FP8E4M3 && (!q_scale || (Nc_cap > 0 && !k_scale)))
+    return fail(CSA_E_ARG, "csa_indexer_topk: fp8 needs q_scale and k_scale");
+  if (topk > 8192) return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: topk > 8192");
+  if (Nc_cap > 1024 * 2048) return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: Nc_cap > 2^21");
+  if (qk_dt == CSA_DT_F32) {
+    if (!((H_I == 4 && d_I == 32) || (H_I == 16 && d_I == 64)))
+      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: f32 needs (H_I, d_I) in {(4,32),(16,64)}");
+  } else if (qk_dt == CSA_DT_BF16 || qk_dt == CSA_DT_FP8E4M3) {
+    if (H_I != 16 || d_I != 64)
+      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: bf16/fp8 need H_I = 16, d_I = 64");
+    if (!aligned16(q_idx) || (Nc_cap > 0 && !aligned16(k_idx)))
+      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: q_idx and k_idx must be 16-byte aligned");
+    if (qk_dt == CSA_DT_BF16 && Nc_cap > 8192 && T != 1)
+      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: bf16 rows longer than 8192 need T == 1");
+  } else {
+    return fail(CSA_E_ARG, "csa_indexer_topk: bad qk_dt %d", (int)qk_dt);
+  }
+  const size_t need = csa_host::indexer_ws_bytes(B, T, H_I, d_I, Nc_cap, topk, qk_dt);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "csa_indexer_topk: workspace %zu < %zu bytes", ws_bytes, need);
+  csa_host::IndexerArgs a{B, T, H_I, d_I, Nc_cap, m, topk, q_pos, n_cmp, q_idx, q_scale, w_idx,
+                          k_idx, k_scale, qk_dt, idx_out, score_out, workspace};
+  return hip_status(csa_host::launch_indexer_topk(a, stream), "csa_indexer_topk launch");
+}
+
+static csa_status_t check_attn(const char* fn, int B, int T, int H, int D, int window,
+                               const int64_t* q_pos, const void* q, const void* kv_cmp, int Nc_cap,
+                               const void* kv_raw, int R_cap, const int64_t* raw_base,
+                               csa_dtype_t dt, void* out) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || window < 0 || Nc_cap < 0 || R_cap < 0)
+    return fail(CSA_E_ARG, "%s: B, T, H, D must be > 0; window, Nc_cap, R_cap >= 0", fn);
+  if (!q_pos || !q || !out || !raw_base || (Nc_cap > 0 && !kv_cmp) || (R_cap > 0 && !kv_raw))
+    return fail(CSA_E_ARG, "%s: missing required pointer", fn);
+  if (dt == CSA_DT_F32) {
+    if (D != 64 && D != 128) return fail(CSA_E_UNSUPPORTED, "%s: f32 needs D in {64, 128}", fn);
+  } else if (dt == CSA_DT_BF16) {
+    if (D != 128 || (H != 32 && H != 64))
+      return fail(CSA_E_UNSUPPORTED, "%s: bf16 needs D = 128 and H in {32, 64}", fn);
+    if (!aligned16(q) || (kv_cmp && !aligned16(kv_cmp)) || (kv_raw && !aligned16(kv_raw)) ||
+        !aligned16(out))
+      return fail(CSA_E_UNSUPPORTED, "%s: bf16 tensors must be 16-byte aligned", fn);
+  } else {
+    return fail(CSA_E_UNSUPPORTED, "%s: dt must be F32 or BF16", fn);
+  }
+  return CSA_OK;
+}
+
+size_t csa_sparse_attn_workspace_size(int B, int T, int H, int D, int topk, int window) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
+  return csa_host::attn_ws_bytes(B, T, H, D, topk + window);
+}
+
+csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, float scale,
+                             const int64_t* q_pos, const void* q, const void* kv_cmp, int Nc_cap,
+                             const int32_t* idx, const void* kv_raw, int R_cap,
+                             const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  csa_status_t st = check_attn("csa_sparse_attn", B, T, H, D, window, q_pos, q, kv_cmp, Nc_cap,
+                               kv_raw, R_cap, raw_base, dt, out);
+  if (st != CSA_OK) return st;
+  if (topk < 0) return fail(CSA_E_ARG, "csa_sparse_attn: topk must be >= 0");
+  if (topk > 0 && !idx) return fail(CSA_E_ARG, "csa_sparse_attn: idx is required when topk > 0");
+  const size_t need = dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, topk + window);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "csa_sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
+  csa_host::AttnArgs a{B, T, H, D, topk, window, 1, Nc_cap, R_cap, false, scale, q_pos, nullptr,
+                       q, kv_cmp, idx, kv_raw, raw_base, dt, out, lse, workspace};
+  return hip_status(csa_host::launch_attn(a, stream), "csa_sparse_attn launch");
+}
+
+size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
+  return csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window);
+}
+
+csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float scale,
+                            const int64_t* q_pos, const int32_t* n_cmp, const void* q,
+                            const void* kv_cmp, int Nc_cap, const void* kv_raw, int R_cap,
+                            const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  csa_status_t st = check_attn("hca_dense_attn", B, T, H, D, window, q_pos, q, kv_cmp, Nc_cap,
+                               kv_raw, R_cap, raw_base, dt, out);
+  if (st != CSA_OK) return st;
+  if (m < 1) return fail(CSA_E_ARG, "hca_dense_attn: m must be >= 1");
+  if (!n_cmp) return fail(CSA_E_ARG, "hca_dense_attn: n_cmp is required");
+  const size_t need = dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "hca_dense_attn: workspace %zu < %zu bytes", ws_bytes, need);
+  csa_host::AttnArgs a{B, T, H, D, 0, window, m, Nc_cap, R_cap, true, scale, q_pos, n_cmp,
+                       q, kv_cmp, nullptr, kv_raw, raw_base, dt, out, lse, workspace};
+  return hip_status(csa_host::launch_attn(a, stream), "hca_dense_attn launch");
+}
+
+}  // extern "C"

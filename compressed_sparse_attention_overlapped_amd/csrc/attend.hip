@@ -1,0 +1,372 @@
+// Sparse / dense MQA attention over compressed entries plus the raw sliding
+// window, for gfx950.
+//
+// DS-V4 analysis section 1.2 (attend to the k selected compressed entries and
+// the sliding-window KV), section 1.4 (HCA: every compressed entry), Notion
+// copy section 1.1 (softmax(q K^T / sqrt(d)) V) and the MQA remark there (one
+// KV head shared by every query head).
+//
+// Key list of a query row (b, t) at position pos: first the compressed part
+// (CSA: the topk slots of idx; HCA: entries 0 .. n_vis - 1), then the raw
+// tokens max(0, pos - W + 1) .. pos.  Invalid slots are masked.  One softmax
+// runs over the whole list.
+//
+// bf16 kernel: a work item is (row, split); its 4 waves take 32-key tiles in
+// turn.  A tile of [K | V] rows (512 B each) is loaded with 16-byte coalesced
+// loads into the wave's LDS region, then
+//     S^T (32 keys x 32 heads) = K (32 x 128) . Q^T     (8 MFMA 32x32x16 / head tile)
+//     O^T (128 x 32 heads)    += V^T (128 x 32) . P^T   (8 MFMA / head tile)
+// The S^T accumulator of a lane holds one head and 16 keys, which is exactly
+// the P^T operand of the second product once the k order of that product is
+// permuted to match; V^T fragments are read from LDS element-wise.  Online
+// softmax runs in base 2 with the scale folded in.  The 4 waves merge their
+// (max, sum, O) through LDS; split items write fp32 partials that a combine
+// kernel merges by log-sum-exp.
+#include "common.h"
+
+namespace csa {
+
+constexpr int AT_KT = 32;            // keys per tile
+constexpr int AT_ROW = 256 + 8;      // bf16 per LDS row: [K | V] (D = 128) + 16 B pad
+constexpr int AT_WAVES = 4;
+constexpr int AT_MIN_SPLIT_KEYS = 256;
+
+struct KeyList {
+  int n_c;       // compressed positions (topk slots or n_vis)
+  int64_t lo;    // first window token
+  int n_w;       // window tokens
+};
+
+__device__ __forceinline__ KeyList key_list(bool dense, int topk, int window, int64_t pos,
+                                            int32_t ncmp, int m, int Nc_cap) {
+  KeyList L;
+  L.n_c = dense ? n_visible(pos, ncmp, m, Nc_cap) : topk;
+  if (window > 0 && pos >= 0) {
+    L.lo = pos - window + 1;
+    if (L.lo < 0) L.lo = 0;
+    L.n_w = (int)(pos - L.lo + 1);
+  } else {
+    L.lo = 0;
+    L.n_w = 0;
+  }
+  return L;
+}
+
+// Source row of list position p (nullptr if the slot is empty).
+template <typename Tp>
+__device__ __forceinline__ const Tp* key_row(int p, const KeyList& L, bool dense,
+                                             const int32_t* idx_row, const Tp* kv_cmp_b,
+                                             int Nc_cap, const Tp* kv_raw_b, int R_cap,
+                                             int64_t raw_base, int row_elems) {
+  if (p < L.n_c) {
+    int j = dense ? p : idx_row[p];
+    if (j < 0 || j >= Nc_cap) return nullptr;
+    return kv_cmp_b + (size_t)j * row_elems;
+  }
+  int64_t r = L.lo + (p - L.n_c) - raw_base;
+  if (r < 0 || r >= R_cap) return nullptr;
+  return kv_raw_b + (size_t)r * row_elems;
+}
+
+// ---------------------------------------------------------------- bf16, D = 128
+template <int NH>  // head tiles of 32: H = 32 NH
+__global__ void __launch_bounds__(256) attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv_cmp,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
+    const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
+    const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
+    int R_cap, bool dense, float scale_log2, int n_split, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int H = 32 * NH, D = 128;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int item = blockIdx.x;
+  const int rowi = item / n_split, split = item % n_split;
+  const int b = rowi / T, t = rowi % T;
+  const int64_t pos = q_pos[b] + t;
+  const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
+  const int nk = L.n_c + L.n_w;
+  int per = (nk + n_split - 1) / n_split;
+  per = (per + AT_KT - 1) / AT_KT * AT_KT;
+  const int kb = min(nk, split * per), ke = min(nk, kb + per);
+  const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
+  const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
+  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  const int64_t rbase = raw_base[b];
+
+  uint16_t* tile = smem + wave * (AT_KT * AT_ROW);
+  __shared__ int valid_s[AT_WAVES][AT_KT];
+
+  // Q^T fragments: head tile ht, k-step s: lane holds q[h = 32 ht + lane%32]
+  // dims 16 s + 8 (lane / 32) .. + 8
+  bf16x8 qf[NH][8];
+  {
+    const uint16_t* qrow = q + (size_t)rowi * H * D;
+    for (int ht = 0; ht < NH; ++ht)
+      for (int s = 0; s < 8; ++s)
+        qf[ht][s] = *(const bf16x8*)(qrow + (size_t)(32 * ht + (lane & 31)) * D + 16 * s +
+                                     8 * (lane >> 5));
+  }
+  f32x16 o[4][NH];
+  for (int dt = 0; dt < 4; ++dt)
+    for (int ht = 0; ht < NH; ++ht)
+      for (int r = 0; r < 16; ++r) o[dt][ht][r] = 0.0f;
+  float mrun[NH], lrun[NH];
+  for (int ht = 0; ht < NH; ++ht) {
+    mrun[ht] = -INFINITY;
+    lrun[ht] = 0.0f;
+  }
+
+  const int ntiles = (ke - kb + AT_KT - 1) / AT_KT;
+  const int col = lane & 31;  // 16-byte column of the 512-byte row
+  for (int ti = wave; ti < ntiles; ti += AT_WAVES) {
+    const int p0 = kb + ti * AT_KT;
+    // ---- load: lane covers rows 2 i + lane/32, column `col`
+    for (int i = 0; i < AT_KT / 2; ++i) {
+      const int rr = 2 * i + (lane >> 5);
+      const int p = p0 + rr;
+      const uint16_t* src = p < ke ? key_row(p, L, dense, idx_row, kvc_b, Nc_cap, kvr_b, R_cap,
+                                             rbase, 2 * D)
+                                   : nullptr;
+      u32x4 v = {0, 0, 0, 0};
+      if (src) v = *(const u32x4*)(src + 8 * col);
+      *(u32x4*)(tile + rr * AT_ROW + 8 * col) = v;
+      if (col == 0) valid_s[wave][rr] = src != nullptr;
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // ---- S^T = K Q^T
+    f32x16 sacc[NH];
+    for (int ht = 0; ht < NH; ++ht)
+      for (int r = 0; r < 16; ++r) sacc[ht][r] = 0.0f;
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 kf = *(const bf16x8*)(tile + (lane & 31) * AT_ROW + 16 * s + 8 * (lane >> 5));
+      for (int ht = 0; ht < NH; ++ht)
+        sacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ht][s], sacc[ht], 0, 0, 0);
+    }
+    // ---- online softmax (base 2); lane: head 32 ht + lane%32, keys
+    // kr(r) = 8 (r/4) + 4 (lane/32) + r%4
+    bool kval[16];
+    for (int r = 0; r < 16; ++r) kval[r] = valid_s[wave][8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] != 0;
+    bf16x8 pf[NH][2];
+    for (int ht = 0; ht < NH; ++ht) {
+      float mx = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        float sv = kval[r] ? sacc[ht][r] * scale_log2 : -INFINITY;
+        sacc[ht][r] = sv;
+        mx = fmaxf(mx, sv);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrun[ht], mx);
+      const float muse = mnew == -INFINITY ? 0.0f : mnew;
+      const float corr = exp2f(mrun[ht] - muse);
+      float ps = 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2f(sacc[ht][r] - muse);
+        ps += pv;
+        sacc[ht][r] = pv;
+      }
+      ps += __shfl_xor(ps, 32, 64);
+      lrun[ht] = lrun[ht] * corr + ps;
+      mrun[ht] = mnew;
+      for (int dt = 0; dt < 4; ++dt)
+        for (int r = 0; r < 16; ++r) o[dt][ht][r] *= corr;
+      for (int ks = 0; ks < 2; ++ks)
+        for (int e = 0; e < 8; ++e) pf[ht][ks][e] = (__bf16)sacc[ht][8 * ks + e];
+    }
+    // ---- O^T += V^T P^T.  k slot (8 half + e) of step ks is key
+    // 16 ks + 8 (e / 4) + 4 half + e % 4 for both operands.
+    for (int dt = 0; dt < 4; ++dt) {
+      const int d = 32 * dt + (lane & 31);
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 vf;
+        for (int e = 0; e < 8; ++e) {
+          const int key = 16 * ks + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          vf[e] = __builtin_bit_cast(__bf16, tile[key * AT_ROW + D + d]);
+        }
+        for (int ht = 0; ht < NH; ++ht)
+          o[dt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ht][ks], o[dt][ht], 0, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+
+  // ---- merge the 4 waves through LDS (reusing the tile buffers)
+  __syncthreads();
+  float* mb = (float*)smem;           // [H]
+  float* lb = mb + H;                 // [H]
+  float* ob = lb + H;                 // [H][D]
+  for (int w = 0; w < AT_WAVES; ++w) {
+    if (wave == w) {
+      for (int ht = 0; ht < NH; ++ht) {
+        const int h = 32 * ht + (lane & 31);
+        float m_prev = w ? mb[h] : -INFINITY, l_prev = w ? lb[h] : 0.0f;
+        float mnew = fmaxf(m_prev, mrun[ht]);
+        float muse = mnew == -INFINITY ? 0.0f : mnew;
+        float c_prev = exp2f(m_prev - muse), c_me = exp2f(mrun[ht] - muse);
+        for (int dt = 0; dt < 4; ++dt)
+          for (int r = 0; r < 16; ++r) {
+            const int d = 32 * dt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            float prev = w ? ob[h * D + d] : 0.0f;
+            ob[h * D + d] = prev * c_prev + o[dt][ht][r] * c_me;
+          }
+        if (lane < 32) {
+          mb[h] = mnew;
+          lb[h] = l_prev * c_prev + lrun[ht] * c_me;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // ---- write: final (n_split == 1) or partial
+  if (n_split == 1) {
+    for (int i = tid; i < H * D / 4; i += blockDim.x) {
+      const int h = (4 * i) / D, d = (4 * i) % D;
+      const float l = lb[h];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      uint16_t* orow = out + ((size_t)rowi * H + h) * D + d;
+      uint32_t lo = (uint32_t)f32_to_bf16(ob[h * D + d] * inv) |
+                    ((uint32_t)f32_to_bf16(ob[h * D + d + 1] * inv) << 16);
+      uint32_t hi = (uint32_t)f32_to_bf16(ob[h * D + d + 2] * inv) |
+                    ((uint32_t)f32_to_bf16(ob[h * D + d + 3] * inv) << 16);
+      *(u32x2*)orow = u32x2{lo, hi};
+    }
+    if (lse)
+      for (int h = tid; h < H; h += blockDim.x) {
+        const float l = lb[h];
+        lse[(size_t)rowi * H + h] = l > 0.0f ? (mb[h] + __log2f(l)) * kLn2 : -INFINITY;
+      }
+  } else {
+    float* po = part_o + (size_t)item * H * D;
+    for (int i = tid; i < H * D / 4; i += blockDim.x)
+      *(f32x4*)(po + 4 * i) = *(const f32x4*)(ob + 4 * i);
+    for (int h = tid; h < H; h += blockDim.x) {
+      part_ml[((size_t)item * H + h) * 2 + 0] = mb[h];
+      part_ml[((size_t)item * H + h) * 2 + 1] = lb[h];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+template <int OUT_DT>
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      int n_split, int H, int D, void* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  const int rowi = blockIdx.x;
+  for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
+    const int h = i / D;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s)
+      M = fmaxf(M, part_ml[(((size_t)rowi * n_split + s) * H + h) * 2]);
+    const float Mu = M == -INFINITY ? 0.0f : M;
+    float Ls = 0.0f, O = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+      const size_t it = (size_t)rowi * n_split + s;
+      const float c = exp2f(part_ml[(it * H + h) * 2] - Mu);
+      Ls += part_ml[(it * H + h) * 2 + 1] * c;
+      O += part_o[it * H * D + i] * c;
+    }
+    const float v = Ls > 0.0f ? O / Ls : 0.0f;
+    if (OUT_DT == CSA_DT_BF16)
+      ((uint16_t*)out)[(size_t)rowi * H * D + i] = f32_to_bf16(v);
+    else
+      ((float*)out)[(size_t)rowi * H * D + i] = v;
+    if (lse && (i % D) == 0) lse[(size_t)rowi * H + h] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- fp32
+// One wave per (row, head); lane owns dims lane and lane + 64.
+__global__ void __launch_bounds__(64) attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kv_cmp, const int32_t* __restrict__ idx,
+    const float* __restrict__ kv_raw, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, const int64_t* __restrict__ raw_base, int T, int H, int D,
+    int topk, int window, int m, int Nc_cap, int R_cap, bool dense, float scale_log2,
+    float* __restrict__ out, float* __restrict__ lse) {
+  const int lane = threadIdx.x;
+  const int rowi = blockIdx.x / H, h = blockIdx.x % H;
+  const int b = rowi / T, t = rowi % T;
+  const int64_t pos = q_pos[b] + t;
+  const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
+  const int nk = L.n_c + L.n_w;
+  const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
+  const float* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
+  const float* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  const int64_t rbase = raw_base[b];
+  const float* qr = q + ((size_t)rowi * H + h) * D;
+  const float q0 = lane < D ? qr[lane] : 0.0f;
+  const float q1 = lane + 64 < D ? qr[lane + 64] : 0.0f;
+  float mrun = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int p = 0; p < nk; ++p) {
+    const float* src = key_row(p, L, dense, idx_row, kvc_b, Nc_cap, kvr_b, R_cap, rbase, 2 * D);
+    if (!src) continue;
+    float part = (lane < D ? q0 * src[lane] : 0.0f) + (lane + 64 < D ? q1 * src[lane + 64] : 0.0f);
+    const float s = wave_sum(part) * scale_log2;
+    const float mnew = fmaxf(mrun, s);
+    const float corr = exp2f(mrun - mnew);
+    const float pv = exp2f(s - mnew);
+    l = l * corr + pv;
+    o0 = o0 * corr + pv * (lane < D ? src[D + lane] : 0.0f);
+    o1 = o1 * corr + pv * (lane + 64 < D ? src[D + lane + 64] : 0.0f);
+    mrun = mnew;
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* orow = out + ((size_t)rowi * H + h) * D;
+  if (lane < D) orow[lane] = o0 * inv;
+  if (lane + 64 < D) orow[lane + 64] = o1 * inv;
+  if (lse && lane == 0) lse[(size_t)rowi * H + h] = l > 0.0f ? (mrun + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+}  // namespace csa
+
+namespace csa_host {
+using namespace csa;
+
+static int attn_splits(int rows, int keys_per_row) {
+  // enough work items to fill the chip; every split keeps >= 256 keys
+  if (rows >= 1024 || keys_per_row <= AT_MIN_SPLIT_KEYS) return 1;
+  int s = (1024 + rows - 1) / rows;
+  int smax = (keys_per_row + AT_MIN_SPLIT_KEYS - 1) / AT_MIN_SPLIT_KEYS;
+  return s < smax ? s : smax;
+}
+
+size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row) {
+  const int rows = B * T;
+  const int s = attn_splits(rows, keys_per_row);
+  if (s == 1) return 0;
+  return (size_t)rows * s * H * (D + 2) * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+  const int rows = a.B * a.T;
+  const float scale_log2 = a.scale * kLog2e;
+  if (a.dt == CSA_DT_F32) {
+    attn_f32_kernel<<<rows * a.H, 64, 0, st>>>(
+        (const float*)a.q, (const float*)a.kv_cmp, a.idx, (const float*)a.kv_raw, a.q_pos,
+        a.n_cmp, a.raw_base, a.T, a.H, a.D, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
+        scale_log2, (float*)a.out, a.lse);
+    return hipGetLastError();
+  }
+  const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
+  const int n_split = attn_splits(rows, keys);
+  float* part_o = (float*)a.ws;
+  float* part_ml = part_o ? part_o + (size_t)rows * n_split * a.H * a.D : nullptr;
+  const size_t lds = (size_t)AT_WAVES * AT_KT * AT_ROW * sizeof(uint16_t);
+  const unsigned grid = (unsigned)(rows * n_split);
+  if (a.H == 64)
+    attn_bf16_kernel<2><<<grid, 256, lds, st>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,
+        a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,
+        n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+  else
+    attn_bf16_kernel<1><<<grid, 256, lds, st>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,
+        a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,
+        n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+  if (n_split > 1)
+    combine_kernel<CSA_DT_BF16><<<rows, 256, 0, st>>>(part_o, part_ml, n_split, a.H, a.D, a.out,
+                                                      a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace csa_host

@@ -1,0 +1,270 @@
+// Gated overlapping compressor for gfx950.
+//
+// Two launches (migration notes section 3.2: linear_wkv + linear_wgate, then
+// a softmax over the overlapping window; DS-V4 analysis section 1.3):
+//  1. proj: PG[s][row][c] = sum_{k in split s} x[row][k] * W[c][k] for the
+//     stacked weight [W_kv; W_gate] (c < E: value channel, c >= E: gate
+//     logit).  bf16 uses MFMA 32x32x16 tiles staged through LDS; fp32 uses a
+//     plain VALU dot product.  Small-M calls (decode) split K so that enough
+//     workgroups stream the weights.
+//  2. pool: one workgroup per emitted entry: per channel, a softmax of
+//     G + ape over the window tokens (taken from this call's rows or from the
+//     carried state), the weighted sum of P, then the storage rounding (fp32,
+//     bf16 RNE, or e4m3 with a per-row amax/448 scale).  Extra workgroups
+//     write the carried state for the next call.
+#include "common.h"
+
+namespace csa {
+
+// ---------------------------------------------------------------- proj (bf16)
+// Tile 128 x 128 x 32, 256 threads = 4 waves in a 2 x 2 grid of 64 x 64.
+constexpr int PJ_BM = 128, PJ_BN = 128, PJ_BK = 32;
+constexpr int PJ_LDS_STRIDE = PJ_BK + 8;  // bf16 elements per LDS row (pad 16 B)
+
+__global__ void __launch_bounds__(256) proj_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
+    const uint16_t* __restrict__ w_gate, float* __restrict__ pg, int M, int E, int K,
+    int k_per_split) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[PJ_BM * PJ_LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[PJ_BN * PJ_LDS_STRIDE];
+  const int N = 2 * E;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * PJ_BM, n0 = blockIdx.y * PJ_BN;
+  const int split = blockIdx.z;
+  const int kb = split * k_per_split, ke = min(K, kb + k_per_split);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  f32x16 acc[2][2];
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // global -> LDS mapping: each tile row is 32 bf16 = 64 B = 4 chunks of 16 B;
+  // 128 rows x 4 chunks = 512 chunks per operand, 2 per thread.
+  for (int k0 = kb; k0 < ke; k0 += PJ_BK) {
+    for (int c = tid; c < PJ_BM * 4; c += 256) {
+      int r = c >> 2, q = c & 3;
+      u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+      int gm = m0 + r;
+      if (gm < M) va = *(const u32x4*)(x + (size_t)gm * K + k0 + q * 8);
+      int gn = n0 + r;
+      if (gn < N) {
+        const uint16_t* wrow = gn < E ? (w_kv + (size_t)gn * K) : (w_gate + (size_t)(gn - E) * K);
+        vb = *(const u32x4*)(wrow + k0 + q * 8);
+      }
+      *(u32x4*)(As + r * PJ_LDS_STRIDE + q * 8) = va;
+      *(u32x4*)(Bs + r * PJ_LDS_STRIDE + q * 8) = vb;
+    }
+    __syncthreads();
+    // two k-steps of 16; lane holds 8 consecutive k of one row (A) / column (B)
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[2], b[2];
+      for (int i = 0; i < 2; ++i) {
+        int row = wm + i * 32 + (lane & 31);
+        a[i] = *(const bf16x8*)(As + row * PJ_LDS_STRIDE + ks * 16 + (lane >> 5) * 8);
+      }
+      for (int j = 0; j < 2; ++j) {
+        int col = wn + j * 32 + (lane & 31);
+        b[j] = *(const bf16x8*)(Bs + col * PJ_LDS_STRIDE + ks * 16 + (lane >> 5) * 8);
+      }
+      for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // accumulator layout (32x32): lane holds column (lane & 31), rows
+  // 8 (r / 4) + 4 (lane / 32) + (r % 4)
+  float* out = pg + (size_t)split * M * N;
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) {
+      int col = n0 + wn + j * 32 + (lane & 31);
+      if (col >= N) continue;
+      for (int r = 0; r < 16; ++r) {
+        int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) out[(size_t)row * N + col] = acc[i][j][r];
+      }
+    }
+}
+
+// ---------------------------------------------------------------- proj (fp32)
+__global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__ x,
+                                                       const float* __restrict__ w_kv,
+                                                       const float* __restrict__ w_gate,
+                                                       float* __restrict__ pg, int M, int E,
+                                                       int K) {
+  const int N = 2 * E;
+  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= (size_t)M * N) return;
+  const int row = (int)(id / N), col = (int)(id % N);
+  const float* w = col < E ? (w_kv + (size_t)col * K) : (w_gate + (size_t)(col - E) * K);
+  const float* xr = x + (size_t)row * K;
+  float s = 0.0f;
+  for (int k = 0; k < K; ++k) s = fmaf(xr[k], w[k], s);
+  pg[id] = s;
+}
+
+// ---------------------------------------------------------------- pool
+// Grid (n_slots + 1, B).  Slot q < n_slots handles entry i_lo(b) + q; the last
+// slot writes state_out.  Each thread owns channels e = tid, tid + 256, ...
+template <int OUT_DT>
+__global__ void __launch_bounds__(256) pool_kernel(
+    const float* __restrict__ pg, int n_split, const int64_t* __restrict__ pos0, int B, int L,
+    int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
+    float* __restrict__ state_out, void* __restrict__ out, float* __restrict__ out_scale,
+    int Nc_cap, int n_slots) {
+  const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
+  const int ns = (1 + overlap) * m - 1;
+  const int64_t p0 = pos0[b];
+  const size_t M = (size_t)B * L, N = 2 * (size_t)E;
+  const size_t split_stride = M * N;
+
+  // P (c = 0) or G (c = 1) of token at absolute position j, channel e; the
+  // caller guarantees pos0 - ns <= j < pos0 + L.
+  auto fetch = [&](int64_t j, int c, int e, bool& present) -> float {
+    present = true;
+    if (j < 0) { present = false; return 0.0f; }
+    if (j >= p0) {
+      size_t off = ((size_t)b * L + (size_t)(j - p0)) * N + (size_t)c * E + e;
+      float v = 0.0f;
+      for (int s = 0; s < n_split; ++s) v += pg[off + s * split_stride];
+      return v;
+    }
+    if (!state_in) { present = false; return 0.0f; }
+    int slot = (int)(j - (p0 - ns));
+    float v = state_in[(((size_t)b * ns + slot) * 2 + c) * E + e];
+    if (c == 1 && v == -INFINITY) present = false;
+    return v;
+  };
+
+  if (q == n_slots) {  // carried state for the next call
+    if (!state_out) return;
+    for (int idx = tid; idx < ns * E; idx += blockDim.x) {
+      int slot = idx / E, e = idx % E;
+      int64_t j = p0 + L - ns + slot;
+      bool pr1, pr2;
+      float pv = fetch(j, 0, e, pr1);
+      float gv = fetch(j, 1, e, pr2);
+      if (!pr1 || !pr2) { pv = 0.0f; gv = -INFINITY; }
+      state_out[(((size_t)b * ns + slot) * 2 + 0) * E + e] = pv;
+      state_out[(((size_t)b * ns + slot) * 2 + 1) * E + e] = gv;
+    }
+    return;
+  }
+
+  const int64_t i_lo = (p0 + m) / m - 1;  // first entry whose last token is >= p0
+  const int64_t i = i_lo + q;
+  if (i < 0 || i >= Nc_cap) return;
+  const int64_t last = (int64_t)m * (i + 1) - 1;
+  if (last >= p0 + L) return;
+  const int64_t first = (int64_t)m * (i - overlap);
+
+  __shared__ float red[256];
+  float vals[4];  // E <= 1024 supported (checked by the host)
+  float amax = 0.0f;
+  int nv = 0;
+  for (int e = tid; e < E; e += blockDim.x, ++nv) {
+    float mx = -INFINITY;
+    for (int64_t j = first; j <= last; ++j) {
+      bool pr;
+      float g = fetch(j, 1, e, pr);
+      if (!pr) continue;
+      g += ape ? ape[(size_t)(j - first) * E + e] : 0.0f;
+      mx = fmaxf(mx, g);
+    }
+    float den = 0.0f, num = 0.0f;
+    for (int64_t j = first; j <= last; ++j) {
+      bool pr;
+      float g = fetch(j, 1, e, pr);
+      if (!pr) continue;
+      g += ape ? ape[(size_t)(j - first) * E + e] : 0.0f;
+      float p = fetch(j, 0, e, pr);
+      float wgt = __expf(g - mx);
+      den += wgt;
+      num = fmaf(wgt, p, num);
+    }
+    float c = num / den;
+    vals[nv] = c;
+    amax = fmaxf(amax, fabsf(c));
+  }
+  const size_t orow = (size_t)b * Nc_cap + (size_t)i;
+  if (OUT_DT == CSA_DT_F32) {
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) ((float*)out)[orow * E + e] = vals[nv];
+  } else if (OUT_DT == CSA_DT_BF16) {
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv)
+      ((uint16_t*)out)[orow * E + e] = f32_to_bf16(vals[nv]);
+  } else {
+    red[tid] = amax;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+      __syncthreads();
+    }
+    float s = red[0] > 0.0f ? red[0] / 448.0f : 1.0f;
+    if (tid == 0) out_scale[orow] = s;
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv)
+      ((uint8_t*)out)[orow * E + e] = (uint8_t)(f32x2_to_e4m3x2(vals[nv] / s, 0.0f) & 0xff);
+  }
+}
+
+}  // namespace csa
+
+namespace csa_host {
+using namespace csa;
+
+static int proj_splits(int M, int E, int K, csa_dtype_t dt) {
+  if (dt != CSA_DT_BF16) return 1;
+  int tiles = ((M + PJ_BM - 1) / PJ_BM) * ((2 * E + PJ_BN - 1) / PJ_BN);
+  int s = 1;
+  // split K while the grid is small and every split keeps >= 64 k
+  while (tiles * s < 256 && K / (2 * s) >= 64 && (K / (2 * s)) % PJ_BK == 0) s *= 2;
+  return s;
+}
+
+size_t compress_ws_bytes(int B, int L, int d_model, int E, int m, int overlap,
+                         csa_dtype_t in_dt) {
+  (void)m;
+  (void)overlap;
+  int M = B * L;
+  int s = proj_splits(M, E, d_model, in_dt);
+  return (size_t)s * M * 2 * E * sizeof(float);
+}
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
+  const int M = a.B * a.L, K = a.d_model, E = a.E;
+  const int splits = proj_splits(M, E, K, a.in_dt);
+  float* pg = (float*)a.ws;
+  if (a.in_dt == CSA_DT_BF16) {
+    dim3 grid((M + PJ_BM - 1) / PJ_BM, (2 * E + PJ_BN - 1) / PJ_BN, splits);
+    proj_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t*)a.x, (const uint16_t*)a.w_kv,
+                                           (const uint16_t*)a.w_gate, pg, M, E, K, K / splits);
+  } else {
+    size_t n = (size_t)M * 2 * E;
+    proj_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
+        (const float*)a.x, (const float*)a.w_kv, (const float*)a.w_gate, pg, M, E, K);
+  }
+  const int n_slots = (a.L + a.m - 1) / a.m + 1;
+  dim3 pgrid(n_slots + 1, a.B);
+  switch (a.out_dt) {
+    case CSA_DT_F32:
+      pool_kernel<CSA_DT_F32><<<pgrid, 256, 0, st>>>(pg, splits, a.pos0, a.B, a.L, E, a.m,
+                                                      a.overlap, a.ape, a.state_in, a.state_out,
+                                                      a.out, a.out_scale, a.Nc_cap, n_slots);
+      break;
+    case CSA_DT_BF16:
+      pool_kernel<CSA_DT_BF16><<<pgrid, 256, 0, st>>>(pg, splits, a.pos0, a.B, a.L, E, a.m,
+                                                       a.overlap, a.ape, a.state_in, a.state_out,
+                                                       a.out, a.out_scale, a.Nc_cap, n_slots);
+      break;
+    default:
+      pool_kernel<CSA_DT_FP8E4M3><<<pgrid, 256, 0, st>>>(
+          pg, splits, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,
+          a.out_scale, a.Nc_cap, n_slots);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa_host

@@ -1,0 +1,792 @@
+// Lightning Indexer scores and per-row top-k for gfx950.
+//
+// Score (DS-V4 analysis section 1.2; article section 3.2, here with the
+// multi-head ReLU form of the DeepSeek lightning indexer):
+//     s(t, j) = sum_h w[t, h] ReLU(sq[t, h] sk[j] q[t, h] . k[j])
+// for visible entries j < n_vis(t).  Scores go to an fp32 workspace row.
+//
+// Selection keeps the min(topk, n_vis) best scores under (score desc, index
+// asc) and writes them in ascending index order, -1 padded.  Scores map to
+// order-preserving 32-bit keys.
+//  * short rows (Nc_cap <= kShortMax): one workgroup per row; the keys sit in
+//    LDS, an MSB-first radix select (8-bit digits) finds the k-th key, and an
+//    ordered compaction writes the selected indices, taking equal keys in
+//    index order.
+//  * long rows: the score kernel also builds a per-row histogram of the top
+//    11 key bits; "collect" workgroups (one per 2048-entry chunk) find the
+//    threshold bin, and write, in index order, the chunk's entries above it
+//    (certainly selected) and inside it (candidates); "finalize" (one
+//    workgroup per row) picks the missing entries among the candidates by an
+//    exact radix select on (key, -index) and merges the per-chunk lists into
+//    the ascending output.
+#include <algorithm>
+
+#include "common.h"
+
+namespace csa {
+
+constexpr int kHistBins = 2048, kHistShift = 21;
+constexpr int kShortMax = 8192;
+constexpr int kChunk = 2048;
+constexpr int kFinalCandLds = 8192;  // candidates held in LDS by finalize
+constexpr int kMaxChunks = 1024;     // Nc_cap <= kMaxChunks * kChunk
+
+__device__ __forceinline__ void hist_flush(const uint32_t* lhist, uint32_t* ghist) {
+  for (int bin = threadIdx.x; bin < kHistBins; bin += blockDim.x) {
+    uint32_t c = lhist[bin];
+    if (c) atomicAdd(ghist + bin, c);
+  }
+}
+
+// ---------------------------------------------------------------- scores: fp32
+// One thread per (row, entry); any H_I, d_I.  Grid (ceil(Nc_cap / 256), rows).
+template <bool HIST>
+__global__ void __launch_bounds__(256) score_f32_kernel(
+    const float* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const float* __restrict__ k_idx, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, int T, int H_I, int d_I, int Nc_cap, int m,
+    float* __restrict__ scores, uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+  const int row = blockIdx.y, b = row / T, t = row % T;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  if (HIST) {
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lhist[i] = 0;
+    __syncthreads();
+  }
+  if (j < nv) {
+    const float* qr = q_idx + (size_t)row * H_I * d_I;
+    const float* kr = k_idx + ((size_t)b * Nc_cap + j) * d_I;
+    float s = 0.0f;
+    for (int h = 0; h < H_I; ++h) {
+      float dot = 0.0f;
+      for (int e = 0; e < d_I; ++e) dot = fmaf(qr[h * d_I + e], kr[e], dot);
+      s = fmaf(w_idx[(size_t)row * H_I + h], fmaxf(dot, 0.0f), s);
+    }
+    scores[(size_t)row * Nc_cap + j] = s;
+    if (HIST) atomicAdd(&lhist[score_key(s) >> kHistShift], 1u);
+  }
+  if (HIST) {
+    __syncthreads();
+    hist_flush(lhist, ghist + (size_t)row * kHistBins);
+  }
+}
+
+// ---------------------------------------------------------------- scores: bf16
+// H_I = 16, d_I = 64.  A workgroup (4 waves) owns 16 consecutive query rows of
+// one sequence (4 per wave: two 32-row MFMA tiles of 2 rows x 16 heads) and a
+// chunk of entries; 64-entry key tiles are staged in LDS for all waves.
+constexpr int SB_ROWS = 16, SB_KT = 64, SB_KSTRIDE = 64 + 8;  // bf16 per LDS key row
+
+template <bool HIST>
+__global__ void __launch_bounds__(256) score_bf16_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int key_chunk,
+    float* __restrict__ scores, uint32_t* __restrict__ ghist) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[SB_KT * SB_KSTRIDE];
+  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+  const int b = blockIdx.z, t0 = blockIdx.x * SB_ROWS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t p0 = q_pos[b];
+  const int ncb = n_cmp[b];
+  const int jb = blockIdx.y * key_chunk;
+  // entries this workgroup must score: up to the largest n_vis of its rows
+  const int t_last = min(T - 1, t0 + SB_ROWS - 1);
+  const int nv_max = n_visible(p0 + t_last, ncb, m, Nc_cap);
+  const int je = min(nv_max, jb + key_chunk);
+
+  if (HIST) {
+    for (int i = tid; i < kHistBins; i += blockDim.x) lhist[i] = 0;
+  }
+  // A operands: rows (token, head) -> lane row (lane & 31) of tile mt:
+  // token = wave*4 + mt*2 + (lane&31)/16, head = lane & 15; k-step s covers
+  // dims 16 s + 8 (lane / 32) .. + 8.
+  bf16x8 a[2][4];
+  int trow[2];
+  for (int mt = 0; mt < 2; ++mt) {
+    int tt = t0 + wave * 4 + mt * 2 + ((lane & 31) >> 4);
+    trow[mt] = tt;
+    int h = lane & 15;
+    for (int s = 0; s < 4; ++s) {
+      if (tt < T) {
+        a[mt][s] = *(const bf16x8*)(q_idx + (((size_t)b * T + tt) * 16 + h) * 64 + 16 * s +
+                                    8 * (lane >> 5));
+      } else {
+        for (int e = 0; e < 8; ++e) a[mt][s][e] = (__bf16)0.0f;
+      }
+    }
+  }
+  // head weights for the accumulator rows: tile mt, register r -> token
+  // wave*4 + mt*2 + r/8, head 8 ((r%8)/4) + 4 (lane/32) + r%4
+  float wv[2][16];
+  int nvis[2][2];
+  for (int mt = 0; mt < 2; ++mt) {
+    for (int r = 0; r < 16; ++r) {
+      int tt = t0 + wave * 4 + mt * 2 + (r >> 3);
+      int h = 8 * ((r & 7) >> 2) + 4 * (lane >> 5) + (r & 3);
+      wv[mt][r] = tt < T ? w_idx[((size_t)b * T + tt) * 16 + h] : 0.0f;
+    }
+    for (int u = 0; u < 2; ++u) {
+      int tt = t0 + wave * 4 + mt * 2 + u;
+      nvis[mt][u] = tt < T ? n_visible(p0 + tt, ncb, m, Nc_cap) : 0;
+    }
+  }
+  __syncthreads();
+
+  for (int j0 = jb; j0 < je; j0 += SB_KT) {
+    // stage 64 keys x 128 B: 512 chunks of 16 B, 2 per thread
+    for (int c = tid; c < SB_KT * 8; c += 256) {
+      int r = c >> 3, q8 = c & 7;
+      u32x4 v = {0, 0, 0, 0};
+      if (j0 + r < je) v = *(const u32x4*)(k_idx + ((size_t)b * Nc_cap + j0 + r) * 64 + q8 * 8);
+      *(u32x4*)(Ks + r * SB_KSTRIDE + q8 * 8) = v;
+    }
+    __syncthreads();
+    for (int nt = 0; nt < 2; ++nt) {
+      bf16x8 bk[4];
+      for (int s = 0; s < 4; ++s)
+        bk[s] = *(const bf16x8*)(Ks + (nt * 32 + (lane & 31)) * SB_KSTRIDE + 16 * s + 8 * (lane >> 5));
+      const int j = j0 + nt * 32 + (lane & 31);
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16 acc;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        for (int s = 0; s < 4; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][s], bk[s], acc, 0, 0, 0);
+        float s0 = 0.0f, s1 = 0.0f;
+        for (int r = 0; r < 8; ++r) s0 = fmaf(wv[mt][r], fmaxf(acc[r], 0.0f), s0);
+        for (int r = 8; r < 16; ++r) s1 = fmaf(wv[mt][r], fmaxf(acc[r], 0.0f), s1);
+        s0 += __shfl_xor(s0, 32, 64);
+        s1 += __shfl_xor(s1, 32, 64);
+        const int u = lane >> 5;  // lanes < 32 write token 0 of the pair, others token 1
+        const float sc = u ? s1 : s0;
+        const int tt = trow[mt] - ((lane & 31) >> 4) + u;
+        if (tt < T && j < nvis[mt][u]) {
+          scores[((size_t)b * T + tt) * Nc_cap + j] = sc;
+          if (HIST) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (HIST) {
+    // one histogram per query row: flush each row's counts (rows of this
+    // workgroup share the LDS histogram only when T == 1)
+    __syncthreads();
+    hist_flush(lhist, ghist + ((size_t)b * T + t0) * kHistBins);
+  }
+}
+
+// ---------------------------------------------------------------- scores: fp8
+// H_I = 16, d_I = 64, e4m3 codes with positive row scales.  One query row per
+// workgroup, a chunk of kChunk entries split over 4 waves; each 16-entry group
+// is two 16x16x32 fp8 MFMAs (heads x entries).  Lane l loads 16 contiguous
+// bytes of entry (l % 16) at byte offset 16 (l / 16); the first 8 bytes feed
+// the first MFMA and the next 8 the second (the query uses the same k order).
+constexpr int SF_UNROLL = 8;
+
+template <bool HIST>
+__global__ void __launch_bounds__(256) score_fp8_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ w_idx, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, float* __restrict__ scores,
+    uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+  const int row = blockIdx.y, b = row / T, t = row % T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  const int jb = blockIdx.x * kChunk;
+  if (HIST) {
+    for (int i = tid; i < kHistBins; i += blockDim.x) lhist[i] = 0;
+    __syncthreads();
+  }
+  const int je = min(nv, jb + kChunk);
+  if (jb < je) {
+    const int h = lane & 15, g = lane >> 4;
+    const u32x4 qv = *(const u32x4*)(q_idx + ((size_t)row * 16 + h) * 64 + 16 * g);
+    const long qa0 = (long)qv[0] | ((long)qv[1] << 32);
+    const long qa1 = (long)qv[2] | ((long)qv[3] << 32);
+    float wq[4];
+    for (int i = 0; i < 4; ++i) {
+      int hh = 4 * g + i;
+      wq[i] = w_idx[(size_t)row * 16 + hh] * q_scale[(size_t)row * 16 + hh];
+    }
+    const uint8_t* kb = k_idx + (size_t)b * Nc_cap * 64;
+    const float* ks = k_scale + (size_t)b * Nc_cap;
+    float* srow = scores + (size_t)row * Nc_cap;
+    // this wave's entries: [wb, we) in 16-entry groups
+    const int per_wave = kChunk / 4;
+    const int wb = jb + wave * per_wave;
+    const int we = min(je, wb + per_wave);
+    for (int j0 = wb; j0 < we; j0 += 16 * SF_UNROLL) {
+      u32x4 kv[SF_UNROLL];
+      float ksc[SF_UNROLL];
+      for (int u = 0; u < SF_UNROLL; ++u) {
+        int j = j0 + 16 * u + (lane & 15);
+        if (j < we) {
+          kv[u] = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)j * 64 + 16 * g));
+          ksc[u] = ks[j];
+        } else {
+          kv[u] = u32x4{0, 0, 0, 0};
+          ksc[u] = 0.0f;
+        }
+      }
+      float res[SF_UNROLL];
+      for (int u = 0; u < SF_UNROLL; ++u) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        long kb0 = (long)kv[u][0] | ((long)kv[u][1] << 32);
+        long kb1 = (long)kv[u][2] | ((long)kv[u][3] << 32);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa0, kb0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa1, kb1, acc, 0, 0, 0);
+        // acc[i]: head 4 (lane / 16) + i, entry lane % 16
+        float p = 0.0f;
+        for (int i = 0; i < 4; ++i) p = fmaf(wq[i], fmaxf(acc[i], 0.0f), p);
+        p += __shfl_xor(p, 16, 64);
+        p += __shfl_xor(p, 32, 64);
+        res[u] = p * ksc[u];
+      }
+      // lane l writes entry j0 + l (group l / 16) for each half of the unroll
+      for (int half = 0; half < SF_UNROLL / 4; ++half) {
+        float v = res[half * 4 + 0];
+        const int gsel = lane >> 4;
+        v = gsel == 1 ? res[half * 4 + 1] : v;
+        v = gsel == 2 ? res[half * 4 + 2] : v;
+        v = gsel == 3 ? res[half * 4 + 3] : v;
+        int j = j0 + 64 * half + lane;
+        if (j < we) {
+          srow[j] = v;
+          if (HIST) atomicAdd(&lhist[score_key(v) >> kHistShift], 1u);
+        }
+      }
+    }
+  }
+  if (HIST) {
+    __syncthreads();
+    hist_flush(lhist, ghist + (size_t)row * kHistBins);
+  }
+}
+
+// ---------------------------------------------------------------- block scans
+// Exclusive prefix sum over blockDim.x (= 256) values; returns the total.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) base += sh[w];
+    tot += sh[w];
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+// Radix select over `n` keys in LDS: finds the prefix/mask pair such that the
+// selected set is {x : (x & mask) >= prefix} when `all_eq` is set, or, when
+// the full key width got resolved, {x > prefix} plus the first `remaining`
+// keys equal to prefix.  need >= 1 and need <= n.  Uses hist[256] scratch.
+struct RadixResult {
+  uint32_t prefix, mask, remaining;
+  bool all_eq;
+};
+
+__device__ RadixResult radix_select_u32(const uint32_t* keys, int n, uint32_t need,
+                                        uint32_t* hist, uint32_t* sh) {
+  RadixResult r{0u, 0u, need, false};
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      uint32_t x = keys[i];
+      if ((x & r.mask) == r.prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // digit d with cum_above(d) < remaining <= cum_above(d) + hist[d]
+    if (threadIdx.x == 0) {
+      uint32_t cum = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (cum + hist[d] >= r.remaining) break;
+        cum += hist[d];
+      }
+      sh[0] = (uint32_t)d;
+      sh[1] = cum;
+      sh[2] = hist[d];
+    }
+    __syncthreads();
+    uint32_t d = sh[0], cum = sh[1], cnt = sh[2];
+    __syncthreads();
+    r.remaining -= cum;
+    r.prefix |= d << shift;
+    r.mask |= 255u << shift;
+    if (cnt == r.remaining) {
+      r.all_eq = true;
+      break;
+    }
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- short rows
+// One workgroup (256 threads) per row; Nc_cap <= kShortMax.
+__global__ void __launch_bounds__(256) select_short_kernel(
+    const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  __shared__ uint32_t keys[kShortMax];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[8];
+  const int row = blockIdx.x, b = row / T, t = row % T;
+  const int tid = threadIdx.x;
+  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  const float* srow = scores + (size_t)row * Nc_cap;
+  int32_t* orow = idx_out + (size_t)row * topk;
+  float* sorow = score_out ? score_out + (size_t)row * topk : nullptr;
+  const int nsel = min(topk, nv);
+  // pad
+  for (int k = nsel + tid; k < topk; k += blockDim.x) {
+    orow[k] = -1;
+    if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
+  }
+  if (nsel == 0) return;
+  if (nsel == nv) {  // everything visible is selected
+    for (int j = tid; j < nv; j += blockDim.x) {
+      orow[j] = j;
+      if (sorow) sorow[j] = srow[j];
+    }
+    return;
+  }
+  for (int j = tid; j < nv; j += blockDim.x) keys[j] = score_key(srow[j]);
+  __syncthreads();
+  RadixResult rr = radix_select_u32(keys, nv, (uint32_t)nsel, hist, sh);
+  // ordered compaction: thread owns indices [c0, c1)
+  const int per = (nv + blockDim.x - 1) / blockDim.x;
+  const int c0 = min(nv, tid * per), c1 = min(nv, c0 + per);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int j = c0; j < c1; ++j) {
+    uint32_t x = keys[j] & rr.mask;
+    if (x > rr.prefix) ++n_gt;
+    else if (x == rr.prefix) ++n_eq;
+  }
+  uint32_t tot;
+  uint32_t eq_base = block_excl_scan(n_eq, sh, tot);
+  // equal keys taken in index order: all of them if all_eq, else the first
+  // `remaining`
+  uint32_t take_eq = 0;
+  {
+    uint32_t lim = rr.all_eq ? 0xffffffffu : rr.remaining;
+    if (eq_base < lim) take_eq = min(n_eq, lim - eq_base);
+  }
+  uint32_t out_base = block_excl_scan(n_gt + take_eq, sh, tot);
+  uint32_t taken = 0, pos = out_base;
+  for (int j = c0; j < c1; ++j) {
+    uint32_t x = keys[j] & rr.mask;
+    bool sel = x > rr.prefix;
+    if (!sel && x == rr.prefix && taken < take_eq) {
+      sel = true;
+      ++taken;
+    }
+    if (sel) {
+      orow[pos] = j;
+      if (sorow) sorow[pos] = srow[j];
+      ++pos;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- long rows
+// Threshold bin from the row histogram: the bin where the count from the top
+// reaches `need`; returns the count strictly above it.
+__device__ void threshold_bin(const uint32_t* __restrict__ ghist_row, uint32_t need,
+                              uint32_t* sh, uint32_t& bin, uint32_t& above) {
+  // each thread sums 8 consecutive bins (from the top)
+  const int tid = threadIdx.x;
+  uint32_t c[8], s = 0;
+  for (int i = 0; i < 8; ++i) {
+    c[i] = ghist_row[kHistBins - 1 - (tid * 8 + i)];
+    s += c[i];
+  }
+  uint32_t tot;
+  uint32_t base = block_excl_scan(s, sh, tot);
+  __syncthreads();
+  if (base < need && base + s >= need) {
+    uint32_t cum = base;
+    for (int i = 0; i < 8; ++i) {
+      if (cum + c[i] >= need) {
+        sh[4] = (uint32_t)(kHistBins - 1 - (tid * 8 + i));
+        sh[5] = cum;
+        break;
+      }
+      cum += c[i];
+    }
+  }
+  __syncthreads();
+  bin = sh[4];
+  above = sh[5];
+  __syncthreads();
+}
+
+// Grid (n_chunks, rows).  Writes per chunk, in index order, the entries above
+// the threshold bin (def) and inside it (cand), with their counts.
+__global__ void __launch_bounds__(256) collect_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ ghist,
+    const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp, int T, int Nc_cap,
+    int m, int topk, int n_chunks, uint32_t* __restrict__ def_cnt, uint32_t* __restrict__ cand_cnt,
+    uint32_t* __restrict__ def_list, uint32_t* __restrict__ cand_list) {
+  __shared__ uint32_t sh[8];
+  const int chunk = blockIdx.x, row = blockIdx.y, b = row / T, t = row % T;
+  const int tid = threadIdx.x;
+  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  const int nsel = min(topk, nv);
+  const size_t cidx = (size_t)row * n_chunks + chunk;
+  const int j0 = chunk * kChunk, j1 = min(nv, j0 + kChunk);
+  uint32_t bin = 0, above = 0;
+  bool all = nsel == nv;
+  if (!all && nsel > 0) threshold_bin(ghist + (size_t)row * kHistBins, (uint32_t)nsel, sh, bin, above);
+  // 8 entries per thread, contiguous
+  const float* srow = scores + (size_t)row * Nc_cap;
+  uint32_t nd = 0, nc = 0;
+  uint8_t kind[8];
+  for (int i = 0; i < 8; ++i) {
+    int j = j0 + tid * 8 + i;
+    uint8_t k = 0;
+    if (j < j1 && nsel > 0) {
+      if (all) k = 1;
+      else {
+        uint32_t kb = score_key(srow[j]) >> kHistShift;
+        k = kb > bin ? 1 : (kb == bin ? 2 : 0);
+      }
+    }
+    kind[i] = k;
+    nd += k == 1;
+    nc += k == 2;
+  }
+  uint32_t td, tc;
+  uint32_t db = block_excl_scan(nd, sh, td);
+  uint32_t cb = block_excl_scan(nc, sh, tc);
+  uint32_t* dl = def_list + cidx * kChunk;
+  uint32_t* cl = cand_list + cidx * kChunk;
+  for (int i = 0; i < 8; ++i) {
+    int j = j0 + tid * 8 + i;
+    if (kind[i] == 1) dl[db++] = (uint32_t)j;
+    else if (kind[i] == 2) cl[cb++] = (uint32_t)j;
+  }
+  if (tid == 0) {
+    def_cnt[cidx] = td;
+    cand_cnt[cidx] = tc;
+  }
+}
+
+// One workgroup per row.  Chooses `need` candidates by (key desc, index asc)
+// and merges the per-chunk lists into the ascending output row.  Candidate
+// lists are ascending within a chunk and chunks are in index order, so among
+// candidates with the threshold key the lowest indices are simply the first
+// ones met in chunk order.
+__device__ __forceinline__ uint32_t cand_key(const float* srow, uint32_t j) {
+  return score_key(srow[j]) & ((1u << kHistShift) - 1u);
+}
+
+__global__ void __launch_bounds__(256) finalize_kernel(
+    const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk, int n_chunks,
+    const uint32_t* __restrict__ def_cnt, const uint32_t* __restrict__ cand_cnt,
+    const uint32_t* __restrict__ def_list, const uint32_t* __restrict__ cand_list,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  __shared__ uint32_t ckey[kFinalCandLds];  // low key bits of the candidates
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[8];
+  __shared__ uint32_t coff[kMaxChunks], doff[kMaxChunks], soff[kMaxChunks], eqoff[kMaxChunks];
+  __shared__ uint32_t ngt[kMaxChunks], neq[kMaxChunks];
+  const int row = blockIdx.x, b = row / T, t = row % T;
+  const int tid = threadIdx.x;
+  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  const int nsel = min(topk, nv);
+  const float* srow = scores + (size_t)row * Nc_cap;
+  int32_t* orow = idx_out + (size_t)row * topk;
+  float* sorow = score_out ? score_out + (size_t)row * topk : nullptr;
+  for (int k = nsel + tid; k < topk; k += blockDim.x) {
+    orow[k] = -1;
+    if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
+  }
+  if (nsel == 0) return;
+  const uint32_t* dc = def_cnt + (size_t)row * n_chunks;
+  const uint32_t* cc = cand_cnt + (size_t)row * n_chunks;
+  const uint32_t* dlists = def_list + (size_t)row * n_chunks * kChunk;
+  const uint32_t* clists = cand_list + (size_t)row * n_chunks * kChunk;
+
+  uint32_t tot_c = 0, tot_d = 0;
+  for (int base = 0; base < n_chunks; base += blockDim.x) {
+    int c = base + tid;
+    uint32_t vc = c < n_chunks ? cc[c] : 0, vd = c < n_chunks ? dc[c] : 0;
+    uint32_t tc, td;
+    uint32_t oc = block_excl_scan(vc, sh, tc);
+    uint32_t od = block_excl_scan(vd, sh, td);
+    if (c < n_chunks) {
+      coff[c] = tot_c + oc;
+      doff[c] = tot_d + od;
+    }
+    tot_c += tc;
+    tot_d += td;
+  }
+  __syncthreads();
+  const uint32_t need = (uint32_t)nsel - tot_d;  // candidates still to take (<= tot_c)
+
+  // threshold on the low key bits of the candidates
+  RadixResult rk{0u, 0u, need, true};
+  if (need > 0 && need < tot_c) {
+    if (tot_c <= (uint32_t)kFinalCandLds) {
+      for (int c = 0; c < n_chunks; ++c)
+        for (uint32_t i = tid; i < cc[c]; i += blockDim.x)
+          ckey[coff[c] + i] = cand_key(srow, clists[(size_t)c * kChunk + i]);
+      __syncthreads();
+      rk = radix_select_u32(ckey, (int)tot_c, need, hist, sh);
+    } else {
+      // more candidates than LDS holds (heavy ties): the same select with the
+      // keys re-read from the score row on every pass
+      rk = RadixResult{0u, 0u, need, false};
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+        for (int c = 0; c < n_chunks; ++c)
+          for (uint32_t i = tid; i < cc[c]; i += blockDim.x) {
+            uint32_t x = cand_key(srow, clists[(size_t)c * kChunk + i]);
+            if ((x & rk.mask) == rk.prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+          }
+        __syncthreads();
+        if (tid == 0) {
+          uint32_t cum = 0;
+          int d = 255;
+          for (; d > 0; --d) {
+            if (cum + hist[d] >= rk.remaining) break;
+            cum += hist[d];
+          }
+          sh[0] = d;
+          sh[1] = cum;
+          sh[2] = hist[d];
+        }
+        __syncthreads();
+        uint32_t d = sh[0], cum = sh[1], cnt = sh[2];
+        __syncthreads();
+        rk.remaining -= cum;
+        rk.prefix |= d << shift;
+        rk.mask |= 255u << shift;
+        if (cnt == rk.remaining) {
+          rk.all_eq = true;
+          break;
+        }
+      }
+    }
+  }
+  const bool take_all = need >= tot_c;
+  // per chunk: candidates above the threshold and equal to it
+  for (int c = tid; c < n_chunks; c += blockDim.x) {
+    uint32_t g = 0, e = 0;
+    if (need > 0 && !take_all) {
+      const uint32_t* cl = clists + (size_t)c * kChunk;
+      for (uint32_t i = 0; i < cc[c]; ++i) {
+        uint32_t x = cand_key(srow, cl[i]) & rk.mask;
+        g += x > rk.prefix;
+        e += x == rk.prefix;
+      }
+    }
+    ngt[c] = g;
+    neq[c] = e;
+  }
+  __syncthreads();
+  // equal-key candidates are taken in index order: chunk offsets of them
+  uint32_t run_e = 0;
+  for (int base = 0; base < n_chunks; base += blockDim.x) {
+    int c = base + tid;
+    uint32_t te;
+    uint32_t o = block_excl_scan(c < n_chunks ? neq[c] : 0u, sh, te);
+    if (c < n_chunks) eqoff[c] = run_e + o;
+    run_e += te;
+  }
+  __syncthreads();
+  const uint32_t eq_lim = rk.all_eq ? 0xffffffffu : rk.remaining;
+  uint32_t run_s = 0;
+  for (int base = 0; base < n_chunks; base += blockDim.x) {
+    int c = base + tid;
+    uint32_t cnt = 0;
+    if (c < n_chunks) {
+      if (need == 0) cnt = 0;
+      else if (take_all) cnt = cc[c];
+      else {
+        uint32_t te = eqoff[c] < eq_lim ? min(neq[c], eq_lim - eqoff[c]) : 0u;
+        cnt = ngt[c] + te;
+        neq[c] = te;  // now: equal candidates taken from this chunk
+      }
+    }
+    uint32_t tt;
+    uint32_t o = block_excl_scan(cnt, sh, tt);
+    if (c < n_chunks) soff[c] = run_s + o;
+    run_s += tt;
+  }
+  __syncthreads();
+  // merge (thread per chunk): definite and chosen candidates, both ascending
+  for (int c = tid; c < n_chunks; c += blockDim.x) {
+    const uint32_t* dl = dlists + (size_t)c * kChunk;
+    const uint32_t* cl = clists + (size_t)c * kChunk;
+    const uint32_t nd = dc[c], ncn = cc[c];
+    const uint32_t eq_take = take_all ? 0u : neq[c];
+    uint32_t pos = doff[c] + soff[c];
+    uint32_t i = 0, k = 0, eq_seen = 0;
+    auto next_cand = [&]() -> uint32_t {
+      while (need > 0 && k < ncn) {
+        uint32_t j = cl[k];
+        if (take_all) return j;
+        uint32_t x = cand_key(srow, j) & rk.mask;
+        if (x > rk.prefix) return j;
+        if (x == rk.prefix) {
+          if (eq_seen < eq_take) {
+            ++eq_seen;
+            return j;
+          }
+        }
+        ++k;
+      }
+      return 0xffffffffu;
+    };
+    uint32_t cj = next_cand();
+    while (i < nd || cj != 0xffffffffu) {
+      uint32_t dj = i < nd ? dl[i] : 0xffffffffu;
+      uint32_t j;
+      if (dj < cj) {
+        j = dj;
+        ++i;
+      } else {
+        j = cj;
+        ++k;
+        cj = next_cand();
+      }
+      orow[pos] = (int32_t)j;
+      if (sorow) sorow[pos] = srow[j];
+      ++pos;
+    }
+  }
+}
+
+__global__ void zero_u32_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace csa
+
+namespace csa_host {
+using namespace csa;
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct IdxLayout {
+  bool long_rows;
+  int n_chunks;
+  size_t scores, hist, def_cnt, cand_cnt, def_list, cand_list, total;
+};
+
+static IdxLayout idx_layout(int B, int T, int Nc_cap) {
+  IdxLayout L{};
+  const size_t rows = (size_t)B * T;
+  L.long_rows = Nc_cap > kShortMax;
+  L.n_chunks = (Nc_cap + kChunk - 1) / kChunk;
+  size_t off = 0;
+  L.scores = off;
+  off += align256(rows * (size_t)Nc_cap * 4);
+  if (L.long_rows) {
+    L.hist = off;
+    off += align256(rows * kHistBins * 4);
+    L.def_cnt = off;
+    off += align256(rows * L.n_chunks * 4);
+    L.cand_cnt = off;
+    off += align256(rows * L.n_chunks * 4);
+    L.def_list = off;
+    off += align256(rows * L.n_chunks * (size_t)kChunk * 4);
+    L.cand_list = off;
+    off += align256(rows * L.n_chunks * (size_t)kChunk * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+size_t indexer_ws_bytes(int B, int T, int H_I, int d_I, int Nc_cap, int topk, csa_dtype_t dt) {
+  (void)H_I;
+  (void)d_I;
+  (void)topk;
+  (void)dt;
+  return idx_layout(B, T, Nc_cap).total;
+}
+
+hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
+  const IdxLayout L = idx_layout(a.B, a.T, a.Nc_cap);
+  char* ws = (char*)a.ws;
+  float* scores = (float*)(ws + L.scores);
+  uint32_t* hist = L.long_rows ? (uint32_t*)(ws + L.hist) : nullptr;
+  const int rows = a.B * a.T;
+  if (L.long_rows) {
+    size_t n = (size_t)rows * kHistBins;
+    zero_u32_kernel<<<(unsigned)std::min<size_t>((n + 255) / 256, 1024), 256, 0, st>>>(hist, n);
+  }
+  if (a.Nc_cap == 0) {
+    // no entry exists: every output row is padding
+  } else if (a.dt == CSA_DT_F32) {
+    dim3 g((a.Nc_cap + 255) / 256, rows);
+    if (L.long_rows)
+      score_f32_kernel<true><<<g, 256, 0, st>>>((const float*)a.q_idx, a.w_idx,
+                                                (const float*)a.k_idx, a.q_pos, a.n_cmp, a.T,
+                                                a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist);
+    else
+      score_f32_kernel<false><<<g, 256, 0, st>>>((const float*)a.q_idx, a.w_idx,
+                                                 (const float*)a.k_idx, a.q_pos, a.n_cmp, a.T,
+                                                 a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist);
+  } else if (a.dt == CSA_DT_BF16) {
+    // long rows need one histogram per row: one row per workgroup then
+    const int key_chunk = L.long_rows ? kChunk : a.Nc_cap;
+    dim3 g((a.T + SB_ROWS - 1) / SB_ROWS, (a.Nc_cap + key_chunk - 1) / key_chunk, a.B);
+    if (L.long_rows) {
+      // rows of a workgroup must share a histogram: only T == 1 qualifies
+      if (a.T != 1) return hipErrorNotSupported;
+      score_bf16_kernel<true><<<g, 256, 0, st>>>((const uint16_t*)a.q_idx, a.w_idx,
+                                                 (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,
+                                                 a.Nc_cap, a.m, key_chunk, scores, hist);
+    } else {
+      score_bf16_kernel<false><<<g, 256, 0, st>>>((const uint16_t*)a.q_idx, a.w_idx,
+                                                  (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,
+                                                  a.Nc_cap, a.m, key_chunk, scores, hist);
+    }
+  } else {
+    dim3 g((a.Nc_cap + kChunk - 1) / kChunk, rows);
+    if (L.long_rows)
+      score_fp8_kernel<true><<<g, 256, 0, st>>>((const uint8_t*)a.q_idx, a.q_scale, a.w_idx,
+                                                (const uint8_t*)a.k_idx, a.k_scale, a.q_pos,
+                                                a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist);
+    else
+      score_fp8_kernel<false><<<g, 256, 0, st>>>((const uint8_t*)a.q_idx, a.q_scale, a.w_idx,
+                                                 (const uint8_t*)a.k_idx, a.k_scale, a.q_pos,
+                                                 a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist);
+  }
+  if (!L.long_rows) {
+    select_short_kernel<<<rows, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m,
+                                              a.topk, a.idx_out, a.score_out);
+  } else {
+    uint32_t* dcnt = (uint32_t*)(ws + L.def_cnt);
+    uint32_t* ccnt = (uint32_t*)(ws + L.cand_cnt);
+    uint32_t* dl = (uint32_t*)(ws + L.def_list);
+    uint32_t* cl = (uint32_t*)(ws + L.cand_list);
+    collect_kernel<<<dim3(L.n_chunks, rows), 256, 0, st>>>(scores, hist, a.q_pos, a.n_cmp, a.T,
+                                                           a.Nc_cap, a.m, a.topk, L.n_chunks,
+                                                           dcnt, ccnt, dl, cl);
+    finalize_kernel<<<rows, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m, a.topk,
+                                          L.n_chunks, dcnt, ccnt, dl, cl, a.idx_out, a.score_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa_host

@@ -1,0 +1,177 @@
+"""GPU parity of csa_sparse_attn and hca_dense_attn against the CPU oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_overlapped_amd as csa
+from compressed_sparse_attention_overlapped_amd import inputs as gen
+from oracle import oracle as orc
+from tests.helpers import assert_bf16_close, assert_rows_rel, dev_i32, dev_i64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _n_vis(pos, ncmp, m, cap):
+    return max(0, min(ncmp, (pos + 1) // m, cap))
+
+
+def _rand_idx(d, B, T, topk, n_vis_fn, pad_frac=0.1):
+    nv = torch.tensor([[n_vis_fn(b, t) for t in range(T)] for b in range(B)])
+    return gen.random_index_sets(d, B, T, topk, nv, pad_frac)
+
+
+def _check(out, lse, ref, ref_lse, dt, what):
+    g = out.float().cpu().numpy()
+    if dt == torch.float32:
+        assert_rows_rel(g, ref, 1e-5, what)
+    else:
+        assert_bf16_close(g, ref, what)
+    gl = lse.cpu().numpy()
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(gl), fin), what + " lse finiteness"
+    np.testing.assert_allclose(gl[fin], ref_lse[fin], rtol=1e-4, atol=1e-4)
+
+
+def _sparse(q, kv_cmp, idx, kv_raw, W, q_pos, raw_base, scale=None):
+    out, lse = csa.csa_sparse_attn(q.to(DEV), kv_cmp.to(DEV), idx.to(DEV), kv_raw.to(DEV), W,
+                                   dev_i64(q_pos), dev_i64(raw_base), scale=scale, want_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_sparse_attn_tiny_f32():
+    w = gen.WORKLOADS["csa_prefill_tiny_f32"]
+    d = gen.Draw(31)
+    q = gen.store(d.normal(1, w.T, w.H, w.D), gen.F32)
+    kv_cmp = gen.store(d.normal(1, w.n_cmp, 2 * w.D), gen.F32)
+    kv_raw = gen.store(d.normal(1, w.T, 2 * w.D), gen.F32)
+    idx = _rand_idx(d, 1, w.T, w.topk, lambda b, t: _n_vis(t, w.n_cmp, w.m, w.n_cmp), 0.0)
+    out, lse = _sparse(q, kv_cmp, idx, kv_raw, w.window, [0], [0])
+    ref, rl = orc.sparse_attn(q.numpy(), kv_cmp.numpy(), idx.numpy(), kv_raw.numpy(), w.window,
+                              0, 0)
+    _check(out, lse, ref, rl, torch.float32, "sparse f32 tiny")
+
+
+@pytest.mark.parametrize("H", [64, 32])
+def test_sparse_attn_bf16_ragged(H):
+    d = gen.Draw(32 + H)
+    B, T, D, Nc, R, topk, W = 3, 37, 128, 90, 300, 64, 48
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    q_pos = [0, 200, 330]
+    raw_base = [0, 170, 20]      # sequence 1 misses early window rows (absent)
+    idx = _rand_idx(d, B, T, topk, lambda b, t: _n_vis(q_pos[b] + t, Nc, 4, Nc), 0.2)
+    idx[0, 0] = -1               # q at position 0 with no compressed entry
+    out, lse = _sparse(q, kv_cmp, idx, kv_raw, W, q_pos, raw_base)
+    ref, rl = orc.sparse_attn(gen.host_bits(q), gen.host_bits(kv_cmp), idx.numpy(),
+                              gen.host_bits(kv_raw), W, q_pos, raw_base)
+    _check(out, lse, ref, rl, torch.bfloat16, "sparse bf16 H=%d" % H)
+
+
+def test_sparse_attn_empty_rows_give_zero():
+    d = gen.Draw(33)
+    B, T, H, D = 1, 4, 64, 128
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv = gen.store(d.normal(B, 8, 2 * D), gen.BF16)
+    idx = torch.full((B, T, 16), -1, dtype=torch.int32)
+    out, lse = _sparse(q, kv, idx, kv, 0, [5], [0])
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_sparse_attn_prefill_8k_sampled():
+    w = gen.WORKLOADS["csa_prefill_8k_bf16"]
+    d = gen.Draw(w.seed + 200, DEV)
+    q = gen.store(d.normal(1, w.T, w.H, w.D), gen.BF16)
+    kv_cmp = gen.store(d.normal(1, w.n_cmp, 2 * w.D), gen.BF16)
+    kv_raw = gen.store(d.normal(1, w.T, 2 * w.D), gen.BF16)
+    dc = gen.Draw(w.seed + 201)
+    idx = _rand_idx(dc, 1, w.T, w.topk, lambda b, t: _n_vis(t, w.n_cmp, w.m, w.n_cmp), 0.0)
+    out, lse = _sparse(q, kv_cmp, idx, kv_raw, w.window, [0], [0])
+    kvc, kvr = gen.host_bits(kv_cmp), gen.host_bits(kv_raw)
+    for t in [0, 1, 3, 511, 512, 2047, 4000, 8191]:
+        ref, rl = orc.sparse_attn(gen.host_bits(q[:, t:t + 1]), kvc, idx[:, t:t + 1].numpy(), kvr,
+                                  w.window, [t], [0])
+        _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl, torch.bfloat16, "8k token %d" % t)
+
+
+@pytest.mark.parametrize("name", ["csa_decode_128k_b32", "csa_decode_1m_b8_stream"])
+def test_sparse_attn_decode_split_k(name):
+    w = gen.WORKLOADS[name]
+    d = gen.Draw(w.seed + 300, DEV)
+    B = w.B
+    Nc = 40000                              # entries the indices point into
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * w.D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, w.window, 2 * w.D), gen.BF16)
+    q = gen.store(d.normal(B, 1, w.H, w.D), gen.BF16)
+    dc = gen.Draw(w.seed + 301)
+    idx = _rand_idx(dc, B, 1, w.topk, lambda b, t: Nc, 0.0)
+    q_pos = [w.ctx - 1] * B
+    raw_base = [w.ctx - w.window] * B
+    out, lse = _sparse(q, kv_cmp, idx, kv_raw, w.window, q_pos, raw_base)
+    ref, rl = orc.sparse_attn(gen.host_bits(q), gen.host_bits(kv_cmp), idx.numpy(),
+                              gen.host_bits(kv_raw), w.window, q_pos, raw_base)
+    _check(out, lse, ref, rl, torch.bfloat16, name)
+
+
+def test_hca_bf16_ragged():
+    d = gen.Draw(34)
+    B, T, H, D, m, W = 2, 50, 64, 128, 16, 40
+    Nc = 30
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    R = 200
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    q_pos, n_cmp, raw_base = [0, 420], [Nc, 27], [0, 300]
+    out, lse = csa.hca_dense_attn(q.to(DEV), kv_cmp.to(DEV), kv_raw.to(DEV), m, W, dev_i64(q_pos),
+                                  dev_i32(n_cmp), dev_i64(raw_base), want_lse=True)
+    torch.cuda.synchronize()
+    ref, rl = orc.hca_dense_attn(gen.host_bits(q), gen.host_bits(kv_cmp), gen.host_bits(kv_raw), m,
+                                 W, q_pos, n_cmp, raw_base)
+    _check(out, lse, ref, rl, torch.bfloat16, "hca ragged")
+
+
+def test_hca_1m_chunk_sampled():
+    w = gen.WORKLOADS["hca_prefill_1m_chunk4k"]
+    inp = gen.hca_inputs(w, device=DEV)
+    q0 = w.ctx - w.T
+    raw_base = q0 - w.window + 1
+    out, lse = csa.hca_dense_attn(inp["q"], inp["kv_cmp"], inp["kv_raw"], w.m, w.window,
+                                  dev_i64([q0]), dev_i32([w.n_cmp]), dev_i64([raw_base]),
+                                  want_lse=True)
+    torch.cuda.synchronize()
+    kvc, kvr = gen.host_bits(inp["kv_cmp"]), gen.host_bits(inp["kv_raw"])
+    for t in [0, 1, 127, 2000, 4094, 4095]:
+        ref, rl = orc.hca_dense_attn(gen.host_bits(inp["q"][:, t:t + 1]), kvc, kvr, w.m, w.window,
+                                     [q0 + t], [w.n_cmp], [raw_base])
+        _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl, torch.bfloat16, "hca token %d" % t)
+
+
+def test_csa_with_all_visible_selected_equals_hca():
+    # When every slot of the index list names a visible entry, in order, the
+    # CSA key list is the HCA key list position for position: bitwise equal.
+    # With some slots masked (early rows) the lists tile differently, so the
+    # online-softmax rounding differs: compared to bf16 accuracy there.
+    d = gen.Draw(35)
+    B, T, H, D, m, W, Nc = 1, 30, 64, 128, 4, 16, 20
+    q = gen.store(d.normal(B, T, H, D), gen.BF16).to(DEV)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16).to(DEV)
+    kv_raw = gen.store(d.normal(B, 200, 2 * D), gen.BF16).to(DEV)
+    for q_pos, exact in ((100, True), (50, False)):
+        idx = torch.full((B, T, Nc), -1, dtype=torch.int32)
+        for t in range(T):
+            nv = _n_vis(q_pos + t, Nc, m, Nc)
+            idx[0, t, :nv] = torch.arange(nv)
+        a, la = csa.csa_sparse_attn(q, kv_cmp, idx.to(DEV), kv_raw, W, dev_i64([q_pos]),
+                                    dev_i64([0]), want_lse=True)
+        b, lb = csa.hca_dense_attn(q, kv_cmp, kv_raw, m, W, dev_i64([q_pos]), dev_i32([Nc]),
+                                   dev_i64([0]), want_lse=True)
+        torch.cuda.synchronize()
+        if exact:
+            assert torch.equal(a, b) and torch.equal(la, lb)
+        else:
+            assert_bf16_close(a.float().cpu().numpy(), b.float().cpu().numpy(), "csa vs hca")
+            np.testing.assert_allclose(la.cpu().numpy(), lb.cpu().numpy(), rtol=1e-5, atol=1e-5)

@@ -1,0 +1,165 @@
+"""GPU parity of csa_compress against the CPU oracle (called through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_overlapped_amd as csa
+from compressed_sparse_attention_overlapped_amd import inputs as gen
+from oracle import oracle as orc
+from tests.helpers import assert_bf16_close, assert_rows_rel, dev_i64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(x, w_kv, w_gate, pos0, m, o, Nc_cap, out_dtype, ape=None, state_in=None, want_state=True):
+    B = x.shape[0]
+    E = w_kv.shape[0]
+    out = torch.full((B, Nc_cap, E), float("nan"), device=DEV).to(out_dtype)
+    out_scale = torch.zeros(B, Nc_cap, device=DEV) if out_dtype == torch.float8_e4m3fn else None
+    ns = (1 + o) * m - 1
+    state_out = torch.full((B, ns, 2, E), 7.0, device=DEV) if want_state else None
+    csa.csa_compress(x, w_kv, w_gate, dev_i64(pos0), m, o, out, out_scale=out_scale,
+                     ape=ape, state_in=state_in, state_out=state_out)
+    torch.cuda.synchronize()
+    return out, out_scale, state_out
+
+
+def _oracle(x, w_kv, w_gate, pos0, m, o, Nc_cap, ape=None, state_in=None):
+    return orc.compress(gen.host_bits(x), gen.host_bits(w_kv), gen.host_bits(w_gate), m, o,
+                        np.asarray(pos0), Nc_cap,
+                        ape=None if ape is None else ape.cpu().numpy(),
+                        state_in=None if state_in is None else state_in.cpu().numpy())
+
+
+@pytest.mark.parametrize("E", [128, 32])
+def test_compress_tiny_f32(E):
+    w = gen.WORKLOADS["csa_prefill_tiny_f32"]
+    d = gen.Draw(7 + E)
+    x = gen.store(d.normal(1, w.T, w.d_model), gen.F32)
+    w_kv, w_gate = gen.compressor_weights(d, w.d_model, E, gen.F32)
+    out, _, st = _run(x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), [0], w.m, w.overlap, w.n_cmp,
+                      torch.float32)
+    ref, written, st_ref = _oracle(x, w_kv, w_gate, [0], w.m, w.overlap, w.n_cmp)
+    assert written.all()
+    assert_rows_rel(out.cpu().numpy()[0], ref[0], 1e-5, "compress f32")
+    np.testing.assert_allclose(st.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("out_kind", ["bf16", "fp8", "f32"])
+def test_compress_bf16_ragged_with_ape(out_kind):
+    d = gen.Draw(11)
+    B, L, dm, E, m, o = 3, 61, 256, 64, 4, 1
+    x = gen.store(d.normal(B, L, dm), gen.BF16)
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    ape = d.normal(2 * m, E)
+    pos0 = [0, 5, 130]          # ragged starts; tokens before pos0 absent (no state)
+    Nc = 64
+    odt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "f32": torch.float32}[out_kind]
+    out, osc, st = _run(x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), pos0, m, o, Nc, odt,
+                        ape=ape.to(DEV))
+    ref, written, st_ref = _oracle(x, w_kv, w_gate, pos0, m, o, Nc, ape=ape)
+    if out_kind == "fp8":
+        codes, scales = orc.quant_rows_e4m3(np.nan_to_num(ref))
+        g_codes = gen.host_bits(out)
+        g_sc = osc.cpu().numpy()
+        for b in range(B):
+            for i in np.nonzero(written[b])[0]:
+                np.testing.assert_allclose(g_sc[b, i], scales[b, i], rtol=1e-5)
+                # within one e4m3 step: compare decoded values by code distance
+                gv = np.array([orc.e4m3_decode(c) for c in g_codes[b, i]])
+                rv = np.array([orc.e4m3_decode(c) for c in codes[b, i]])
+                step = np.maximum(np.abs(rv), 2.0 ** -6) * 2.0 ** -3
+                assert (np.abs(gv - rv) <= step + 1e-12).all(), (b, i)
+    else:
+        g = out.float().cpu().numpy()
+        for b in range(B):
+            wr = written[b]
+            assert np.isnan(g[b, ~wr]).all(), "rows not completed must be untouched"
+            if out_kind == "f32":
+                assert_rows_rel(g[b, wr], ref[b, wr], 1e-5, "compress bf16->f32")
+            else:
+                assert_bf16_close(g[b, wr], ref[b, wr], "compress bf16->bf16")
+    np.testing.assert_allclose(st.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=2e-5, atol=2e-5)
+    assert np.array_equal(np.isneginf(st.cpu().numpy()[:, :, 1]), np.isneginf(st_ref[:, :, 1]))
+
+
+@pytest.mark.parametrize("m,o", [(4, 1), (128, 0), (3, 1)])
+def test_compress_chunked_with_state_equals_one_shot(m, o):
+    d = gen.Draw(12 + m)
+    B, S, dm, E = 2, 3 * m + 37, 64, 48
+    x = gen.store(d.normal(B, S, dm), gen.F32)
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.F32)
+    ape = d.normal((1 + o) * m, E)
+    Nc = S // m + 1
+    ref, written, st_ref = _oracle(x, w_kv, w_gate, [0] * B, m, o, Nc, ape=ape)
+    xg, wk, wg, ag = x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), ape.to(DEV)
+    ns = (1 + o) * m - 1
+    out = torch.full((B, Nc, E), float("nan"), device=DEV)
+    st = [torch.zeros(B, ns, 2, E, device=DEV), torch.zeros(B, ns, 2, E, device=DEV)]
+    st_in, p, k = None, 0, 0
+    for L in [1, 5, 1, m + 3, 2, S]:
+        L = min(L, S - p)
+        if L <= 0:
+            break
+        csa.csa_compress(xg[:, p:p + L].contiguous(), wk, wg, dev_i64([p] * B), m, o, out,
+                         ape=ag, state_in=st_in, state_out=st[k])
+        st_in = st[k]
+        k ^= 1
+        p += L
+    assert p == S
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    for b in range(B):
+        assert_rows_rel(g[b, written[b]], ref[b, written[b]], 1e-5, "chunked compress")
+    np.testing.assert_allclose(st_in.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=1e-5, atol=1e-5)
+
+
+def test_compress_decode_step_splits_k():
+    # one token per sequence at 4096-wide input: the projection splits K over
+    # many workgroups; the emitted entry must match the oracle's streaming step
+    w = gen.WORKLOADS["csa_decode_1m_b8_stream"]
+    d = gen.Draw(13)
+    B, dm, E, m, o = 4, w.d_model, 2 * w.D, w.m, w.overlap
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    x_tail = gen.store(d.normal(B, 7, dm), gen.BF16)
+    x_new = gen.store(d.normal(B, 1, dm), gen.BF16)
+    T = 1 << 16                     # position of the new token: T - 1
+    Nc = T // m
+    pos_tail = [T - 8] * B
+    ref1, _, st1 = _oracle(x_tail, w_kv, w_gate, pos_tail, m, o, Nc)
+    ref2, wr2, _ = _oracle(x_new, w_kv, w_gate, [T - 1] * B, m, o, Nc,
+                           state_in=torch.from_numpy(st1))
+    assert wr2[:, Nc - 1].all()
+    wk, wg = w_kv.to(DEV), w_gate.to(DEV)
+    ns = 2 * m - 1
+    s0 = torch.zeros(B, ns, 2, E, device=DEV)
+    s1 = torch.zeros(B, ns, 2, E, device=DEV)
+    out = torch.zeros(B, Nc, E, device=DEV, dtype=torch.bfloat16)
+    csa.csa_compress(x_tail.to(DEV), wk, wg, dev_i64(pos_tail), m, o, out, state_out=s0)
+    csa.csa_compress(x_new.to(DEV), wk, wg, dev_i64([T - 1] * B), m, o, out, state_in=s0,
+                     state_out=s1)
+    torch.cuda.synchronize()
+    assert_bf16_close(out[:, Nc - 1].float().cpu().numpy(), ref2[:, Nc - 1], "decode entry")
+
+
+def test_compress_prefill_8k_sampled_entries():
+    w = gen.WORKLOADS["csa_prefill_8k_bf16"]
+    inp = gen.prefill_inputs(w, device="cpu")
+    x = inp["x"]
+    out = torch.empty(w.B, w.n_cmp, 2 * w.D, device=DEV, dtype=torch.bfloat16)
+    kidx = torch.empty(w.B, w.n_cmp, w.d_I, device=DEV, dtype=torch.bfloat16)
+    xg = x.to(DEV)
+    pos0 = dev_i64([0])
+    csa.csa_compress(xg, inp["w_kv"].to(DEV), inp["w_gate"].to(DEV), pos0, w.m, w.overlap, out)
+    csa.csa_compress(xg, inp["w_ikv"].to(DEV), inp["w_igate"].to(DEV), pos0, w.m, w.overlap, kidx)
+    torch.cuda.synchronize()
+    g_main, g_idx = out.float().cpu().numpy(), kidx.float().cpu().numpy()
+    for i in [0, 1, 2, 511, 1024, 2046, 2047]:
+        lo = max(0, w.m * (i - 1))
+        xs = x[:, lo:w.m * (i + 1)]
+        Nc = i + 1
+        for wk, wg, g in ((inp["w_kv"], inp["w_gate"], g_main), (inp["w_ikv"], inp["w_igate"], g_idx)):
+            ref, wr, _ = _oracle(xs, wk, wg, [lo], w.m, w.overlap, Nc)
+            assert wr[0, i]
+            assert_bf16_close(g[0, i], ref[0, i], "prefill entry %d" % i)

@@ -1,0 +1,170 @@
+"""GPU parity of csa_indexer_topk against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_overlapped_amd as csa
+from compressed_sparse_attention_overlapped_amd import inputs as gen
+from oracle import oracle as orc
+from tests.helpers import check_topk_row, dev_i32, dev_i64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _n_vis(pos, ncmp, m, cap):
+    return max(0, min(ncmp, (pos + 1) // m, cap))
+
+
+def _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None, k_scale=None):
+    idx, sc = csa.csa_indexer_topk(q_idx.to(DEV), w_idx.to(DEV), k_idx.to(DEV), m, topk,
+                                   dev_i64(q_pos), dev_i32(n_cmp),
+                                   q_scale=None if q_scale is None else q_scale.to(DEV),
+                                   k_scale=None if k_scale is None else k_scale.to(DEV),
+                                   want_scores=True)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None, k_scale=None):
+    return orc.indexer_topk(gen.host_bits(q_idx), gen.host_bits(w_idx), gen.host_bits(k_idx), m,
+                            topk, np.asarray(q_pos), np.asarray(n_cmp),
+                            q_scale=None if q_scale is None else gen.host_bits(q_scale),
+                            k_scale=None if k_scale is None else gen.host_bits(k_scale),
+                            want_all=True)
+
+
+def _compare(g_idx, g_sc, o_all, m, topk, q_pos, n_cmp, Nc, what):
+    B, T, _ = g_idx.shape
+    near = 0
+    for b in range(B):
+        for t in range(T):
+            nv = _n_vis(int(q_pos[b]) + t, int(n_cmp[b]), m, Nc)
+            near += check_topk_row(g_idx[b, t], o_all[b, t], topk, nv, "%s b%d t%d" % (what, b, t))
+            sel = g_idx[b, t][g_idx[b, t] >= 0]
+            np.testing.assert_allclose(g_sc[b, t, :sel.size], o_all[b, t, sel], rtol=1e-4, atol=1e-4)
+    return near
+
+
+def test_indexer_tiny_f32_full():
+    w = gen.WORKLOADS["csa_prefill_tiny_f32"]
+    d = gen.Draw(21)
+    q_idx, _, w_idx = gen.indexer_query(d, 1, w.T, w.H_I, w.d_I, gen.F32)
+    k_idx, _ = gen.indexer_keys(d, 1, w.n_cmp, w.d_I, gen.F32)
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, w.m, w.topk, [0], [w.n_cmp])
+    o = _oracle_rows(q_idx, w_idx, k_idx, w.m, w.topk, [0], [w.n_cmp])
+    _compare(g_idx, g_sc, o[3], w.m, w.topk, [0], [w.n_cmp], w.n_cmp, "f32 tiny")
+
+
+@pytest.mark.parametrize("topk", [16, 512])
+def test_indexer_bf16_ragged_batch(topk):
+    d = gen.Draw(22 + topk)
+    B, T, Nc, m = 3, 70, 600, 4
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    q_pos, n_cmp = [0, 300, 2300], [Nc, 90, 550]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "bf16 ragged")
+
+
+def test_indexer_bf16_exact_ties_lower_index():
+    d = gen.Draw(23)
+    B, T, Nc, m, topk = 1, 20, 300, 4, 40
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    k_idx[0, 100:200] = k_idx[0, 7]            # 101 identical keys -> identical scores
+    k_idx[0, 250:] = k_idx[0, 3]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, [2000], [Nc])
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, [2000], [Nc])
+    # exact equality must resolve exactly like the oracle (no exemption)
+    for t in range(T):
+        s = o[3][0, t]
+        sel = set(g_idx[0, t].tolist())
+        ref = set(o[0][0, t].tolist())
+        diff = sel ^ ref
+        tau = o[2][0, t]
+        assert all(abs(s[j] - tau) <= 1e-3 for j in diff)
+        # among the duplicated block, chosen members are its lowest indices
+        blk = [j for j in range(100, 200) if j in sel] + ([7] if 7 in sel else [])
+        if blk and len(blk) < 101:
+            members = sorted([7] + list(range(100, 200)))
+            assert sorted(blk) == members[:len(blk)]
+
+
+def test_indexer_prefill_8k_sampled_rows():
+    w = gen.WORKLOADS["csa_prefill_8k_bf16"]
+    d = gen.Draw(w.seed + 100)
+    q_idx, _, w_idx = gen.indexer_query(d, 1, w.T, w.H_I, w.d_I, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, 1, w.n_cmp, w.d_I, gen.BF16)
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, w.m, w.topk, [0], [w.n_cmp])
+    rows = [0, 3, 4, 2047, 2048, 2051, 4095, 6000, 8190, 8191]
+    for t in rows:
+        o = _oracle_rows(q_idx[:, t:t + 1], w_idx[:, t:t + 1], k_idx, w.m, w.topk, [t], [w.n_cmp])
+        _compare(g_idx[:, t:t + 1], g_sc[:, t:t + 1], o[3], w.m, w.topk, [t], [w.n_cmp], w.n_cmp,
+                 "8k row %d" % t)
+
+
+@pytest.mark.parametrize("name,rows", [("csa_decode_128k_b32", [0, 13, 31]),
+                                       ("csa_decode_1m_b8_stream", [2])])
+def test_indexer_fp8_decode_long_rows(name, rows):
+    w = gen.WORKLOADS[name]
+    d = gen.Draw(w.seed, DEV)
+    B, Nc = w.B, w.n_cmp
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, w.d_I, gen.FP8)
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, 1, w.H_I, w.d_I, gen.FP8)
+    q_pos = [w.ctx - 1] * B
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, w.m, w.topk, q_pos, [Nc] * B, q_scale, k_scale)
+    for b in rows:
+        sl = slice(b, b + 1)
+        o = _oracle_rows(q_idx[sl], w_idx[sl], k_idx[sl], w.m, w.topk, [w.ctx - 1], [Nc],
+                         q_scale[sl], k_scale[sl])
+        _compare(g_idx[sl], g_sc[sl], o[3], w.m, w.topk, [w.ctx - 1], [Nc], Nc, "%s b%d" % (name, b))
+
+
+def test_indexer_fp8_long_rows_heavy_ties_and_partial_visibility():
+    # 20000 entries with one repeated key: every candidate ties exactly, which
+    # overflows the LDS candidate buffer and exercises the exact global path
+    d = gen.Draw(24, "cpu")
+    B, Nc, m, topk = 3, 20000, 4, 300
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
+    kb = k_idx.view(torch.uint8)            # edit the stored codes directly
+    kb[0] = kb[0, 5].clone()
+    k_scale[0] = k_scale[0, 5].clone()
+    kb[1, ::2] = kb[1, 11].clone()
+    k_scale[1, ::2] = k_scale[1, 11].clone()
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, 2, 16, 64, gen.FP8)
+    w_idx[0] = w_idx[0].abs()
+    q_pos = [4 * Nc, 4 * Nc, 4 * 150]       # third sequence sees only ~150 entries
+    n_cmp = [Nc, Nc - 7, Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "fp8 ties")
+    # all-equal row: the lowest indices win, bit-exact
+    if (o[3][0, 0, :Nc] == o[3][0, 0, 0]).all():
+        assert np.array_equal(g_idx[0, 0], np.arange(topk))
+
+
+def test_indexer_edge_rows():
+    d = gen.Draw(25)
+    B, T, Nc, m, topk = 2, 9, 40, 4, 16
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    q_pos = [0, 60]                  # rows with n_vis = 0, 1, 2 and rows with n_vis > topk
+    n_cmp = [Nc, Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    assert (g_idx[0, :3] == -1).all()        # positions 0..2 see no entry
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "edge")
+
+
+def test_indexer_deterministic():
+    d = gen.Draw(26, "cpu")
+    B, Nc, m, topk = 2, 40000, 4, 2048
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, 1, 16, 64, gen.FP8)
+    args = (q_idx, w_idx, k_idx, m, topk, [4 * Nc] * B, [Nc] * B, q_scale, k_scale)
+    a = _gpu(*args)
+    for _ in range(3):
+        b = _gpu(*args)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
