@@ -246,32 +246,230 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bf16 decode
+// Few query rows, long key lists (decode): a work item is (row, split) and its
+// waves split the heads - wave w owns heads 16 w .. 16 w + 15 - so a 64-key
+// tile of [K | V] rows is loaded once per workgroup and read by every wave.
+// Per wave and tile:
+//     S^T (16 keys x 16 heads) = K Q^T        4 blocks x 4 MFMA 16x16x32
+//     O^T (16 dims x 16 heads) += V^T P^T     8 dim tiles x 2 MFMA
+// The S^T accumulator of lane l holds head l%16 and keys 4 (l/16) + i of each
+// 16-key block, which is the P^T operand once the k order of the second
+// product pairs keys {32 ks + 4 g + i} and {32 ks + 16 + 4 g + i}; V^T
+// fragments of 4 consecutive keys per lane come from the LDS transpose read
+// (lane i of a 16-lane group gets element i % 4 of the 8-byte chunks whose
+// addresses lanes i/4 + 4 v supplied).  The next tile's rows are loaded into
+// registers while the current one is computed.
+constexpr int DC_KT = 64;                // keys per tile
+constexpr int DC_ROW = 256 + 16;         // bf16 per LDS row (544 B: conflict-free reads)
+constexpr int DC_IDX_MAX = 4096;         // index slots staged in LDS per work item
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+template <int WAVES>  // H = 16 WAVES
+__global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv_cmp,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
+    const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
+    const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
+    int R_cap, bool dense, float scale_log2, int n_split, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
+  constexpr int CH = DC_KT * 32 / NT;  // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t tile[DC_KT * DC_ROW];
+  __shared__ int vmask[DC_KT];
+  __shared__ int idx_s[DC_IDX_MAX];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, hl = lane & 15;
+  const int item = blockIdx.x;
+  const int rowi = item / n_split, split = item % n_split;
+  const int b = rowi / T, t = rowi % T;
+  const int64_t pos = q_pos[b] + t;
+  const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
+  const int nk = L.n_c + L.n_w;
+  int per = (nk + n_split - 1) / n_split;
+  per = (per + DC_KT - 1) / DC_KT * DC_KT;
+  const int kb = min(nk, split * per), ke = min(nk, kb + per);
+  const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
+  const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
+  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  const int64_t rbase = raw_base[b];
+
+  // index slots of this item's compressed positions, staged once
+  const int c_lo = min(kb, L.n_c), c_hi = min(ke, L.n_c);
+  const bool stage = !dense && (c_hi - c_lo) <= DC_IDX_MAX;
+  if (stage)
+    for (int i = tid; i < c_hi - c_lo; i += NT) idx_s[i] = idx_row[c_lo + i];
+  __syncthreads();
+  auto src_of = [&](int p) -> const uint16_t* {
+    if (p >= ke) return nullptr;
+    if (p < L.n_c) {
+      int j = dense ? p : (stage ? idx_s[p - c_lo] : idx_row[p]);
+      if (j < 0 || j >= Nc_cap) return nullptr;
+      return kvc_b + (size_t)j * 2 * D;
+    }
+    int64_t r = L.lo + (p - L.n_c) - rbase;
+    if (r < 0 || r >= R_cap) return nullptr;
+    return kvr_b + (size_t)r * 2 * D;
+  };
+
+  // Q^T operand: lane holds head 16 wave + hl, dims 32 s + 8 g .. + 8
+  bf16x8 qf[4];
+  {
+    const uint16_t* qr = q + ((size_t)rowi * H + 16 * wave + hl) * D;
+    for (int s = 0; s < 4; ++s) qf[s] = *(const bf16x8*)(qr + 32 * s + 8 * g);
+  }
+  f32x4 o[8];
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float mrun = -INFINITY, lrun = 0.0f;
+
+  const int ntiles = (ke - kb + DC_KT - 1) / DC_KT;
+  const int col = tid & 31;
+  u32x4 pf[CH];
+  bool pv[CH];
+  auto issue = [&](int ti) {
+    const int p0 = kb + ti * DC_KT;
+    for (int i = 0; i < CH; ++i) {
+      const int rr = i * (NT / 32) + (tid >> 5);
+      const uint16_t* src = src_of(p0 + rr);
+      pv[i] = src != nullptr;
+      pf[i] = src ? __builtin_nontemporal_load((const u32x4*)(src + 8 * col)) : u32x4{0, 0, 0, 0};
+    }
+  };
+  if (ntiles > 0) issue(0);
+  for (int ti = 0; ti < ntiles; ++ti) {
+    __syncthreads();  // every wave is done reading the previous tile
+    for (int i = 0; i < CH; ++i) {
+      const int rr = i * (NT / 32) + (tid >> 5);
+      *(u32x4*)(tile + rr * DC_ROW + 8 * col) = pf[i];
+      if (col == 0) vmask[rr] = pv[i];
+    }
+    __syncthreads();
+    if (ti + 1 < ntiles) issue(ti + 1);
+    // ---- S^T = K Q^T for 4 blocks of 16 keys
+    f32x4 sacc[4];
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      sacc[kb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const uint16_t* krow = tile + (16 * kb4 + hl) * DC_ROW + 8 * g;
+      for (int s = 0; s < 4; ++s)
+        sacc[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(krow + 32 * s),
+                                                           qf[s], sacc[kb4], 0, 0, 0);
+    }
+    // ---- online softmax over the 64 keys; lane: head hl, keys 16 kb4 + 4 g + i
+    float mx = -INFINITY;
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = vmask[16 * kb4 + 4 * g + i] != 0;
+        const float sv = ok ? sacc[kb4][i] * scale_log2 : -INFINITY;
+        sacc[kb4][i] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);
+    const float muse = mnew == -INFINITY ? 0.0f : mnew;
+    const float corr = exp2f(mrun - muse);
+    float ps = 0.0f;
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+      for (int i = 0; i < 4; ++i) {
+        const float pv2 = exp2f(sacc[kb4][i] - muse);
+        sacc[kb4][i] = pv2;
+        ps += pv2;
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lrun = lrun * corr + ps;
+    mrun = mnew;
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= corr;
+    // ---- O^T += V^T P^T (k slot 8 g + i: key 32 ks + 4 g + i, then 32 ks + 16 + 4 g + i)
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pfr;
+      for (int i = 0; i < 4; ++i) {
+        pfr[i] = (__bf16)sacc[2 * ks][i];
+        pfr[4 + i] = (__bf16)sacc[2 * ks + 1][i];
+      }
+      // transpose-read addresses: lane j of the group supplies row k0 + j/4,
+      // dims D0 + 4 (j % 4)
+      const uint16_t* base1 = tile + (32 * ks + 4 * g + (hl >> 2)) * DC_ROW + D + 4 * (hl & 3);
+      const uint16_t* base2 = base1 + 16 * DC_ROW;
+      for (int dt = 0; dt < 8; ++dt) {
+        // whole-register moves only: the four 16-bit values of a transpose
+        // read are not extracted one by one
+        const u32x2 v1 = __builtin_bit_cast(u32x2, lds_read_tr16(base1 + 16 * dt));
+        const u32x2 v2 = __builtin_bit_cast(u32x2, lds_read_tr16(base2 + 16 * dt));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{v1[0], v1[1], v2[0], v2[1]});
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfr, o[dt], 0, 0, 0);
+      }
+    }
+  }
+  // ---- results: lane holds head 16 wave + hl, dims 16 dt + 4 g + i
+  const int h = 16 * wave + hl;
+  if (n_split == 1) {
+    const float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
+    uint16_t* orow = out + ((size_t)rowi * H + h) * D;
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + 4 * g;
+      uint32_t lo = (uint32_t)f32_to_bf16(o[dt][0] * inv) | ((uint32_t)f32_to_bf16(o[dt][1] * inv) << 16);
+      uint32_t hi = (uint32_t)f32_to_bf16(o[dt][2] * inv) | ((uint32_t)f32_to_bf16(o[dt][3] * inv) << 16);
+      *(u32x2*)(orow + d) = u32x2{lo, hi};
+    }
+    if (lse && g == 0)
+      lse[(size_t)rowi * H + h] = lrun > 0.0f ? (mrun + __log2f(lrun)) * kLn2 : -INFINITY;
+  } else {
+    float* po = part_o + ((size_t)item * H + h) * D;
+    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt + 4 * g) = o[dt];
+    if (g == 0) {
+      part_ml[((size_t)item * H + h) * 2 + 0] = mrun;
+      part_ml[((size_t)item * H + h) * 2 + 1] = lrun;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- combine
+// Grid (rows, H / 8): the workgroup merges 8 heads of one query row.  Per head
+// the split maxima fix the weights exp2(m_s - M) once (in LDS); then every
+// output element is a weighted sum of its split partials, read coalesced.
+constexpr int CB_HEADS = 8, CB_MAX_SPLIT = 64;
+
 template <int OUT_DT>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int n_split, int H, int D, void* __restrict__ out,
                                                       float* __restrict__ lse) {
-  const int rowi = blockIdx.x;
-  for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
-    const int h = i / D;
+  __shared__ float wgt[CB_HEADS][CB_MAX_SPLIT];
+  __shared__ float inv_l[CB_HEADS];
+  const int rowi = blockIdx.x, h0 = blockIdx.y * CB_HEADS;
+  const int tid = threadIdx.x;
+  if (tid < CB_HEADS) {
+    const int h = h0 + tid;
     float M = -INFINITY;
     for (int s = 0; s < n_split; ++s)
       M = fmaxf(M, part_ml[(((size_t)rowi * n_split + s) * H + h) * 2]);
     const float Mu = M == -INFINITY ? 0.0f : M;
-    float Ls = 0.0f, O = 0.0f;
+    float Ls = 0.0f;
     for (int s = 0; s < n_split; ++s) {
       const size_t it = (size_t)rowi * n_split + s;
       const float c = exp2f(part_ml[(it * H + h) * 2] - Mu);
+      wgt[tid][s] = c;
       Ls += part_ml[(it * H + h) * 2 + 1] * c;
-      O += part_o[it * H * D + i] * c;
     }
-    const float v = Ls > 0.0f ? O / Ls : 0.0f;
+    inv_l[tid] = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    if (lse) lse[(size_t)rowi * H + h] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  for (int i = tid; i < CB_HEADS * D; i += blockDim.x) {
+    const int hh = i / D, d = i % D, h = h0 + hh;
+    float O = 0.0f;
+    for (int s = 0; s < n_split; ++s)
+      O = fmaf(part_o[(((size_t)rowi * n_split + s) * H + h) * D + d], wgt[hh][s], O);
+    const float v = O * inv_l[hh];
     if (OUT_DT == CSA_DT_BF16)
-      ((uint16_t*)out)[(size_t)rowi * H * D + i] = f32_to_bf16(v);
+      ((uint16_t*)out)[((size_t)rowi * H + h) * D + d] = f32_to_bf16(v);
     else
-      ((float*)out)[(size_t)rowi * H * D + i] = v;
-    if (lse && (i % D) == 0) lse[(size_t)rowi * H + h] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+      ((float*)out)[((size_t)rowi * H + h) * D + d] = v;
   }
 }
 
@@ -322,17 +520,35 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
 namespace csa_host {
 using namespace csa;
 
-static int attn_splits(int rows, int keys_per_row) {
+// Rows at or above this count use the one-row-per-wave kernel; fewer rows
+// (decode) use the head-split kernel with split-K.
+constexpr int AT_DECODE_ROWS = 1024;
+constexpr int DC_MIN_SPLIT_KEYS = 128;
+
+static bool use_decode_kernel(int rows, int H) {
+  return rows < AT_DECODE_ROWS && (H == 32 || H == 64);
+}
+
+static int attn_splits(int rows, int keys_per_row, int H) {
+  if (use_decode_kernel(rows, H)) {
+    // about two workgroups per CU of the 256, each with >= 128 keys
+    int s = (512 + rows - 1) / rows;
+    int smax = (keys_per_row + DC_MIN_SPLIT_KEYS - 1) / DC_MIN_SPLIT_KEYS;
+    if (smax > CB_MAX_SPLIT) smax = CB_MAX_SPLIT;
+    s = s < smax ? s : smax;
+    return s < 1 ? 1 : s;
+  }
   // enough work items to fill the chip; every split keeps >= 256 keys
   if (rows >= 1024 || keys_per_row <= AT_MIN_SPLIT_KEYS) return 1;
   int s = (1024 + rows - 1) / rows;
   int smax = (keys_per_row + AT_MIN_SPLIT_KEYS - 1) / AT_MIN_SPLIT_KEYS;
+  if (smax > CB_MAX_SPLIT) smax = CB_MAX_SPLIT;
   return s < smax ? s : smax;
 }
 
 size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row) {
   const int rows = B * T;
-  const int s = attn_splits(rows, keys_per_row);
+  const int s = attn_splits(rows, keys_per_row, H);
   if (s == 1) return 0;
   return (size_t)rows * s * H * (D + 2) * sizeof(float);
 }
@@ -348,12 +564,23 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
-  const int n_split = attn_splits(rows, keys);
+  const int n_split = attn_splits(rows, keys, a.H);
   float* part_o = (float*)a.ws;
   float* part_ml = part_o ? part_o + (size_t)rows * n_split * a.H * a.D : nullptr;
   const size_t lds = (size_t)AT_WAVES * AT_KT * AT_ROW * sizeof(uint16_t);
   const unsigned grid = (unsigned)(rows * n_split);
-  if (a.H == 64)
+  if (use_decode_kernel(rows, a.H)) {
+    if (a.H == 64)
+      attn_dec_kernel<4><<<grid, 256, 0, st>>>(
+          (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
+          a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
+          scale_log2, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+    else
+      attn_dec_kernel<2><<<grid, 128, 0, st>>>(
+          (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
+          a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
+          scale_log2, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+  } else if (a.H == 64)
     attn_bf16_kernel<2><<<grid, 256, lds, st>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,
         a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,
@@ -364,8 +591,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
         a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,
         n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
   if (n_split > 1)
-    combine_kernel<CSA_DT_BF16><<<rows, 256, 0, st>>>(part_o, part_ml, n_split, a.H, a.D, a.out,
-                                                      a.lse);
+    combine_kernel<CSA_DT_BF16><<<dim3(rows, a.H / CB_HEADS), 256, 0, st>>>(
+        part_o, part_ml, n_split, a.H, a.D, a.out, a.lse);
   return hipGetLastError();
 }
 

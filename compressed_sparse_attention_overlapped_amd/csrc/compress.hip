@@ -12,6 +12,8 @@
 //     carried state), the weighted sum of P, then the storage rounding (fp32,
 //     bf16 RNE, or e4m3 with a per-row amax/448 scale).  Extra workgroups
 //     write the carried state for the next call.
+#include <algorithm>
+
 #include "common.h"
 
 namespace csa {
@@ -104,37 +106,65 @@ __global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__
   pg[id] = s;
 }
 
+// ---------------------------------------------------------------- split-K sum
+// pg[0][i] = sum_s pg[s][i] in a fixed order, in place.  A workgroup owns 64
+// consecutive elements; its 4 waves sum interleaved quarters of the splits
+// and the quarters are added in LDS.
+__global__ void __launch_bounds__(256) split_sum_kernel(float* __restrict__ pg, size_t n,
+                                                        int n_split) {
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t i = (size_t)blockIdx.x * 64 + lane;
+  float v = 0.0f;
+  if (i < n) {
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int s = wave;
+    for (; s + 12 < n_split; s += 16) {
+      a[0] += pg[(size_t)s * n + i];
+      a[1] += pg[(size_t)(s + 4) * n + i];
+      a[2] += pg[(size_t)(s + 8) * n + i];
+      a[3] += pg[(size_t)(s + 12) * n + i];
+    }
+    for (; s < n_split; s += 4) a[0] += pg[(size_t)s * n + i];
+    v = (a[0] + a[1]) + (a[2] + a[3]);
+  }
+  part[wave][lane] = v;
+  __syncthreads();
+  if (wave == 0 && i < n) pg[i] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+}
+
 // ---------------------------------------------------------------- pool
 // Grid (n_slots + 1, B).  Slot q < n_slots handles entry i_lo(b) + q; the last
 // slot writes state_out.  Each thread owns channels e = tid, tid + 256, ...
 template <int OUT_DT>
 __global__ void __launch_bounds__(256) pool_kernel(
-    const float* __restrict__ pg, int n_split, const int64_t* __restrict__ pos0, int B, int L,
+    const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, float* __restrict__ out_scale,
     int Nc_cap, int n_slots) {
   const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
   const int ns = (1 + overlap) * m - 1;
   const int64_t p0 = pos0[b];
-  const size_t M = (size_t)B * L, N = 2 * (size_t)E;
-  const size_t split_stride = M * N;
+  const size_t N = 2 * (size_t)E;
 
-  // P (c = 0) or G (c = 1) of token at absolute position j, channel e; the
-  // caller guarantees pos0 - ns <= j < pos0 + L.
-  auto fetch = [&](int64_t j, int c, int e, bool& present) -> float {
-    present = true;
-    if (j < 0) { present = false; return 0.0f; }
+  // P and G of the token at absolute position j, channel e; the caller
+  // guarantees pos0 - ns <= j < pos0 + L.  Absent tokens get G = -inf.
+  auto fetch = [&](int64_t j, int e, float& pv, float& gv) {
+    pv = 0.0f;
+    gv = -INFINITY;
+    if (j < 0) return;
     if (j >= p0) {
-      size_t off = ((size_t)b * L + (size_t)(j - p0)) * N + (size_t)c * E + e;
-      float v = 0.0f;
-      for (int s = 0; s < n_split; ++s) v += pg[off + s * split_stride];
-      return v;
+      const float* r = pg + ((size_t)b * L + (size_t)(j - p0)) * N;
+      pv = r[e];
+      gv = r[E + e];
+      return;
     }
-    if (!state_in) { present = false; return 0.0f; }
-    int slot = (int)(j - (p0 - ns));
-    float v = state_in[(((size_t)b * ns + slot) * 2 + c) * E + e];
-    if (c == 1 && v == -INFINITY) present = false;
-    return v;
+    if (!state_in) return;
+    const int slot = (int)(j - (p0 - ns));
+    const float* r = state_in + (((size_t)b * ns + slot) * 2) * E;
+    pv = r[e];
+    gv = r[E + e];
+    if (gv == -INFINITY) pv = 0.0f;
   };
 
   if (q == n_slots) {  // carried state for the next call
@@ -142,10 +172,8 @@ __global__ void __launch_bounds__(256) pool_kernel(
     for (int idx = tid; idx < ns * E; idx += blockDim.x) {
       int slot = idx / E, e = idx % E;
       int64_t j = p0 + L - ns + slot;
-      bool pr1, pr2;
-      float pv = fetch(j, 0, e, pr1);
-      float gv = fetch(j, 1, e, pr2);
-      if (!pr1 || !pr2) { pv = 0.0f; gv = -INFINITY; }
+      float pv, gv;
+      fetch(j, e, pv, gv);
       state_out[(((size_t)b * ns + slot) * 2 + 0) * E + e] = pv;
       state_out[(((size_t)b * ns + slot) * 2 + 1) * E + e] = gv;
     }
@@ -164,24 +192,33 @@ __global__ void __launch_bounds__(256) pool_kernel(
   float amax = 0.0f;
   int nv = 0;
   for (int e = tid; e < E; e += blockDim.x, ++nv) {
-    float mx = -INFINITY;
-    for (int64_t j = first; j <= last; ++j) {
-      bool pr;
-      float g = fetch(j, 1, e, pr);
-      if (!pr) continue;
-      g += ape ? ape[(size_t)(j - first) * E + e] : 0.0f;
-      mx = fmaxf(mx, g);
-    }
-    float den = 0.0f, num = 0.0f;
-    for (int64_t j = first; j <= last; ++j) {
-      bool pr;
-      float g = fetch(j, 1, e, pr);
-      if (!pr) continue;
-      g += ape ? ape[(size_t)(j - first) * E + e] : 0.0f;
-      float p = fetch(j, 0, e, pr);
-      float wgt = __expf(g - mx);
-      den += wgt;
-      num = fmaf(wgt, p, num);
+    // online softmax over the window in chunks of 8 tokens; every chunk's
+    // loads are independent of each other
+    float mx = -INFINITY, den = 0.0f, num = 0.0f;
+    for (int64_t j0 = first; j0 <= last; j0 += 8) {
+      float pv[8], gv[8];
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = j0 + u;
+        if (j <= last) {
+          fetch(j, e, pv[u], gv[u]);
+          if (gv[u] != -INFINITY && ape) gv[u] += ape[(size_t)(j - first) * E + e];
+        } else {
+          pv[u] = 0.0f;
+          gv[u] = -INFINITY;
+        }
+      }
+      float cm = mx;
+      for (int u = 0; u < 8; ++u) cm = fmaxf(cm, gv[u]);
+      if (cm == -INFINITY) continue;
+      const float corr = __expf(mx - cm);  // mx = -inf -> 0
+      den *= corr;
+      num *= corr;
+      for (int u = 0; u < 8; ++u) {
+        const float w = __expf(gv[u] - cm);
+        den += w;
+        num = fmaf(w, pv[u], num);
+      }
+      mx = cm;
     }
     float c = num / den;
     vals[nv] = c;
@@ -246,22 +283,26 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
     proj_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
         (const float*)a.x, (const float*)a.w_kv, (const float*)a.w_gate, pg, M, E, K);
   }
+  if (splits > 1) {
+    const size_t n = (size_t)M * 2 * E;
+    split_sum_kernel<<<(unsigned)((n + 63) / 64), 256, 0, st>>>(pg, n, splits);
+  }
   const int n_slots = (a.L + a.m - 1) / a.m + 1;
   dim3 pgrid(n_slots + 1, a.B);
   switch (a.out_dt) {
     case CSA_DT_F32:
-      pool_kernel<CSA_DT_F32><<<pgrid, 256, 0, st>>>(pg, splits, a.pos0, a.B, a.L, E, a.m,
+      pool_kernel<CSA_DT_F32><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m,
                                                       a.overlap, a.ape, a.state_in, a.state_out,
                                                       a.out, a.out_scale, a.Nc_cap, n_slots);
       break;
     case CSA_DT_BF16:
-      pool_kernel<CSA_DT_BF16><<<pgrid, 256, 0, st>>>(pg, splits, a.pos0, a.B, a.L, E, a.m,
+      pool_kernel<CSA_DT_BF16><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m,
                                                        a.overlap, a.ape, a.state_in, a.state_out,
                                                        a.out, a.out_scale, a.Nc_cap, n_slots);
       break;
     default:
       pool_kernel<CSA_DT_FP8E4M3><<<pgrid, 256, 0, st>>>(
-          pg, splits, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,
+          pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,
           a.out_scale, a.Nc_cap, n_slots);
   }
   return hipGetLastError();

@@ -14,11 +14,11 @@
 //    index order.
 //  * long rows: the score kernel also builds a per-row histogram of the top
 //    11 key bits; "collect" workgroups (one per 2048-entry chunk) find the
-//    threshold bin, and write, in index order, the chunk's entries above it
-//    (certainly selected) and inside it (candidates); "finalize" (one
-//    workgroup per row) picks the missing entries among the candidates by an
-//    exact radix select on (key, -index) and merges the per-chunk lists into
-//    the ascending output.
+//    bin holding the k-th key and append the chunk's entries above it
+//    (certainly selected) and inside it (candidates) to per-row lists;
+//    "finalize" (one workgroup per row) picks the missing entries among the
+//    candidates by an exact radix select on (key, then inverted index) and
+//    writes the selected set sorted ascending.
 #include <algorithm>
 
 #include "common.h"
@@ -29,7 +29,6 @@ constexpr int kHistBins = 2048, kHistShift = 21;
 constexpr int kShortMax = 8192;
 constexpr int kChunk = 2048;
 constexpr int kFinalCandLds = 8192;  // candidates held in LDS by finalize
-constexpr int kMaxChunks = 1024;     // Nc_cap <= kMaxChunks * kChunk
 
 __device__ __forceinline__ void hist_flush(const uint32_t* lhist, uint32_t* ghist) {
   for (int bin = threadIdx.x; bin < kHistBins; bin += blockDim.x) {
@@ -179,11 +178,27 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
 
 // ---------------------------------------------------------------- scores: fp8
 // H_I = 16, d_I = 64, e4m3 codes with positive row scales.  One query row per
-// workgroup, a chunk of kChunk entries split over 4 waves; each 16-entry group
-// is two 16x16x32 fp8 MFMAs (heads x entries).  Lane l loads 16 contiguous
-// bytes of entry (l % 16) at byte offset 16 (l / 16); the first 8 bytes feed
-// the first MFMA and the next 8 the second (the query uses the same k order).
+// workgroup, a chunk of kChunk entries split over 4 waves.  The codes are
+// widened to bf16 (exact: e4m3 values are bf16 values) and multiplied on the
+// bf16 16x16x32 MFMA, whose fp32 accumulation is exact to fp32 rounding; the
+// fp8 MFMA accumulates with fewer bits, which would move scores by more than
+// the top-k tie tolerance.  Each 16-entry group is two MFMAs (heads x
+// entries).  Lane l loads 16 contiguous bytes of entry (l % 16) at byte
+// offset 16 (l / 16); the first 8 codes feed the first MFMA and the next 8
+// the second (the query uses the same k order).
 constexpr int SF_UNROLL = 8;
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
 
 template <bool HIST>
 __global__ void __launch_bounds__(256) score_fp8_kernel(
@@ -205,8 +220,8 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
   if (jb < je) {
     const int h = lane & 15, g = lane >> 4;
     const u32x4 qv = *(const u32x4*)(q_idx + ((size_t)row * 16 + h) * 64 + 16 * g);
-    const long qa0 = (long)qv[0] | ((long)qv[1] << 32);
-    const long qa1 = (long)qv[2] | ((long)qv[3] << 32);
+    const bf16x8 qa0 = e4m3x8_to_bf16x8(qv[0], qv[1]);
+    const bf16x8 qa1 = e4m3x8_to_bf16x8(qv[2], qv[3]);
     float wq[4];
     for (int i = 0; i < 4; ++i) {
       int hh = 4 * g + i;
@@ -235,10 +250,10 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
       float res[SF_UNROLL];
       for (int u = 0; u < SF_UNROLL; ++u) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        long kb0 = (long)kv[u][0] | ((long)kv[u][1] << 32);
-        long kb1 = (long)kv[u][2] | ((long)kv[u][3] << 32);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa0, kb0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa1, kb1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, e4m3x8_to_bf16x8(kv[u][0], kv[u][1]),
+                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, e4m3x8_to_bf16x8(kv[u][2], kv[u][3]),
+                                                      acc, 0, 0, 0);
         // acc[i]: head 4 (lane / 16) + i, entry lane % 16
         float p = 0.0f;
         for (int i = 0; i < 4; ++i) p = fmaf(wq[i], fmaxf(acc[i], 0.0f), p);
@@ -246,7 +261,7 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
         p += __shfl_xor(p, 32, 64);
         res[u] = p * ksc[u];
       }
-      // lane l writes entry j0 + l (group l / 16) for each half of the unroll
+      // lane l writes entry j0 + 64 half + l (group 4 half + l / 16)
       for (int half = 0; half < SF_UNROLL / 4; ++half) {
         float v = res[half * 4 + 0];
         const int gsel = lane >> 4;
@@ -268,7 +283,8 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
 }
 
 // ---------------------------------------------------------------- block scans
-// Exclusive prefix sum over blockDim.x (= 256) values; returns the total.
+// Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64);
+// returns the caller's offset and sets the block total.  sh: >= 16 words.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t x = v;
@@ -288,39 +304,47 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   return base + x - v;
 }
 
-// Radix select over `n` keys in LDS: finds the prefix/mask pair such that the
-// selected set is {x : (x & mask) >= prefix} when `all_eq` is set, or, when
-// the full key width got resolved, {x > prefix} plus the first `remaining`
-// keys equal to prefix.  need >= 1 and need <= n.  Uses hist[256] scratch.
+// MSB-first radix select (8-bit digits) of the `need` largest of n keys,
+// 1 <= need <= n.  get(i) returns key i.  The result describes the selected
+// set: all_eq -> {x : (x & mask) >= prefix}; otherwise the key width got fully
+// resolved and the set is {x > prefix} plus `remaining` keys equal to prefix.
+// hist: 256 words of LDS; sh: >= 24 words; blockDim.x >= 256.
 struct RadixResult {
   uint32_t prefix, mask, remaining;
   bool all_eq;
 };
 
-__device__ RadixResult radix_select_u32(const uint32_t* keys, int n, uint32_t need,
-                                        uint32_t* hist, uint32_t* sh) {
+// Digit search of one radix pass, in parallel: thread i owns bin 255 - i
+// (blockDim.x >= 256); a block scan gives the count above each bin.  Sets
+// sh[0] = digit, sh[1] = count above it, sh[2] = its count.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remaining,
+                                           uint32_t* sh) {
+  const int tid = threadIdx.x;
+  const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
+  uint32_t tot;
+  const uint32_t above = block_excl_scan(c, sh + 8, tot);
+  if (tid < 256 && above < remaining && above + c >= remaining) {
+    sh[0] = 255u - tid;
+    sh[1] = above;
+    sh[2] = c;
+  }
+  __syncthreads();
+}
+
+template <class Get>
+__device__ RadixResult radix_select(Get get, int n, uint32_t need, uint32_t* hist,
+                                    uint32_t* sh) {
   RadixResult r{0u, 0u, need, false};
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      uint32_t x = keys[i];
+      uint32_t x = get(i);
       if ((x & r.mask) == r.prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
     __syncthreads();
     // digit d with cum_above(d) < remaining <= cum_above(d) + hist[d]
-    if (threadIdx.x == 0) {
-      uint32_t cum = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (cum + hist[d] >= r.remaining) break;
-        cum += hist[d];
-      }
-      sh[0] = (uint32_t)d;
-      sh[1] = cum;
-      sh[2] = hist[d];
-    }
-    __syncthreads();
+    find_digit(hist, r.remaining, sh);
     uint32_t d = sh[0], cum = sh[1], cnt = sh[2];
     __syncthreads();
     r.remaining -= cum;
@@ -334,6 +358,11 @@ __device__ RadixResult radix_select_u32(const uint32_t* keys, int n, uint32_t ne
   return r;
 }
 
+__device__ RadixResult radix_select_u32(const uint32_t* keys, int n, uint32_t need,
+                                        uint32_t* hist, uint32_t* sh) {
+  return radix_select([&](int i) { return keys[i]; }, n, need, hist, sh);
+}
+
 // ---------------------------------------------------------------- short rows
 // One workgroup (256 threads) per row; Nc_cap <= kShortMax.
 __global__ void __launch_bounds__(256) select_short_kernel(
@@ -342,7 +371,7 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
   __shared__ uint32_t keys[kShortMax];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[8];
+  __shared__ uint32_t sh[32];
   const int row = blockIdx.x, b = row / T, t = row % T;
   const int tid = threadIdx.x;
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
@@ -403,10 +432,9 @@ __global__ void __launch_bounds__(256) select_short_kernel(
 
 // ---------------------------------------------------------------- long rows
 // Threshold bin from the row histogram: the bin where the count from the top
-// reaches `need`; returns the count strictly above it.
+// reaches `need`; returns the count strictly above it.  256 threads.
 __device__ void threshold_bin(const uint32_t* __restrict__ ghist_row, uint32_t need,
                               uint32_t* sh, uint32_t& bin, uint32_t& above) {
-  // each thread sums 8 consecutive bins (from the top)
   const int tid = threadIdx.x;
   uint32_t c[8], s = 0;
   for (int i = 0; i < 8; ++i) {
@@ -415,52 +443,55 @@ __device__ void threshold_bin(const uint32_t* __restrict__ ghist_row, uint32_t n
   }
   uint32_t tot;
   uint32_t base = block_excl_scan(s, sh, tot);
-  __syncthreads();
   if (base < need && base + s >= need) {
     uint32_t cum = base;
     for (int i = 0; i < 8; ++i) {
       if (cum + c[i] >= need) {
-        sh[4] = (uint32_t)(kHistBins - 1 - (tid * 8 + i));
-        sh[5] = cum;
+        sh[20] = (uint32_t)(kHistBins - 1 - (tid * 8 + i));
+        sh[21] = cum;
         break;
       }
       cum += c[i];
     }
   }
   __syncthreads();
-  bin = sh[4];
-  above = sh[5];
+  bin = sh[20];
+  above = sh[21];
   __syncthreads();
 }
 
-// Grid (n_chunks, rows).  Writes per chunk, in index order, the entries above
-// the threshold bin (def) and inside it (cand), with their counts.
+// Grid (n_chunks, rows), 256 threads.  Appends the chunk's entries above the
+// threshold bin to the row's definite list and those inside it (index and low
+// key bits) to the candidate list; one atomic per list per workgroup.  The
+// order inside the lists does not matter: finalize sorts.
 __global__ void __launch_bounds__(256) collect_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ ghist,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp, int T, int Nc_cap,
-    int m, int topk, int n_chunks, uint32_t* __restrict__ def_cnt, uint32_t* __restrict__ cand_cnt,
-    uint32_t* __restrict__ def_list, uint32_t* __restrict__ cand_list) {
-  __shared__ uint32_t sh[8];
+    int m, int topk, uint32_t* __restrict__ counts, uint32_t* __restrict__ def_list,
+    uint32_t* __restrict__ cand_idx, uint32_t* __restrict__ cand_key) {
+  __shared__ uint32_t sh[32];
   const int chunk = blockIdx.x, row = blockIdx.y, b = row / T, t = row % T;
   const int tid = threadIdx.x;
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const int nsel = min(topk, nv);
-  const size_t cidx = (size_t)row * n_chunks + chunk;
   const int j0 = chunk * kChunk, j1 = min(nv, j0 + kChunk);
+  if (nsel == 0 || j0 >= j1) return;
   uint32_t bin = 0, above = 0;
-  bool all = nsel == nv;
-  if (!all && nsel > 0) threshold_bin(ghist + (size_t)row * kHistBins, (uint32_t)nsel, sh, bin, above);
-  // 8 entries per thread, contiguous
+  const bool all = nsel == nv;
+  if (!all) threshold_bin(ghist + (size_t)row * kHistBins, (uint32_t)nsel, sh, bin, above);
   const float* srow = scores + (size_t)row * Nc_cap;
   uint32_t nd = 0, nc = 0;
   uint8_t kind[8];
+  uint32_t key[8];
   for (int i = 0; i < 8; ++i) {
     int j = j0 + tid * 8 + i;
     uint8_t k = 0;
-    if (j < j1 && nsel > 0) {
+    key[i] = 0;
+    if (j < j1) {
       if (all) k = 1;
       else {
-        uint32_t kb = score_key(srow[j]) >> kHistShift;
+        key[i] = score_key(srow[j]);
+        uint32_t kb = key[i] >> kHistShift;
         k = kb > bin ? 1 : (kb == bin ? 2 : 0);
       }
     }
@@ -471,39 +502,43 @@ __global__ void __launch_bounds__(256) collect_kernel(
   uint32_t td, tc;
   uint32_t db = block_excl_scan(nd, sh, td);
   uint32_t cb = block_excl_scan(nc, sh, tc);
-  uint32_t* dl = def_list + cidx * kChunk;
-  uint32_t* cl = cand_list + cidx * kChunk;
+  if (tid == 0) {
+    sh[16] = td ? atomicAdd(&counts[2 * row + 0], td) : 0u;
+    sh[17] = tc ? atomicAdd(&counts[2 * row + 1], tc) : 0u;
+  }
+  __syncthreads();
+  db += sh[16];
+  cb += sh[17];
+  uint32_t* dl = def_list + (size_t)row * topk;
+  uint32_t* ci = cand_idx + (size_t)row * Nc_cap;
+  uint32_t* ck = cand_key + (size_t)row * Nc_cap;
   for (int i = 0; i < 8; ++i) {
     int j = j0 + tid * 8 + i;
     if (kind[i] == 1) dl[db++] = (uint32_t)j;
-    else if (kind[i] == 2) cl[cb++] = (uint32_t)j;
-  }
-  if (tid == 0) {
-    def_cnt[cidx] = td;
-    cand_cnt[cidx] = tc;
+    else if (kind[i] == 2) {
+      ci[cb] = (uint32_t)j;
+      ck[cb++] = key[i] & ((1u << kHistShift) - 1u);
+    }
   }
 }
 
-// One workgroup per row.  Chooses `need` candidates by (key desc, index asc)
-// and merges the per-chunk lists into the ascending output row.  Candidate
-// lists are ascending within a chunk and chunks are in index order, so among
-// candidates with the threshold key the lowest indices are simply the first
-// ones met in chunk order.
-__device__ __forceinline__ uint32_t cand_key(const float* srow, uint32_t j) {
-  return score_key(srow[j]) & ((1u << kHistShift) - 1u);
-}
+// One workgroup (1024 threads) per row: picks the missing entries among the
+// candidates by (key desc, index asc) - an exact radix select on the low key
+// bits, then, for keys equal to the threshold, on the inverted index - and
+// writes the selected set sorted ascending (bitonic sort in LDS).
+constexpr int FIN_THREADS = 1024;
 
-__global__ void __launch_bounds__(256) finalize_kernel(
+__global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk, int n_chunks,
-    const uint32_t* __restrict__ def_cnt, const uint32_t* __restrict__ cand_cnt,
-    const uint32_t* __restrict__ def_list, const uint32_t* __restrict__ cand_list,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk,
+    const uint32_t* __restrict__ counts, const uint32_t* __restrict__ def_list,
+    const uint32_t* __restrict__ cand_idx, const uint32_t* __restrict__ cand_key,
     int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
-  __shared__ uint32_t ckey[kFinalCandLds];  // low key bits of the candidates
+  __shared__ uint32_t ckey[kFinalCandLds];
+  __shared__ uint32_t cidx[kFinalCandLds];
+  __shared__ uint32_t outl[8192];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[8];
-  __shared__ uint32_t coff[kMaxChunks], doff[kMaxChunks], soff[kMaxChunks], eqoff[kMaxChunks];
-  __shared__ uint32_t ngt[kMaxChunks], neq[kMaxChunks];
+  __shared__ uint32_t sh[32];
   const int row = blockIdx.x, b = row / T, t = row % T;
   const int tid = threadIdx.x;
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
@@ -516,160 +551,78 @@ __global__ void __launch_bounds__(256) finalize_kernel(
     if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
   }
   if (nsel == 0) return;
-  const uint32_t* dc = def_cnt + (size_t)row * n_chunks;
-  const uint32_t* cc = cand_cnt + (size_t)row * n_chunks;
-  const uint32_t* dlists = def_list + (size_t)row * n_chunks * kChunk;
-  const uint32_t* clists = cand_list + (size_t)row * n_chunks * kChunk;
-
-  uint32_t tot_c = 0, tot_d = 0;
-  for (int base = 0; base < n_chunks; base += blockDim.x) {
-    int c = base + tid;
-    uint32_t vc = c < n_chunks ? cc[c] : 0, vd = c < n_chunks ? dc[c] : 0;
-    uint32_t tc, td;
-    uint32_t oc = block_excl_scan(vc, sh, tc);
-    uint32_t od = block_excl_scan(vd, sh, td);
-    if (c < n_chunks) {
-      coff[c] = tot_c + oc;
-      doff[c] = tot_d + od;
-    }
-    tot_c += tc;
-    tot_d += td;
-  }
-  __syncthreads();
-  const uint32_t need = (uint32_t)nsel - tot_d;  // candidates still to take (<= tot_c)
-
-  // threshold on the low key bits of the candidates
-  RadixResult rk{0u, 0u, need, true};
-  if (need > 0 && need < tot_c) {
-    if (tot_c <= (uint32_t)kFinalCandLds) {
-      for (int c = 0; c < n_chunks; ++c)
-        for (uint32_t i = tid; i < cc[c]; i += blockDim.x)
-          ckey[coff[c] + i] = cand_key(srow, clists[(size_t)c * kChunk + i]);
-      __syncthreads();
-      rk = radix_select_u32(ckey, (int)tot_c, need, hist, sh);
-    } else {
-      // more candidates than LDS holds (heavy ties): the same select with the
-      // keys re-read from the score row on every pass
-      rk = RadixResult{0u, 0u, need, false};
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
-        __syncthreads();
-        for (int c = 0; c < n_chunks; ++c)
-          for (uint32_t i = tid; i < cc[c]; i += blockDim.x) {
-            uint32_t x = cand_key(srow, clists[(size_t)c * kChunk + i]);
-            if ((x & rk.mask) == rk.prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
-          }
-        __syncthreads();
-        if (tid == 0) {
-          uint32_t cum = 0;
-          int d = 255;
-          for (; d > 0; --d) {
-            if (cum + hist[d] >= rk.remaining) break;
-            cum += hist[d];
-          }
-          sh[0] = d;
-          sh[1] = cum;
-          sh[2] = hist[d];
-        }
-        __syncthreads();
-        uint32_t d = sh[0], cum = sh[1], cnt = sh[2];
-        __syncthreads();
-        rk.remaining -= cum;
-        rk.prefix |= d << shift;
-        rk.mask |= 255u << shift;
-        if (cnt == rk.remaining) {
-          rk.all_eq = true;
-          break;
-        }
+  const uint32_t n_def = counts[2 * row], n_cand = counts[2 * row + 1];
+  const uint32_t need = (uint32_t)nsel - n_def;  // <= n_cand
+  const uint32_t* dl = def_list + (size_t)row * topk;
+  const uint32_t* gci = cand_idx + (size_t)row * Nc_cap;
+  const uint32_t* gck = cand_key + (size_t)row * Nc_cap;
+  for (uint32_t i = tid; i < n_def; i += blockDim.x) outl[i] = dl[i];
+  if (need > 0) {
+    const bool in_lds = n_cand <= (uint32_t)kFinalCandLds;
+    if (in_lds) {
+      for (uint32_t i = tid; i < n_cand; i += blockDim.x) {
+        ckey[i] = gck[i];
+        cidx[i] = gci[i];
       }
     }
-  }
-  const bool take_all = need >= tot_c;
-  // per chunk: candidates above the threshold and equal to it
-  for (int c = tid; c < n_chunks; c += blockDim.x) {
-    uint32_t g = 0, e = 0;
-    if (need > 0 && !take_all) {
-      const uint32_t* cl = clists + (size_t)c * kChunk;
-      for (uint32_t i = 0; i < cc[c]; ++i) {
-        uint32_t x = cand_key(srow, cl[i]) & rk.mask;
-        g += x > rk.prefix;
-        e += x == rk.prefix;
+    __syncthreads();
+    auto key_at = [&](uint32_t i) -> uint32_t { return in_lds ? ckey[i] : gck[i]; };
+    auto idx_at = [&](uint32_t i) -> uint32_t { return in_lds ? cidx[i] : gci[i]; };
+    RadixResult rk{0u, 0u, need, true};
+    RadixResult ri{0u, 0u, 0u, true};
+    bool tie_break = false;
+    if (need < n_cand) {
+      rk = radix_select([&](int i) { return key_at(i); }, (int)n_cand, need, hist, sh);
+      if (!rk.all_eq) {
+        // rk.remaining of the candidates whose key equals rk.prefix: lowest
+        // indices first, i.e. the largest inverted indices
+        tie_break = true;
+        ri = radix_select([&](int i) { return key_at(i) == rk.prefix ? ~idx_at(i) : 0u; },
+                          (int)n_cand, rk.remaining, hist, sh);
       }
     }
-    ngt[c] = g;
-    neq[c] = e;
-  }
-  __syncthreads();
-  // equal-key candidates are taken in index order: chunk offsets of them
-  uint32_t run_e = 0;
-  for (int base = 0; base < n_chunks; base += blockDim.x) {
-    int c = base + tid;
-    uint32_t te;
-    uint32_t o = block_excl_scan(c < n_chunks ? neq[c] : 0u, sh, te);
-    if (c < n_chunks) eqoff[c] = run_e + o;
-    run_e += te;
-  }
-  __syncthreads();
-  const uint32_t eq_lim = rk.all_eq ? 0xffffffffu : rk.remaining;
-  uint32_t run_s = 0;
-  for (int base = 0; base < n_chunks; base += blockDim.x) {
-    int c = base + tid;
-    uint32_t cnt = 0;
-    if (c < n_chunks) {
-      if (need == 0) cnt = 0;
-      else if (take_all) cnt = cc[c];
-      else {
-        uint32_t te = eqoff[c] < eq_lim ? min(neq[c], eq_lim - eqoff[c]) : 0u;
-        cnt = ngt[c] + te;
-        neq[c] = te;  // now: equal candidates taken from this chunk
-      }
-    }
-    uint32_t tt;
-    uint32_t o = block_excl_scan(cnt, sh, tt);
-    if (c < n_chunks) soff[c] = run_s + o;
-    run_s += tt;
-  }
-  __syncthreads();
-  // merge (thread per chunk): definite and chosen candidates, both ascending
-  for (int c = tid; c < n_chunks; c += blockDim.x) {
-    const uint32_t* dl = dlists + (size_t)c * kChunk;
-    const uint32_t* cl = clists + (size_t)c * kChunk;
-    const uint32_t nd = dc[c], ncn = cc[c];
-    const uint32_t eq_take = take_all ? 0u : neq[c];
-    uint32_t pos = doff[c] + soff[c];
-    uint32_t i = 0, k = 0, eq_seen = 0;
-    auto next_cand = [&]() -> uint32_t {
-      while (need > 0 && k < ncn) {
-        uint32_t j = cl[k];
-        if (take_all) return j;
-        uint32_t x = cand_key(srow, j) & rk.mask;
-        if (x > rk.prefix) return j;
-        if (x == rk.prefix) {
-          if (eq_seen < eq_take) {
-            ++eq_seen;
-            return j;
-          }
-        }
-        ++k;
-      }
-      return 0xffffffffu;
+    // chosen candidates -> output list after the definite ones
+    const uint32_t per = (n_cand + blockDim.x - 1) / blockDim.x;
+    const uint32_t c0 = min(n_cand, tid * per), c1 = min(n_cand, c0 + per);
+    auto chosen = [&](uint32_t i) -> bool {
+      if (need >= n_cand) return true;
+      uint32_t x = key_at(i) & rk.mask;
+      if (x != rk.prefix) return x > rk.prefix;
+      if (!tie_break) return true;
+      return ((~idx_at(i)) & ri.mask) >= ri.prefix;
     };
-    uint32_t cj = next_cand();
-    while (i < nd || cj != 0xffffffffu) {
-      uint32_t dj = i < nd ? dl[i] : 0xffffffffu;
-      uint32_t j;
-      if (dj < cj) {
-        j = dj;
-        ++i;
-      } else {
-        j = cj;
-        ++k;
-        cj = next_cand();
+    uint32_t cnt = 0;
+    for (uint32_t i = c0; i < c1; ++i) cnt += chosen(i);
+    uint32_t tot;
+    uint32_t pos = n_def + block_excl_scan(cnt, sh, tot);
+    for (uint32_t i = c0; i < c1; ++i)
+      if (chosen(i)) outl[pos++] = idx_at(i);
+  }
+  // bitonic sort of outl[0, nsel) padded to a power of two
+  int N = 1;
+  while (N < nsel) N <<= 1;
+  for (int i = nsel + tid; i < N; i += blockDim.x) outl[i] = 0xffffffffu;
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += blockDim.x) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          uint32_t a = outl[i], c = outl[ixj];
+          bool up = (i & k) == 0;
+          if ((a > c) == up) {
+            outl[i] = c;
+            outl[ixj] = a;
+          }
+        }
       }
-      orow[pos] = (int32_t)j;
-      if (sorow) sorow[pos] = srow[j];
-      ++pos;
+      __syncthreads();
     }
+  }
+  for (int i = tid; i < nsel; i += blockDim.x) {
+    uint32_t j = outl[i];
+    orow[i] = (int32_t)j;
+    if (sorow) sorow[i] = srow[j];
   }
 }
 
@@ -689,10 +642,10 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct IdxLayout {
   bool long_rows;
   int n_chunks;
-  size_t scores, hist, def_cnt, cand_cnt, def_list, cand_list, total;
+  size_t scores, hist, counts, def_list, cand_idx, cand_key, total;
 };
 
-static IdxLayout idx_layout(int B, int T, int Nc_cap) {
+static IdxLayout idx_layout(int B, int T, int Nc_cap, int topk) {
   IdxLayout L{};
   const size_t rows = (size_t)B * T;
   L.long_rows = Nc_cap > kShortMax;
@@ -701,16 +654,16 @@ static IdxLayout idx_layout(int B, int T, int Nc_cap) {
   L.scores = off;
   off += align256(rows * (size_t)Nc_cap * 4);
   if (L.long_rows) {
-    L.hist = off;
-    off += align256(rows * kHistBins * 4);
-    L.def_cnt = off;
-    off += align256(rows * L.n_chunks * 4);
-    L.cand_cnt = off;
-    off += align256(rows * L.n_chunks * 4);
+    L.hist = off;  // histogram and counters are contiguous: zeroed together
+    off += rows * kHistBins * 4;
+    L.counts = off;
+    off += align256(rows * 2 * 4);
     L.def_list = off;
-    off += align256(rows * L.n_chunks * (size_t)kChunk * 4);
-    L.cand_list = off;
-    off += align256(rows * L.n_chunks * (size_t)kChunk * 4);
+    off += align256(rows * (size_t)topk * 4);
+    L.cand_idx = off;
+    off += align256(rows * (size_t)Nc_cap * 4);
+    L.cand_key = off;
+    off += align256(rows * (size_t)Nc_cap * 4);
   }
   L.total = off;
   return L;
@@ -719,19 +672,18 @@ static IdxLayout idx_layout(int B, int T, int Nc_cap) {
 size_t indexer_ws_bytes(int B, int T, int H_I, int d_I, int Nc_cap, int topk, csa_dtype_t dt) {
   (void)H_I;
   (void)d_I;
-  (void)topk;
   (void)dt;
-  return idx_layout(B, T, Nc_cap).total;
+  return idx_layout(B, T, Nc_cap, topk).total;
 }
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
-  const IdxLayout L = idx_layout(a.B, a.T, a.Nc_cap);
+  const IdxLayout L = idx_layout(a.B, a.T, a.Nc_cap, a.topk);
   char* ws = (char*)a.ws;
   float* scores = (float*)(ws + L.scores);
   uint32_t* hist = L.long_rows ? (uint32_t*)(ws + L.hist) : nullptr;
   const int rows = a.B * a.T;
   if (L.long_rows) {
-    size_t n = (size_t)rows * kHistBins;
+    size_t n = (size_t)rows * (kHistBins + 2);
     zero_u32_kernel<<<(unsigned)std::min<size_t>((n + 255) / 256, 1024), 256, 0, st>>>(hist, n);
   }
   if (a.Nc_cap == 0) {
@@ -776,15 +728,16 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     select_short_kernel<<<rows, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m,
                                               a.topk, a.idx_out, a.score_out);
   } else {
-    uint32_t* dcnt = (uint32_t*)(ws + L.def_cnt);
-    uint32_t* ccnt = (uint32_t*)(ws + L.cand_cnt);
+    uint32_t* counts = (uint32_t*)(ws + L.counts);
     uint32_t* dl = (uint32_t*)(ws + L.def_list);
-    uint32_t* cl = (uint32_t*)(ws + L.cand_list);
+    uint32_t* ci = (uint32_t*)(ws + L.cand_idx);
+    uint32_t* ck = (uint32_t*)(ws + L.cand_key);
     collect_kernel<<<dim3(L.n_chunks, rows), 256, 0, st>>>(scores, hist, a.q_pos, a.n_cmp, a.T,
-                                                           a.Nc_cap, a.m, a.topk, L.n_chunks,
-                                                           dcnt, ccnt, dl, cl);
-    finalize_kernel<<<rows, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m, a.topk,
-                                          L.n_chunks, dcnt, ccnt, dl, cl, a.idx_out, a.score_out);
+                                                           a.Nc_cap, a.m, a.topk, counts, dl, ci,
+                                                           ck);
+    finalize_kernel<<<rows, FIN_THREADS, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m,
+                                                  a.topk, counts, dl, ci, ck, a.idx_out,
+                                                  a.score_out);
   }
   return hipGetLastError();
 }
