@@ -11,25 +11,18 @@
 // tokens max(0, pos - W + 1) .. pos.  Invalid slots are masked.  One softmax
 // runs over the whole list.
 //
-// bf16 kernel: a work item is (row, split); its 4 waves take 32-key tiles in
-// turn.  A tile of [K | V] rows (512 B each) is loaded with 16-byte coalesced
-// loads into the wave's LDS region, then
-//     S^T (32 keys x 32 heads) = K (32 x 128) . Q^T     (8 MFMA 32x32x16 / head tile)
-//     O^T (128 x 32 heads)    += V^T (128 x 32) . P^T   (8 MFMA / head tile)
-// The S^T accumulator of a lane holds one head and 16 keys, which is exactly
-// the P^T operand of the second product once the k order of that product is
-// permuted to match; V^T fragments are read from LDS element-wise.  Online
-// softmax runs in base 2 with the scale folded in.  The 4 waves merge their
-// (max, sum, O) through LDS; split items write fp32 partials that a combine
-// kernel merges by log-sum-exp.
+// Two bf16 kernels share the tile arithmetic (S^T = K Q^T and O^T += V^T P^T
+// on MFMA with online softmax, V^T from the LDS transpose read):
+//  * prefill (many rows): one row per wave, all heads per wave, key ranges
+//    common to neighbouring rows shared through LDS;
+//  * decode (few rows): the waves of a workgroup split the heads of one row,
+//    split-K across workgroups, partials merged by log-sum-exp in a combine
+//    kernel.
+// fp32 runs a plain per-(row, head) wave kernel.
 #include "common.h"
 
 namespace csa {
 
-constexpr int AT_KT = 32;            // keys per tile
-constexpr int AT_ROW = 256 + 8;      // bf16 per LDS row: [K | V] (D = 128) + 16 B pad
-constexpr int AT_WAVES = 4;
-constexpr int AT_MIN_SPLIT_KEYS = 256;
 
 struct KeyList {
   int n_c;       // compressed positions (topk slots or n_vis)
@@ -68,44 +61,76 @@ __device__ __forceinline__ const Tp* key_row(int p, const KeyList& L, bool dense
   return kv_raw_b + (size_t)r * row_elems;
 }
 
-// ---------------------------------------------------------------- bf16, D = 128
-template <int NH>  // head tiles of 32: H = 32 NH
-__global__ void __launch_bounds__(256) attn_bf16_kernel(
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// LDS transpose read: lane i of each 16-lane group receives element i % 4 of
+// the 8-byte chunks whose addresses lanes i/4 + 4 v (v = 0..3) supplied.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+// ---------------------------------------------------------------- bf16 prefill
+// Many query rows: a workgroup owns PF_WAVES consecutive rows of one
+// sequence, one per wave, and each wave owns all heads of its row.
+//  * phase A - key ranges shared by the rows (HCA: the compressed entries;
+//    always: the union of the rows' windows) go through LDS once per
+//    workgroup; each wave masks keys outside its own row's visibility;
+//  * phase B - CSA only: each wave gathers its own selected compressed rows
+//    into a private LDS tile (the index row is staged in LDS first).
+// Per wave and 32-key tile: S^T = K Q^T (NH x 8 MFMA 32x32x16) and
+// O^T += V^T P^T (4 x NH x 2 MFMA); V^T fragments come from the LDS transpose
+// read, two reads of 4 keys each per operand.  The running maximum is only
+// raised when a tile exceeds it by more than 2^8 (the final normalisation
+// makes the result independent of the maximum used), so most tiles skip the
+// rescale of O.  The next tile is loaded into registers while the current one
+// is computed.
+constexpr int PF_KT = 32;
+constexpr int PF_ROW = 256 + 16;     // bf16 per LDS row (544 B: conflict-free reads)
+constexpr int PF_WAVES = 4;
+constexpr int PF_IDX_MAX = 2048;     // index slots per wave staged in LDS
+constexpr float PF_RESCALE = 8.0f;   // log2 headroom before the maximum is raised
+
+template <int NH>  // H = 32 NH
+__global__ void __launch_bounds__(64 * PF_WAVES) attn_pf_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv_cmp,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
-    int R_cap, bool dense, float scale_log2, int n_split, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int H = 32 * NH, D = 128;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    int R_cap, bool dense, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int H = 32 * NH, D = 128, NT = 64 * PF_WAVES;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[(1 + PF_WAVES) * PF_KT * PF_ROW];
+  __shared__ int idx_all[PF_WAVES][PF_IDX_MAX];
+  uint16_t* shared_tile = smem;                                  // [PF_KT][PF_ROW]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int item = blockIdx.x;
-  const int rowi = item / n_split, split = item % n_split;
-  const int b = rowi / T, t = rowi % T;
-  const int64_t pos = q_pos[b] + t;
-  const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
-  const int nk = L.n_c + L.n_w;
-  int per = (nk + n_split - 1) / n_split;
-  per = (per + AT_KT - 1) / AT_KT * AT_KT;
-  const int kb = min(nk, split * per), ke = min(nk, kb + per);
-  const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
+  uint16_t* priv_tile = smem + (1 + wave) * PF_KT * PF_ROW;      // phase B, per wave
+  int* idx_s = idx_all[wave];
+  const int h2 = lane >> 5, l32 = lane & 31;
+
+  const int tiles_per_b = (T + PF_WAVES - 1) / PF_WAVES;
+  const int b = blockIdx.x / tiles_per_b;
+  const int t0 = (blockIdx.x % tiles_per_b) * PF_WAVES;
+  const int t = t0 + wave;
+  const bool active = t < T;
+  const int t_last = min(T - 1, t0 + PF_WAVES - 1);
+  const int64_t qp = q_pos[b];
+  const int64_t pos = qp + t, pos_first = qp + t0, pos_last = qp + t_last;
+  const int32_t ncb = n_cmp ? n_cmp[b] : 0;
+  const int64_t rbase = raw_base[b];
   const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
   const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
-  const int64_t rbase = raw_base[b];
+  const size_t rowi = (size_t)b * T + (active ? t : t_last);
 
-  uint16_t* tile = smem + wave * (AT_KT * AT_ROW);
-  __shared__ int valid_s[AT_WAVES][AT_KT];
+  // this row's visibility
+  const int nv_me = dense ? n_visible(pos, ncb, m, Nc_cap) : 0;
+  const int64_t w_lo = window > 0 ? (pos - window + 1 < 0 ? 0 : pos - window + 1) : 1;
+  const int64_t w_hi = window > 0 ? pos : 0;   // window empty when w_lo > w_hi
 
-  // Q^T fragments: head tile ht, k-step s: lane holds q[h = 32 ht + lane%32]
-  // dims 16 s + 8 (lane / 32) .. + 8
   bf16x8 qf[NH][8];
   {
-    const uint16_t* qrow = q + (size_t)rowi * H * D;
+    const uint16_t* qr = q + rowi * H * D;
     for (int ht = 0; ht < NH; ++ht)
       for (int s = 0; s < 8; ++s)
-        qf[ht][s] = *(const bf16x8*)(qrow + (size_t)(32 * ht + (lane & 31)) * D + 16 * s +
-                                     8 * (lane >> 5));
+        qf[ht][s] = *(const bf16x8*)(qr + (size_t)(32 * ht + l32) * D + 16 * s + 8 * h2);
   }
   f32x16 o[4][NH];
   for (int dt = 0; dt < 4; ++dt)
@@ -117,132 +142,173 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(
     lrun[ht] = 0.0f;
   }
 
-  const int ntiles = (ke - kb + AT_KT - 1) / AT_KT;
-  const int col = lane & 31;  // 16-byte column of the 512-byte row
-  for (int ti = wave; ti < ntiles; ti += AT_WAVES) {
-    const int p0 = kb + ti * AT_KT;
-    // ---- load: lane covers rows 2 i + lane/32, column `col`
-    for (int i = 0; i < AT_KT / 2; ++i) {
-      const int rr = 2 * i + (lane >> 5);
-      const int p = p0 + rr;
-      const uint16_t* src = p < ke ? key_row(p, L, dense, idx_row, kvc_b, Nc_cap, kvr_b, R_cap,
-                                             rbase, 2 * D)
-                                   : nullptr;
-      u32x4 v = {0, 0, 0, 0};
-      if (src) v = *(const u32x4*)(src + 8 * col);
-      *(u32x4*)(tile + rr * AT_ROW + 8 * col) = v;
-      if (col == 0) valid_s[wave][rr] = src != nullptr;
-    }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    // ---- S^T = K Q^T
+  // transpose-read addresses (element offsets inside a tile): lane j of a
+  // 16-lane group supplies key row 16 ks + 4 h' + j/4 (+ 8 for the second
+  // read), dims 32 dt + 16 (group & 1) + 4 (j & 3) of the V half.
+  const int gg = lane >> 4, jj = lane & 15;
+  const int tr_off = (4 * (gg >> 1) + (jj >> 2)) * PF_ROW + D + 16 * (gg & 1) + 4 * (jj & 3);
+
+  // One tile for this wave: vmask bit k = key k of the tile is attended.
+  auto compute = [&](const uint16_t* tl, uint32_t vmask) {
     f32x16 sacc[NH];
     for (int ht = 0; ht < NH; ++ht)
       for (int r = 0; r < 16; ++r) sacc[ht][r] = 0.0f;
+    const uint16_t* krow = tl + l32 * PF_ROW + 8 * h2;
     for (int s = 0; s < 8; ++s) {
-      bf16x8 kf = *(const bf16x8*)(tile + (lane & 31) * AT_ROW + 16 * s + 8 * (lane >> 5));
+      const bf16x8 kf = *(const bf16x8*)(krow + 16 * s);
       for (int ht = 0; ht < NH; ++ht)
         sacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ht][s], sacc[ht], 0, 0, 0);
     }
-    // ---- online softmax (base 2); lane: head 32 ht + lane%32, keys
-    // kr(r) = 8 (r/4) + 4 (lane/32) + r%4
-    bool kval[16];
-    for (int r = 0; r < 16; ++r) kval[r] = valid_s[wave][8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] != 0;
+    // keys of register r: 8 (r/4) + 4 h2 + r%4
+    bool raise = false;
+    float mx[NH];
+    for (int ht = 0; ht < NH; ++ht) {
+      float x = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const float sv = ((vmask >> kr) & 1u) ? sacc[ht][r] * scale_log2 : -INFINITY;
+        sacc[ht][r] = sv;
+        x = fmaxf(x, sv);
+      }
+      x = fmaxf(x, __shfl_xor(x, 32, 64));
+      mx[ht] = x;
+      raise |= x > mrun[ht] + PF_RESCALE;
+    }
+    if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
+      for (int ht = 0; ht < NH; ++ht) {
+        const bool up = mx[ht] > mrun[ht] + PF_RESCALE;
+        const float corr = up ? __builtin_amdgcn_exp2f(mrun[ht] - mx[ht]) : 1.0f;
+        if (up) mrun[ht] = mx[ht];
+        lrun[ht] *= corr;
+        for (int dt = 0; dt < 4; ++dt)
+          for (int r = 0; r < 16; ++r) o[dt][ht][r] *= corr;
+      }
+    }
     bf16x8 pf[NH][2];
     for (int ht = 0; ht < NH; ++ht) {
-      float mx = -INFINITY;
-      for (int r = 0; r < 16; ++r) {
-        float sv = kval[r] ? sacc[ht][r] * scale_log2 : -INFINITY;
-        sacc[ht][r] = sv;
-        mx = fmaxf(mx, sv);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrun[ht], mx);
-      const float muse = mnew == -INFINITY ? 0.0f : mnew;
-      const float corr = exp2f(mrun[ht] - muse);
+      const float muse = mrun[ht] == -INFINITY ? 0.0f : mrun[ht];
       float ps = 0.0f;
       for (int r = 0; r < 16; ++r) {
-        float pv = exp2f(sacc[ht][r] - muse);
+        const float pv = __builtin_amdgcn_exp2f(sacc[ht][r] - muse);
         ps += pv;
         sacc[ht][r] = pv;
       }
       ps += __shfl_xor(ps, 32, 64);
-      lrun[ht] = lrun[ht] * corr + ps;
-      mrun[ht] = mnew;
-      for (int dt = 0; dt < 4; ++dt)
-        for (int r = 0; r < 16; ++r) o[dt][ht][r] *= corr;
+      lrun[ht] += ps;
       for (int ks = 0; ks < 2; ++ks)
         for (int e = 0; e < 8; ++e) pf[ht][ks][e] = (__bf16)sacc[ht][8 * ks + e];
     }
-    // ---- O^T += V^T P^T.  k slot (8 half + e) of step ks is key
-    // 16 ks + 8 (e / 4) + 4 half + e % 4 for both operands.
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = 32 * dt + (lane & 31);
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vf;
-        for (int e = 0; e < 8; ++e) {
-          const int key = 16 * ks + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          vf[e] = __builtin_bit_cast(__bf16, tile[key * AT_ROW + D + d]);
-        }
+    for (int ks = 0; ks < 2; ++ks)
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint16_t* tp = tl + tr_off + 16 * ks * PF_ROW + 32 * dt;
+        const u32x2 v1 = __builtin_bit_cast(u32x2, lds_read_tr16(tp));
+        const u32x2 v2 = __builtin_bit_cast(u32x2, lds_read_tr16(tp + 8 * PF_ROW));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{v1[0], v1[1], v2[0], v2[1]});
         for (int ht = 0; ht < NH; ++ht)
           o[dt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ht][ks], o[dt][ht], 0, 0, 0);
       }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  }
+  };
 
-  // ---- merge the 4 waves through LDS (reusing the tile buffers)
-  __syncthreads();
-  float* mb = (float*)smem;           // [H]
-  float* lb = mb + H;                 // [H]
-  float* ob = lb + H;                 // [H][D]
-  for (int w = 0; w < AT_WAVES; ++w) {
-    if (wave == w) {
-      for (int ht = 0; ht < NH; ++ht) {
-        const int h = 32 * ht + (lane & 31);
-        float m_prev = w ? mb[h] : -INFINITY, l_prev = w ? lb[h] : 0.0f;
-        float mnew = fmaxf(m_prev, mrun[ht]);
-        float muse = mnew == -INFINITY ? 0.0f : mnew;
-        float c_prev = exp2f(m_prev - muse), c_me = exp2f(mrun[ht] - muse);
-        for (int dt = 0; dt < 4; ++dt)
-          for (int r = 0; r < 16; ++r) {
-            const int d = 32 * dt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            float prev = w ? ob[h * D + d] : 0.0f;
-            ob[h * D + d] = prev * c_prev + o[dt][ht][r] * c_me;
-          }
-        if (lane < 32) {
-          mb[h] = mnew;
-          lb[h] = l_prev * c_prev + lrun[ht] * c_me;
-        }
+  // ---------------- phase A: shared contiguous segments
+  // segment 0 (HCA): entries [0, nv_max); segment 1: window tokens
+  // [lo_first, pos_last].  Tile key k of segment 0 tile at e0 is entry e0 + k.
+  const int nv_max = dense ? n_visible(pos_last, ncb, m, Nc_cap) : 0;
+  int64_t win_first = pos_first - window + 1;
+  if (win_first < 0) win_first = 0;
+  const int n_win = window > 0 ? (int)(pos_last - win_first + 1) : 0;
+  const int tiles0 = (nv_max + PF_KT - 1) / PF_KT;
+  const int tiles1 = (n_win + PF_KT - 1) / PF_KT;
+  const int ntA = tiles0 + tiles1;
+  constexpr int CHA = PF_KT * 32 / NT;  // 16-byte chunks per thread per shared tile
+  const int colA = tid & 31;
+  u32x4 pfa[CHA];
+  auto issueA = [&](int ti) {
+    for (int i = 0; i < CHA; ++i) {
+      const int rr = i * (NT / 32) + (tid >> 5);
+      const uint16_t* src = nullptr;
+      if (ti < tiles0) {
+        const int e = ti * PF_KT + rr;
+        if (e < nv_max) src = kvc_b + (size_t)e * 2 * D;
+      } else {
+        const int64_t tok = win_first + (int64_t)(ti - tiles0) * PF_KT + rr;
+        const int64_t r = tok - rbase;
+        if (tok <= pos_last && r >= 0 && r < R_cap) src = kvr_b + (size_t)r * 2 * D;
       }
+      pfa[i] = src ? *(const u32x4*)(src + 8 * colA) : u32x4{0, 0, 0, 0};
+    }
+  };
+  if (ntA > 0) issueA(0);
+  for (int ti = 0; ti < ntA; ++ti) {
+    __syncthreads();
+    for (int i = 0; i < CHA; ++i) {
+      const int rr = i * (NT / 32) + (tid >> 5);
+      *(u32x4*)(shared_tile + rr * PF_ROW + 8 * colA) = pfa[i];
     }
     __syncthreads();
+    if (ti + 1 < ntA) issueA(ti + 1);
+    // this wave's mask over the tile's 32 keys (key = lane & 31)
+    bool ok;
+    if (ti < tiles0) {
+      ok = ti * PF_KT + l32 < nv_me;
+    } else {
+      const int64_t tok = win_first + (int64_t)(ti - tiles0) * PF_KT + l32;
+      const int64_t r = tok - rbase;
+      ok = tok >= w_lo && tok <= w_hi && r >= 0 && r < R_cap;
+    }
+    const uint32_t vmask = (uint32_t)__ballot(ok);
+    if (active && vmask) compute(shared_tile, vmask);
   }
-  // ---- write: final (n_split == 1) or partial
-  if (n_split == 1) {
-    for (int i = tid; i < H * D / 4; i += blockDim.x) {
-      const int h = (4 * i) / D, d = (4 * i) % D;
-      const float l = lb[h];
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      uint16_t* orow = out + ((size_t)rowi * H + h) * D + d;
-      uint32_t lo = (uint32_t)f32_to_bf16(ob[h * D + d] * inv) |
-                    ((uint32_t)f32_to_bf16(ob[h * D + d + 1] * inv) << 16);
-      uint32_t hi = (uint32_t)f32_to_bf16(ob[h * D + d + 2] * inv) |
-                    ((uint32_t)f32_to_bf16(ob[h * D + d + 3] * inv) << 16);
-      *(u32x2*)orow = u32x2{lo, hi};
-    }
-    if (lse)
-      for (int h = tid; h < H; h += blockDim.x) {
-        const float l = lb[h];
-        lse[(size_t)rowi * H + h] = l > 0.0f ? (mb[h] + __log2f(l)) * kLn2 : -INFINITY;
+
+  // ---------------- phase B: this wave's selected compressed entries
+  if (!dense && active && topk > 0) {
+    const int32_t* idx_row = idx + rowi * topk;
+    const bool stage = topk <= PF_IDX_MAX;
+    if (stage)
+      for (int i = lane; i < topk; i += 64) idx_s[i] = idx_row[i];
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    const int ntB = (topk + PF_KT - 1) / PF_KT;
+    const int colB = lane & 31;
+    u32x4 pfb[PF_KT / 2];
+    auto slot = [&](int p) -> int {
+      if (p >= topk) return -1;
+      const int j = stage ? idx_s[p] : idx_row[p];
+      return (j < 0 || j >= Nc_cap) ? -1 : j;
+    };
+    auto issueB = [&](int ti) {
+      for (int i = 0; i < PF_KT / 2; ++i) {
+        const int j = slot(ti * PF_KT + 2 * i + h2);
+        pfb[i] = j >= 0 ? *(const u32x4*)(kvc_b + (size_t)j * 2 * D + 8 * colB) : u32x4{0, 0, 0, 0};
       }
-  } else {
-    float* po = part_o + (size_t)item * H * D;
-    for (int i = tid; i < H * D / 4; i += blockDim.x)
-      *(f32x4*)(po + 4 * i) = *(const f32x4*)(ob + 4 * i);
-    for (int h = tid; h < H; h += blockDim.x) {
-      part_ml[((size_t)item * H + h) * 2 + 0] = mb[h];
-      part_ml[((size_t)item * H + h) * 2 + 1] = lb[h];
+    };
+    issueB(0);
+    for (int ti = 0; ti < ntB; ++ti) {
+      for (int i = 0; i < PF_KT / 2; ++i)
+        *(u32x4*)(priv_tile + (2 * i + h2) * PF_ROW + 8 * colB) = pfb[i];
+      const uint32_t vmask = (uint32_t)__ballot(slot(ti * PF_KT + l32) >= 0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (ti + 1 < ntB) issueB(ti + 1);
+      if (vmask) compute(priv_tile, vmask);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
+  }
+
+  // ---------------- output: lane holds head 32 ht + l32, dims
+  // 32 dt + 8 (r/4) + 4 h2 + r%4
+  if (!active) return;
+  for (int ht = 0; ht < NH; ++ht) {
+    const int h = 32 * ht + l32;
+    const float inv = lrun[ht] > 0.0f ? 1.0f / lrun[ht] : 0.0f;
+    uint16_t* orow = out + (rowi * H + h) * D;
+    for (int dt = 0; dt < 4; ++dt)
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = 32 * dt + 8 * rq + 4 * h2;
+        const f32x16& a = o[dt][ht];
+        uint32_t lo = (uint32_t)f32_to_bf16(a[4 * rq] * inv) | ((uint32_t)f32_to_bf16(a[4 * rq + 1] * inv) << 16);
+        uint32_t hi = (uint32_t)f32_to_bf16(a[4 * rq + 2] * inv) | ((uint32_t)f32_to_bf16(a[4 * rq + 3] * inv) << 16);
+        *(u32x2*)(orow + d) = u32x2{lo, hi};
+      }
+    if (lse && h2 == 0)
+      lse[rowi * H + h] = lrun[ht] > 0.0f ? (mrun[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
   }
 }
 
@@ -263,11 +329,6 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(
 constexpr int DC_KT = 64;                // keys per tile
 constexpr int DC_ROW = 256 + 16;         // bf16 per LDS row (544 B: conflict-free reads)
 constexpr int DC_IDX_MAX = 4096;         // index slots staged in LDS per work item
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-}
 
 template <int WAVES>  // H = 16 WAVES
 __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
@@ -538,12 +599,7 @@ static int attn_splits(int rows, int keys_per_row, int H) {
     s = s < smax ? s : smax;
     return s < 1 ? 1 : s;
   }
-  // enough work items to fill the chip; every split keeps >= 256 keys
-  if (rows >= 1024 || keys_per_row <= AT_MIN_SPLIT_KEYS) return 1;
-  int s = (1024 + rows - 1) / rows;
-  int smax = (keys_per_row + AT_MIN_SPLIT_KEYS - 1) / AT_MIN_SPLIT_KEYS;
-  if (smax > CB_MAX_SPLIT) smax = CB_MAX_SPLIT;
-  return s < smax ? s : smax;
+  return 1;  // the prefill kernel has enough rows to fill the chip
 }
 
 size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row) {
@@ -567,7 +623,6 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   const int n_split = attn_splits(rows, keys, a.H);
   float* part_o = (float*)a.ws;
   float* part_ml = part_o ? part_o + (size_t)rows * n_split * a.H * a.D : nullptr;
-  const size_t lds = (size_t)AT_WAVES * AT_KT * AT_ROW * sizeof(uint16_t);
   const unsigned grid = (unsigned)(rows * n_split);
   if (use_decode_kernel(rows, a.H)) {
     if (a.H == 64)
@@ -580,16 +635,19 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
-  } else if (a.H == 64)
-    attn_bf16_kernel<2><<<grid, 256, lds, st>>>(
-        (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,
-        a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,
-        n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
-  else
-    attn_bf16_kernel<1><<<grid, 256, lds, st>>>(
-        (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,
-        a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,
-        n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+  } else {
+    const unsigned g = (unsigned)(a.B * ((a.T + PF_WAVES - 1) / PF_WAVES));
+    if (a.H == 64)
+      attn_pf_kernel<2><<<g, 64 * PF_WAVES, 0, st>>>(
+          (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
+          a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
+          scale_log2, (uint16_t*)a.out, a.lse);
+    else
+      attn_pf_kernel<1><<<g, 64 * PF_WAVES, 0, st>>>(
+          (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
+          a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
+          scale_log2, (uint16_t*)a.out, a.lse);
+  }
   if (n_split > 1)
     combine_kernel<CSA_DT_BF16><<<dim3(rows, a.H / CB_HEADS), 256, 0, st>>>(
         part_o, part_ml, n_split, a.H, a.D, a.out, a.lse);
