@@ -240,81 +240,72 @@ def step_hca(w, st):
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, budget_s=12.0):
-    """Time the oracle on a bounded sample of the workload on the host cores."""
+    """Time the oracle on a bounded sample of the workload on the host cores.
+
+    The oracle parallelises over query rows (and over tokens inside the
+    compressor), so samples are batched: 16 consecutive query rows per call
+    for prefill, 8 sequences per call for decode."""
     from oracle import oracle as orc
     cores = orc.num_threads()
     rng = np.random.default_rng(0)
+    d = gen.Draw(w.seed + 999)
     if w.kind == "csa_prefill":
-        # sample query tokens spread over the sequence; per token the oracle
-        # runs its share of the compressor (one entry per m tokens, both
-        # compressors), the indexer row and the attention row
-        d = gen.Draw(w.seed + 999)
-        dm, S = w.d_model, w.T
-        x = gen.host_bits(gen.store(d.normal(1, 2 * w.m, dm), w.dt))
+        dm, S, blk = w.d_model, w.T, 16
         wk, wg = (gen.host_bits(t) for t in gen.compressor_weights(d, dm, 2 * w.D, w.dt))
         wik, wig = (gen.host_bits(t) for t in gen.compressor_weights(d, dm, w.d_I, w.dt))
         kv_cmp = gen.host_bits(gen.store(d.normal(1, w.n_cmp, 2 * w.D), w.dt))
         kv_raw = gen.host_bits(gen.store(d.normal(1, S, 2 * w.D), w.dt))
         k_idx = gen.host_bits(gen.store(d.normal(1, w.n_cmp, w.d_I), w.idx_dt))
-        n_tok = 0
-        t_comp = t_idx = t_att = 0.0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            tt = int(rng.integers(0, S))
-            q_idx = gen.host_bits(gen.store(d.normal(1, 1, w.H_I, w.d_I), w.idx_dt))
-            w_idx = d.normal(1, 1, w.H_I).numpy()
-            q = gen.host_bits(gen.store(d.normal(1, 1, w.H, w.D), w.dt))
+        n_tok, tot = 0, 0.0
+        while tot < budget_s:
+            s0 = int(rng.integers(0, S - blk + 1))
+            x = gen.host_bits(gen.store(d.normal(1, blk, dm), w.dt))
+            q_idx = gen.host_bits(gen.store(d.normal(1, blk, w.H_I, w.d_I), w.idx_dt))
+            w_idx = d.normal(1, blk, w.H_I).numpy()
+            q = gen.host_bits(gen.store(d.normal(1, blk, w.H, w.D), w.dt))
             a = time.perf_counter()
-            if n_tok % w.m == 0:       # one entry of each compressor per m tokens
-                orc.compress(x, wk, wg, w.m, w.overlap, 0, 2, want_state=False)
-                orc.compress(x, wik, wig, w.m, w.overlap, 0, 2, want_state=False)
-            b = time.perf_counter()
-            idx = orc.indexer_topk(q_idx, w_idx, k_idx, w.m, w.topk, tt, w.n_cmp)[0]
-            c = time.perf_counter()
-            orc.sparse_attn(q, kv_cmp, idx, kv_raw, w.window, tt, 0)
-            e = time.perf_counter()
-            t_comp += b - a
-            t_idx += c - b
-            t_att += e - c
-            n_tok += 1
-        tot = t_comp + t_idx + t_att
+            # the block's share of both compressors (blk / m entries each) ...
+            orc.compress(x, wk, wg, w.m, w.overlap, s0, w.n_cmp, want_state=False)
+            orc.compress(x, wik, wig, w.m, w.overlap, s0, w.n_cmp, want_state=False)
+            # ... its indexer rows and attention rows
+            idx = orc.indexer_topk(q_idx, w_idx, k_idx, w.m, w.topk, s0, w.n_cmp)[0]
+            orc.sparse_attn(q, kv_cmp, idx, kv_raw, w.window, s0, 0)
+            tot += time.perf_counter() - a
+            n_tok += blk
         return {"value": n_tok / tot, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-                "sample": "%d query tokens at uniformly drawn positions of the 8192-token "
-                          "prefill, each with its indexer row and attention row, plus one "
-                          "compressed entry of each compressor per %d tokens" % (n_tok, w.m)}
+                "sample": "%d query tokens in blocks of %d consecutive positions drawn uniformly "
+                          "from the %d-token prefill; per block both compressors over the block, "
+                          "its indexer rows and its attention rows" % (n_tok, blk, S)}
     if w.kind == "csa_decode":
-        d = gen.Draw(w.seed + 999)
-        Bs = 2
+        Bs = 8
+        Ns = min(w.n_cmp, 65536)
         k_idx, k_scale = gen.indexer_keys(d, Bs, w.n_cmp, w.d_I, w.idx_dt)
         q_idx, q_scale, w_idx = gen.indexer_query(d, Bs, 1, w.H_I, w.d_I, w.idx_dt)
-        kv_cmp = gen.host_bits(gen.store(d.normal(Bs, min(w.n_cmp, 65536), 2 * w.D), w.dt))
+        kv_cmp = gen.host_bits(gen.store(d.normal(Bs, Ns, 2 * w.D), w.dt))
         kv_raw = gen.host_bits(gen.store(d.normal(Bs, w.window, 2 * w.D), w.dt))
         q = gen.host_bits(gen.store(d.normal(Bs, 1, w.H, w.D), w.dt))
         kb, ks = gen.host_bits(k_idx), gen.host_bits(k_scale)
         qb, qs, wb = gen.host_bits(q_idx), gen.host_bits(q_scale), w_idx.numpy()
         n_q, tot = 0, 0.0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
+        while tot < budget_s:
             a = time.perf_counter()
             idx = orc.indexer_topk(qb, wb, kb, w.m, w.topk, w.ctx - 1, w.n_cmp, q_scale=qs,
                                    k_scale=ks)[0]
-            idx = np.where(idx >= kv_cmp.shape[1], idx % kv_cmp.shape[1], idx)
+            idx = np.where(idx >= Ns, idx % Ns, idx)
             orc.sparse_attn(q, kv_cmp, idx, kv_raw, w.window, w.ctx - 1, w.ctx - w.window)
             tot += time.perf_counter() - a
             n_q += Bs
         return {"value": n_q / tot, "unit": "queries/s", "cores": cores, "kind": "oracle",
-                "sample": "%d decode queries (indexer over all %d entries + top-%d + "
-                          "attention over %d keys), %d sequences per oracle call"
-                          % (n_q, w.n_cmp, w.topk, w.topk + w.window, Bs)}
+                "sample": "%d decode queries, %d sequences per oracle call: indexer over all %d "
+                          "entries, top-%d, attention over %d keys (the selected rows are read "
+                          "from a %d-entry cache sample)" % (n_q, Bs, w.n_cmp, w.topk,
+                                                             w.topk + w.window, Ns)}
     if w.kind == "hca_prefill":
-        d = gen.Draw(w.seed + 999)
         kv_cmp = gen.host_bits(gen.store(d.normal(1, w.n_cmp, 2 * w.D), w.dt))
         kv_raw = gen.host_bits(gen.store(d.normal(1, w.T + w.window - 1, 2 * w.D), w.dt))
         q0 = w.ctx - w.T
-        n_tok, tot = 0, 0.0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            Ts = 16
+        n_tok, tot, Ts = 0, 0.0, 16
+        while tot < budget_s:
             t = int(rng.integers(0, w.T - Ts))
             q = gen.host_bits(gen.store(d.normal(1, Ts, w.H, w.D), w.dt))
             a = time.perf_counter()
@@ -322,7 +313,8 @@ def cpu_baseline(w, budget_s=12.0):
             tot += time.perf_counter() - a
             n_tok += Ts
         return {"value": n_tok / tot, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-                "sample": "%d query tokens of the 4096-token chunk (16 per oracle call)" % n_tok}
+                "sample": "%d query tokens of the %d-token chunk, %d consecutive per oracle call"
+                          % (n_tok, w.T, Ts)}
     return None
 
 
@@ -358,7 +350,7 @@ def measure(name, steps, warmup, with_cpu):
     if w.kind == "csa_prefill":
         if w.dt == gen.BF16:
             ach = attn_flops / (sm["sparse_attn"] / 1e3) / 1e12
-            res["roofline"] = {"bound": "mfma", "kernel": "attn_bf16_kernel",
+            res["roofline"] = {"bound": "mfma", "kernel": "attn_pf_kernel",
                                "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
         else:
@@ -392,7 +384,7 @@ def measure(name, steps, warmup, with_cpu):
         visits = hca_visits(w, w.ctx - w.T)
         flops = visits * w.H * w.D * 4
         ach = flops / step_s / 1e12
-        res["roofline"] = {"bound": "mfma", "kernel": "attn_bf16_kernel (dense)", "achieved": ach,
+        res["roofline"] = {"bound": "mfma", "kernel": "attn_pf_kernel (dense)", "achieved": ach,
                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
         res["work"] = {"attn_gflop": flops / 1e9}
