@@ -17,6 +17,11 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "attend.hip"]
+# Per-source extra flags.  attend.hip keeps its MFMA accumulators in VGPRs: the
+# attention loops rescale the output accumulator conditionally, and with the
+# accumulators in AGPRs the compiler round-trips all of them through VGPRs
+# on every key tile.
+EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -25,7 +30,7 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = ["hipcc", *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -70,48 +70,57 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
 }
 
 // ---------------------------------------------------------------- bf16 prefill
-// Many query rows: a workgroup owns PF_WAVES consecutive rows of one
-// sequence, one per wave, and each wave owns all heads of its row.
+// Many query rows: a workgroup owns PF_ROWS consecutive rows of one sequence;
+// each row has H/32 waves, one per 32-head slice (8 waves for H = 64, two per
+// SIMD, so one wave's softmax overlaps another's MFMAs).
 //  * phase A - key ranges shared by the rows (HCA: the compressed entries;
 //    always: the union of the rows' windows) go through LDS once per
-//    workgroup; each wave masks keys outside its own row's visibility;
-//  * phase B - CSA only: each wave gathers its own selected compressed rows
-//    into a private LDS tile (the index row is staged in LDS first).
-// Per wave and 32-key tile: S^T = K Q^T (NH x 8 MFMA 32x32x16) and
-// O^T += V^T P^T (4 x NH x 2 MFMA); V^T fragments come from the LDS transpose
-// read, two reads of 4 keys each per operand.  The running maximum is only
-// raised when a tile exceeds it by more than 2^8 (the final normalisation
-// makes the result independent of the maximum used), so most tiles skip the
-// rescale of O.  The next tile is loaded into registers while the current one
-// is computed.
+//    workgroup (double-buffered, one barrier per tile); each wave masks keys
+//    outside its own row's visibility;
+//  * phase B - CSA only: each row's selected compressed rows are gathered into
+//    that row's LDS tile by the row's waves (the index row is staged first).
+// Per wave and 32-key tile: S^T (32 keys x 32 heads) = K Q^T in 8 MFMA
+// 32x32x16 and O^T (128 dims x 32 heads) += V^T P^T in 8 more; the S^T
+// accumulator is the P^T operand once the second product's k order is
+// permuted to match, and V^T fragments come from the LDS transpose read.
+// K and V halves of a row sit in separate LDS arrays whose strides suit their
+// readers: 272 B for the 16-byte K reads (16 rows hit 16 distinct bank
+// groups), 288 B for the 8-byte transpose reads of V.  The running maximum is
+// only raised when a tile exceeds it by more than 2^8 (the final
+// normalisation makes the result independent of the maximum used).
 constexpr int PF_KT = 32;
-constexpr int PF_ROW = 256 + 16;     // bf16 per LDS row (544 B: conflict-free reads)
-constexpr int PF_WAVES = 4;
-constexpr int PF_IDX_MAX = 2048;     // index slots per wave staged in LDS
+constexpr int PF_KS = 128 + 8;       // bf16 per K row in LDS (272 B)
+constexpr int PF_VS = 128 + 16;      // bf16 per V row in LDS (288 B)
+constexpr int PF_TILE = PF_KT * (PF_KS + PF_VS);
+constexpr int PF_ROWS = 4;           // query rows per workgroup
+constexpr int PF_IDX_MAX = 2048;     // index slots per row staged in LDS
 constexpr float PF_RESCALE = 8.0f;   // log2 headroom before the maximum is raised
 
-template <int NH>  // H = 32 NH
-__global__ void __launch_bounds__(64 * PF_WAVES) attn_pf_kernel(
+template <int NH>  // H = 32 NH: waves per row
+__global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv_cmp,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, bool dense, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int H = 32 * NH, D = 128, NT = 64 * PF_WAVES;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[(1 + PF_WAVES) * PF_KT * PF_ROW];
-  __shared__ int idx_all[PF_WAVES][PF_IDX_MAX];
-  uint16_t* shared_tile = smem;                                  // [PF_KT][PF_ROW]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint16_t* priv_tile = smem + (1 + wave) * PF_KT * PF_ROW;      // phase B, per wave
-  int* idx_s = idx_all[wave];
+  constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH;
+  // phase A uses tiles 0..1 (double buffer); phase B tile r per row
+  constexpr int NTILES = PF_ROWS > 2 ? PF_ROWS : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NTILES * PF_TILE];
+  __shared__ int idx_all[PF_ROWS][PF_IDX_MAX];
+  // the wave index is a scalar so that every per-wave decision below is a
+  // uniform branch
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row_w = wave / NH, hh = wave % NH;     // query row and 32-head slice
   const int h2 = lane >> 5, l32 = lane & 31;
 
-  const int tiles_per_b = (T + PF_WAVES - 1) / PF_WAVES;
+  const int tiles_per_b = (T + PF_ROWS - 1) / PF_ROWS;
   const int b = blockIdx.x / tiles_per_b;
-  const int t0 = (blockIdx.x % tiles_per_b) * PF_WAVES;
-  const int t = t0 + wave;
+  const int t0 = (blockIdx.x % tiles_per_b) * PF_ROWS;
+  const int t = t0 + row_w;
   const bool active = t < T;
-  const int t_last = min(T - 1, t0 + PF_WAVES - 1);
+  const int t_last = min(T - 1, t0 + PF_ROWS - 1);
   const int64_t qp = q_pos[b];
   const int64_t pos = qp + t, pos_first = qp + t0, pos_last = qp + t_last;
   const int32_t ncb = n_cmp ? n_cmp[b] : 0;
@@ -125,93 +134,83 @@ __global__ void __launch_bounds__(64 * PF_WAVES) attn_pf_kernel(
   const int64_t w_lo = window > 0 ? (pos - window + 1 < 0 ? 0 : pos - window + 1) : 1;
   const int64_t w_hi = window > 0 ? pos : 0;   // window empty when w_lo > w_hi
 
-  bf16x8 qf[NH][8];
+  // Q^T operand: head 32 hh + l32, dims 16 s + 8 h2 .. + 8
+  bf16x8 qf[8];
   {
-    const uint16_t* qr = q + rowi * H * D;
-    for (int ht = 0; ht < NH; ++ht)
-      for (int s = 0; s < 8; ++s)
-        qf[ht][s] = *(const bf16x8*)(qr + (size_t)(32 * ht + l32) * D + 16 * s + 8 * h2);
+    const uint16_t* qr = q + (rowi * H + 32 * hh + l32) * D + 8 * h2;
+    for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8*)(qr + 16 * s);
   }
-  f32x16 o[4][NH];
+  f32x16 o[4];
   for (int dt = 0; dt < 4; ++dt)
-    for (int ht = 0; ht < NH; ++ht)
-      for (int r = 0; r < 16; ++r) o[dt][ht][r] = 0.0f;
-  float mrun[NH], lrun[NH];
-  for (int ht = 0; ht < NH; ++ht) {
-    mrun[ht] = -INFINITY;
-    lrun[ht] = 0.0f;
-  }
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+  float mrun = -INFINITY, lrun = 0.0f;
 
-  // transpose-read addresses (element offsets inside a tile): lane j of a
-  // 16-lane group supplies key row 16 ks + 4 h' + j/4 (+ 8 for the second
-  // read), dims 32 dt + 16 (group & 1) + 4 (j & 3) of the V half.
+  // transpose-read offset inside a V tile: lane j of a 16-lane group supplies
+  // key row 16 ks + 4 h' + j/4 (+ 8 for the second read), dims
+  // 32 dt + 16 (group & 1) + 4 (j & 3)
   const int gg = lane >> 4, jj = lane & 15;
-  const int tr_off = (4 * (gg >> 1) + (jj >> 2)) * PF_ROW + D + 16 * (gg & 1) + 4 * (jj & 3);
+  const int tr_off = (4 * (gg >> 1) + (jj >> 2)) * PF_VS + 16 * (gg & 1) + 4 * (jj & 3);
 
-  // One tile for this wave: vmask bit k = key k of the tile is attended.
-  auto compute = [&](const uint16_t* tl, uint32_t vmask) {
-    f32x16 sacc[NH];
-    for (int ht = 0; ht < NH; ++ht)
-      for (int r = 0; r < 16; ++r) sacc[ht][r] = 0.0f;
-    const uint16_t* krow = tl + l32 * PF_ROW + 8 * h2;
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 kf = *(const bf16x8*)(krow + 16 * s);
-      for (int ht = 0; ht < NH; ++ht)
-        sacc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ht][s], sacc[ht], 0, 0, 0);
-    }
-    // keys of register r: 8 (r/4) + 4 h2 + r%4
-    bool raise = false;
-    float mx[NH];
-    for (int ht = 0; ht < NH; ++ht) {
-      float x = -INFINITY;
+  // One tile (K rows at ks_t, V rows at vs_t); vmask bit k: key k attended.
+  auto compute = [&](const uint16_t* ks_t, const uint16_t* vs_t, uint32_t vmask) {
+    f32x16 sacc;
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+    const uint16_t* krow = ks_t + l32 * PF_KS + 8 * h2;
+    for (int s = 0; s < 8; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + 16 * s), qf[s], sacc,
+                                                     0, 0, 0);
+    // keys of register r: 8 (r/4) + 4 h2 + r%4; partial tiles mask, full
+    // tiles skip the per-key work; the scale (> 0) is applied inside the FMA
+    if (vmask != 0xffffffffu) {
       for (int r = 0; r < 16; ++r) {
         const int kr = 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const float sv = ((vmask >> kr) & 1u) ? sacc[ht][r] * scale_log2 : -INFINITY;
-        sacc[ht][r] = sv;
-        x = fmaxf(x, sv);
-      }
-      x = fmaxf(x, __shfl_xor(x, 32, 64));
-      mx[ht] = x;
-      raise |= x > mrun[ht] + PF_RESCALE;
-    }
-    if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
-      for (int ht = 0; ht < NH; ++ht) {
-        const bool up = mx[ht] > mrun[ht] + PF_RESCALE;
-        const float corr = up ? __builtin_amdgcn_exp2f(mrun[ht] - mx[ht]) : 1.0f;
-        if (up) mrun[ht] = mx[ht];
-        lrun[ht] *= corr;
-        for (int dt = 0; dt < 4; ++dt)
-          for (int r = 0; r < 16; ++r) o[dt][ht][r] *= corr;
+        if (!((vmask >> kr) & 1u)) sacc[r] = -INFINITY;
       }
     }
-    bf16x8 pf[NH][2];
-    for (int ht = 0; ht < NH; ++ht) {
-      const float muse = mrun[ht] == -INFINITY ? 0.0f : mrun[ht];
-      float ps = 0.0f;
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[ht][r] - muse);
-        ps += pv;
-        sacc[ht][r] = pv;
-      }
-      ps += __shfl_xor(ps, 32, 64);
-      lrun[ht] += ps;
-      for (int ks = 0; ks < 2; ++ks)
-        for (int e = 0; e < 8; ++e) pf[ht][ks][e] = (__bf16)sacc[ht][8 * ks + e];
+    float x = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+    for (int r = 3; r < 15; r += 2) x = fmaxf(fmaxf(x, sacc[r]), sacc[r + 1]);
+    x = fmaxf(x, sacc[15]);
+    x = fmaxf(x, __shfl_xor(x, 32, 64)) * scale_log2;
+    const bool up = x > mrun + PF_RESCALE;
+    if (__ballot(up)) {
+      const float corr = up ? __builtin_amdgcn_exp2f(mrun - x) : 1.0f;
+      if (up) mrun = x;
+      lrun *= corr;
+      for (int dt = 0; dt < 4; ++dt)
+        for (int r = 0; r < 16; ++r) o[dt][r] *= corr;
     }
+    const float nmuse = mrun == -INFINITY ? 0.0f : -mrun;
+    float ps = 0.0f;
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, nmuse));
+      ps += pv;
+      sacc[r] = pv;
+    }
+    ps += __shfl_xor(ps, 32, 64);
+    lrun += ps;
+    bf16x8 pf[2];
+    for (int ks = 0; ks < 2; ++ks)
+      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)sacc[8 * ks + e];
     for (int ks = 0; ks < 2; ++ks)
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* tp = tl + tr_off + 16 * ks * PF_ROW + 32 * dt;
+        const uint16_t* tp = vs_t + tr_off + 16 * ks * PF_VS + 32 * dt;
         const u32x2 v1 = __builtin_bit_cast(u32x2, lds_read_tr16(tp));
-        const u32x2 v2 = __builtin_bit_cast(u32x2, lds_read_tr16(tp + 8 * PF_ROW));
+        const u32x2 v2 = __builtin_bit_cast(u32x2, lds_read_tr16(tp + 8 * PF_VS));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{v1[0], v1[1], v2[0], v2[1]});
-        for (int ht = 0; ht < NH; ++ht)
-          o[dt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ht][ks], o[dt][ht], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
       }
+  };
+  // LDS stores of one 16-byte chunk of row rr: chunks 0..15 are K, 16..31 V
+  auto put = [&](uint16_t* tile, int rr, int col, const u32x4& v) {
+    if (col < 16)
+      *(u32x4*)(tile + rr * PF_KS + 8 * col) = v;
+    else
+      *(u32x4*)(tile + PF_KT * PF_KS + rr * PF_VS + 8 * (col - 16)) = v;
   };
 
   // ---------------- phase A: shared contiguous segments
   // segment 0 (HCA): entries [0, nv_max); segment 1: window tokens
-  // [lo_first, pos_last].  Tile key k of segment 0 tile at e0 is entry e0 + k.
+  // [win_first, pos_last]
   const int nv_max = dense ? n_visible(pos_last, ncb, m, Nc_cap) : 0;
   int64_t win_first = pos_first - window + 1;
   if (win_first < 0) win_first = 0;
@@ -237,15 +236,14 @@ __global__ void __launch_bounds__(64 * PF_WAVES) attn_pf_kernel(
       pfa[i] = src ? *(const u32x4*)(src + 8 * colA) : u32x4{0, 0, 0, 0};
     }
   };
-  if (ntA > 0) issueA(0);
+  if (ntA > 0) {
+    issueA(0);
+    for (int i = 0; i < CHA; ++i) put(smem, i * (NT / 32) + (tid >> 5), colA, pfa[i]);
+    if (ntA > 1) issueA(1);
+    __syncthreads();
+  }
   for (int ti = 0; ti < ntA; ++ti) {
-    __syncthreads();
-    for (int i = 0; i < CHA; ++i) {
-      const int rr = i * (NT / 32) + (tid >> 5);
-      *(u32x4*)(shared_tile + rr * PF_ROW + 8 * colA) = pfa[i];
-    }
-    __syncthreads();
-    if (ti + 1 < ntA) issueA(ti + 1);
+    uint16_t* cur = smem + (ti & 1) * PF_TILE;
     // this wave's mask over the tile's 32 keys (key = lane & 31)
     bool ok;
     if (ti < tiles0) {
@@ -256,60 +254,72 @@ __global__ void __launch_bounds__(64 * PF_WAVES) attn_pf_kernel(
       ok = tok >= w_lo && tok <= w_hi && r >= 0 && r < R_cap;
     }
     const uint32_t vmask = (uint32_t)__ballot(ok);
-    if (active && vmask) compute(shared_tile, vmask);
+    if (active && vmask) compute(cur, cur + PF_KT * PF_KS, vmask);
+    if (ti + 1 < ntA) {
+      // tile ti+1 goes into the other buffer, last read for tile ti-1 before
+      // the previous barrier
+      uint16_t* nxt = smem + ((ti + 1) & 1) * PF_TILE;
+      for (int i = 0; i < CHA; ++i) put(nxt, i * (NT / 32) + (tid >> 5), colA, pfa[i]);
+      if (ti + 2 < ntA) issueA(ti + 2);
+    }
+    __syncthreads();
   }
 
-  // ---------------- phase B: this wave's selected compressed entries
-  if (!dense && active && topk > 0) {
-    const int32_t* idx_row = idx + rowi * topk;
+  // ---------------- phase B: each row's selected compressed entries
+  if (!dense && topk > 0) {
+    // stage the index rows (every thread takes part: barriers follow)
     const bool stage = topk <= PF_IDX_MAX;
+    const int32_t* idx_rows = idx + ((size_t)b * T + t0) * topk;
+    const int nrows = t_last - t0 + 1;
     if (stage)
-      for (int i = lane; i < topk; i += 64) idx_s[i] = idx_row[i];
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    const int ntB = (topk + PF_KT - 1) / PF_KT;
-    const int colB = lane & 31;
-    u32x4 pfb[PF_KT / 2];
+      for (int i = tid; i < nrows * topk; i += NT) idx_all[i / topk][i % topk] = idx_rows[i];
+    __syncthreads();
+    const int32_t* idx_row = idx + rowi * topk;
+    const int* idx_s = idx_all[row_w];
     auto slot = [&](int p) -> int {
       if (p >= topk) return -1;
       const int j = stage ? idx_s[p] : idx_row[p];
       return (j < 0 || j >= Nc_cap) ? -1 : j;
     };
+    // the row's NH waves load its tile: 1024 chunks over 64 NH threads
+    constexpr int CHB = PF_KT * 32 / (64 * NH);
+    const int rt = (wave % NH) * 64 + lane;     // thread index within the row
+    const int colB = rt & 31;
+    uint16_t* mine = smem + row_w * PF_TILE;
+    u32x4 pfb[CHB];
     auto issueB = [&](int ti) {
-      for (int i = 0; i < PF_KT / 2; ++i) {
-        const int j = slot(ti * PF_KT + 2 * i + h2);
+      for (int i = 0; i < CHB; ++i) {
+        const int rr = i * (64 * NH / 32) + (rt >> 5);
+        const int j = active ? slot(ti * PF_KT + rr) : -1;
         pfb[i] = j >= 0 ? *(const u32x4*)(kvc_b + (size_t)j * 2 * D + 8 * colB) : u32x4{0, 0, 0, 0};
       }
     };
+    const int ntB = (topk + PF_KT - 1) / PF_KT;
     issueB(0);
     for (int ti = 0; ti < ntB; ++ti) {
-      for (int i = 0; i < PF_KT / 2; ++i)
-        *(u32x4*)(priv_tile + (2 * i + h2) * PF_ROW + 8 * colB) = pfb[i];
-      const uint32_t vmask = (uint32_t)__ballot(slot(ti * PF_KT + l32) >= 0);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      for (int i = 0; i < CHB; ++i) put(mine, i * (64 * NH / 32) + (rt >> 5), colB, pfb[i]);
+      __syncthreads();
       if (ti + 1 < ntB) issueB(ti + 1);
-      if (vmask) compute(priv_tile, vmask);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const uint32_t vmask = (uint32_t)__ballot(active && slot(ti * PF_KT + l32) >= 0);
+      if (vmask) compute(mine, mine + PF_KT * PF_KS, vmask);
+      __syncthreads();
     }
   }
 
-  // ---------------- output: lane holds head 32 ht + l32, dims
+  // ---------------- output: lane holds head 32 hh + l32, dims
   // 32 dt + 8 (r/4) + 4 h2 + r%4
   if (!active) return;
-  for (int ht = 0; ht < NH; ++ht) {
-    const int h = 32 * ht + l32;
-    const float inv = lrun[ht] > 0.0f ? 1.0f / lrun[ht] : 0.0f;
-    uint16_t* orow = out + (rowi * H + h) * D;
-    for (int dt = 0; dt < 4; ++dt)
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d = 32 * dt + 8 * rq + 4 * h2;
-        const f32x16& a = o[dt][ht];
-        uint32_t lo = (uint32_t)f32_to_bf16(a[4 * rq] * inv) | ((uint32_t)f32_to_bf16(a[4 * rq + 1] * inv) << 16);
-        uint32_t hi = (uint32_t)f32_to_bf16(a[4 * rq + 2] * inv) | ((uint32_t)f32_to_bf16(a[4 * rq + 3] * inv) << 16);
-        *(u32x2*)(orow + d) = u32x2{lo, hi};
-      }
-    if (lse && h2 == 0)
-      lse[rowi * H + h] = lrun[ht] > 0.0f ? (mrun[ht] + __log2f(lrun[ht])) * kLn2 : -INFINITY;
-  }
+  const int h = 32 * hh + l32;
+  const float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
+  uint16_t* orow = out + (rowi * H + h) * D;
+  for (int dt = 0; dt < 4; ++dt)
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d = 32 * dt + 8 * rq + 4 * h2;
+      uint32_t lo = (uint32_t)f32_to_bf16(o[dt][4 * rq] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * rq + 1] * inv) << 16);
+      uint32_t hi = (uint32_t)f32_to_bf16(o[dt][4 * rq + 2] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * rq + 3] * inv) << 16);
+      *(u32x2*)(orow + d) = u32x2{lo, hi};
+    }
+  if (lse && h2 == 0) lse[rowi * H + h] = lrun > 0.0f ? (mrun + __log2f(lrun)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- bf16 decode
@@ -343,7 +353,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t tile[DC_KT * DC_ROW];
   __shared__ int vmask[DC_KT];
   __shared__ int idx_s[DC_IDX_MAX];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, hl = lane & 15;
   const int item = blockIdx.x;
   const int rowi = item / n_split, split = item % n_split;
@@ -636,14 +647,14 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
   } else {
-    const unsigned g = (unsigned)(a.B * ((a.T + PF_WAVES - 1) / PF_WAVES));
+    const unsigned g = (unsigned)(a.B * ((a.T + PF_ROWS - 1) / PF_ROWS));
     if (a.H == 64)
-      attn_pf_kernel<2><<<g, 64 * PF_WAVES, 0, st>>>(
+      attn_pf_kernel<2><<<g, 64 * PF_ROWS * 2, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, (uint16_t*)a.out, a.lse);
     else
-      attn_pf_kernel<1><<<g, 64 * PF_WAVES, 0, st>>>(
+      attn_pf_kernel<1><<<g, 64 * PF_ROWS, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, (uint16_t*)a.out, a.lse);
