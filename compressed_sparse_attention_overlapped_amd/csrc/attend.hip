@@ -92,11 +92,10 @@ constexpr int PF_KT = 32;
 constexpr int PF_KS = 128 + 8;       // bf16 per K row in LDS (272 B)
 constexpr int PF_VS = 128 + 16;      // bf16 per V row in LDS (288 B)
 constexpr int PF_TILE = PF_KT * (PF_KS + PF_VS);
-constexpr int PF_ROWS = 4;           // query rows per workgroup
 constexpr int PF_IDX_MAX = 2048;     // index slots per row staged in LDS
 constexpr float PF_RESCALE = 8.0f;   // log2 headroom before the maximum is raised
 
-template <int NH>  // H = 32 NH: waves per row
+template <int NH, int PF_ROWS>  // H = 32 NH: waves per row; query rows per workgroup
 __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv_cmp,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
@@ -647,17 +646,22 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
   } else {
-    const unsigned g = (unsigned)(a.B * ((a.T + PF_ROWS - 1) / PF_ROWS));
-    if (a.H == 64)
-      attn_pf_kernel<2><<<g, 64 * PF_ROWS * 2, 0, st>>>(
-          (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
-          a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, (uint16_t*)a.out, a.lse);
-    else
-      attn_pf_kernel<1><<<g, 64 * PF_ROWS, 0, st>>>(
-          (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
-          a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, (uint16_t*)a.out, a.lse);
+    // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
+    // rows share only the window: 2 rows, so that two independent
+    // workgroups fill each CU.
+#define CSA_LAUNCH_PF(NH, ROWS)                                                                   \
+  attn_pf_kernel<NH, ROWS><<<(unsigned)(a.B * ((a.T + ROWS - 1) / ROWS)), 64 * ROWS * NH, 0, st>>>( \
+      (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,  \
+      a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,      \
+      (uint16_t*)a.out, a.lse)
+    if (a.H == 64) {
+      if (a.dense) CSA_LAUNCH_PF(2, 4);
+      else CSA_LAUNCH_PF(2, 2);
+    } else {
+      if (a.dense) CSA_LAUNCH_PF(1, 4);
+      else CSA_LAUNCH_PF(1, 2);
+    }
+#undef CSA_LAUNCH_PF
   }
   if (n_split > 1)
     combine_kernel<CSA_DT_BF16><<<dim3(rows, a.H / CB_HEADS), 256, 0, st>>>(

@@ -14,11 +14,12 @@
 //    index order.
 //  * long rows: the score kernel also builds a per-row histogram of the top
 //    11 key bits; "collect" workgroups (one per 2048-entry chunk) find the
-//    bin holding the k-th key and append the chunk's entries above it
-//    (certainly selected) and inside it (candidates) to per-row lists;
-//    "finalize" (one workgroup per row) picks the missing entries among the
-//    candidates by an exact radix select on (key, then inverted index) and
-//    writes the selected set sorted ascending.
+//    bin holding the k-th key, mark the chunk's entries above it (certainly
+//    selected) in a bitmap of the row and pack those inside it (candidates)
+//    into the chunk's segment; "finalize" (one workgroup per row) picks the
+//    missing entries among the candidates by an exact radix select on (key,
+//    then index), adds them to the bitmap and writes the selection in
+//    ascending order from it.
 #include <algorithm>
 
 #include "common.h"
@@ -35,6 +36,54 @@ __device__ __forceinline__ void hist_flush(const uint32_t* lhist, uint32_t* ghis
     uint32_t c = lhist[bin];
     if (c) atomicAdd(ghist + bin, c);
   }
+}
+
+// ---------------------------------------------------------------- block scans
+// Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64);
+// returns the caller's offset and sets the block total.  sh: >= 16 words.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) base += sh[w];
+    tot += sh[w];
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+// Threshold bin of a row from its histogram: the bin where the count from the
+// top first reaches `need` (1 <= need <= total).  256 threads; each owns 8
+// consecutive bins from the top.  Returns the bin in every thread.
+__device__ uint32_t threshold_bin(const uint32_t* __restrict__ hist, uint32_t need, uint32_t* sh) {
+  const int tid = threadIdx.x;
+  uint32_t c[8], s = 0;
+  for (int i = 0; i < 8; ++i) {
+    c[i] = hist[kHistBins - 1 - (tid * 8 + i)];
+    s += c[i];
+  }
+  uint32_t tot;
+  const uint32_t base = block_excl_scan(s, sh, tot);
+  if (base < need && base + s >= need) {
+    uint32_t cum = base;
+    for (int i = 0; i < 8; ++i) {
+      if (cum + c[i] >= need) {
+        sh[20] = (uint32_t)(kHistBins - 1 - (tid * 8 + i));
+        break;
+      }
+      cum += c[i];
+    }
+  }
+  __syncthreads();
+  return sh[20];
 }
 
 // ---------------------------------------------------------------- scores: fp32
@@ -169,8 +218,8 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     __syncthreads();
   }
   if (HIST) {
-    // one histogram per query row: flush each row's counts (rows of this
-    // workgroup share the LDS histogram only when T == 1)
+    // one histogram per query row: rows of this workgroup share the LDS
+    // histogram, so long rows run with T == 1 (row = b)
     __syncthreads();
     hist_flush(lhist, ghist + ((size_t)b * T + t0) * kHistBins);
   }
@@ -205,8 +254,8 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, float* __restrict__ scores,
-    uint32_t* __restrict__ ghist) {
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m,
+    float* __restrict__ scores, uint32_t* __restrict__ ghist) {
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
   const int row = blockIdx.y, b = row / T, t = row % T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -280,28 +329,6 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
     __syncthreads();
     hist_flush(lhist, ghist + (size_t)row * kHistBins);
   }
-}
-
-// ---------------------------------------------------------------- block scans
-// Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64);
-// returns the caller's offset and sets the block total.  sh: >= 16 words.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) base += sh[w];
-    tot += sh[w];
-  }
-  __syncthreads();
-  total = tot;
-  return base + x - v;
 }
 
 // MSB-first radix select (8-bit digits) of the `need` largest of n keys,
@@ -431,116 +458,135 @@ __global__ void __launch_bounds__(256) select_short_kernel(
 }
 
 // ---------------------------------------------------------------- long rows
-// Threshold bin from the row histogram: the bin where the count from the top
-// reaches `need`; returns the count strictly above it.  256 threads.
-__device__ void threshold_bin(const uint32_t* __restrict__ ghist_row, uint32_t need,
-                              uint32_t* sh, uint32_t& bin, uint32_t& above) {
-  const int tid = threadIdx.x;
-  uint32_t c[8], s = 0;
-  for (int i = 0; i < 8; ++i) {
-    c[i] = ghist_row[kHistBins - 1 - (tid * 8 + i)];
-    s += c[i];
-  }
-  uint32_t tot;
-  uint32_t base = block_excl_scan(s, sh, tot);
-  if (base < need && base + s >= need) {
-    uint32_t cum = base;
-    for (int i = 0; i < 8; ++i) {
-      if (cum + c[i] >= need) {
-        sh[20] = (uint32_t)(kHistBins - 1 - (tid * 8 + i));
-        sh[21] = cum;
-        break;
-      }
-      cum += c[i];
-    }
-  }
-  __syncthreads();
-  bin = sh[20];
-  above = sh[21];
-  __syncthreads();
-}
-
-// Grid (n_chunks, rows), 256 threads.  Appends the chunk's entries above the
-// threshold bin to the row's definite list and those inside it (index and low
-// key bits) to the candidate list; one atomic per list per workgroup.  The
-// order inside the lists does not matter: finalize sorts.
+// Grid (n_chunks, rows), 256 threads; wave w owns the 512 consecutive entries
+// [j0 + 512 w, + 512) of the chunk.  Each workgroup finds the row's threshold
+// bin from the histogram, writes the chunk's words of the row bitmap of
+// entries above that bin (certainly selected; 64-entry ballots, one word pair
+// per group) and packs the entries inside the bin (candidates: index and low
+// key bits) at the start of the chunk's own segment, with their count in
+// chunk_cnt.  No counter is shared between workgroups.  Rows that keep every
+// visible entry, or none, are left to finalize.
 __global__ void __launch_bounds__(256) collect_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ ghist,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp, int T, int Nc_cap,
-    int m, int topk, uint32_t* __restrict__ counts, uint32_t* __restrict__ def_list,
-    uint32_t* __restrict__ cand_idx, uint32_t* __restrict__ cand_key) {
+    int m, int topk, int n_chunks, int bm_words, uint32_t* __restrict__ def_bm,
+    uint32_t* __restrict__ chunk_cnt, uint32_t* __restrict__ cand_idx,
+    uint32_t* __restrict__ cand_key) {
   __shared__ uint32_t sh[32];
   const int chunk = blockIdx.x, row = blockIdx.y, b = row / T, t = row % T;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const int nsel = min(topk, nv);
   const int j0 = chunk * kChunk, j1 = min(nv, j0 + kChunk);
-  if (nsel == 0 || j0 >= j1) return;
-  uint32_t bin = 0, above = 0;
-  const bool all = nsel == nv;
-  if (!all) threshold_bin(ghist + (size_t)row * kHistBins, (uint32_t)nsel, sh, bin, above);
+  if (nsel == 0 || nsel == nv || j0 >= j1) return;
+  const uint32_t bin = threshold_bin(ghist + (size_t)row * kHistBins, (uint32_t)nsel, sh);
   const float* srow = scores + (size_t)row * Nc_cap;
-  uint32_t nd = 0, nc = 0;
-  uint8_t kind[8];
-  uint32_t key[8];
-  for (int i = 0; i < 8; ++i) {
-    int j = j0 + tid * 8 + i;
-    uint8_t k = 0;
-    key[i] = 0;
-    if (j < j1) {
-      if (all) k = 1;
-      else {
-        key[i] = score_key(srow[j]);
-        uint32_t kb = key[i] >> kHistShift;
-        k = kb > bin ? 1 : (kb == bin ? 2 : 0);
-      }
-    }
-    kind[i] = k;
-    nd += k == 1;
-    nc += k == 2;
+  uint32_t* bm = def_bm + (size_t)row * bm_words;
+  const int wb = j0 + wave * 512;
+  constexpr int kGroups = kChunk / 256;
+  uint32_t key[kGroups];
+  uint32_t n_wave = 0;
+  for (int g = 0; g < kGroups; ++g) {
+    const int j = wb + g * 64 + lane;
+    const bool valid = j < j1;
+    key[g] = valid ? score_key(srow[j]) : 0u;
+    const uint32_t kb = key[g] >> kHistShift;
+    const uint64_t dm = __ballot(valid && kb > bin);
+    const uint64_t cm = __ballot(valid && kb == bin);
+    if (lane == 0 && wb + g * 64 < j1) *(uint64_t*)(bm + (wb + g * 64) / 32) = dm;
+    n_wave += (uint32_t)__popcll(cm);
   }
-  uint32_t td, tc;
-  uint32_t db = block_excl_scan(nd, sh, td);
-  uint32_t cb = block_excl_scan(nc, sh, tc);
-  if (tid == 0) {
-    sh[16] = td ? atomicAdd(&counts[2 * row + 0], td) : 0u;
-    sh[17] = tc ? atomicAdd(&counts[2 * row + 1], tc) : 0u;
-  }
+  if (lane == 0) sh[24 + wave] = n_wave;
   __syncthreads();
-  db += sh[16];
-  cb += sh[17];
-  uint32_t* dl = def_list + (size_t)row * topk;
-  uint32_t* ci = cand_idx + (size_t)row * Nc_cap;
-  uint32_t* ck = cand_key + (size_t)row * Nc_cap;
-  for (int i = 0; i < 8; ++i) {
-    int j = j0 + tid * 8 + i;
-    if (kind[i] == 1) dl[db++] = (uint32_t)j;
-    else if (kind[i] == 2) {
-      ci[cb] = (uint32_t)j;
-      ck[cb++] = key[i] & ((1u << kHistShift) - 1u);
+  uint32_t pos = 0;
+  for (int w = 0; w < wave; ++w) pos += sh[24 + w];
+  if (tid == 0) chunk_cnt[(size_t)row * n_chunks + chunk] = sh[24] + sh[25] + sh[26] + sh[27];
+  uint32_t* ci = cand_idx + (size_t)row * Nc_cap + j0;
+  uint32_t* ck = cand_key + (size_t)row * Nc_cap + j0;
+  for (int g = 0; g < kGroups; ++g) {
+    const int j = wb + g * 64 + lane;
+    const bool c = j < j1 && (key[g] >> kHistShift) == bin;
+    const uint64_t cm = __ballot(c);
+    if (c) {
+      const uint32_t p = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
+      ci[p] = (uint32_t)j;
+      ck[p] = key[g] & ((1u << kHistShift) - 1u);
     }
+    pos += (uint32_t)__popcll(cm);
   }
 }
 
-// One workgroup (1024 threads) per row: picks the missing entries among the
-// candidates by (key desc, index asc) - an exact radix select on the low key
-// bits, then, for keys equal to the threshold, on the inverted index - and
-// writes the selected set sorted ascending (bitonic sort in LDS).
-constexpr int FIN_THREADS = 1024;
+// MSB-first radix select with 11-bit digits over 22-bit keys (two passes) of
+// the `need` largest of n keys, 1 <= need < n; same result convention as
+// radix_select.  hist: 2048 words of LDS; sh: >= 32 words; blockDim.x = 1024.
+template <class Get>
+__device__ RadixResult radix_select22(Get get, int n, uint32_t need, uint32_t* hist,
+                                      uint32_t* sh) {
+  RadixResult r{0u, 0u, need, false};
+  const int tid = threadIdx.x;
+  for (int shift = 11; shift >= 0; shift -= 11) {
+    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+      const uint32_t x = get(i);
+      if ((x & r.mask) == r.prefix) atomicAdd(&hist[(x >> shift) & 2047u], 1u);
+    }
+    __syncthreads();
+    // thread i owns bins 2047 - 2i (upper) and 2046 - 2i (lower)
+    const uint32_t c_hi = hist[2047 - 2 * tid], c_lo = hist[2046 - 2 * tid];
+    uint32_t tot;
+    const uint32_t above = block_excl_scan(c_hi + c_lo, sh + 8, tot);
+    if (above < r.remaining && above + c_hi >= r.remaining) {
+      sh[0] = 2047u - 2 * tid;
+      sh[1] = above;
+      sh[2] = c_hi;
+    } else if (above + c_hi < r.remaining && above + c_hi + c_lo >= r.remaining) {
+      sh[0] = 2046u - 2 * tid;
+      sh[1] = above + c_hi;
+      sh[2] = c_lo;
+    }
+    __syncthreads();
+    const uint32_t d = sh[0], cum = sh[1], cnt = sh[2];
+    __syncthreads();
+    r.remaining -= cum;
+    r.prefix |= d << shift;
+    r.mask |= 2047u << shift;
+    if (cnt == r.remaining) {
+      r.all_eq = true;
+      break;
+    }
+  }
+  return r;
+}
 
+// One workgroup (1024 threads) per long row.  The selected set is the
+// entries marked in the collect bitmap plus the `need` best candidates under
+// (key desc, index asc): a radix select on the low key bits, then, among
+// candidates whose key equals the k-th, one on (Nc_cap - index).  Candidates
+// are gathered from the chunk segments into LDS (or, beyond kFinalCandLds, a
+// flat workspace list); chosen ones are added to the bitmap (in LDS up to
+// kBitmapLds words, else in place in the workspace), and a popcount scan over
+// the bitmap writes the selection in ascending order.
+constexpr int FIN_THREADS = 1024;
+constexpr int kBitmapLds = 16384;  // 2^19 entries
+
+template <bool BM_LDS>
 __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk,
-    const uint32_t* __restrict__ counts, const uint32_t* __restrict__ def_list,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk, int n_chunks,
+    int bm_words, uint32_t* __restrict__ def_bm, const uint32_t* __restrict__ chunk_cnt,
     const uint32_t* __restrict__ cand_idx, const uint32_t* __restrict__ cand_key,
-    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+    uint32_t* __restrict__ cand_flat, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
   __shared__ uint32_t ckey[kFinalCandLds];
   __shared__ uint32_t cidx[kFinalCandLds];
-  __shared__ uint32_t outl[8192];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t lbm[BM_LDS ? kBitmapLds : 1];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t coff[FIN_THREADS], ccnt[FIN_THREADS];
   __shared__ uint32_t sh[32];
   const int row = blockIdx.x, b = row / T, t = row % T;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const int nsel = min(topk, nv);
   const float* srow = scores + (size_t)row * Nc_cap;
@@ -551,78 +597,103 @@ __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
     if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
   }
   if (nsel == 0) return;
-  const uint32_t n_def = counts[2 * row], n_cand = counts[2 * row + 1];
+  if (nsel == nv) {  // every visible entry is kept
+    for (int j = tid; j < nv; j += blockDim.x) {
+      orow[j] = j;
+      if (sorow) sorow[j] = srow[j];
+    }
+    return;
+  }
+  uint32_t* gbm = def_bm + (size_t)row * bm_words;
+  uint32_t* bm = BM_LDS ? lbm : gbm;
+  const int nwords = (nv + 31) / 32;
+  const int nch = (nv + kChunk - 1) / kChunk;  // chunks collect wrote (<= FIN_THREADS)
+  uint32_t n_bits = 0;
+  for (int w = tid; w < nwords; w += blockDim.x) {
+    const uint32_t x = gbm[w];
+    if (BM_LDS) lbm[w] = x;
+    n_bits += __popc(x);
+  }
+  const uint32_t cc = tid < nch ? chunk_cnt[(size_t)row * n_chunks + tid] : 0u;
+  uint32_t n_def, n_cand;
+  block_excl_scan(n_bits, sh, n_def);
+  const uint32_t off = block_excl_scan(cc, sh, n_cand);
+  coff[tid] = off;
+  ccnt[tid] = cc;
+  __syncthreads();
   const uint32_t need = (uint32_t)nsel - n_def;  // <= n_cand
-  const uint32_t* dl = def_list + (size_t)row * topk;
-  const uint32_t* gci = cand_idx + (size_t)row * Nc_cap;
-  const uint32_t* gck = cand_key + (size_t)row * Nc_cap;
-  for (uint32_t i = tid; i < n_def; i += blockDim.x) outl[i] = dl[i];
+  const bool in_lds = n_cand <= (uint32_t)kFinalCandLds;
+  uint32_t* fkey = cand_flat + (size_t)row * Nc_cap * 2;
+  uint32_t* fidx = fkey + Nc_cap;
   if (need > 0) {
-    const bool in_lds = n_cand <= (uint32_t)kFinalCandLds;
-    if (in_lds) {
-      for (uint32_t i = tid; i < n_cand; i += blockDim.x) {
-        ckey[i] = gck[i];
-        cidx[i] = gci[i];
+    // gather the chunk segments: wave w takes chunks w, w + 16, ...
+    const uint32_t* gci = cand_idx + (size_t)row * Nc_cap;
+    const uint32_t* gck = cand_key + (size_t)row * Nc_cap;
+    for (int c = wave; c < nch; c += FIN_THREADS / 64) {
+      const uint32_t n = ccnt[c], o = coff[c];
+      for (uint32_t i = lane; i < n; i += 64) {
+        const uint32_t k = gck[(size_t)c * kChunk + i], j = gci[(size_t)c * kChunk + i];
+        if (in_lds) {
+          ckey[o + i] = k;
+          cidx[o + i] = j;
+        } else {
+          fkey[o + i] = k;
+          fidx[o + i] = j;
+        }
       }
     }
     __syncthreads();
-    auto key_at = [&](uint32_t i) -> uint32_t { return in_lds ? ckey[i] : gck[i]; };
-    auto idx_at = [&](uint32_t i) -> uint32_t { return in_lds ? cidx[i] : gci[i]; };
+    auto key_at = [&](uint32_t i) -> uint32_t { return in_lds ? ckey[i] : fkey[i]; };
+    auto idx_at = [&](uint32_t i) -> uint32_t { return in_lds ? cidx[i] : fidx[i]; };
     RadixResult rk{0u, 0u, need, true};
     RadixResult ri{0u, 0u, 0u, true};
     bool tie_break = false;
     if (need < n_cand) {
-      rk = radix_select([&](int i) { return key_at(i); }, (int)n_cand, need, hist, sh);
+      rk = radix_select22([&](int i) { return key_at(i); }, (int)n_cand, need, hist, sh);
       if (!rk.all_eq) {
-        // rk.remaining of the candidates whose key equals rk.prefix: lowest
-        // indices first, i.e. the largest inverted indices
+        // rk.remaining of the candidates whose key equals rk.prefix, lowest
+        // indices first: the largest values of Nc_cap - index (>= 1, so the
+        // other candidates' 0 never ties with them)
         tie_break = true;
-        ri = radix_select([&](int i) { return key_at(i) == rk.prefix ? ~idx_at(i) : 0u; },
-                          (int)n_cand, rk.remaining, hist, sh);
+        ri = radix_select22(
+            [&](int i) { return key_at(i) == rk.prefix ? (uint32_t)Nc_cap - idx_at(i) : 0u; },
+            (int)n_cand, rk.remaining, hist, sh);
       }
     }
-    // chosen candidates -> output list after the definite ones
-    const uint32_t per = (n_cand + blockDim.x - 1) / blockDim.x;
-    const uint32_t c0 = min(n_cand, tid * per), c1 = min(n_cand, c0 + per);
-    auto chosen = [&](uint32_t i) -> bool {
-      if (need >= n_cand) return true;
-      uint32_t x = key_at(i) & rk.mask;
-      if (x != rk.prefix) return x > rk.prefix;
-      if (!tie_break) return true;
-      return ((~idx_at(i)) & ri.mask) >= ri.prefix;
-    };
-    uint32_t cnt = 0;
-    for (uint32_t i = c0; i < c1; ++i) cnt += chosen(i);
-    uint32_t tot;
-    uint32_t pos = n_def + block_excl_scan(cnt, sh, tot);
-    for (uint32_t i = c0; i < c1; ++i)
-      if (chosen(i)) outl[pos++] = idx_at(i);
+    for (uint32_t i = tid; i < n_cand; i += blockDim.x) {
+      bool sel = true;
+      if (need < n_cand) {
+        const uint32_t x = key_at(i) & rk.mask;
+        if (x != rk.prefix) sel = x > rk.prefix;
+        else if (tie_break) sel = (((uint32_t)Nc_cap - idx_at(i)) & ri.mask) >= ri.prefix;
+      }
+      if (sel) {
+        const uint32_t j = idx_at(i);
+        atomicOr(&bm[j >> 5], 1u << (j & 31));
+      }
+    }
   }
-  // bitonic sort of outl[0, nsel) padded to a power of two
-  int N = 1;
-  while (N < nsel) N <<= 1;
-  for (int i = nsel + tid; i < N; i += blockDim.x) outl[i] = 0xffffffffu;
   __syncthreads();
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += blockDim.x) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          uint32_t a = outl[i], c = outl[ixj];
-          bool up = (i & k) == 0;
-          if ((a > c) == up) {
-            outl[i] = c;
-            outl[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
+  // ascending output: thread owns words [w0, w1)
+  auto word = [&](int w) -> uint32_t {
+    return BM_LDS ? lbm[w] : __hip_atomic_load(gbm + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  const int per = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(word(w));
+  uint32_t tot;
+  uint32_t pos = block_excl_scan(cnt, sh, tot);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = word(w);
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int j = w * 32 + bit;
+      orow[pos] = j;
+      if (sorow) sorow[pos] = srow[j];
+      ++pos;
     }
-  }
-  for (int i = tid; i < nsel; i += blockDim.x) {
-    uint32_t j = outl[i];
-    orow[i] = (int32_t)j;
-    if (sorow) sorow[i] = srow[j];
   }
 }
 
@@ -640,30 +711,35 @@ using namespace csa;
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct IdxLayout {
-  bool long_rows;
-  int n_chunks;
-  size_t scores, hist, counts, def_list, cand_idx, cand_key, total;
+  bool long_rows, bm_lds;
+  int n_chunks, bm_words;
+  size_t scores, hist, chunk_cnt, def_bm, cand_idx, cand_key, cand_flat, total;
 };
 
 static IdxLayout idx_layout(int B, int T, int Nc_cap, int topk) {
+  (void)topk;
   IdxLayout L{};
   const size_t rows = (size_t)B * T;
   L.long_rows = Nc_cap > kShortMax;
+  L.bm_lds = Nc_cap <= kBitmapLds * 32;
   L.n_chunks = (Nc_cap + kChunk - 1) / kChunk;
+  L.bm_words = 2 * ((Nc_cap + 63) / 64);  // even: collect stores word pairs
   size_t off = 0;
   L.scores = off;
   off += align256(rows * (size_t)Nc_cap * 4);
   if (L.long_rows) {
-    L.hist = off;  // histogram and counters are contiguous: zeroed together
-    off += rows * kHistBins * 4;
-    L.counts = off;
-    off += align256(rows * 2 * 4);
-    L.def_list = off;
-    off += align256(rows * (size_t)topk * 4);
+    L.hist = off;  // the only part that must start at zero
+    off += align256(rows * kHistBins * 4);
+    L.chunk_cnt = off;
+    off += align256(rows * (size_t)L.n_chunks * 4);
+    L.def_bm = off;
+    off += align256(rows * (size_t)L.bm_words * 4);
     L.cand_idx = off;
     off += align256(rows * (size_t)Nc_cap * 4);
     L.cand_key = off;
     off += align256(rows * (size_t)Nc_cap * 4);
+    L.cand_flat = off;
+    off += align256(rows * (size_t)Nc_cap * 8);
   }
   L.total = off;
   return L;
@@ -683,7 +759,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   uint32_t* hist = L.long_rows ? (uint32_t*)(ws + L.hist) : nullptr;
   const int rows = a.B * a.T;
   if (L.long_rows) {
-    size_t n = (size_t)rows * (kHistBins + 2);
+    size_t n = (size_t)rows * kHistBins;
     zero_u32_kernel<<<(unsigned)std::min<size_t>((n + 255) / 256, 1024), 256, 0, st>>>(hist, n);
   }
   if (a.Nc_cap == 0) {
@@ -728,16 +804,23 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     select_short_kernel<<<rows, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m,
                                               a.topk, a.idx_out, a.score_out);
   } else {
-    uint32_t* counts = (uint32_t*)(ws + L.counts);
-    uint32_t* dl = (uint32_t*)(ws + L.def_list);
+    uint32_t* cnt = (uint32_t*)(ws + L.chunk_cnt);
+    uint32_t* bm = (uint32_t*)(ws + L.def_bm);
     uint32_t* ci = (uint32_t*)(ws + L.cand_idx);
     uint32_t* ck = (uint32_t*)(ws + L.cand_key);
+    uint32_t* cf = (uint32_t*)(ws + L.cand_flat);
     collect_kernel<<<dim3(L.n_chunks, rows), 256, 0, st>>>(scores, hist, a.q_pos, a.n_cmp, a.T,
-                                                           a.Nc_cap, a.m, a.topk, counts, dl, ci,
-                                                           ck);
-    finalize_kernel<<<rows, FIN_THREADS, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m,
-                                                  a.topk, counts, dl, ci, ck, a.idx_out,
-                                                  a.score_out);
+                                                           a.Nc_cap, a.m, a.topk, L.n_chunks,
+                                                           L.bm_words, bm, cnt, ci, ck);
+    if (L.bm_lds)
+      finalize_kernel<true><<<rows, FIN_THREADS, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap,
+                                                          a.m, a.topk, L.n_chunks, L.bm_words, bm,
+                                                          cnt, ci, ck, cf, a.idx_out, a.score_out);
+    else
+      finalize_kernel<false><<<rows, FIN_THREADS, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T,
+                                                           a.Nc_cap, a.m, a.topk, L.n_chunks,
+                                                           L.bm_words, bm, cnt, ci, ck, cf,
+                                                           a.idx_out, a.score_out);
   }
   return hipGetLastError();
 }

@@ -168,3 +168,41 @@ def test_indexer_deterministic():
     for _ in range(3):
         b = _gpu(*args)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_indexer_f32_long_rows_ragged():
+    # rows longer than the LDS-resident limit on the fp32 score path, several
+    # query rows per sequence, with ragged visibility across the batch
+    d = gen.Draw(27)
+    B, T, Nc, m, topk = 2, 3, 9000, 4, 700
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 4, 32, gen.F32)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 32, gen.F32)
+    q_pos = [4 * Nc, 4 * 2500 - 2]          # second sequence: ~2500 visible
+    n_cmp = [Nc, Nc - 3]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "f32 long")
+
+
+def test_indexer_bf16_long_row_single_query():
+    d = gen.Draw(28)
+    B, Nc, m, topk = 2, 12000, 4, 1024
+    q_idx, _, w_idx = gen.indexer_query(d, B, 1, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    q_pos, n_cmp = [4 * Nc, 4 * 9000 + 1], [Nc, Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "bf16 long")
+
+
+def test_indexer_fp8_rows_beyond_lds_bitmap():
+    # 600000 entries (2.4M tokens at m = 4): the ordering bitmap of the row no
+    # longer fits in LDS and lives in the workspace
+    d = gen.Draw(29, "cpu")
+    B, Nc, m, topk = 1, 600000, 4, 2048
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, 2, 16, 64, gen.FP8)
+    q_pos, n_cmp = [4 * 550000], [Nc]        # row 0: 550000 visible, row 1: 550000
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "fp8 bitmap in workspace")
