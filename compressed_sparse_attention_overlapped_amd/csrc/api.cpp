@@ -154,7 +154,7 @@ static csa_status_t check_attn(const char* fn, int B, int T, int H, int D, int w
 
 size_t csa_sparse_attn_workspace_size(int B, int T, int H, int D, int topk, int window) {
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
-  return csa_host::attn_ws_bytes(B, T, H, D, topk + window);
+  return csa_host::attn_ws_bytes(B, T, H, D, topk + window, true);
 }
 
 csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, float scale,
@@ -167,7 +167,10 @@ csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, f
   if (st != CSA_OK) return st;
   if (topk < 0) return fail(CSA_E_ARG, "csa_sparse_attn: topk must be >= 0");
   if (topk > 0 && !idx) return fail(CSA_E_ARG, "csa_sparse_attn: idx is required when topk > 0");
-  const size_t need = dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, topk + window);
+  if (dt == CSA_DT_BF16 && !csa_host::attn_supported(B, T, H, topk + window, true))
+    return fail(CSA_E_UNSUPPORTED, "csa_sparse_attn: topk + window too large for %d rows", B * T);
+  const size_t need =
+      dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, topk + window, true);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "csa_sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
   csa_host::AttnArgs a{B, T, H, D, topk, window, 1, Nc_cap, R_cap, false, scale, q_pos, nullptr,
@@ -177,7 +180,7 @@ csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, f
 
 size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window) {
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
-  return csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window);
+  return csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window, false);
 }
 
 csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float scale,
@@ -190,7 +193,8 @@ csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float
   if (st != CSA_OK) return st;
   if (m < 1) return fail(CSA_E_ARG, "hca_dense_attn: m must be >= 1");
   if (!n_cmp) return fail(CSA_E_ARG, "hca_dense_attn: n_cmp is required");
-  const size_t need = dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window);
+  const size_t need =
+      dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window, false);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "hca_dense_attn: workspace %zu < %zu bytes", ws_bytes, need);
   csa_host::AttnArgs a{B, T, H, D, 0, window, m, Nc_cap, R_cap, true, scale, q_pos, n_cmp,

@@ -19,6 +19,8 @@
 //    split-K across workgroups, partials merged by log-sum-exp in a combine
 //    kernel.
 // fp32 runs a plain per-(row, head) wave kernel.
+#include <type_traits>
+
 #include "common.h"
 
 namespace csa {
@@ -333,8 +335,8 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
 // product pairs keys {32 ks + 4 g + i} and {32 ks + 16 + 4 g + i}; V^T
 // fragments of 4 consecutive keys per lane come from the LDS transpose read
 // (lane i of a 16-lane group gets element i % 4 of the 8-byte chunks whose
-// addresses lanes i/4 + 4 v supplied).  The next tile's rows are loaded into
-// registers while the current one is computed.
+// addresses lanes i/4 + 4 v supplied).  The rows of the next two tiles are
+// loaded into registers while the current one is computed.
 constexpr int DC_KT = 64;                // keys per tile
 constexpr int DC_ROW = 256 + 16;         // bf16 per LDS row (544 B: conflict-free reads)
 constexpr int DC_IDX_MAX = 4096;         // index slots staged in LDS per work item
@@ -350,7 +352,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;  // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t tile[DC_KT * DC_ROW];
-  __shared__ int vmask[DC_KT];
+  __shared__ __attribute__((aligned(16))) int vmask[DC_KT];
   __shared__ int idx_s[DC_IDX_MAX];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -368,23 +370,37 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
   const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
   const int64_t rbase = raw_base[b];
-
-  // index slots of this item's compressed positions, staged once
+  // index slots of this item's compressed positions, staged once (loads
+  // batched four per thread before their LDS stores); the host splits the
+  // list so that an item holds at most DC_IDX_MAX of them
   const int c_lo = min(kb, L.n_c), c_hi = min(ke, L.n_c);
-  const bool stage = !dense && (c_hi - c_lo) <= DC_IDX_MAX;
-  if (stage)
-    for (int i = tid; i < c_hi - c_lo; i += NT) idx_s[i] = idx_row[c_lo + i];
-  __syncthreads();
-  auto src_of = [&](int p) -> const uint16_t* {
-    if (p >= ke) return nullptr;
-    if (p < L.n_c) {
-      int j = dense ? p : (stage ? idx_s[p - c_lo] : idx_row[p]);
-      if (j < 0 || j >= Nc_cap) return nullptr;
-      return kvc_b + (size_t)j * 2 * D;
+  if (!dense) {
+    for (int i0 = 0; i0 < c_hi - c_lo; i0 += 4 * NT) {
+      int v[4];
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT + tid;
+        v[u] = i < c_hi - c_lo ? idx_row[c_lo + i] : 0;
+      }
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT + tid;
+        if (i < c_hi - c_lo) idx_s[i] = v[u];
+      }
     }
-    int64_t r = L.lo + (p - L.n_c) - rbase;
-    if (r < 0 || r >= R_cap) return nullptr;
-    return kvr_b + (size_t)r * 2 * D;
+  }
+  __syncthreads();
+  // Source row of list position p; empty slots read this row's query
+  // instead (a valid address; the slot is masked), so that every load of a
+  // tile is issued unconditionally and the waits count them exactly.
+  const uint16_t* dummy = q + (size_t)rowi * H * D;
+  auto src_of = [&](int p, bool& ok) -> const uint16_t* {
+    const bool in_c = p < L.n_c;
+    const int j = dense ? p : (in_c ? idx_s[min(max(0, p - c_lo), DC_IDX_MAX - 1)] : 0);
+    const int64_t r = L.lo + (p - L.n_c) - rbase;
+    const bool okc = in_c && j >= 0 && j < Nc_cap;
+    const bool okr = !in_c && r >= 0 && r < R_cap;
+    ok = p < ke && (okc || okr);
+    const uint16_t* src = okc ? kvc_b + (size_t)j * 2 * D : kvr_b + (size_t)r * 2 * D;
+    return ok ? src : dummy;
   };
 
   // Q^T operand: lane holds head 16 wave + hl, dims 32 s + 8 g .. + 8
@@ -399,19 +415,22 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
 
   const int ntiles = (ke - kb + DC_KT - 1) / DC_KT;
   const int col = tid & 31;
-  u32x4 pf[CH];
-  bool pv[CH];
-  auto issue = [&](int ti) {
+  // Two tiles in flight in registers: tile i + 2 is requested as soon as
+  // tile i has moved to LDS.
+  u32x4 pfa[CH], pfb[CH];
+  bool pva[CH], pvb[CH];
+  auto issue = [&](int ti, u32x4(&pf)[CH], bool(&pv)[CH]) {
     const int p0 = kb + ti * DC_KT;
     for (int i = 0; i < CH; ++i) {
       const int rr = i * (NT / 32) + (tid >> 5);
-      const uint16_t* src = src_of(p0 + rr);
-      pv[i] = src != nullptr;
-      pf[i] = src ? __builtin_nontemporal_load((const u32x4*)(src + 8 * col)) : u32x4{0, 0, 0, 0};
+      const uint16_t* src = src_of(p0 + rr, pv[i]);
+      pf[i] = __builtin_nontemporal_load((const u32x4*)(src + 8 * col));
     }
   };
-  if (ntiles > 0) issue(0);
-  for (int ti = 0; ti < ntiles; ++ti) {
+  // step(ti, regs, refill): tile ti moves from regs to LDS and is computed;
+  // with refill the registers then request tile ti + 2 (past the end: the
+  // dummy row), unconditionally, so that every wait counts exactly.
+  auto step = [&](int ti, u32x4(&pf)[CH], bool(&pv)[CH], auto refill) {
     __syncthreads();  // every wave is done reading the previous tile
     for (int i = 0; i < CH; ++i) {
       const int rr = i * (NT / 32) + (tid >> 5);
@@ -419,21 +438,31 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
       if (col == 0) vmask[rr] = pv[i];
     }
     __syncthreads();
-    if (ti + 1 < ntiles) issue(ti + 1);
-    // ---- S^T = K Q^T for 4 blocks of 16 keys
+    if constexpr (decltype(refill)::value) issue(ti + 2, pf, pv);
+    // ---- S^T = K Q^T for 4 blocks of 16 keys; the fragments of a block are
+    // read together, the next block's while the current one multiplies
     f32x4 sacc[4];
-    for (int kb4 = 0; kb4 < 4; ++kb4) {
-      sacc[kb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 kf[2][4];
+    auto read_k = [&](int kb4, bf16x8(&f)[4]) {
       const uint16_t* krow = tile + (16 * kb4 + hl) * DC_ROW + 8 * g;
+      for (int s = 0; s < 4; ++s) f[s] = *(const bf16x8*)(krow + 32 * s);
+    };
+    read_k(0, kf[0]);
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      if (kb4 + 1 < 4) read_k(kb4 + 1, kf[(kb4 + 1) & 1]);
+      sacc[kb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       for (int s = 0; s < 4; ++s)
-        sacc[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(krow + 32 * s),
-                                                           qf[s], sacc[kb4], 0, 0, 0);
+        sacc[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb4 & 1][s], qf[s], sacc[kb4], 0,
+                                                           0, 0);
     }
     // ---- online softmax over the 64 keys; lane: head hl, keys 16 kb4 + 4 g + i
+    int4 vm[4];
+    for (int kb4 = 0; kb4 < 4; ++kb4) vm[kb4] = *(const int4*)(vmask + 16 * kb4 + 4 * g);
     float mx = -INFINITY;
     for (int kb4 = 0; kb4 < 4; ++kb4)
       for (int i = 0; i < 4; ++i) {
-        const bool ok = vmask[16 * kb4 + 4 * g + i] != 0;
+        const bool ok = vm[kb4][i] != 0;
         const float sv = ok ? sacc[kb4][i] * scale_log2 : -INFINITY;
         sacc[kb4][i] = sv;
         mx = fmaxf(mx, sv);
@@ -466,16 +495,29 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
       // dims D0 + 4 (j % 4)
       const uint16_t* base1 = tile + (32 * ks + 4 * g + (hl >> 2)) * DC_ROW + D + 4 * (hl & 3);
       const uint16_t* base2 = base1 + 16 * DC_ROW;
+      // all 16 transpose reads first, then the 8 products (whole-register
+      // moves only: the four 16-bit values of a transpose read are not
+      // extracted one by one)
+      u32x2 v1[8], v2[8];
       for (int dt = 0; dt < 8; ++dt) {
-        // whole-register moves only: the four 16-bit values of a transpose
-        // read are not extracted one by one
-        const u32x2 v1 = __builtin_bit_cast(u32x2, lds_read_tr16(base1 + 16 * dt));
-        const u32x2 v2 = __builtin_bit_cast(u32x2, lds_read_tr16(base2 + 16 * dt));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{v1[0], v1[1], v2[0], v2[1]});
+        v1[dt] = __builtin_bit_cast(u32x2, lds_read_tr16(base1 + 16 * dt));
+        v2[dt] = __builtin_bit_cast(u32x2, lds_read_tr16(base2 + 16 * dt));
+      }
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 vf =
+            __builtin_bit_cast(bf16x8, u32x4{v1[dt][0], v1[dt][1], v2[dt][0], v2[dt][1]});
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfr, o[dt], 0, 0, 0);
       }
     }
+  };
+  issue(0, pfa, pva);
+  issue(1, pfb, pvb);
+  int ti = 0;
+  for (; ti + 1 < ntiles; ti += 2) {
+    step(ti, pfa, pva, std::true_type{});
+    step(ti + 1, pfb, pvb, std::true_type{});
   }
+  if (ti < ntiles) step(ti, pfa, pva, std::false_type{});
   // ---- results: lane holds head 16 wave + hl, dims 16 dt + 4 g + i
   const int h = 16 * wave + hl;
   if (n_split == 1) {
@@ -500,48 +542,45 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
 }
 
 // ---------------------------------------------------------------- combine
-// Grid (rows, H / 8): the workgroup merges 8 heads of one query row.  Per head
-// the split maxima fix the weights exp2(m_s - M) once (in LDS); then every
-// output element is a weighted sum of its split partials, read coalesced.
-constexpr int CB_HEADS = 8, CB_MAX_SPLIT = 64;
+// Grid (rows, H / 2), 256 threads: thread (h, d) merges output element d of
+// head h over the splits, O = sum_s exp2(m_s - M) O_s / sum_s exp2(m_s - M) l_s
+// with M = max_s m_s.  Lane s of each wave computes the weight of split s
+// (n_split <= 64); the partial loads are issued eight splits at a time.
+// D = 128.
+constexpr int CB_MAX_SPLIT = 64;
 
 template <int OUT_DT>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
-                                                      int n_split, int H, int D, void* __restrict__ out,
+                                                      int n_split, int H, void* __restrict__ out,
                                                       float* __restrict__ lse) {
-  __shared__ float wgt[CB_HEADS][CB_MAX_SPLIT];
-  __shared__ float inv_l[CB_HEADS];
-  const int rowi = blockIdx.x, h0 = blockIdx.y * CB_HEADS;
-  const int tid = threadIdx.x;
-  if (tid < CB_HEADS) {
-    const int h = h0 + tid;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s)
-      M = fmaxf(M, part_ml[(((size_t)rowi * n_split + s) * H + h) * 2]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
-    float Ls = 0.0f;
-    for (int s = 0; s < n_split; ++s) {
-      const size_t it = (size_t)rowi * n_split + s;
-      const float c = exp2f(part_ml[(it * H + h) * 2] - Mu);
-      wgt[tid][s] = c;
-      Ls += part_ml[(it * H + h) * 2 + 1] * c;
-    }
-    inv_l[tid] = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    if (lse) lse[(size_t)rowi * H + h] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+  constexpr int D = 128;
+  const int rowi = blockIdx.x;
+  const int h = blockIdx.y * 2 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
+  const int d = threadIdx.x & (D - 1), lane = threadIdx.x & 63;
+  const float* ml = part_ml + ((size_t)rowi * n_split * H + h) * 2;  // split s at + 2 H s
+  const float* po = part_o + ((size_t)rowi * n_split * H + h) * D + d;  // split s at + H D s
+  // lane s holds split s: weights exp2(m_s - M) and the merged sum
+  const float ms = lane < n_split ? ml[(size_t)2 * H * lane] : -INFINITY;
+  const float ls = lane < n_split ? ml[(size_t)2 * H * lane + 1] : 0.0f;
+  const float M = wave_max(ms);
+  const float Mu = M == -INFINITY ? 0.0f : M;
+  const float c = lane < n_split ? exp2f(ms - Mu) : 0.0f;
+  const float Ls = wave_sum(ls * c);
+  float O = 0.0f;
+  for (int s0 = 0; s0 < n_split; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s0 + k < n_split ? po[(size_t)H * D * (s0 + k)] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) O = fmaf(v[k], __shfl(c, s0 + k, 64), O);
   }
-  __syncthreads();
-  for (int i = tid; i < CB_HEADS * D; i += blockDim.x) {
-    const int hh = i / D, d = i % D, h = h0 + hh;
-    float O = 0.0f;
-    for (int s = 0; s < n_split; ++s)
-      O = fmaf(part_o[(((size_t)rowi * n_split + s) * H + h) * D + d], wgt[hh][s], O);
-    const float v = O * inv_l[hh];
-    if (OUT_DT == CSA_DT_BF16)
-      ((uint16_t*)out)[((size_t)rowi * H + h) * D + d] = f32_to_bf16(v);
-    else
-      ((float*)out)[((size_t)rowi * H + h) * D + d] = v;
-  }
+  const float v = Ls > 0.0f ? O / Ls : 0.0f;
+  if (OUT_DT == CSA_DT_BF16)
+    ((uint16_t*)out)[((size_t)rowi * H + h) * D + d] = f32_to_bf16(v);
+  else
+    ((float*)out)[((size_t)rowi * H + h) * D + d] = v;
+  if (lse && d == 0) lse[(size_t)rowi * H + h] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- fp32
@@ -600,22 +639,34 @@ static bool use_decode_kernel(int rows, int H) {
   return rows < AT_DECODE_ROWS && (H == 32 || H == 64);
 }
 
-static int attn_splits(int rows, int keys_per_row, int H) {
+// Splits of the decode kernel: about two workgroups per CU of the 256, each
+// with >= 128 keys, and for index lists enough that no split holds more than
+// DC_IDX_MAX index slots (its staging buffer).  0: unsupported.
+static int attn_splits(int rows, int keys_per_row, bool sparse, int H) {
   if (use_decode_kernel(rows, H)) {
-    // about two workgroups per CU of the 256, each with >= 128 keys
     int s = (512 + rows - 1) / rows;
     int smax = (keys_per_row + DC_MIN_SPLIT_KEYS - 1) / DC_MIN_SPLIT_KEYS;
     if (smax > CB_MAX_SPLIT) smax = CB_MAX_SPLIT;
     s = s < smax ? s : smax;
+    if (sparse) {
+      // a split covers at most ceil(keys / s) rounded up to a tile
+      const int smin = (keys_per_row + DC_IDX_MAX - DC_KT - 1) / (DC_IDX_MAX - DC_KT);
+      if (s < smin) s = smin;
+      if (s > CB_MAX_SPLIT) return 0;
+    }
     return s < 1 ? 1 : s;
   }
   return 1;  // the prefill kernel has enough rows to fill the chip
 }
 
-size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row) {
+bool attn_supported(int B, int T, int H, int keys_per_row, bool sparse) {
+  return attn_splits(B * T, keys_per_row, sparse, H) > 0;
+}
+
+size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse) {
   const int rows = B * T;
-  const int s = attn_splits(rows, keys_per_row, H);
-  if (s == 1) return 0;
+  const int s = attn_splits(rows, keys_per_row, sparse, H);
+  if (s <= 1) return 0;
   return (size_t)rows * s * H * (D + 2) * sizeof(float);
 }
 
@@ -630,7 +681,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
-  const int n_split = attn_splits(rows, keys, a.H);
+  const int n_split = attn_splits(rows, keys, !a.dense, a.H);
+  if (n_split == 0) return hipErrorNotSupported;
   float* part_o = (float*)a.ws;
   float* part_ml = part_o ? part_o + (size_t)rows * n_split * a.H * a.D : nullptr;
   const unsigned grid = (unsigned)(rows * n_split);
@@ -664,8 +716,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
 #undef CSA_LAUNCH_PF
   }
   if (n_split > 1)
-    combine_kernel<CSA_DT_BF16><<<dim3(rows, a.H / CB_HEADS), 256, 0, st>>>(
-        part_o, part_ml, n_split, a.H, a.D, a.out, a.lse);
+    combine_kernel<CSA_DT_BF16><<<dim3(rows, a.H / 2), 256, 0, st>>>(part_o, part_ml, n_split,
+                                                                      a.H, a.out, a.lse);
   return hipGetLastError();
 }
 

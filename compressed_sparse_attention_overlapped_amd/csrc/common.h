@@ -150,7 +150,8 @@ struct AttnArgs {
   float* lse;
   void* ws;
 };
-size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row);
+size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse);
+bool attn_supported(int B, int T, int H, int keys_per_row, bool sparse);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 
 }  // namespace csa_host

@@ -254,8 +254,8 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m,
-    float* __restrict__ scores, uint32_t* __restrict__ ghist) {
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, float* __restrict__ scores,
+    uint32_t* __restrict__ ghist) {
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
   const int row = blockIdx.y, b = row / T, t = row % T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -266,12 +266,17 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
     __syncthreads();
   }
   const int je = min(nv, jb + kChunk);
-  if (jb < je) {
+  // this wave's entries: [wb, we), in SF_ITERS steps of 16 * SF_UNROLL
+  constexpr int kPerWave = kChunk / 4, kStep = 16 * SF_UNROLL, SF_ITERS = kPerWave / kStep;
+  const int wb = jb + wave * kPerWave;
+  const int we = min(je, wb + kPerWave);
+  if (wb < we) {
     const int h = lane & 15, g = lane >> 4;
     const u32x4 qv = *(const u32x4*)(q_idx + ((size_t)row * 16 + h) * 64 + 16 * g);
     const bf16x8 qa0 = e4m3x8_to_bf16x8(qv[0], qv[1]);
     const bf16x8 qa1 = e4m3x8_to_bf16x8(qv[2], qv[3]);
     float wq[4];
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
       int hh = 4 * g + i;
       wq[i] = w_idx[(size_t)row * 16 + hh] * q_scale[(size_t)row * 16 + hh];
@@ -279,45 +284,58 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
     const uint8_t* kb = k_idx + (size_t)b * Nc_cap * 64;
     const float* ks = k_scale + (size_t)b * Nc_cap;
     float* srow = scores + (size_t)row * Nc_cap;
-    // this wave's entries: [wb, we) in 16-entry groups
-    const int per_wave = kChunk / 4;
-    const int wb = jb + wave * per_wave;
-    const int we = min(je, wb + per_wave);
-    for (int j0 = wb; j0 < we; j0 += 16 * SF_UNROLL) {
-      u32x4 kv[SF_UNROLL];
-      float ksc[SF_UNROLL];
+    // two register stages: the codes of step i + 2 load while step i computes
+    u32x4 kv[2][SF_UNROLL];
+    float ksc[2][SF_UNROLL / 4];  // scale of the entry this lane writes, per 64-entry half
+    auto load = [&](int it, int st) {
+#pragma unroll
       for (int u = 0; u < SF_UNROLL; ++u) {
-        int j = j0 + 16 * u + (lane & 15);
-        if (j < we) {
-          kv[u] = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)j * 64 + 16 * g));
-          ksc[u] = ks[j];
-        } else {
-          kv[u] = u32x4{0, 0, 0, 0};
-          ksc[u] = 0.0f;
-        }
+        const int j = wb + it * kStep + 16 * u + (lane & 15);
+        kv[st][u] = j < we ? __builtin_nontemporal_load((const u32x4*)(kb + (size_t)j * 64 + 16 * g))
+                           : u32x4{0, 0, 0, 0};
       }
-      float res[SF_UNROLL];
+#pragma unroll
+      for (int hf = 0; hf < SF_UNROLL / 4; ++hf) {
+        const int j = wb + it * kStep + 64 * hf + lane;
+        ksc[st][hf] = j < we ? ks[j] : 0.0f;
+      }
+    };
+    load(0, 0);
+    load(1, 1);
+    const bool b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1;
+#pragma unroll
+    for (int it = 0; it < SF_ITERS; ++it) {
+      const int st = it & 1;
+      const int j0 = wb + it * kStep;
+      float part[SF_UNROLL];
+#pragma unroll
       for (int u = 0; u < SF_UNROLL; ++u) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, e4m3x8_to_bf16x8(kv[u][0], kv[u][1]),
-                                                      acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, e4m3x8_to_bf16x8(kv[u][2], kv[u][3]),
-                                                      acc, 0, 0, 0);
-        // acc[i]: head 4 (lane / 16) + i, entry lane % 16
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qa0, e4m3x8_to_bf16x8(kv[st][u][0], kv[st][u][1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qa1, e4m3x8_to_bf16x8(kv[st][u][2], kv[st][u][3]), acc, 0, 0, 0);
+        // acc[i]: head 4 (lane / 16) + i, entry lane % 16 of group u
         float p = 0.0f;
+#pragma unroll
         for (int i = 0; i < 4; ++i) p = fmaf(wq[i], fmaxf(acc[i], 0.0f), p);
-        p += __shfl_xor(p, 16, 64);
-        p += __shfl_xor(p, 32, 64);
-        res[u] = p * ksc[u];
+        part[u] = p;
       }
-      // lane l writes entry j0 + 64 half + l (group 4 half + l / 16)
+      float sc[SF_UNROLL / 4];
+      sc[0] = ksc[st][0];
+      sc[1] = ksc[st][1];
+      if (it + 2 < SF_ITERS) load(it + 2, st);
+      // Reduce-scatter over the four 16-lane head groups: afterwards lane l
+      // holds the full score of entry l % 16 of group 4 half + l / 16, i.e.
+      // entry j0 + 64 half + l.  Exchange across lane bit 5, then bit 4.
+#pragma unroll
       for (int half = 0; half < SF_UNROLL / 4; ++half) {
-        float v = res[half * 4 + 0];
-        const int gsel = lane >> 4;
-        v = gsel == 1 ? res[half * 4 + 1] : v;
-        v = gsel == 2 ? res[half * 4 + 2] : v;
-        v = gsel == 3 ? res[half * 4 + 3] : v;
-        int j = j0 + 64 * half + lane;
+        const float* q = part + 4 * half;
+        const float s0 = b5 ? q[0] : q[2], s1 = b5 ? q[1] : q[3];
+        const float k0 = b5 ? q[2] : q[0], k1 = b5 ? q[3] : q[1];
+        const float r0 = k0 + __shfl_xor(s0, 32, 64), r1 = k1 + __shfl_xor(s1, 32, 64);
+        const float v = ((b4 ? r1 : r0) + __shfl_xor(b4 ? r0 : r1, 16, 64)) * sc[half];
+        const int j = j0 + 64 * half + lane;
         if (j < we) {
           srow[j] = v;
           if (HIST) atomicAdd(&lhist[score_key(v) >> kHistShift], 1u);
