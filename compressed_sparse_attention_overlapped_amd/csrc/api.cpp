@@ -146,6 +146,8 @@ static csa_status_t check_attn(const char* fn, int B, int T, int H, int D, int w
     if (!aligned16(q) || (kv_cmp && !aligned16(kv_cmp)) || (kv_raw && !aligned16(kv_raw)) ||
         !aligned16(out))
       return fail(CSA_E_UNSUPPORTED, "%s: bf16 tensors must be 16-byte aligned", fn);
+    if (Nc_cap > (1 << 23) || R_cap > (1 << 23))
+      return fail(CSA_E_UNSUPPORTED, "%s: bf16 caches hold at most 2^23 rows", fn);
   } else {
     return fail(CSA_E_UNSUPPORTED, "%s: dt must be F32 or BF16", fn);
   }

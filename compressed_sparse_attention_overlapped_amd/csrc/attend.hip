@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
     float x = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
     for (int r = 3; r < 15; r += 2) x = fmaxf(fmaxf(x, sacc[r]), sacc[r + 1]);
     x = fmaxf(x, sacc[15]);
-    x = fmaxf(x, __shfl_xor(x, 32, 64)) * scale_log2;
+    x = max_xor32(x) * scale_log2;
     const bool up = x > mrun + PF_RESCALE;
     if (__ballot(up)) {
       const float corr = up ? __builtin_amdgcn_exp2f(mrun - x) : 1.0f;
@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
       ps += pv;
       sacc[r] = pv;
     }
-    ps += __shfl_xor(ps, 32, 64);
+    ps = sum_xor32(ps);
     lrun += ps;
     bf16x8 pf[2];
     for (int ks = 0; ks < 2; ++ks)
@@ -340,6 +340,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
 constexpr int DC_KT = 64;                // keys per tile
 constexpr int DC_ROW = 256 + 16;         // bf16 per LDS row (544 B: conflict-free reads)
 constexpr int DC_IDX_MAX = 4096;         // index slots staged in LDS per work item
+constexpr float DC_RESCALE = 8.0f;       // log2 headroom before the maximum is raised
 
 template <int WAVES>  // H = 16 WAVES
 __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
@@ -350,9 +351,11 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     int R_cap, bool dense, float scale_log2, int n_split, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
-  constexpr int CH = DC_KT * 32 / NT;  // 16-byte chunks per thread per tile
+  constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
+  constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
   __shared__ __attribute__((aligned(16))) uint16_t tile[DC_KT * DC_ROW];
   __shared__ __attribute__((aligned(16))) int vmask[DC_KT];
+  __shared__ __attribute__((aligned(16))) int partial[4];
   __shared__ int idx_s[DC_IDX_MAX];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -362,18 +365,27 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   const int b = rowi / T, t = rowi % T;
   const int64_t pos = q_pos[b] + t;
   const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
-  const int nk = L.n_c + L.n_w;
-  int per = (nk + n_split - 1) / n_split;
-  per = (per + DC_KT - 1) / DC_KT * DC_KT;
-  const int kb = min(nk, split * per), ke = min(nk, kb + per);
+  // Tile-aligned list: compressed slots [0, n_c) padded to a whole tile, then
+  // the window, so that every tile reads from one of the two caches.  Splits
+  // take whole tiles.
+  const int nc_pad = (L.n_c + DC_KT - 1) / DC_KT * DC_KT;
+  const int n_tiles_row = (nc_pad + L.n_w + DC_KT - 1) / DC_KT;
+  const int tiles_per = (n_tiles_row + n_split - 1) / n_split;
+  const int ta = min(n_tiles_row, split * tiles_per), tb = min(n_tiles_row, ta + tiles_per);
+  const int ntiles = tb - ta;
+  const int kb = ta * DC_KT;
   const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
-  const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
-  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
-  const int64_t rbase = raw_base[b];
+  const uint16_t* dummy = q + (size_t)rowi * H * D;  // a valid row for empty slots
+  const char* cbase = Nc_cap > 0 ? (const char*)(kv_cmp + (size_t)b * Nc_cap * 2 * D)
+                                 : (const char*)dummy;
+  const char* wbase = R_cap > 0 ? (const char*)(kv_raw + (size_t)b * R_cap * 2 * D)
+                                : (const char*)dummy;
+  const int n_c = L.n_c, n_w = L.n_w;
+  const int64_t w_row0 = L.lo - raw_base[b];  // cache row of window slot 0
   // index slots of this item's compressed positions, staged once (loads
   // batched four per thread before their LDS stores); the host splits the
   // list so that an item holds at most DC_IDX_MAX of them
-  const int c_lo = min(kb, L.n_c), c_hi = min(ke, L.n_c);
+  const int c_lo = min(kb, L.n_c), c_hi = min(tb * DC_KT, L.n_c);
   if (!dense) {
     for (int i0 = 0; i0 < c_hi - c_lo; i0 += 4 * NT) {
       int v[4];
@@ -388,20 +400,6 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     }
   }
   __syncthreads();
-  // Source row of list position p; empty slots read this row's query
-  // instead (a valid address; the slot is masked), so that every load of a
-  // tile is issued unconditionally and the waits count them exactly.
-  const uint16_t* dummy = q + (size_t)rowi * H * D;
-  auto src_of = [&](int p, bool& ok) -> const uint16_t* {
-    const bool in_c = p < L.n_c;
-    const int j = dense ? p : (in_c ? idx_s[min(max(0, p - c_lo), DC_IDX_MAX - 1)] : 0);
-    const int64_t r = L.lo + (p - L.n_c) - rbase;
-    const bool okc = in_c && j >= 0 && j < Nc_cap;
-    const bool okr = !in_c && r >= 0 && r < R_cap;
-    ok = p < ke && (okc || okr);
-    const uint16_t* src = okc ? kvc_b + (size_t)j * 2 * D : kvr_b + (size_t)r * 2 * D;
-    return ok ? src : dummy;
-  };
 
   // Q^T operand: lane holds head 16 wave + hl, dims 32 s + 8 g .. + 8
   bf16x8 qf[4];
@@ -413,30 +411,61 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float mrun = -INFINITY, lrun = 0.0f;
 
-  const int ntiles = (ke - kb + DC_KT - 1) / DC_KT;
   const int col = tid & 31;
-  // Two tiles in flight in registers: tile i + 2 is requested as soon as
-  // tile i has moved to LDS.
+  // Tile rows in registers: byte offsets from the tile's cache base (empty
+  // slots: offset 0 of a valid base, masked), loads issued unconditionally
+  // so that the waits count them exactly.  Tiles past the end read the
+  // dummy row.
   u32x4 pfa[CH], pfb[CH];
   bool pva[CH], pvb[CH];
-  auto issue = [&](int ti, u32x4(&pf)[CH], bool(&pv)[CH]) {
+  auto issue = [&](int ti, u32x4(&pf)[CH], bool(&pv)[CH]) __attribute__((always_inline)) {
     const int p0 = kb + ti * DC_KT;
-    for (int i = 0; i < CH; ++i) {
-      const int rr = i * (NT / 32) + (tid >> 5);
-      const uint16_t* src = src_of(p0 + rr, pv[i]);
-      pf[i] = __builtin_nontemporal_load((const u32x4*)(src + 8 * col));
+    const bool ct = p0 < nc_pad && ti < ntiles;  // uniform
+    // base by masks rather than a select: a select between captured
+    // variables would be folded into one between their addresses, which
+    // keeps the whole capture block in scratch memory
+    const uint64_t mc = 0 - (uint64_t)ct, md = 0 - (uint64_t)(ti >= ntiles);
+    const uint64_t bsel = ((uint64_t)cbase & mc) | ((uint64_t)wbase & ~mc);
+    const char* base = (const char*)(((uint64_t)dummy & md) | (bsel & ~md));
+    uint32_t off[CH];
+    if (ct) {
+      #pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int p = p0 + i * (NT / 32) + (tid >> 5);
+        const int j = dense ? p : idx_s[min(max(0, p - c_lo), DC_IDX_MAX - 1)];
+        const bool ok = (p < n_c) & (j >= 0) & (j < Nc_cap);
+        pv[i] = ok;
+        off[i] = ok ? (uint32_t)j * kRowBytes : 0u;
+      }
+    } else {
+      #pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int w = p0 - nc_pad + i * (NT / 32) + (tid >> 5);
+        const int64_t r = w_row0 + w;
+        const bool ok = (ti < ntiles) & (w < n_w) & (r >= 0) & (r < R_cap);
+        pv[i] = ok;
+        off[i] = ok ? (uint32_t)r * kRowBytes : 0u;
+      }
     }
+    #pragma unroll
+    for (int i = 0; i < CH; ++i)
+      pf[i] = __builtin_nontemporal_load((const u32x4*)(base + off[i] + 16 * col));
   };
   // step(ti, regs, refill): tile ti moves from regs to LDS and is computed;
-  // with refill the registers then request tile ti + 2 (past the end: the
-  // dummy row), unconditionally, so that every wait counts exactly.
-  auto step = [&](int ti, u32x4(&pf)[CH], bool(&pv)[CH], auto refill) {
+  // with refill the registers then request tile ti + 2, unconditionally.
+  auto step = [&](int ti, u32x4(&pf)[CH], bool(&pv)[CH], auto refill)
+                  __attribute__((always_inline)) {
     __syncthreads();  // every wave is done reading the previous tile
+    bool mine = true;
+    #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int rr = i * (NT / 32) + (tid >> 5);
       *(u32x4*)(tile + rr * DC_ROW + 8 * col) = pf[i];
       if (col == 0) vmask[rr] = pv[i];
+      mine = mine && pv[i];
     }
+    const bool wave_partial = __ballot(!mine) != 0;
+    if (lane == 0) partial[wave] = wave_partial;
     __syncthreads();
     if constexpr (decltype(refill)::value) issue(ti + 2, pf, pv);
     // ---- S^T = K Q^T for 4 blocks of 16 keys; the fragments of a block are
@@ -456,34 +485,39 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
         sacc[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb4 & 1][s], qf[s], sacc[kb4], 0,
                                                            0, 0);
     }
-    // ---- online softmax over the 64 keys; lane: head hl, keys 16 kb4 + 4 g + i
-    int4 vm[4];
-    for (int kb4 = 0; kb4 < 4; ++kb4) vm[kb4] = *(const int4*)(vmask + 16 * kb4 + 4 * g);
+    // ---- online softmax over the 64 keys; lane: head hl, keys 16 kb4 + 4 g + i.
+    // Only tiles with empty slots pay for the mask.  The running maximum is
+    // raised only when a score exceeds it by more than DC_RESCALE (log2
+    // units), so most tiles skip the rescale of the accumulators.
+    const int4 pw = *(const int4*)partial;
+    if (pw[0] | pw[1] | (WAVES > 2 ? pw[2] | pw[3] : 0)) {
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        const int4 vm = *(const int4*)(vmask + 16 * kb4 + 4 * g);
+        for (int i = 0; i < 4; ++i)
+          if (!vm[i]) sacc[kb4][i] = -INFINITY;
+      }
+    }
     float mx = -INFINITY;
     for (int kb4 = 0; kb4 < 4; ++kb4)
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = vm[kb4][i] != 0;
-        const float sv = ok ? sacc[kb4][i] * scale_log2 : -INFINITY;
-        sacc[kb4][i] = sv;
-        mx = fmaxf(mx, sv);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrun, mx);
-    const float muse = mnew == -INFINITY ? 0.0f : mnew;
-    const float corr = exp2f(mrun - muse);
+      mx = fmaxf(fmaxf(mx, fmaxf(sacc[kb4][0], sacc[kb4][1])), fmaxf(sacc[kb4][2], sacc[kb4][3]));
+    mx = max_xor32(max_xor16(mx)) * scale_log2;
+    const bool up = mx > mrun + DC_RESCALE;
+    if (__ballot(up)) {
+      const float corr = up ? __builtin_amdgcn_exp2f(mrun - mx) : 1.0f;
+      if (up) mrun = mx;
+      lrun *= corr;
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= corr;
+    }
+    const float nmuse = mrun == -INFINITY ? 0.0f : -mrun;
     float ps = 0.0f;
     for (int kb4 = 0; kb4 < 4; ++kb4)
       for (int i = 0; i < 4; ++i) {
-        const float pv2 = exp2f(sacc[kb4][i] - muse);
+        const float pv2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb4][i], scale_log2, nmuse));
         sacc[kb4][i] = pv2;
         ps += pv2;
       }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    lrun = lrun * corr + ps;
-    mrun = mnew;
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= corr;
+    ps = sum_xor32(sum_xor16(ps));
+    lrun += ps;
     // ---- O^T += V^T P^T (k slot 8 g + i: key 32 ks + 4 g + i, then 32 ks + 16 + 4 g + i)
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pfr;
@@ -649,8 +683,10 @@ static int attn_splits(int rows, int keys_per_row, bool sparse, int H) {
     if (smax > CB_MAX_SPLIT) smax = CB_MAX_SPLIT;
     s = s < smax ? s : smax;
     if (sparse) {
-      // a split covers at most ceil(keys / s) rounded up to a tile
-      const int smin = (keys_per_row + DC_IDX_MAX - DC_KT - 1) / (DC_IDX_MAX - DC_KT);
+      // the kernel's tile-aligned list has at most this many tiles; a split
+      // takes ceil(tiles / s) of them
+      const int tiles = (keys_per_row + 2 * DC_KT - 1) / DC_KT;
+      const int smin = (tiles + DC_IDX_MAX / DC_KT - 1) / (DC_IDX_MAX / DC_KT);
       if (s < smin) s = smin;
       if (s > CB_MAX_SPLIT) return 0;
     }

@@ -94,6 +94,44 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Value of lane l ^ 32 (resp. l ^ 16) through the gfx950 permlane swaps, a
+// VALU path instead of the LDS crossbar of a shuffle.  permlane32_swap(x, x)
+// gives (x[l], x[l - 32]) for l >= 32 and (x[l], x[l + 32]) as its second
+// word for l < 32 - in lane order: word 0 = l < 32 ? x[l] : x[l - 32],
+// word 1 = l < 32 ? x[l + 32] : x[l]; the 16-lane swap does the same between
+// the even and odd rows of 16 lanes.
+__device__ __forceinline__ float lane_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+// max / sum of a value and its partner: both words of the swap, no select
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace csa
 
 // ---- host-side launch entry points (defined in the kernel sources) --------

@@ -204,8 +204,8 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
         float s0 = 0.0f, s1 = 0.0f;
         for (int r = 0; r < 8; ++r) s0 = fmaf(wv[mt][r], fmaxf(acc[r], 0.0f), s0);
         for (int r = 8; r < 16; ++r) s1 = fmaf(wv[mt][r], fmaxf(acc[r], 0.0f), s1);
-        s0 += __shfl_xor(s0, 32, 64);
-        s1 += __shfl_xor(s1, 32, 64);
+        s0 = sum_xor32(s0);
+        s1 = sum_xor32(s1);
         const int u = lane >> 5;  // lanes < 32 write token 0 of the pair, others token 1
         const float sc = u ? s1 : s0;
         const int tt = trow[mt] - ((lane & 31) >> 4) + u;
@@ -333,8 +333,8 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
         const float* q = part + 4 * half;
         const float s0 = b5 ? q[0] : q[2], s1 = b5 ? q[1] : q[3];
         const float k0 = b5 ? q[2] : q[0], k1 = b5 ? q[3] : q[1];
-        const float r0 = k0 + __shfl_xor(s0, 32, 64), r1 = k1 + __shfl_xor(s1, 32, 64);
-        const float v = ((b4 ? r1 : r0) + __shfl_xor(b4 ? r0 : r1, 16, 64)) * sc[half];
+        const float r0 = k0 + lane_xor32(s0), r1 = k1 + lane_xor32(s1);
+        const float v = ((b4 ? r1 : r0) + lane_xor16(b4 ? r0 : r1)) * sc[half];
         const int j = j0 + 64 * half + lane;
         if (j < we) {
           srow[j] = v;

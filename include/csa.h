@@ -145,9 +145,9 @@ size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_ca
  *  q        [B, T, H, D] in dt;  out [B, T, H, D] in dt;  lse fp32 [B, T, H] or NULL
  *  kv_cmp   [B, Nc_cap, 2 D] in dt;  idx int32 [B, T, topk] (topk may be 0)
  *  kv_raw   [B, R_cap, 2 D] in dt;   raw_base int64 [B]
- * Supported: dt F32 with D in {64, 128}; dt BF16 with D = 128 and H in {32, 64};
- * with BF16 and fewer than 1024 query rows (the split-key decode kernel),
- * topk + window <= 64 * 4032.
+ * Supported: dt F32 with D in {64, 128}; dt BF16 with D = 128, H in {32, 64}
+ * and Nc_cap, R_cap <= 2^23; with BF16 and fewer than 1024 query rows (the
+ * split-key decode kernel), topk + window <= 64 * 4032.
  */
 csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, float scale,
                              const int64_t* q_pos, const void* q, const void* kv_cmp,
