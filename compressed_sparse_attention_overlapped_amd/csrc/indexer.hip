@@ -578,17 +578,95 @@ __device__ RadixResult radix_select22(Get get, int n, uint32_t need, uint32_t* h
   return r;
 }
 
-// One workgroup (1024 threads) per long row.  The selected set is the
-// entries marked in the collect bitmap plus the `need` best candidates under
-// (key desc, index asc): a radix select on the low key bits, then, among
-// candidates whose key equals the k-th, one on (Nc_cap - index).  Candidates
-// are gathered from the chunk segments into LDS (or, beyond kFinalCandLds, a
-// flat workspace list); chosen ones are added to the bitmap (in LDS up to
-// kBitmapLds words, else in place in the workspace), and a popcount scan over
-// the bitmap writes the selection in ascending order.
 constexpr int FIN_THREADS = 1024;
 constexpr int kBitmapLds = 16384;  // 2^19 entries
 
+// Marks in bm the `need` best of n_cand candidates under (key desc, index asc):
+// a radix select on the low key bits, then, among candidates whose key
+// equals the k-th, one on (Nc_cap - index).  FIN_THREADS threads; hist: 2048
+// words of LDS.  Ends with a barrier.
+template <class KeyAt, class IdxAt>
+__device__ void select_candidates(KeyAt key_at, IdxAt idx_at, uint32_t n_cand, uint32_t need,
+                                  int Nc_cap, uint32_t* bm, uint32_t* hist, uint32_t* sh) {
+  RadixResult rk{0u, 0u, need, true};
+  RadixResult ri{0u, 0u, 0u, true};
+  bool tie_break = false;
+  if (need < n_cand) {
+    rk = radix_select22([&](int i) { return key_at(i); }, (int)n_cand, need, hist, sh);
+    if (!rk.all_eq) {
+      // rk.remaining of the candidates whose key equals rk.prefix, lowest
+      // indices first: the largest values of Nc_cap - index (>= 1, so the
+      // other candidates' 0 never ties with them)
+      tie_break = true;
+      ri = radix_select22(
+          [&](int i) { return key_at(i) == rk.prefix ? (uint32_t)Nc_cap - idx_at(i) : 0u; },
+          (int)n_cand, rk.remaining, hist, sh);
+    }
+  }
+  for (uint32_t i = threadIdx.x; i < n_cand; i += blockDim.x) {
+    bool sel = true;
+    if (need < n_cand) {
+      const uint32_t x = key_at(i) & rk.mask;
+      if (x != rk.prefix) sel = x > rk.prefix;
+      else if (tie_break) sel = (((uint32_t)Nc_cap - idx_at(i)) & ri.mask) >= ri.prefix;
+    }
+    if (sel) {
+      const uint32_t j = idx_at(i);
+      atomicOr(&bm[j >> 5], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+}
+
+// Ascending output of the entries marked in a row bitmap of nwords words:
+// thread t owns words [t per, (t + 1) per); a popcount scan places them.
+template <class Word>
+__device__ void write_selection(Word word, int nwords, const float* srow, int32_t* orow,
+                                float* sorow, uint32_t* sh) {
+  const int per = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int w0 = min(nwords, (int)threadIdx.x * per), w1 = min(nwords, w0 + per);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(word(w));
+  uint32_t tot;
+  uint32_t pos = block_excl_scan(cnt, sh, tot);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = word(w);
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int j = w * 32 + bit;
+      orow[pos] = j;
+      if (sorow) sorow[pos] = srow[j];
+      ++pos;
+    }
+  }
+}
+
+// Padding, and the rows that need no selection (none or every visible entry
+// kept).  Returns true when the row is finished.
+__device__ bool trivial_row(int nsel, int nv, int topk, const float* srow, int32_t* orow,
+                            float* sorow) {
+  for (int k = nsel + threadIdx.x; k < topk; k += blockDim.x) {
+    orow[k] = -1;
+    if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
+  }
+  if (nsel == 0) return true;
+  if (nsel == nv) {
+    for (int j = threadIdx.x; j < nv; j += blockDim.x) {
+      orow[j] = j;
+      if (sorow) sorow[j] = srow[j];
+    }
+    return true;
+  }
+  return false;
+}
+
+// One workgroup (1024 threads) per long row after collect.  The selected set
+// is the entries marked in the collect bitmap plus the best candidates
+// (select_candidates).  Candidates are gathered from the chunk segments into
+// LDS (or, beyond kFinalCandLds, a flat workspace list); chosen ones are added
+// to the bitmap (in LDS up to kBitmapLds words, else in place in the
+// workspace), which then gives the ascending output.
 template <bool BM_LDS>
 __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
@@ -610,18 +688,7 @@ __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
   const float* srow = scores + (size_t)row * Nc_cap;
   int32_t* orow = idx_out + (size_t)row * topk;
   float* sorow = score_out ? score_out + (size_t)row * topk : nullptr;
-  for (int k = nsel + tid; k < topk; k += blockDim.x) {
-    orow[k] = -1;
-    if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
-  }
-  if (nsel == 0) return;
-  if (nsel == nv) {  // every visible entry is kept
-    for (int j = tid; j < nv; j += blockDim.x) {
-      orow[j] = j;
-      if (sorow) sorow[j] = srow[j];
-    }
-    return;
-  }
+  if (trivial_row(nsel, nv, topk, srow, orow, sorow)) return;
   uint32_t* gbm = def_bm + (size_t)row * bm_words;
   uint32_t* bm = BM_LDS ? lbm : gbm;
   const int nwords = (nv + 31) / 32;
@@ -661,58 +728,17 @@ __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
       }
     }
     __syncthreads();
-    auto key_at = [&](uint32_t i) -> uint32_t { return in_lds ? ckey[i] : fkey[i]; };
-    auto idx_at = [&](uint32_t i) -> uint32_t { return in_lds ? cidx[i] : fidx[i]; };
-    RadixResult rk{0u, 0u, need, true};
-    RadixResult ri{0u, 0u, 0u, true};
-    bool tie_break = false;
-    if (need < n_cand) {
-      rk = radix_select22([&](int i) { return key_at(i); }, (int)n_cand, need, hist, sh);
-      if (!rk.all_eq) {
-        // rk.remaining of the candidates whose key equals rk.prefix, lowest
-        // indices first: the largest values of Nc_cap - index (>= 1, so the
-        // other candidates' 0 never ties with them)
-        tie_break = true;
-        ri = radix_select22(
-            [&](int i) { return key_at(i) == rk.prefix ? (uint32_t)Nc_cap - idx_at(i) : 0u; },
-            (int)n_cand, rk.remaining, hist, sh);
-      }
-    }
-    for (uint32_t i = tid; i < n_cand; i += blockDim.x) {
-      bool sel = true;
-      if (need < n_cand) {
-        const uint32_t x = key_at(i) & rk.mask;
-        if (x != rk.prefix) sel = x > rk.prefix;
-        else if (tie_break) sel = (((uint32_t)Nc_cap - idx_at(i)) & ri.mask) >= ri.prefix;
-      }
-      if (sel) {
-        const uint32_t j = idx_at(i);
-        atomicOr(&bm[j >> 5], 1u << (j & 31));
-      }
-    }
+    select_candidates([&](uint32_t i) -> uint32_t { return in_lds ? ckey[i] : fkey[i]; },
+                      [&](uint32_t i) -> uint32_t { return in_lds ? cidx[i] : fidx[i]; },
+                      n_cand, need, Nc_cap, bm, hist, sh);
   }
   __syncthreads();
-  // ascending output: thread owns words [w0, w1)
-  auto word = [&](int w) -> uint32_t {
-    return BM_LDS ? lbm[w] : __hip_atomic_load(gbm + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  const int per = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
-  uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(word(w));
-  uint32_t tot;
-  uint32_t pos = block_excl_scan(cnt, sh, tot);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = word(w);
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int j = w * 32 + bit;
-      orow[pos] = j;
-      if (sorow) sorow[pos] = srow[j];
-      ++pos;
-    }
-  }
+  write_selection(
+      [&](int w) -> uint32_t {
+        return BM_LDS ? lbm[w]
+                      : __hip_atomic_load(gbm + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      },
+      nwords, srow, orow, sorow, sh);
 }
 
 __global__ void zero_u32_kernel(uint32_t* __restrict__ p, size_t n) {
