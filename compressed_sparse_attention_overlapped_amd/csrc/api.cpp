@@ -75,10 +75,10 @@ csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap,
   if (out_dt == CSA_DT_FP8E4M3 && !out_scale)
     return fail(CSA_E_ARG, "csa_compress: fp8 output needs out_scale");
   if (E > 1024) return fail(CSA_E_UNSUPPORTED, "csa_compress: E > 1024");
-  if (in_dt == CSA_DT_BF16 && (d_model % 32 != 0 || !aligned16(x) || !aligned16(w_kv) ||
+  if (in_dt == CSA_DT_BF16 && (d_model % 64 != 0 || !aligned16(x) || !aligned16(w_kv) ||
                                !aligned16(w_gate)))
     return fail(CSA_E_UNSUPPORTED,
-                "csa_compress: bf16 needs d_model %% 32 == 0 and 16-byte aligned x and weights");
+                "csa_compress: bf16 needs d_model %% 64 == 0 and 16-byte aligned x and weights");
   const size_t need = csa_host::compress_ws_bytes(B, L, d_model, E, m, overlap, in_dt);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "csa_compress: workspace %zu < %zu bytes", ws_bytes, need);

@@ -5,8 +5,8 @@
 //  1. proj: PG[s][row][c] = sum_{k in split s} x[row][k] * W[c][k] for the
 //     stacked weight [W_kv; W_gate] (c < E: value channel, c >= E: gate
 //     logit).  bf16 uses MFMA 32x32x16 tiles staged through LDS; fp32 uses a
-//     plain VALU dot product.  Small-M calls (decode) split K so that enough
-//     workgroups stream the weights.
+//     plain VALU dot product.  Calls with few output tiles split K so that
+//     enough workgroups run; the pool sums the split partials.
 //  2. pool: one workgroup per emitted entry: per channel, a softmax of
 //     G + ape over the window tokens (taken from this call's rows or from the
 //     carried state), the weighted sum of P, then the storage rounding (fp32,
@@ -19,60 +19,86 @@
 namespace csa {
 
 // ---------------------------------------------------------------- proj (bf16)
-// Tile 128 x 128 x 32, 256 threads = 4 waves in a 2 x 2 grid of 64 x 64.
-constexpr int PJ_BM = 128, PJ_BN = 128, PJ_BK = 32;
-constexpr int PJ_LDS_STRIDE = PJ_BK + 8;  // bf16 elements per LDS row (pad 16 B)
+// Tile 128 x 128 x 64, 256 threads = 4 waves in a 2 x 2 grid of 64 x 64
+// (2 x 2 MFMA 32x32x16 per 16-deep k step).  The LDS tiles are double
+// buffered and the next k tile is loaded into registers while the current
+// one multiplies: one barrier per k tile.  LDS rows are padded to 72 bf16
+// (36 dwords) so that the 16-byte fragment reads of 16 consecutive rows hit
+// all 64 banks once.  K % 64 == 0 (checked by the host).
+constexpr int PJ_BM = 128, PJ_BN = 128, PJ_BK = 64;
+constexpr int PJ_LDS_STRIDE = PJ_BK + 8;
+constexpr int PJ_TILE = PJ_BM * PJ_LDS_STRIDE;  // bf16 per operand tile
 
 __global__ void __launch_bounds__(256) proj_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
     const uint16_t* __restrict__ w_gate, float* __restrict__ pg, int M, int E, int K,
     int k_per_split) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[PJ_BM * PJ_LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[PJ_BN * PJ_LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][PJ_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][PJ_TILE];
   const int N = 2 * E;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m0 = blockIdx.x * PJ_BM, n0 = blockIdx.y * PJ_BN;
   const int split = blockIdx.z;
   const int kb = split * k_per_split, ke = min(K, kb + k_per_split);
+  const int nk = (ke - kb) / PJ_BK;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  // global -> LDS: a tile row is 64 bf16 = 8 chunks of 16 B; 128 rows x 8 =
+  // 1024 chunks per operand, 4 per thread (rows r = c / 8, chunk q = c % 8)
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+  bool aok[4], bok[4];
+  for (int u = 0; u < 4; ++u) {
+    const int c = u * 256 + tid, r = c >> 3, q = c & 7;
+    const int gm = m0 + r, gn = n0 + r;
+    aok[u] = gm < M;
+    bok[u] = gn < N;
+    arow[u] = x + (size_t)(aok[u] ? gm : 0) * K + q * 8;
+    brow[u] = (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(bok[u] ? gn - E : 0) * K) + q * 8;
+  }
+  u32x4 ra[4], rb[4];
+  auto load = [&](int k0) {
+    for (int u = 0; u < 4; ++u) {
+      ra[u] = aok[u] ? *(const u32x4*)(arow[u] + k0) : u32x4{0, 0, 0, 0};
+      rb[u] = bok[u] ? *(const u32x4*)(brow[u] + k0) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store = [&](int buf) {
+    for (int u = 0; u < 4; ++u) {
+      const int c = u * 256 + tid, r = c >> 3, q = c & 7;
+      *(u32x4*)(&As[buf][r * PJ_LDS_STRIDE + q * 8]) = ra[u];
+      *(u32x4*)(&Bs[buf][r * PJ_LDS_STRIDE + q * 8]) = rb[u];
+    }
+  };
 
   f32x16 acc[2][2];
   for (int i = 0; i < 2; ++i)
     for (int j = 0; j < 2; ++j)
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // global -> LDS mapping: each tile row is 32 bf16 = 64 B = 4 chunks of 16 B;
-  // 128 rows x 4 chunks = 512 chunks per operand, 2 per thread.
-  for (int k0 = kb; k0 < ke; k0 += PJ_BK) {
-    for (int c = tid; c < PJ_BM * 4; c += 256) {
-      int r = c >> 2, q = c & 3;
-      u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-      int gm = m0 + r;
-      if (gm < M) va = *(const u32x4*)(x + (size_t)gm * K + k0 + q * 8);
-      int gn = n0 + r;
-      if (gn < N) {
-        const uint16_t* wrow = gn < E ? (w_kv + (size_t)gn * K) : (w_gate + (size_t)(gn - E) * K);
-        vb = *(const u32x4*)(wrow + k0 + q * 8);
-      }
-      *(u32x4*)(As + r * PJ_LDS_STRIDE + q * 8) = va;
-      *(u32x4*)(Bs + r * PJ_LDS_STRIDE + q * 8) = vb;
-    }
-    __syncthreads();
-    // two k-steps of 16; lane holds 8 consecutive k of one row (A) / column (B)
-    for (int ks = 0; ks < 2; ++ks) {
+  if (nk > 0) {
+    load(kb);
+    store(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load(kb + (kt + 1) * PJ_BK);
+    // four k steps of 16; lane holds 8 consecutive k of one row (A) / column (B)
+    for (int ks = 0; ks < PJ_BK / 16; ++ks) {
       bf16x8 a[2], b[2];
-      for (int i = 0; i < 2; ++i) {
-        int row = wm + i * 32 + (lane & 31);
-        a[i] = *(const bf16x8*)(As + row * PJ_LDS_STRIDE + ks * 16 + (lane >> 5) * 8);
-      }
-      for (int j = 0; j < 2; ++j) {
-        int col = wn + j * 32 + (lane & 31);
-        b[j] = *(const bf16x8*)(Bs + col * PJ_LDS_STRIDE + ks * 16 + (lane >> 5) * 8);
-      }
+      for (int i = 0; i < 2; ++i)
+        a[i] = *(const bf16x8*)(&As[buf][(wm + i * 32 + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 +
+                                         (lane >> 5) * 8]);
+      for (int j = 0; j < 2; ++j)
+        b[j] = *(const bf16x8*)(&Bs[buf][(wn + j * 32 + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 +
+                                         (lane >> 5) * 8]);
       for (int i = 0; i < 2; ++i)
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+    if (kt + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
   // accumulator layout (32x32): lane holds column (lane & 31), rows
@@ -106,33 +132,6 @@ __global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__
   pg[id] = s;
 }
 
-// ---------------------------------------------------------------- split-K sum
-// pg[0][i] = sum_s pg[s][i] in a fixed order, in place.  A workgroup owns 64
-// consecutive elements; its 4 waves sum interleaved quarters of the splits
-// and the quarters are added in LDS.
-__global__ void __launch_bounds__(256) split_sum_kernel(float* __restrict__ pg, size_t n,
-                                                        int n_split) {
-  __shared__ float part[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const size_t i = (size_t)blockIdx.x * 64 + lane;
-  float v = 0.0f;
-  if (i < n) {
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int s = wave;
-    for (; s + 12 < n_split; s += 16) {
-      a[0] += pg[(size_t)s * n + i];
-      a[1] += pg[(size_t)(s + 4) * n + i];
-      a[2] += pg[(size_t)(s + 8) * n + i];
-      a[3] += pg[(size_t)(s + 12) * n + i];
-    }
-    for (; s < n_split; s += 4) a[0] += pg[(size_t)s * n + i];
-    v = (a[0] + a[1]) + (a[2] + a[3]);
-  }
-  part[wave][lane] = v;
-  __syncthreads();
-  if (wave == 0 && i < n) pg[i] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-}
-
 // ---------------------------------------------------------------- pool
 // Grid (n_slots + 1, B).  Slot q < n_slots handles entry i_lo(b) + q; the last
 // slot writes state_out.  Each thread owns channels e = tid, tid + 256, ...
@@ -141,7 +140,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
     const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, float* __restrict__ out_scale,
-    int Nc_cap, int n_slots) {
+    int Nc_cap, int n_slots, int n_split) {
   const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
   const int ns = (1 + overlap) * m - 1;
   const int64_t p0 = pos0[b];
@@ -154,9 +153,25 @@ __global__ void __launch_bounds__(256) pool_kernel(
     gv = -INFINITY;
     if (j < 0) return;
     if (j >= p0) {
+      // the projection's split-K partials are summed here, in split order
       const float* r = pg + ((size_t)b * L + (size_t)(j - p0)) * N;
+      const size_t stride = (size_t)B * L * N;
       pv = r[e];
       gv = r[E + e];
+      for (int s0 = 1; s0 < n_split; s0 += 8) {  // eight splits' loads in flight
+        float a[8], c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool ok = s0 + u < n_split;
+          a[u] = ok ? r[(s0 + u) * stride + e] : 0.0f;
+          c[u] = ok ? r[(s0 + u) * stride + E + e] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          pv += a[u];
+          gv += c[u];
+        }
+      }
       return;
     }
     if (!state_in) return;
@@ -256,8 +271,11 @@ static int proj_splits(int M, int E, int K, csa_dtype_t dt) {
   if (dt != CSA_DT_BF16) return 1;
   int tiles = ((M + PJ_BM - 1) / PJ_BM) * ((2 * E + PJ_BN - 1) / PJ_BN);
   int s = 1;
-  // split K while the grid is small and every split keeps >= 64 k
-  while (tiles * s < 256 && K / (2 * s) >= 64 && (K / (2 * s)) % PJ_BK == 0) s *= 2;
+  // split K while the grid holds fewer than two workgroups per CU; every
+  // split keeps whole k tiles - at least four when the pool has many rows to
+  // re-read the partials for, one for the few rows of a decode step
+  const int min_k = M <= PJ_BM ? 2 * PJ_BK : 4 * PJ_BK;
+  while (tiles * s < 512 && K / (2 * s) >= min_k && (K / (2 * s)) % PJ_BK == 0) s *= 2;
   return s;
 }
 
@@ -283,27 +301,23 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
     proj_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
         (const float*)a.x, (const float*)a.w_kv, (const float*)a.w_gate, pg, M, E, K);
   }
-  if (splits > 1) {
-    const size_t n = (size_t)M * 2 * E;
-    split_sum_kernel<<<(unsigned)((n + 63) / 64), 256, 0, st>>>(pg, n, splits);
-  }
   const int n_slots = (a.L + a.m - 1) / a.m + 1;
   dim3 pgrid(n_slots + 1, a.B);
   switch (a.out_dt) {
     case CSA_DT_F32:
       pool_kernel<CSA_DT_F32><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m,
                                                       a.overlap, a.ape, a.state_in, a.state_out,
-                                                      a.out, a.out_scale, a.Nc_cap, n_slots);
+                                                      a.out, a.out_scale, a.Nc_cap, n_slots, splits);
       break;
     case CSA_DT_BF16:
       pool_kernel<CSA_DT_BF16><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m,
                                                        a.overlap, a.ape, a.state_in, a.state_out,
-                                                       a.out, a.out_scale, a.Nc_cap, n_slots);
+                                                       a.out, a.out_scale, a.Nc_cap, n_slots, splits);
       break;
     default:
       pool_kernel<CSA_DT_FP8E4M3><<<pgrid, 256, 0, st>>>(
           pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,
-          a.out_scale, a.Nc_cap, n_slots);
+          a.out_scale, a.Nc_cap, n_slots, splits);
   }
   return hipGetLastError();
 }

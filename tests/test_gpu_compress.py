@@ -163,3 +163,24 @@ def test_compress_prefill_8k_sampled_entries():
             ref, wr, _ = _oracle(xs, wk, wg, [lo], w.m, w.overlap, Nc)
             assert wr[0, i]
             assert_bf16_close(g[0, i], ref[0, i], "prefill entry %d" % i)
+
+
+def test_compress_bf16_ragged_tiles_and_split_k():
+    # output width 2E = 80 (a partial 128-column tile), 300 rows (a partial
+    # 128-row tile) and d_model 1024 so that the projection splits K and the
+    # pool sums the split partials
+    d = gen.Draw(19)
+    B, L, dm, E, m, o = 2, 150, 1024, 40, 4, 1
+    x = gen.store(d.normal(B, L, dm), gen.BF16)
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    pos0 = [3, 0]
+    Nc = 40
+    out, _, st = _run(x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), pos0, m, o, Nc, torch.float32)
+    ref, written, st_ref = _oracle(x, w_kv, w_gate, pos0, m, o, Nc)
+    g = out.cpu().numpy()
+    for b in range(B):
+        wr = written[b]
+        assert wr.any()
+        assert np.isnan(g[b, ~wr]).all()
+        assert_rows_rel(g[b, wr], ref[b, wr], 1e-5, "compress bf16 ragged tiles")
+    np.testing.assert_allclose(st.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=2e-5, atol=2e-5)
