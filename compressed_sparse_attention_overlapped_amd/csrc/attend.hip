@@ -86,13 +86,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
 // accumulator is the P^T operand once the second product's k order is
 // permuted to match, and V^T fragments come from the LDS transpose read.
 // K and V halves of a row sit in separate LDS arrays whose strides suit their
-// readers: 272 B for the 16-byte K reads (16 rows hit 16 distinct bank
-// groups), 288 B for the 8-byte transpose reads of V.  The running maximum is
+// readers: 272 B (68 dwords) for the 16-byte K reads, so that 16 rows hit 16
+// distinct 4-bank groups; 320 B (80 dwords, 16 mod 64) for the 8-byte
+// transpose reads of V, whose 32-lane halves cover 4 rows x 16 dwords each.
+// Every tile load is issued unconditionally (empty slots read a valid dummy
+// row and are masked), so that the waits count the loads exactly.  The running maximum is
 // only raised when a tile exceeds it by more than 2^8 (the final
 // normalisation makes the result independent of the maximum used).
 constexpr int PF_KT = 32;
 constexpr int PF_KS = 128 + 8;       // bf16 per K row in LDS (272 B)
-constexpr int PF_VS = 128 + 16;      // bf16 per V row in LDS (288 B)
+constexpr int PF_VS = 128 + 32;      // bf16 per V row in LDS (320 B)
 constexpr int PF_TILE = PF_KT * (PF_KS + PF_VS);
 constexpr int PF_IDX_MAX = 2048;     // index slots per row staged in LDS
 constexpr float PF_RESCALE = 8.0f;   // log2 headroom before the maximum is raised
@@ -129,6 +132,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
   const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
   const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
   const size_t rowi = (size_t)b * T + (active ? t : t_last);
+  const uint16_t* dummy = q + ((size_t)b * T + t0) * H * D;  // finite, readable row
 
   // this row's visibility
   const int nv_me = dense ? n_visible(pos, ncb, m, Nc_cap) : 0;
@@ -203,10 +207,8 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
   };
   // LDS stores of one 16-byte chunk of row rr: chunks 0..15 are K, 16..31 V
   auto put = [&](uint16_t* tile, int rr, int col, const u32x4& v) {
-    if (col < 16)
-      *(u32x4*)(tile + rr * PF_KS + 8 * col) = v;
-    else
-      *(u32x4*)(tile + PF_KT * PF_KS + rr * PF_VS + 8 * (col - 16)) = v;
+    const int off = col < 16 ? rr * PF_KS + 8 * col : PF_KT * PF_KS + rr * PF_VS + 8 * (col - 16);
+    *(u32x4*)(tile + off) = v;
   };
 
   // ---------------- phase A: shared contiguous segments
@@ -223,18 +225,17 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
   const int colA = tid & 31;
   u32x4 pfa[CHA];
   auto issueA = [&](int ti) {
+#pragma unroll
     for (int i = 0; i < CHA; ++i) {
       const int rr = i * (NT / 32) + (tid >> 5);
-      const uint16_t* src = nullptr;
-      if (ti < tiles0) {
-        const int e = ti * PF_KT + rr;
-        if (e < nv_max) src = kvc_b + (size_t)e * 2 * D;
-      } else {
-        const int64_t tok = win_first + (int64_t)(ti - tiles0) * PF_KT + rr;
-        const int64_t r = tok - rbase;
-        if (tok <= pos_last && r >= 0 && r < R_cap) src = kvr_b + (size_t)r * 2 * D;
-      }
-      pfa[i] = src ? *(const u32x4*)(src + 8 * colA) : u32x4{0, 0, 0, 0};
+      const int e = ti * PF_KT + rr;
+      const int64_t tok = win_first + (int64_t)(ti - tiles0) * PF_KT + rr;
+      const int64_t r = tok - rbase;
+      const bool okc = (ti < tiles0) & (e < nv_max);
+      const bool okr = (ti >= tiles0) & (tok <= pos_last) & (r >= 0) & (r < R_cap);
+      const uint16_t* src = okc ? kvc_b + (size_t)e * 2 * D : kvr_b + (size_t)r * 2 * D;
+      src = (okc | okr) ? src : dummy;
+      pfa[i] = *(const u32x4*)(src + 8 * colA);
     }
   };
   if (ntA > 0) {
@@ -289,10 +290,12 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
     uint16_t* mine = smem + row_w * PF_TILE;
     u32x4 pfb[CHB];
     auto issueB = [&](int ti) {
+#pragma unroll
       for (int i = 0; i < CHB; ++i) {
         const int rr = i * (64 * NH / 32) + (rt >> 5);
         const int j = active ? slot(ti * PF_KT + rr) : -1;
-        pfb[i] = j >= 0 ? *(const u32x4*)(kvc_b + (size_t)j * 2 * D + 8 * colB) : u32x4{0, 0, 0, 0};
+        const uint16_t* src = j >= 0 ? kvc_b + (size_t)j * 2 * D : dummy;
+        pfb[i] = *(const u32x4*)(src + 8 * colB);
       }
     };
     const int ntB = (topk + PF_KT - 1) / PF_KT;
@@ -338,7 +341,10 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
 // addresses lanes i/4 + 4 v supplied).  The rows of the next two tiles are
 // loaded into registers while the current one is computed.
 constexpr int DC_KT = 64;                // keys per tile
-constexpr int DC_ROW = 256 + 16;         // bf16 per LDS row (544 B: conflict-free reads)
+// K and V halves in separate LDS arrays: K rows of 68 dwords (16 rows of
+// 16-byte reads hit 16 distinct 4-bank groups), V rows of 72 dwords (the
+// transpose reads of a 32-lane half cover 8 rows x 8 dwords)
+constexpr int DC_KS = 128 + 8, DC_VS = 128 + 16;
 constexpr int DC_IDX_MAX = 4096;         // index slots staged in LDS per work item
 constexpr float DC_RESCALE = 8.0f;       // log2 headroom before the maximum is raised
 
@@ -353,7 +359,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
   constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
-  __shared__ __attribute__((aligned(16))) uint16_t tile[DC_KT * DC_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[DC_KT * (DC_KS + DC_VS)];
+  uint16_t* const vtile = tile + DC_KT * DC_KS;
   __shared__ __attribute__((aligned(16))) int vmask[DC_KT];
   __shared__ __attribute__((aligned(16))) int partial[4];
   __shared__ int idx_s[DC_IDX_MAX];
@@ -460,7 +467,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int rr = i * (NT / 32) + (tid >> 5);
-      *(u32x4*)(tile + rr * DC_ROW + 8 * col) = pf[i];
+      const int off = col < 16 ? rr * DC_KS + 8 * col : DC_KT * DC_KS + rr * DC_VS + 8 * (col - 16);
+      *(u32x4*)(tile + off) = pf[i];
       if (col == 0) vmask[rr] = pv[i];
       mine = mine && pv[i];
     }
@@ -473,7 +481,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     f32x4 sacc[4];
     bf16x8 kf[2][4];
     auto read_k = [&](int kb4, bf16x8(&f)[4]) {
-      const uint16_t* krow = tile + (16 * kb4 + hl) * DC_ROW + 8 * g;
+      const uint16_t* krow = tile + (16 * kb4 + hl) * DC_KS + 8 * g;
       for (int s = 0; s < 4; ++s) f[s] = *(const bf16x8*)(krow + 32 * s);
     };
     read_k(0, kf[0]);
@@ -527,8 +535,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
       }
       // transpose-read addresses: lane j of the group supplies row k0 + j/4,
       // dims D0 + 4 (j % 4)
-      const uint16_t* base1 = tile + (32 * ks + 4 * g + (hl >> 2)) * DC_ROW + D + 4 * (hl & 3);
-      const uint16_t* base2 = base1 + 16 * DC_ROW;
+      const uint16_t* base1 = vtile + (32 * ks + 4 * g + (hl >> 2)) * DC_VS + 4 * (hl & 3);
+      const uint16_t* base2 = base1 + 16 * DC_VS;
       // all 16 transpose reads first, then the 8 products (whole-register
       // moves only: the four 16-bit values of a transpose read are not
       // extracted one by one)
