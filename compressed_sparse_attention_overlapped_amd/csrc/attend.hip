@@ -476,21 +476,23 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     if (lane == 0) partial[wave] = wave_partial;
     __syncthreads();
     if constexpr (decltype(refill)::value) issue(ti + 2, pf, pv);
-    // ---- S^T = K Q^T for 4 blocks of 16 keys; the fragments of a block are
-    // read together, the next block's while the current one multiplies
+    // ---- S^T = K Q^T for 4 blocks of 16 keys; the fragments of a k step are
+    // read together, the next step's while the current one multiplies
+    // k step s of all four blocks back to back: consecutive MFMAs are
+    // independent (a dependent 16x16x32 waits out the full result latency)
     f32x4 sacc[4];
     bf16x8 kf[2][4];
-    auto read_k = [&](int kb4, bf16x8(&f)[4]) {
-      const uint16_t* krow = tile + (16 * kb4 + hl) * DC_KS + 8 * g;
-      for (int s = 0; s < 4; ++s) f[s] = *(const bf16x8*)(krow + 32 * s);
+    auto read_k = [&](int s, bf16x8(&f)[4]) {
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+        f[kb4] = *(const bf16x8*)(tile + (16 * kb4 + hl) * DC_KS + 8 * g + 32 * s);
     };
+    for (int kb4 = 0; kb4 < 4; ++kb4) sacc[kb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     read_k(0, kf[0]);
 #pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4) {
-      if (kb4 + 1 < 4) read_k(kb4 + 1, kf[(kb4 + 1) & 1]);
-      sacc[kb4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int s = 0; s < 4; ++s)
-        sacc[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb4 & 1][s], qf[s], sacc[kb4], 0,
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) read_k(s + 1, kf[(s + 1) & 1]);
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+        sacc[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][kb4], qf[s], sacc[kb4], 0,
                                                            0, 0);
     }
     // ---- online softmax over the 64 keys; lane: head hl, keys 16 kb4 + 4 g + i.
