@@ -40,6 +40,29 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 DEV = "cuda"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the stored counter
+    runs (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel calibration), or
+    None when none is stored or the kernel's source changed since."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entries = json.load(f)["entries"]
+    except (OSError, ValueError, KeyError):
+        return None
+    for e in entries:
+        if e.get("kernel") != kernel or e.get("workload") != workload:
+            continue
+        try:
+            with open(os.path.join(ROOT, e["source"]), "rb") as f:
+                digest = hashlib.sha256(f.read()).hexdigest()
+        except OSError:
+            return None
+        return e["bytes_per_launch"] if digest == e.get("source_sha256") else None
+    return None
 
 
 def i64(v):
@@ -352,7 +375,8 @@ def measure(name, steps, warmup, with_cpu):
             ach = attn_flops / (sm["sparse_attn"] / 1e3) / 1e12
             res["roofline"] = {"bound": "mfma", "kernel": "attn_pf_kernel",
                                "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                               "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                               "traffic": measured_traffic("attn_pf_kernel", name)}
         else:
             ach = attn_flops / (sm["sparse_attn"] / 1e3) / 1e12
             res["roofline"] = {"bound": "alu", "kernel": "attn_f32_kernel", "achieved": ach,
@@ -375,7 +399,8 @@ def measure(name, steps, warmup, with_cpu):
         ach = key_bytes / (sm["indexer_topk"] / 1e3) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "indexer_topk (score_fp8_kernel + select)",
                            "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBS, "traffic": None}
+                           "frac": ach / HBM_PEAK_GBS,
+                           "traffic": measured_traffic("indexer_topk", name)}
         res["work"] = {"step_bytes": total, "indexer_key_bytes": key_bytes,
                        "attn_gather_bytes": gather,
                        "step_hbm_frac": total / step_s / 1e9 / HBM_PEAK_GBS,
@@ -386,7 +411,8 @@ def measure(name, steps, warmup, with_cpu):
         ach = flops / step_s / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": "attn_pf_kernel (dense)", "achieved": ach,
                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                           "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                           "traffic": measured_traffic("attn_pf_kernel", name)}
         res["work"] = {"attn_gflop": flops / 1e9}
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
@@ -402,6 +428,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="default")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device to device three times (the reference "
+                         "kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (the path shards by sequence across "
@@ -411,6 +440,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device=DEV)
+        dst = torch.empty_like(src)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=DEV)
+        for _ in range(3):
+            flush_caches(flush)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
     csa.lib()
     if args.workload == "all":
         for name in gen.WORKLOADS:
