@@ -1,0 +1,66 @@
+"""The decode step (indexer top-k on long rows, split-key sparse attention)
+captured as a HIP graph and replayed gives the eager result on every replay.
+
+bench.py times decode steps as graph replays; this checks that capture adds
+nothing and drops nothing: all library launches are kernels (no memset), and
+every buffer is preallocated.  Replays are separated by eager work and host
+synchronisations, and each one is compared bit for bit with the eager run."""
+import pytest
+import torch
+
+import compressed_sparse_attention_overlapped_amd as csa
+from compressed_sparse_attention_overlapped_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def test_decode_step_graph_replays_match_eager():
+    d = gen.Draw(31, DEV)
+    B, Nc, m, topk, W, H, D = 4, 20000, 4, 512, 64, 64, 128
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, 1, 16, 64, gen.FP8)
+    kv = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kvr = gen.store(d.normal(B, W, 2 * D), gen.BF16)
+    q = gen.store(d.normal(B, 1, H, D), gen.BF16)
+    ctx = [4 * Nc, 4 * Nc - 9, 4 * 15000 + 2, 4 * 3000]      # ragged visibility
+    q_pos = torch.tensor([c - 1 for c in ctx], dtype=torch.int64, device=DEV)
+    n_cmp = torch.tensor([Nc] * B, dtype=torch.int32, device=DEV)
+    raw_base = torch.tensor([c - W for c in ctx], dtype=torch.int64, device=DEV)
+    idx = torch.empty(B, 1, topk, dtype=torch.int32, device=DEV)
+    out = torch.empty(B, 1, H, D, dtype=torch.bfloat16, device=DEV)
+    ws_i = torch.empty(csa.csa_indexer_topk_workspace_size(B, 1, 16, 64, Nc, topk, torch.float8_e4m3fn),
+                       dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(B, 1, H, D, topk, W)),
+                       dtype=torch.uint8, device=DEV)
+
+    def step():
+        csa.csa_indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=q_scale,
+                             k_scale=k_scale, idx_out=idx, workspace=ws_i)
+        csa.csa_sparse_attn(q, kv, idx, kvr, W, q_pos, raw_base, out=out, workspace=ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    ref_idx, ref_out = idx.clone(), out.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        idx.fill_(-7)
+        out.fill_(float("nan"))
+        ws_i.fill_(0xA5)                 # stale workspace contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx), "replay %d: indices differ" % rep
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "replay %d" % rep
+        step()                           # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx) and torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
