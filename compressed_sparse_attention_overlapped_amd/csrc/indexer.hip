@@ -8,10 +8,10 @@
 // Selection keeps the min(topk, n_vis) best scores under (score desc, index
 // asc) and writes them in ascending index order, -1 padded.  Scores map to
 // order-preserving 32-bit keys.
-//  * short rows (Nc_cap <= kShortMax): one workgroup per row; the keys sit in
-//    LDS, an MSB-first radix select (8-bit digits) finds the k-th key, and an
-//    ordered compaction writes the selected indices, taking equal keys in
-//    index order.
+//  * short rows (Nc_cap <= kShortMax): one wave per row; the keys sit in LDS,
+//    an MSB-first radix select (8-bit digits) finds the k-th key, and an
+//    ordered pass writes the selected indices, taking equal keys in index
+//    order.
 //  * long rows: the score kernel also builds a per-row histogram of the top
 //    11 key bits; "collect" workgroups (one per 2048-entry chunk) find the
 //    bin holding the k-th key, mark the chunk's entries above it (certainly
@@ -349,129 +349,128 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
   }
 }
 
-// MSB-first radix select (8-bit digits) of the `need` largest of n keys,
-// 1 <= need <= n.  get(i) returns key i.  The result describes the selected
-// set: all_eq -> {x : (x & mask) >= prefix}; otherwise the key width got fully
-// resolved and the set is {x > prefix} plus `remaining` keys equal to prefix.
-// hist: 256 words of LDS; sh: >= 24 words; blockDim.x >= 256.
+// Result of an MSB-first radix select of the `need` largest of n keys: with
+// all_eq the selected set is {x : (x & mask) >= prefix}; otherwise the key
+// width got fully resolved and the set is {x > prefix} plus `remaining` keys
+// equal to prefix.
 struct RadixResult {
   uint32_t prefix, mask, remaining;
   bool all_eq;
 };
 
-// Digit search of one radix pass, in parallel: thread i owns bin 255 - i
-// (blockDim.x >= 256); a block scan gives the count above each bin.  Sets
-// sh[0] = digit, sh[1] = count above it, sh[2] = its count.
-__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remaining,
-                                           uint32_t* sh) {
-  const int tid = threadIdx.x;
-  const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
-  uint32_t tot;
-  const uint32_t above = block_excl_scan(c, sh + 8, tot);
-  if (tid < 256 && above < remaining && above + c >= remaining) {
-    sh[0] = 255u - tid;
-    sh[1] = above;
-    sh[2] = c;
-  }
-  __syncthreads();
-}
-
-template <class Get>
-__device__ RadixResult radix_select(Get get, int n, uint32_t need, uint32_t* hist,
-                                    uint32_t* sh) {
-  RadixResult r{0u, 0u, need, false};
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      uint32_t x = get(i);
-      if ((x & r.mask) == r.prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    // digit d with cum_above(d) < remaining <= cum_above(d) + hist[d]
-    find_digit(hist, r.remaining, sh);
-    uint32_t d = sh[0], cum = sh[1], cnt = sh[2];
-    __syncthreads();
-    r.remaining -= cum;
-    r.prefix |= d << shift;
-    r.mask |= 255u << shift;
-    if (cnt == r.remaining) {
-      r.all_eq = true;
-      break;
-    }
-  }
-  return r;
-}
-
-__device__ RadixResult radix_select_u32(const uint32_t* keys, int n, uint32_t need,
-                                        uint32_t* hist, uint32_t* sh) {
-  return radix_select([&](int i) { return keys[i]; }, n, need, hist, sh);
-}
-
 // ---------------------------------------------------------------- short rows
-// One workgroup (256 threads) per row; Nc_cap <= kShortMax.
+// One wave per row (4 rows per workgroup), Nc_cap <= KMAX: the row's keys sit
+// in the wave's LDS slice, an MSB-first radix select (8-bit digits, a
+// wave-private 256-bin histogram) finds the k-th key, and one ordered pass
+// over 64-key groups (ballots) writes the selected indices ascending, taking
+// keys equal to the k-th in index order.  No workgroup barrier: every step
+// is the wave's own, and a wave's LDS operations complete in issue order.
+template <int KMAX>
 __global__ void __launch_bounds__(256) select_short_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk,
+    const int32_t* __restrict__ n_cmp, int rows, int T, int Nc_cap, int m, int topk,
     int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
-  __shared__ uint32_t keys[kShortMax];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[32];
-  const int row = blockIdx.x, b = row / T, t = row % T;
-  const int tid = threadIdx.x;
+  __shared__ uint32_t keys_all[4][KMAX];
+  __shared__ uint32_t hist_all[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const int b = row / T, t = row % T;
+  uint32_t* keys = keys_all[wave];
+  uint32_t* hist = hist_all[wave];
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const float* srow = scores + (size_t)row * Nc_cap;
   int32_t* orow = idx_out + (size_t)row * topk;
   float* sorow = score_out ? score_out + (size_t)row * topk : nullptr;
   const int nsel = min(topk, nv);
-  // pad
-  for (int k = nsel + tid; k < topk; k += blockDim.x) {
+  for (int k = nsel + lane; k < topk; k += 64) {
     orow[k] = -1;
     if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
   }
   if (nsel == 0) return;
   if (nsel == nv) {  // everything visible is selected
-    for (int j = tid; j < nv; j += blockDim.x) {
+    for (int j = lane; j < nv; j += 64) {
       orow[j] = j;
       if (sorow) sorow[j] = srow[j];
     }
     return;
   }
-  for (int j = tid; j < nv; j += blockDim.x) keys[j] = score_key(srow[j]);
-  __syncthreads();
-  RadixResult rr = radix_select_u32(keys, nv, (uint32_t)nsel, hist, sh);
-  // ordered compaction: thread owns indices [c0, c1)
-  const int per = (nv + blockDim.x - 1) / blockDim.x;
-  const int c0 = min(nv, tid * per), c1 = min(nv, c0 + per);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int j = c0; j < c1; ++j) {
-    uint32_t x = keys[j] & rr.mask;
-    if (x > rr.prefix) ++n_gt;
-    else if (x == rr.prefix) ++n_eq;
+  for (int j0 = 0; j0 < nv; j0 += 256) {  // four loads in flight per lane
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = j0 + 64 * u + lane < nv ? srow[j0 + 64 * u + lane] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + 64 * u + lane < nv) keys[j0 + 64 * u + lane] = score_key(v[u]);
   }
-  uint32_t tot;
-  uint32_t eq_base = block_excl_scan(n_eq, sh, tot);
-  // equal keys taken in index order: all of them if all_eq, else the first
-  // `remaining`
-  uint32_t take_eq = 0;
-  {
-    uint32_t lim = rr.all_eq ? 0xffffffffu : rr.remaining;
-    if (eq_base < lim) take_eq = min(n_eq, lim - eq_base);
-  }
-  uint32_t out_base = block_excl_scan(n_gt + take_eq, sh, tot);
-  uint32_t taken = 0, pos = out_base;
-  for (int j = c0; j < c1; ++j) {
-    uint32_t x = keys[j] & rr.mask;
-    bool sel = x > rr.prefix;
-    if (!sel && x == rr.prefix && taken < take_eq) {
-      sel = true;
-      ++taken;
+  // radix select: lane l owns bins 255 - 4 l .. 252 - 4 l of each pass
+  uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)nsel;
+  bool all_eq = false;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0u;
+    for (int j = lane; j < nv; j += 64) {
+      const uint32_t x = keys[j];
+      if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
+    uint32_t c[4], sum = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = hist[255 - (4 * lane + i)];
+      sum += c[i];
+    }
+    uint32_t incl = sum;  // inclusive prefix over lanes (lane 0 = top bins)
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    uint32_t above = incl - sum;
+    int dsel = -1;
+    uint32_t cum_sel = 0u, cnt_sel = 0u;
+    if (above < remaining && above + sum >= remaining) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (dsel < 0 && above + c[i] >= remaining) {
+          dsel = 255 - (4 * lane + i);
+          cum_sel = above;
+          cnt_sel = c[i];
+        }
+        above += c[i];
+      }
+    }
+    const uint64_t who = __ballot(dsel >= 0);
+    const int src = (int)__ffsll((unsigned long long)who) - 1;
+    const uint32_t d = (uint32_t)__shfl(dsel, src, 64);
+    const uint32_t cum = __shfl(cum_sel, src, 64), cnt = __shfl(cnt_sel, src, 64);
+    remaining -= cum;
+    prefix |= d << shift;
+    mask |= 255u << shift;
+    if (cnt == remaining) {
+      all_eq = true;
+      break;
+    }
+  }
+  // ordered output: groups of 64 consecutive entries
+  uint32_t out_base = 0u, eq_taken = 0u;
+  for (int j0 = 0; j0 < nv; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t x = j < nv ? keys[j] & mask : 0u;
+    const bool gt = j < nv && x > prefix;
+    const bool eq = j < nv && x == prefix;
+    const uint64_t eqm = __ballot(eq);
+    const uint32_t eq_rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
+    const bool sel = gt || (eq && (all_eq || eq_taken + eq_rank < remaining));
+    const uint64_t sm = __ballot(sel);
     if (sel) {
+      const uint32_t pos = out_base + __builtin_amdgcn_mbcnt_hi(
+                                          (uint32_t)(sm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
       orow[pos] = j;
       if (sorow) sorow[pos] = srow[j];
-      ++pos;
     }
+    out_base += (uint32_t)__popcll(sm);
+    eq_taken += (uint32_t)__popcll(eqm);
   }
 }
 
@@ -845,8 +844,14 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
                                                  a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist);
   }
   if (!L.long_rows) {
-    select_short_kernel<<<rows, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m,
-                                              a.topk, a.idx_out, a.score_out);
+    const unsigned g = (unsigned)((rows + 3) / 4);
+    if (a.Nc_cap <= 2048)
+      select_short_kernel<2048><<<g, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, rows, a.T, a.Nc_cap,
+                                                   a.m, a.topk, a.idx_out, a.score_out);
+    else
+      select_short_kernel<kShortMax><<<g, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, rows, a.T,
+                                                        a.Nc_cap, a.m, a.topk, a.idx_out,
+                                                        a.score_out);
   } else {
     uint32_t* cnt = (uint32_t*)(ws + L.chunk_cnt);
     uint32_t* bm = (uint32_t*)(ws + L.def_bm);
