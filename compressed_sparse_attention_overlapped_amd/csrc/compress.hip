@@ -21,10 +21,14 @@ namespace csa {
 // ---------------------------------------------------------------- proj (bf16)
 // Tile 128 x 128 x 64, 256 threads = 4 waves in a 2 x 2 grid of 64 x 64
 // (2 x 2 MFMA 32x32x16 per 16-deep k step).  The LDS tiles are double
-// buffered and the next k tile is loaded into registers while the current
-// one multiplies: one barrier per k tile.  LDS rows are padded to 72 bf16
-// (36 dwords) so that the 16-byte fragment reads of 16 consecutive rows hit
-// all 64 banks once.  K % 64 == 0 (checked by the host).
+// buffered; two more k tiles are in flight in two register stages (k tile
+// t + 2 is requested as soon as k tile t has moved to LDS), so the load
+// latency is hidden behind two tiles of products.  Loads are unconditional
+// (rows past M and columns past N read row 0 and are dropped at the store;
+// k tiles past the end re-read the last one) so that every wait counts them
+// exactly.  LDS rows are padded to 72 bf16 (36 dwords) so that the 16-byte
+// fragment reads of 16 consecutive rows hit all 64 banks once.  K % 64 == 0
+// (checked by the host).
 constexpr int PJ_BM = 128, PJ_BN = 128, PJ_BK = 64;
 constexpr int PJ_LDS_STRIDE = PJ_BK + 8;
 constexpr int PJ_TILE = PJ_BM * PJ_LDS_STRIDE;  // bf16 per operand tile
@@ -48,27 +52,27 @@ __global__ void __launch_bounds__(256) proj_bf16_kernel(
   // 1024 chunks per operand, 4 per thread (rows r = c / 8, chunk q = c % 8)
   const uint16_t* arow[4];
   const uint16_t* brow[4];
-  bool aok[4], bok[4];
   for (int u = 0; u < 4; ++u) {
     const int c = u * 256 + tid, r = c >> 3, q = c & 7;
-    const int gm = m0 + r, gn = n0 + r;
-    aok[u] = gm < M;
-    bok[u] = gn < N;
-    arow[u] = x + (size_t)(aok[u] ? gm : 0) * K + q * 8;
-    brow[u] = (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(bok[u] ? gn - E : 0) * K) + q * 8;
+    const int gm = m0 + r < M ? m0 + r : 0, gn = n0 + r < N ? n0 + r : 0;
+    arow[u] = x + (size_t)gm * K + kb + q * 8;
+    brow[u] = (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(gn - E) * K) + kb + q * 8;
   }
-  u32x4 ra[4], rb[4];
-  auto load = [&](int k0) {
+  u32x4 ra[2][4], rb[2][4];
+  auto load = [&](int kt, u32x4(&a)[4], u32x4(&bq)[4]) {
+    const int k0 = min(kt, nk - 1) * PJ_BK;
+#pragma unroll
     for (int u = 0; u < 4; ++u) {
-      ra[u] = aok[u] ? *(const u32x4*)(arow[u] + k0) : u32x4{0, 0, 0, 0};
-      rb[u] = bok[u] ? *(const u32x4*)(brow[u] + k0) : u32x4{0, 0, 0, 0};
+      a[u] = *(const u32x4*)(arow[u] + k0);
+      bq[u] = *(const u32x4*)(brow[u] + k0);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const u32x4(&a)[4], const u32x4(&bq)[4]) {
+#pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = u * 256 + tid, r = c >> 3, q = c & 7;
-      *(u32x4*)(&As[buf][r * PJ_LDS_STRIDE + q * 8]) = ra[u];
-      *(u32x4*)(&Bs[buf][r * PJ_LDS_STRIDE + q * 8]) = rb[u];
+      *(u32x4*)(&As[buf][r * PJ_LDS_STRIDE + q * 8]) = a[u];
+      *(u32x4*)(&Bs[buf][r * PJ_LDS_STRIDE + q * 8]) = bq[u];
     }
   };
 
@@ -77,15 +81,9 @@ __global__ void __launch_bounds__(256) proj_bf16_kernel(
     for (int j = 0; j < 2; ++j)
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if (nk > 0) {
-    load(kb);
-    store(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load(kb + (kt + 1) * PJ_BK);
+  auto compute = [&](int buf) {
     // four k steps of 16; lane holds 8 consecutive k of one row (A) / column (B)
+#pragma unroll
     for (int ks = 0; ks < PJ_BK / 16; ++ks) {
       bf16x8 a[2], b[2];
       for (int i = 0; i < 2; ++i)
@@ -98,8 +96,33 @@ __global__ void __launch_bounds__(256) proj_bf16_kernel(
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store(buf ^ 1);
+  };
+  // step kt: multiply k tile kt (LDS buffer kt & 1), move k tile kt + 1 from
+  // its register stage to the other buffer, refill that stage with k tile
+  // kt + 3
+  auto step = [&](int kt, u32x4(&a)[4], u32x4(&bq)[4]) {
+    compute(kt & 1);
+    store((kt + 1) & 1, a, bq);
+    load(kt + 3, a, bq);
     __syncthreads();
+  };
+  if (nk > 0) {
+    load(0, ra[0], rb[0]);
+    store(0, ra[0], rb[0]);
+    load(1, ra[1], rb[1]);
+    load(2, ra[0], rb[0]);
+    __syncthreads();
+    int kt = 0;
+    // stage (kt + 1) & 1 holds k tile kt + 1
+    for (; kt + 2 < nk; kt += 2) {
+      step(kt, ra[1], rb[1]);
+      step(kt + 1, ra[0], rb[0]);
+    }
+    for (; kt < nk; ++kt) {  // the last one or two k tiles
+      compute(kt & 1);
+      if (kt + 1 < nk) store((kt + 1) & 1, (kt & 1) ? ra[0] : ra[1], (kt & 1) ? rb[0] : rb[1]);
+      __syncthreads();
+    }
   }
   // accumulator layout (32x32): lane holds column (lane & 31), rows
   // 8 (r / 4) + 4 (lane / 32) + (r % 4)
@@ -275,7 +298,8 @@ static int proj_splits(int M, int E, int K, csa_dtype_t dt) {
   // split keeps whole k tiles - at least four when the pool has many rows to
   // re-read the partials for, one for the few rows of a decode step
   const int min_k = M <= PJ_BM ? 2 * PJ_BK : 4 * PJ_BK;
-  while (tiles * s < 512 && K / (2 * s) >= min_k && (K / (2 * s)) % PJ_BK == 0) s *= 2;
+  const int target = M <= PJ_BM ? 512 : 128;
+  while (tiles * s < target && K / (2 * s) >= min_k && (K / (2 * s)) % PJ_BK == 0) s *= 2;
   return s;
 }
 
