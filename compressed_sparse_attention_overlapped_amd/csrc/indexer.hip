@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     const uint16_t* __restrict__ k_idx, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int key_chunk,
     float* __restrict__ scores, uint32_t* __restrict__ ghist) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[SB_KT * SB_KSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][SB_KT * SB_KSTRIDE];
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
   const int b = blockIdx.z, t0 = blockIdx.x * SB_ROWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -156,14 +156,12 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     int tt = t0 + wave * 4 + mt * 2 + ((lane & 31) >> 4);
     trow[mt] = tt;
     int h = lane & 15;
-    for (int s = 0; s < 4; ++s) {
-      if (tt < T) {
-        a[mt][s] = *(const bf16x8*)(q_idx + (((size_t)b * T + tt) * 16 + h) * 64 + 16 * s +
-                                    8 * (lane >> 5));
-      } else {
-        for (int e = 0; e < 8; ++e) a[mt][s][e] = (__bf16)0.0f;
-      }
-    }
+    // rows past T read row T - 1 (loads stay unconditional, so that the
+    // waits in the key loop count loads exactly); their scores are not stored
+    const int tq = min(tt, T - 1);
+    for (int s = 0; s < 4; ++s)
+      a[mt][s] = *(const bf16x8*)(q_idx + (((size_t)b * T + tq) * 16 + h) * 64 + 16 * s +
+                                  8 * (lane >> 5));
   }
   // head weights for the accumulator rows: tile mt, register r -> token
   // wave*4 + mt*2 + r/8, head 8 ((r%8)/4) + 4 (lane/32) + r%4
@@ -173,7 +171,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     for (int r = 0; r < 16; ++r) {
       int tt = t0 + wave * 4 + mt * 2 + (r >> 3);
       int h = 8 * ((r & 7) >> 2) + 4 * (lane >> 5) + (r & 3);
-      wv[mt][r] = tt < T ? w_idx[((size_t)b * T + tt) * 16 + h] : 0.0f;
+      wv[mt][r] = w_idx[((size_t)b * T + min(tt, T - 1)) * 16 + h];
     }
     for (int u = 0; u < 2; ++u) {
       int tt = t0 + wave * 4 + mt * 2 + u;
@@ -182,38 +180,65 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
   }
   __syncthreads();
 
-  for (int j0 = jb; j0 < je; j0 += SB_KT) {
-    // stage 64 keys x 128 B: 512 chunks of 16 B, 2 per thread
-    for (int c = tid; c < SB_KT * 8; c += 256) {
-      int r = c >> 3, q8 = c & 7;
-      u32x4 v = {0, 0, 0, 0};
-      if (j0 + r < je) v = *(const u32x4*)(k_idx + ((size_t)b * Nc_cap + j0 + r) * 64 + q8 * 8);
-      *(u32x4*)(Ks + r * SB_KSTRIDE + q8 * 8) = v;
+  // 64-key tiles, LDS double-buffered; the next tile's 512 chunks of 16 B
+  // (2 per thread) load into registers while the current one multiplies.
+  // Rows past je re-read row je - 1 (valid) and their scores are not stored.
+  u32x4 pk[2];
+  auto loadk = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid, r = c >> 3, q8 = c & 7;
+      const int row = min(j0 + r, je - 1);
+      pk[i] = *(const u32x4*)(k_idx + ((size_t)b * Nc_cap + row) * 64 + q8 * 8);
     }
-    __syncthreads();
+  };
+  auto storek = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid, r = c >> 3, q8 = c & 7;
+      *(u32x4*)(Ks[buf] + r * SB_KSTRIDE + q8 * 8) = pk[i];
+    }
+  };
+  if (jb < je) {
+    loadk(jb);
+    storek(0);
+    loadk(jb + SB_KT);
+  }
+  __syncthreads();
+  for (int j0 = jb, it = 0; j0 < je; j0 += SB_KT, ++it) {
+    const uint16_t* kt = Ks[it & 1];
     for (int nt = 0; nt < 2; ++nt) {
       bf16x8 bk[4];
       for (int s = 0; s < 4; ++s)
-        bk[s] = *(const bf16x8*)(Ks + (nt * 32 + (lane & 31)) * SB_KSTRIDE + 16 * s + 8 * (lane >> 5));
+        bk[s] = *(const bf16x8*)(kt + (nt * 32 + (lane & 31)) * SB_KSTRIDE + 16 * s + 8 * (lane >> 5));
       const int j = j0 + nt * 32 + (lane & 31);
+      // the two row tiles' products interleaved: consecutive MFMAs independent
+      f32x16 acc[2];
+      for (int mt = 0; mt < 2; ++mt)
+        for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
+      for (int s = 0; s < 4; ++s)
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][s], bk[s], acc[mt], 0, 0, 0);
       for (int mt = 0; mt < 2; ++mt) {
-        f32x16 acc;
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-        for (int s = 0; s < 4; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][s], bk[s], acc, 0, 0, 0);
         float s0 = 0.0f, s1 = 0.0f;
-        for (int r = 0; r < 8; ++r) s0 = fmaf(wv[mt][r], fmaxf(acc[r], 0.0f), s0);
-        for (int r = 8; r < 16; ++r) s1 = fmaf(wv[mt][r], fmaxf(acc[r], 0.0f), s1);
+        for (int r = 0; r < 8; ++r) s0 = fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.0f), s0);
+        for (int r = 8; r < 16; ++r) s1 = fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.0f), s1);
         s0 = sum_xor32(s0);
         s1 = sum_xor32(s1);
         const int u = lane >> 5;  // lanes < 32 write token 0 of the pair, others token 1
         const float sc = u ? s1 : s0;
         const int tt = trow[mt] - ((lane & 31) >> 4) + u;
-        if (tt < T && j < nvis[mt][u]) {
+        if (tt < T && j < je && j < nvis[mt][u]) {
           scores[((size_t)b * T + tt) * Nc_cap + j] = sc;
           if (HIST) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
         }
       }
+    }
+    if (j0 + SB_KT < je) {
+      // buffer (it + 1) & 1 was last read for tile it - 1, before the
+      // previous barrier
+      storek((it + 1) & 1);
+      loadk(j0 + 2 * SB_KT);
     }
     __syncthreads();
   }
