@@ -100,18 +100,23 @@ constexpr int PF_TILE = PF_KT * (PF_KS + PF_VS);
 constexpr int PF_IDX_MAX = 2048;     // index slots per row staged in LDS
 constexpr float PF_RESCALE = 8.0f;   // log2 headroom before the maximum is raised
 
-template <int NH, int PF_ROWS>  // H = 32 NH: waves per row; query rows per workgroup
-__global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
+// H = 32 NH: waves per row; PF_ROWS query rows per workgroup; SPARSE: CSA
+// (top-k entries + window) rather than HCA (every visible entry + window).
+// Two waves per SIMD: the register budget is held to 256 so that a second
+// workgroup hides the first one's load and barrier latency.
+template <int NH, int PF_ROWS, bool SPARSE>
+__global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv_cmp,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
-    int R_cap, bool dense, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int R_cap, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH;
+  constexpr bool dense = !SPARSE;
   // phase A uses tiles 0..1 (double buffer); phase B tile r per row
-  constexpr int NTILES = PF_ROWS > 2 ? PF_ROWS : 2;
+  constexpr int NTILES = SPARSE && PF_ROWS > 2 ? PF_ROWS : 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NTILES * PF_TILE];
-  __shared__ int idx_all[PF_ROWS][PF_IDX_MAX];
+  __shared__ int idx_all[SPARSE ? PF_ROWS : 1][SPARSE ? PF_IDX_MAX : 1];
   // the wave index is a scalar so that every per-wave decision below is a
   // uniform branch
   const int tid = threadIdx.x, lane = tid & 63;
@@ -268,45 +273,66 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH) attn_pf_kernel(
   }
 
   // ---------------- phase B: each row's selected compressed entries
-  if (!dense && topk > 0) {
-    // stage the index rows (every thread takes part: barriers follow)
-    const bool stage = topk <= PF_IDX_MAX;
+  // The index rows are staged in LDS, PF_IDX_MAX slots at a time, so that the
+  // gathered loads of a tile never wait on an index load.
+  if (SPARSE && topk > 0) {
     const int32_t* idx_rows = idx + ((size_t)b * T + t0) * topk;
     const int nrows = t_last - t0 + 1;
-    if (stage)
-      for (int i = tid; i < nrows * topk; i += NT) idx_all[i / topk][i % topk] = idx_rows[i];
-    __syncthreads();
-    const int32_t* idx_row = idx + rowi * topk;
     const int* idx_s = idx_all[row_w];
-    auto slot = [&](int p) -> int {
-      if (p >= topk) return -1;
-      const int j = stage ? idx_s[p] : idx_row[p];
-      return (j < 0 || j >= Nc_cap) ? -1 : j;
-    };
     // the row's NH waves load its tile: 1024 chunks over 64 NH threads
     constexpr int CHB = PF_KT * 32 / (64 * NH);
     const int rt = (wave % NH) * 64 + lane;     // thread index within the row
     const int colB = rt & 31;
     uint16_t* mine = smem + row_w * PF_TILE;
-    u32x4 pfb[CHB];
-    auto issueB = [&](int ti) {
+    for (int c0 = 0; c0 < topk; c0 += PF_IDX_MAX) {
+      const int cn = min(PF_IDX_MAX, topk - c0);
+      // every thread takes part: the barrier below, and the last one of the
+      // previous chunk's tile loop, order these stores against the reads
+      // (loads batched four per thread, from clamped addresses, before the
+      // stores)
+      const int n_st = nrows * cn;
+      for (int i0 = 0; i0 < n_st; i0 += 4 * NT) {
+        int v[4];
 #pragma unroll
-      for (int i = 0; i < CHB; ++i) {
-        const int rr = i * (64 * NH / 32) + (rt >> 5);
-        const int j = active ? slot(ti * PF_KT + rr) : -1;
-        const uint16_t* src = j >= 0 ? kvc_b + (size_t)j * 2 * D : dummy;
-        pfb[i] = *(const u32x4*)(src + 8 * colB);
+        for (int u = 0; u < 4; ++u) {
+          const int i = min(i0 + u * NT + tid, n_st - 1);
+          const int r = i / cn;
+          v[u] = idx_rows[(size_t)r * topk + c0 + (i - r * cn)];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * NT + tid;
+          const int r = i / cn;
+          if (i < n_st) idx_all[r][i - r * cn] = v[u];
+        }
       }
-    };
-    const int ntB = (topk + PF_KT - 1) / PF_KT;
-    issueB(0);
-    for (int ti = 0; ti < ntB; ++ti) {
-      for (int i = 0; i < CHB; ++i) put(mine, i * (64 * NH / 32) + (rt >> 5), colB, pfb[i]);
       __syncthreads();
-      if (ti + 1 < ntB) issueB(ti + 1);
-      const uint32_t vmask = (uint32_t)__ballot(active && slot(ti * PF_KT + l32) >= 0);
-      if (vmask) compute(mine, mine + PF_KT * PF_KS, vmask);
-      __syncthreads();
+      // slot p of the chunk: a compressed entry, or -1 (past the list, unused
+      // or out of range); the LDS read is always in bounds
+      auto slot = [&](int p) -> int {
+        const int j = idx_s[min(p, PF_IDX_MAX - 1)];
+        return (p >= cn || j < 0 || j >= Nc_cap) ? -1 : j;
+      };
+      u32x4 pfb[CHB];
+      auto issueB = [&](int ti) {
+#pragma unroll
+        for (int i = 0; i < CHB; ++i) {
+          const int rr = i * (64 * NH / 32) + (rt >> 5);
+          const int j = active ? slot(ti * PF_KT + rr) : -1;
+          const uint16_t* src = j >= 0 ? kvc_b + (size_t)j * 2 * D : dummy;
+          pfb[i] = *(const u32x4*)(src + 8 * colB);
+        }
+      };
+      const int ntB = (cn + PF_KT - 1) / PF_KT;
+      issueB(0);
+      for (int ti = 0; ti < ntB; ++ti) {
+        for (int i = 0; i < CHB; ++i) put(mine, i * (64 * NH / 32) + (rt >> 5), colB, pfb[i]);
+        __syncthreads();
+        if (ti + 1 < ntB) issueB(ti + 1);
+        const uint32_t vmask = (uint32_t)__ballot(active && slot(ti * PF_KT + l32) >= 0);
+        if (vmask) compute(mine, mine + PF_KT * PF_KS, vmask);
+        __syncthreads();
+      }
     }
   }
 
@@ -747,17 +773,18 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
     // rows share only the window: 2 rows, so that two independent
     // workgroups fill each CU.
-#define CSA_LAUNCH_PF(NH, ROWS)                                                                   \
-  attn_pf_kernel<NH, ROWS><<<(unsigned)(a.B * ((a.T + ROWS - 1) / ROWS)), 64 * ROWS * NH, 0, st>>>( \
+#define CSA_LAUNCH_PF(NH, ROWS, SP)                                                               \
+  attn_pf_kernel<NH, ROWS, SP><<<(unsigned)(a.B * ((a.T + ROWS - 1) / ROWS)), 64 * ROWS * NH, 0,   \
+                                 st>>>(                                                             \
       (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,  \
-      a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense, scale_log2,      \
+      a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, scale_log2,              \
       (uint16_t*)a.out, a.lse)
     if (a.H == 64) {
-      if (a.dense) CSA_LAUNCH_PF(2, 4);
-      else CSA_LAUNCH_PF(2, 2);
+      if (a.dense) CSA_LAUNCH_PF(2, 4, false);
+      else CSA_LAUNCH_PF(2, 2, true);
     } else {
-      if (a.dense) CSA_LAUNCH_PF(1, 4);
-      else CSA_LAUNCH_PF(1, 2);
+      if (a.dense) CSA_LAUNCH_PF(1, 4, false);
+      else CSA_LAUNCH_PF(1, 2, true);
     }
 #undef CSA_LAUNCH_PF
   }

@@ -98,6 +98,30 @@ def test_sparse_attn_prefill_8k_sampled():
         _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl, torch.bfloat16, "8k token %d" % t)
 
 
+@pytest.mark.parametrize("H", [64, 32])
+def test_sparse_attn_prefill_long_index_rows(H):
+    # prefill rows whose index lists exceed one LDS staging chunk of the
+    # kernel (2048 slots): the second chunk is ragged and slots are masked
+    # throughout
+    d = gen.Draw(36 + H, DEV)
+    B, T, D, Nc, topk, W = 1, 1030, 128, 2600, 2100, 64
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, 1200, 2 * D), gen.BF16)
+    q_pos, raw_base = [9000], [8900]
+    dc = gen.Draw(36 + H)
+    idx = _rand_idx(dc, B, T, topk, lambda b, t: _n_vis(q_pos[b] + t, Nc, 4, Nc), 0.0)
+    drop = torch.rand(idx.shape, generator=dc.g) < 0.05
+    idx[drop] = -1
+    out, lse = _sparse(q, kv_cmp, idx, kv_raw, W, q_pos, raw_base)
+    kvc, kvr = gen.host_bits(kv_cmp), gen.host_bits(kv_raw)
+    for t in [0, 1, 2, 515, 1028, 1029]:
+        ref, rl = orc.sparse_attn(gen.host_bits(q[:, t:t + 1]), kvc, idx[:, t:t + 1].numpy(), kvr,
+                                  W, [q_pos[0] + t], raw_base)
+        _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl, torch.bfloat16,
+               "long index rows H=%d token %d" % (H, t))
+
+
 @pytest.mark.parametrize("name", ["csa_decode_128k_b32", "csa_decode_1m_b8_stream"])
 def test_sparse_attn_decode_split_k(name):
     w = gen.WORKLOADS[name]
