@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   // phase A uses tiles 0..1 (double buffer); phase B tile r per row
   constexpr int NTILES = SPARSE && PF_ROWS > 2 ? PF_ROWS : 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NTILES * PF_TILE];
-  __shared__ int idx_all[SPARSE ? PF_ROWS : 1][SPARSE ? PF_IDX_MAX : 1];
+  __shared__ __attribute__((aligned(16))) int idx_all[SPARSE ? PF_ROWS : 1][SPARSE ? PF_IDX_MAX : 1];
   // the wave index is a scalar so that every per-wave decision below is a
   // uniform branch
   const int tid = threadIdx.x, lane = tid & 63;
@@ -137,7 +137,6 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
   const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
   const size_t rowi = (size_t)b * T + (active ? t : t_last);
-  const uint16_t* dummy = q + ((size_t)b * T + t0) * H * D;  // finite, readable row
 
   // this row's visibility
   const int nv_me = dense ? n_visible(pos, ncb, m, Nc_cap) : 0;
@@ -222,25 +221,36 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   const int nv_max = dense ? n_visible(pos_last, ncb, m, Nc_cap) : 0;
   int64_t win_first = pos_first - window + 1;
   if (win_first < 0) win_first = 0;
-  const int n_win = window > 0 ? (int)(pos_last - win_first + 1) : 0;
+  // (no window tile without a raw cache: none of its tokens could be present)
+  const int n_win = window > 0 && R_cap > 0 ? (int)(pos_last - win_first + 1) : 0;
   const int tiles0 = (nv_max + PF_KT - 1) / PF_KT;
   const int tiles1 = (n_win + PF_KT - 1) / PF_KT;
   const int ntA = tiles0 + tiles1;
+  // cache row of window key 0, clamped into the int range (rows outside
+  // [0, R_cap) are skipped either way)
+  const int64_t rw0_64 = win_first - rbase;
+  const int rw0 = (int)(rw0_64 < -(1 << 30) ? -(1 << 30) : (rw0_64 > (1 << 30) ? (1 << 30) : rw0_64));
   constexpr int CHA = PF_KT * 32 / NT;  // 16-byte chunks per thread per shared tile
   const int colA = tid & 31;
   u32x4 pfa[CHA];
+  // Key kk of a segment is cache row row0 + kk; it is loaded when kk < kk_lim
+  // and the row is below row_lim, else row 0 of the same cache stands in (a
+  // segment has tiles only when its cache has rows).  Byte offsets fit in 32
+  // bits: caches hold at most 2^23 rows of 512 bytes.
   auto issueA = [&](int ti) {
+    const bool seg0 = ti < tiles0;  // uniform
+    const char* base = (const char*)(seg0 ? kvc_b : kvr_b);
+    const int kk0 = (seg0 ? ti : ti - tiles0) * PF_KT;
+    const int kk_lim = seg0 ? nv_max : n_win;
+    const int row0 = seg0 ? kk0 : rw0 + kk0;
+    const uint32_t row_lim = (uint32_t)(seg0 ? Nc_cap : R_cap);
 #pragma unroll
     for (int i = 0; i < CHA; ++i) {
       const int rr = i * (NT / 32) + (tid >> 5);
-      const int e = ti * PF_KT + rr;
-      const int64_t tok = win_first + (int64_t)(ti - tiles0) * PF_KT + rr;
-      const int64_t r = tok - rbase;
-      const bool okc = (ti < tiles0) & (e < nv_max);
-      const bool okr = (ti >= tiles0) & (tok <= pos_last) & (r >= 0) & (r < R_cap);
-      const uint16_t* src = okc ? kvc_b + (size_t)e * 2 * D : kvr_b + (size_t)r * 2 * D;
-      src = (okc | okr) ? src : dummy;
-      pfa[i] = *(const u32x4*)(src + 8 * colA);
+      const int row = row0 + rr;
+      const bool ok = (kk0 + rr < kk_lim) & ((uint32_t)row < row_lim);
+      const uint32_t off = (uint32_t)(ok ? row : 0) * (uint32_t)(4 * D) + 16u * (uint32_t)colA;
+      pfa[i] = *(const u32x4*)(base + off);
     }
   };
   if (ntA > 0) {
@@ -273,63 +283,68 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   }
 
   // ---------------- phase B: each row's selected compressed entries
-  // The index rows are staged in LDS, PF_IDX_MAX slots at a time, so that the
-  // gathered loads of a tile never wait on an index load.
-  if (SPARSE && topk > 0) {
+  // The index rows are staged in LDS, PF_IDX_MAX slots at a time, as entry
+  // numbers or -1 (padding, out of range, past the list, a row past T), so
+  // that a tile's loads need one LDS read per four rows and never wait on a
+  // global index load.
+  if (SPARSE && topk > 0 && Nc_cap > 0) {
     const int32_t* idx_rows = idx + ((size_t)b * T + t0) * topk;
     const int nrows = t_last - t0 + 1;
     const int* idx_s = idx_all[row_w];
-    // the row's NH waves load its tile: 1024 chunks over 64 NH threads
+    // the row's NH waves load its tile: lane group gB (32 lanes, one 512-byte
+    // row per load) takes rows CHB gB .. CHB gB + CHB - 1
     constexpr int CHB = PF_KT * 32 / (64 * NH);
+    static_assert(CHB % 4 == 0, "index slots are read four at a time");
     const int rt = (wave % NH) * 64 + lane;     // thread index within the row
-    const int colB = rt & 31;
+    const int colB = rt & 31, gB = rt >> 5;
     uint16_t* mine = smem + row_w * PF_TILE;
     for (int c0 = 0; c0 < topk; c0 += PF_IDX_MAX) {
       const int cn = min(PF_IDX_MAX, topk - c0);
+      const int cw = (cn + PF_KT - 1) / PF_KT * PF_KT;  // whole tiles
       // every thread takes part: the barrier below, and the last one of the
       // previous chunk's tile loop, order these stores against the reads
-      // (loads batched four per thread, from clamped addresses, before the
-      // stores)
-      const int n_st = nrows * cn;
+      // (loads batched four per thread, from clamped addresses)
+      const int n_st = PF_ROWS * cw;
       for (int i0 = 0; i0 < n_st; i0 += 4 * NT) {
         int v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int i = min(i0 + u * NT + tid, n_st - 1);
-          const int r = i / cn;
-          v[u] = idx_rows[(size_t)r * topk + c0 + (i - r * cn)];
+          const int i = i0 + u * NT + tid;
+          const int r = i / cw, pp = i - r * cw;
+          v[u] = idx_rows[(size_t)min(r, nrows - 1) * topk + c0 + min(pp, cn - 1)];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = i0 + u * NT + tid;
-          const int r = i / cn;
-          if (i < n_st) idx_all[r][i - r * cn] = v[u];
+          const int r = i / cw, pp = i - r * cw;
+          const bool ok = r < nrows && pp < cn && (uint32_t)v[u] < (uint32_t)Nc_cap;
+          if (i < n_st) idx_all[r][pp] = ok ? v[u] : -1;
         }
       }
       __syncthreads();
-      // slot p of the chunk: a compressed entry, or -1 (past the list, unused
-      // or out of range); the LDS read is always in bounds
-      auto slot = [&](int p) -> int {
-        const int j = idx_s[min(p, PF_IDX_MAX - 1)];
-        return (p >= cn || j < 0 || j >= Nc_cap) ? -1 : j;
-      };
       u32x4 pfb[CHB];
       auto issueB = [&](int ti) {
+        const int* sp = idx_s + ti * PF_KT + CHB * gB;
+        int jv[CHB];
+#pragma unroll
+        for (int q4 = 0; q4 < CHB / 4; ++q4) {
+          const i32x4 x = *(const i32x4*)(sp + 4 * q4);
+          for (int e = 0; e < 4; ++e) jv[4 * q4 + e] = x[e];
+        }
 #pragma unroll
         for (int i = 0; i < CHB; ++i) {
-          const int rr = i * (64 * NH / 32) + (rt >> 5);
-          const int j = active ? slot(ti * PF_KT + rr) : -1;
-          const uint16_t* src = j >= 0 ? kvc_b + (size_t)j * 2 * D : dummy;
-          pfb[i] = *(const u32x4*)(src + 8 * colB);
+          const uint32_t off = (uint32_t)max(jv[i], 0) * (uint32_t)(4 * D) + 16u * (uint32_t)colB;
+          pfb[i] = *(const u32x4*)((const char*)kvc_b + off);
         }
       };
-      const int ntB = (cn + PF_KT - 1) / PF_KT;
+      const int ntB = cw / PF_KT;
       issueB(0);
       for (int ti = 0; ti < ntB; ++ti) {
-        for (int i = 0; i < CHB; ++i) put(mine, i * (64 * NH / 32) + (rt >> 5), colB, pfb[i]);
+#pragma unroll
+        for (int i = 0; i < CHB; ++i) put(mine, CHB * gB + i, colB, pfb[i]);
         __syncthreads();
         if (ti + 1 < ntB) issueB(ti + 1);
-        const uint32_t vmask = (uint32_t)__ballot(active && slot(ti * PF_KT + l32) >= 0);
+        const uint32_t vmask = (uint32_t)__ballot(idx_s[ti * PF_KT + l32] >= 0);
         if (vmask) compute(mine, mine + PF_KT * PF_KS, vmask);
         __syncthreads();
       }
