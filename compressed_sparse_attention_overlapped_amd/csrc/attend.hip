@@ -165,9 +165,16 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     f32x16 sacc;
     for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
     const uint16_t* krow = ks_t + l32 * PF_KS + 8 * h2;
+    // all eight K fragments are read before the products start, so that one
+    // LDS latency is exposed per tile instead of one per pair
+    bf16x8 kf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = *(const bf16x8*)(krow + 16 * s);
+#pragma unroll
     for (int s = 0; s < 8; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + 16 * s), qf[s], sacc,
-                                                     0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     // keys of register r: 8 (r/4) + 4 h2 + r%4; partial tiles mask, full
     // tiles skip the per-key work; the scale (> 0) is applied inside the FMA
     if (vmask != 0xffffffffu) {
