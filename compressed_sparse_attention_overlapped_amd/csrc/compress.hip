@@ -158,7 +158,10 @@ __global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__
 // ---------------------------------------------------------------- pool
 // Grid (n_slots + 1, B).  Slot q < n_slots handles entry i_lo(b) + q; the last
 // slot writes state_out.  Each thread owns channels e = tid, tid + 256, ...
-template <int OUT_DT>
+// WIN > 0: the window is WIN tokens, and entries whose whole window lies in
+// this call's rows (with one projection partial) take a path whose loads are
+// all issued before the softmax; WIN = 0: the general path only.
+template <int OUT_DT, int WIN>
 __global__ void __launch_bounds__(256) pool_kernel(
     const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
@@ -229,7 +232,42 @@ __global__ void __launch_bounds__(256) pool_kernel(
   float vals[4];  // E <= 1024 supported (checked by the host)
   float amax = 0.0f;
   int nv = 0;
-  for (int e = tid; e < E; e += blockDim.x, ++nv) {
+  bool done = false;
+  if constexpr (WIN > 0) {
+    if (n_split == 1 && first >= p0) {  // uniform
+      // rows first .. first + WIN - 1 of this call; the same arithmetic, in
+      // the same order, as one chunk of the general path below
+      const float* r0 = pg + ((size_t)b * L + (size_t)(first - p0)) * N;
+      const float* ap = ape ? ape : pg;  // a readable stand-in when there is no ape
+      for (int e = tid; e < E; e += blockDim.x, ++nv) {
+        float pv[WIN], gv[WIN], av[WIN];
+#pragma unroll
+        for (int u = 0; u < WIN; ++u) {
+          pv[u] = r0[(size_t)u * N + e];
+          gv[u] = r0[(size_t)u * N + E + e];
+          av[u] = ap[(size_t)u * E + e];
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < WIN; ++u) {
+          gv[u] = ape ? gv[u] + av[u] : gv[u];
+          cm = fmaxf(cm, gv[u]);
+        }
+        float den = 0.0f, num = 0.0f;
+#pragma unroll
+        for (int u = 0; u < WIN; ++u) {
+          const float w = __expf(gv[u] - cm);
+          den += w;
+          num = fmaf(w, pv[u], num);
+        }
+        const float c = num / den;
+        vals[nv] = c;
+        amax = fmaxf(amax, fabsf(c));
+      }
+      done = true;
+    }
+  }
+  if (!done) for (int e = tid; e < E; e += blockDim.x, ++nv) {
     // online softmax over the window in chunks of 8 tokens; every chunk's
     // loads are independent of each other
     float mx = -INFINITY, den = 0.0f, num = 0.0f;
@@ -327,22 +365,26 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   }
   const int n_slots = (a.L + a.m - 1) / a.m + 1;
   dim3 pgrid(n_slots + 1, a.B);
+  // the common gated window (m = 4 with overlap: 8 tokens) has a batched path
+  const bool w8 = (1 + a.overlap) * a.m == 8;
+#define CSA_LAUNCH_POOL(DT, W)                                                                  \
+  pool_kernel<DT, W><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape,    \
+                                            a.state_in, a.state_out, a.out, a.out_scale,       \
+                                            a.Nc_cap, n_slots, splits)
   switch (a.out_dt) {
     case CSA_DT_F32:
-      pool_kernel<CSA_DT_F32><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m,
-                                                      a.overlap, a.ape, a.state_in, a.state_out,
-                                                      a.out, a.out_scale, a.Nc_cap, n_slots, splits);
+      if (w8) CSA_LAUNCH_POOL(CSA_DT_F32, 8);
+      else CSA_LAUNCH_POOL(CSA_DT_F32, 0);
       break;
     case CSA_DT_BF16:
-      pool_kernel<CSA_DT_BF16><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m,
-                                                       a.overlap, a.ape, a.state_in, a.state_out,
-                                                       a.out, a.out_scale, a.Nc_cap, n_slots, splits);
+      if (w8) CSA_LAUNCH_POOL(CSA_DT_BF16, 8);
+      else CSA_LAUNCH_POOL(CSA_DT_BF16, 0);
       break;
     default:
-      pool_kernel<CSA_DT_FP8E4M3><<<pgrid, 256, 0, st>>>(
-          pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,
-          a.out_scale, a.Nc_cap, n_slots, splits);
+      if (w8) CSA_LAUNCH_POOL(CSA_DT_FP8E4M3, 8);
+      else CSA_LAUNCH_POOL(CSA_DT_FP8E4M3, 0);
   }
+#undef CSA_LAUNCH_POOL
   return hipGetLastError();
 }
 
