@@ -178,10 +178,10 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     // keys of register r: 8 (r/4) + 4 h2 + r%4; partial tiles mask, full
     // tiles skip the per-key work; the scale (> 0) is applied inside the FMA
     if (vmask != 0xffffffffu) {
-      for (int r = 0; r < 16; ++r) {
-        const int kr = 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (!((vmask >> kr) & 1u)) sacc[r] = -INFINITY;
-      }
+      // one per-lane shift, then constant bit positions
+      const uint32_t mv = vmask >> (4 * h2);
+      for (int r = 0; r < 16; ++r)
+        if (!((mv >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[r] = -INFINITY;
     }
     float x = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
     for (int r = 3; r < 15; r += 2) x = fmaxf(fmaxf(x, sacc[r]), sacc[r + 1]);
