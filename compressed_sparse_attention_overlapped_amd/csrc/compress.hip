@@ -138,6 +138,65 @@ __global__ void __launch_bounds__(256) proj_bf16_kernel(
     }
 }
 
+// ------------------------------------------------------- proj (bf16, few rows)
+// Decode steps and short chunks (M <= 16 rows): one workgroup per 16 output
+// columns computes them over all of K (no partials), its 16 waves taking a
+// sixteenth of K each, so that a 4096-deep projection issues all of its
+// loads at once (one memory round trip); MFMA 16x16x32 with the rows as M
+// (rows past M read row M - 1 and are dropped) and 16 columns of the stacked
+// weight as N.  Each weight byte is read once; the few x rows stay in L2.
+// The partial sums are added in wave order through LDS.  K % 512 == 0
+// (checked by the host).
+constexpr int PS_COLS = 16, PS_UNROLL = 8, PS_WAVES = 16;
+
+__global__ void __launch_bounds__(64 * PS_WAVES) proj_small_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
+    const uint16_t* __restrict__ w_gate, float* __restrict__ pg, int M, int E, int K) {
+  __shared__ float red[PS_WAVES][16 * PS_COLS];
+  const int N = 2 * E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * PS_COLS;
+  const int kq = K / PS_WAVES;
+  // operand lanes: row / column lane % 16, k chunk 8 (lane / 16) of each
+  // 32-deep step (the same k order for both operands)
+  const int arow = min(lane & 15, M - 1);
+  const uint16_t* ap = x + (size_t)arow * K + wave * kq + 8 * (lane >> 4);
+  const int gn = min(n0 + (lane & 15), N - 1);
+  const uint16_t* bp =
+      (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(gn - E) * K) + wave * kq + 8 * (lane >> 4);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int k = 0;
+  for (; k + 32 * PS_UNROLL <= kq; k += 32 * PS_UNROLL) {
+    bf16x8 a[PS_UNROLL], bv[PS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PS_UNROLL; ++u) {
+      a[u] = *(const bf16x8*)(ap + k + 32 * u);
+      bv[u] = *(const bf16x8*)(bp + k + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < PS_UNROLL; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bv[u], acc, 0, 0, 0);
+  }
+  for (; k < kq; k += 32) {
+    const bf16x8 a = *(const bf16x8*)(ap + k), bv = *(const bf16x8*)(bp + k);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc, 0, 0, 0);
+  }
+  // accumulator: lane holds column lane % 16, rows 4 (lane / 16) + i
+  for (int i = 0; i < 4; ++i) red[wave][(4 * (lane >> 4) + i) * PS_COLS + (lane & 15)] = acc[i];
+  __syncthreads();
+  if (tid < 16 * PS_COLS) {
+    const int row = tid / PS_COLS, col = n0 + tid % PS_COLS;
+    float sum = red[0][tid];
+    for (int w = 1; w < PS_WAVES; ++w) sum += red[w][tid];
+    if (row < M && col < N) pg[(size_t)row * N + col] = sum;
+  }
+}
+
+static bool use_proj_small(int M, int K, csa_dtype_t dt) {
+  return dt == CSA_DT_BF16 && M <= 16 && K % (32 * PS_WAVES) == 0;
+}
+
 // ---------------------------------------------------------------- proj (fp32)
 __global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__ x,
                                                        const float* __restrict__ w_kv,
@@ -210,7 +269,40 @@ __global__ void __launch_bounds__(256) pool_kernel(
 
   if (q == n_slots) {  // carried state for the next call
     if (!state_out) return;
-    for (int idx = tid; idx < ns * E; idx += blockDim.x) {
+    const int total = ns * E;
+    if (n_split == 1) {
+      // four elements per thread with every load issued first (from a
+      // readable stand-in for absent tokens)
+      for (int i0 = 0; i0 < total; i0 += 4 * (int)blockDim.x) {
+        float pv[4], gv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = min(i0 + u * (int)blockDim.x + tid, total - 1);
+          const int slot = idx / E, e = idx - slot * E;
+          const int64_t j = p0 + L - ns + slot;
+          const bool in_call = j >= p0;
+          const bool in_state = !in_call && state_in && j >= 0;
+          const float* src =
+              in_call ? pg + ((size_t)b * L + (size_t)(j - p0)) * N
+                      : (in_state ? state_in + ((size_t)b * ns + (size_t)(j - (p0 - ns))) * 2 * E : pg);
+          pv[u] = src[e];
+          gv[u] = src[E + e];
+          if (!(in_call || in_state)) gv[u] = -INFINITY;
+          if (gv[u] == -INFINITY) pv[u] = 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = i0 + u * (int)blockDim.x + tid;
+          if (idx < total) {
+            const int slot = idx / E, e = idx - slot * E;
+            state_out[(((size_t)b * ns + slot) * 2 + 0) * E + e] = pv[u];
+            state_out[(((size_t)b * ns + slot) * 2 + 1) * E + e] = gv[u];
+          }
+        }
+      }
+      return;
+    }
+    for (int idx = tid; idx < total; idx += blockDim.x) {
       int slot = idx / E, e = idx % E;
       int64_t j = p0 + L - ns + slot;
       float pv, gv;
@@ -234,23 +326,42 @@ __global__ void __launch_bounds__(256) pool_kernel(
   int nv = 0;
   bool done = false;
   if constexpr (WIN > 0) {
-    if (n_split == 1 && first >= p0) {  // uniform
-      // rows first .. first + WIN - 1 of this call; the same arithmetic, in
-      // the same order, as one chunk of the general path below
-      const float* r0 = pg + ((size_t)b * L + (size_t)(first - p0)) * N;
+    if (n_split == 1) {  // uniform
+      // Window token u is a row of this call, a carried-state slot, or
+      // absent; the choice depends on u only (scalar), and every load is
+      // issued before the softmax, which repeats one chunk of the general
+      // path below (the same arithmetic in the same order).
+      const float* src[WIN];
+      bool present[WIN];
+#pragma unroll
+      for (int u = 0; u < WIN; ++u) {
+        const int64_t j = first + u;
+        if (j >= p0) {
+          src[u] = pg + ((size_t)b * L + (size_t)(j - p0)) * N;
+          present[u] = true;
+        } else if (state_in && j >= 0 && j >= p0 - ns) {
+          src[u] = state_in + ((size_t)b * ns + (size_t)(j - (p0 - ns))) * 2 * E;
+          present[u] = true;
+        } else {
+          src[u] = pg;  // a readable stand-in; the token is absent
+          present[u] = false;
+        }
+      }
       const float* ap = ape ? ape : pg;  // a readable stand-in when there is no ape
       for (int e = tid; e < E; e += blockDim.x, ++nv) {
         float pv[WIN], gv[WIN], av[WIN];
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {
-          pv[u] = r0[(size_t)u * N + e];
-          gv[u] = r0[(size_t)u * N + E + e];
+          pv[u] = src[u][e];
+          gv[u] = src[u][E + e];
           av[u] = ap[(size_t)u * E + e];
         }
         float cm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {
-          gv[u] = ape ? gv[u] + av[u] : gv[u];
+          if (!present[u]) gv[u] = -INFINITY;
+          if (gv[u] == -INFINITY) pv[u] = 0.0f;
+          else if (ape) gv[u] += av[u];
           cm = fmaxf(cm, gv[u]);
         }
         float den = 0.0f, num = 0.0f;
@@ -329,7 +440,7 @@ namespace csa_host {
 using namespace csa;
 
 static int proj_splits(int M, int E, int K, csa_dtype_t dt) {
-  if (dt != CSA_DT_BF16) return 1;
+  if (dt != CSA_DT_BF16 || use_proj_small(M, K, dt)) return 1;
   int tiles = ((M + PJ_BM - 1) / PJ_BM) * ((2 * E + PJ_BN - 1) / PJ_BN);
   int s = 1;
   // split K while the grid holds fewer than two workgroups per CU; every
@@ -354,7 +465,10 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   const int M = a.B * a.L, K = a.d_model, E = a.E;
   const int splits = proj_splits(M, E, K, a.in_dt);
   float* pg = (float*)a.ws;
-  if (a.in_dt == CSA_DT_BF16) {
+  if (use_proj_small(M, K, a.in_dt)) {
+    proj_small_kernel<<<(2 * E + PS_COLS - 1) / PS_COLS, 64 * PS_WAVES, 0, st>>>(
+        (const uint16_t*)a.x, (const uint16_t*)a.w_kv, (const uint16_t*)a.w_gate, pg, M, E, K);
+  } else if (a.in_dt == CSA_DT_BF16) {
     dim3 grid((M + PJ_BM - 1) / PJ_BM, (2 * E + PJ_BN - 1) / PJ_BN, splits);
     proj_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t*)a.x, (const uint16_t*)a.w_kv,
                                            (const uint16_t*)a.w_gate, pg, M, E, K, K / splits);

@@ -143,6 +143,81 @@ def test_compress_decode_step_splits_k():
     assert_bf16_close(out[:, Nc - 1].float().cpu().numpy(), ref2[:, Nc - 1], "decode entry")
 
 
+@pytest.mark.parametrize("E,out_kind", [(256, "bf16"), (64, "fp8")])
+def test_compress_decode_step_main_and_indexer_widths(E, out_kind):
+    # the decode step of both compressors of the streaming decode workload
+    # (main: 2D channels to bf16; indexer: d_I channels to e4m3 with a row
+    # scale): few-row projection over all of K, pool from the carried state
+    w = gen.WORKLOADS["csa_decode_1m_b8_stream"]
+    d = gen.Draw(14 + E)
+    B, dm, m, o = w.B, w.d_model, w.m, w.overlap
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    x_tail = gen.store(d.normal(B, 7, dm), gen.BF16)
+    x_new = gen.store(d.normal(B, 1, dm), gen.BF16)
+    T = w.ctx
+    Nc = T // m
+    pos_tail = [T - 8] * B
+    _, _, st1 = _oracle(x_tail, w_kv, w_gate, pos_tail, m, o, Nc)
+    ref2, wr2, st2 = _oracle(x_new, w_kv, w_gate, [T - 1] * B, m, o, Nc,
+                             state_in=torch.from_numpy(st1))
+    assert wr2[:, Nc - 1].all()
+    wk, wg = w_kv.to(DEV), w_gate.to(DEV)
+    ns = 2 * m - 1
+    s0 = torch.zeros(B, ns, 2, E, device=DEV)
+    odt = torch.bfloat16 if out_kind == "bf16" else torch.float8_e4m3fn
+    out, osc, s1 = None, None, None
+    tmp = torch.zeros(B, Nc, E, device=DEV, dtype=odt)
+    tsc = torch.zeros(B, Nc, device=DEV) if out_kind == "fp8" else None
+    csa.csa_compress(x_tail.to(DEV), wk, wg, dev_i64(pos_tail), m, o, tmp, out_scale=tsc,
+                     state_out=s0)
+    out, osc, s1 = _run(x_new.to(DEV), wk, wg, [T - 1] * B, m, o, Nc, odt, state_in=s0)
+    np.testing.assert_allclose(s1.cpu().numpy()[:, :, 0], st2[:, :, 0], rtol=2e-5, atol=2e-5)
+    np.testing.assert_allclose(s1.cpu().numpy()[:, :, 1], st2[:, :, 1], rtol=2e-5, atol=2e-5)
+    if out_kind == "bf16":
+        assert_bf16_close(out[:, Nc - 1].float().cpu().numpy(), ref2[:, Nc - 1], "decode entry")
+        return
+    codes, scales = orc.quant_rows_e4m3(np.nan_to_num(ref2[:, Nc - 1:Nc]))
+    g_codes = gen.host_bits(out[:, Nc - 1:Nc])
+    np.testing.assert_allclose(osc[:, Nc - 1].cpu().numpy(), scales[:, 0], rtol=1e-5)
+    for b in range(B):
+        gv = np.array([orc.e4m3_decode(c) for c in g_codes[b, 0]])
+        rv = np.array([orc.e4m3_decode(c) for c in codes[b, 0]])
+        step = np.maximum(np.abs(rv), 2.0 ** -6) * 2.0 ** -3
+        assert (np.abs(gv - rv) <= step + 1e-12).all(), b
+
+
+def test_compress_few_rows_chunks_ragged_k():
+    # 15-row chunks (the few-row projection) with K = 512 (no full unrolled
+    # k block per wave), 2E = 88 columns (a partial 16-column group), ragged
+    # starts, a carried state between the chunks and an ape
+    d = gen.Draw(21)
+    B, L, dm, E, m, o = 3, 5, 512, 44, 4, 1
+    x = gen.store(d.normal(B, 2 * L, dm), gen.BF16)
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    ape = d.normal(2 * m, E)
+    pos0 = [0, 6, 13]
+    Nc = 8
+    ref, written, st_ref = _oracle(x, w_kv, w_gate, pos0, m, o, Nc, ape=ape)
+    xg, wk, wg, ag = x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), ape.to(DEV)
+    out = torch.full((B, Nc, E), float("nan"), device=DEV)
+    ns = 2 * m - 1
+    s0 = torch.full((B, ns, 2, E), 7.0, device=DEV)
+    s1 = torch.full((B, ns, 2, E), 7.0, device=DEV)
+    csa.csa_compress(xg[:, :L].contiguous(), wk, wg, dev_i64(pos0), m, o, out, ape=ag,
+                     state_out=s0)
+    csa.csa_compress(xg[:, L:].contiguous(), wk, wg, dev_i64([p + L for p in pos0]), m, o, out,
+                     ape=ag, state_in=s0, state_out=s1)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    for b in range(B):
+        wr = written[b]
+        assert wr.any()
+        assert np.isnan(g[b, ~wr]).all()
+        assert_rows_rel(g[b, wr], ref[b, wr], 1e-5, "few-row chunks")
+    np.testing.assert_allclose(s1.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=2e-5, atol=2e-5)
+    assert np.array_equal(np.isneginf(s1.cpu().numpy()[:, :, 1]), np.isneginf(st_ref[:, :, 1]))
+
+
 def test_compress_prefill_8k_sampled_entries():
     w = gen.WORKLOADS["csa_prefill_8k_bf16"]
     inp = gen.prefill_inputs(w, device="cpu")
