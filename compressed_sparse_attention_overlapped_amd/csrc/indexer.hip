@@ -528,10 +528,14 @@ __global__ void __launch_bounds__(256) collect_kernel(
   constexpr int kGroups = kChunk / 256;
   uint32_t key[kGroups];
   uint32_t n_wave = 0;
+  // every score load is issued before the first is used (clamped addresses)
+  float sv[kGroups];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) sv[g] = srow[min(wb + g * 64 + lane, j1 - 1)];
   for (int g = 0; g < kGroups; ++g) {
     const int j = wb + g * 64 + lane;
     const bool valid = j < j1;
-    key[g] = valid ? score_key(srow[j]) : 0u;
+    key[g] = valid ? score_key(sv[g]) : 0u;
     const uint32_t kb = key[g] >> kHistShift;
     const uint64_t dm = __ballot(valid && kb > bin);
     const uint64_t cm = __ballot(valid && kb == bin);
@@ -706,7 +710,7 @@ __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
   __shared__ uint32_t coff[FIN_THREADS], ccnt[FIN_THREADS];
   __shared__ uint32_t sh[32];
   const int row = blockIdx.x, b = row / T, t = row % T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const int nsel = min(topk, nv);
   const float* srow = scores + (size_t)row * Nc_cap;
@@ -718,10 +722,19 @@ __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
   const int nwords = (nv + 31) / 32;
   const int nch = (nv + kChunk - 1) / kChunk;  // chunks collect wrote (<= FIN_THREADS)
   uint32_t n_bits = 0;
-  for (int w = tid; w < nwords; w += blockDim.x) {
-    const uint32_t x = gbm[w];
-    if (BM_LDS) lbm[w] = x;
-    n_bits += __popc(x);
+  // eight words per thread in flight (clamped addresses)
+  for (int w0 = 0; w0 < nwords; w0 += 8 * FIN_THREADS) {
+    uint32_t xw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xw[u] = gbm[min(w0 + u * FIN_THREADS + tid, nwords - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int w = w0 + u * FIN_THREADS + tid;
+      if (w < nwords) {
+        if (BM_LDS) lbm[w] = xw[u];
+        n_bits += __popc(xw[u]);
+      }
+    }
   }
   const uint32_t cc = tid < nch ? chunk_cnt[(size_t)row * n_chunks + tid] : 0u;
   uint32_t n_def, n_cand;
@@ -735,19 +748,36 @@ __global__ void __launch_bounds__(FIN_THREADS) finalize_kernel(
   uint32_t* fkey = cand_flat + (size_t)row * Nc_cap * 2;
   uint32_t* fidx = fkey + Nc_cap;
   if (need > 0) {
-    // gather the chunk segments: wave w takes chunks w, w + 16, ...
+    // gather the chunk segments: candidate i (of the flat list) lies in the
+    // last chunk whose offset is <= i; four candidates per thread in flight
     const uint32_t* gci = cand_idx + (size_t)row * Nc_cap;
     const uint32_t* gck = cand_key + (size_t)row * Nc_cap;
-    for (int c = wave; c < nch; c += FIN_THREADS / 64) {
-      const uint32_t n = ccnt[c], o = coff[c];
-      for (uint32_t i = lane; i < n; i += 64) {
-        const uint32_t k = gck[(size_t)c * kChunk + i], j = gci[(size_t)c * kChunk + i];
-        if (in_lds) {
-          ckey[o + i] = k;
-          cidx[o + i] = j;
-        } else {
-          fkey[o + i] = k;
-          fidx[o + i] = j;
+    for (uint32_t i0 = 0; i0 < n_cand; i0 += 4 * FIN_THREADS) {
+      uint32_t kv[4], jv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = min(i0 + u * FIN_THREADS + tid, n_cand - 1);
+        int lo = 0, hi = nch - 1;  // coff[lo] <= i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (coff[mid] <= i) lo = mid;
+          else hi = mid - 1;
+        }
+        const size_t at = (size_t)lo * kChunk + (i - coff[lo]);
+        kv[u] = gck[at];
+        jv[u] = gci[at];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * FIN_THREADS + tid;
+        if (i < n_cand) {
+          if (in_lds) {
+            ckey[i] = kv[u];
+            cidx[i] = jv[u];
+          } else {
+            fkey[i] = kv[u];
+            fidx[i] = jv[u];
+          }
         }
       }
     }
