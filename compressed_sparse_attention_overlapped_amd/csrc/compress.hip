@@ -19,9 +19,10 @@
 namespace csa {
 
 // ---------------------------------------------------------------- proj (bf16)
-// Tile 128 x 128 x 64, 256 threads = 4 waves in a 2 x 2 grid of 64 x 64
-// (2 x 2 MFMA 32x32x16 per 16-deep k step).  The LDS tiles are double
-// buffered; two more k tiles are in flight in two register stages (k tile
+// Tile 128 x 128 x 64, 512 threads = 8 waves in a 2 x 4 grid of 64 x 32
+// (2 x 1 MFMA 32x32x16 per 16-deep k step; two waves per SIMD, so that one
+// wave's products overlap another's loads and barrier).  The LDS tiles are
+// double buffered; two more k tiles are in flight in two register stages (k tile
 // t + 2 is requested as soon as k tile t has moved to LDS), so the load
 // latency is hidden behind two tiles of products.  Loads are unconditional
 // (rows past M and columns past N read row 0 and are dropped at the store;
@@ -33,7 +34,7 @@ constexpr int PJ_BM = 128, PJ_BN = 128, PJ_BK = 64;
 constexpr int PJ_LDS_STRIDE = PJ_BK + 8;
 constexpr int PJ_TILE = PJ_BM * PJ_LDS_STRIDE;  // bf16 per operand tile
 
-__global__ void __launch_bounds__(256) proj_bf16_kernel(
+__global__ void __launch_bounds__(512) proj_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
     const uint16_t* __restrict__ w_gate, float* __restrict__ pg, int M, int E, int K,
     int k_per_split) {
@@ -46,61 +47,58 @@ __global__ void __launch_bounds__(256) proj_bf16_kernel(
   const int split = blockIdx.z;
   const int kb = split * k_per_split, ke = min(K, kb + k_per_split);
   const int nk = (ke - kb) / PJ_BK;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 2) * 64, wn = (wave & 3) * 32;
 
   // global -> LDS: a tile row is 64 bf16 = 8 chunks of 16 B; 128 rows x 8 =
-  // 1024 chunks per operand, 4 per thread (rows r = c / 8, chunk q = c % 8)
-  const uint16_t* arow[4];
-  const uint16_t* brow[4];
-  for (int u = 0; u < 4; ++u) {
-    const int c = u * 256 + tid, r = c >> 3, q = c & 7;
+  // 1024 chunks per operand, 2 per thread (rows r = c / 8, chunk q = c % 8)
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  for (int u = 0; u < 2; ++u) {
+    const int c = u * 512 + tid, r = c >> 3, q = c & 7;
     const int gm = m0 + r < M ? m0 + r : 0, gn = n0 + r < N ? n0 + r : 0;
     arow[u] = x + (size_t)gm * K + kb + q * 8;
     brow[u] = (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(gn - E) * K) + kb + q * 8;
   }
-  u32x4 ra[2][4], rb[2][4];
-  auto load = [&](int kt, u32x4(&a)[4], u32x4(&bq)[4]) {
+  u32x4 ra[2][2], rb[2][2];
+  auto load = [&](int kt, u32x4(&a)[2], u32x4(&bq)[2]) {
     const int k0 = min(kt, nk - 1) * PJ_BK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       a[u] = *(const u32x4*)(arow[u] + k0);
       bq[u] = *(const u32x4*)(brow[u] + k0);
     }
   };
-  auto store = [&](int buf, const u32x4(&a)[4], const u32x4(&bq)[4]) {
+  auto store = [&](int buf, const u32x4(&a)[2], const u32x4(&bq)[2]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = u * 256 + tid, r = c >> 3, q = c & 7;
+    for (int u = 0; u < 2; ++u) {
+      const int c = u * 512 + tid, r = c >> 3, q = c & 7;
       *(u32x4*)(&As[buf][r * PJ_LDS_STRIDE + q * 8]) = a[u];
       *(u32x4*)(&Bs[buf][r * PJ_LDS_STRIDE + q * 8]) = bq[u];
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2];
   for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j)
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
   auto compute = [&](int buf) {
     // four k steps of 16; lane holds 8 consecutive k of one row (A) / column (B)
 #pragma unroll
     for (int ks = 0; ks < PJ_BK / 16; ++ks) {
-      bf16x8 a[2], b[2];
+      bf16x8 a[2];
       for (int i = 0; i < 2; ++i)
         a[i] = *(const bf16x8*)(&As[buf][(wm + i * 32 + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 +
                                          (lane >> 5) * 8]);
-      for (int j = 0; j < 2; ++j)
-        b[j] = *(const bf16x8*)(&Bs[buf][(wn + j * 32 + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 +
-                                         (lane >> 5) * 8]);
+      const bf16x8 b =
+          *(const bf16x8*)(&Bs[buf][(wn + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 + (lane >> 5) * 8]);
       for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i], 0, 0, 0);
     }
   };
   // step kt: multiply k tile kt (LDS buffer kt & 1), move k tile kt + 1 from
   // its register stage to the other buffer, refill that stage with k tile
   // kt + 3
-  auto step = [&](int kt, u32x4(&a)[4], u32x4(&bq)[4]) {
+  auto step = [&](int kt, u32x4(&a)[2], u32x4(&bq)[2]) {
     compute(kt & 1);
     store((kt + 1) & 1, a, bq);
     load(kt + 3, a, bq);
@@ -127,15 +125,13 @@ __global__ void __launch_bounds__(256) proj_bf16_kernel(
   // accumulator layout (32x32): lane holds column (lane & 31), rows
   // 8 (r / 4) + 4 (lane / 32) + (r % 4)
   float* out = pg + (size_t)split * M * N;
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) {
-      int col = n0 + wn + j * 32 + (lane & 31);
-      if (col >= N) continue;
+  const int col = n0 + wn + (lane & 31);
+  if (col < N)
+    for (int i = 0; i < 2; ++i)
       for (int r = 0; r < 16; ++r) {
-        int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M) out[(size_t)row * N + col] = acc[i][j][r];
+        const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) out[(size_t)row * N + col] = acc[i][r];
       }
-    }
 }
 
 // ------------------------------------------------------- proj (bf16, few rows)
@@ -217,10 +213,10 @@ __global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__
 // ---------------------------------------------------------------- pool
 // Grid (n_slots + 1, B).  Slot q < n_slots handles entry i_lo(b) + q; the last
 // slot writes state_out.  Each thread owns channels e = tid, tid + 256, ...
-// WIN > 0: the window is WIN tokens, and entries whose whole window lies in
-// this call's rows (with one projection partial) take a path whose loads are
-// all issued before the softmax; WIN = 0: the general path only.
-template <int OUT_DT, int WIN>
+// WIN > 0: the window is WIN tokens and, with at most NSP projection
+// partials, every entry takes a path whose loads are all issued before the
+// softmax; WIN = 0: the general path only.
+template <int OUT_DT, int WIN, int NSP>
 __global__ void __launch_bounds__(256) pool_kernel(
     const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
@@ -326,16 +322,18 @@ __global__ void __launch_bounds__(256) pool_kernel(
   int nv = 0;
   bool done = false;
   if constexpr (WIN > 0) {
-    if (n_split == 1) {  // uniform
-      // Window token u is a row of this call, a carried-state slot, or
-      // absent; the choice depends on u only (scalar), and every load is
-      // issued before the softmax, which repeats one chunk of the general
-      // path below (the same arithmetic in the same order).
+    if (n_split <= NSP) {  // uniform
+      // Window token u is a row of this call (with n_split partials), a
+      // carried-state slot, or absent; the choice depends on u only
+      // (scalar), and every load is issued before the softmax, which repeats
+      // one chunk of the general path below (the same arithmetic, partials
+      // summed in split order).
       const float* src[WIN];
-      bool present[WIN];
+      bool present[WIN], in_call[WIN];
 #pragma unroll
       for (int u = 0; u < WIN; ++u) {
         const int64_t j = first + u;
+        in_call[u] = j >= p0;
         if (j >= p0) {
           src[u] = pg + ((size_t)b * L + (size_t)(j - p0)) * N;
           present[u] = true;
@@ -347,15 +345,33 @@ __global__ void __launch_bounds__(256) pool_kernel(
           present[u] = false;
         }
       }
+      const size_t sstride = (size_t)B * L * N;  // between split partials
       const float* ap = ape ? ape : pg;  // a readable stand-in when there is no ape
       for (int e = tid; e < E; e += blockDim.x, ++nv) {
         float pv[WIN], gv[WIN], av[WIN];
+        float pe[NSP > 1 ? NSP - 1 : 1][WIN], ge[NSP > 1 ? NSP - 1 : 1][WIN];
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {
           pv[u] = src[u][e];
           gv[u] = src[u][E + e];
           av[u] = ap[(size_t)u * E + e];
         }
+#pragma unroll
+        for (int sp = 1; sp < NSP; ++sp)
+#pragma unroll
+          for (int u = 0; u < WIN; ++u) {
+            const float* r = src[u] + (in_call[u] ? (size_t)min(sp, n_split - 1) * sstride : 0);
+            pe[sp - 1][u] = r[e];
+            ge[sp - 1][u] = r[E + e];
+          }
+#pragma unroll
+        for (int sp = 1; sp < NSP; ++sp)
+#pragma unroll
+          for (int u = 0; u < WIN; ++u)
+            if (sp < n_split && in_call[u]) {
+              pv[u] += pe[sp - 1][u];
+              gv[u] += ge[sp - 1][u];
+            }
         float cm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {
@@ -443,12 +459,15 @@ static int proj_splits(int M, int E, int K, csa_dtype_t dt) {
   if (dt != CSA_DT_BF16 || use_proj_small(M, K, dt)) return 1;
   int tiles = ((M + PJ_BM - 1) / PJ_BM) * ((2 * E + PJ_BN - 1) / PJ_BN);
   int s = 1;
-  // split K while the grid holds fewer than two workgroups per CU; every
-  // split keeps whole k tiles - at least four when the pool has many rows to
-  // re-read the partials for, one for the few rows of a decode step
+  // split K while the grid holds fewer than one workgroup per CU (two for
+  // the few rows of a decode step); every split keeps whole k tiles - at
+  // least four when the pool has many rows to re-read the partials for, and
+  // then at most four splits (the pool's batched path)
   const int min_k = M <= PJ_BM ? 2 * PJ_BK : 4 * PJ_BK;
-  const int target = M <= PJ_BM ? 512 : 128;
-  while (tiles * s < target && K / (2 * s) >= min_k && (K / (2 * s)) % PJ_BK == 0) s *= 2;
+  const int target = M <= PJ_BM ? 512 : 256;
+  while (tiles * s < target && K / (2 * s) >= min_k && (K / (2 * s)) % PJ_BK == 0 &&
+         (M <= PJ_BM || s < 4))
+    s *= 2;
   return s;
 }
 
@@ -470,7 +489,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
         (const uint16_t*)a.x, (const uint16_t*)a.w_kv, (const uint16_t*)a.w_gate, pg, M, E, K);
   } else if (a.in_dt == CSA_DT_BF16) {
     dim3 grid((M + PJ_BM - 1) / PJ_BM, (2 * E + PJ_BN - 1) / PJ_BN, splits);
-    proj_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t*)a.x, (const uint16_t*)a.w_kv,
+    proj_bf16_kernel<<<grid, 512, 0, st>>>((const uint16_t*)a.x, (const uint16_t*)a.w_kv,
                                            (const uint16_t*)a.w_gate, pg, M, E, K, K / splits);
   } else {
     size_t n = (size_t)M * 2 * E;
@@ -480,24 +499,27 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   const int n_slots = (a.L + a.m - 1) / a.m + 1;
   dim3 pgrid(n_slots + 1, a.B);
   // the common gated window (m = 4 with overlap: 8 tokens) has a batched path
-  const bool w8 = (1 + a.overlap) * a.m == 8;
-#define CSA_LAUNCH_POOL(DT, W)                                                                  \
-  pool_kernel<DT, W><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape,    \
-                                            a.state_in, a.state_out, a.out, a.out_scale,       \
-                                            a.Nc_cap, n_slots, splits)
+  // (for up to four projection partials)
+  const int w8 = (1 + a.overlap) * a.m == 8 ? (splits == 1 ? 1 : (splits <= 4 ? 4 : 0)) : 0;
+#define CSA_LAUNCH_POOL(DT, W, NS)                                                                \
+  pool_kernel<DT, W, NS><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape,  \
+                                                a.state_in, a.state_out, a.out, a.out_scale,     \
+                                                a.Nc_cap, n_slots, splits)
+#define CSA_POOL_DT(DT)                            \
+  if (w8 == 1) CSA_LAUNCH_POOL(DT, 8, 1);          \
+  else if (w8 == 4) CSA_LAUNCH_POOL(DT, 8, 4);     \
+  else CSA_LAUNCH_POOL(DT, 0, 1);
   switch (a.out_dt) {
     case CSA_DT_F32:
-      if (w8) CSA_LAUNCH_POOL(CSA_DT_F32, 8);
-      else CSA_LAUNCH_POOL(CSA_DT_F32, 0);
+      CSA_POOL_DT(CSA_DT_F32);
       break;
     case CSA_DT_BF16:
-      if (w8) CSA_LAUNCH_POOL(CSA_DT_BF16, 8);
-      else CSA_LAUNCH_POOL(CSA_DT_BF16, 0);
+      CSA_POOL_DT(CSA_DT_BF16);
       break;
     default:
-      if (w8) CSA_LAUNCH_POOL(CSA_DT_FP8E4M3, 8);
-      else CSA_LAUNCH_POOL(CSA_DT_FP8E4M3, 0);
+      CSA_POOL_DT(CSA_DT_FP8E4M3);
   }
+#undef CSA_POOL_DT
 #undef CSA_LAUNCH_POOL
   return hipGetLastError();
 }
