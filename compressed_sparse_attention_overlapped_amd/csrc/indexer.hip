@@ -395,14 +395,18 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int rows, int T, int Nc_cap, int m, int topk,
     int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
-  __shared__ uint32_t keys_all[4][KMAX];
+  // rows of up to 2048 keys keep them in registers (lane l: keys l, l + 64,
+  // ...), longer ones in the wave's LDS slice
+  constexpr bool REG = KMAX <= 2048;
+  constexpr int KPL = KMAX / 64;  // keys per lane
+  __shared__ uint32_t keys_all[REG ? 1 : 4][REG ? 1 : KMAX];
   __shared__ uint32_t hist_all[4][256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;
   const int b = row / T, t = row % T;
-  uint32_t* keys = keys_all[wave];
+  uint32_t* keys = keys_all[REG ? 0 : wave];
   uint32_t* hist = hist_all[wave];
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const float* srow = scores + (size_t)row * Nc_cap;
@@ -421,24 +425,68 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     }
     return;
   }
-  for (int j0 = 0; j0 < nv; j0 += 256) {  // four loads in flight per lane
-    float v[4];
+  const int ng = (nv + 63) / 64;  // 64-key groups
+  // keys (order-preserving u32 of the scores), sixteen loads in flight per
+  // lane from clamped addresses, and the row's smallest and largest key
+  uint32_t kr[REG ? KPL : 1];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int g0 = 0; g0 < (REG ? KPL : ng); g0 += 16) {
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = j0 + 64 * u + lane < nv ? srow[j0 + 64 * u + lane] : 0.0f;
+    for (int u = 0; u < 16; ++u) v[u] = srow[min(64 * (g0 + u) + lane, nv - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (j0 + 64 * u + lane < nv) keys[j0 + 64 * u + lane] = score_key(v[u]);
+    for (int u = 0; u < 16; ++u) {
+      const int j = 64 * (g0 + u) + lane;
+      const uint32_t x = score_key(v[u]);
+      if (REG) kr[g0 + u] = x;
+      else if (g0 + u < ng) keys[min(j, KMAX - 1)] = x;
+      if (j < nv) {
+        kmin = min(kmin, x);
+        kmax = max(kmax, x);
+      }
+    }
   }
-  // radix select: lane l owns bins 255 - 4 l .. 252 - 4 l of each pass
-  uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)nsel;
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  // the histogram of one digit over the keys still matching the prefix; the
+  // atomics of a batch are issued back to back
+  auto count = [&](uint32_t mask, uint32_t prefix, int shift, uint32_t dmask) {
+    if constexpr (REG) {
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) {
+        const int j = 64 * u + lane;
+        if (j < nv && (kr[u] & mask) == prefix) atomicAdd(&hist[(kr[u] >> shift) & dmask], 1u);
+      }
+    } else {
+      for (int g0 = 0; g0 < ng; g0 += 8) {
+        uint32_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = keys[min(64 * (g0 + u) + lane, KMAX - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = 64 * (g0 + u) + lane;
+          if (j < nv && (x[u] & mask) == prefix) atomicAdd(&hist[(x[u] >> shift) & dmask], 1u);
+        }
+      }
+    }
+  };
+  // radix select over the bits below the keys' common prefix: lane l owns
+  // bins 255 - 4 l .. 252 - 4 l of each pass; digits of up to 8 bits.  (Every
+  // key equal: the mask covers all bits, and the output pass takes the first
+  // nsel entries.)
+  const uint32_t diff = kmin ^ kmax;
+  int hi = diff ? 31 - __clz((int)diff) : -1;  // highest bit where keys differ
+  uint32_t mask = hi < 0 ? 0xffffffffu : (hi >= 31 ? 0u : ~((2u << hi) - 1u));
+  uint32_t prefix = kmax & mask, remaining = (uint32_t)nsel;
   bool all_eq = false;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  while (!all_eq && hi >= 0) {
+    const int width = min(8, hi + 1), shift = hi - width + 1;
+    const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0u;
-    for (int j = lane; j < nv; j += 64) {
-      const uint32_t x = keys[j];
-      if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
-    }
+    count(mask, prefix, shift, dmask);
     uint32_t c[4], sum = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -470,17 +518,15 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     const uint32_t cum = __shfl(cum_sel, src, 64), cnt = __shfl(cnt_sel, src, 64);
     remaining -= cum;
     prefix |= d << shift;
-    mask |= 255u << shift;
-    if (cnt == remaining) {
-      all_eq = true;
-      break;
-    }
+    mask |= dmask << shift;
+    hi = shift - 1;
+    if (cnt == remaining) all_eq = true;
   }
   // ordered output: groups of 64 consecutive entries
   uint32_t out_base = 0u, eq_taken = 0u;
-  for (int j0 = 0; j0 < nv; j0 += 64) {
-    const int j = j0 + lane;
-    const uint32_t x = j < nv ? keys[j] & mask : 0u;
+  auto emit = [&](int g, uint32_t key) {
+    const int j = 64 * g + lane;
+    const uint32_t x = key & mask;
     const bool gt = j < nv && x > prefix;
     const bool eq = j < nv && x == prefix;
     const uint64_t eqm = __ballot(eq);
@@ -496,6 +542,13 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     }
     out_base += (uint32_t)__popcll(sm);
     eq_taken += (uint32_t)__popcll(eqm);
+  };
+  if constexpr (REG) {
+#pragma unroll
+    for (int u = 0; u < KPL; ++u)
+      if (u < ng) emit(u, kr[u]);
+  } else {
+    for (int g = 0; g < ng; ++g) emit(g, keys[64 * g + lane]);
   }
 }
 

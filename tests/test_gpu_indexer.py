@@ -92,6 +92,47 @@ def test_indexer_bf16_exact_ties_lower_index():
             assert sorted(blk) == members[:len(blk)]
 
 
+def test_indexer_bf16_rows_between_2k_and_8k():
+    # rows longer than the register-resident path (2048 keys) but short
+    # enough for one wave's LDS slice (8192)
+    d = gen.Draw(25)
+    B, T, Nc, m, topk = 2, 12, 5000, 4, 512
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    k_idx[1, 1000:1300] = k_idx[1, 20]       # a block of tied scores
+    q_pos, n_cmp = [20000, 3000], [Nc, 4990]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "bf16 2k-8k rows")
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "two_values", "one_high"])
+def test_indexer_bf16_degenerate_score_rows(kind):
+    # rows whose scores are all equal (keys all zero), take two values, or
+    # have a single outlier: ties resolve to the lowest indices, the radix
+    # passes start below the keys' common prefix
+    d = gen.Draw(24)
+    B, T, Nc, m, topk = 1, 6, 700, 4, 64
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    if kind == "all_equal":
+        k_idx[:] = 0
+    elif kind == "two_values":
+        k_idx[0, 0::2] = k_idx[0, 5]
+        k_idx[0, 1::2] = k_idx[0, 8]
+    else:
+        k_idx[0, :] = 0
+        k_idx[0, 333] = k_idx[0, 333] + 1.0
+    q_pos, n_cmp = [2600], [Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    for t in range(T):
+        # exact equality resolves exactly like the oracle
+        assert sorted(g_idx[0, t].tolist()) == sorted(o[0][0, t].tolist()), (kind, t)
+    if kind == "all_equal":
+        assert (g_idx[0] == np.arange(topk)[None, :]).all()
+
+
 def test_indexer_prefill_8k_sampled_rows():
     w = gen.WORKLOADS["csa_prefill_8k_bf16"]
     d = gen.Draw(w.seed + 100)
