@@ -37,7 +37,11 @@
  *    special case, so the multi-head form is "parity unpinned"; the top-k
  *    order is pinned against a library sort.
  *  - orc_sparse_attn / orc_hca_dense_attn: pinned to a library scaled
- *    dot-product attention with an explicit mask.
+ *    dot-product attention with an explicit mask.  The optional per-head
+ *    attention sink (the migration page lists `attn_sink` among the state of
+ *    CompressedSparseAttention; read as one more softmax term with logit
+ *    sink[h] and no value) is pinned to the same attention with one extra
+ *    key whose logit equals the sink and whose value is zero.
  */
 #include <math.h>
 #include <stdint.h>
@@ -343,11 +347,14 @@ int orc_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk
  * whose row r = j - raw_base lies in [0, R_cap).  One softmax runs over J:
  *     l_j = scale * q . K_j,  out = sum_j softmax(l)_j V_j,
  *     lse = log sum_j exp(l_j)   (natural log).
- * An empty J gives out = 0 and lse = -inf. */
+ * With a sink z (finite), the softmax runs over the logits l_j and z, the
+ * sink carrying no value:  out = sum_j e^{l_j} V_j / (e^z + sum_j e^{l_j}),
+ * lse = log(e^z + sum_j e^{l_j}).  sink = -inf is no sink.
+ * An empty J gives out = 0 and lse = -inf (= z with a sink). */
 static void attend_row(int D, double scale, const void* q, size_t qoff, int dt,
                        const void* const* rows_src, const size_t* rows_off, int n,
-                       double* o, double* lse) {
-  double mx = -INFINITY, den = 0;
+                       double sink, double* o, double* lse) {
+  double mx = sink, den = 0;
   double* l = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
   for (int d = 0; d < D; ++d) o[d] = 0;
   for (int r = 0; r < n; ++r) {
@@ -361,7 +368,8 @@ static void attend_row(int D, double scale, const void* q, size_t qoff, int dt,
     den += p;
     for (int d = 0; d < D; ++d) o[d] += p * ld(rows_src[r], rows_off[r] + D + d, dt);
   }
-  if (n > 0) {
+  if (sink > -INFINITY) den += exp(sink - mx);
+  if (den > 0) {
     for (int d = 0; d < D; ++d) o[d] /= den;
     *lse = mx + log(den);
   } else {
@@ -370,9 +378,10 @@ static void attend_row(int D, double scale, const void* q, size_t qoff, int dt,
   free(l);
 }
 
+/* sink: [H] logits or NULL (no sink), for both attention forms. */
 int orc_sparse_attn(int B, int T, int H, int D, int topk, int window, double scale,
-                    const int64_t* q_pos, const void* q, const void* kv_cmp, int Nc_cap,
-                    const int32_t* idx, const void* kv_raw, int R_cap,
+                    const double* sink, const int64_t* q_pos, const void* q, const void* kv_cmp,
+                    int Nc_cap, const int32_t* idx, const void* kv_raw, int R_cap,
                     const int64_t* raw_base, int dt, double* out, double* lse) {
   if (B < 0 || T < 0 || H < 1 || D < 1 || topk < 0 || window < 0) return 1;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -402,7 +411,8 @@ int orc_sparse_attn(int B, int T, int H, int D, int topk, int window, double sca
     for (int h = 0; h < H; ++h) {
       size_t row = ((size_t)b * T + t) * H + h;
       double l;
-      attend_row(D, scale, q, row * D, dt, src, off, n, out + row * D, &l);
+      attend_row(D, scale, q, row * D, dt, src, off, n, sink ? sink[h] : -INFINITY, out + row * D,
+                 &l);
       if (lse) lse[row] = l;
     }
     free(src);
@@ -414,7 +424,7 @@ int orc_sparse_attn(int B, int T, int H, int D, int topk, int window, double sca
 /* HCA: the compressed part of the key set is every visible entry
  * [0, n_vis(pos)), n_vis as for the indexer; the window part is as above. */
 int orc_hca_dense_attn(int B, int T, int H, int D, int m, int window, double scale,
-                       const int64_t* q_pos, const int32_t* n_cmp, const void* q,
+                       const double* sink, const int64_t* q_pos, const int32_t* n_cmp, const void* q,
                        const void* kv_cmp, int Nc_cap, const void* kv_raw, int R_cap,
                        const int64_t* raw_base, int dt, double* out, double* lse) {
   if (B < 0 || T < 0 || H < 1 || D < 1 || m < 1 || window < 0) return 1;
@@ -444,7 +454,8 @@ int orc_hca_dense_attn(int B, int T, int H, int D, int m, int window, double sca
     for (int h = 0; h < H; ++h) {
       size_t row = ((size_t)b * T + t) * H + h;
       double l;
-      attend_row(D, scale, q, row * D, dt, src, off, n, out + row * D, &l);
+      attend_row(D, scale, q, row * D, dt, src, off, n, sink ? sink[h] : -INFINITY, out + row * D,
+                 &l);
       if (lse) lse[row] = l;
     }
     free(src);

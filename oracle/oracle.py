@@ -47,8 +47,8 @@ def lib():
         vp, i32, i64p, dp = C.c_void_p, C.c_int, C.c_void_p, C.c_void_p
         L.orc_compress.argtypes = [i32] * 6 + [i64p, vp, vp, vp, i32, dp, dp, dp, i32, dp, vp]
         L.orc_indexer_topk.argtypes = [i32] * 7 + [i64p, vp, vp, vp, vp, vp, vp, i32, vp, dp, dp, dp]
-        L.orc_sparse_attn.argtypes = [i32] * 6 + [C.c_double, i64p, vp, vp, i32, vp, vp, i32, i64p, i32, dp, dp]
-        L.orc_hca_dense_attn.argtypes = [i32] * 6 + [C.c_double, i64p, vp, vp, vp, i32, vp, i32, i64p, i32, dp, dp]
+        L.orc_sparse_attn.argtypes = [i32] * 6 + [C.c_double, dp, i64p, vp, vp, i32, vp, vp, i32, i64p, i32, dp, dp]
+        L.orc_hca_dense_attn.argtypes = [i32] * 6 + [C.c_double, dp, i64p, vp, vp, vp, i32, vp, i32, i64p, i32, dp, dp]
         for f in (L.orc_compress, L.orc_indexer_topk, L.orc_sparse_attn, L.orc_hca_dense_attn):
             f.restype = C.c_int
         L.orc_e4m3_encode.argtypes = [C.c_double]
@@ -178,10 +178,17 @@ def indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None,
     return idx, sel, kth, alls
 
 
-def sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None):
+def _sink(sink, H):
+    if sink is None:
+        return None
+    return _c(np.broadcast_to(np.asarray(sink, np.float64), (H,)), np.float64)
+
+
+def sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None, sink=None):
     """CSA attention: joint softmax over the selected compressed rows and the
     raw sliding window.  q [B, T, H, D], kv_cmp [B, Nc_cap, 2D],
-    idx [B, T, topk], kv_raw [B, R_cap, 2D].  Returns (out, lse) float64."""
+    idx [B, T, topk], kv_raw [B, R_cap, 2D]; sink [H] logits or None (one
+    more softmax term per head, with no value).  Returns (out, lse) float64."""
     q, kv_cmp, kv_raw = _c(q), _c(kv_cmp), _c(kv_raw)
     idx = _c(idx, np.int32)
     B, T, H, D = q.shape
@@ -193,15 +200,17 @@ def sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None):
     raw_base = _c(np.broadcast_to(np.asarray(raw_base, np.int64), (B,)), np.int64)
     out = np.zeros((B, T, H, D), np.float64)
     lse = np.zeros((B, T, H), np.float64)
-    rc = lib().orc_sparse_attn(B, T, H, D, topk, window, scale, _p(q_pos), _p(q), _p(kv_cmp),
+    sk = _sink(sink, H)
+    rc = lib().orc_sparse_attn(B, T, H, D, topk, window, scale, _p(sk), _p(q_pos), _p(q), _p(kv_cmp),
                                kv_cmp.shape[1], _p(idx), _p(kv_raw), kv_raw.shape[1],
                                _p(raw_base), dt, _p(out), _p(lse))
     assert rc == 0
     return out, lse
 
 
-def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=None):
-    """HCA attention: every visible compressed entry plus the raw window."""
+def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=None, sink=None):
+    """HCA attention: every visible compressed entry plus the raw window
+    (sink as for sparse_attn)."""
     q, kv_cmp, kv_raw = _c(q), _c(kv_cmp), _c(kv_raw)
     B, T, H, D = q.shape
     dt = _dt(q)
@@ -212,7 +221,8 @@ def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=N
     raw_base = _c(np.broadcast_to(np.asarray(raw_base, np.int64), (B,)), np.int64)
     out = np.zeros((B, T, H, D), np.float64)
     lse = np.zeros((B, T, H), np.float64)
-    rc = lib().orc_hca_dense_attn(B, T, H, D, m, window, scale, _p(q_pos), _p(n_cmp), _p(q),
+    sk = _sink(sink, H)
+    rc = lib().orc_hca_dense_attn(B, T, H, D, m, window, scale, _p(sk), _p(q_pos), _p(n_cmp), _p(q),
                                   _p(kv_cmp), kv_cmp.shape[1], _p(kv_raw), kv_raw.shape[1],
                                   _p(raw_base), dt, _p(out), _p(lse))
     assert rc == 0

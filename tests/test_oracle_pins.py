@@ -316,6 +316,57 @@ def test_sparse_attn_matches_sdpa_with_mask():
         np.testing.assert_allclose(lse[b], rl, rtol=1e-10, atol=1e-12)
 
 
+def test_attention_sink_is_a_zero_value_key():
+    # A sink of logit z behaves as one more attended key whose scaled logit
+    # is z and whose value is zero: built explicitly for one head and query
+    # (q[0] = 1, scale = 1 and k* = z e_0 give q . k* = z exactly), appended
+    # to the compressed rows and selected.
+    r = rng(24)
+    D, Nc = 8, 7
+    q = r.normal(0, 1, (1, 1, 1, D)).astype(np.float32)
+    q[..., 0] = 1.0
+    kv = r.normal(0, 1, (1, Nc, 2 * D)).astype(np.float32)
+    for z in (-3.0, 0.5, 2.5, 9.0):
+        kstar = np.zeros(2 * D, np.float32)
+        kstar[0] = z
+        kv2 = np.concatenate([kv, kstar[None, None]], axis=1)
+        idx = np.arange(Nc, dtype=np.int32)[None, None]
+        idx2 = np.arange(Nc + 1, dtype=np.int32)[None, None]
+        raw = np.zeros((1, 1, 2 * D), np.float32)
+        out_s, lse_s = orc.sparse_attn(q, kv, idx, raw, 0, 5, 0, scale=1.0, sink=[z])
+        out_k, lse_k = orc.sparse_attn(q, kv2, idx2, raw, 0, 5, 0, scale=1.0)
+        np.testing.assert_allclose(out_s, out_k, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse_s, lse_k, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_sink_closed_form_and_limits():
+    # out_sink = out * sigmoid(lse - z), lse_sink = logaddexp(lse, z); a sink
+    # of -inf is no sink; an empty key set gives out = 0 and lse = z
+    q, kv_cmp, kv_raw, idx = _attn_case(25)
+    B, T, H, D = q.shape
+    q_pos, raw_base = np.array([14, 3]), np.array([5, 0])
+    idx[1, 0] = -1
+    z = np.linspace(-2.0, 3.0, H)
+    out, lse = orc.sparse_attn(q, kv_cmp, idx, kv_raw, 0, q_pos, raw_base)
+    out_s, lse_s = orc.sparse_attn(q, kv_cmp, idx, kv_raw, 0, q_pos, raw_base, sink=z)
+    fin = np.isfinite(lse)
+    sig = np.where(fin, 1 / (1 + np.exp(z[None, None] - np.where(fin, lse, 0))), 0.0)
+    np.testing.assert_allclose(out_s, out * sig[..., None], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse_s[fin], np.logaddexp(lse, z[None, None])[fin], rtol=1e-12)
+    assert (out_s[1, 0] == 0).all()
+    np.testing.assert_array_equal(lse_s[1, 0], z)
+    out_n, lse_n = orc.sparse_attn(q, kv_cmp, idx, kv_raw, 0, q_pos, raw_base,
+                                   sink=np.full(H, -np.inf))
+    np.testing.assert_array_equal(out_n, out)
+    np.testing.assert_array_equal(lse_n, lse)
+    m, n_cmp = 4, [kv_cmp.shape[1]] * B
+    oh, lh = orc.hca_dense_attn(q, kv_cmp, kv_raw, m, 3, q_pos, n_cmp, raw_base)
+    ohs, lhs = orc.hca_dense_attn(q, kv_cmp, kv_raw, m, 3, q_pos, n_cmp, raw_base, sink=z)
+    fin = np.isfinite(lh)
+    sig = np.where(fin, 1 / (1 + np.exp(z[None, None] - np.where(fin, lh, 0))), 0.0)
+    np.testing.assert_allclose(ohs, oh * sig[..., None], rtol=1e-12, atol=1e-14)
+
+
 def test_sparse_attn_window_only_is_causal_attention():
     # topk = 0 and W >= S: full causal attention over the raw KV (the ratio-0
     # sliding-window layer with a window covering everything).
