@@ -46,9 +46,9 @@ def lib():
         L.csa_compress_workspace_size.argtypes = [i32] * 7
         L.csa_indexer_topk.argtypes = [i32] * 7 + [vp] * 7 + [i32, vp, vp, vp, sz, vp]
         L.csa_indexer_topk_workspace_size.argtypes = [i32] * 7
-        L.csa_sparse_attn.argtypes = [i32] * 6 + [f32, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+        L.csa_sparse_attn.argtypes = [i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, sz, vp]
         L.csa_sparse_attn_workspace_size.argtypes = [i32] * 6
-        L.hca_dense_attn.argtypes = [i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+        L.hca_dense_attn.argtypes = [i32] * 6 + [f32, vp, vp, vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
         L.hca_dense_attn_workspace_size.argtypes = [i32] * 6
         for f in (L.csa_compress, L.csa_indexer_topk, L.csa_sparse_attn, L.hca_dense_attn):
             f.restype = C.c_int
@@ -150,10 +150,19 @@ def csa_indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None, k
     return idx_out, score_out
 
 
+def _sink(sink, H):
+    if sink is None:
+        return None
+    if sink.dtype != torch.float32 or sink.shape != (H,) or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 tensor of shape [H]")
+    return sink
+
+
 def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None, out=None,
-                    lse=None, want_lse=False, workspace=None):
-    """CSA attention; returns (out [B, T, H, D], lse f32 [B, T, H] or None)."""
-    _dense(q, kv_cmp, idx, kv_raw, q_pos, raw_base)
+                    lse=None, want_lse=False, workspace=None, sink=None):
+    """CSA attention; returns (out [B, T, H, D], lse f32 [B, T, H] or None).
+    sink: f32 [H] per-head sink logits or None."""
+    _dense(q, kv_cmp, idx, kv_raw, q_pos, raw_base, sink)
     B, T, H, D = q.shape
     topk = idx.shape[2] if idx is not None else 0
     scale = D ** -0.5 if scale is None else float(scale)
@@ -162,7 +171,8 @@ def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None,
     if want_lse and lse is None:
         lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
     ws, nb = _workspace(csa_sparse_attn_workspace_size(B, T, H, D, topk, window), q, workspace)
-    rc = lib().csa_sparse_attn(B, T, H, D, topk, window, scale, _p(q_pos), _p(q), _p(kv_cmp),
+    rc = lib().csa_sparse_attn(B, T, H, D, topk, window, scale, _p(_sink(sink, H)), _p(q_pos),
+                               _p(q), _p(kv_cmp),
                                kv_cmp.shape[1], _p(idx), _p(kv_raw), kv_raw.shape[1],
                                _p(raw_base), _DT[q.dtype], _p(out), _p(lse), _p(ws), nb,
                                _stream(q))
@@ -171,9 +181,10 @@ def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None,
 
 
 def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=None, out=None,
-                   lse=None, want_lse=False, workspace=None):
-    """HCA attention; returns (out [B, T, H, D], lse or None)."""
-    _dense(q, kv_cmp, kv_raw, q_pos, n_cmp, raw_base)
+                   lse=None, want_lse=False, workspace=None, sink=None):
+    """HCA attention; returns (out [B, T, H, D], lse or None).
+    sink: f32 [H] per-head sink logits or None."""
+    _dense(q, kv_cmp, kv_raw, q_pos, n_cmp, raw_base, sink)
     B, T, H, D = q.shape
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
@@ -182,7 +193,8 @@ def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=N
         lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
     ws, nb = _workspace(hca_dense_attn_workspace_size(B, T, H, D, kv_cmp.shape[1], window), q,
                         workspace)
-    rc = lib().hca_dense_attn(B, T, H, D, m, window, scale, _p(q_pos), _p(n_cmp), _p(q),
+    rc = lib().hca_dense_attn(B, T, H, D, m, window, scale, _p(_sink(sink, H)), _p(q_pos),
+                              _p(n_cmp), _p(q),
                               _p(kv_cmp), kv_cmp.shape[1], _p(kv_raw), kv_raw.shape[1],
                               _p(raw_base), _DT[q.dtype], _p(out), _p(lse), _p(ws), nb, _stream(q))
     _check("hca_dense_attn", rc)

@@ -160,7 +160,8 @@ size_t csa_sparse_attn_workspace_size(int B, int T, int H, int D, int topk, int 
 }
 
 csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, float scale,
-                             const int64_t* q_pos, const void* q, const void* kv_cmp, int Nc_cap,
+                             const float* sink, const int64_t* q_pos, const void* q,
+                             const void* kv_cmp, int Nc_cap,
                              const int32_t* idx, const void* kv_raw, int R_cap,
                              const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
                              void* workspace, size_t ws_bytes, hipStream_t stream) {
@@ -175,8 +176,8 @@ csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, f
       dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, topk + window, true);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "csa_sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
-  csa_host::AttnArgs a{B, T, H, D, topk, window, 1, Nc_cap, R_cap, false, scale, q_pos, nullptr,
-                       q, kv_cmp, idx, kv_raw, raw_base, dt, out, lse, workspace};
+  csa_host::AttnArgs a{B, T, H, D, topk, window, 1, Nc_cap, R_cap, false, scale, sink, q_pos,
+                       nullptr, q, kv_cmp, idx, kv_raw, raw_base, dt, out, lse, workspace};
   return hip_status(csa_host::launch_attn(a, stream), "csa_sparse_attn launch");
 }
 
@@ -186,7 +187,8 @@ size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int
 }
 
 csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float scale,
-                            const int64_t* q_pos, const int32_t* n_cmp, const void* q,
+                            const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                            const void* q,
                             const void* kv_cmp, int Nc_cap, const void* kv_raw, int R_cap,
                             const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
                             void* workspace, size_t ws_bytes, hipStream_t stream) {
@@ -199,8 +201,8 @@ csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float
       dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window, false);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "hca_dense_attn: workspace %zu < %zu bytes", ws_bytes, need);
-  csa_host::AttnArgs a{B, T, H, D, 0, window, m, Nc_cap, R_cap, true, scale, q_pos, n_cmp,
-                       q, kv_cmp, nullptr, kv_raw, raw_base, dt, out, lse, workspace};
+  csa_host::AttnArgs a{B, T, H, D, 0, window, m, Nc_cap, R_cap, true, scale, sink, q_pos,
+                       n_cmp, q, kv_cmp, nullptr, kv_raw, raw_base, dt, out, lse, workspace};
   return hip_status(csa_host::launch_attn(a, stream), "hca_dense_attn launch");
 }
 

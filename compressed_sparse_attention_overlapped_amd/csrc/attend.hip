@@ -71,6 +71,26 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
+// Final normalisation of one (row, head) softmax from its running maximum m
+// (log2 units of the scaled logits) and sum l, with the head's sink logit
+// (natural-log units, one more term with no value) when sink is given and
+// the head's entry is finite: inv multiplies the numerator accumulated
+// relative to m; lse is the natural-log sum.
+__device__ __forceinline__ void finish_softmax(float m, float l, const float* sink, int h,
+                                               float& inv, float& lse_out) {
+  const float z = sink ? sink[h] * kLog2e : -INFINITY;
+  if (z > -INFINITY) {
+    const float mn = fmaxf(m, z);
+    const float c = m == -INFINITY ? 0.0f : exp2f(m - mn);
+    const float lt = l * c + exp2f(z - mn);
+    inv = c / lt;
+    lse_out = (mn + __log2f(lt)) * kLn2;
+  } else {
+    inv = l > 0.0f ? 1.0f / l : 0.0f;
+    lse_out = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- bf16 prefill
 // Many query rows: a workgroup owns PF_ROWS consecutive rows of one sequence;
 // each row has H/32 waves, one per 32-head slice (8 waves for H = 64, two per
@@ -110,7 +130,8 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
-    int R_cap, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int R_cap, float scale_log2, const float* __restrict__ sink, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
   constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH;
   constexpr bool dense = !SPARSE;
   // phase A uses tiles 0..1 (double buffer); phase B tile r per row
@@ -362,7 +383,8 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   // 32 dt + 8 (r/4) + 4 h2 + r%4
   if (!active) return;
   const int h = 32 * hh + l32;
-  const float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
+  float inv, lse_v;
+  finish_softmax(mrun, lrun, sink, h, inv, lse_v);
   uint16_t* orow = out + (rowi * H + h) * D;
   for (int dt = 0; dt < 4; ++dt)
     for (int rq = 0; rq < 4; ++rq) {
@@ -371,7 +393,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
       uint32_t hi = (uint32_t)f32_to_bf16(o[dt][4 * rq + 2] * inv) | ((uint32_t)f32_to_bf16(o[dt][4 * rq + 3] * inv) << 16);
       *(u32x2*)(orow + d) = u32x2{lo, hi};
     }
-  if (lse && h2 == 0) lse[rowi * H + h] = lrun > 0.0f ? (mrun + __log2f(lrun)) * kLn2 : -INFINITY;
+  if (lse && h2 == 0) lse[rowi * H + h] = lse_v;
 }
 
 // ---------------------------------------------------------------- bf16 decode
@@ -402,8 +424,9 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
-    int R_cap, bool dense, float scale_log2, int n_split, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    int R_cap, bool dense, float scale_log2, const float* __restrict__ sink, int n_split,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
   constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
@@ -613,7 +636,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   // ---- results: lane holds head 16 wave + hl, dims 16 dt + 4 g + i
   const int h = 16 * wave + hl;
   if (n_split == 1) {
-    const float inv = lrun > 0.0f ? 1.0f / lrun : 0.0f;
+    float inv, lse_v;
+    finish_softmax(mrun, lrun, sink, h, inv, lse_v);
     uint16_t* orow = out + ((size_t)rowi * H + h) * D;
     for (int dt = 0; dt < 8; ++dt) {
       const int d = 16 * dt + 4 * g;
@@ -621,8 +645,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
       uint32_t hi = (uint32_t)f32_to_bf16(o[dt][2] * inv) | ((uint32_t)f32_to_bf16(o[dt][3] * inv) << 16);
       *(u32x2*)(orow + d) = u32x2{lo, hi};
     }
-    if (lse && g == 0)
-      lse[(size_t)rowi * H + h] = lrun > 0.0f ? (mrun + __log2f(lrun)) * kLn2 : -INFINITY;
+    if (lse && g == 0) lse[(size_t)rowi * H + h] = lse_v;
   } else {
     float* po = part_o + ((size_t)item * H + h) * D;
     for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt + 4 * g) = o[dt];
@@ -644,7 +667,9 @@ constexpr int CB_MAX_SPLIT = 64;
 template <int OUT_DT>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
-                                                      int n_split, int H, void* __restrict__ out,
+                                                      int n_split, int H,
+                                                      const float* __restrict__ sink,
+                                                      void* __restrict__ out,
                                                       float* __restrict__ lse) {
   constexpr int D = 128;
   const int rowi = blockIdx.x;
@@ -667,12 +692,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 #pragma unroll
     for (int k = 0; k < 8; ++k) O = fmaf(v[k], __shfl(c, s0 + k, 64), O);
   }
-  const float v = Ls > 0.0f ? O / Ls : 0.0f;
+  float inv, lse_v;
+  finish_softmax(M, Ls, sink, h, inv, lse_v);
+  const float v = O * inv;
   if (OUT_DT == CSA_DT_BF16)
     ((uint16_t*)out)[((size_t)rowi * H + h) * D + d] = f32_to_bf16(v);
   else
     ((float*)out)[((size_t)rowi * H + h) * D + d] = v;
-  if (lse && d == 0) lse[(size_t)rowi * H + h] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+  if (lse && d == 0) lse[(size_t)rowi * H + h] = lse_v;
 }
 
 // ---------------------------------------------------------------- fp32
@@ -682,7 +709,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
     const float* __restrict__ kv_raw, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, const int64_t* __restrict__ raw_base, int T, int H, int D,
     int topk, int window, int m, int Nc_cap, int R_cap, bool dense, float scale_log2,
-    float* __restrict__ out, float* __restrict__ lse) {
+    const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x;
   const int rowi = blockIdx.x / H, h = blockIdx.x % H;
   const int b = rowi / T, t = rowi % T;
@@ -710,11 +737,12 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
     o1 = o1 * corr + pv * (lane + 64 < D ? src[D + lane + 64] : 0.0f);
     mrun = mnew;
   }
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float inv, lse_v;
+  finish_softmax(mrun, l, sink, h, inv, lse_v);
   float* orow = out + ((size_t)rowi * H + h) * D;
   if (lane < D) orow[lane] = o0 * inv;
   if (lane + 64 < D) orow[lane + 64] = o1 * inv;
-  if (lse && lane == 0) lse[(size_t)rowi * H + h] = l > 0.0f ? (mrun + __log2f(l)) * kLn2 : -INFINITY;
+  if (lse && lane == 0) lse[(size_t)rowi * H + h] = lse_v;
 }
 
 }  // namespace csa
@@ -771,7 +799,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     attn_f32_kernel<<<rows * a.H, 64, 0, st>>>(
         (const float*)a.q, (const float*)a.kv_cmp, a.idx, (const float*)a.kv_raw, a.q_pos,
         a.n_cmp, a.raw_base, a.T, a.H, a.D, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-        scale_log2, (float*)a.out, a.lse);
+        scale_log2, a.sink, (float*)a.out, a.lse);
     return hipGetLastError();
   }
   const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
@@ -785,12 +813,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
       attn_dec_kernel<4><<<grid, 256, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
     else
       attn_dec_kernel<2><<<grid, 128, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
   } else {
     // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
     // rows share only the window: 2 rows, so that two independent
@@ -799,7 +827,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   attn_pf_kernel<NH, ROWS, SP><<<(unsigned)(a.B * ((a.T + ROWS - 1) / ROWS)), 64 * ROWS * NH, 0,   \
                                  st>>>(                                                             \
       (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,  \
-      a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, scale_log2,              \
+      a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, scale_log2, a.sink,      \
       (uint16_t*)a.out, a.lse)
     if (a.H == 64) {
       if (a.dense) CSA_LAUNCH_PF(2, 4, false);
@@ -812,7 +840,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   }
   if (n_split > 1)
     combine_kernel<CSA_DT_BF16><<<dim3(rows, a.H / 2), 256, 0, st>>>(part_o, part_ml, n_split,
-                                                                      a.H, a.out, a.lse);
+                                                                      a.H, a.sink, a.out, a.lse);
   return hipGetLastError();
 }
 

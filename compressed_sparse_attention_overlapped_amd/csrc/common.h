@@ -177,6 +177,7 @@ struct AttnArgs {
   int B, T, H, D, topk, window, m, Nc_cap, R_cap;
   bool dense;  // HCA: every visible entry instead of an index list
   float scale;
+  const float* sink;  // [H] per-head sink logits or null
   const int64_t* q_pos;
   const int32_t* n_cmp;
   const void* q;

@@ -141,7 +141,14 @@ size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_ca
  *     lse = ln sum_j exp(l_j).
  * A KV row is [K | V] of width 2 D; every head shares it.  Slots with idx < 0
  * or idx >= Nc_cap are skipped; an empty J gives out = 0 and lse = -inf.
+ * Attention sink (the migration page, section 3.2, lists attn_sink among the
+ * attention's state): when sink is given, head h's softmax has one more term
+ * with logit sink[h] (natural-log units of l) and no value:
+ *     out = sum_j e^{l_j} V_j / (e^{sink[h]} + sum_j e^{l_j}),
+ *     lse = ln(e^{sink[h]} + sum_j e^{l_j});
+ * a sink of -inf is none, and an empty J then gives out = 0, lse = sink[h].
  *
+ *  sink     fp32 [H] (device) or NULL
  *  q        [B, T, H, D] in dt;  out [B, T, H, D] in dt;  lse fp32 [B, T, H] or NULL
  *  kv_cmp   [B, Nc_cap, 2 D] in dt;  idx int32 [B, T, topk] (topk may be 0)
  *  kv_raw   [B, R_cap, 2 D] in dt;   raw_base int64 [B]
@@ -150,7 +157,8 @@ size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_ca
  * split-key decode kernel), topk + window <= 64 * 4032.
  */
 csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, float scale,
-                             const int64_t* q_pos, const void* q, const void* kv_cmp,
+                             const float* sink, const int64_t* q_pos, const void* q,
+                             const void* kv_cmp,
                              int Nc_cap, const int32_t* idx, const void* kv_raw, int R_cap,
                              const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
                              void* workspace, size_t ws_bytes, hipStream_t stream);
@@ -159,11 +167,12 @@ size_t csa_sparse_attn_workspace_size(int B, int T, int H, int D, int topk, int 
 /*
  * HCA: heavily compressed attention (DS-V4 analysis sections 1.4-1.5: ratio
  * m' >> m, dense attention over every compressed entry, plus the window).
- * As csa_sparse_attn with the compressed part of J being every visible entry
- * j < n_vis(t) = min(n_cmp[b], floor((t + 1) / m), Nc_cap).
+ * As csa_sparse_attn (sink included) with the compressed part of J being
+ * every visible entry j < n_vis(t) = min(n_cmp[b], floor((t + 1) / m), Nc_cap).
  */
 csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float scale,
-                            const int64_t* q_pos, const int32_t* n_cmp, const void* q,
+                            const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                            const void* q,
                             const void* kv_cmp, int Nc_cap, const void* kv_raw, int R_cap,
                             const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
                             void* workspace, size_t ws_bytes, hipStream_t stream);

@@ -80,10 +80,10 @@ def test_argument_errors_are_reported_without_launch(L):
                             None, 1, dummy, None, None, 0, None)
     assert rc == 3
     # bf16 attention with an unsupported head count
-    rc = L.csa_sparse_attn(1, 1, 8, 128, 4, 4, C.c_float(1.0), dummy, dummy, dummy, 4, dummy,
-                           dummy, 4, dummy, 1, dummy, None, None, 0, None)
+    rc = L.csa_sparse_attn(1, 1, 8, 128, 4, 4, C.c_float(1.0), None, dummy, dummy, dummy, 4,
+                           dummy, dummy, 4, dummy, 1, dummy, None, None, 0, None)
     assert rc == 2
     # HCA without n_cmp
-    rc = L.hca_dense_attn(1, 1, 64, 128, 128, 4, C.c_float(1.0), dummy, None, dummy, dummy, 4,
-                          dummy, 4, dummy, 1, dummy, None, None, 0, None)
+    rc = L.hca_dense_attn(1, 1, 64, 128, 128, 4, C.c_float(1.0), None, dummy, None, dummy, dummy,
+                          4, dummy, 4, dummy, 1, dummy, None, None, 0, None)
     assert rc == 1

@@ -72,6 +72,76 @@ def test_sparse_attn_bf16_ragged(H):
     _check(out, lse, ref, rl, torch.bfloat16, "sparse bf16 H=%d" % H)
 
 
+def _sink_vec(d, H):
+    z = (d.normal(H) * 2.0).float()
+    z[0] = -math.inf          # no sink for head 0
+    z[1] = 12.0               # a sink above every logit
+    return z
+
+
+@pytest.mark.parametrize("case", ["decode_split", "decode_one", "prefill", "f32"])
+def test_sparse_attn_with_sink(case):
+    d = gen.Draw(40 + len(case))
+    H, D = 64, 128
+    if case == "decode_split":      # split-key decode kernel + combine
+        B, T, Nc, R, topk, W = 2, 1, 2000, 600, 300, 200
+    elif case == "decode_one":      # decode kernel, one split
+        B, T, Nc, R, topk, W = 3, 20, 90, 300, 32, 24
+    elif case == "prefill":         # prefill kernel
+        B, T, Nc, R, topk, W = 1, 1030, 300, 1100, 64, 64
+    else:
+        B, T, Nc, R, topk, W, H, D = 1, 30, 40, 60, 8, 6, 8, 64
+    fmt = gen.F32 if case == "f32" else gen.BF16
+    q = gen.store(d.normal(B, T, H, D), fmt)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), fmt)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), fmt)
+    q_pos = [min(4 * Nc, 6000) + 7 * b for b in range(B)]
+    raw_base = [max(0, q_pos[b] + T - R) for b in range(B)]
+    idx = _rand_idx(d, B, T, topk, lambda b, t: _n_vis(q_pos[b] + t, Nc, 4, Nc), 0.2)
+    idx[0, 0] = -1
+    z = _sink_vec(d, H)
+    out, lse = csa.csa_sparse_attn(q.to(DEV), kv_cmp.to(DEV), idx.to(DEV), kv_raw.to(DEV), W,
+                                   dev_i64(q_pos), dev_i64(raw_base), want_lse=True,
+                                   sink=z.to(DEV))
+    torch.cuda.synchronize()
+    rows = range(T) if T <= 40 else [0, 1, 515, T - 1]
+    for t in rows:
+        ref, rl = orc.sparse_attn(gen.host_bits(q[:, t:t + 1]), gen.host_bits(kv_cmp),
+                                  idx[:, t:t + 1].numpy(), gen.host_bits(kv_raw), W,
+                                  [p + t for p in q_pos], raw_base, sink=z.double().numpy())
+        _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl,
+               torch.float32 if case == "f32" else torch.bfloat16, "sink %s t=%d" % (case, t))
+
+
+def test_sink_on_empty_rows_and_hca():
+    d = gen.Draw(45)
+    B, T, H, D = 1, 4, 64, 128
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv = gen.store(d.normal(B, 8, 2 * D), gen.BF16)
+    z = _sink_vec(d, H)
+    idx = torch.full((B, T, 16), -1, dtype=torch.int32)
+    out, lse = csa.csa_sparse_attn(q.to(DEV), kv.to(DEV), idx.to(DEV), kv.to(DEV), 0, dev_i64([5]),
+                                   dev_i64([0]), want_lse=True, sink=z.to(DEV))
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()
+    l = lse.cpu()
+    assert torch.isneginf(l[..., 0]).all()
+    torch.testing.assert_close(l[..., 1:], z[1:].expand_as(l[..., 1:]), rtol=1e-6, atol=1e-6)
+    # HCA with a sink
+    B, T, m, W, Nc, R = 2, 50, 16, 40, 30, 200
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    q_pos, n_cmp, raw_base = [0, 420], [Nc, 27], [0, 300]
+    out, lse = csa.hca_dense_attn(q.to(DEV), kv_cmp.to(DEV), kv_raw.to(DEV), m, W, dev_i64(q_pos),
+                                  dev_i32(n_cmp), dev_i64(raw_base), want_lse=True,
+                                  sink=z.to(DEV))
+    torch.cuda.synchronize()
+    ref, rl = orc.hca_dense_attn(gen.host_bits(q), gen.host_bits(kv_cmp), gen.host_bits(kv_raw), m,
+                                 W, q_pos, n_cmp, raw_base, sink=z.double().numpy())
+    _check(out, lse, ref, rl, torch.bfloat16, "hca sink")
+
+
 def test_sparse_attn_empty_rows_give_zero():
     d = gen.Draw(33)
     B, T, H, D = 1, 4, 64, 128
