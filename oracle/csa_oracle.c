@@ -31,7 +31,10 @@
  *  - orc_compress: the uniform-gate / no-overlap case is pinned to the
  *    mean-pool closed form; the non-uniform overlapping gate form is the
  *    plainest reading of section 3.2 of the migration page and is otherwise
- *    "parity unpinned" by the pages.
+ *    "parity unpinned" by the pages.  The optional Hadamard rotation of an
+ *    entry (the migration page names a Hadamard step in the compressor and
+ *    the indexer, section 3.2; read as the Sylvester-ordered Walsh-Hadamard
+ *    matrix scaled by 1/sqrt(E)) is pinned to a library Hadamard matrix.
  *  - orc_indexer_topk: the score formula (sum over heads of w * ReLU(q.k)) is
  *    the published Lightning Indexer form; the pages print only its one-head
  *    special case, so the multi-head form is "parity unpinned"; the top-k
@@ -152,14 +155,29 @@ void orc_quant_rows_e4m3(int rows, int cols, const double* in, uint8_t* codes,
  * order; absent tokens carry P = 0, G = -inf, which gives them zero weight).
  * state_out receives the same record for the last (1 + o) m - 1 tokens.
  * Output rows are written (double, before any storage rounding) for every
- * entry completed in the call with i < Nc_cap; written[b, i] flags them. */
-int orc_compress(int B, int L, int d_model, int E, int m, int overlap,
+ * entry completed in the call with i < Nc_cap; written[b, i] flags them.
+ * With rotate, each written row C_i is replaced by H C_i / sqrt(E), H the
+ * Walsh-Hadamard matrix of order E (a power of two) in Sylvester order,
+ * H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]. */
+static void hadamard_rows(double* v, int E) {
+  for (int len = 1; len < E; len <<= 1)
+    for (int blk = 0; blk < E; blk += 2 * len)
+      for (int j = blk; j < blk + len; ++j) {
+        const double a = v[j], c = v[j + len];
+        v[j] = a + c;
+        v[j + len] = a - c;
+      }
+  for (int e = 0; e < E; ++e) v[e] /= sqrt((double)E);
+}
+
+int orc_compress(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                  const int64_t* pos0, const void* x, const void* w_kv,
                  const void* w_gate, int in_dt, const double* ape,
                  const double* state_in, double* state_out, int Nc_cap,
                  double* out, uint8_t* written) {
   const int Sw = (1 + overlap) * m, ns = Sw - 1;
   if (B < 0 || L < 0 || m < 1 || E < 1 || d_model < 1) return 1;
+  if (rotate && (E & (E - 1))) return 1;
   for (int b = 0; b < B; ++b) {
     const int64_t p0 = pos0[b];
     const int64_t base = p0 - ns; /* position of token-table row 0 */
@@ -219,6 +237,7 @@ int orc_compress(int B, int L, int d_model, int E, int m, int overlap,
           }
           out[((size_t)b * Nc_cap + i) * E + e] = num / den;
         }
+        if (rotate) hadamard_rows(out + ((size_t)b * Nc_cap + i) * E, E);
         if (written) written[(size_t)b * Nc_cap + i] = 1;
       }
     }

@@ -45,7 +45,7 @@ def lib():
             build()
         L = C.CDLL(LIB)
         vp, i32, i64p, dp = C.c_void_p, C.c_int, C.c_void_p, C.c_void_p
-        L.orc_compress.argtypes = [i32] * 6 + [i64p, vp, vp, vp, i32, dp, dp, dp, i32, dp, vp]
+        L.orc_compress.argtypes = [i32] * 7 + [i64p, vp, vp, vp, i32, dp, dp, dp, i32, dp, vp]
         L.orc_indexer_topk.argtypes = [i32] * 7 + [i64p, vp, vp, vp, vp, vp, vp, i32, vp, dp, dp, dp]
         L.orc_sparse_attn.argtypes = [i32] * 6 + [C.c_double, dp, i64p, vp, vp, i32, vp, vp, i32, i64p, i32, dp, dp]
         L.orc_hca_dense_attn.argtypes = [i32] * 6 + [C.c_double, dp, i64p, vp, vp, vp, i32, vp, i32, i64p, i32, dp, dp]
@@ -119,11 +119,12 @@ def quant_rows_e4m3(x):
 
 
 def compress(x, w_kv, w_gate, m, overlap, pos0, Nc_cap, ape=None, state_in=None,
-             want_state=True):
+             want_state=True, rotate=False):
     """Gated overlapping compressor.
 
     x [B, L, d_model], w_kv / w_gate [E, d_model] (same stored format);
-    ape [(1+o) m, E] float; state_in [B, (1+o) m - 1, 2, E] float or None.
+    ape [(1+o) m, E] float; state_in [B, (1+o) m - 1, 2, E] float or None;
+    rotate: each entry times the Sylvester Hadamard matrix / sqrt(E).
     Returns (out [B, Nc_cap, E] float64 with NaN in unwritten rows,
     written [B, Nc_cap] bool, state_out or None).
     """
@@ -139,7 +140,8 @@ def compress(x, w_kv, w_gate, m, overlap, pos0, Nc_cap, ape=None, state_in=None,
     state_out = np.zeros((B, ns, 2, E), np.float64) if want_state else None
     out = np.full((B, Nc_cap, E), np.nan, np.float64)
     written = np.zeros((B, Nc_cap), np.uint8)
-    rc = lib().orc_compress(B, L, d_model, E, m, overlap, _p(pos0), _p(x), _p(w_kv),
+    rc = lib().orc_compress(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(pos0), _p(x),
+                            _p(w_kv),
                             _p(w_gate), dt, _p(ape), _p(state_in), _p(state_out),
                             Nc_cap, _p(out), _p(written))
     assert rc == 0

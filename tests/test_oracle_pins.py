@@ -159,6 +159,37 @@ def test_compress_streaming_and_chunked_equal_one_shot(m, o):
         np.testing.assert_allclose(st, st_ref, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("E", [1, 2, 8, 64])
+def test_compress_rotation_is_the_library_hadamard(E):
+    # the rotated entries equal scipy's Hadamard matrix (Sylvester order)
+    # times the unrotated entries, divided by sqrt(E); inner products between
+    # entries are unchanged (the rotation is orthogonal)
+    import scipy.linalg
+    r = rng(40 + E)
+    B, S, dm, m, o = 2, 23, 16, 4, 1
+    x = r.normal(0, 1, (B, S, dm)).astype(np.float32)
+    w_kv = r.normal(0, 0.3, (E, dm)).astype(np.float32)
+    w_g = r.normal(0, 0.3, (E, dm)).astype(np.float32)
+    ape = r.normal(0, 1, (2 * m, E))
+    Nc = S // m
+    plain, wr, _ = orc.compress(x, w_kv, w_g, m, o, 0, Nc, ape=ape, want_state=False)
+    rot, wr2, _ = orc.compress(x, w_kv, w_g, m, o, 0, Nc, ape=ape, want_state=False, rotate=True)
+    assert (wr == wr2).all() and wr.all()
+    Hm = scipy.linalg.hadamard(E).astype(np.float64) / math.sqrt(E)
+    np.testing.assert_allclose(rot, plain @ Hm.T, rtol=1e-12, atol=1e-12)
+    for b in range(B):
+        np.testing.assert_allclose(rot[b] @ rot[b].T, plain[b] @ plain[b].T, rtol=1e-10,
+                                   atol=1e-10)
+
+
+def test_compress_rotation_needs_power_of_two_width():
+    r = rng(45)
+    x = r.normal(0, 1, (1, 8, 8)).astype(np.float32)
+    w = r.normal(0, 1, (6, 8)).astype(np.float32)
+    with pytest.raises(AssertionError):
+        orc.compress(x, w, w, 4, 1, 0, 2, want_state=False, rotate=True)
+
+
 def test_compress_never_reads_future_tokens():
     r = rng(6)
     m, o, S, dm, E = 4, 1, 40, 5, 3
