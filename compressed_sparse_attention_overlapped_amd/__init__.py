@@ -42,7 +42,7 @@ def lib():
             raise RuntimeError("libcsa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
         L = C.CDLL(LIB_PATH)
         vp, i32, f32, sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
-        L.csa_compress.argtypes = [i32] * 6 + [vp] * 4 + [i32, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+        L.csa_compress.argtypes = [i32] * 7 + [vp] * 4 + [i32, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
         L.csa_compress_workspace_size.argtypes = [i32] * 7
         L.csa_indexer_topk.argtypes = [i32] * 7 + [vp] * 7 + [i32, vp, vp, vp, sz, vp]
         L.csa_indexer_topk_workspace_size.argtypes = [i32] * 7
@@ -113,18 +113,20 @@ def hca_dense_attn_workspace_size(B, T, H, D, Nc_cap, window) -> int:
 # ---------------------------------------------------------------- calls
 
 def csa_compress(x, w_kv, w_gate, pos0, m, overlap, out, out_scale=None, ape=None,
-                 state_in=None, state_out=None, workspace=None):
+                 state_in=None, state_out=None, workspace=None, rotate=False):
     """Gated overlapping compressor; see ``csa_compress`` in include/csa.h.
 
     x [B, L, d_model]; w_kv, w_gate [E, d_model]; pos0 int64 [B];
     out [B, Nc_cap, E] (f32, bf16 or float8_e4m3fn, then out_scale [B, Nc_cap]);
-    ape f32 [(1+o) m, E]; state_in / state_out f32 [B, (1+o) m - 1, 2, E]."""
+    ape f32 [(1+o) m, E]; state_in / state_out f32 [B, (1+o) m - 1, 2, E];
+    rotate: entries times the Hadamard matrix / sqrt(E) before storage."""
     _dense(x, w_kv, w_gate, pos0, out, out_scale, ape, state_in, state_out)
     B, L, d_model = x.shape
     E = w_kv.shape[0]
     ws, nb = _workspace(csa_compress_workspace_size(B, L, d_model, E, m, overlap, x.dtype), x,
                         workspace)
-    rc = lib().csa_compress(B, L, d_model, E, m, overlap, _p(pos0), _p(x), _p(w_kv), _p(w_gate),
+    rc = lib().csa_compress(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(pos0), _p(x),
+                            _p(w_kv), _p(w_gate),
                             _DT[x.dtype], _p(ape), _p(state_in), _p(state_out), _p(out),
                             _p(out_scale), _DT[out.dtype], out.shape[1], _p(ws), nb, _stream(x))
     _check("csa_compress", rc)

@@ -54,7 +54,7 @@ size_t csa_compress_workspace_size(int B, int L, int d_model, int E, int m, int 
   return csa_host::compress_ws_bytes(B, L, d_model, E, m, overlap, in_dt);
 }
 
-csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap,
+csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                           const int64_t* pos0, const void* x, const void* w_kv,
                           const void* w_gate, csa_dtype_t in_dt, const float* ape,
                           const float* state_in, float* state_out, void* out, float* out_scale,
@@ -64,6 +64,9 @@ csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap,
     return fail(CSA_E_ARG, "csa_compress: B, L, d_model, E must be > 0 and Nc_cap >= 0");
   if (m < 1) return fail(CSA_E_ARG, "csa_compress: m must be >= 1 (got %d)", m);
   if (overlap != 0 && overlap != 1) return fail(CSA_E_ARG, "csa_compress: overlap must be 0 or 1");
+  if (rotate != 0 && rotate != 1) return fail(CSA_E_ARG, "csa_compress: rotate must be 0 or 1");
+  if (rotate && (E & (E - 1)))
+    return fail(CSA_E_ARG, "csa_compress: rotate needs E a power of two (got %d)", E);
   if (!pos0 || !x || !w_kv || !w_gate || !out)
     return fail(CSA_E_ARG, "csa_compress: pos0, x, w_kv, w_gate and out are required");
   if (state_in && state_in == state_out)
@@ -82,8 +85,8 @@ csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap,
   const size_t need = csa_host::compress_ws_bytes(B, L, d_model, E, m, overlap, in_dt);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "csa_compress: workspace %zu < %zu bytes", ws_bytes, need);
-  csa_host::CompressArgs a{B, L, d_model, E, m, overlap, Nc_cap, pos0, x, w_kv, w_gate, in_dt,
-                           out_dt, ape, state_in, state_out, out, out_scale, workspace};
+  csa_host::CompressArgs a{B, L, d_model, E, m, overlap, rotate, Nc_cap, pos0, x, w_kv, w_gate,
+                           in_dt, out_dt, ape, state_in, state_out, out, out_scale, workspace};
   return hip_status(csa_host::launch_compress(a, stream), "csa_compress launch");
 }
 

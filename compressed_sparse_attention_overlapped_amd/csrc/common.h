@@ -140,7 +140,7 @@ __device__ __forceinline__ float sum_xor16(float v) {
 namespace csa_host {
 
 struct CompressArgs {
-  int B, L, d_model, E, m, overlap, Nc_cap;
+  int B, L, d_model, E, m, overlap, rotate, Nc_cap;
   const int64_t* pos0;
   const void* x;
   const void* w_kv;

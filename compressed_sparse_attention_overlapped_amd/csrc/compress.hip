@@ -13,6 +13,7 @@
 //     bf16 RNE, or e4m3 with a per-row amax/448 scale).  Extra workgroups
 //     write the carried state for the next call.
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 
@@ -221,7 +222,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
     const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, float* __restrict__ out_scale,
-    int Nc_cap, int n_slots, int n_split) {
+    int Nc_cap, int n_slots, int n_split, bool rotate, float rot_scale) {
   const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
   const int ns = (1 + overlap) * m - 1;
   const int64_t p0 = pos0[b];
@@ -427,6 +428,27 @@ __global__ void __launch_bounds__(256) pool_kernel(
     vals[nv] = c;
     amax = fmaxf(amax, fabsf(c));
   }
+  if (rotate) {  // uniform: the entry times H_E / sqrt(E) (Sylvester order)
+    __shared__ float hb[1024];
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) hb[e] = vals[nv];
+    __syncthreads();
+    for (int len = 1; len < E; len <<= 1) {
+      for (int k = tid; k < E / 2; k += blockDim.x) {
+        const int j = (k / len) * 2 * len + (k % len);
+        const float a = hb[j], c = hb[j + len];
+        hb[j] = a + c;
+        hb[j + len] = a - c;
+      }
+      __syncthreads();
+    }
+    amax = 0.0f;
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) {
+      vals[nv] = hb[e] * rot_scale;
+      amax = fmaxf(amax, fabsf(vals[nv]));
+    }
+  }
   const size_t orow = (size_t)b * Nc_cap + (size_t)i;
   if (OUT_DT == CSA_DT_F32) {
     nv = 0;
@@ -504,7 +526,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
 #define CSA_LAUNCH_POOL(DT, W, NS)                                                                \
   pool_kernel<DT, W, NS><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape,  \
                                                 a.state_in, a.state_out, a.out, a.out_scale,     \
-                                                a.Nc_cap, n_slots, splits)
+                                                a.Nc_cap, n_slots, splits, a.rotate != 0,     \
+                                                (float)(1.0 / std::sqrt((double)E)))
 #define CSA_POOL_DT(DT)                            \
   if (w8 == 1) CSA_LAUNCH_POOL(DT, 8, 1);          \
   else if (w8 == 4) CSA_LAUNCH_POOL(DT, 8, 4);     \

@@ -70,6 +70,13 @@ typedef enum {
  *  d_model, E   input width, output width per entry (main compressor:
  *               E = 2 D = [K | V]; indexer compressor: E = d_I)
  *  m, overlap   ratio (>= 1) and overlap flag (0 or 1)
+ *  rotate       0, or 1: each entry is multiplied by H_E / sqrt(E) before the
+ *               storage rounding, H_E the Walsh-Hadamard matrix in Sylvester
+ *               order (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]); E must be
+ *               a power of two (the migration notes name a Hadamard step in the
+ *               compressor and the indexer, section 3.2; the rotation is
+ *               orthogonal, so indexer scores of rotated queries and keys are
+ *               unchanged while e4m3 rounding sees flatter rows)
  *  pos0         int64 [B]: absolute position of x[b, 0]
  *  x            [B, L, d_model] in in_dt
  *  w_kv, w_gate [E, d_model] each, in in_dt (output-major, like a Linear weight)
@@ -92,7 +99,7 @@ typedef enum {
  *               (NULL allowed when that size is 0)
  * Supported: in_dt F32 with any d_model; in_dt BF16 with d_model % 64 == 0.
  */
-csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap,
+csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                           const int64_t* pos0, const void* x, const void* w_kv,
                           const void* w_gate, csa_dtype_t in_dt, const float* ape,
                           const float* state_in, float* state_out, void* out,

@@ -56,19 +56,23 @@ def test_argument_errors_are_reported_without_launch(L):
     vp = C.c_void_p
     dummy = vp(16)   # never dereferenced: validation fails first
     # B = 0
-    rc = L.csa_compress(0, 1, 64, 8, 4, 1, dummy, dummy, dummy, dummy, 0, None, None, None,
+    rc = L.csa_compress(0, 1, 64, 8, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, None, None,
                         dummy, None, 0, 10, None, 0, None)
     assert rc == 1 and b"must be > 0" in L.csa_last_error()
     # overlap 2
-    rc = L.csa_compress(1, 1, 64, 8, 4, 2, dummy, dummy, dummy, dummy, 0, None, None, None,
+    rc = L.csa_compress(1, 1, 64, 8, 4, 2, 0, dummy, dummy, dummy, dummy, 0, None, None, None,
                         dummy, None, 0, 10, None, 0, None)
     assert rc == 1
+    # rotation of a width that is not a power of two
+    rc = L.csa_compress(1, 1, 64, 6, 4, 1, 1, dummy, dummy, dummy, dummy, 0, None, None, None,
+                        dummy, None, 0, 10, None, 0, None)
+    assert rc == 1 and b"power of two" in L.csa_last_error()
     # fp8 output without scales
-    rc = L.csa_compress(1, 1, 64, 8, 4, 1, dummy, dummy, dummy, dummy, 0, None, None, None,
+    rc = L.csa_compress(1, 1, 64, 8, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, None, None,
                         dummy, None, 2, 10, None, 0, None)
     assert rc == 1 and b"out_scale" in L.csa_last_error()
     # state aliasing
-    rc = L.csa_compress(1, 1, 64, 8, 4, 1, dummy, dummy, dummy, dummy, 0, None, dummy, dummy,
+    rc = L.csa_compress(1, 1, 64, 8, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, dummy, dummy,
                         dummy, None, 0, 10, None, 0, None)
     assert rc == 1 and b"alias" in L.csa_last_error()
     # unsupported indexer geometry

@@ -12,7 +12,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(x, w_kv, w_gate, pos0, m, o, Nc_cap, out_dtype, ape=None, state_in=None, want_state=True):
+def _run(x, w_kv, w_gate, pos0, m, o, Nc_cap, out_dtype, ape=None, state_in=None, want_state=True,
+         rotate=False):
     B = x.shape[0]
     E = w_kv.shape[0]
     out = torch.full((B, Nc_cap, E), float("nan"), device=DEV).to(out_dtype)
@@ -20,16 +21,17 @@ def _run(x, w_kv, w_gate, pos0, m, o, Nc_cap, out_dtype, ape=None, state_in=None
     ns = (1 + o) * m - 1
     state_out = torch.full((B, ns, 2, E), 7.0, device=DEV) if want_state else None
     csa.csa_compress(x, w_kv, w_gate, dev_i64(pos0), m, o, out, out_scale=out_scale,
-                     ape=ape, state_in=state_in, state_out=state_out)
+                     ape=ape, state_in=state_in, state_out=state_out, rotate=rotate)
     torch.cuda.synchronize()
     return out, out_scale, state_out
 
 
-def _oracle(x, w_kv, w_gate, pos0, m, o, Nc_cap, ape=None, state_in=None):
+def _oracle(x, w_kv, w_gate, pos0, m, o, Nc_cap, ape=None, state_in=None, rotate=False):
     return orc.compress(gen.host_bits(x), gen.host_bits(w_kv), gen.host_bits(w_gate), m, o,
                         np.asarray(pos0), Nc_cap,
                         ape=None if ape is None else ape.cpu().numpy(),
-                        state_in=None if state_in is None else state_in.cpu().numpy())
+                        state_in=None if state_in is None else state_in.cpu().numpy(),
+                        rotate=rotate)
 
 
 @pytest.mark.parametrize("E", [128, 32])
@@ -46,8 +48,9 @@ def test_compress_tiny_f32(E):
     np.testing.assert_allclose(st.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("out_kind", ["bf16", "fp8", "f32"])
-def test_compress_bf16_ragged_with_ape(out_kind):
+@pytest.mark.parametrize("out_kind,rotate", [("bf16", False), ("fp8", False), ("f32", False),
+                                             ("bf16", True), ("fp8", True), ("f32", True)])
+def test_compress_bf16_ragged_with_ape(out_kind, rotate):
     d = gen.Draw(11)
     B, L, dm, E, m, o = 3, 61, 256, 64, 4, 1
     x = gen.store(d.normal(B, L, dm), gen.BF16)
@@ -57,8 +60,8 @@ def test_compress_bf16_ragged_with_ape(out_kind):
     Nc = 64
     odt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "f32": torch.float32}[out_kind]
     out, osc, st = _run(x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), pos0, m, o, Nc, odt,
-                        ape=ape.to(DEV))
-    ref, written, st_ref = _oracle(x, w_kv, w_gate, pos0, m, o, Nc, ape=ape)
+                        ape=ape.to(DEV), rotate=rotate)
+    ref, written, st_ref = _oracle(x, w_kv, w_gate, pos0, m, o, Nc, ape=ape, rotate=rotate)
     if out_kind == "fp8":
         codes, scales = orc.quant_rows_e4m3(np.nan_to_num(ref))
         g_codes = gen.host_bits(out)
@@ -143,8 +146,9 @@ def test_compress_decode_step_splits_k():
     assert_bf16_close(out[:, Nc - 1].float().cpu().numpy(), ref2[:, Nc - 1], "decode entry")
 
 
-@pytest.mark.parametrize("E,out_kind", [(256, "bf16"), (64, "fp8")])
-def test_compress_decode_step_main_and_indexer_widths(E, out_kind):
+@pytest.mark.parametrize("E,out_kind,rotate", [(256, "bf16", False), (64, "fp8", False),
+                                               (64, "fp8", True)])
+def test_compress_decode_step_main_and_indexer_widths(E, out_kind, rotate):
     # the decode step of both compressors of the streaming decode workload
     # (main: 2D channels to bf16; indexer: d_I channels to e4m3 with a row
     # scale): few-row projection over all of K, pool from the carried state
@@ -159,7 +163,7 @@ def test_compress_decode_step_main_and_indexer_widths(E, out_kind):
     pos_tail = [T - 8] * B
     _, _, st1 = _oracle(x_tail, w_kv, w_gate, pos_tail, m, o, Nc)
     ref2, wr2, st2 = _oracle(x_new, w_kv, w_gate, [T - 1] * B, m, o, Nc,
-                             state_in=torch.from_numpy(st1))
+                             state_in=torch.from_numpy(st1), rotate=rotate)
     assert wr2[:, Nc - 1].all()
     wk, wg = w_kv.to(DEV), w_gate.to(DEV)
     ns = 2 * m - 1
@@ -169,8 +173,9 @@ def test_compress_decode_step_main_and_indexer_widths(E, out_kind):
     tmp = torch.zeros(B, Nc, E, device=DEV, dtype=odt)
     tsc = torch.zeros(B, Nc, device=DEV) if out_kind == "fp8" else None
     csa.csa_compress(x_tail.to(DEV), wk, wg, dev_i64(pos_tail), m, o, tmp, out_scale=tsc,
-                     state_out=s0)
-    out, osc, s1 = _run(x_new.to(DEV), wk, wg, [T - 1] * B, m, o, Nc, odt, state_in=s0)
+                     state_out=s0, rotate=rotate)
+    out, osc, s1 = _run(x_new.to(DEV), wk, wg, [T - 1] * B, m, o, Nc, odt, state_in=s0,
+                        rotate=rotate)
     np.testing.assert_allclose(s1.cpu().numpy()[:, :, 0], st2[:, :, 0], rtol=2e-5, atol=2e-5)
     np.testing.assert_allclose(s1.cpu().numpy()[:, :, 1], st2[:, :, 1], rtol=2e-5, atol=2e-5)
     if out_kind == "bf16":
