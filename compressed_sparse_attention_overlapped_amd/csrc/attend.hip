@@ -759,12 +759,14 @@ static bool use_decode_kernel(int rows, int H) {
   return rows < AT_DECODE_ROWS && (H == 32 || H == 64);
 }
 
-// Splits of the decode kernel: about two workgroups per CU of the 256, each
-// with >= 128 keys, and for index lists enough that no split holds more than
-// DC_IDX_MAX index slots (its staging buffer).  0: unsupported.
+// Splits of the decode kernel: about one workgroup per CU of the 256 (more,
+// shorter work items measured slower: each carries fixed index, query and
+// partial-output costs, and the combine reads more partials), each with >= 128
+// keys, and for index lists enough that no split holds more than DC_IDX_MAX
+// index slots (its staging buffer).  0: unsupported.
 static int attn_splits(int rows, int keys_per_row, bool sparse, int H) {
   if (use_decode_kernel(rows, H)) {
-    int s = (512 + rows - 1) / rows;
+    int s = (256 + rows - 1) / rows;
     int smax = (keys_per_row + DC_MIN_SPLIT_KEYS - 1) / DC_MIN_SPLIT_KEYS;
     if (smax > CB_MAX_SPLIT) smax = CB_MAX_SPLIT;
     s = s < smax ? s : smax;
