@@ -17,11 +17,13 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "attend.hip"]
-# Per-source extra flags.  attend.hip keeps its MFMA accumulators in VGPRs: the
-# attention loops rescale the output accumulator conditionally, and with the
-# accumulators in AGPRs the compiler round-trips all of them through VGPRs
-# on every key tile.
-EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags.  attend.hip and indexer.hip keep their MFMA
+# accumulators in VGPRs: the attention loops rescale the output accumulator
+# conditionally and the score epilogues read every accumulator element, and
+# with the accumulators in AGPRs the compiler copies them to VGPRs on every
+# key tile.
+EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -120,6 +120,13 @@ __global__ void __launch_bounds__(256) score_f32_kernel(
   }
 }
 
+// max(x, 0) on the bit pattern: a float with its sign bit set is a negative
+// integer, so the signed integer maximum with 0 is the ReLU of every finite
+// value in one instruction (fmaxf also quiets NaN inputs first)
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ---------------------------------------------------------------- scores: bf16
 // H_I = 16, d_I = 64.  A workgroup (4 waves) owns 16 consecutive query rows of
 // one sequence (4 per wave: two 32-row MFMA tiles of 2 rows x 16 heads) and a
@@ -134,7 +141,8 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     float* __restrict__ scores, uint32_t* __restrict__ ghist) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][SB_KT * SB_KSTRIDE];
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
-  const int b = blockIdx.z, t0 = blockIdx.x * SB_ROWS;
+  // later rows see more entries: they are dispatched first
+  const int b = blockIdx.z, t0 = (gridDim.x - 1 - blockIdx.x) * SB_ROWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t p0 = q_pos[b];
   const int ncb = n_cmp[b];
@@ -221,8 +229,8 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
           acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][s], bk[s], acc[mt], 0, 0, 0);
       for (int mt = 0; mt < 2; ++mt) {
         float s0 = 0.0f, s1 = 0.0f;
-        for (int r = 0; r < 8; ++r) s0 = fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.0f), s0);
-        for (int r = 8; r < 16; ++r) s1 = fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.0f), s1);
+        for (int r = 0; r < 8; ++r) s0 = fmaf(wv[mt][r], relu_bits(acc[mt][r]), s0);
+        for (int r = 8; r < 16; ++r) s1 = fmaf(wv[mt][r], relu_bits(acc[mt][r]), s1);
         s0 = sum_xor32(s0);
         s1 = sum_xor32(s1);
         const int u = lane >> 5;  // lanes < 32 write token 0 of the pair, others token 1
@@ -343,7 +351,7 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
         // acc[i]: head 4 (lane / 16) + i, entry lane % 16 of group u
         float p = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p = fmaf(wq[i], fmaxf(acc[i], 0.0f), p);
+        for (int i = 0; i < 4; ++i) p = fmaf(wq[i], relu_bits(acc[i]), p);
         part[u] = p;
       }
       float sc[SF_UNROLL / 4];
@@ -926,8 +934,10 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
                                                  (const float*)a.k_idx, a.q_pos, a.n_cmp, a.T,
                                                  a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist);
   } else if (a.dt == CSA_DT_BF16) {
-    // long rows need one histogram per row: one row per workgroup then
-    const int key_chunk = L.long_rows ? kChunk : a.Nc_cap;
+    // long rows need one histogram per row: one row per workgroup then;
+    // short rows split their entries in chunks of 512 so that the causal
+    // growth of the visible range spreads over more, smaller workgroups
+    const int key_chunk = L.long_rows ? kChunk : std::min(a.Nc_cap, 512);
     dim3 g((a.T + SB_ROWS - 1) / SB_ROWS, (a.Nc_cap + key_chunk - 1) / key_chunk, a.B);
     if (L.long_rows) {
       // rows of a workgroup must share a histogram: only T == 1 qualifies
