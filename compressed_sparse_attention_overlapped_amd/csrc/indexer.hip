@@ -22,6 +22,8 @@
 //    ascending order from it.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace csa {
@@ -408,7 +410,7 @@ __global__ void __launch_bounds__(256) select_short_kernel(
   constexpr bool REG = KMAX <= 2048;
   constexpr int KPL = KMAX / 64;  // keys per lane
   __shared__ uint32_t keys_all[REG ? 1 : 4][REG ? 1 : KMAX];
-  __shared__ uint32_t hist_all[4][256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][2048];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * 4 + wave;
@@ -480,27 +482,36 @@ __global__ void __launch_bounds__(256) select_short_kernel(
       }
     }
   };
-  // radix select over the bits below the keys' common prefix: lane l owns
-  // bins 255 - 4 l .. 252 - 4 l of each pass; digits of up to 8 bits.  (Every
-  // key equal: the mask covers all bits, and the output pass takes the first
-  // nsel entries.)
+  // radix select over the bits below the keys' common prefix.  The first
+  // digit is up to 11 bits wide (2048 bins, 32 per lane), so that the LDS
+  // atomics of the full pass spread over many bins and few keys share the
+  // threshold bin; later digits are up to 8 bits (256 bins, 4 per lane).
+  // Lane l owns bins NB - 1 - (BPL l + i), i = 0 .. BPL - 1 (top bins first).
+  // (Every key equal: the mask covers all bits, and the output pass takes the
+  // first nsel entries.)
   const uint32_t diff = kmin ^ kmax;
   int hi = diff ? 31 - __clz((int)diff) : -1;  // highest bit where keys differ
   uint32_t mask = hi < 0 ? 0xffffffffu : (hi >= 31 ? 0u : ~((2u << hi) - 1u));
   uint32_t prefix = kmax & mask, remaining = (uint32_t)nsel;
   bool all_eq = false;
-  while (!all_eq && hi >= 0) {
-    const int width = min(8, hi + 1), shift = hi - width + 1;
+  auto radix_pass = [&](auto bpl_tag) {
+    constexpr int BPL = decltype(bpl_tag)::value, NB = 64 * BPL;
+    constexpr int WMAX = BPL == 32 ? 11 : 8;
+    const int width = min(WMAX, hi + 1), shift = hi - width + 1;
     const uint32_t dmask = (1u << width) - 1u;
+    const int base = NB - BPL * (lane + 1);  // lowest bin of this lane
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0u;
+    for (int i = 0; i < BPL; i += 4) *(u32x4*)&hist[base + i] = u32x4{0u, 0u, 0u, 0u};
     count(mask, prefix, shift, dmask);
-    uint32_t c[4], sum = 0u;
+    uint32_t c[BPL], sum = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[i] = hist[255 - (4 * lane + i)];
-      sum += c[i];
+    for (int i = 0; i < BPL; i += 4) {
+      const u32x4 v = *(const u32x4*)&hist[base + i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[BPL - 1 - (i + e)] = v[e];
     }
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) sum += c[i];
     uint32_t incl = sum;  // inclusive prefix over lanes (lane 0 = top bins)
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_up(incl, o, 64);
@@ -511,9 +522,9 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     uint32_t cum_sel = 0u, cnt_sel = 0u;
     if (above < remaining && above + sum >= remaining) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < BPL; ++i) {
         if (dsel < 0 && above + c[i] >= remaining) {
-          dsel = 255 - (4 * lane + i);
+          dsel = NB - 1 - (BPL * lane + i);
           cum_sel = above;
           cnt_sel = c[i];
         }
@@ -529,7 +540,9 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     mask |= dmask << shift;
     hi = shift - 1;
     if (cnt == remaining) all_eq = true;
-  }
+  };
+  if (hi >= 0) radix_pass(std::integral_constant<int, 32>{});
+  while (!all_eq && hi >= 0) radix_pass(std::integral_constant<int, 4>{});
   // ordered output: groups of 64 consecutive entries
   uint32_t out_base = 0u, eq_taken = 0u;
   auto emit = [&](int g, uint32_t key) {
