@@ -168,18 +168,20 @@ def test_sparse_attn_prefill_8k_sampled():
         _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl, torch.bfloat16, "8k token %d" % t)
 
 
-@pytest.mark.parametrize("H", [64, 32])
-def test_sparse_attn_prefill_long_index_rows(H):
+@pytest.mark.parametrize("H,p0", [(64, 9000), (32, 9000), (64, 0)])
+def test_sparse_attn_prefill_long_index_rows(H, p0):
     # prefill rows whose index lists exceed one LDS staging chunk of the
     # kernel (2048 slots): the second chunk is ragged and slots are masked
-    # throughout
-    d = gen.Draw(36 + H, DEV)
+    # throughout.  From position 0 the rows see at most 257 entries, so the
+    # second chunk holds no entry for any row and the first none for rows
+    # 0-2 (the kernel then visits no gathered tile of that chunk)
+    d = gen.Draw(36 + H + p0, DEV)
     B, T, D, Nc, topk, W = 1, 1030, 128, 2600, 2100, 64
     q = gen.store(d.normal(B, T, H, D), gen.BF16)
     kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
     kv_raw = gen.store(d.normal(B, 1200, 2 * D), gen.BF16)
-    q_pos, raw_base = [9000], [8900]
-    dc = gen.Draw(36 + H)
+    q_pos, raw_base = [p0], [max(0, p0 - 100)]
+    dc = gen.Draw(36 + H + p0)
     idx = _rand_idx(dc, B, T, topk, lambda b, t: _n_vis(q_pos[b] + t, Nc, 4, Nc), 0.0)
     drop = torch.rand(idx.shape, generator=dc.g) < 0.05
     idx[drop] = -1
