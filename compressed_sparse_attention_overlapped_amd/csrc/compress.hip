@@ -213,7 +213,8 @@ __global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------- pool
 // Grid (n_slots + 1, B).  Slot q < n_slots handles entry i_lo(b) + q; the last
-// slot writes state_out.  Each thread owns channels e = tid, tid + 256, ...
+// slot writes state_out.  Each thread owns channels e = tid, tid + blockDim.x,
+// ... (64, 128 or 256 threads by E, at most four channels each)
 // WIN > 0: the window is WIN tokens and, with at most NSP projection
 // partials, every entry takes a path whose loads are all issued before the
 // softmax; WIN = 0: the general path only.
@@ -460,7 +461,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
   } else {
     red[tid] = amax;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
+    for (int o = (int)blockDim.x / 2; o > 0; o >>= 1) {
       if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
       __syncthreads();
     }
@@ -523,11 +524,13 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   // the common gated window (m = 4 with overlap: 8 tokens) has a batched path
   // (for up to four projection partials)
   const int w8 = (1 + a.overlap) * a.m == 8 ? (splits == 1 ? 1 : (splits <= 4 ? 4 : 0)) : 0;
-#define CSA_LAUNCH_POOL(DT, W, NS)                                                                \
-  pool_kernel<DT, W, NS><<<pgrid, 256, 0, st>>>(pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape,  \
-                                                a.state_in, a.state_out, a.out, a.out_scale,     \
-                                                a.Nc_cap, n_slots, splits, a.rotate != 0,     \
-                                                (float)(1.0 / std::sqrt((double)E)))
+  // a thread per channel (at most four per thread): narrow entries take
+  // narrower workgroups
+  const int pthreads = E <= 64 ? 64 : (E <= 128 ? 128 : 256);
+#define CSA_LAUNCH_POOL(DT, W, NS)                                                              \
+  pool_kernel<DT, W, NS><<<pgrid, pthreads, 0, st>>>(                                           \
+      pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,           \
+      a.out_scale, a.Nc_cap, n_slots, splits, a.rotate != 0, (float)(1.0 / std::sqrt((double)E)))
 #define CSA_POOL_DT(DT)                            \
   if (w8 == 1) CSA_LAUNCH_POOL(DT, 8, 1);          \
   else if (w8 == 4) CSA_LAUNCH_POOL(DT, 8, 4);     \
