@@ -462,12 +462,19 @@ __global__ void __launch_bounds__(256) select_short_kernel(
   }
   // the histogram of one digit over the keys still matching the prefix; the
   // atomics of a batch are issued back to back
-  auto count = [&](uint32_t mask, uint32_t prefix, int shift, uint32_t dmask) {
+  // bin b lives at word b, or with swz at b ^ (((b >> 6) & 7) << 2): the
+  // 16-byte groups of each 32-bin lane range are permuted by the range's
+  // index, so that the lanes' 16-byte reads of their ranges hit distinct banks
+  auto count = [&](uint32_t mask, uint32_t prefix, int shift, uint32_t dmask, bool swz) {
+    auto bin_at = [&](uint32_t x) {
+      const uint32_t bn = (x >> shift) & dmask;
+      return swz ? bn ^ (((bn >> 6) & 7u) << 2) : bn;
+    };
     if constexpr (REG) {
 #pragma unroll
       for (int u = 0; u < KPL; ++u) {
         const int j = 64 * u + lane;
-        if (j < nv && (kr[u] & mask) == prefix) atomicAdd(&hist[(kr[u] >> shift) & dmask], 1u);
+        if (j < nv && (kr[u] & mask) == prefix) atomicAdd(&hist[bin_at(kr[u])], 1u);
       }
     } else {
       for (int g0 = 0; g0 < ng; g0 += 8) {
@@ -477,7 +484,7 @@ __global__ void __launch_bounds__(256) select_short_kernel(
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int j = 64 * (g0 + u) + lane;
-          if (j < nv && (x[u] & mask) == prefix) atomicAdd(&hist[(x[u] >> shift) & dmask], 1u);
+          if (j < nv && (x[u] & mask) == prefix) atomicAdd(&hist[bin_at(x[u])], 1u);
         }
       }
     }
@@ -500,13 +507,15 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     const int width = min(WMAX, hi + 1), shift = hi - width + 1;
     const uint32_t dmask = (1u << width) - 1u;
     const int base = NB - BPL * (lane + 1);  // lowest bin of this lane
+    constexpr bool SWZ = BPL == 32;          // 2048 bins: swizzled groups
 #pragma unroll
-    for (int i = 0; i < BPL; i += 4) *(u32x4*)&hist[base + i] = u32x4{0u, 0u, 0u, 0u};
-    count(mask, prefix, shift, dmask);
+    for (int i = 0; i < BPL; i += 4) *(u32x4*)&hist[4 * lane + 64 * i] = u32x4{0u, 0u, 0u, 0u};
+    count(mask, prefix, shift, dmask, SWZ);
     uint32_t c[BPL], sum = 0u;
 #pragma unroll
     for (int i = 0; i < BPL; i += 4) {
-      const u32x4 v = *(const u32x4*)&hist[base + i];
+      const int at = SWZ ? base + (i ^ ((((base >> 6) & 7) << 2))) : base + i;
+      const u32x4 v = *(const u32x4*)&hist[at];
 #pragma unroll
       for (int e = 0; e < 4; ++e) c[BPL - 1 - (i + e)] = v[e];
     }
