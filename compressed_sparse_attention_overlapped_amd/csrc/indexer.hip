@@ -573,7 +573,29 @@ __global__ void __launch_bounds__(256) select_short_kernel(
     out_base += (uint32_t)__popcll(sm);
     eq_taken += (uint32_t)__popcll(eqm);
   };
-  if constexpr (REG) {
+  // when the threshold bin holds exactly the keys still needed (all_eq),
+  // every key at or above the threshold is taken: no ranking of equal keys
+  auto emit_all = [&](int g, uint32_t key) {
+    const int j = 64 * g + lane;
+    const bool sel = j < nv && (key & mask) >= prefix;
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const uint32_t pos = out_base + __builtin_amdgcn_mbcnt_hi(
+                                          (uint32_t)(sm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+      orow[pos] = j;
+      if (sorow) sorow[pos] = srow[j];
+    }
+    out_base += (uint32_t)__popcll(sm);
+  };
+  if (all_eq) {
+    if constexpr (REG) {
+#pragma unroll
+      for (int u = 0; u < KPL; ++u)
+        if (u < ng) emit_all(u, kr[u]);
+    } else {
+      for (int g = 0; g < ng; ++g) emit_all(g, keys[64 * g + lane]);
+    }
+  } else if constexpr (REG) {
 #pragma unroll
     for (int u = 0; u < KPL; ++u)
       if (u < ng) emit(u, kr[u]);
