@@ -38,7 +38,12 @@
  *  - orc_indexer_topk: the score formula (sum over heads of w * ReLU(q.k)) is
  *    the published Lightning Indexer form; the pages print only its one-head
  *    special case, so the multi-head form is "parity unpinned"; the top-k
- *    order is pinned against a library sort.
+ *    order is pinned against a library sort.  The optional MXFP4
+ *    inputs (the DS-V4 analysis, section 3.2, says the indexer computes in
+ *    FP4 and nothing more; read as OCP MXFP4: E2M1 values with an E8M0 scale
+ *    per 32) are pinned to the standard's E2M1 table, to nearest-value
+ *    rounding by brute force, to a library E8M0 decode, and to the fp32
+ *    path on the decoded values.
  *  - orc_sparse_attn / orc_hca_dense_attn: pinned to a library scaled
  *    dot-product attention with an explicit mask.  The optional per-head
  *    attention sink (the migration page lists `attn_sink` among the state of
@@ -54,7 +59,7 @@
 #include <omp.h>
 #endif
 
-enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_E4M3 = 2 };
+enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_E4M3 = 2, ODT_MXFP4 = 3 };
 
 /* ---- number formats ---------------------------------------------------- */
 
@@ -118,6 +123,76 @@ uint16_t orc_bf16_encode(double v) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+/* OCP MX FP4 element (E2M1): 1 sign, 2 exponent (bias 1), 1 mantissa bit, no
+ * infinities or NaN.  Exponent field e > 0: (1 + m / 2) 2^(e - 1); e = 0: the
+ * subnormal m / 2.  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double orc_e2m1_decode(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, mant = c & 1;
+  double v = e == 0 ? 0.5 * mant : ldexp(1.0 + 0.5 * mant, e - 1);
+  return s ? -v : v;
+}
+
+/* Encode a double as E2M1 with round-to-nearest-even; magnitudes beyond 6
+ * saturate to +-6.  The 4-bit code is returned in the low nibble. */
+uint8_t orc_e2m1_encode(double v) {
+  uint8_t sign = signbit(v) ? 8 : 0;
+  double a = fabs(v), q, r;
+  int ex, e;
+  if (isnan(v) || a == 0) return sign;
+  frexp(a, &ex);
+  e = ex - 1;           /* a lies in [2^e, 2^(e+1)) */
+  if (e < 0) e = 0;     /* below 1 the subnormal spacing 0.5 continues */
+  q = ldexp(1.0, e - 1); /* spacing of the 1-bit mantissa in this binade */
+  r = rne(a / q) * q;
+  if (r > 6.0) r = 6.0;
+  if (r == 0) return sign;
+  if (r == 0.5) return sign | 1;
+  frexp(r, &ex);
+  e = ex - 1;
+  return sign | (uint8_t)(((e + 1) << 1) | (int)((r / ldexp(1.0, e) - 1.0) * 2.0));
+}
+
+/* MX block scale (OCP Microscaling formats v1.0, the conversion section):
+ * shared exponent X = floor(log2(amax)) - 2 (2 = the largest E2M1 exponent),
+ * clamped to the E8M0 range [-127, 127]; X = 0 for an all-zero block.  The
+ * E8M0 code is X + 127 and the scale 2^X. */
+static int mx_exponent(double amax) {
+  int ex, x;
+  if (!(amax > 0)) return 0;
+  frexp(amax, &ex);
+  x = (ex - 1) - 2;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+/* MXFP4 quantisation of rows of `cols` values (cols a multiple of 32): per
+ * 32-value block the shared exponent above, then code = E2M1(v / 2^X).  Codes
+ * pack two per byte, element 2i in the low nibble; scales are E8M0 codes,
+ * cols / 32 per row. */
+void orc_quant_rows_mxfp4(int rows, int cols, const double* in, uint8_t* codes,
+                          uint8_t* scales) {
+  for (int r = 0; r < rows; ++r)
+    for (int blk = 0; blk < cols / 32; ++blk) {
+      const double* v = in + (size_t)r * cols + 32 * blk;
+      double amax = 0;
+      int x;
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[i]));
+      x = mx_exponent(amax);
+      scales[(size_t)r * (cols / 32) + blk] = (uint8_t)(x + 127);
+      for (int i = 0; i < 32; i += 2) {
+        uint8_t lo = orc_e2m1_encode(ldexp(v[i], -x));
+        uint8_t hi = orc_e2m1_encode(ldexp(v[i + 1], -x));
+        codes[(size_t)r * (cols / 2) + 16 * blk + i / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+}
+
+/* Value of element i of an MXFP4 row store (codes as above, scales E8M0). */
+static double ld_mxfp4(const uint8_t* codes, const uint8_t* scales, size_t i) {
+  uint8_t byte = codes[i / 2];
+  uint8_t c = (i & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+  return ldexp(orc_e2m1_decode(c), (int)scales[i / 32] - 127);
 }
 
 static double ld(const void* p, size_t i, int dt) {
@@ -277,7 +352,8 @@ static int64_t n_visible(int64_t t, int64_t n_cmp, int m, int64_t cap) {
 
 /* ---- Lightning Indexer score + top-k --------------------------------------
  * score(t, j) = sum_h w[t,h] * ReLU(sq[t,h] * sk[j] * sum_e q[t,h,e] k[j,e])
- * over the visible entries j < n_vis(t) (sq = sk = 1 unless e4m3).
+ * over the visible entries j < n_vis(t) (sq = sk = 1 unless e4m3; MXFP4
+ * values carry their block scales: q and k are the decoded values).
  * Selection: the first min(topk, n_vis) entries under the order
  * (score descending, index ascending), written in ascending index order and
  * padded with -1.  sel_score receives the selected scores aligned with
@@ -304,10 +380,11 @@ static int by_int_asc(const void* a, const void* b) {
 
 int orc_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
                      const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
-                     const float* q_scale, const float* w_idx, const void* k_idx,
-                     const float* k_scale, int qk_dt, int32_t* idx_out,
+                     const void* q_scale, const float* w_idx, const void* k_idx,
+                     const void* k_scale, int qk_dt, int32_t* idx_out,
                      double* sel_score, double* kth, double* all_scores) {
   if (B < 0 || T < 0 || H_I < 1 || d_I < 1 || m < 1 || topk < 0) return 1;
+  if (qk_dt == ODT_MXFP4 && d_I % 32 != 0) return 1;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
     int b = (int)(bt / T), t = (int)(bt % T);
@@ -317,15 +394,24 @@ int orc_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk
     scored* row = (scored*)malloc(sizeof(scored) * (nv > 0 ? nv : 1));
     int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (nsel > 0 ? nsel : 1));
     for (int64_t j = 0; j < nv; ++j) {
-      double sk = (qk_dt == ODT_E4M3) ? (double)k_scale[(size_t)b * Nc_cap + j] : 1.0;
+      const size_t krow = (size_t)b * Nc_cap + j;
+      double sk = (qk_dt == ODT_E4M3) ? (double)((const float*)k_scale)[krow] : 1.0;
       double s = 0;
       for (int h = 0; h < H_I; ++h) {
         size_t qrow = (((size_t)b * T + t) * H_I + h);
-        double sq = (qk_dt == ODT_E4M3) ? (double)q_scale[qrow] : 1.0;
+        double sq = (qk_dt == ODT_E4M3) ? (double)((const float*)q_scale)[qrow] : 1.0;
         double dot = 0, v;
-        for (int e = 0; e < d_I; ++e)
-          dot += ld(q_idx, qrow * d_I + e, qk_dt) *
-                 ld(k_idx, ((size_t)b * Nc_cap + j) * d_I + e, qk_dt);
+        if (qk_dt == ODT_MXFP4) {
+          /* per-block scales are part of each value */
+          const uint8_t* qc = (const uint8_t*)q_idx + qrow * (d_I / 2);
+          const uint8_t* qs = (const uint8_t*)q_scale + qrow * (d_I / 32);
+          const uint8_t* kc = (const uint8_t*)k_idx + krow * (d_I / 2);
+          const uint8_t* ks = (const uint8_t*)k_scale + krow * (d_I / 32);
+          for (int e = 0; e < d_I; ++e) dot += ld_mxfp4(qc, qs, e) * ld_mxfp4(kc, ks, e);
+        } else {
+          for (int e = 0; e < d_I; ++e)
+            dot += ld(q_idx, qrow * d_I + e, qk_dt) * ld(k_idx, krow * d_I + e, qk_dt);
+        }
         v = sq * sk * dot;
         s += (double)w_idx[qrow] * (v > 0 ? v : 0.0);
       }

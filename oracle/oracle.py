@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
 the CPU-baseline leg of the benchmark.  The GPU product path never imports it.
 
 Arrays are passed in their stored formats: fp32 as ``float32``, bf16 as the
-``uint16`` bit pattern, OCP e4m3 as the ``uint8`` code.  Results come back as
+``uint16`` bit pattern, OCP e4m3 as the ``uint8`` code, MXFP4 as packed E2M1
+codes (two per byte) with E8M0 block scales (``uint8``).  Results come back as
 ``float64`` arrays (values before any storage rounding).
 
 Citations follow the C file: the migration page's section 3.2 (compressor),
@@ -23,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csa_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-DT_F32, DT_BF16, DT_E4M3 = 0, 1, 2
+DT_F32, DT_BF16, DT_E4M3, DT_MXFP4 = 0, 1, 2, 3
 
 
 def build() -> str:
@@ -61,6 +62,12 @@ def lib():
         L.orc_bf16_decode.restype = C.c_double
         L.orc_quant_rows_e4m3.argtypes = [i32, i32, dp, vp, dp]
         L.orc_quant_rows_e4m3.restype = None
+        L.orc_e2m1_encode.argtypes = [C.c_double]
+        L.orc_e2m1_encode.restype = C.c_uint8
+        L.orc_e2m1_decode.argtypes = [C.c_uint8]
+        L.orc_e2m1_decode.restype = C.c_double
+        L.orc_quant_rows_mxfp4.argtypes = [i32, i32, dp, vp, vp]
+        L.orc_quant_rows_mxfp4.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = C.c_int
         _lib = L
@@ -108,6 +115,39 @@ def bf16_decode(h: int) -> float:
     return lib().orc_bf16_decode(int(h))
 
 
+def e2m1_encode(v: float) -> int:
+    return lib().orc_e2m1_encode(float(v))
+
+
+def e2m1_decode(c: int) -> float:
+    return lib().orc_e2m1_decode(int(c))
+
+
+def quant_rows_mxfp4(x):
+    """MXFP4 quantisation of the last axis (a multiple of 32): returns (codes
+    packed two per byte, element 2i in the low nibble; E8M0 scale codes, one
+    per 32 values)."""
+    x = _c(x, np.float64)
+    cols = x.shape[-1]
+    assert cols % 32 == 0
+    rows = x.size // cols
+    codes = np.zeros(x.shape[:-1] + (cols // 2,), np.uint8)
+    scales = np.zeros(x.shape[:-1] + (cols // 32,), np.uint8)
+    lib().orc_quant_rows_mxfp4(rows, cols, _p(x), _p(codes), _p(scales))
+    return codes, scales
+
+
+def mxfp4_decode(codes, scales):
+    """Values of an MXFP4 store (the inverse of quant_rows_mxfp4's packing)."""
+    codes = np.asarray(codes, np.uint8)
+    scales = np.asarray(scales, np.uint8)
+    table = np.array([e2m1_decode(c) for c in range(16)], np.float64)
+    lo, hi = table[codes & 15], table[codes >> 4]
+    v = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (2 * codes.shape[-1],))
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return v * np.repeat(sc, 32, axis=-1)
+
+
 def quant_rows_e4m3(x):
     """Per-row e4m3 quantisation (scale = amax / 448): returns (codes, scales)."""
     x = _c(x, np.float64)
@@ -149,11 +189,14 @@ def compress(x, w_kv, w_gate, m, overlap, pos0, Nc_cap, ape=None, state_in=None,
 
 
 def indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None,
-                 k_scale=None, want_all=False):
+                 k_scale=None, want_all=False, fmt=None):
     """Lightning-indexer scores + per-row top-k.
 
     q_idx [B, T, H_I, d_I], w_idx [B, T, H_I] fp32, k_idx [B, Nc_cap, d_I];
-    e4m3 inputs need q_scale [B, T, H_I] and k_scale [B, Nc_cap].
+    e4m3 inputs need q_scale [B, T, H_I] and k_scale [B, Nc_cap].  With
+    fmt="mxfp4", q_idx [B, T, H_I, d_I / 2] and k_idx [B, Nc_cap, d_I / 2] hold
+    packed E2M1 codes and q_scale [B, T, H_I, d_I / 32], k_scale
+    [B, Nc_cap, d_I / 32] their E8M0 block scales (uint8).
     Returns (idx [B, T, topk] int32 ascending with -1 pads, sel_score, kth,
     all_scores or None).
     """
@@ -161,12 +204,19 @@ def indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None,
     w_idx = _c(w_idx, np.float32)
     B, T, H_I, d_I = q_idx.shape
     Nc_cap = k_idx.shape[1]
-    dt = _dt(q_idx)
-    assert _dt(k_idx) == dt
-    if dt == DT_E4M3:
-        q_scale, k_scale = _c(q_scale, np.float32), _c(k_scale, np.float32)
+    if fmt == "mxfp4":
+        assert q_idx.dtype == np.uint8 and k_idx.dtype == np.uint8
+        dt = DT_MXFP4
+        d_I *= 2
+        q_scale, k_scale = _c(q_scale, np.uint8), _c(k_scale, np.uint8)
+        assert q_scale.shape == (B, T, H_I, d_I // 32) and k_scale.shape == (B, Nc_cap, d_I // 32)
     else:
-        q_scale = k_scale = None
+        dt = _dt(q_idx)
+        assert _dt(k_idx) == dt
+        if dt == DT_E4M3:
+            q_scale, k_scale = _c(q_scale, np.float32), _c(k_scale, np.float32)
+        else:
+            q_scale = k_scale = None
     q_pos = _c(np.broadcast_to(np.asarray(q_pos, np.int64), (B,)), np.int64)
     n_cmp = _c(np.broadcast_to(np.asarray(n_cmp, np.int32), (B,)), np.int32)
     idx = np.zeros((B, T, topk), np.int32)

@@ -317,6 +317,100 @@ def test_indexer_e4m3_scales_fold_into_score():
     np.testing.assert_allclose(a[3], s_ref, rtol=1e-9, atol=1e-9)
 
 
+# The pages say only that the indexer's QK path runs in FP4 (the DS-V4
+# analysis, section 3.2's closing note; the engineering-trick list of the
+# same page).  The reading taken is OCP MXFP4: E2M1 elements with one E8M0
+# power-of-two scale per 32 values.
+
+# the E2M1 magnitudes the OCP Microscaling v1.0 standard lists for codes 0-7
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_is_the_standard_table():
+    vals = [orc.e2m1_decode(c) for c in range(16)]
+    assert vals[:8] == E2M1_TABLE
+    assert vals[8:] == [-v for v in E2M1_TABLE]
+    assert math.copysign(1.0, vals[8]) == -1.0
+
+
+def test_e2m1_encode_is_nearest_with_ties_to_even_and_saturates():
+    # brute force: the nearest table value, a tie going to the code whose
+    # mantissa bit is 0; beyond 6 the largest magnitude
+    grid = np.array(E2M1_TABLE)
+    r = rng(40)
+    vs = np.concatenate([np.linspace(-8, 8, 3201), r.normal(0, 3, 2000),
+                         np.array(E2M1_TABLE) + 0.0, (grid[1:] + grid[:-1]) / 2])
+    for v in vs:
+        a = min(abs(v), 6.0)
+        d = np.abs(grid - a)
+        best = np.flatnonzero(d == d.min())
+        c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        if c != 0 and v < 0:
+            c |= 8
+        got = orc.e2m1_encode(float(v))
+        if c == 0:
+            assert got in (0, 8), v          # +-0
+        else:
+            assert got == c, (v, got, c)
+
+
+def test_e8m0_scales_match_torch():
+    codes = np.arange(0, 255, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    ones = np.full(codes.shape[:0] + (len(codes), 16), 0x22, np.uint8)  # 1.0 in each nibble
+    ours = orc.mxfp4_decode(ones, codes[:, None])[:, 0]
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_mxfp4_block_exponent_and_round_trip():
+    # per block the shared exponent X satisfies 4 * 2^X <= amax < 8 * 2^X
+    # (X = floor(log2 amax) - 2, E2M1's largest exponent being 2); every value
+    # is the E2M1 rounding of v / 2^X; all-zero blocks keep X = 0
+    r = rng(41)
+    x = r.normal(0, 1, (6, 64)) * np.exp(r.normal(0, 4, (6, 1)))
+    x[5, 32:] = 0.0
+    codes, sc = orc.quant_rows_mxfp4(x)
+    X = sc.astype(np.int64) - 127
+    for i in range(6):
+        for blk in range(2):
+            v = x[i, 32 * blk:32 * blk + 32]
+            amax = np.abs(v).max()
+            if amax == 0:
+                assert X[i, blk] == 0
+                continue
+            assert 4.0 * 2.0 ** X[i, blk] <= amax < 8.0 * 2.0 ** X[i, blk]
+            dec = orc.mxfp4_decode(codes[i:i + 1], sc[i:i + 1])[0, 32 * blk:32 * blk + 32]
+            want = [orc.e2m1_decode(orc.e2m1_encode(t * 2.0 ** -X[i, blk])) * 2.0 ** X[i, blk]
+                    for t in v]
+            np.testing.assert_array_equal(dec, want)
+    # packing: element 2i in the low nibble
+    one = np.zeros((1, 32))
+    one[0, 0], one[0, 1] = 4.0, -2.0      # amax 4: X = 0
+    c1, s1 = orc.quant_rows_mxfp4(one)
+    assert s1[0, 0] == 127 and c1[0, 0] == (6 | (12 << 4))
+
+
+def test_indexer_mxfp4_equals_decoded_values():
+    # MXFP4 storage scores the decoded values (block scales inside the dot
+    # products): the same top-k and scores as the fp32 path on those values,
+    # which hold exactly in fp32
+    r = rng(42)
+    B, T, H, d, Nc, m, k = 1, 5, 3, 64, 40, 4, 7
+    qf = r.normal(0, 1, (B, T, H, d)) * np.exp(r.normal(0, 1, (B, T, H, 1)))
+    kf = r.normal(0, 1, (B, Nc, d))
+    qc, qs = orc.quant_rows_mxfp4(qf)
+    kc, ks = orc.quant_rows_mxfp4(kf)
+    w = r.normal(0, 1, (B, T, H)).astype(np.float32)
+    a = orc.indexer_topk(qc, w, kc, m, k, 200, Nc, q_scale=qs, k_scale=ks, want_all=True,
+                         fmt="mxfp4")
+    qd = orc.mxfp4_decode(qc, qs).astype(np.float32)
+    kd = orc.mxfp4_decode(kc, ks).astype(np.float32)
+    assert np.array_equal(qd.astype(np.float64), orc.mxfp4_decode(qc, qs))
+    b = orc.indexer_topk(qd, w, kd, m, k, 200, Nc, want_all=True)
+    assert np.array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[3], b[3])
+
+
 # ---------------------------------------------------------------- attention
 
 def _attn_case(seed, B=2, T=9, H=4, D=16, Nc=12, R=20, topk=5, window=6, dt=np.float32):
