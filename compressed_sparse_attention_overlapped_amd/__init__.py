@@ -19,11 +19,12 @@ import torch
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
-           "CsaError", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8"]
+           "CsaError", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
-DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
-_DT = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float8_e4m3fn: DT_FP8}
+DT_F32, DT_BF16, DT_FP8, DT_MXFP4 = 0, 1, 2, 3
+_DT = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float8_e4m3fn: DT_FP8,
+       torch.float4_e2m1fn_x2: DT_MXFP4}
 
 _lib = None
 
@@ -117,7 +118,9 @@ def csa_compress(x, w_kv, w_gate, pos0, m, overlap, out, out_scale=None, ape=Non
     """Gated overlapping compressor; see ``csa_compress`` in include/csa.h.
 
     x [B, L, d_model]; w_kv, w_gate [E, d_model]; pos0 int64 [B];
-    out [B, Nc_cap, E] (f32, bf16 or float8_e4m3fn, then out_scale [B, Nc_cap]);
+    out [B, Nc_cap, E] (f32, bf16 or float8_e4m3fn, then out_scale f32 [B, Nc_cap]),
+    or float4_e2m1fn_x2 [B, Nc_cap, E / 2] with out_scale E8M0 bytes [B, Nc_cap, E / 32]
+    (float8_e8m0fnu or uint8);
     ape f32 [(1+o) m, E]; state_in / state_out f32 [B, (1+o) m - 1, 2, E];
     rotate: entries times the Hadamard matrix / sqrt(E) before storage."""
     _dense(x, w_kv, w_gate, pos0, out, out_scale, ape, state_in, state_out)

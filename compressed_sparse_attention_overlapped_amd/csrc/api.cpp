@@ -57,7 +57,7 @@ size_t csa_compress_workspace_size(int B, int L, int d_model, int E, int m, int 
 csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                           const int64_t* pos0, const void* x, const void* w_kv,
                           const void* w_gate, csa_dtype_t in_dt, const float* ape,
-                          const float* state_in, float* state_out, void* out, float* out_scale,
+                          const float* state_in, float* state_out, void* out, void* out_scale,
                           csa_dtype_t out_dt, int Nc_cap, void* workspace, size_t ws_bytes,
                           hipStream_t stream) {
   if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0 || Nc_cap < 0)
@@ -73,10 +73,13 @@ csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, 
     return fail(CSA_E_ARG, "csa_compress: state_out must not alias state_in");
   if (in_dt != CSA_DT_F32 && in_dt != CSA_DT_BF16)
     return fail(CSA_E_UNSUPPORTED, "csa_compress: in_dt must be F32 or BF16");
-  if (out_dt != CSA_DT_F32 && out_dt != CSA_DT_BF16 && out_dt != CSA_DT_FP8E4M3)
+  if (out_dt != CSA_DT_F32 && out_dt != CSA_DT_BF16 && out_dt != CSA_DT_FP8E4M3 &&
+      out_dt != CSA_DT_MXFP4)
     return fail(CSA_E_ARG, "csa_compress: bad out_dt %d", (int)out_dt);
-  if (out_dt == CSA_DT_FP8E4M3 && !out_scale)
-    return fail(CSA_E_ARG, "csa_compress: fp8 output needs out_scale");
+  if ((out_dt == CSA_DT_FP8E4M3 || out_dt == CSA_DT_MXFP4) && !out_scale)
+    return fail(CSA_E_ARG, "csa_compress: fp8 and mxfp4 outputs need out_scale");
+  if (out_dt == CSA_DT_MXFP4 && E % 32 != 0)
+    return fail(CSA_E_UNSUPPORTED, "csa_compress: mxfp4 output needs E %% 32 == 0 (got %d)", E);
   if (E > 1024) return fail(CSA_E_UNSUPPORTED, "csa_compress: E > 1024");
   if (in_dt == CSA_DT_BF16 && (d_model % 64 != 0 || !aligned16(x) || !aligned16(w_kv) ||
                                !aligned16(w_gate)))

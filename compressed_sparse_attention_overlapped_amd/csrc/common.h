@@ -150,7 +150,7 @@ struct CompressArgs {
   const float* state_in;
   float* state_out;
   void* out;
-  float* out_scale;
+  void* out_scale;
   void* ws;
 };
 size_t compress_ws_bytes(int B, int L, int d_model, int E, int m, int overlap, csa_dtype_t in_dt);

@@ -211,6 +211,33 @@ __global__ void __launch_bounds__(256) proj_f32_kernel(const float* __restrict__
   pg[id] = s;
 }
 
+// ---------------------------------------------------------------- MXFP4 store
+// OCP MXFP4: a block of 32 values shares the exponent X = floor(log2(amax))
+// - 2 (2: the largest E2M1 exponent), clamped to [-127, 127] and 0 for an
+// all-zero block; stored as the E8M0 byte X + 127.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 255u);
+  return ef == 0 ? -127 : max(ef - 129, -127);  // subnormal amax: below 2^-126
+}
+
+// E2M1 code of y (sign in bit 3): the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+// a tie going to the even mantissa bit, beyond 6 saturating.  The decision
+// points are the midpoints, and a midpoint belongs to its even neighbour.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const uint32_t sgn = (__float_as_uint(y) >> 31) << 3;
+  const float a = fabsf(y);
+  const uint32_t mag = a <= 0.25f ? 0u
+                     : a < 0.75f  ? 1u
+                     : a <= 1.25f ? 2u
+                     : a < 1.75f  ? 3u
+                     : a <= 2.5f  ? 4u
+                     : a < 3.5f   ? 5u
+                     : a <= 5.0f  ? 6u
+                                  : 7u;
+  return sgn | mag;
+}
+
 // ---------------------------------------------------------------- pool
 // Grid (n_slots + 1, B).  Slot q < n_slots handles entry i_lo(b) + q; the last
 // slot writes state_out.  Each thread owns channels e = tid, tid + blockDim.x,
@@ -222,7 +249,7 @@ template <int OUT_DT, int WIN, int NSP>
 __global__ void __launch_bounds__(256) pool_kernel(
     const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
-    float* __restrict__ state_out, void* __restrict__ out, float* __restrict__ out_scale,
+    float* __restrict__ state_out, void* __restrict__ out, void* __restrict__ out_scale,
     int Nc_cap, int n_slots, int n_split, bool rotate, float rot_scale) {
   const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
   const int ns = (1 + overlap) * m - 1;
@@ -458,6 +485,20 @@ __global__ void __launch_bounds__(256) pool_kernel(
     nv = 0;
     for (int e = tid; e < E; e += blockDim.x, ++nv)
       ((uint16_t*)out)[orow * E + e] = f32_to_bf16(vals[nv]);
+  } else if (OUT_DT == CSA_DT_MXFP4) {
+    // per 32 channels (32 consecutive lanes: E and the block size are
+    // multiples of 32) one E8M0 exponent and E2M1 codes, two per byte
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) {
+      const float v = vals[nv];
+      float am = fabsf(v);
+      for (int o = 16; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+      const int x = mx_block_exponent(am);
+      const uint32_t c = e2m1_code(v * __builtin_ldexpf(1.0f, -x));
+      const uint32_t c_next = (uint32_t)__shfl_xor((int)c, 1, 64);
+      if ((e & 1) == 0) ((uint8_t*)out)[orow * (E / 2) + e / 2] = (uint8_t)(c | (c_next << 4));
+      if ((e & 31) == 0) ((uint8_t*)out_scale)[orow * (E / 32) + e / 32] = (uint8_t)(x + 127);
+    }
   } else {
     red[tid] = amax;
     __syncthreads();
@@ -466,7 +507,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
       __syncthreads();
     }
     float s = red[0] > 0.0f ? red[0] / 448.0f : 1.0f;
-    if (tid == 0) out_scale[orow] = s;
+    if (tid == 0) ((float*)out_scale)[orow] = s;
     nv = 0;
     for (int e = tid; e < E; e += blockDim.x, ++nv)
       ((uint8_t*)out)[orow * E + e] = (uint8_t)(f32x2_to_e4m3x2(vals[nv] / s, 0.0f) & 0xff);
@@ -541,6 +582,9 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
       break;
     case CSA_DT_BF16:
       CSA_POOL_DT(CSA_DT_BF16);
+      break;
+    case CSA_DT_MXFP4:
+      CSA_POOL_DT(CSA_DT_MXFP4);
       break;
     default:
       CSA_POOL_DT(CSA_DT_FP8E4M3);

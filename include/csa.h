@@ -28,6 +28,13 @@
  *    fallback.
  *  - fp8 means OCP FP8 E4M3 ("e4m3fn", largest finite value 448) codes with a
  *    positive fp32 scale per row: value = code * scale.
+ *  - mxfp4 means OCP MXFP4: E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+ *    6; sign in bit 3) packed two per byte, element 2i of a row in the low
+ *    nibble, with one E8M0 scale byte per 32 consecutive values of a row:
+ *    value = e2m1(code) * 2^(scale - 127).  A row of n values takes n / 2
+ *    code bytes and n / 32 scale bytes.  (The DS-V4 analysis, section 3.2,
+ *    says the indexer computes in FP4 and names no format; MXFP4 is the
+ *    reading taken.)
  */
 #ifndef CSA_H_
 #define CSA_H_
@@ -40,7 +47,7 @@
 extern "C" {
 #endif
 
-typedef enum { CSA_DT_F32 = 0, CSA_DT_BF16 = 1, CSA_DT_FP8E4M3 = 2 } csa_dtype_t;
+typedef enum { CSA_DT_F32 = 0, CSA_DT_BF16 = 1, CSA_DT_FP8E4M3 = 2, CSA_DT_MXFP4 = 3 } csa_dtype_t;
 
 typedef enum {
   CSA_OK = 0,
@@ -90,11 +97,16 @@ typedef enum {
  *               means "absent".
  *  state_out    same layout for positions pos0 + L - ns .. pos0 + L - 1, or
  *               NULL.  Must not alias state_in (ping-pong two buffers).
- *  out          [B, Nc_cap, E] in out_dt (F32, BF16 or FP8E4M3); rows of
- *               entries not completed by this call are left untouched
- *  out_scale    fp32 [B, Nc_cap], required iff out_dt is FP8E4M3: the row
- *               scale amax|C_i| / 448 (1 for an all-zero row); the codes are
- *               e4m3(C / scale) rounded to nearest even, saturated at 448
+ *  out          [B, Nc_cap, E] in out_dt (F32, BF16 or FP8E4M3; MXFP4: bytes
+ *               [B, Nc_cap, E / 2]); rows of entries not completed by this
+ *               call are left untouched
+ *  out_scale    FP8E4M3: fp32 [B, Nc_cap], the row scale amax|C_i| / 448 (1
+ *               for an all-zero row), the codes e4m3(C / scale) rounded to
+ *               nearest even and saturated at 448.  MXFP4: E8M0 bytes
+ *               [B, Nc_cap, E / 32]; per block of 32 values X =
+ *               floor(log2 amax) - 2 clamped to [-127, 127] (0 for an
+ *               all-zero block), the codes e2m1(C / 2^X) rounded to nearest
+ *               even and saturated at 6 (E % 32 == 0).  NULL otherwise.
  *  workspace    device scratch of at least csa_compress_workspace_size() bytes
  *               (NULL allowed when that size is 0)
  * Supported: in_dt F32 with any d_model; in_dt BF16 with d_model % 64 == 0.
@@ -103,7 +115,7 @@ csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, 
                           const int64_t* pos0, const void* x, const void* w_kv,
                           const void* w_gate, csa_dtype_t in_dt, const float* ape,
                           const float* state_in, float* state_out, void* out,
-                          float* out_scale, csa_dtype_t out_dt, int Nc_cap,
+                          void* out_scale, csa_dtype_t out_dt, int Nc_cap,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 size_t csa_compress_workspace_size(int B, int L, int d_model, int E, int m, int overlap,
                                    csa_dtype_t in_dt);

@@ -71,6 +71,13 @@ def test_argument_errors_are_reported_without_launch(L):
     rc = L.csa_compress(1, 1, 64, 8, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, None, None,
                         dummy, None, 2, 10, None, 0, None)
     assert rc == 1 and b"out_scale" in L.csa_last_error()
+    # mxfp4 output without scales, and with a width that is not a multiple of 32
+    rc = L.csa_compress(1, 1, 64, 64, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, None, None,
+                        dummy, None, 3, 10, None, 0, None)
+    assert rc == 1 and b"out_scale" in L.csa_last_error()
+    rc = L.csa_compress(1, 1, 64, 48, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, None, None,
+                        dummy, dummy, 3, 10, None, 0, None)
+    assert rc == 2 and b"E % 32" in L.csa_last_error()
     # state aliasing
     rc = L.csa_compress(1, 1, 64, 8, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, dummy, dummy,
                         dummy, None, 0, 10, None, 0, None)

@@ -87,6 +87,57 @@ def test_compress_bf16_ragged_with_ape(out_kind, rotate):
     assert np.array_equal(np.isneginf(st.cpu().numpy()[:, :, 1]), np.isneginf(st_ref[:, :, 1]))
 
 
+def _mxfp4_step(r, x):
+    """One E2M1 step at magnitude r in a block of shared exponent x."""
+    u = np.abs(r) / 2.0 ** x
+    return np.where(u < 2, 0.5, np.where(u < 4, 1.0, 2.0)) * 2.0 ** x
+
+
+def check_mxfp4_rows(g_codes, g_scales, ref_rows, what):
+    """GPU MXFP4 rows against the oracle's quantisation of its own entries:
+    block exponents equal (or one apart where the block maximum lies within
+    fp32 rounding of a power of two) and values within one E2M1 step."""
+    codes, scales = orc.quant_rows_mxfp4(ref_rows)
+    xo = scales.astype(np.int64) - 127
+    xg = g_scales.astype(np.int64) - 127
+    amax = np.abs(ref_rows).reshape(ref_rows.shape[:-1] + (-1, 32)).max(-1)
+    near = np.abs(np.log2(np.maximum(amax, 1e-300)) - np.round(np.log2(np.maximum(amax, 1e-300)))) < 1e-5
+    assert ((xo == xg) | ((np.abs(xo - xg) == 1) & near)).all(), what + " block exponents"
+    gv = orc.mxfp4_decode(g_codes, g_scales)
+    rv = orc.mxfp4_decode(codes, scales)
+    x = np.repeat(np.minimum(xo, xg), 32, axis=-1)
+    assert (np.abs(gv - rv) <= _mxfp4_step(rv, x) + 1e-30).all(), what + " values"
+    same = (xo == xg)
+    frac = (np.repeat(same, 16, axis=-1) & (g_codes == codes)).mean()
+    assert frac > 0.99, "%s: only %.4f of the code bytes agree" % (what, frac)
+
+
+@pytest.mark.parametrize("E,rotate", [(64, False), (64, True), (256, False)])
+def test_compress_mxfp4_output(E, rotate):
+    # OCP MXFP4 entries (E2M1 codes, one E8M0 exponent per 32 channels):
+    # ragged starts with ape, as the bf16/fp8 test above
+    d = gen.Draw(13 + E + rotate)
+    B, L, dm, m, o = 3, 61, 256, 4, 1
+    x = gen.store(d.normal(B, L, dm), gen.BF16)
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    ape = d.normal(2 * m, E)
+    pos0 = [0, 5, 130]
+    Nc = 64
+    out = torch.full((B, Nc, E // 2), 0xAB, dtype=torch.uint8, device=DEV)
+    osc = torch.full((B, Nc, E // 32), 0xCD, dtype=torch.uint8, device=DEV)
+    csa.csa_compress(x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), dev_i64(pos0), m, o,
+                     out.view(torch.float4_e2m1fn_x2), out_scale=osc, ape=ape.to(DEV),
+                     rotate=rotate)
+    torch.cuda.synchronize()
+    ref, written, _ = _oracle(x, w_kv, w_gate, pos0, m, o, Nc, ape=ape, rotate=rotate)
+    g_codes, g_sc = out.cpu().numpy(), osc.cpu().numpy()
+    for b in range(B):
+        wr = written[b]
+        assert (g_codes[b, ~wr] == 0xAB).all() and (g_sc[b, ~wr] == 0xCD).all(), \
+            "rows not completed must be untouched"
+        check_mxfp4_rows(g_codes[b, wr], g_sc[b, wr], ref[b, wr], "mxfp4 E=%d b=%d" % (E, b))
+
+
 @pytest.mark.parametrize("m,o", [(4, 1), (128, 0), (3, 1)])
 def test_compress_chunked_with_state_equals_one_shot(m, o):
     d = gen.Draw(12 + m)
