@@ -138,9 +138,14 @@ def csa_compress(x, w_kv, w_gate, pos0, m, overlap, out, out_scale=None, ape=Non
 
 def csa_indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None, k_scale=None,
                      idx_out=None, score_out=None, want_scores=False, workspace=None):
-    """Lightning-indexer scores + top-k; returns (idx int32 [B, T, topk], scores or None)."""
+    """Lightning-indexer scores + top-k; returns (idx int32 [B, T, topk], scores or None).
+    fp8: float8_e4m3fn q_idx / k_idx with f32 q_scale [B, T, H_I], k_scale [B, Nc_cap];
+    mxfp4: float4_e2m1fn_x2 q_idx [B, T, H_I, d_I / 2], k_idx [B, Nc_cap, d_I / 2] with
+    E8M0 byte scales q_scale [B, T, H_I, d_I / 32], k_scale [B, Nc_cap, d_I / 32]."""
     _dense(q_idx, w_idx, k_idx, q_pos, n_cmp, q_scale, k_scale)
     B, T, H_I, d_I = q_idx.shape
+    if q_idx.dtype == torch.float4_e2m1fn_x2:
+        d_I *= 2                       # two E2M1 codes per element
     Nc_cap = k_idx.shape[1]
     if idx_out is None:
         idx_out = torch.empty(B, T, topk, dtype=torch.int32, device=q_idx.device)

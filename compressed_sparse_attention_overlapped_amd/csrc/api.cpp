@@ -101,8 +101,8 @@ size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_ca
 
 csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
                               const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
-                              const float* q_scale, const float* w_idx, const void* k_idx,
-                              const float* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
+                              const void* q_scale, const float* w_idx, const void* k_idx,
+                              const void* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
                               float* score_out, void* workspace, size_t ws_bytes,
                               hipStream_t stream) {
   if (B <= 0 || T <= 0 || H_I <= 0 || d_I <= 0 || Nc_cap < 0 || topk < 0)
@@ -111,16 +111,17 @@ csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m,
   if (topk == 0) return ok();  // nothing to select, nothing to write
   if (!q_pos || !n_cmp || !q_idx || !w_idx || !idx_out || (Nc_cap > 0 && !k_idx))
     return fail(CSA_E_ARG, "csa_indexer_topk: missing required pointer");
-  if (qk_dt == CSA_DT_FP8E4M3 && (!q_scale || (Nc_cap > 0 && !k_scale)))
-    return fail(CSA_E_ARG, "csa_indexer_topk: fp8 needs q_scale and k_scale");
+  if ((qk_dt == CSA_DT_FP8E4M3 || qk_dt == CSA_DT_MXFP4) &&
+      (!q_scale || (Nc_cap > 0 && !k_scale)))
+    return fail(CSA_E_ARG, "csa_indexer_topk: fp8 and mxfp4 need q_scale and k_scale");
   if (topk > 8192) return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: topk > 8192");
   if (Nc_cap > 1024 * 2048) return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: Nc_cap > 2^21");
   if (qk_dt == CSA_DT_F32) {
     if (!((H_I == 4 && d_I == 32) || (H_I == 16 && d_I == 64)))
       return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: f32 needs (H_I, d_I) in {(4,32),(16,64)}");
-  } else if (qk_dt == CSA_DT_BF16 || qk_dt == CSA_DT_FP8E4M3) {
+  } else if (qk_dt == CSA_DT_BF16 || qk_dt == CSA_DT_FP8E4M3 || qk_dt == CSA_DT_MXFP4) {
     if (H_I != 16 || d_I != 64)
-      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: bf16/fp8 need H_I = 16, d_I = 64");
+      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: bf16/fp8/mxfp4 need H_I = 16, d_I = 64");
     if (!aligned16(q_idx) || (Nc_cap > 0 && !aligned16(k_idx)))
       return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: q_idx and k_idx must be 16-byte aligned");
     if (qk_dt == CSA_DT_BF16 && Nc_cap > 8192 && T != 1)

@@ -161,10 +161,10 @@ struct IndexerArgs {
   const int64_t* q_pos;
   const int32_t* n_cmp;
   const void* q_idx;
-  const float* q_scale;
+  const void* q_scale;  // fp32 (e4m3) or E8M0 bytes (mxfp4)
   const float* w_idx;
   const void* k_idx;
-  const float* k_scale;
+  const void* k_scale;
   csa_dtype_t dt;
   int32_t* idx_out;
   float* score_out;

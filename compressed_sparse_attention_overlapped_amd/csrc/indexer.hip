@@ -284,13 +284,38 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-template <bool HIST>
+// MXFP4 (OCP): eight E2M1 codes of one 32-bit word (element 2i in the low
+// nibble of byte i) to bf16 times the block scale; exact, E2M1 values having
+// at most two significant bits.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+// E8M0 scale byte to its value 2^(code - 127) (code 0: the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+  return __uint_as_float(code ? code << 23 : 0x00400000u);
+}
+
+// QK = CSA_DT_FP8E4M3: rows of 64 e4m3 codes with fp32 row scales (q_scale
+// per head row, k_scale per entry).  QK = CSA_DT_MXFP4: rows of 32 bytes of
+// E2M1 codes with two E8M0 block scales each; lane l then loads 8 bytes (the
+// same 16 dims as above) and its block's scale byte.
+template <bool HIST, int QK>
 __global__ void __launch_bounds__(256) score_fp8_kernel(
-    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const uint8_t* __restrict__ q_idx, const void* __restrict__ q_scale,
     const float* __restrict__ w_idx, const uint8_t* __restrict__ k_idx,
-    const float* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
+    const void* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, float* __restrict__ scores,
     uint32_t* __restrict__ ghist) {
+  constexpr bool FP4 = QK == CSA_DT_MXFP4;
+  constexpr int KB = FP4 ? 32 : 64;  // code bytes per row of 64 values
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
   const int row = blockIdx.y, b = row / T, t = row % T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -307,32 +332,49 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
   const int we = min(je, wb + kPerWave);
   if (wb < we) {
     const int h = lane & 15, g = lane >> 4;
-    const u32x4 qv = *(const u32x4*)(q_idx + ((size_t)row * 16 + h) * 64 + 16 * g);
-    const bf16x8 qa0 = e4m3x8_to_bf16x8(qv[0], qv[1]);
-    const bf16x8 qa1 = e4m3x8_to_bf16x8(qv[2], qv[3]);
+    bf16x8 qa0, qa1;
+    if constexpr (FP4) {
+      const u32x2 qw = *(const u32x2*)(q_idx + ((size_t)row * 16 + h) * 32 + 8 * g);
+      const float qs = e8m0_value(((const uint8_t*)q_scale)[((size_t)row * 16 + h) * 2 + (g >> 1)]);
+      qa0 = fp4x8_to_bf16x8(qw[0], qs);
+      qa1 = fp4x8_to_bf16x8(qw[1], qs);
+    } else {
+      const u32x4 qv = *(const u32x4*)(q_idx + ((size_t)row * 16 + h) * 64 + 16 * g);
+      qa0 = e4m3x8_to_bf16x8(qv[0], qv[1]);
+      qa1 = e4m3x8_to_bf16x8(qv[2], qv[3]);
+    }
     float wq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int hh = 4 * g + i;
-      wq[i] = w_idx[(size_t)row * 16 + hh] * q_scale[(size_t)row * 16 + hh];
+      wq[i] = w_idx[(size_t)row * 16 + hh] *
+              (FP4 ? 1.0f : ((const float*)q_scale)[(size_t)row * 16 + hh]);
     }
-    const uint8_t* kb = k_idx + (size_t)b * Nc_cap * 64;
-    const float* ks = k_scale + (size_t)b * Nc_cap;
+    const uint8_t* kb = k_idx + (size_t)b * Nc_cap * KB;
+    const float* ks = FP4 ? nullptr : (const float*)k_scale + (size_t)b * Nc_cap;
+    const uint8_t* ks8 = FP4 ? (const uint8_t*)k_scale + (size_t)b * Nc_cap * 2 : nullptr;
     float* srow = scores + (size_t)row * Nc_cap;
     // two register stages: the codes of step i + 2 load while step i computes
     u32x4 kv[2][SF_UNROLL];
     float ksc[2][SF_UNROLL / 4];  // scale of the entry this lane writes, per 64-entry half
+    // (MXFP4: words 0-1 the 16 codes, word 2 the block's scale byte)
     auto load = [&](int it, int st) {
 #pragma unroll
       for (int u = 0; u < SF_UNROLL; ++u) {
         const int j = wb + it * kStep + 16 * u + (lane & 15);
-        kv[st][u] = j < we ? __builtin_nontemporal_load((const u32x4*)(kb + (size_t)j * 64 + 16 * g))
-                           : u32x4{0, 0, 0, 0};
+        if constexpr (FP4) {
+          const u32x2 w = j < we ? __builtin_nontemporal_load((const u32x2*)(kb + (size_t)j * 32 + 8 * g))
+                                 : u32x2{0, 0};
+          kv[st][u] = u32x4{w[0], w[1], j < we ? (uint32_t)ks8[(size_t)j * 2 + (g >> 1)] : 127u, 0u};
+        } else {
+          kv[st][u] = j < we ? __builtin_nontemporal_load((const u32x4*)(kb + (size_t)j * 64 + 16 * g))
+                             : u32x4{0, 0, 0, 0};
+        }
       }
 #pragma unroll
       for (int hf = 0; hf < SF_UNROLL / 4; ++hf) {
         const int j = wb + it * kStep + 64 * hf + lane;
-        ksc[st][hf] = j < we ? ks[j] : 0.0f;
+        ksc[st][hf] = FP4 ? 1.0f : (j < we ? ks[j] : 0.0f);
       }
     };
     load(0, 0);
@@ -346,10 +388,17 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
 #pragma unroll
       for (int u = 0; u < SF_UNROLL; ++u) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qa0, e4m3x8_to_bf16x8(kv[st][u][0], kv[st][u][1]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qa1, e4m3x8_to_bf16x8(kv[st][u][2], kv[st][u][3]), acc, 0, 0, 0);
+        bf16x8 k0, k1;
+        if constexpr (FP4) {
+          const float sc_blk = e8m0_value(kv[st][u][2]);
+          k0 = fp4x8_to_bf16x8(kv[st][u][0], sc_blk);
+          k1 = fp4x8_to_bf16x8(kv[st][u][1], sc_blk);
+        } else {
+          k0 = e4m3x8_to_bf16x8(kv[st][u][0], kv[st][u][1]);
+          k1 = e4m3x8_to_bf16x8(kv[st][u][2], kv[st][u][3]);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, k0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, k1, acc, 0, 0, 0);
         // acc[i]: head 4 (lane / 16) + i, entry lane % 16 of group u
         float p = 0.0f;
 #pragma unroll
@@ -996,14 +1045,18 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     }
   } else {
     dim3 g((a.Nc_cap + kChunk - 1) / kChunk, rows);
-    if (L.long_rows)
-      score_fp8_kernel<true><<<g, 256, 0, st>>>((const uint8_t*)a.q_idx, a.q_scale, a.w_idx,
-                                                (const uint8_t*)a.k_idx, a.k_scale, a.q_pos,
-                                                a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist);
-    else
-      score_fp8_kernel<false><<<g, 256, 0, st>>>((const uint8_t*)a.q_idx, a.q_scale, a.w_idx,
-                                                 (const uint8_t*)a.k_idx, a.k_scale, a.q_pos,
-                                                 a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist);
+#define CSA_LAUNCH_SF(HS, QK)                                                                 \
+  score_fp8_kernel<HS, QK><<<g, 256, 0, st>>>((const uint8_t*)a.q_idx, a.q_scale, a.w_idx,   \
+                                              (const uint8_t*)a.k_idx, a.k_scale, a.q_pos,   \
+                                              a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist)
+    if (a.dt == CSA_DT_MXFP4) {
+      if (L.long_rows) CSA_LAUNCH_SF(true, CSA_DT_MXFP4);
+      else CSA_LAUNCH_SF(false, CSA_DT_MXFP4);
+    } else {
+      if (L.long_rows) CSA_LAUNCH_SF(true, CSA_DT_FP8E4M3);
+      else CSA_LAUNCH_SF(false, CSA_DT_FP8E4M3);
+    }
+#undef CSA_LAUNCH_SF
   }
   if (!L.long_rows) {
     const unsigned g = (unsigned)((rows + 3) / 4);

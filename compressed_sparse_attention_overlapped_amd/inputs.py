@@ -10,7 +10,9 @@ seed a test passes), tensors drawn in the order listed by each builder.
 Weights are N(0, 1/fan_in); activations, caches and indexer head weights are
 N(0, 1).  bf16 storage uses torch's round-to-nearest-even conversion; e4m3
 storage divides each row by ``amax / 448`` and converts with torch's
-``float8_e4m3fn`` cast.  Small inputs are drawn on the CPU (identical on
+``float8_e4m3fn`` cast.  MXFP4 storage (OCP: E2M1 codes two per byte, one
+E8M0 exponent per 32 values) is drawn directly: code bytes uniform over
+0..255 and block exponents uniform over -3..3 (E8M0 bytes 124..130).  Small inputs are drawn on the CPU (identical on
 every machine); the multi-GiB decode caches are drawn on the device they are
 used on, and the checks copy the sampled rows back to the host.
 """
@@ -22,7 +24,7 @@ from typing import Optional
 
 import torch
 
-F32, BF16, FP8 = "f32", "bf16", "fp8"
+F32, BF16, FP8, MXFP4 = "f32", "bf16", "fp8", "mxfp4"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -75,7 +77,8 @@ WORKLOADS = {
 
 
 def torch_dtype(fmt: str) -> torch.dtype:
-    return {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.float8_e4m3fn}[fmt]
+    return {F32: torch.float32, BF16: torch.bfloat16, FP8: torch.float8_e4m3fn,
+            MXFP4: torch.float4_e2m1fn_x2}[fmt]
 
 
 class Draw:
@@ -123,7 +126,8 @@ def host_bits(t: torch.Tensor):
         return t.numpy()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float4_e2m1fn_x2, torch.float8_e8m0fnu,
+                   torch.uint8):
         return t.view(torch.uint8).numpy()
     if t.dtype in (torch.int32, torch.int64):
         return t.numpy()
@@ -142,8 +146,21 @@ def compressor_weights(d: Draw, d_model: int, E: int, fmt: str):
     return w_kv, w_gate
 
 
+def mxfp4_random(d: Draw, *shape_n):
+    """Random MXFP4 rows of n values (n a multiple of 32): (codes as
+    float4_e2m1fn_x2 [..., n / 2], E8M0 scale bytes uint8 [..., n / 32])."""
+    *lead, n = shape_n
+    codes = d.ints(0, 256, *lead, n // 2).to(torch.uint8).view(torch.float4_e2m1fn_x2)
+    scales = d.ints(124, 131, *lead, n // 32).to(torch.uint8)
+    return codes.contiguous(), scales.contiguous()
+
+
 def indexer_query(d: Draw, B: int, T: int, H_I: int, d_I: int, fmt: str):
-    """q_idx [B,T,H_I,d_I] (+ per-(t,h) scales when e4m3) and w_idx [B,T,H_I]."""
+    """q_idx [B,T,H_I,d_I] (+ per-(t,h) scales when e4m3; MXFP4: codes
+    [B,T,H_I,d_I/2] and E8M0 block scales [B,T,H_I,d_I/32]) and w_idx [B,T,H_I]."""
+    if fmt == MXFP4:
+        q_idx, q_scale = mxfp4_random(d, B, T, H_I, d_I)
+        return q_idx, q_scale, d.normal(B, T, H_I)
     q = d.normal(B, T, H_I, d_I)
     if fmt == FP8:
         q_idx, q_scale = store_fp8(q)
@@ -154,6 +171,8 @@ def indexer_query(d: Draw, B: int, T: int, H_I: int, d_I: int, fmt: str):
 
 
 def indexer_keys(d: Draw, B: int, Nc: int, d_I: int, fmt: str):
+    if fmt == MXFP4:
+        return mxfp4_random(d, B, Nc, d_I)
     k = d.normal(B, Nc, d_I)
     if fmt == FP8:
         return store_fp8(k)

@@ -133,17 +133,21 @@ size_t csa_compress_workspace_size(int B, int L, int d_model, int E, int m, int 
  *  q_idx     [B, T, H_I, d_I] in qk_dt;  q_scale fp32 [B, T, H_I] iff fp8
  *  w_idx     fp32 [B, T, H_I]
  *  k_idx     [B, Nc_cap, d_I] in qk_dt;  k_scale fp32 [B, Nc_cap] iff fp8
+ *            (mxfp4: q_idx bytes [B, T, H_I, d_I / 2] with q_scale E8M0 bytes
+ *            [B, T, H_I, d_I / 32], k_idx bytes [B, Nc_cap, d_I / 2] with
+ *            k_scale E8M0 bytes [B, Nc_cap, d_I / 32]; the score uses the
+ *            decoded values, each with its block scale, and sq = sk = 1)
  *  idx_out   int32 [B, T, topk]
  *  score_out fp32 [B, T, topk] or NULL: the score of each selected index
  *            (NaN in padded slots)
  *  workspace at least csa_indexer_topk_workspace_size() bytes
- * Supported: (H_I, d_I) in {(4, 32), (16, 64)} for F32; (16, 64) for BF16 and
- * FP8E4M3; topk <= 8192.  fp8 scales must be positive.
+ * Supported: (H_I, d_I) in {(4, 32), (16, 64)} for F32; (16, 64) for BF16,
+ * FP8E4M3 and MXFP4; topk <= 8192.  fp8 scales must be positive.
  */
 csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
                               const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
-                              const float* q_scale, const float* w_idx, const void* k_idx,
-                              const float* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
+                              const void* q_scale, const float* w_idx, const void* k_idx,
+                              const void* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
                               float* score_out, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_cap, int topk,

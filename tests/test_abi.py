@@ -82,6 +82,10 @@ def test_argument_errors_are_reported_without_launch(L):
     rc = L.csa_compress(1, 1, 64, 8, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, dummy, dummy,
                         dummy, None, 0, 10, None, 0, None)
     assert rc == 1 and b"alias" in L.csa_last_error()
+    # mxfp4 indexer inputs without their block scales
+    rc = L.csa_indexer_topk(1, 1, 16, 64, 100, 4, 10, dummy, dummy, dummy, None, dummy, dummy,
+                            None, 3, dummy, None, None, 0, None)
+    assert rc == 1 and b"q_scale" in L.csa_last_error()
     # unsupported indexer geometry
     rc = L.csa_indexer_topk(1, 1, 8, 64, 100, 4, 10, dummy, dummy, dummy, None, dummy, dummy, None,
                             1, dummy, None, None, 0, None)

@@ -27,11 +27,12 @@ def _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None, k_scale=None)
 
 
 def _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None, k_scale=None):
+    fmt = "mxfp4" if q_idx.dtype == torch.float4_e2m1fn_x2 else None
     return orc.indexer_topk(gen.host_bits(q_idx), gen.host_bits(w_idx), gen.host_bits(k_idx), m,
                             topk, np.asarray(q_pos), np.asarray(n_cmp),
                             q_scale=None if q_scale is None else gen.host_bits(q_scale),
                             k_scale=None if k_scale is None else gen.host_bits(k_scale),
-                            want_all=True)
+                            want_all=True, fmt=fmt)
 
 
 def _compare(g_idx, g_sc, o_all, m, topk, q_pos, n_cmp, Nc, what):
@@ -161,6 +162,37 @@ def test_indexer_fp8_decode_long_rows(name, rows):
         o = _oracle_rows(q_idx[sl], w_idx[sl], k_idx[sl], w.m, w.topk, [w.ctx - 1], [Nc],
                          q_scale[sl], k_scale[sl])
         _compare(g_idx[sl], g_sc[sl], o[3], w.m, w.topk, [w.ctx - 1], [Nc], Nc, "%s b%d" % (name, b))
+
+
+@pytest.mark.parametrize("name,rows", [("csa_decode_128k_b32", [0, 13, 31])])
+def test_indexer_mxfp4_decode_long_rows(name, rows):
+    # MXFP4 keys and queries (E2M1 codes, one E8M0 exponent per 32 values)
+    # at the 128K decode shape: the long-row collect / finalize path
+    w = gen.WORKLOADS[name]
+    d = gen.Draw(w.seed + 7, DEV)
+    B, Nc = w.B, w.n_cmp
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, w.d_I, gen.MXFP4)
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, 1, w.H_I, w.d_I, gen.MXFP4)
+    q_pos = [w.ctx - 1] * B
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, w.m, w.topk, q_pos, [Nc] * B, q_scale, k_scale)
+    for b in rows:
+        sl = slice(b, b + 1)
+        o = _oracle_rows(q_idx[sl], w_idx[sl], k_idx[sl], w.m, w.topk, [w.ctx - 1], [Nc],
+                         q_scale[sl], k_scale[sl])
+        _compare(g_idx[sl], g_sc[sl], o[3], w.m, w.topk, [w.ctx - 1], [Nc], Nc,
+                 "mxfp4 %s b%d" % (name, b))
+
+
+def test_indexer_mxfp4_short_rows_ragged():
+    # prefill-shaped MXFP4 rows (the short-row select), ragged visibility
+    d = gen.Draw(27)
+    B, T, Nc, m, topk = 2, 90, 700, 4, 64
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.MXFP4)
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.MXFP4)
+    q_pos, n_cmp = [2500, 37], [Nc, 500]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "mxfp4 short rows")
 
 
 def test_indexer_fp8_long_rows_heavy_ties_and_partial_visibility():
