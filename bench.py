@@ -354,7 +354,7 @@ def cpu_baseline(w, budget_s=12.0):
         while tot < budget_s:
             a = time.perf_counter()
             idx = orc.indexer_topk(qb, wb, kb, w.m, w.topk, w.ctx - 1, w.n_cmp, q_scale=qs,
-                                   k_scale=ks)[0]
+                                   k_scale=ks, fmt="mxfp4" if w.idx_dt == gen.MXFP4 else None)[0]
             idx = np.where(idx >= Ns, idx % Ns, idx)
             orc.sparse_attn(q, kv_cmp, idx, kv_raw, w.window, w.ctx - 1, w.ctx - w.window)
             tot += time.perf_counter() - a
@@ -435,7 +435,8 @@ def measure(name, steps, warmup, with_cpu):
                        / MFMA_BF16_PEAK_TFLOPS}
     elif w.kind == "csa_decode":
         B, Nc = w.B, w.n_cmp
-        key_bytes = B * Nc * (w.d_I + 4)
+        # per entry: e4m3 codes + an fp32 scale, or MXFP4 codes + E8M0 block scales
+        key_bytes = B * Nc * ((w.d_I // 2 + w.d_I // 32) if w.idx_dt == gen.MXFP4 else (w.d_I + 4))
         gather = B * (w.topk + w.window) * 4 * w.D
         small = B * (2 * w.H * w.D * 2 + 2 * w.topk * 4 + w.H_I * w.d_I + w.H_I * 8)
         total = key_bytes + gather + small

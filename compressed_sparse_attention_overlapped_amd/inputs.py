@@ -64,6 +64,11 @@ WORKLOADS = {
     "csa_decode_128k_b32": Workload("csa_decode_128k_b32", "csa_decode", B=32, ctx=131072, T=1,
                                     H=64, D=128, m=4, overlap=1, window=512, topk=2048, H_I=16,
                                     d_I=64, dt=BF16, idx_dt=FP8, n_cmp=32768, seed=1003),
+    # the same decode with MXFP4 indexer keys and queries (FP4 indexer)
+    "csa_decode_128k_b32_mxfp4": Workload("csa_decode_128k_b32_mxfp4", "csa_decode", B=32,
+                                          ctx=131072, T=1, H=64, D=128, m=4, overlap=1,
+                                          window=512, topk=2048, H_I=16, d_I=64, dt=BF16,
+                                          idx_dt=MXFP4, n_cmp=32768, seed=1006),
     # HCA prefill chunk of 4096 tokens at the tail of a 1M context
     "hca_prefill_1m_chunk4k": Workload("hca_prefill_1m_chunk4k", "hca_prefill", B=1, ctx=1 << 20,
                                        T=4096, H=64, D=128, m=128, overlap=0, window=512,
