@@ -32,9 +32,9 @@
  *    6; sign in bit 3) packed two per byte, element 2i of a row in the low
  *    nibble, with one E8M0 scale byte per 32 consecutive values of a row:
  *    value = e2m1(code) * 2^(scale - 127).  A row of n values takes n / 2
- *    code bytes and n / 32 scale bytes.  (The DS-V4 analysis, section 3.2,
- *    says the indexer computes in FP4 and names no format; MXFP4 is the
- *    reading taken.)
+ *    code bytes and n / 32 scale bytes.  (The CSA/HCA article, section 3.2,
+ *    notes that the indexer computes in FP4 and names no format; MXFP4 is
+ *    the reading taken.)
  */
 #ifndef CSA_H_
 #define CSA_H_

@@ -39,9 +39,9 @@
  *    the published Lightning Indexer form; the pages print only its one-head
  *    special case, so the multi-head form is "parity unpinned"; the top-k
  *    order is pinned against a library sort.  The optional MXFP4
- *    inputs (the DS-V4 analysis, section 3.2, says the indexer computes in
- *    FP4 and nothing more; read as OCP MXFP4: E2M1 values with an E8M0 scale
- *    per 32) are pinned to the standard's E2M1 table, to nearest-value
+ *    inputs (the CSA/HCA article, section 3.2, notes that the indexer
+ *    computes in FP4 and nothing more; read as OCP MXFP4: E2M1 values with an
+ *    E8M0 scale per 32) are pinned to the standard's E2M1 table, to nearest-value
  *    rounding by brute force, to a library E8M0 decode, and to the fp32
  *    path on the decoded values.
  *  - orc_sparse_attn / orc_hca_dense_attn: pinned to a library scaled

@@ -317,10 +317,10 @@ def test_indexer_e4m3_scales_fold_into_score():
     np.testing.assert_allclose(a[3], s_ref, rtol=1e-9, atol=1e-9)
 
 
-# The pages say only that the indexer's QK path runs in FP4 (the DS-V4
-# analysis, section 3.2's closing note; the engineering-trick list of the
-# same page).  The reading taken is OCP MXFP4: E2M1 elements with one E8M0
-# power-of-two scale per 32 values.
+# The pages say only that the indexer's QK path runs in FP4 (the CSA/HCA
+# article, section 3.2's closing note; the DS-V4 analysis, section 4, asks
+# for a low-precision QK path).  The reading taken is OCP MXFP4: E2M1
+# elements with one E8M0 power-of-two scale per 32 values.
 
 # the E2M1 magnitudes the OCP Microscaling v1.0 standard lists for codes 0-7
 E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
