@@ -138,6 +138,37 @@ def test_compress_mxfp4_output(E, rotate):
         check_mxfp4_rows(g_codes[b, wr], g_sc[b, wr], ref[b, wr], "mxfp4 E=%d b=%d" % (E, b))
 
 
+def test_compress_decode_step_mxfp4():
+    # the indexer compressor's decode step (few-row projection, pool from the
+    # carried state) with an MXFP4 store
+    w = gen.WORKLOADS["csa_decode_1m_b8_stream"]
+    d = gen.Draw(15)
+    B, dm, m, o, E = w.B, w.d_model, w.m, w.overlap, w.d_I
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    x_tail = gen.store(d.normal(B, 7, dm), gen.BF16)
+    x_new = gen.store(d.normal(B, 1, dm), gen.BF16)
+    T = w.ctx
+    Nc = T // m
+    pos_tail = [T - 8] * B
+    _, _, st1 = _oracle(x_tail, w_kv, w_gate, pos_tail, m, o, Nc)
+    ref2, wr2, _ = _oracle(x_new, w_kv, w_gate, [T - 1] * B, m, o, Nc,
+                           state_in=torch.from_numpy(st1))
+    assert wr2[:, Nc - 1].all()
+    wk, wg = w_kv.to(DEV), w_gate.to(DEV)
+    s0 = torch.zeros(B, 2 * m - 1, 2, E, device=DEV)
+    s1 = torch.zeros(B, 2 * m - 1, 2, E, device=DEV)
+    out = torch.zeros(B, Nc, E // 2, dtype=torch.uint8, device=DEV)
+    osc = torch.zeros(B, Nc, E // 32, dtype=torch.uint8, device=DEV)
+    o4 = out.view(torch.float4_e2m1fn_x2)
+    csa.csa_compress(x_tail.to(DEV), wk, wg, dev_i64(pos_tail), m, o, o4, out_scale=osc,
+                     state_out=s0)
+    csa.csa_compress(x_new.to(DEV), wk, wg, dev_i64([T - 1] * B), m, o, o4, out_scale=osc,
+                     state_in=s0, state_out=s1)
+    torch.cuda.synchronize()
+    check_mxfp4_rows(out[:, Nc - 1].cpu().numpy(), osc[:, Nc - 1].cpu().numpy(),
+                     ref2[:, Nc - 1], "mxfp4 decode entry")
+
+
 @pytest.mark.parametrize("m,o", [(4, 1), (128, 0), (3, 1)])
 def test_compress_chunked_with_state_equals_one_shot(m, o):
     d = gen.Draw(12 + m)
