@@ -136,15 +136,16 @@ __global__ void __launch_bounds__(512) proj_bf16_kernel(
 }
 
 // ------------------------------------------------------- proj (bf16, few rows)
-// Decode steps and short chunks (M <= 16 rows): one workgroup per 16 output
-// columns computes them over all of K (no partials), its 16 waves taking a
-// sixteenth of K each, so that a 4096-deep projection issues all of its
-// loads at once (one memory round trip); MFMA 16x16x32 with the rows as M
-// (rows past M read row M - 1 and are dropped) and 16 columns of the stacked
+// Decode steps and short chunks (M <= 16 rows): a workgroup per 16 output
+// columns and K split (grid y, at most four split partials, so that the
+// grid covers the chip), its 8 waves taking an eighth of its K range each,
+// with all of a wave's loads in flight at once (batches of eight k steps,
+// the last one clamped and masked); MFMA 16x16x32 with the rows as M (rows
+// past M read row M - 1 and are dropped) and 16 columns of the stacked
 // weight as N.  Each weight byte is read once; the few x rows stay in L2.
-// The partial sums are added in wave order through LDS.  K % 512 == 0
-// (checked by the host).
-constexpr int PS_COLS = 16, PS_UNROLL = 8, PS_WAVES = 16;
+// The waves' partial sums are added in wave order through LDS, the splits'
+// by the pool, in split order.  K % (256 splits) == 0 (checked by the host).
+constexpr int PS_COLS = 16, PS_UNROLL = 8, PS_WAVES = 8;
 
 __global__ void __launch_bounds__(64 * PS_WAVES) proj_small_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
@@ -154,30 +155,28 @@ __global__ void __launch_bounds__(64 * PS_WAVES) proj_small_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * PS_COLS;
-  const int kq = K / PS_WAVES;
+  const int kq = K / (PS_WAVES * (int)gridDim.y);
+  const int k0 = ((int)blockIdx.y * PS_WAVES + wave) * kq;
   // operand lanes: row / column lane % 16, k chunk 8 (lane / 16) of each
   // 32-deep step (the same k order for both operands)
   const int arow = min(lane & 15, M - 1);
-  const uint16_t* ap = x + (size_t)arow * K + wave * kq + 8 * (lane >> 4);
+  const uint16_t* ap = x + (size_t)arow * K + k0 + 8 * (lane >> 4);
   const int gn = min(n0 + (lane & 15), N - 1);
   const uint16_t* bp =
-      (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(gn - E) * K) + wave * kq + 8 * (lane >> 4);
+      (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(gn - E) * K) + k0 + 8 * (lane >> 4);
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int k = 0;
-  for (; k + 32 * PS_UNROLL <= kq; k += 32 * PS_UNROLL) {
+  for (int k = 0; k < kq; k += 32 * PS_UNROLL) {
     bf16x8 a[PS_UNROLL], bv[PS_UNROLL];
 #pragma unroll
     for (int u = 0; u < PS_UNROLL; ++u) {
-      a[u] = *(const bf16x8*)(ap + k + 32 * u);
-      bv[u] = *(const bf16x8*)(bp + k + 32 * u);
+      const int kk = min(k + 32 * u, kq - 32);  // in range; masked below
+      a[u] = *(const bf16x8*)(ap + kk);
+      bv[u] = *(const bf16x8*)(bp + kk);
     }
 #pragma unroll
     for (int u = 0; u < PS_UNROLL; ++u)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bv[u], acc, 0, 0, 0);
-  }
-  for (; k < kq; k += 32) {
-    const bf16x8 a = *(const bf16x8*)(ap + k), bv = *(const bf16x8*)(bp + k);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc, 0, 0, 0);
+      if (k + 32 * u < kq)  // uniform
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bv[u], acc, 0, 0, 0);
   }
   // accumulator: lane holds column lane % 16, rows 4 (lane / 16) + i
   for (int i = 0; i < 4; ++i) red[wave][(4 * (lane >> 4) + i) * PS_COLS + (lane & 15)] = acc[i];
@@ -186,12 +185,21 @@ __global__ void __launch_bounds__(64 * PS_WAVES) proj_small_kernel(
     const int row = tid / PS_COLS, col = n0 + tid % PS_COLS;
     float sum = red[0][tid];
     for (int w = 1; w < PS_WAVES; ++w) sum += red[w][tid];
-    if (row < M && col < N) pg[(size_t)row * N + col] = sum;
+    if (row < M && col < N) pg[((size_t)blockIdx.y * M + row) * N + col] = sum;
   }
 }
 
 static bool use_proj_small(int M, int K, csa_dtype_t dt) {
   return dt == CSA_DT_BF16 && M <= 16 && K % (32 * PS_WAVES) == 0;
+}
+
+// K splits of the few-row projection: up to four, while the grid has fewer
+// than 256 workgroups and every wave keeps whole 32-deep k steps
+static int proj_small_splits(int E, int K) {
+  const int groups = (2 * E + PS_COLS - 1) / PS_COLS;
+  int s = 1;
+  while (s < 4 && groups * s < 256 && K % (32 * PS_WAVES * 2 * s) == 0) s *= 2;
+  return s;
 }
 
 // ---------------------------------------------------------------- proj (fp32)
@@ -520,7 +528,8 @@ namespace csa_host {
 using namespace csa;
 
 static int proj_splits(int M, int E, int K, csa_dtype_t dt) {
-  if (dt != CSA_DT_BF16 || use_proj_small(M, K, dt)) return 1;
+  if (use_proj_small(M, K, dt)) return proj_small_splits(E, K);
+  if (dt != CSA_DT_BF16) return 1;
   int tiles = ((M + PJ_BM - 1) / PJ_BM) * ((2 * E + PJ_BN - 1) / PJ_BN);
   int s = 1;
   // split K while the grid holds fewer than one workgroup per CU (two for
@@ -549,7 +558,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   const int splits = proj_splits(M, E, K, a.in_dt);
   float* pg = (float*)a.ws;
   if (use_proj_small(M, K, a.in_dt)) {
-    proj_small_kernel<<<(2 * E + PS_COLS - 1) / PS_COLS, 64 * PS_WAVES, 0, st>>>(
+    proj_small_kernel<<<dim3((2 * E + PS_COLS - 1) / PS_COLS, splits), 64 * PS_WAVES, 0, st>>>(
         (const uint16_t*)a.x, (const uint16_t*)a.w_kv, (const uint16_t*)a.w_gate, pg, M, E, K);
   } else if (a.in_dt == CSA_DT_BF16) {
     dim3 grid((M + PJ_BM - 1) / PJ_BM, (2 * E + PJ_BN - 1) / PJ_BN, splits);

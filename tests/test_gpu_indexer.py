@@ -195,11 +195,12 @@ def test_indexer_mxfp4_short_rows_ragged():
     _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "mxfp4 short rows")
 
 
-def test_indexer_fp8_long_rows_heavy_ties_and_partial_visibility():
-    # 20000 entries with one repeated key: every candidate ties exactly, which
-    # overflows the LDS candidate buffer and exercises the exact global path
+@pytest.mark.parametrize("Nc", [20000, 40000])
+def test_indexer_fp8_long_rows_heavy_ties_and_partial_visibility(Nc):
+    # one repeated key: every candidate ties exactly, which overflows the LDS
+    # candidate buffer and exercises the exact global path
     d = gen.Draw(24, "cpu")
-    B, Nc, m, topk = 3, 20000, 4, 300
+    B, m, topk = 3, 4, 300
     k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
     kb = k_idx.view(torch.uint8)            # edit the stored codes directly
     kb[0] = kb[0, 5].clone()
@@ -212,10 +213,56 @@ def test_indexer_fp8_long_rows_heavy_ties_and_partial_visibility():
     n_cmp = [Nc, Nc - 7, Nc]
     g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
     o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
-    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "fp8 ties")
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "fp8 ties %d" % Nc)
     # all-equal row: the lowest indices win, bit-exact
     if (o[3][0, 0, :Nc] == o[3][0, 0, 0]).all():
         assert np.array_equal(g_idx[0, 0], np.arange(topk))
+
+
+@pytest.mark.parametrize("Nc", [8193, 32768])
+def test_indexer_bf16_long_rows_bounds_and_ragged(Nc):
+    # the shortest row length past the one-wave select, and the 128K-context
+    # length, over sequences whose visibility runs from a few entries (every
+    # visible entry kept) to the whole row
+    d = gen.Draw(30 + Nc % 7)
+    B, m, topk = 3, 4, 1000
+    q_idx, _, w_idx = gen.indexer_query(d, B, 1, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    k_idx[1, 4000:4500] = k_idx[1, 77]       # a block of tied scores
+    q_pos, n_cmp = [4 * Nc - 2, 4 * 6000, 4 * 900], [Nc, Nc - 5, Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "bf16 long rows %d" % Nc)
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "two_values", "one_high"])
+def test_indexer_fp8_long_rows_degenerate(kind):
+    # degenerate long score rows: ties resolve to the lowest indices,
+    # bit-exact against the oracle
+    d = gen.Draw(31, "cpu")
+    B, Nc, m, topk = 1, 24000, 4, 2048
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
+    kb = k_idx.view(torch.uint8)
+    if kind == "all_equal":
+        kb[0] = kb[0, 9].clone()
+        k_scale[0] = k_scale[0, 9].clone()
+    elif kind == "two_values":
+        kb[0, 0::2] = kb[0, 5].clone()
+        k_scale[0, 0::2] = k_scale[0, 5].clone()
+        kb[0, 1::2] = kb[0, 8].clone()
+        k_scale[0, 1::2] = k_scale[0, 8].clone()
+    else:
+        kb[0] = kb[0, 9].clone()
+        k_scale[0] = k_scale[0, 9].clone()
+        k_scale[0, 12345] = k_scale[0, 12345] * 4.0
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, 1, 16, 64, gen.FP8)
+    q_pos, n_cmp = [4 * Nc], [Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    assert sorted(g_idx[0, 0].tolist()) == sorted(o[0][0, 0].tolist()), kind
+    assert (np.diff(g_idx[0, 0]) > 0).all()
+    if kind == "all_equal":
+        assert (g_idx[0, 0] == np.arange(topk)).all()
 
 
 def test_indexer_edge_rows():
