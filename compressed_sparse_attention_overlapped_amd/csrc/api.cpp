@@ -5,6 +5,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <algorithm>
+#include <climits>
 #include "common.h"
 
 namespace {
@@ -33,6 +35,29 @@ csa_status_t hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace {
+// Validates an optional page table; null means the unpaged layout.
+csa_status_t check_pages(const char* fn, const csa_page_table_t* pg, int Nc_cap,
+                         csa::PageTable& out) {
+  out = csa::PageTable{nullptr, 0, 0, 0};
+  if (!pg) return CSA_OK;
+  if (!pg->block_table) return fail(CSA_E_ARG, "%s: pages->block_table is required", fn);
+  const int ps = pg->page_size;
+  if (ps < 16 || ps > (1 << 20) || (ps & (ps - 1)))
+    return fail(CSA_E_ARG, "%s: page_size must be a power of two in [16, 2^20] (got %d)", fn, ps);
+  if (pg->max_pages < 1 || pg->n_pages < 1)
+    return fail(CSA_E_ARG, "%s: max_pages and n_pages must be >= 1", fn);
+  if ((int64_t)pg->max_pages * ps < (int64_t)Nc_cap)
+    return fail(CSA_E_ARG, "%s: Nc_cap %d exceeds max_pages * page_size", fn, Nc_cap);
+  if ((int64_t)pg->n_pages * ps > (int64_t)1 << 30)
+    return fail(CSA_E_UNSUPPORTED, "%s: pools hold at most 2^30 rows", fn);
+  int lg = 0;
+  while ((1 << lg) < ps) ++lg;
+  out = csa::PageTable{pg->block_table, lg, pg->max_pages, pg->n_pages};
+  return CSA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* csa_status_string(csa_status_t s) {
@@ -54,12 +79,12 @@ size_t csa_compress_workspace_size(int B, int L, int d_model, int E, int m, int 
   return csa_host::compress_ws_bytes(B, L, d_model, E, m, overlap, in_dt);
 }
 
-csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+static csa_status_t compress_impl(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                           const int64_t* pos0, const void* x, const void* w_kv,
                           const void* w_gate, csa_dtype_t in_dt, const float* ape,
                           const float* state_in, float* state_out, void* out, void* out_scale,
                           csa_dtype_t out_dt, int Nc_cap, void* workspace, size_t ws_bytes,
-                          hipStream_t stream) {
+                          hipStream_t stream, const csa_page_table_t* pages) {
   if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0 || Nc_cap < 0)
     return fail(CSA_E_ARG, "csa_compress: B, L, d_model, E must be > 0 and Nc_cap >= 0");
   if (m < 1) return fail(CSA_E_ARG, "csa_compress: m must be >= 1 (got %d)", m);
@@ -88,9 +113,37 @@ csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, 
   const size_t need = csa_host::compress_ws_bytes(B, L, d_model, E, m, overlap, in_dt);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "csa_compress: workspace %zu < %zu bytes", ws_bytes, need);
+  csa::PageTable pt;
+  const csa_status_t pst = check_pages("csa_compress", pages, Nc_cap, pt);
+  if (pst != CSA_OK) return pst;
   csa_host::CompressArgs a{B, L, d_model, E, m, overlap, rotate, Nc_cap, pos0, x, w_kv, w_gate,
                            in_dt, out_dt, ape, state_in, state_out, out, out_scale, workspace};
+  a.pages = pt;
   return hip_status(csa_host::launch_compress(a, stream), "csa_compress launch");
+}
+
+csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                          const int64_t* pos0, const void* x, const void* w_kv,
+                          const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                          const float* state_in, float* state_out, void* out, void* out_scale,
+                          csa_dtype_t out_dt, int Nc_cap, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  return compress_impl(B, L, d_model, E, m, overlap, rotate, pos0, x, w_kv, w_gate, in_dt, ape,
+                       state_in, state_out, out, out_scale, out_dt, Nc_cap, workspace, ws_bytes,
+                       stream, nullptr);
+}
+
+csa_status_t csa_compress_paged(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                                const int64_t* pos0, const void* x, const void* w_kv,
+                                const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                                const float* state_in, float* state_out, void* out,
+                                void* out_scale, csa_dtype_t out_dt, int Nc_cap,
+                                const csa_page_table_t* pages, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!pages) return fail(CSA_E_ARG, "csa_compress_paged: pages is required");
+  return compress_impl(B, L, d_model, E, m, overlap, rotate, pos0, x, w_kv, w_gate, in_dt, ape,
+                       state_in, state_out, out, out_scale, out_dt, Nc_cap, workspace, ws_bytes,
+                       stream, pages);
 }
 
 size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_cap, int topk,
@@ -99,12 +152,12 @@ size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_ca
   return csa_host::indexer_ws_bytes(B, T, H_I, d_I, Nc_cap, topk, qk_dt);
 }
 
-csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
-                              const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
-                              const void* q_scale, const float* w_idx, const void* k_idx,
-                              const void* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
-                              float* score_out, void* workspace, size_t ws_bytes,
-                              hipStream_t stream) {
+static csa_status_t indexer_impl(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
+                                 const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
+                                 const void* q_scale, const float* w_idx, const void* k_idx,
+                                 const void* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
+                                 float* score_out, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream, const csa_page_table_t* pages) {
   if (B <= 0 || T <= 0 || H_I <= 0 || d_I <= 0 || Nc_cap < 0 || topk < 0)
     return fail(CSA_E_ARG, "csa_indexer_topk: B, T, H_I, d_I must be > 0; Nc_cap, topk >= 0");
   if (m < 1) return fail(CSA_E_ARG, "csa_indexer_topk: m must be >= 1");
@@ -132,9 +185,37 @@ csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m,
   const size_t need = csa_host::indexer_ws_bytes(B, T, H_I, d_I, Nc_cap, topk, qk_dt);
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "csa_indexer_topk: workspace %zu < %zu bytes", ws_bytes, need);
+  csa::PageTable pt;
+  const csa_status_t pst = check_pages("csa_indexer_topk", pages, Nc_cap, pt);
+  if (pst != CSA_OK) return pst;
+  if (pages && qk_dt != CSA_DT_FP8E4M3 && qk_dt != CSA_DT_MXFP4)
+    return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_paged: paged keys need FP8E4M3 or MXFP4");
   csa_host::IndexerArgs a{B, T, H_I, d_I, Nc_cap, m, topk, q_pos, n_cmp, q_idx, q_scale, w_idx,
                           k_idx, k_scale, qk_dt, idx_out, score_out, workspace};
+  a.pages = pt;
   return hip_status(csa_host::launch_indexer_topk(a, stream), "csa_indexer_topk launch");
+}
+
+csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
+                              const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
+                              const void* q_scale, const float* w_idx, const void* k_idx,
+                              const void* k_scale, csa_dtype_t qk_dt, int32_t* idx_out,
+                              float* score_out, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  return indexer_impl(B, T, H_I, d_I, Nc_cap, m, topk, q_pos, n_cmp, q_idx, q_scale, w_idx, k_idx,
+                      k_scale, qk_dt, idx_out, score_out, workspace, ws_bytes, stream, nullptr);
+}
+
+csa_status_t csa_indexer_topk_paged(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
+                                    const int64_t* q_pos, const int32_t* n_cmp,
+                                    const void* q_idx, const void* q_scale, const float* w_idx,
+                                    const void* k_idx, const void* k_scale, csa_dtype_t qk_dt,
+                                    const csa_page_table_t* pages, int32_t* idx_out,
+                                    float* score_out, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!pages) return fail(CSA_E_ARG, "csa_indexer_topk_paged: pages is required");
+  return indexer_impl(B, T, H_I, d_I, Nc_cap, m, topk, q_pos, n_cmp, q_idx, q_scale, w_idx, k_idx,
+                      k_scale, qk_dt, idx_out, score_out, workspace, ws_bytes, stream, pages);
 }
 
 static csa_status_t check_attn(const char* fn, int B, int T, int H, int D, int window,
@@ -166,26 +247,65 @@ size_t csa_sparse_attn_workspace_size(int B, int T, int H, int D, int topk, int 
   return csa_host::attn_ws_bytes(B, T, H, D, topk + window, true);
 }
 
-csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, float scale,
-                             const float* sink, const int64_t* q_pos, const void* q,
-                             const void* kv_cmp, int Nc_cap,
-                             const int32_t* idx, const void* kv_raw, int R_cap,
-                             const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
-                             void* workspace, size_t ws_bytes, hipStream_t stream) {
-  csa_status_t st = check_attn("csa_sparse_attn", B, T, H, D, window, q_pos, q, kv_cmp, Nc_cap,
-                               kv_raw, R_cap, raw_base, dt, out);
+size_t csa_sparse_attn_paged_workspace_size(int B, int T, int H, int D, int topk, int window) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || topk < 0) return 0;
+  return csa_host::attn_ws_bytes(B, T, H, D, topk + window, true) +
+         (size_t)B * T * topk * sizeof(int32_t);
+}
+
+static csa_status_t sparse_attn_impl(int B, int T, int H, int D, int topk, int window,
+                                     float scale, const float* sink, const int64_t* q_pos,
+                                     const void* q, const void* kv_cmp, int Nc_cap,
+                                     const int32_t* idx, const void* kv_raw, int R_cap,
+                                     const int64_t* raw_base, csa_dtype_t dt, void* out,
+                                     float* lse, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream, const csa_page_table_t* pages) {
+  csa::PageTable pt;
+  csa_status_t st = check_pages("csa_sparse_attn", pages, Nc_cap, pt);
+  if (st != CSA_OK) return st;
+  // a paged kv_cmp is the pool: its row count is what the kernels bound
+  const int cmp_rows =
+      pages ? (int)std::min<int64_t>((int64_t)pages->n_pages * pages->page_size, INT32_MAX)
+            : Nc_cap;
+  st = check_attn("csa_sparse_attn", B, T, H, D, window, q_pos, q, kv_cmp, cmp_rows, kv_raw,
+                  R_cap, raw_base, dt, out);
   if (st != CSA_OK) return st;
   if (topk < 0) return fail(CSA_E_ARG, "csa_sparse_attn: topk must be >= 0");
   if (topk > 0 && !idx) return fail(CSA_E_ARG, "csa_sparse_attn: idx is required when topk > 0");
   if (dt == CSA_DT_BF16 && !csa_host::attn_supported(B, T, H, topk + window, true))
     return fail(CSA_E_UNSUPPORTED, "csa_sparse_attn: topk + window too large for %d rows", B * T);
   const size_t need =
-      dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, topk + window, true);
+      pages ? csa_sparse_attn_paged_workspace_size(B, T, H, D, topk, window)
+            : (dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, topk + window, true));
   if (ws_bytes < need || (need && !workspace))
     return fail(CSA_E_WORKSPACE, "csa_sparse_attn: workspace %zu < %zu bytes", ws_bytes, need);
   csa_host::AttnArgs a{B, T, H, D, topk, window, 1, Nc_cap, R_cap, false, scale, sink, q_pos,
                        nullptr, q, kv_cmp, idx, kv_raw, raw_base, dt, out, lse, workspace};
+  a.pages = pt;
   return hip_status(csa_host::launch_attn(a, stream), "csa_sparse_attn launch");
+}
+
+csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, float scale,
+                             const float* sink, const int64_t* q_pos, const void* q,
+                             const void* kv_cmp, int Nc_cap,
+                             const int32_t* idx, const void* kv_raw, int R_cap,
+                             const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return sparse_attn_impl(B, T, H, D, topk, window, scale, sink, q_pos, q, kv_cmp, Nc_cap, idx,
+                          kv_raw, R_cap, raw_base, dt, out, lse, workspace, ws_bytes, stream,
+                          nullptr);
+}
+
+csa_status_t csa_sparse_attn_paged(int B, int T, int H, int D, int topk, int window, float scale,
+                                   const float* sink, const int64_t* q_pos, const void* q,
+                                   const void* kv_cmp, int Nc_cap, const csa_page_table_t* pages,
+                                   const int32_t* idx, const void* kv_raw, int R_cap,
+                                   const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!pages) return fail(CSA_E_ARG, "csa_sparse_attn_paged: pages is required");
+  return sparse_attn_impl(B, T, H, D, topk, window, scale, sink, q_pos, q, kv_cmp, Nc_cap, idx,
+                          kv_raw, R_cap, raw_base, dt, out, lse, workspace, ws_bytes, stream,
+                          pages);
 }
 
 size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window) {

@@ -19,6 +19,7 @@
 //    split-K across workgroups, partials merged by log-sum-exp in a combine
 //    kernel.
 // fp32 runs a plain per-(row, head) wave kernel.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -131,7 +132,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, float scale_log2, const float* __restrict__ sink, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int64_t cmp_rows_b) {
   constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH;
   constexpr bool dense = !SPARSE;
   // phase A uses tiles 0..1 (double buffer); phase B tile r per row
@@ -155,7 +156,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   const int64_t pos = qp + t, pos_first = qp + t0, pos_last = qp + t_last;
   const int32_t ncb = n_cmp ? n_cmp[b] : 0;
   const int64_t rbase = raw_base[b];
-  const uint16_t* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
+  const uint16_t* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
   const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
   const size_t rowi = (size_t)b * T + (active ? t : t_last);
 
@@ -426,7 +427,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, bool dense, float scale_log2, const float* __restrict__ sink, int n_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, int64_t cmp_rows_b) {
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
   constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
@@ -454,7 +455,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   const int kb = ta * DC_KT;
   const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
   const uint16_t* dummy = q + (size_t)rowi * H * D;  // a valid row for empty slots
-  const char* cbase = Nc_cap > 0 ? (const char*)(kv_cmp + (size_t)b * Nc_cap * 2 * D)
+  const char* cbase = Nc_cap > 0 ? (const char*)(kv_cmp + (size_t)b * cmp_rows_b * 2 * D)
                                  : (const char*)dummy;
   const char* wbase = R_cap > 0 ? (const char*)(kv_raw + (size_t)b * R_cap * 2 * D)
                                 : (const char*)dummy;
@@ -709,7 +710,8 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
     const float* __restrict__ kv_raw, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, const int64_t* __restrict__ raw_base, int T, int H, int D,
     int topk, int window, int m, int Nc_cap, int R_cap, bool dense, float scale_log2,
-    const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse) {
+    const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse,
+    int64_t cmp_rows_b) {
   const int lane = threadIdx.x;
   const int rowi = blockIdx.x / H, h = blockIdx.x % H;
   const int b = rowi / T, t = rowi % T;
@@ -717,7 +719,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
   const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
   const int nk = L.n_c + L.n_w;
   const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
-  const float* kvc_b = kv_cmp + (size_t)b * Nc_cap * 2 * D;
+  const float* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
   const float* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
   const int64_t rbase = raw_base[b];
   const float* qr = q + ((size_t)rowi * H + h) * D;
@@ -743,6 +745,18 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
   if (lane < D) orow[lane] = o0 * inv;
   if (lane + 64 < D) orow[lane + 64] = o1 * inv;
   if (lse && lane == 0) lse[(size_t)rowi * H + h] = lse_v;
+}
+
+// Selected logical entries of a paged compressed cache to pool rows (-1
+// stays -1, as does an index outside [0, Nc_cap)); rows of topk slots.
+__global__ void page_index_kernel(const int32_t* __restrict__ idx, size_t n, int T, int topk,
+                                  int Nc_cap, PageTable pt, int32_t* __restrict__ phys) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int j = idx[i];
+    const int b = (int)(i / topk) / T;
+    phys[i] = (j >= 0 && j < Nc_cap) ? (int32_t)paged_row(pt, b, j) : -1;
+  }
 }
 
 }  // namespace csa
@@ -794,14 +808,29 @@ size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse) 
   return (size_t)rows * s * H * (D + 2) * sizeof(float);
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
+  AttnArgs a = a_in;
   const int rows = a.B * a.T;
   const float scale_log2 = a.scale * kLog2e;
+  int64_t cmp_rows_b = a.Nc_cap;  // rows of one sequence's compressed cache
+  if (a.pages.block_table) {
+    // paged (sparse only): the selected entries become pool rows in the
+    // workspace (after the split partials); the kernels then address the
+    // pool as one cache shared by every sequence
+    int32_t* phys = (int32_t*)((char*)a.ws + attn_ws_bytes(a.B, a.T, a.H, a.D, a.topk + a.window,
+                                                           true));
+    const size_t n = (size_t)rows * a.topk;
+    page_index_kernel<<<(unsigned)std::max<size_t>(1, std::min<size_t>((n + 255) / 256, 4096)),
+                        256, 0, st>>>(a.idx, n, a.T, a.topk, a.Nc_cap, a.pages, phys);
+    a.idx = phys;
+    a.Nc_cap = a.pages.n_pages << a.pages.page_log2;
+    cmp_rows_b = 0;
+  }
   if (a.dt == CSA_DT_F32) {
     attn_f32_kernel<<<rows * a.H, 64, 0, st>>>(
         (const float*)a.q, (const float*)a.kv_cmp, a.idx, (const float*)a.kv_raw, a.q_pos,
         a.n_cmp, a.raw_base, a.T, a.H, a.D, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-        scale_log2, a.sink, (float*)a.out, a.lse);
+        scale_log2, a.sink, (float*)a.out, a.lse, cmp_rows_b);
     return hipGetLastError();
   }
   const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
@@ -815,12 +844,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
       attn_dec_kernel<4><<<grid, 256, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b);
     else
       attn_dec_kernel<2><<<grid, 128, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml);
+          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b);
   } else {
     // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
     // rows share only the window: 2 rows, so that two independent
@@ -830,7 +859,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
                                  st>>>(                                                             \
       (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,  \
       a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, scale_log2, a.sink,      \
-      (uint16_t*)a.out, a.lse)
+      (uint16_t*)a.out, a.lse, cmp_rows_b)
     if (a.H == 64) {
       if (a.dense) CSA_LAUNCH_PF(2, 4, false);
       else CSA_LAUNCH_PF(2, 2, true);

@@ -133,6 +133,21 @@ __device__ __forceinline__ float sum_xor16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- paged compressed caches ---------------------------------------------
+// Logical entry j of sequence b lives in pool row
+//   (block_table[b * max_pages + j / 2^page_log2] * 2^page_log2) + j % 2^page_log2;
+// a null block_table means the unpaged layout [B, Nc_cap, row].  Page ids are
+// clamped into [0, n_pages) so that a stale table entry cannot leave the pool.
+struct PageTable {
+  const int32_t* block_table;
+  int page_log2, max_pages, n_pages;
+};
+__device__ __forceinline__ int64_t paged_row(const PageTable& pt, int b, int j) {
+  int pg = pt.block_table[(size_t)b * pt.max_pages + (j >> pt.page_log2)];
+  pg = min(max(pg, 0), pt.n_pages - 1);
+  return ((int64_t)pg << pt.page_log2) | (int64_t)(j & ((1 << pt.page_log2) - 1));
+}
+
 }  // namespace csa
 
 // ---- host-side launch entry points (defined in the kernel sources) --------
@@ -152,6 +167,7 @@ struct CompressArgs {
   void* out;
   void* out_scale;
   void* ws;
+  csa::PageTable pages;  // block_table null: unpaged out
 };
 size_t compress_ws_bytes(int B, int L, int d_model, int E, int m, int overlap, csa_dtype_t in_dt);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
@@ -169,6 +185,7 @@ struct IndexerArgs {
   int32_t* idx_out;
   float* score_out;
   void* ws;
+  csa::PageTable pages;  // block_table null: unpaged k_idx / k_scale
 };
 size_t indexer_ws_bytes(int B, int T, int H_I, int d_I, int Nc_cap, int topk, csa_dtype_t dt);
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
@@ -189,6 +206,7 @@ struct AttnArgs {
   void* out;
   float* lse;
   void* ws;
+  csa::PageTable pages;  // block_table null: unpaged kv_cmp (sparse only)
 };
 size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse);
 bool attn_supported(int B, int T, int H, int keys_per_row, bool sparse);

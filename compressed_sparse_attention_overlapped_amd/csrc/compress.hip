@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
     const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, void* __restrict__ out_scale,
-    int Nc_cap, int n_slots, int n_split, bool rotate, float rot_scale) {
+    int Nc_cap, int n_slots, int n_split, bool rotate, float rot_scale, PageTable pt) {
   const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
   const int ns = (1 + overlap) * m - 1;
   const int64_t p0 = pos0[b];
@@ -485,7 +485,8 @@ __global__ void __launch_bounds__(256) pool_kernel(
       amax = fmaxf(amax, fabsf(vals[nv]));
     }
   }
-  const size_t orow = (size_t)b * Nc_cap + (size_t)i;
+  const size_t orow =
+      pt.block_table ? (size_t)paged_row(pt, b, i) : (size_t)b * Nc_cap + (size_t)i;
   if (OUT_DT == CSA_DT_F32) {
     nv = 0;
     for (int e = tid; e < E; e += blockDim.x, ++nv) ((float*)out)[orow * E + e] = vals[nv];
@@ -580,7 +581,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
 #define CSA_LAUNCH_POOL(DT, W, NS)                                                              \
   pool_kernel<DT, W, NS><<<pgrid, pthreads, 0, st>>>(                                           \
       pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,           \
-      a.out_scale, a.Nc_cap, n_slots, splits, a.rotate != 0, (float)(1.0 / std::sqrt((double)E)))
+      a.out_scale, a.Nc_cap, n_slots, splits, a.rotate != 0, (float)(1.0 / std::sqrt((double)E)), \
+      a.pages)
 #define CSA_POOL_DT(DT)                            \
   if (w8 == 1) CSA_LAUNCH_POOL(DT, 8, 1);          \
   else if (w8 == 4) CSA_LAUNCH_POOL(DT, 8, 4);     \

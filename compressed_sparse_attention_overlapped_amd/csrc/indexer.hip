@@ -307,13 +307,13 @@ __device__ __forceinline__ float e8m0_value(uint32_t code) {
 // per head row, k_scale per entry).  QK = CSA_DT_MXFP4: rows of 32 bytes of
 // E2M1 codes with two E8M0 block scales each; lane l then loads 8 bytes (the
 // same 16 dims as above) and its block's scale byte.
-template <bool HIST, int QK>
+template <bool HIST, int QK, bool PAGED>
 __global__ void __launch_bounds__(256) score_fp8_kernel(
     const uint8_t* __restrict__ q_idx, const void* __restrict__ q_scale,
     const float* __restrict__ w_idx, const uint8_t* __restrict__ k_idx,
     const void* __restrict__ k_scale, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, float* __restrict__ scores,
-    uint32_t* __restrict__ ghist) {
+    uint32_t* __restrict__ ghist, PageTable pt) {
   constexpr bool FP4 = QK == CSA_DT_MXFP4;
   constexpr int KB = FP4 ? 32 : 64;  // code bytes per row of 64 values
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
@@ -350,9 +350,13 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
       wq[i] = w_idx[(size_t)row * 16 + hh] *
               (FP4 ? 1.0f : ((const float*)q_scale)[(size_t)row * 16 + hh]);
     }
-    const uint8_t* kb = k_idx + (size_t)b * Nc_cap * KB;
-    const float* ks = FP4 ? nullptr : (const float*)k_scale + (size_t)b * Nc_cap;
-    const uint8_t* ks8 = FP4 ? (const uint8_t*)k_scale + (size_t)b * Nc_cap * 2 : nullptr;
+    // paged caches: the rows sit in a shared pool (16 consecutive entries,
+    // one load group, never straddle a page)
+    const size_t kbase = PAGED ? 0 : (size_t)b * Nc_cap;
+    auto krow = [&](int j) -> size_t { return PAGED ? (size_t)paged_row(pt, b, j) : (size_t)j; };
+    const uint8_t* kb = k_idx + kbase * KB;
+    const float* ks = FP4 ? nullptr : (const float*)k_scale + kbase;
+    const uint8_t* ks8 = FP4 ? (const uint8_t*)k_scale + kbase * 2 : nullptr;
     float* srow = scores + (size_t)row * Nc_cap;
     // two register stages: the codes of step i + 2 load while step i computes
     u32x4 kv[2][SF_UNROLL];
@@ -363,18 +367,20 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
       for (int u = 0; u < SF_UNROLL; ++u) {
         const int j = wb + it * kStep + 16 * u + (lane & 15);
         if constexpr (FP4) {
-          const u32x2 w = j < we ? __builtin_nontemporal_load((const u32x2*)(kb + (size_t)j * 32 + 8 * g))
+          const size_t r = j < we ? krow(j) : 0;
+          const u32x2 w = j < we ? __builtin_nontemporal_load((const u32x2*)(kb + r * 32 + 8 * g))
                                  : u32x2{0, 0};
-          kv[st][u] = u32x4{w[0], w[1], j < we ? (uint32_t)ks8[(size_t)j * 2 + (g >> 1)] : 127u, 0u};
+          kv[st][u] = u32x4{w[0], w[1], j < we ? (uint32_t)ks8[r * 2 + (g >> 1)] : 127u, 0u};
         } else {
-          kv[st][u] = j < we ? __builtin_nontemporal_load((const u32x4*)(kb + (size_t)j * 64 + 16 * g))
+          const size_t r = j < we ? krow(j) : 0;
+          kv[st][u] = j < we ? __builtin_nontemporal_load((const u32x4*)(kb + r * 64 + 16 * g))
                              : u32x4{0, 0, 0, 0};
         }
       }
 #pragma unroll
       for (int hf = 0; hf < SF_UNROLL / 4; ++hf) {
         const int j = wb + it * kStep + 64 * hf + lane;
-        ksc[st][hf] = FP4 ? 1.0f : (j < we ? ks[j] : 0.0f);
+        ksc[st][hf] = FP4 ? 1.0f : (j < we ? ks[krow(j)] : 0.0f);
       }
     };
     load(0, 0);
@@ -1046,15 +1052,26 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   } else {
     dim3 g((a.Nc_cap + kChunk - 1) / kChunk, rows);
 #define CSA_LAUNCH_SF(HS, QK)                                                                 \
-  score_fp8_kernel<HS, QK><<<g, 256, 0, st>>>((const uint8_t*)a.q_idx, a.q_scale, a.w_idx,   \
-                                              (const uint8_t*)a.k_idx, a.k_scale, a.q_pos,   \
-                                              a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist)
+  if (a.pages.block_table)                                                                    \
+    score_fp8_kernel<HS, QK, true><<<g, 256, 0, st>>>(                                        \
+        (const uint8_t*)a.q_idx, a.q_scale, a.w_idx, (const uint8_t*)a.k_idx, a.k_scale,      \
+        a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist, a.pages);                         \
+  else                                                                                        \
+    score_fp8_kernel<HS, QK, false><<<g, 256, 0, st>>>(                                       \
+        (const uint8_t*)a.q_idx, a.q_scale, a.w_idx, (const uint8_t*)a.k_idx, a.k_scale,      \
+        a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist, a.pages)
     if (a.dt == CSA_DT_MXFP4) {
-      if (L.long_rows) CSA_LAUNCH_SF(true, CSA_DT_MXFP4);
-      else CSA_LAUNCH_SF(false, CSA_DT_MXFP4);
+      if (L.long_rows) {
+        CSA_LAUNCH_SF(true, CSA_DT_MXFP4);
+      } else {
+        CSA_LAUNCH_SF(false, CSA_DT_MXFP4);
+      }
     } else {
-      if (L.long_rows) CSA_LAUNCH_SF(true, CSA_DT_FP8E4M3);
-      else CSA_LAUNCH_SF(false, CSA_DT_FP8E4M3);
+      if (L.long_rows) {
+        CSA_LAUNCH_SF(true, CSA_DT_FP8E4M3);
+      } else {
+        CSA_LAUNCH_SF(false, CSA_DT_FP8E4M3);
+      }
     }
 #undef CSA_LAUNCH_SF
   }

@@ -202,6 +202,76 @@ csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float
 size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window);
 
 /* Static text of a status code. */
+/*
+ * Paged compressed caches (serving-shaped storage: the million-token CSA/HCA
+ * article, section 8.3, lists paged-attention style cache management for
+ * the compressed caches among the serving adaptations; the CSA migration
+ * analysis, section 5, lists packed variable-length batches).
+ * Instead of one [B, Nc_cap, row] tensor, the compressed entries of every
+ * sequence live in a shared pool of n_pages pages of page_size rows each;
+ * logical entry j of sequence b is pool row
+ *     block_table[b * max_pages + j / page_size] * page_size + j % page_size.
+ *  block_table  device int32 [B, max_pages], read-only; entries past a
+ *               sequence's last used page are not read.  A page id outside
+ *               [0, n_pages) is clamped into it (no fault; the caller's
+ *               table is wrong then)
+ *  page_size    rows per page, a power of two in [16, 2^20]
+ *  max_pages    row stride of block_table; Nc_cap <= max_pages * page_size
+ *  n_pages      pages in the pool (pool rows = n_pages * page_size)
+ * The struct is read on the host during the call; the caller owns it and the
+ * table.  Errors: CSA_E_ARG for a missing table or a bad size.
+ */
+typedef struct {
+  const int32_t* block_table;
+  int page_size;
+  int max_pages;
+  int n_pages;
+} csa_page_table_t;
+
+/*
+ * csa_compress with a paged output: out (and out_scale) are pools of
+ * n_pages * page_size rows in the layouts above ([rows, E] in out_dt,
+ * [rows] fp32 scales for FP8E4M3, [rows, E / 32] E8M0 bytes for MXFP4);
+ * entry i of sequence b goes to its pool row.  Everything else is as in
+ * csa_compress (the same workspace size).
+ */
+csa_status_t csa_compress_paged(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                                const int64_t* pos0, const void* x, const void* w_kv,
+                                const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                                const float* state_in, float* state_out, void* out,
+                                void* out_scale, csa_dtype_t out_dt, int Nc_cap,
+                                const csa_page_table_t* pages, void* workspace, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
+ * csa_indexer_topk over paged keys: k_idx and k_scale are pools (FP8E4M3:
+ * [rows, d_I] codes and [rows] fp32 scales; MXFP4: [rows, d_I / 2] bytes and
+ * [rows, d_I / 32] E8M0 scales).  Indices in idx_out stay logical (0 ..
+ * Nc_cap - 1).  qk_dt FP8E4M3 or MXFP4 only (else CSA_E_UNSUPPORTED); the
+ * workspace is csa_indexer_topk_workspace_size().
+ */
+csa_status_t csa_indexer_topk_paged(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
+                                    const int64_t* q_pos, const int32_t* n_cmp,
+                                    const void* q_idx, const void* q_scale, const float* w_idx,
+                                    const void* k_idx, const void* k_scale, csa_dtype_t qk_dt,
+                                    const csa_page_table_t* pages, int32_t* idx_out,
+                                    float* score_out, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/*
+ * csa_sparse_attn over a paged kv_cmp pool ([rows, 2 D]); idx holds logical
+ * indices as csa_indexer_topk writes them.  The workspace is
+ * csa_sparse_attn_paged_workspace_size() bytes (it also holds the selected
+ * entries' pool rows).  BF16 pools hold at most 2^23 rows.
+ */
+csa_status_t csa_sparse_attn_paged(int B, int T, int H, int D, int topk, int window, float scale,
+                                   const float* sink, const int64_t* q_pos, const void* q,
+                                   const void* kv_cmp, int Nc_cap, const csa_page_table_t* pages,
+                                   const int32_t* idx, const void* kv_raw, int R_cap,
+                                   const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t csa_sparse_attn_paged_workspace_size(int B, int T, int H, int D, int topk, int window);
+
 const char* csa_status_string(csa_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* csa_last_error(void);

@@ -102,3 +102,42 @@ def test_argument_errors_are_reported_without_launch(L):
     rc = L.hca_dense_attn(1, 1, 64, 128, 128, 4, C.c_float(1.0), None, dummy, None, dummy, dummy,
                           4, dummy, 4, dummy, 1, dummy, None, None, 0, None)
     assert rc == 1
+
+
+def _PT(block_table, page_size, max_pages, n_pages):
+    import compressed_sparse_attention_overlapped_amd as csa
+    return csa._CPageTable(block_table, page_size, max_pages, n_pages)
+
+
+def test_paged_entry_points_validate_the_page_table(L):
+    vp = C.c_void_p
+    dummy = vp(16)   # never dereferenced: validation fails first
+    import compressed_sparse_attention_overlapped_amd as csa
+    csa.lib()        # argtypes for the paged entry points
+
+    def compress(pt):
+        return L.csa_compress_paged(1, 1, 64, 8, 4, 1, 0, dummy, dummy, dummy, dummy, 0, None, None,
+                                    None, dummy, None, 0, 100, pt, dummy, 1 << 20, None)
+    rc = compress(None)
+    assert rc == 1 and b"pages is required" in L.csa_last_error()
+    rc = compress(C.byref(_PT(None, 64, 4, 4)))
+    assert rc == 1 and b"block_table" in L.csa_last_error()
+    rc = compress(C.byref(_PT(16, 24, 8, 8)))
+    assert rc == 1 and b"power of two" in L.csa_last_error()
+    rc = compress(C.byref(_PT(16, 8, 16, 16)))          # below the 16-row minimum
+    assert rc == 1 and b"power of two" in L.csa_last_error()
+    rc = compress(C.byref(_PT(16, 16, 4, 8)))           # 64 logical rows < Nc_cap 100
+    assert rc == 1 and b"exceeds" in L.csa_last_error()
+    # paged indexer keys must be fp8 or mxfp4
+    rc = L.csa_indexer_topk_paged(1, 1, 16, 64, 100, 4, 10, dummy, dummy, dummy, None, dummy,
+                                  dummy, None, 1, C.byref(_PT(16, 64, 2, 2)), dummy, None, dummy,
+                                  1 << 30, None)
+    assert rc == 2 and b"FP8E4M3 or MXFP4" in L.csa_last_error()
+    # paged attention: the workspace also holds the pool rows of the selection
+    a = L.csa_sparse_attn_paged_workspace_size(2, 1, 64, 128, 512, 128)
+    b = L.csa_sparse_attn_workspace_size(2, 1, 64, 128, 512, 128)
+    assert a == b + 2 * 512 * 4
+    rc = L.csa_sparse_attn_paged(1, 1, 64, 128, 4, 4, C.c_float(1.0), None, dummy, dummy, dummy, 64,
+                                 None, dummy, dummy, 4, dummy, 1, dummy, None, dummy, 1 << 30,
+                                 None)
+    assert rc == 1 and b"pages is required" in L.csa_last_error()
