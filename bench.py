@@ -247,6 +247,26 @@ def setup_decode(w):
     st["out"] = torch.empty(B, 1, w.H, w.D, device=DEV, dtype=torch.bfloat16)
     st["ws_i"] = torch.empty(max(1, csa.csa_indexer_topk_workspace_size(B, 1, w.H_I, w.d_I, w.n_cmp, w.topk, torch.float8_e4m3fn)), dtype=torch.uint8, device=DEV)
     st["ws_a"] = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(B, 1, w.H, w.D, w.topk, w.window)), dtype=torch.uint8, device=DEV)
+    st["pages"] = None
+    if w.page:
+        # paged compressed caches: every sequence's pages shuffled over one
+        # pool (untimed setup); the step reads them through the block table
+        P, n = w.page, -(-w.n_cmp // w.page)
+        n_pages = B * n
+        table = torch.randperm(n_pages, generator=torch.Generator().manual_seed(w.seed))
+        table = table.to(torch.int32).view(B, n).to(DEV)
+        j = torch.arange(w.n_cmp, device=DEV)
+        rows = (table[:, j // P].long() * P + j % P).reshape(-1)
+        for k in ("kv_cmp", "k_idx", "k_scale"):
+            t = st[k]
+            feat = tuple(t.shape[2:]) or (1,)
+            pool = torch.empty((n_pages * P,) + feat, dtype=t.dtype, device=DEV)
+            pool.view(torch.uint8)[rows] = t.reshape((-1,) + feat).view(torch.uint8)
+            st[k] = pool if t.dim() > 2 else pool.view(-1)
+            del t
+        st["pages"] = csa.PageTable(table, P, n_pages, nc_cap=w.n_cmp)
+        st["ws_a"] = torch.empty(csa.lib().csa_sparse_attn_paged_workspace_size(B, 1, w.H, w.D, w.topk, w.window), dtype=torch.uint8, device=DEV)
+        torch.cuda.synchronize()
     if stream:
         ns = 2 * w.m - 1
         for k, E in (("main", 2 * w.D), ("idx", w.d_I)):
@@ -281,11 +301,12 @@ def step_decode(w, st):
             tm.mark(i)
         csa.csa_indexer_topk(st["q_idx"], st["w_idx"], st["k_idx"], w.m, w.topk, st["q_pos"],
                              st["ncmp"], q_scale=st["q_scale"], k_scale=st["k_scale"],
-                             idx_out=st["idx"], workspace=st["ws_i"])
+                             idx_out=st["idx"], workspace=st["ws_i"], pages=st["pages"])
         i += 1
         tm.mark(i)
         csa.csa_sparse_attn(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"], w.window, st["q_pos"],
-                            st["raw_base"], out=st["out"], workspace=st["ws_a"])
+                            st["raw_base"], out=st["out"], workspace=st["ws_a"],
+                            pages=st["pages"])
         i += 1
         tm.mark(i)
     names = (["compress"] if stream else []) + ["indexer_topk", "sparse_attn"]

@@ -427,7 +427,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, bool dense, float scale_log2, const float* __restrict__ sink, int n_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int64_t cmp_rows_b) {
+    float* __restrict__ part_ml, int64_t cmp_rows_b, PageTable pt, int nc_logical) {
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
   constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
@@ -471,6 +471,10 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + u * NT + tid;
         v[u] = i < c_hi - c_lo ? idx_row[c_lo + i] : 0;
+      }
+      if (pt.block_table) {  // paged: logical entries to pool rows
+        for (int u = 0; u < 4; ++u)
+          v[u] = (v[u] >= 0 && v[u] < nc_logical) ? (int)paged_row(pt, b, v[u]) : -1;
       }
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + u * NT + tid;
@@ -813,7 +817,14 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
   const int rows = a.B * a.T;
   const float scale_log2 = a.scale * kLog2e;
   int64_t cmp_rows_b = a.Nc_cap;  // rows of one sequence's compressed cache
-  if (a.pages.block_table) {
+  const int nc_logical = a.Nc_cap;
+  PageTable dec_pages{nullptr, 0, 0, 0};
+  if (a.pages.block_table && a.dt != CSA_DT_F32 && use_decode_kernel(rows, a.H)) {
+    // paged decode rows: the kernel maps each staged index to its pool row
+    dec_pages = a.pages;
+    a.Nc_cap = a.pages.n_pages << a.pages.page_log2;
+    cmp_rows_b = 0;
+  } else if (a.pages.block_table) {
     // paged (sparse only): the selected entries become pool rows in the
     // workspace (after the split partials); the kernels then address the
     // pool as one cache shared by every sequence
@@ -844,12 +855,14 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
       attn_dec_kernel<4><<<grid, 256, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b);
+          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
+          dec_pages, nc_logical);
     else
       attn_dec_kernel<2><<<grid, 128, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b);
+          scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
+          dec_pages, nc_logical);
   } else {
     // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
     // rows share only the window: 2 rows, so that two independent

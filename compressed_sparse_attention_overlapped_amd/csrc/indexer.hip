@@ -317,14 +317,24 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
   constexpr bool FP4 = QK == CSA_DT_MXFP4;
   constexpr int KB = FP4 ? 32 : 64;  // code bytes per row of 64 values
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+  // paged caches: the chunk's page ids (pages of at least 16 entries), read
+  // once so that a key load waits on LDS rather than on the block table
+  __shared__ int32_t pg_s[PAGED ? kChunk / 16 + 1 : 1];
   const int row = blockIdx.y, b = row / T, t = row % T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const int jb = blockIdx.x * kChunk;
+  const int p_first = PAGED ? jb >> pt.page_log2 : 0;
+  if (PAGED) {
+    const int n_pg = ((min(jb + kChunk, Nc_cap) - 1) >> pt.page_log2) - p_first + 1;
+    for (int i = tid; i < n_pg; i += blockDim.x)
+      pg_s[i] = min(max(pt.block_table[(size_t)b * pt.max_pages + p_first + i], 0),
+                    pt.n_pages - 1);
+  }
   if (HIST) {
     for (int i = tid; i < kHistBins; i += blockDim.x) lhist[i] = 0;
-    __syncthreads();
   }
+  if (HIST || PAGED) __syncthreads();
   const int je = min(nv, jb + kChunk);
   // this wave's entries: [wb, we), in SF_ITERS steps of 16 * SF_UNROLL
   constexpr int kPerWave = kChunk / 4, kStep = 16 * SF_UNROLL, SF_ITERS = kPerWave / kStep;
@@ -353,7 +363,12 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
     // paged caches: the rows sit in a shared pool (16 consecutive entries,
     // one load group, never straddle a page)
     const size_t kbase = PAGED ? 0 : (size_t)b * Nc_cap;
-    auto krow = [&](int j) -> size_t { return PAGED ? (size_t)paged_row(pt, b, j) : (size_t)j; };
+    auto krow = [&](int j) -> size_t {
+      if constexpr (PAGED)
+        return ((size_t)pg_s[(j >> pt.page_log2) - p_first] << pt.page_log2) |
+               (size_t)(j & ((1 << pt.page_log2) - 1));
+      return (size_t)j;
+    };
     const uint8_t* kb = k_idx + kbase * KB;
     const float* ks = FP4 ? nullptr : (const float*)k_scale + kbase;
     const uint8_t* ks8 = FP4 ? (const uint8_t*)k_scale + kbase * 2 : nullptr;

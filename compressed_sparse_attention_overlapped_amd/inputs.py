@@ -49,6 +49,7 @@ class Workload:
     tail: int = 0        # tokens streamed into the compressor state before the step
     n_cmp: int = 0       # compressed entries held in the cache for the step
     seed: int = 1000
+    page: int = 0        # paged compressed caches: entries per page (0: unpaged)
 
 
 WORKLOADS = {
@@ -69,6 +70,12 @@ WORKLOADS = {
                                           ctx=131072, T=1, H=64, D=128, m=4, overlap=1,
                                           window=512, topk=2048, H_I=16, d_I=64, dt=BF16,
                                           idx_dt=MXFP4, n_cmp=32768, seed=1006),
+    # the e4m3 128K decode with paged compressed caches (256-entry pages,
+    # shuffled over the pool)
+    "csa_decode_128k_b32_paged": Workload("csa_decode_128k_b32_paged", "csa_decode", B=32,
+                                          ctx=131072, T=1, H=64, D=128, m=4, overlap=1,
+                                          window=512, topk=2048, H_I=16, d_I=64, dt=BF16,
+                                          idx_dt=FP8, n_cmp=32768, seed=1003, page=256),
     # HCA prefill chunk of 4096 tokens at the tail of a 1M context
     "hca_prefill_1m_chunk4k": Workload("hca_prefill_1m_chunk4k", "hca_prefill", B=1, ctx=1 << 20,
                                        T=4096, H=64, D=128, m=128, overlap=0, window=512,
