@@ -188,8 +188,8 @@ static csa_status_t indexer_impl(int B, int T, int H_I, int d_I, int Nc_cap, int
   csa::PageTable pt;
   const csa_status_t pst = check_pages("csa_indexer_topk", pages, Nc_cap, pt);
   if (pst != CSA_OK) return pst;
-  if (pages && qk_dt != CSA_DT_FP8E4M3 && qk_dt != CSA_DT_MXFP4)
-    return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_paged: paged keys need FP8E4M3 or MXFP4");
+  if (pages && qk_dt == CSA_DT_F32)
+    return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_paged: paged keys need BF16, FP8E4M3 or MXFP4");
   csa_host::IndexerArgs a{B, T, H_I, d_I, Nc_cap, m, topk, q_pos, n_cmp, q_idx, q_scale, w_idx,
                           k_idx, k_scale, qk_dt, idx_out, score_out, workspace};
   a.pages = pt;

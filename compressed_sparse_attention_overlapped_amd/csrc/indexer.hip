@@ -135,14 +135,16 @@ __device__ __forceinline__ float relu_bits(float x) {
 // chunk of entries; 64-entry key tiles are staged in LDS for all waves.
 constexpr int SB_ROWS = 16, SB_KT = 64, SB_KSTRIDE = 64 + 8;  // bf16 per LDS key row
 
-template <bool HIST>
+template <bool HIST, bool PAGED>
 __global__ void __launch_bounds__(256) score_bf16_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int key_chunk,
-    float* __restrict__ scores, uint32_t* __restrict__ ghist) {
+    float* __restrict__ scores, uint32_t* __restrict__ ghist, PageTable pt) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][SB_KT * SB_KSTRIDE];
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+  // paged caches: the chunk's page ids (pages of at least 16 entries)
+  __shared__ int32_t pg_s[PAGED ? kChunk / 16 + 1 : 1];
   // later rows see more entries: they are dispatched first
   const int b = blockIdx.z, t0 = (gridDim.x - 1 - blockIdx.x) * SB_ROWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -156,6 +158,13 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
 
   if (HIST) {
     for (int i = tid; i < kHistBins; i += blockDim.x) lhist[i] = 0;
+  }
+  const int p_first = PAGED ? jb >> pt.page_log2 : 0;
+  if (PAGED && jb < Nc_cap) {
+    const int n_pg = ((min(jb + key_chunk, Nc_cap) - 1) >> pt.page_log2) - p_first + 1;
+    for (int i = tid; i < n_pg; i += blockDim.x)
+      pg_s[i] = min(max(pt.block_table[(size_t)b * pt.max_pages + p_first + i], 0),
+                    pt.n_pages - 1);
   }
   // A operands: rows (token, head) -> lane row (lane & 31) of tile mt:
   // token = wave*4 + mt*2 + (lane&31)/16, head = lane & 15; k-step s covers
@@ -199,7 +208,11 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     for (int i = 0; i < 2; ++i) {
       const int c = i * 256 + tid, r = c >> 3, q8 = c & 7;
       const int row = min(j0 + r, je - 1);
-      pk[i] = *(const u32x4*)(k_idx + ((size_t)b * Nc_cap + row) * 64 + q8 * 8);
+      size_t at = (size_t)b * Nc_cap + row;
+      if constexpr (PAGED)
+        at = ((size_t)pg_s[(row >> pt.page_log2) - p_first] << pt.page_log2) |
+             (size_t)(row & ((1 << pt.page_log2) - 1));
+      pk[i] = *(const u32x4*)(k_idx + at * 64 + q8 * 8);
     }
   };
   auto storek = [&](int buf) {
@@ -1053,17 +1066,23 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     // growth of the visible range spreads over more, smaller workgroups
     const int key_chunk = L.long_rows ? kChunk : std::min(a.Nc_cap, 512);
     dim3 g((a.T + SB_ROWS - 1) / SB_ROWS, (a.Nc_cap + key_chunk - 1) / key_chunk, a.B);
+#define CSA_LAUNCH_SB(HS)                                                                     \
+  if (a.pages.block_table)                                                                    \
+    score_bf16_kernel<HS, true><<<g, 256, 0, st>>>(                                           \
+        (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,   \
+        a.Nc_cap, a.m, key_chunk, scores, hist, a.pages);                                      \
+  else                                                                                        \
+    score_bf16_kernel<HS, false><<<g, 256, 0, st>>>(                                          \
+        (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,   \
+        a.Nc_cap, a.m, key_chunk, scores, hist, a.pages)
     if (L.long_rows) {
       // rows of a workgroup must share a histogram: only T == 1 qualifies
       if (a.T != 1) return hipErrorNotSupported;
-      score_bf16_kernel<true><<<g, 256, 0, st>>>((const uint16_t*)a.q_idx, a.w_idx,
-                                                 (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,
-                                                 a.Nc_cap, a.m, key_chunk, scores, hist);
+      CSA_LAUNCH_SB(true);
     } else {
-      score_bf16_kernel<false><<<g, 256, 0, st>>>((const uint16_t*)a.q_idx, a.w_idx,
-                                                  (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,
-                                                  a.Nc_cap, a.m, key_chunk, scores, hist);
+      CSA_LAUNCH_SB(false);
     }
+#undef CSA_LAUNCH_SB
   } else {
     dim3 g((a.Nc_cap + kChunk - 1) / kChunk, rows);
 #define CSA_LAUNCH_SF(HS, QK)                                                                 \

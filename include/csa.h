@@ -244,11 +244,12 @@ csa_status_t csa_compress_paged(int B, int L, int d_model, int E, int m, int ove
                                 hipStream_t stream);
 
 /*
- * csa_indexer_topk over paged keys: k_idx and k_scale are pools (FP8E4M3:
- * [rows, d_I] codes and [rows] fp32 scales; MXFP4: [rows, d_I / 2] bytes and
- * [rows, d_I / 32] E8M0 scales).  Indices in idx_out stay logical (0 ..
- * Nc_cap - 1).  qk_dt FP8E4M3 or MXFP4 only (else CSA_E_UNSUPPORTED); the
- * workspace is csa_indexer_topk_workspace_size().
+ * csa_indexer_topk over paged keys: k_idx and k_scale are pools (BF16:
+ * [rows, d_I]; FP8E4M3: [rows, d_I] codes and [rows] fp32 scales; MXFP4:
+ * [rows, d_I / 2] bytes and [rows, d_I / 32] E8M0 scales).  Indices in
+ * idx_out stay logical (0 .. Nc_cap - 1).  qk_dt BF16, FP8E4M3 or MXFP4
+ * (F32: CSA_E_UNSUPPORTED); the workspace is
+ * csa_indexer_topk_workspace_size().
  */
 csa_status_t csa_indexer_topk_paged(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
                                     const int64_t* q_pos, const int32_t* n_cmp,

@@ -128,11 +128,11 @@ def test_paged_entry_points_validate_the_page_table(L):
     assert rc == 1 and b"power of two" in L.csa_last_error()
     rc = compress(C.byref(_PT(16, 16, 4, 8)))           # 64 logical rows < Nc_cap 100
     assert rc == 1 and b"exceeds" in L.csa_last_error()
-    # paged indexer keys must be fp8 or mxfp4
-    rc = L.csa_indexer_topk_paged(1, 1, 16, 64, 100, 4, 10, dummy, dummy, dummy, None, dummy,
-                                  dummy, None, 1, C.byref(_PT(16, 64, 2, 2)), dummy, None, dummy,
+    # paged indexer keys must be bf16, fp8 or mxfp4 (an fp32 call is refused before launch)
+    rc = L.csa_indexer_topk_paged(1, 1, 4, 32, 100, 4, 10, dummy, dummy, dummy, None, dummy,
+                                  dummy, None, 0, C.byref(_PT(16, 64, 2, 2)), dummy, None, dummy,
                                   1 << 30, None)
-    assert rc == 2 and b"FP8E4M3 or MXFP4" in L.csa_last_error()
+    assert rc == 2 and b"BF16, FP8E4M3 or MXFP4" in L.csa_last_error()
     # paged attention: the workspace also holds the pool rows of the selection
     a = L.csa_sparse_attn_paged_workspace_size(2, 1, 64, 128, 512, 128)
     b = L.csa_sparse_attn_workspace_size(2, 1, 64, 128, 512, 128)

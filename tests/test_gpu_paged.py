@@ -53,7 +53,7 @@ def _same_bits(a, b, what):
     assert torch.equal(_bytes(a), _bytes(b)), what
 
 
-@pytest.mark.parametrize("fmt", [gen.FP8, gen.MXFP4])
+@pytest.mark.parametrize("fmt", [gen.BF16, gen.FP8, gen.MXFP4])
 @pytest.mark.parametrize("P", [16, 256])
 @pytest.mark.parametrize("Nc,T", [(3000, 3), (20000, 1)])
 def test_paged_indexer_matches_unpaged_and_oracle(fmt, P, Nc, T):
@@ -64,16 +64,17 @@ def test_paged_indexer_matches_unpaged_and_oracle(fmt, P, Nc, T):
     q_pos = [4 * Nc, 4 * (Nc // 3) + 1, 4 * 200]
     n_cmp = [Nc, Nc - 9, Nc]
     args = (dev_i64(q_pos), dev_i32(n_cmp))
+    dev = lambda t: None if t is None else t.to(DEV)
     iu, su = csa.csa_indexer_topk(q_idx.to(DEV), w_idx.to(DEV), k_idx.to(DEV), m, topk, *args,
-                                  q_scale=q_scale.to(DEV), k_scale=k_scale.to(DEV),
-                                  want_scores=True)
+                                  q_scale=dev(q_scale), k_scale=dev(k_scale), want_scores=True)
     pt, table = _pages(B, Nc, P, seed=P + Nc)
     rows = _rows(table, P, Nc)
     n_rows = pt.n_pages * P
     ip, sp = csa.csa_indexer_topk(q_idx.to(DEV), w_idx.to(DEV), _to_pool(k_idx, rows, n_rows), m,
-                                  topk, *args, q_scale=q_scale.to(DEV),
-                                  k_scale=_to_pool(k_scale, rows, n_rows), want_scores=True,
-                                  pages=pt)
+                                  topk, *args, q_scale=dev(q_scale),
+                                  k_scale=None if k_scale is None else _to_pool(k_scale, rows,
+                                                                                 n_rows),
+                                  want_scores=True, pages=pt)
     torch.cuda.synchronize()
     _same_bits(ip, iu, "paged indexer indices")
     _same_bits(sp, su, "paged indexer scores")
