@@ -15,7 +15,24 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def test_decode_step_graph_replays_match_eager():
+def _paged(B, Nc, P, tensors):
+    """Shuffled page table and pools of the given [B, Nc, ...] caches."""
+    n = -(-Nc // P)
+    table = torch.randperm(B * n, generator=torch.Generator().manual_seed(5)).to(torch.int32)
+    table = table.view(B, n).to(DEV)
+    j = torch.arange(Nc, device=DEV)
+    rows = (table[:, j // P].long() * P + j % P).reshape(-1)
+    pools = []
+    for t in tensors:
+        feat = tuple(t.shape[2:]) or (1,)
+        pool = torch.zeros((B * n * P,) + feat, dtype=t.dtype, device=DEV)
+        pool.view(torch.uint8)[rows] = t.reshape((-1,) + feat).view(torch.uint8)
+        pools.append(pool if t.dim() > 2 else pool.view(-1))
+    return csa.PageTable(table, P, B * n, nc_cap=Nc), pools
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_step_graph_replays_match_eager(paged):
     d = gen.Draw(31, DEV)
     B, Nc, m, topk, W, H, D = 4, 20000, 4, 512, 64, 64, 128
     k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
@@ -33,15 +50,27 @@ def test_decode_step_graph_replays_match_eager():
                        dtype=torch.uint8, device=DEV)
     ws_a = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(B, 1, H, D, topk, W)),
                        dtype=torch.uint8, device=DEV)
+    pages = None
 
     def step():
         csa.csa_indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=q_scale,
-                             k_scale=k_scale, idx_out=idx, workspace=ws_i)
-        csa.csa_sparse_attn(q, kv, idx, kvr, W, q_pos, raw_base, out=out, workspace=ws_a)
+                             k_scale=k_scale, idx_out=idx, workspace=ws_i, pages=pages)
+        csa.csa_sparse_attn(q, kv, idx, kvr, W, q_pos, raw_base, out=out, workspace=ws_a,
+                            pages=pages)
 
     step()
     torch.cuda.synchronize()
     ref_idx, ref_out = idx.clone(), out.clone()
+    if paged:
+        # the same step on paged caches: bit-exact with the unpaged one, and
+        # captured and replayed below
+        pages, (k_idx, k_scale, kv) = _paged(B, Nc, 64, (k_idx, k_scale, kv))
+        ws_a = torch.empty(csa.lib().csa_sparse_attn_paged_workspace_size(B, 1, H, D, topk, W),
+                           dtype=torch.uint8, device=DEV)
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx)
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
