@@ -28,6 +28,13 @@
  *    rule: token i sees [max(0, i - W + 1), i]).
  *
  * Parity status per function (see the tests under tests/):
+ *  - number formats: orc_bf16_decode is pinned to torch's bfloat16 on all
+ *    65536 bit patterns, orc_e4m3_decode on all 256 codes, the encoders to
+ *    torch's round-to-nearest-even casts (midpoints included), and
+ *    orc_quant_rows_e4m3 (row scale amax / 448 in fp32, codes of the fp32
+ *    quotient) to torch's float8_e4m3fn cast of the same quotient, zero rows
+ *    and midpoint rows included.  Every stage fed bf16 patterns equals the
+ *    same stage fed their torch-decoded values.
  *  - orc_compress: the uniform-gate / no-overlap case is pinned to the
  *    mean-pool closed form; the non-uniform overlapping gate form is the
  *    plainest reading of section 3.2 of the migration page and is otherwise
@@ -203,17 +210,25 @@ static double ld(const void* p, size_t i, int dt) {
   }
 }
 
-/* Per-row e4m3 quantisation as the compressor's fp8 store defines it:
- * scale s = amax / 448 (s = 1 for an all-zero row), code = e4m3(v / s). */
+/* Per-row e4m3 quantisation as the compressor's fp8 store defines it: the
+ * stored row scale is the fp32 value s = amax / 448 (s = 1 for an all-zero
+ * row), and each code is the e4m3 rounding (nearest even, saturating at 448)
+ * of the IEEE fp32 quotient v / s.  The quotient is formed in fp32 because
+ * that is the precision the scale is stored and applied in; rounding it to
+ * e4m3 afterwards is the reading taken of "divide by the row scale, then
+ * round". */
 void orc_quant_rows_e4m3(int rows, int cols, const double* in, uint8_t* codes,
                          double* scales) {
   for (int r = 0; r < rows; ++r) {
-    double amax = 0, s;
+    double amax = 0;
+    float s;
     for (int c = 0; c < cols; ++c) amax = fmax(amax, fabs(in[(size_t)r * cols + c]));
-    s = amax > 0 ? amax / 448.0 : 1.0;
-    scales[r] = s;
-    for (int c = 0; c < cols; ++c)
-      codes[(size_t)r * cols + c] = orc_e4m3_encode(in[(size_t)r * cols + c] / s);
+    s = amax > 0 ? (float)(amax / 448.0) : 1.0f;
+    scales[r] = (double)s;
+    for (int c = 0; c < cols; ++c) {
+      volatile float q = (float)in[(size_t)r * cols + c] / s; /* one fp32 divide */
+      codes[(size_t)r * cols + c] = orc_e4m3_encode((double)q);
+    }
   }
 }
 

@@ -64,6 +64,103 @@ def test_bf16_encode_matches_torch():
     assert np.array_equal(ref, ours)
 
 
+def test_bf16_decode_matches_torch_all_patterns():
+    # every one of the 65536 bf16 bit patterns: the oracle's decode against
+    # torch's bfloat16 -> float64 conversion (NaN payloads compare as NaN)
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = brute.decode_bits(bits)
+    ours = np.array([orc.bf16_decode(int(h)) for h in bits])
+    both_nan = np.isnan(ref) & np.isnan(ours)
+    assert np.all(both_nan | (ref == ours))
+    assert np.array_equal(np.signbit(ref[~both_nan]), np.signbit(ours[~both_nan]))
+
+
+def _e4m3_midpoints():
+    lo = np.array([orc.e4m3_decode(c) for c in range(0, 0x7E)])
+    hi = np.array([orc.e4m3_decode(c + 1) for c in range(0, 0x7E)])
+    return 0.5 * (lo + hi)
+
+
+def test_quant_rows_e4m3_matches_library_store():
+    # The fp8 store rule (row scale amax / 448 in fp32, codes = e4m3 of the
+    # fp32 quotient, nearest even, saturating) against torch's float8_e4m3fn
+    # cast of the same quotient, through the input generator's store_fp8.
+    from compressed_sparse_attention_overlapped_amd import inputs as gen
+    r = rng(3)
+    mids = _e4m3_midpoints()
+    rows = [np.zeros(64), np.full(64, 448.0)]
+    # rows whose quotients land exactly on e4m3 midpoints: the row maximum
+    # is 448 * 2^k, so the scale is the power of two 2^k and v / s = midpoint
+    for k in (-3, 0, 2, 9):
+        v = r.choice(mids, 63) * r.choice([-1.0, 1.0], 63)
+        rows.append(np.concatenate([[448.0], v]) * 2.0 ** k)
+    for k in range(40):                     # random rows over a wide range
+        rows.append(r.normal(0, 1, 64) * 2.0 ** r.integers(-20, 20))
+    x = np.stack(rows).astype(np.float32)
+    codes, scales = orc.quant_rows_e4m3(x.astype(np.float64))
+    t_codes, t_scales = gen.store_fp8(torch.from_numpy(x))
+    assert np.array_equal(scales, t_scales.double().numpy())
+    assert np.array_equal(codes, t_codes.view(torch.uint8).numpy())
+    assert scales[0] == 1.0 and not codes[0].any()          # a zero row
+    assert scales[1] == 1.0 and (codes[1] == 0x7E).all()    # 448 / 1 -> the top code
+    # a wrong scale rule (amax / 240, say) changes the codes
+    xs = x[2:]
+    bad = (xs / (np.abs(xs).max(1, keepdims=True) / 240.0)).astype(np.float32)
+    assert not np.array_equal(codes[2:], torch.from_numpy(bad).clamp(-448, 448)
+                              .to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_oracle_reads_bf16_inputs_as_their_values():
+    # Every oracle stage fed bf16 bit patterns equals the same stage fed the
+    # patterns' values (decoded by torch) as fp32: the bf16 input path of the
+    # oracle is the value each pattern stands for.
+    r = rng(4)
+
+    def bf(shape, scale=1.0):
+        t = torch.from_numpy(r.normal(0, scale, shape).astype(np.float32)).to(torch.bfloat16)
+        bits = t.view(torch.int16).numpy().view(np.uint16)
+        return bits, brute.decode_bits(bits).astype(np.float32)
+
+    B, L, dm, E, m = 2, 13, 32, 8, 4
+    xb, xf = bf((B, L, dm))
+    wkb, wkf = bf((E, dm), dm ** -0.5)
+    wgb, wgf = bf((E, dm), dm ** -0.5)
+    a = orc.compress(xb, wkb, wgb, m, 1, [0, 3], 8)
+    f = orc.compress(xf, wkf, wgf, m, 1, [0, 3], 8)
+    np.testing.assert_array_equal(a[0], f[0])
+    np.testing.assert_array_equal(a[2], f[2])
+
+    T, H_I, d_I, Nc = 5, 3, 16, 20
+    qb, qf = bf((B, T, H_I, d_I))
+    kb, kf = bf((B, Nc, d_I))
+    w = r.normal(0, 1, (B, T, H_I)).astype(np.float32)
+    ia = orc.indexer_topk(qb, w, kb, m, 4, [70, 60], Nc, want_all=True)
+    iff = orc.indexer_topk(qf, w, kf, m, 4, [70, 60], Nc, want_all=True)
+    np.testing.assert_array_equal(ia[0], iff[0])
+    np.testing.assert_array_equal(ia[3], iff[3])
+
+    H, D, R, W = 4, 16, 30, 6
+    q_b, q_f = bf((B, T, H, D))
+    cb, cf = bf((B, Nc, 2 * D))
+    rb, rf = bf((B, R, 2 * D))
+    idx = ia[0]
+    sa = orc.sparse_attn(q_b, cb, idx, rb, W, [20, 25], [0, 0])
+    sf = orc.sparse_attn(q_f, cf, idx, rf, W, [20, 25], [0, 0])
+    np.testing.assert_array_equal(sa[0], sf[0])
+    ha = orc.hca_dense_attn(q_b, cb, rb, m, W, [20, 25], Nc, [0, 0])
+    hf = orc.hca_dense_attn(q_f, cf, rf, m, W, [20, 25], Nc, [0, 0])
+    np.testing.assert_array_equal(ha[0], hf[0])
+    # and the bf16 attention against the library attention on torch's values
+    for b in range(B):
+        pos0 = [20, 25][b]
+        sets = [[j for j in idx[b, t] if j >= 0] for t in range(T)]
+        mask = brute.csa_mask(T, pos0, sets, Nc, R, 0, W)
+        keys = np.concatenate([cf[b, :, :D], rf[b, :, :D]]).astype(np.float64)
+        vals = np.concatenate([cf[b, :, D:], rf[b, :, D:]]).astype(np.float64)
+        ref, _ = brute.sdpa_masked(q_f[b].astype(np.float64), keys, vals, mask, D ** -0.5)
+        np.testing.assert_allclose(sa[0][b], ref, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- compressor
 
 def test_compress_worked_example():
