@@ -60,6 +60,24 @@ class PageTable:
         return C.byref(_CPageTable(self.block_table.data_ptr(), self.page_size, self.max_pages,
                                    self.n_pages))
 
+    def check(self, B: int, *pools):
+        """Raise ValueError unless the table can serve B sequences on the
+        pools' device and every pool holds n_pages * page_size rows (the C
+        ABI sees only pointers, so a short table or pool would be read or
+        written out of bounds)."""
+        bt = self.block_table
+        if bt.shape[0] < B:
+            raise ValueError("block_table has %d rows for %d sequences" % (bt.shape[0], B))
+        for p in pools:
+            if p is None:
+                continue
+            if p.dim() < 1 or p.shape[0] < self.n_pages * self.page_size:
+                raise ValueError("a paged pool needs n_pages * page_size = %d rows (got %s)"
+                                 % (self.n_pages * self.page_size, tuple(p.shape)))
+            if not bt.is_cuda or bt.device != p.device:
+                raise ValueError("block_table must live on the caches' device (%s, got %s)"
+                                 % (p.device, bt.device))
+
 
 def lib():
     """Load libcsa.so (built in-tree by ``__graft_entry__.build()``)."""
@@ -165,6 +183,7 @@ def csa_compress(x, w_kv, w_gate, pos0, m, overlap, out, out_scale=None, ape=Non
     ws, nb = _workspace(csa_compress_workspace_size(B, L, d_model, E, m, overlap, x.dtype), x,
                         workspace)
     if pages is not None:
+        pages.check(B, out, out_scale)
         rc = lib().csa_compress_paged(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(pos0),
                                       _p(x), _p(w_kv), _p(w_gate), _DT[x.dtype], _p(ape),
                                       _p(state_in), _p(state_out), _p(out), _p(out_scale),
@@ -199,6 +218,7 @@ def csa_indexer_topk(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale=None, k
     ws, nb = _workspace(csa_indexer_topk_workspace_size(B, T, H_I, d_I, Nc_cap, topk, q_idx.dtype),
                         q_idx, workspace)
     if pages is not None:
+        pages.check(B, k_idx, k_scale)
         rc = lib().csa_indexer_topk_paged(B, T, H_I, d_I, Nc_cap, m, topk, _p(q_pos), _p(n_cmp),
                                           _p(q_idx), _p(q_scale), _p(w_idx), _p(k_idx),
                                           _p(k_scale), _DT[q_idx.dtype], pages.c(), _p(idx_out),
@@ -234,6 +254,7 @@ def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None,
     if want_lse and lse is None:
         lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
     if pages is not None:
+        pages.check(B, kv_cmp)
         ws, nb = _workspace(lib().csa_sparse_attn_paged_workspace_size(B, T, H, D, topk, window),
                             q, workspace)
         rc = lib().csa_sparse_attn_paged(B, T, H, D, topk, window, scale, _p(_sink(sink, H)),

@@ -136,16 +136,22 @@ __device__ __forceinline__ float sum_xor16(float v) {
 // ---- paged compressed caches ---------------------------------------------
 // Logical entry j of sequence b lives in pool row
 //   (block_table[b * max_pages + j / 2^page_log2] * 2^page_log2) + j % 2^page_log2;
-// a null block_table means the unpaged layout [B, Nc_cap, row].  Page ids are
-// clamped into [0, n_pages) so that a stale table entry cannot leave the pool.
+// a null block_table means the unpaged layout [B, Nc_cap, row].  A page id
+// outside [0, n_pages) marks its entries absent: paged_row() returns -1 and
+// no kernel reads or writes a pool row for them.
 struct PageTable {
   const int32_t* block_table;
   int page_log2, max_pages, n_pages;
 };
 __device__ __forceinline__ int64_t paged_row(const PageTable& pt, int b, int j) {
-  int pg = pt.block_table[(size_t)b * pt.max_pages + (j >> pt.page_log2)];
-  pg = min(max(pg, 0), pt.n_pages - 1);
+  const int pg = pt.block_table[(size_t)b * pt.max_pages + (j >> pt.page_log2)];
+  if ((unsigned)pg >= (unsigned)pt.n_pages) return -1;
   return ((int64_t)pg << pt.page_log2) | (int64_t)(j & ((1 << pt.page_log2) - 1));
+}
+// A page id as staged in LDS by the score kernels: the id, or -1 if absent.
+__device__ __forceinline__ int32_t page_or_absent(const PageTable& pt, int b, int p) {
+  const int pg = pt.block_table[(size_t)b * pt.max_pages + p];
+  return (unsigned)pg < (unsigned)pt.n_pages ? pg : -1;
 }
 
 }  // namespace csa

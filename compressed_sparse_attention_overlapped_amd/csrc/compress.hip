@@ -352,6 +352,9 @@ __global__ void __launch_bounds__(256) pool_kernel(
   const int64_t last = (int64_t)m * (i + 1) - 1;
   if (last >= p0 + L) return;
   const int64_t first = (int64_t)m * (i - overlap);
+  // paged output: an entry whose page is absent is not stored (uniform)
+  const int64_t orow64 = pt.block_table ? paged_row(pt, b, (int)i) : (int64_t)b * Nc_cap + i;
+  if (orow64 < 0) return;
 
   __shared__ float red[256];
   float vals[4];  // E <= 1024 supported (checked by the host)
@@ -485,8 +488,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
       amax = fmaxf(amax, fabsf(vals[nv]));
     }
   }
-  const size_t orow =
-      pt.block_table ? (size_t)paged_row(pt, b, i) : (size_t)b * Nc_cap + (size_t)i;
+  const size_t orow = (size_t)orow64;
   if (OUT_DT == CSA_DT_F32) {
     nv = 0;
     for (int e = tid; e < E; e += blockDim.x, ++nv) ((float*)out)[orow * E + e] = vals[nv];

@@ -162,9 +162,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
   const int p_first = PAGED ? jb >> pt.page_log2 : 0;
   if (PAGED && jb < Nc_cap) {
     const int n_pg = ((min(jb + key_chunk, Nc_cap) - 1) >> pt.page_log2) - p_first + 1;
-    for (int i = tid; i < n_pg; i += blockDim.x)
-      pg_s[i] = min(max(pt.block_table[(size_t)b * pt.max_pages + p_first + i], 0),
-                    pt.n_pages - 1);
+    for (int i = tid; i < n_pg; i += blockDim.x) pg_s[i] = page_or_absent(pt, b, p_first + i);
   }
   // A operands: rows (token, head) -> lane row (lane & 31) of tile mt:
   // token = wave*4 + mt*2 + (lane&31)/16, head = lane & 15; k-step s covers
@@ -209,9 +207,12 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
       const int c = i * 256 + tid, r = c >> 3, q8 = c & 7;
       const int row = min(j0 + r, je - 1);
       size_t at = (size_t)b * Nc_cap + row;
-      if constexpr (PAGED)
-        at = ((size_t)pg_s[(row >> pt.page_log2) - p_first] << pt.page_log2) |
-             (size_t)(row & ((1 << pt.page_log2) - 1));
+      if constexpr (PAGED) {
+        // an absent page reads pool row 0 (its scores are replaced below)
+        const int pg = pg_s[(row >> pt.page_log2) - p_first];
+        at = pg < 0 ? 0
+                    : ((size_t)pg << pt.page_log2) | (size_t)(row & ((1 << pt.page_log2) - 1));
+      }
       pk[i] = *(const u32x4*)(k_idx + at * 64 + q8 * 8);
     }
   };
@@ -249,9 +250,12 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
         s0 = sum_xor32(s0);
         s1 = sum_xor32(s1);
         const int u = lane >> 5;  // lanes < 32 write token 0 of the pair, others token 1
-        const float sc = u ? s1 : s0;
+        float sc = u ? s1 : s0;
         const int tt = trow[mt] - ((lane & 31) >> 4) + u;
         if (tt < T && j < je && j < nvis[mt][u]) {
+          // an entry of an absent page has no key: the lowest score
+          if constexpr (PAGED)
+            if (pg_s[(j >> pt.page_log2) - p_first] < 0) sc = -INFINITY;
           scores[((size_t)b * T + tt) * Nc_cap + j] = sc;
           if (HIST) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
         }
@@ -340,9 +344,7 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
   const int p_first = PAGED ? jb >> pt.page_log2 : 0;
   if (PAGED) {
     const int n_pg = ((min(jb + kChunk, Nc_cap) - 1) >> pt.page_log2) - p_first + 1;
-    for (int i = tid; i < n_pg; i += blockDim.x)
-      pg_s[i] = min(max(pt.block_table[(size_t)b * pt.max_pages + p_first + i], 0),
-                    pt.n_pages - 1);
+    for (int i = tid; i < n_pg; i += blockDim.x) pg_s[i] = page_or_absent(pt, b, p_first + i);
   }
   if (HIST) {
     for (int i = tid; i < kHistBins; i += blockDim.x) lhist[i] = 0;
@@ -376,10 +378,12 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
     // paged caches: the rows sit in a shared pool (16 consecutive entries,
     // one load group, never straddle a page)
     const size_t kbase = PAGED ? 0 : (size_t)b * Nc_cap;
+    // (an absent page reads pool row 0; its scores are replaced below)
     auto krow = [&](int j) -> size_t {
-      if constexpr (PAGED)
-        return ((size_t)pg_s[(j >> pt.page_log2) - p_first] << pt.page_log2) |
-               (size_t)(j & ((1 << pt.page_log2) - 1));
+      if constexpr (PAGED) {
+        const int pg = pg_s[(j >> pt.page_log2) - p_first];
+        return pg < 0 ? 0 : ((size_t)pg << pt.page_log2) | (size_t)(j & ((1 << pt.page_log2) - 1));
+      }
       return (size_t)j;
     };
     const uint8_t* kb = k_idx + kbase * KB;
@@ -452,9 +456,12 @@ __global__ void __launch_bounds__(256) score_fp8_kernel(
         const float s0 = b5 ? q[0] : q[2], s1 = b5 ? q[1] : q[3];
         const float k0 = b5 ? q[2] : q[0], k1 = b5 ? q[3] : q[1];
         const float r0 = k0 + lane_xor32(s0), r1 = k1 + lane_xor32(s1);
-        const float v = ((b4 ? r1 : r0) + lane_xor16(b4 ? r0 : r1)) * sc[half];
+        float v = ((b4 ? r1 : r0) + lane_xor16(b4 ? r0 : r1)) * sc[half];
         const int j = j0 + 64 * half + lane;
         if (j < we) {
+          // an entry of an absent page has no key: the lowest score
+          if constexpr (PAGED)
+            if (pg_s[(j >> pt.page_log2) - p_first] < 0) v = -INFINITY;
           srow[j] = v;
           if (HIST) atomicAdd(&lhist[score_key(v) >> kHistShift], 1u);
         }

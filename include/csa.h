@@ -201,7 +201,6 @@ csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float
                             void* workspace, size_t ws_bytes, hipStream_t stream);
 size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window);
 
-/* Static text of a status code. */
 /*
  * Paged compressed caches (serving-shaped storage: the million-token CSA/HCA
  * article, section 8.3, lists paged-attention style cache management for
@@ -211,10 +210,16 @@ size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int
  * sequence live in a shared pool of n_pages pages of page_size rows each;
  * logical entry j of sequence b is pool row
  *     block_table[b * max_pages + j / page_size] * page_size + j % page_size.
- *  block_table  device int32 [B, max_pages], read-only; entries past a
- *               sequence's last used page are not read.  A page id outside
- *               [0, n_pages) is clamped into it (no fault; the caller's
- *               table is wrong then)
+ *  block_table  device int32 [B, max_pages], read-only.  Table entries of
+ *               the pages that cover logical entries 0 .. Nc_cap - 1 may be
+ *               read whatever n_cmp[b] is; only those of pages holding
+ *               existing entries (j < n_cmp[b]) affect results.  A page id
+ *               outside [0, n_pages) marks its entries absent: the
+ *               compressor does not store them, the indexer gives them the
+ *               score -inf (they are selected only when fewer than topk
+ *               other visible entries exist), and sparse attention skips
+ *               them as it skips a -1 slot.  No pool row is read or written
+ *               for an absent page.
  *  page_size    rows per page, a power of two in [16, 2^20]
  *  max_pages    row stride of block_table; Nc_cap <= max_pages * page_size
  *  n_pages      pages in the pool (pool rows = n_pages * page_size)
@@ -273,6 +278,7 @@ csa_status_t csa_sparse_attn_paged(int B, int T, int H, int D, int topk, int win
                                    void* workspace, size_t ws_bytes, hipStream_t stream);
 size_t csa_sparse_attn_paged_workspace_size(int B, int T, int H, int D, int topk, int window);
 
+/* Static text of a status code. */
 const char* csa_status_string(csa_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* csa_last_error(void);

@@ -141,3 +141,21 @@ def test_paged_entry_points_validate_the_page_table(L):
                                  None, dummy, dummy, 4, dummy, 1, dummy, None, dummy, 1 << 30,
                                  None)
     assert rc == 1 and b"pages is required" in L.csa_last_error()
+
+
+def test_page_table_checks_reject_bad_tables_before_any_call():
+    # the C ABI sees only pointers: the binding checks what it can see
+    import torch
+
+    import compressed_sparse_attention_overlapped_amd as csa
+    table = torch.zeros(2, 4, dtype=torch.int32)
+    pt = csa.PageTable(table, 16, n_pages=8)
+    pool = torch.zeros(8 * 16, 64)
+    with pytest.raises(ValueError, match="sequences"):
+        pt.check(3, pool)                       # a table row per sequence
+    with pytest.raises(ValueError, match="rows"):
+        pt.check(2, torch.zeros(8 * 16 - 1, 64))  # pool shorter than n_pages pages
+    with pytest.raises(ValueError, match="device"):
+        pt.check(2, pool)                       # a host table with the caches
+    with pytest.raises(ValueError, match="int32"):
+        csa.PageTable(table.long(), 16, 8)

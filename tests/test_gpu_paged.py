@@ -160,3 +160,143 @@ def test_paged_compress_matches_unpaged(out_fmt, L):
     used = torch.zeros(n_rows, dtype=torch.bool)
     used[rows] = True
     assert not pb[~used].any()
+
+
+def _absent(table, n_pages, P, nc_cap):
+    """Marks one page of sequence 0 with -1 and one of the last sequence with
+    an id past the pool; returns the table, and the logical entries that the
+    two pages held, per sequence."""
+    t = table.clone()
+    B, max_pages = t.shape
+    gone = {}
+    for b, pg, bad in ((0, 1, -1), (B - 1, max_pages // 2, n_pages + 5)):
+        t[b, pg] = bad
+        gone[b] = np.arange(pg * P, min((pg + 1) * P, nc_cap))
+    return t, gone
+
+
+@pytest.mark.parametrize("fmt", [gen.BF16, gen.FP8])
+def test_paged_indexer_absent_pages_score_minus_inf(fmt):
+    # an out-of-range page id marks its entries absent: score -inf, so they
+    # lose to every present entry, and no pool row is read for them
+    d = gen.Draw(70)
+    B, T, Nc, m, topk, P = 3, 2, 3000, 4, 300, 64
+    k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, fmt)
+    q_idx, q_scale, w_idx = gen.indexer_query(d, B, T, 16, 64, fmt)
+    q_pos, n_cmp = [4 * Nc, 4 * Nc - 10, 4 * 1500], [Nc, Nc, Nc]
+    pt, table = _pages(B, Nc, P, seed=7)
+    rows = _rows(table, P, Nc)
+    n_rows = pt.n_pages * P
+    bad_table, gone = _absent(table, pt.n_pages, P, Nc)
+    pt_bad = csa.PageTable(bad_table.to(DEV), P, pt.n_pages, nc_cap=Nc)
+    dev = lambda t: None if t is None else t.to(DEV)
+    ip, sp = csa.csa_indexer_topk(q_idx.to(DEV), w_idx.to(DEV), _to_pool(k_idx, rows, n_rows), m,
+                                  topk, dev_i64(q_pos), dev_i32(n_cmp), q_scale=dev(q_scale),
+                                  k_scale=None if k_scale is None else _to_pool(k_scale, rows,
+                                                                                 n_rows),
+                                  want_scores=True, pages=pt_bad)
+    torch.cuda.synchronize()
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    alls = o[3].copy()
+    for b, js in gone.items():
+        alls[b, :, js] = -np.inf
+    g_idx = ip.cpu().numpy()
+    for b, js in gone.items():
+        assert not np.isin(g_idx[b], js).any(), "an absent entry was selected"
+    _compare(g_idx, sp.cpu().numpy(), alls, m, topk, q_pos, n_cmp, Nc, "absent pages " + fmt)
+
+
+@pytest.mark.parametrize("B,T", [(4, 1), (1, 1100)])
+def test_paged_sparse_attn_absent_pages_are_skipped(B, T):
+    # (4, 1): the decode kernel maps indices while staging them; (1, 1100):
+    # the translation launch feeds the prefill kernel
+    d = gen.Draw(71 + T)
+    H, D, Nc, R, W, m, P, topk = 64, 128, 3000, 1300, 128, 4, 64, 64
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    q_pos = [4 * Nc - T - 5 - 40 * b for b in range(B)]
+    raw_base = [p + T - R for p in q_pos]
+    # indices crowd into the first pages so that the absent ones are hit
+    nv = torch.tensor([[min(_n_vis(q_pos[b] + t, Nc, m, Nc), 400) for t in range(T)]
+                       for b in range(B)])
+    idx = gen.random_index_sets(d, B, T, topk, nv, 0.1)
+    pt, table = _pages(B, Nc, P, seed=T)
+    bad_table, gone = _absent(table, pt.n_pages, P, Nc)
+    pt_bad = csa.PageTable(bad_table.to(DEV), P, pt.n_pages, nc_cap=Nc)
+    pool = _to_pool(kv_cmp, _rows(table, P, Nc), pt.n_pages * P)
+    op, lp = csa.csa_sparse_attn(q.to(DEV), pool, idx.to(DEV), kv_raw.to(DEV), W,
+                                 dev_i64(q_pos), dev_i64(raw_base), want_lse=True, pages=pt_bad)
+    torch.cuda.synchronize()
+    ref_idx = idx.numpy().copy()
+    hit = 0
+    for b, js in gone.items():
+        m_ = np.isin(ref_idx[b], js)
+        hit += int(m_.sum())
+        ref_idx[b][m_] = -1
+    assert hit > 0, "the test must name entries of an absent page"
+    ref, rl = orc.sparse_attn(gen.host_bits(q), gen.host_bits(kv_cmp), ref_idx,
+                              gen.host_bits(kv_raw), W, q_pos, raw_base)
+    attn_check(op, lp, ref, rl, q.dtype, "absent pages B=%d T=%d" % (B, T))
+
+
+def test_paged_sparse_attn_bf16_prefill_rows_match_unpaged():
+    # 1024 or more query rows: the page translation launch, then the
+    # one-row-per-wave prefill kernel over the pool
+    d = gen.Draw(72)
+    B, T, H, D, Nc, W, m, P, topk = 1, 1024, 64, 128, 2048, 128, 4, 64, 64
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, 4 * Nc, 2 * D), gen.BF16)
+    q_pos = [4 * Nc - T]
+    raw_base = [0]
+    idx = _rand_idx(d, B, T, topk, lambda b, t: _n_vis(q_pos[b] + t, Nc, m, Nc), 0.1)
+    common = (W, dev_i64(q_pos), dev_i64(raw_base))
+    ou, lu = csa.csa_sparse_attn(q.to(DEV), kv_cmp.to(DEV), idx.to(DEV), kv_raw.to(DEV), *common,
+                                 want_lse=True)
+    pt, table = _pages(B, Nc, P, seed=72)
+    pool = _to_pool(kv_cmp, _rows(table, P, Nc), pt.n_pages * P)
+    op, lp = csa.csa_sparse_attn(q.to(DEV), pool, idx.to(DEV), kv_raw.to(DEV), *common,
+                                 want_lse=True, pages=pt)
+    torch.cuda.synchronize()
+    _same_bits(op, ou, "paged prefill attention out")
+    _same_bits(lp, lu, "paged prefill attention lse")
+    rows = np.arange(0, T, 7)
+    # sampled rows against the oracle (each row is independent: a one-row
+    # oracle call per sampled position)
+    for t in rows[:40]:
+        r, l = orc.sparse_attn(gen.host_bits(q)[:, t:t + 1], gen.host_bits(kv_cmp),
+                               idx.numpy()[:, t:t + 1], gen.host_bits(kv_raw), W,
+                               [q_pos[0] + t], raw_base)
+        attn_check(op[:, t:t + 1], lp[:, t:t + 1], r, l, q.dtype, "paged prefill row %d" % t)
+
+
+def test_paged_compress_absent_page_is_not_stored():
+    d = gen.Draw(73)
+    B, L, d_model, E, m, o, P, Nc = 2, 128, 512, 64, 4, 1, 16, 32
+    wk, wg = (w.to(DEV) for w in gen.compressor_weights(d, d_model, E, gen.BF16))
+    x = gen.store(d.normal(B, L, d_model), gen.BF16).to(DEV)
+    pos0 = dev_i64([0, 0])
+    pt, table = _pages(B, Nc, P, seed=73, spare=2)
+    n_rows = pt.n_pages * P
+    bad = table.clone()
+    bad[0, 1] = -1                   # entries 16..31 of sequence 0
+    bad[1, 0] = pt.n_pages           # entries 0..15 of sequence 1
+    out_u = torch.zeros(B, Nc, E, dtype=torch.bfloat16, device=DEV)
+    csa.csa_compress(x, wk, wg, pos0, m, o, out_u)
+    sentinel = torch.full((n_rows, E), 7.0, dtype=torch.bfloat16, device=DEV)
+    out_p = sentinel.clone()
+    csa.csa_compress(x, wk, wg, pos0, m, o, out_p,
+                     pages=csa.PageTable(bad.to(DEV), P, pt.n_pages, nc_cap=Nc))
+    torch.cuda.synchronize()
+    rows = _rows(table, P, Nc)
+    pb, ub, sb = out_p.cpu(), out_u.cpu(), sentinel.cpu()
+    # present pages hold the unpaged entries
+    assert torch.equal(pb[rows[0, :16]], ub[0, :16])
+    assert torch.equal(pb[rows[1, 16:]], ub[1, 16:])
+    # every other pool row (the absent pages' own rows and the spare pages)
+    # keeps its old contents
+    keep = torch.ones(n_rows, dtype=torch.bool)
+    keep[rows[0, :16]] = False
+    keep[rows[1, 16:]] = False
+    assert torch.equal(pb[keep], sb[keep])
