@@ -171,7 +171,8 @@ def _absent(table, n_pages, P, nc_cap):
     gone = {}
     for b, pg, bad in ((0, 1, -1), (B - 1, max_pages // 2, n_pages + 5)):
         t[b, pg] = bad
-        gone[b] = np.arange(pg * P, min((pg + 1) * P, nc_cap))
+        gone[b] = np.union1d(gone.get(b, np.zeros(0, np.int64)),
+                             np.arange(pg * P, min((pg + 1) * P, nc_cap)))
     return t, gone
 
 
