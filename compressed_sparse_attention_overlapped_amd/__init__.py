@@ -17,6 +17,7 @@ from typing import Optional
 import torch
 
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
+           "csa_sparse_attn_noalloc",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
            "CsaError", "PageTable", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
@@ -101,6 +102,9 @@ def lib():
         L.csa_indexer_topk_paged.argtypes = [i32] * 7 + [vp] * 7 + [i32, pt, vp, vp, vp, sz, vp]
         L.csa_sparse_attn_paged.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, pt, vp, vp, i32,
                                             vp, i32, vp, vp, vp, sz, vp])
+        L.csa_sparse_attn_noalloc.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32,
+                                              vp, i32, vp, vp, vp])
+        L.csa_sparse_attn_noalloc.restype = C.c_int
         L.csa_sparse_attn_paged_workspace_size.argtypes = [i32] * 6
         L.csa_sparse_attn_paged_workspace_size.restype = C.c_size_t
         for f in (L.csa_compress, L.csa_indexer_topk, L.csa_sparse_attn, L.hca_dense_attn,
@@ -270,6 +274,23 @@ def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None,
                                _p(raw_base), _DT[q.dtype], _p(out), _p(lse), _p(ws), nb,
                                _stream(q))
     _check("csa_sparse_attn", rc)
+    return out, lse
+
+
+def csa_sparse_attn_noalloc(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, out, scale=None,
+                            lse=None, sink=None):
+    """csa_sparse_attn that allocates nothing: out (and lse, if wanted) are
+    the caller's; split-key partials use the library's static device scratch
+    (see csa_sparse_attn_noalloc in include/csa.h).  Returns (out, lse)."""
+    _dense(q, kv_cmp, idx, kv_raw, q_pos, raw_base, sink, out, lse)
+    B, T, H, D = q.shape
+    topk = idx.shape[2] if idx is not None else 0
+    scale = D ** -0.5 if scale is None else float(scale)
+    rc = lib().csa_sparse_attn_noalloc(B, T, H, D, topk, window, scale, _p(_sink(sink, H)),
+                                       _p(q_pos), _p(q), _p(kv_cmp), kv_cmp.shape[1], _p(idx),
+                                       _p(kv_raw), kv_raw.shape[1], _p(raw_base), _DT[q.dtype],
+                                       _p(out), _p(lse), _stream(q))
+    _check("csa_sparse_attn_noalloc", rc)
     return out, lse
 
 

@@ -308,6 +308,36 @@ csa_status_t csa_sparse_attn_paged(int B, int T, int H, int D, int topk, int win
                           pages);
 }
 
+csa_status_t csa_sparse_attn_noalloc(int B, int T, int H, int D, int topk, int window,
+                                     float scale, const float* sink, const int64_t* q_pos,
+                                     const void* q, const void* kv_cmp, int Nc_cap,
+                                     const int32_t* idx, const void* kv_raw, int R_cap,
+                                     const int64_t* raw_base, csa_dtype_t dt, void* out,
+                                     float* lse, hipStream_t stream) {
+  csa_status_t st = check_attn("csa_sparse_attn_noalloc", B, T, H, D, window, q_pos, q, kv_cmp,
+                               Nc_cap, kv_raw, R_cap, raw_base, dt, out);
+  if (st != CSA_OK) return st;
+  if (topk < 0) return fail(CSA_E_ARG, "csa_sparse_attn_noalloc: topk must be >= 0");
+  if (dt == CSA_DT_BF16 && !csa_host::attn_supported(B, T, H, topk + window, true))
+    return fail(CSA_E_UNSUPPORTED, "csa_sparse_attn_noalloc: topk + window too large for %d rows",
+                B * T);
+  const size_t need =
+      dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(B, T, H, D, topk + window, true);
+  const size_t cap = csa_host::noalloc_scratch_bytes();
+  if (need > cap)
+    return fail(CSA_E_UNSUPPORTED,
+                "csa_sparse_attn_noalloc: this call needs %zu bytes of scratch; the static "
+                "scratch holds %zu (use csa_sparse_attn with a workspace)", need, cap);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = csa_host::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "csa_sparse_attn_noalloc: scratch address");
+  }
+  return sparse_attn_impl(B, T, H, D, topk, window, scale, sink, q_pos, q, kv_cmp, Nc_cap, idx,
+                          kv_raw, R_cap, raw_base, dt, out, lse, ws, need > 0 ? cap : 0, stream,
+                          nullptr);
+}
+
 size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window) {
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
   return csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window, false);

@@ -20,6 +20,7 @@
 //    kernel.
 // fp32 runs a plain per-(row, head) wave kernel.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -765,8 +766,38 @@ __global__ void page_index_kernel(const int32_t* __restrict__ idx, size_t n, int
 
 }  // namespace csa
 
+// Scratch of csa_sparse_attn_noalloc (for callers that cannot allocate):
+// the split-key partials of the decode kernel live here instead of in a
+// caller workspace.  Each GPU the library runs on holds one copy for the
+// life of the process; every call on that GPU shares it.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace csa_host {
 using namespace csa;
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (the host-side name is only a stand-in
+// for the symbol, never a device address).
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 // Rows at or above this count use the one-row-per-wave kernel; fewer rows
 // (decode) use the head-split kernel with split-K.

@@ -215,6 +215,10 @@ struct AttnArgs {
   csa::PageTable pages;  // block_table null: unpaged kv_cmp (sparse only)
 };
 size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse);
+// the static scratch of csa_sparse_attn_noalloc: its size and its device
+// address on the current device
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
 bool attn_supported(int B, int T, int H, int keys_per_row, bool sparse);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 

@@ -188,6 +188,28 @@ csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, f
 size_t csa_sparse_attn_workspace_size(int B, int T, int H, int D, int topk, int window);
 
 /*
+ * csa_sparse_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  Arguments, results and errors are those of
+ * csa_sparse_attn; the split-key partials of few-row calls go to a static
+ * device buffer of 16 MiB that the library holds on each GPU it runs on
+ * until the process ends, instead of a caller workspace.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * its first call on a device looks up the buffer's device address once.
+ * A call whose partials would exceed 16 MiB returns CSA_E_UNSUPPORTED (the
+ * message gives the size); csa_sparse_attn_workspace_size() tells the size
+ * a call needs.  Every call on one GPU shares the buffer, and it keeps the
+ * last call's contents: calls that overlap on one GPU (concurrent streams,
+ * host threads) race and must be serialised by the caller.
+ */
+csa_status_t csa_sparse_attn_noalloc(int B, int T, int H, int D, int topk, int window,
+                                     float scale, const float* sink, const int64_t* q_pos,
+                                     const void* q, const void* kv_cmp, int Nc_cap,
+                                     const int32_t* idx, const void* kv_raw, int R_cap,
+                                     const int64_t* raw_base, csa_dtype_t dt, void* out,
+                                     float* lse, hipStream_t stream);
+
+/*
  * HCA: heavily compressed attention (DS-V4 analysis sections 1.4-1.5: ratio
  * m' >> m, dense attention over every compressed entry, plus the window).
  * As csa_sparse_attn (sink included) with the compressed part of J being
