@@ -1,16 +1,20 @@
 """Benchmark of the compressed sparse attention hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input:
-  * csa_prefill_8k_bf16 (default, the line's `value`): compress (main and
-    indexer) -> indexer top-k -> sparse attention for 8192 tokens;
-  * csa_decode_128k_b32 (reported in the same line under "decode_128k"):
-    indexer top-k -> sparse attention for 32 sequences at 131072 tokens of
-    context, caches resident in HBM;
-  * --workload selects any of the five workloads instead.
-Timing uses HIP events on the stream the library launches on.  Decode steps
-run with the L2 and the 256 MB last-level cache flushed (a 1 GiB write)
-before each step, outside the timed events, so cache-resident reuse across
-steps does not pass for HBM bandwidth.
+  * csa_prefill_8k_bf16 (the line's `value`): compress (main and indexer) ->
+    indexer top-k -> sparse attention for 8192 tokens;
+  * reported in the same line: csa_decode_128k_b32 ("decode_128k": indexer
+    top-k -> sparse attention for 32 sequences at 131072 tokens of context,
+    caches resident in HBM), hca_prefill_1m_chunk4k ("hca_1m_chunk4k": dense
+    compressed attention of a 4096-token chunk at 1M context) and
+    csa_decode_1m_b8_stream ("decode_1m_stream": streaming compressor step,
+    indexer top-k and sparse attention for 8 sequences at 1M context);
+  * --workload selects any workload instead.
+Timing uses HIP events on the stream the library launches on.  Every step
+runs with the L2 and the 256 MB last-level cache flushed (a 1 GiB write)
+before it, outside the timed events, so cache-resident reuse across steps
+does not pass for HBM bandwidth.  Each record gives the mean, median and p90
+step time.
 
 The CPU baseline times the oracle (test infrastructure under oracle/) on a
 bounded sample of the same workload on the host cores.
@@ -335,6 +339,17 @@ def step_hca(w, st):
 
 # ---------------------------------------------------------------- CPU baseline
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s=12.0):
     """Time the oracle on a bounded sample of the workload on the host cores.
 
@@ -416,12 +431,12 @@ def cpu_baseline(w, budget_s=12.0):
 
 # ---------------------------------------------------------------- driver
 
-def measure(name, steps, warmup, with_cpu):
+def measure(name, steps, warmup, with_cpu, graph=True):
     w = gen.WORKLOADS[name]
+    flush = True   # every workload: L2 and the last-level cache flushed before each step
     if w.kind == "csa_prefill":
         st = setup_prefill(w)
         fn, names = step_prefill(w, st)
-        flush = False
         pairs, visits = csa_counts(w, 0, w.T, w.n_cmp)
         attn_flops = visits * w.H * w.D * 4
         idx_flops = pairs * w.H_I * w.d_I * 2
@@ -430,19 +445,18 @@ def measure(name, steps, warmup, with_cpu):
     elif w.kind == "csa_decode":
         st = setup_decode(w)
         fn, names = step_decode(w, st)
-        flush = True
         unit_items, unit = w.B, "queries/s"
     else:
         st = setup_hca(w)
         fn, names = step_hca(w, st)
-        flush = False
         unit_items, unit = w.B * w.T, "tokens/s"
     r = run_steps(fn, names, steps, warmup, flush)
     step_s = r["step_ms_mean"] / 1e3
     res = {"workload": name, "value": unit_items / step_s, "unit": unit,
            "ms_per_step": r["step_ms_mean"], "ms_median": r["step_ms_median"],
-           "ms_p90": r["step_ms_p90"], "stage_ms": r["stage_ms"]}
-    if w.kind == "csa_decode":
+           "ms_p90": r["step_ms_p90"], "stage_ms": r["stage_ms"],
+           "cache": "L2 + last-level cache flushed before every step (outside the timed events)"}
+    if w.kind == "csa_decode" and graph:
         # the same step captured as a HIP graph and replayed, for comparison
         # (on this stack the replay is not faster than the eager launches)
         gr = run_graph(fn, steps, warmup, flush)
@@ -494,6 +508,8 @@ def measure(name, steps, warmup, with_cpu):
         res["work"] = {"attn_gflop": flops / 1e9}
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
+        if res["cpu_baseline"] is not None:
+            res["cpu_baseline"]["cpu_model"] = cpu_model()
     del st
     torch.cuda.empty_cache()
     return res
@@ -539,24 +555,31 @@ def main():
         print(json.dumps(measure(args.workload, args.steps, args.warmup, not args.no_cpu)), flush=True)
         return
     prim = measure("csa_prefill_8k_bf16", args.steps, args.warmup, not args.no_cpu)
-    dec = measure("csa_decode_128k_b32", args.steps, args.warmup, not args.no_cpu)
+    sub = {}
+    for key, wl, graph in (("decode_128k", "csa_decode_128k_b32", True),
+                           ("hca_1m_chunk4k", "hca_prefill_1m_chunk4k", False),
+                           ("decode_1m_stream", "csa_decode_1m_b8_stream", False)):
+        r = measure(wl, args.steps, args.warmup, not args.no_cpu, graph=graph)
+        sub[key] = {k: r[k] for k in ("workload", "value", "unit", "ms_per_step", "ms_median",
+                                      "ms_p90", "stage_ms", "roofline", "work", "cache")
+                    if k in r}
+        if "ms_per_step_graph" in r:
+            sub[key]["ms_per_step_graph"] = r["ms_per_step_graph"]
+        sub[key]["cpu_baseline"] = r.get("cpu_baseline")
     line = {
         "metric": "CSA prefill tokens/s + decode queries/s at 128K ctx; % of HBM/MFMA peak",
         "value": prim["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": prim["ms_per_step"],
+        "ms_median": prim["ms_median"], "ms_p90": prim["ms_p90"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "csa_prefill_8k_bf16", "batch": 1, "seq_len": 8192,
                    "d_model": 4096, "m": 4, "overlap": 1, "heads": 64, "head_dim": 128,
                    "indexer": "16x64 bf16", "topk": 512, "window": 512, "parallelism": "none"},
         "roofline": prim["roofline"],
         "cpu_baseline": prim.get("cpu_baseline"),
-        "stage_ms": prim["stage_ms"], "work": prim["work"],
-        "decode_128k": {k: dec[k] for k in ("value", "unit", "ms_per_step", "ms_median", "ms_p90",
-                                             "ms_per_step_graph", "stage_ms", "roofline",
-                                             "work")}
-        | {"cpu_baseline": dec.get("cpu_baseline"), "workload": "csa_decode_128k_b32",
-           "cache": "L2 + last-level cache flushed before every step"},
+        "stage_ms": prim["stage_ms"], "work": prim["work"], "cache": prim["cache"],
     }
+    line.update(sub)
     print(json.dumps(line), flush=True)
 
 

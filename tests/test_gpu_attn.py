@@ -162,10 +162,15 @@ def test_sparse_attn_prefill_8k_sampled():
     idx = _rand_idx(dc, 1, w.T, w.topk, lambda b, t: _n_vis(t, w.n_cmp, w.m, w.n_cmp), 0.0)
     out, lse = _sparse(q, kv_cmp, idx, kv_raw, w.window, [0], [0])
     kvc, kvr = gen.host_bits(kv_cmp), gen.host_bits(kv_raw)
-    for t in [0, 1, 3, 511, 512, 2047, 4000, 8191]:
-        ref, rl = orc.sparse_attn(gen.host_bits(q[:, t:t + 1]), kvc, idx[:, t:t + 1].numpy(), kvr,
-                                  w.window, [t], [0])
-        _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl, torch.bfloat16, "8k token %d" % t)
+    # blocks of 16 consecutive rows (both rows of every two-row workgroup,
+    # even and odd starts), through the window fill (rows < 512), the index
+    # lists' growth and the last rows: 256 rows
+    for t0 in (0, 17, 500, 1001, 2040, 2555, 3333, 4000, 4601, 5120, 5999, 6400, 7001, 7502,
+               8000, 8176):
+        sl = slice(t0, t0 + 16)
+        ref, rl = orc.sparse_attn(gen.host_bits(q[:, sl]), kvc, idx[:, sl].numpy(), kvr,
+                                  w.window, [t0], [0])
+        _check(out[:, sl], lse[:, sl], ref, rl, torch.bfloat16, "8k tokens %d.." % t0)
 
 
 @pytest.mark.parametrize("H,p0", [(64, 9000), (32, 9000), (64, 0)])
@@ -199,7 +204,7 @@ def test_sparse_attn_decode_split_k(name):
     w = gen.WORKLOADS[name]
     d = gen.Draw(w.seed + 300, DEV)
     B = w.B
-    Nc = 40000                              # entries the indices point into
+    Nc = w.n_cmp                            # the full cache the indices span
     kv_cmp = gen.store(d.normal(B, Nc, 2 * w.D), gen.BF16)
     kv_raw = gen.store(d.normal(B, w.window, 2 * w.D), gen.BF16)
     q = gen.store(d.normal(B, 1, w.H, w.D), gen.BF16)
@@ -240,10 +245,13 @@ def test_hca_1m_chunk_sampled():
                                   want_lse=True)
     torch.cuda.synchronize()
     kvc, kvr = gen.host_bits(inp["kv_cmp"]), gen.host_bits(inp["kv_raw"])
-    for t in [0, 1, 127, 2000, 4094, 4095]:
-        ref, rl = orc.hca_dense_attn(gen.host_bits(inp["q"][:, t:t + 1]), kvc, kvr, w.m, w.window,
-                                     [q0 + t], [w.n_cmp], [raw_base])
-        _check(out[:, t:t + 1], lse[:, t:t + 1], ref, rl, torch.bfloat16, "hca token %d" % t)
+    # blocks of 16 consecutive rows (every row of the four-row workgroups),
+    # including the first rows and the last: 128 rows
+    for t0 in (0, 126, 1001, 1600, 2222, 3000, 3571, 4080):
+        sl = slice(t0, t0 + 16)
+        ref, rl = orc.hca_dense_attn(gen.host_bits(inp["q"][:, sl]), kvc, kvr, w.m, w.window,
+                                     [q0 + t0], [w.n_cmp], [raw_base])
+        _check(out[:, sl], lse[:, sl], ref, rl, torch.bfloat16, "hca tokens %d.." % t0)
 
 
 def test_csa_with_all_visible_selected_equals_hca():

@@ -317,14 +317,21 @@ def test_compress_prefill_8k_sampled_entries():
     csa.csa_compress(xg, inp["w_ikv"].to(DEV), inp["w_igate"].to(DEV), pos0, w.m, w.overlap, kidx)
     torch.cuda.synchronize()
     g_main, g_idx = out.float().cpu().numpy(), kidx.float().cpu().numpy()
-    for i in [0, 1, 2, 511, 1024, 2046, 2047]:
-        lo = max(0, w.m * (i - 1))
-        xs = x[:, lo:w.m * (i + 1)]
-        Nc = i + 1
+    # blocks of 16 consecutive entries (136 in all): the first entries, blocks
+    # across the projection's 128-token tile boundaries (entries 31/32, 63/64)
+    # and the last entries; each block's oracle call starts at the block's
+    # first window token
+    checked = 0
+    for i0 in (0, 24, 56, 500, 1017, 1530, 1777, 2032):
+        i1 = min(i0 + 16, w.n_cmp)
+        lo = max(0, w.m * (i0 - 1))
+        xs = x[:, lo:w.m * i1]
         for wk, wg, g in ((inp["w_kv"], inp["w_gate"], g_main), (inp["w_ikv"], inp["w_igate"], g_idx)):
-            ref, wr, _ = _oracle(xs, wk, wg, [lo], w.m, w.overlap, Nc)
-            assert wr[0, i]
-            assert_bf16_close(g[0, i], ref[0, i], "prefill entry %d" % i)
+            ref, wr, _ = _oracle(xs, wk, wg, [lo], w.m, w.overlap, i1)
+            assert wr[0, i0:i1].all()
+            assert_bf16_close(g[0, i0:i1], ref[0, i0:i1], "prefill entries %d..%d" % (i0, i1 - 1))
+        checked += i1 - i0
+    assert checked >= 128
 
 
 def test_compress_bf16_ragged_tiles_and_split_k():

@@ -140,15 +140,23 @@ def test_indexer_prefill_8k_sampled_rows():
     q_idx, _, w_idx = gen.indexer_query(d, 1, w.T, w.H_I, w.d_I, gen.BF16)
     k_idx, _ = gen.indexer_keys(d, 1, w.n_cmp, w.d_I, gen.BF16)
     g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, w.m, w.topk, [0], [w.n_cmp])
-    rows = [0, 3, 4, 2047, 2048, 2051, 4095, 6000, 8190, 8191]
-    for t in rows:
-        o = _oracle_rows(q_idx[:, t:t + 1], w_idx[:, t:t + 1], k_idx, w.m, w.topk, [t], [w.n_cmp])
-        _compare(g_idx[:, t:t + 1], g_sc[:, t:t + 1], o[3], w.m, w.topk, [t], [w.n_cmp], w.n_cmp,
-                 "8k row %d" % t)
+    # blocks of 16 consecutive rows (every row of a 16-row score group, at
+    # aligned and unaligned starts), through the 512-entry chunk boundaries
+    # (rows 2047/2048, 4095/4096, 6143/6144) and the last rows: 288 rows
+    starts = [0, 9, 1000, 2040, 3001, 4088, 4500, 5123, 6136, 6700, 7007, 7500, 7777, 7900,
+              8000, 8100, 8150, 8176]
+    n = 0
+    for t0 in starts:
+        sl = slice(t0, t0 + 16)
+        o = _oracle_rows(q_idx[:, sl], w_idx[:, sl], k_idx, w.m, w.topk, [t0], [w.n_cmp])
+        _compare(g_idx[:, sl], g_sc[:, sl], o[3], w.m, w.topk, [t0], [w.n_cmp], w.n_cmp,
+                 "8k rows %d.." % t0)
+        n += 16
+    assert n >= 256
 
 
-@pytest.mark.parametrize("name,rows", [("csa_decode_128k_b32", [0, 13, 31]),
-                                       ("csa_decode_1m_b8_stream", [2])])
+@pytest.mark.parametrize("name,rows", [("csa_decode_128k_b32", [0, 5, 13, 22, 31]),
+                                       ("csa_decode_1m_b8_stream", list(range(8)))])
 def test_indexer_fp8_decode_long_rows(name, rows):
     w = gen.WORKLOADS[name]
     d = gen.Draw(w.seed, DEV)
@@ -157,11 +165,12 @@ def test_indexer_fp8_decode_long_rows(name, rows):
     q_idx, q_scale, w_idx = gen.indexer_query(d, B, 1, w.H_I, w.d_I, gen.FP8)
     q_pos = [w.ctx - 1] * B
     g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, w.m, w.topk, q_pos, [Nc] * B, q_scale, k_scale)
-    for b in rows:
-        sl = slice(b, b + 1)
-        o = _oracle_rows(q_idx[sl], w_idx[sl], k_idx[sl], w.m, w.topk, [w.ctx - 1], [Nc],
-                         q_scale[sl], k_scale[sl])
-        _compare(g_idx[sl], g_sc[sl], o[3], w.m, w.topk, [w.ctx - 1], [Nc], Nc, "%s b%d" % (name, b))
+    # the sampled sequences in one oracle call (its rows run in parallel)
+    sl = torch.tensor(rows)
+    o = _oracle_rows(q_idx[sl], w_idx[sl], k_idx[sl], w.m, w.topk, [w.ctx - 1] * len(rows),
+                     [Nc] * len(rows), q_scale[sl], k_scale[sl])
+    _compare(g_idx[rows], g_sc[rows], o[3], w.m, w.topk, [w.ctx - 1] * len(rows),
+             [Nc] * len(rows), Nc, name)
 
 
 @pytest.mark.parametrize("name,rows", [("csa_decode_128k_b32", [0, 13, 31])])
