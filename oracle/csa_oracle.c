@@ -260,14 +260,73 @@ static void hadamard_rows(double* v, int E) {
   for (int e = 0; e < E; ++e) v[e] /= sqrt((double)E);
 }
 
+/* Entry post-processing, applied in this order to each emitted entry C_i
+ * (migration page, section 3.2: the compressor carries a norm submodule,
+ * ApplyRotaryPosEmb for the key positions, and a Hadamard step; section 4.3
+ * gives layernorm_epsilon and rotary_interleaved = False as its config):
+ *  - RMS norm (norm_w != NULL): C_e <- C_e / sqrt(mean_e C_e^2 + eps) * w_e
+ *    over the entry's E channels;
+ *  - rotary position embedding (rope_dim > 0): the channels
+ *    [rope_off, rope_off + rope_dim) rotate by the angles p * base^(-2k/rope_dim),
+ *    k < rope_dim / 2, at the entry's position p = m i (the first token of its
+ *    own block).  Non-interleaved: channel k pairs with k + rope_dim / 2;
+ *    interleaved: 2k with 2k + 1.  A pair (a, b) becomes
+ *    (a cos - b sin, b cos + a sin);
+ *  - the Hadamard rotation (rotate).
+ * The three readings (RMS norm over the whole entry, the block's first token
+ * as the position, this order) are the plainest ones the pages leave open. */
+typedef struct {
+  const double* norm_w;
+  double norm_eps;
+  int rope_dim, rope_off, rope_interleaved;
+  double rope_base;
+} orc_compress_opts;
+
+static void rms_norm_row(double* v, int E, const double* w, double eps) {
+  double ss = 0;
+  for (int e = 0; e < E; ++e) ss += v[e] * v[e];
+  const double r = 1.0 / sqrt(ss / E + eps);
+  for (int e = 0; e < E; ++e) v[e] = v[e] * r * w[e];
+}
+
+static void rope_row(double* v, int R, int interleaved, double base, int64_t pos) {
+  for (int k = 0; k < R / 2; ++k) {
+    const double ang = (double)pos * pow(base, -2.0 * k / R);
+    const double c = cos(ang), s = sin(ang);
+    const int i0 = interleaved ? 2 * k : k, i1 = interleaved ? 2 * k + 1 : k + R / 2;
+    const double a = v[i0], b = v[i1];
+    v[i0] = a * c - b * s;
+    v[i1] = b * c + a * s;
+  }
+}
+
+int orc_compress_ex(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                    const int64_t* pos0, const void* x, const void* w_kv,
+                    const void* w_gate, int in_dt, const double* ape,
+                    const double* state_in, double* state_out, int Nc_cap,
+                    double* out, uint8_t* written, const orc_compress_opts* opts);
+
 int orc_compress(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                  const int64_t* pos0, const void* x, const void* w_kv,
                  const void* w_gate, int in_dt, const double* ape,
                  const double* state_in, double* state_out, int Nc_cap,
                  double* out, uint8_t* written) {
+  return orc_compress_ex(B, L, d_model, E, m, overlap, rotate, pos0, x, w_kv, w_gate, in_dt,
+                         ape, state_in, state_out, Nc_cap, out, written, NULL);
+}
+
+int orc_compress_ex(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                    const int64_t* pos0, const void* x, const void* w_kv,
+                    const void* w_gate, int in_dt, const double* ape,
+                    const double* state_in, double* state_out, int Nc_cap,
+                    double* out, uint8_t* written, const orc_compress_opts* opts) {
   const int Sw = (1 + overlap) * m, ns = Sw - 1;
   if (B < 0 || L < 0 || m < 1 || E < 1 || d_model < 1) return 1;
   if (rotate && (E & (E - 1))) return 1;
+  if (opts && opts->rope_dim &&
+      (opts->rope_dim < 0 || opts->rope_dim % 2 || opts->rope_off < 0 ||
+       opts->rope_off + opts->rope_dim > E))
+    return 1;
   for (int b = 0; b < B; ++b) {
     const int64_t p0 = pos0[b];
     const int64_t base = p0 - ns; /* position of token-table row 0 */
@@ -327,6 +386,11 @@ int orc_compress(int B, int L, int d_model, int E, int m, int overlap, int rotat
           }
           out[((size_t)b * Nc_cap + i) * E + e] = num / den;
         }
+        if (opts && opts->norm_w)
+          rms_norm_row(out + ((size_t)b * Nc_cap + i) * E, E, opts->norm_w, opts->norm_eps);
+        if (opts && opts->rope_dim)
+          rope_row(out + ((size_t)b * Nc_cap + i) * E + opts->rope_off, opts->rope_dim,
+                   opts->rope_interleaved, opts->rope_base, (int64_t)m * i);
         if (rotate) hadamard_rows(out + ((size_t)b * Nc_cap + i) * E, E);
         if (written) written[(size_t)b * Nc_cap + i] = 1;
       }

@@ -39,6 +39,11 @@ def build() -> str:
 _lib = None
 
 
+class _Opts(C.Structure):
+    _fields_ = [("norm_w", C.c_void_p), ("norm_eps", C.c_double), ("rope_dim", C.c_int),
+                ("rope_off", C.c_int), ("rope_interleaved", C.c_int), ("rope_base", C.c_double)]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -47,6 +52,9 @@ def lib():
         L = C.CDLL(LIB)
         vp, i32, i64p, dp = C.c_void_p, C.c_int, C.c_void_p, C.c_void_p
         L.orc_compress.argtypes = [i32] * 7 + [i64p, vp, vp, vp, i32, dp, dp, dp, i32, dp, vp]
+        L.orc_compress_ex.argtypes = ([i32] * 7 + [i64p, vp, vp, vp, i32, dp, dp, dp, i32, dp, vp,
+                                      C.POINTER(_Opts)])
+        L.orc_compress_ex.restype = C.c_int
         L.orc_indexer_topk.argtypes = [i32] * 7 + [i64p, vp, vp, vp, vp, vp, vp, i32, vp, dp, dp, dp]
         L.orc_sparse_attn.argtypes = [i32] * 6 + [C.c_double, dp, i64p, vp, vp, i32, vp, vp, i32, i64p, i32, dp, dp]
         L.orc_hca_dense_attn.argtypes = [i32] * 6 + [C.c_double, dp, i64p, vp, vp, vp, i32, vp, i32, i64p, i32, dp, dp]
@@ -159,12 +167,17 @@ def quant_rows_e4m3(x):
 
 
 def compress(x, w_kv, w_gate, m, overlap, pos0, Nc_cap, ape=None, state_in=None,
-             want_state=True, rotate=False):
+             want_state=True, rotate=False, norm_weight=None, norm_eps=1e-6, rope_dim=0,
+             rope_offset=0, rope_base=10000.0, rope_interleaved=False):
     """Gated overlapping compressor.
 
     x [B, L, d_model], w_kv / w_gate [E, d_model] (same stored format);
     ape [(1+o) m, E] float; state_in [B, (1+o) m - 1, 2, E] float or None;
-    rotate: each entry times the Sylvester Hadamard matrix / sqrt(E).
+    each emitted entry then goes through, in this order: an RMS norm over its
+    E channels with weight norm_weight [E] (None: none), the rotary position
+    embedding of channels [rope_offset, rope_offset + rope_dim) at position
+    m * i (rope_dim 0: none; rotate-half pairs unless rope_interleaved), and
+    rotate: the Sylvester Hadamard matrix / sqrt(E).
     Returns (out [B, Nc_cap, E] float64 with NaN in unwritten rows,
     written [B, Nc_cap] bool, state_out or None).
     """
@@ -180,10 +193,12 @@ def compress(x, w_kv, w_gate, m, overlap, pos0, Nc_cap, ape=None, state_in=None,
     state_out = np.zeros((B, ns, 2, E), np.float64) if want_state else None
     out = np.full((B, Nc_cap, E), np.nan, np.float64)
     written = np.zeros((B, Nc_cap), np.uint8)
-    rc = lib().orc_compress(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(pos0), _p(x),
-                            _p(w_kv),
-                            _p(w_gate), dt, _p(ape), _p(state_in), _p(state_out),
-                            Nc_cap, _p(out), _p(written))
+    nw = _c(norm_weight, np.float64)
+    opts = _Opts(None if nw is None else nw.ctypes.data, float(norm_eps), int(rope_dim),
+                 int(rope_offset), int(bool(rope_interleaved)), float(rope_base))
+    rc = lib().orc_compress_ex(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(pos0), _p(x),
+                               _p(w_kv), _p(w_gate), dt, _p(ape), _p(state_in), _p(state_out),
+                               Nc_cap, _p(out), _p(written), C.byref(opts))
     assert rc == 0
     return out, written.astype(bool), state_out
 

@@ -711,3 +711,100 @@ def test_compress_ape_slot_orientation():
         out, _, _ = orc.compress(x, w_kv, w_gate, m, o, 0, S // m, ape=ape)
         for i in range(1, S // m):
             np.testing.assert_allclose(out[0, i], P[m * (i - o) + s], rtol=1e-9, atol=1e-12)
+
+# ---------------------------------------------------------------- compressor norm + RoPE
+# The migration page (section 3.2) lists a norm submodule and
+# ApplyRotaryPosEmb(config, for_k_pos_emb=True) inside the compressor;
+# section 4.3 gives layernorm_epsilon = 1e-6 and rotary_interleaved = False.
+# Readings: RMS norm over the entry, rotation of a channel slice at the
+# entry's position m * i (first token of its own block), norm before RoPE
+# before the Hadamard step.
+
+def _rope_case(seed, E=32, m=4, L=48):
+    r = rng(seed)
+    x = r.normal(0, 1, (2, L, 16)).astype(np.float32)
+    wk = r.normal(0, 0.25, (E, 16)).astype(np.float32)
+    wg = r.normal(0, 0.25, (E, 16)).astype(np.float32)
+    return x, wk, wg, m
+
+
+def _library_inv_freq(R, base):
+    from transformers import LlamaConfig
+    from transformers.models.llama import modeling_llama as ml
+    c = LlamaConfig(hidden_size=R, num_attention_heads=1, head_dim=R,
+                    rope_parameters={"rope_theta": base, "rope_type": "default"})
+    return ml.LlamaRotaryEmbedding.compute_default_rope_parameters(c)[0].double()
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_compress_rope_matches_library_rotary_embedding(interleaved):
+    from transformers.models.gptj import modeling_gptj as mg
+    from transformers.models.llama import modeling_llama as ml
+    x, wk, wg, m = _rope_case(30 + interleaved)
+    E, R, off, base = 32, 16, 8, 5000.0
+    pos0 = [0, 36]
+    plain, wr, _ = orc.compress(x, wk, wg, m, 1, pos0, 24)
+    roped, wr2, _ = orc.compress(x, wk, wg, m, 1, pos0, 24, rope_dim=R, rope_offset=off,
+                                 rope_base=base, rope_interleaved=interleaved)
+    assert np.array_equal(wr, wr2) and wr.any()
+    # the frequency ladder of the library's default rotary embedding (fp32 there)
+    inv = 1.0 / base ** (np.arange(0, R, 2) / R)
+    np.testing.assert_allclose(inv, _library_inv_freq(R, base).numpy(), rtol=2e-6)
+    b, i = np.nonzero(wr)
+    pos = torch.tensor(m * i, dtype=torch.float64)
+    ang = pos[:, None] * torch.from_numpy(inv)[None, :]            # [n, R/2]
+    sl = torch.from_numpy(plain[b, i, off:off + R])                  # [n, R]
+    if interleaved:   # GPT-J's rotate-every-two
+        ref = mg.apply_rotary_pos_emb(sl[:, None, None, :], torch.sin(ang)[:, None, :],
+                                      torch.cos(ang)[:, None, :])[:, 0, 0]
+    else:             # Llama's rotate-half
+        emb = torch.cat([ang, ang], dim=-1)
+        ref, _ = ml.apply_rotary_pos_emb(sl[:, None, :], sl[:, None, :], emb.cos(), emb.sin())
+        ref = ref[:, 0]
+    np.testing.assert_allclose(roped[b, i, off:off + R], ref.numpy(), rtol=1e-12, atol=1e-12)
+    # channels outside the slice are untouched
+    keep = np.r_[0:off, off + R:E]
+    assert np.array_equal(roped[b, i][:, keep], plain[b, i][:, keep])
+
+
+def test_compress_rope_identity_at_zero_norm_kept_and_relative():
+    # entry 0 sits at position 0 (no rotation); every rotation keeps the
+    # entry's norm; with identical pooled entries (every block the same
+    # tokens), the inner product of two rotated entries depends only on how
+    # many blocks apart they are
+    r = rng(33)
+    E, R, m = 16, 16, 4
+    blk = r.normal(0, 1, (1, m, 16)).astype(np.float32)
+    x = np.tile(blk, (1, 12, 1))
+    wk = r.normal(0, 0.3, (E, 16)).astype(np.float32)
+    wg = r.normal(0, 0.3, (E, 16)).astype(np.float32)
+    plain, _, _ = orc.compress(x, wk, wg, m, 1, 0, 12)
+    roped, _, _ = orc.compress(x, wk, wg, m, 1, 0, 12, rope_dim=R)
+    np.testing.assert_array_equal(roped[0, 0], plain[0, 0])
+    np.testing.assert_allclose(np.linalg.norm(roped[0], axis=1), np.linalg.norm(plain[0], axis=1),
+                               rtol=1e-12)
+    np.testing.assert_allclose(plain[0, 1:], np.broadcast_to(plain[0, 1], (11, E)), rtol=1e-12)
+    for dd in (1, 3, 5):
+        dots = [roped[0, i] @ roped[0, i + dd] for i in range(1, 12 - dd)]
+        np.testing.assert_allclose(dots, dots[0], rtol=1e-9, atol=1e-12)
+    assert not np.allclose(roped[0, 2], plain[0, 2])
+
+
+def test_compress_rms_norm_matches_torch_and_order():
+    x, wk, wg, m = _rope_case(34)
+    E = 32
+    r = rng(35)
+    g = r.normal(1, 0.2, E)
+    plain, wr, _ = orc.compress(x, wk, wg, m, 1, [0, 4], 24)
+    normed, _, _ = orc.compress(x, wk, wg, m, 1, [0, 4], 24, norm_weight=g, norm_eps=1e-6)
+    b, i = np.nonzero(wr)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(plain[b, i]), (E,),
+                                       torch.from_numpy(g), eps=1e-6)
+    np.testing.assert_allclose(normed[b, i], ref.numpy(), rtol=1e-12, atol=1e-12)
+    # norm, then RoPE, then the Hadamard step
+    allp, _, _ = orc.compress(x, wk, wg, m, 1, [0, 4], 24, norm_weight=g, rope_dim=8,
+                              rope_offset=4, rotate=True)
+    ro, _, _ = orc.compress(x, wk, wg, m, 1, [0, 4], 24, norm_weight=g, rope_dim=8, rope_offset=4)
+    from scipy.linalg import hadamard
+    H = hadamard(E) / np.sqrt(E)
+    np.testing.assert_allclose(allp[b, i], ro[b, i] @ H.T, rtol=1e-12, atol=1e-12)
