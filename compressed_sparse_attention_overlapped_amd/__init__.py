@@ -41,6 +41,11 @@ class _CPageTable(C.Structure):
                 ("n_pages", C.c_int)]
 
 
+class _COpts(C.Structure):
+    _fields_ = [("norm_weight", C.c_void_p), ("norm_eps", C.c_float), ("rope_dim", C.c_int),
+                ("rope_offset", C.c_int), ("rope_base", C.c_float), ("rope_interleaved", C.c_int)]
+
+
 class PageTable:
     """Paged compressed caches (``csa_page_table_t`` in include/csa.h): logical
     entry j of sequence b is pool row ``block_table[b, j // page_size] *
@@ -100,6 +105,9 @@ def lib():
         L.csa_compress_paged.argtypes = ([i32] * 7 + [vp] * 4 + [i32, vp, vp, vp, vp, vp, i32, i32,
                                          pt, vp, sz, vp])
         L.csa_indexer_topk_paged.argtypes = [i32] * 7 + [vp] * 7 + [i32, pt, vp, vp, vp, sz, vp]
+        L.csa_compress_ex.argtypes = ([i32] * 7 + [vp] * 4 + [i32, vp, vp, vp, vp, vp, i32, i32,
+                                      pt, C.POINTER(_COpts), vp, sz, vp])
+        L.csa_compress_ex.restype = C.c_int
         L.csa_sparse_attn_paged.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, pt, vp, vp, i32,
                                             vp, i32, vp, vp, vp, sz, vp])
         L.csa_sparse_attn_noalloc.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32,
@@ -171,7 +179,9 @@ def hca_dense_attn_workspace_size(B, T, H, D, Nc_cap, window) -> int:
 # ---------------------------------------------------------------- calls
 
 def csa_compress(x, w_kv, w_gate, pos0, m, overlap, out, out_scale=None, ape=None,
-                 state_in=None, state_out=None, workspace=None, rotate=False, pages=None):
+                 state_in=None, state_out=None, workspace=None, rotate=False, pages=None,
+                 norm_weight=None, norm_eps=1e-6, rope_dim=0, rope_offset=0, rope_base=10000.0,
+                 rope_interleaved=False):
     """Gated overlapping compressor; see ``csa_compress`` in include/csa.h.
 
     x [B, L, d_model]; w_kv, w_gate [E, d_model]; pos0 int64 [B];
@@ -180,13 +190,30 @@ def csa_compress(x, w_kv, w_gate, pos0, m, overlap, out, out_scale=None, ape=Non
     (float8_e8m0fnu or uint8);
     ape f32 [(1+o) m, E]; state_in / state_out f32 [B, (1+o) m - 1, 2, E];
     rotate: entries times the Hadamard matrix / sqrt(E) before storage.
-    pages: a PageTable; out (and out_scale) are then pools [n_pages * page_size, ...]."""
-    _dense(x, w_kv, w_gate, pos0, out, out_scale, ape, state_in, state_out)
+    pages: a PageTable; out (and out_scale) are then pools [n_pages * page_size, ...].
+    norm_weight f32 [E] (RMS norm of each entry, eps norm_eps) and rope_dim / rope_offset /
+    rope_base / rope_interleaved (rotary embedding of a channel slice at the entry's
+    position m * i): csa_compress_opts_t in include/csa.h."""
+    _dense(x, w_kv, w_gate, pos0, out, out_scale, ape, state_in, state_out, norm_weight)
     B, L, d_model = x.shape
     E = w_kv.shape[0]
     ws, nb = _workspace(csa_compress_workspace_size(B, L, d_model, E, m, overlap, x.dtype), x,
                         workspace)
-    if pages is not None:
+    if norm_weight is not None or rope_dim:
+        if norm_weight is not None and (norm_weight.dtype != torch.float32 or
+                                        norm_weight.shape != (E,)):
+            raise ValueError("norm_weight must be a float32 tensor of shape [E]")
+        if pages is not None:
+            pages.check(B, out, out_scale)
+        opts = _COpts(None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps),
+                      int(rope_dim), int(rope_offset), float(rope_base), int(bool(rope_interleaved)))
+        nc_cap = pages.nc_cap if pages is not None else out.shape[1]
+        rc = lib().csa_compress_ex(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(pos0),
+                                   _p(x), _p(w_kv), _p(w_gate), _DT[x.dtype], _p(ape),
+                                   _p(state_in), _p(state_out), _p(out), _p(out_scale),
+                                   _DT[out.dtype], nc_cap, pages.c() if pages is not None else None,
+                                   C.byref(opts), _p(ws), nb, _stream(x))
+    elif pages is not None:
         pages.check(B, out, out_scale)
         rc = lib().csa_compress_paged(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(pos0),
                                       _p(x), _p(w_kv), _p(w_gate), _DT[x.dtype], _p(ape),

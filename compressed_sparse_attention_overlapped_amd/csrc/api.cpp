@@ -84,7 +84,24 @@ static csa_status_t compress_impl(int B, int L, int d_model, int E, int m, int o
                           const void* w_gate, csa_dtype_t in_dt, const float* ape,
                           const float* state_in, float* state_out, void* out, void* out_scale,
                           csa_dtype_t out_dt, int Nc_cap, void* workspace, size_t ws_bytes,
-                          hipStream_t stream, const csa_page_table_t* pages) {
+                          hipStream_t stream, const csa_page_table_t* pages,
+                          const csa_compress_opts_t* opts) {
+  csa_host::EntryOpts eo{nullptr, 0.0f, 0, 0, 0, 10000.0f};
+  if (opts) {
+    const int R = opts->rope_dim;
+    if (R < 0 || (R & 1) || opts->rope_offset < 0 || (int64_t)opts->rope_offset + R > E)
+      return fail(CSA_E_ARG,
+                  "csa_compress: rope_dim must be even and [rope_offset, rope_offset + rope_dim) "
+                  "inside [0, E)");
+    if (R > 0 && !(opts->rope_base > 0.0f))
+      return fail(CSA_E_ARG, "csa_compress: rope_base must be > 0");
+    if (opts->rope_interleaved != 0 && opts->rope_interleaved != 1)
+      return fail(CSA_E_ARG, "csa_compress: rope_interleaved must be 0 or 1");
+    if (opts->norm_weight && !(opts->norm_eps >= 0.0f))
+      return fail(CSA_E_ARG, "csa_compress: norm_eps must be >= 0");
+    eo = csa_host::EntryOpts{opts->norm_weight, opts->norm_eps, R, opts->rope_offset,
+                             opts->rope_interleaved, opts->rope_base};
+  }
   if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0 || Nc_cap < 0)
     return fail(CSA_E_ARG, "csa_compress: B, L, d_model, E must be > 0 and Nc_cap >= 0");
   if (m < 1) return fail(CSA_E_ARG, "csa_compress: m must be >= 1 (got %d)", m);
@@ -119,6 +136,7 @@ static csa_status_t compress_impl(int B, int L, int d_model, int E, int m, int o
   csa_host::CompressArgs a{B, L, d_model, E, m, overlap, rotate, Nc_cap, pos0, x, w_kv, w_gate,
                            in_dt, out_dt, ape, state_in, state_out, out, out_scale, workspace};
   a.pages = pt;
+  a.opt = eo;
   return hip_status(csa_host::launch_compress(a, stream), "csa_compress launch");
 }
 
@@ -130,7 +148,7 @@ csa_status_t csa_compress(int B, int L, int d_model, int E, int m, int overlap, 
                           hipStream_t stream) {
   return compress_impl(B, L, d_model, E, m, overlap, rotate, pos0, x, w_kv, w_gate, in_dt, ape,
                        state_in, state_out, out, out_scale, out_dt, Nc_cap, workspace, ws_bytes,
-                       stream, nullptr);
+                       stream, nullptr, nullptr);
 }
 
 csa_status_t csa_compress_paged(int B, int L, int d_model, int E, int m, int overlap, int rotate,
@@ -143,7 +161,19 @@ csa_status_t csa_compress_paged(int B, int L, int d_model, int E, int m, int ove
   if (!pages) return fail(CSA_E_ARG, "csa_compress_paged: pages is required");
   return compress_impl(B, L, d_model, E, m, overlap, rotate, pos0, x, w_kv, w_gate, in_dt, ape,
                        state_in, state_out, out, out_scale, out_dt, Nc_cap, workspace, ws_bytes,
-                       stream, pages);
+                       stream, pages, nullptr);
+}
+
+csa_status_t csa_compress_ex(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                             const int64_t* pos0, const void* x, const void* w_kv,
+                             const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                             const float* state_in, float* state_out, void* out,
+                             void* out_scale, csa_dtype_t out_dt, int Nc_cap,
+                             const csa_page_table_t* pages, const csa_compress_opts_t* opts,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return compress_impl(B, L, d_model, E, m, overlap, rotate, pos0, x, w_kv, w_gate, in_dt, ape,
+                       state_in, state_out, out, out_scale, out_dt, Nc_cap, workspace, ws_bytes,
+                       stream, pages, opts);
 }
 
 size_t csa_indexer_topk_workspace_size(int B, int T, int H_I, int d_I, int Nc_cap, int topk,

@@ -160,6 +160,15 @@ __device__ __forceinline__ int32_t page_or_absent(const PageTable& pt, int b, in
 
 namespace csa_host {
 
+// Optional post-processing of every emitted compressor entry (RMS norm,
+// rotary position embedding of a channel slice); null / 0 = none.
+struct EntryOpts {
+  const float* norm_w;
+  float norm_eps;
+  int rope_dim, rope_off, rope_interleaved;
+  float rope_base;
+};
+
 struct CompressArgs {
   int B, L, d_model, E, m, overlap, rotate, Nc_cap;
   const int64_t* pos0;
@@ -174,6 +183,7 @@ struct CompressArgs {
   void* out_scale;
   void* ws;
   csa::PageTable pages;  // block_table null: unpaged out
+  EntryOpts opt;
 };
 size_t compress_ws_bytes(int B, int L, int d_model, int E, int m, int overlap, csa_dtype_t in_dt);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);

@@ -258,7 +258,8 @@ __global__ void __launch_bounds__(256) pool_kernel(
     const float* __restrict__ pg, const int64_t* __restrict__ pos0, int B, int L,
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, void* __restrict__ out_scale,
-    int Nc_cap, int n_slots, int n_split, bool rotate, float rot_scale, PageTable pt) {
+    int Nc_cap, int n_slots, int n_split, bool rotate, float rot_scale, PageTable pt,
+    csa_host::EntryOpts opt) {
   const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
   const int ns = (1 + overlap) * m - 1;
   const int64_t p0 = pos0[b];
@@ -467,8 +468,53 @@ __global__ void __launch_bounds__(256) pool_kernel(
     vals[nv] = c;
     amax = fmaxf(amax, fabsf(c));
   }
+  // Post-processing of the entry, in this order (each branch uniform): RMS
+  // norm over the E channels, the rotary embedding of the channel slice
+  // [rope_off, rope_off + rope_dim) at the entry's position m i, and the
+  // Hadamard rotation.  The angles are formed in double precision (positions
+  // reach 2^20 and beyond), then rounded to fp32 sines and cosines.
+  __shared__ float hb[1024];
+  if (opt.norm_w) {
+    float ss = 0.0f;
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) ss = fmaf(vals[nv], vals[nv], ss);
+    red[tid] = ss;
+    __syncthreads();
+    for (int o = (int)blockDim.x / 2; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    const float r = 1.0f / sqrtf(red[0] / (float)E + opt.norm_eps);
+    __syncthreads();  // red is reused by the fp8 store
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) vals[nv] = vals[nv] * r * opt.norm_w[e];
+  }
+  if (opt.rope_dim) {
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) hb[e] = vals[nv];
+    __syncthreads();
+    const int R = opt.rope_dim, half = R / 2;
+    const double pos = (double)m * (double)i;
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) {
+      const int c = e - opt.rope_off;
+      if (c < 0 || c >= R) continue;
+      const int k = opt.rope_interleaved ? c >> 1 : (c < half ? c : c - half);
+      const bool first = opt.rope_interleaved ? (c & 1) == 0 : c < half;
+      const int partner = opt.rope_interleaved ? (first ? e + 1 : e - 1) : (first ? e + half : e - half);
+      const double ang = pos * pow((double)opt.rope_base, -2.0 * k / R);
+      const float cs = (float)cos(ang), sn = (float)sin(ang);
+      const float pv = hb[partner];
+      vals[nv] = fmaf(vals[nv], cs, (first ? -pv : pv) * sn);
+    }
+    __syncthreads();  // hb is reused by the Hadamard step
+  }
+  if (opt.norm_w || opt.rope_dim) {
+    amax = 0.0f;
+    nv = 0;
+    for (int e = tid; e < E; e += blockDim.x, ++nv) amax = fmaxf(amax, fabsf(vals[nv]));
+  }
   if (rotate) {  // uniform: the entry times H_E / sqrt(E) (Sylvester order)
-    __shared__ float hb[1024];
     nv = 0;
     for (int e = tid; e < E; e += blockDim.x, ++nv) hb[e] = vals[nv];
     __syncthreads();
@@ -584,7 +630,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   pool_kernel<DT, W, NS><<<pgrid, pthreads, 0, st>>>(                                           \
       pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,           \
       a.out_scale, a.Nc_cap, n_slots, splits, a.rotate != 0, (float)(1.0 / std::sqrt((double)E)), \
-      a.pages)
+      a.pages, a.opt)
 #define CSA_POOL_DT(DT)                            \
   if (w8 == 1) CSA_LAUNCH_POOL(DT, 8, 1);          \
   else if (w8 == 4) CSA_LAUNCH_POOL(DT, 8, 4);     \

@@ -121,6 +121,54 @@ size_t csa_compress_workspace_size(int B, int L, int d_model, int E, int m, int 
                                    csa_dtype_t in_dt);
 
 /*
+ * Post-processing of every emitted compressor entry (migration notes section
+ * 3.2: the compressor carries a norm submodule and applies the rotary
+ * position embedding to the key positions, ApplyRotaryPosEmb with
+ * for_k_pos_emb; section 4.3: layernorm_epsilon 1e-6, rotary_interleaved
+ * False).  Applied to the pooled entry C_i, in this order, before the
+ * Hadamard rotation and the storage rounding:
+ *  norm_weight      device fp32 [E], or NULL for no norm: RMS norm over the
+ *                   entry, C_e <- C_e / sqrt(mean_e C_e^2 + norm_eps) * w_e
+ *  norm_eps         >= 0
+ *  rope_dim         0 (none) or an even count of channels starting at
+ *                   rope_offset (rope_offset + rope_dim <= E) that rotate by
+ *                   the angles p * rope_base^(-2k / rope_dim), k <
+ *                   rope_dim / 2, at the entry's position p = m i (the first
+ *                   token of its own block; angles in double precision)
+ *  rope_interleaved 0: channel k of the slice pairs with k + rope_dim / 2
+ *                   ("rotate half"); 1: channel 2k pairs with 2k + 1.  A pair
+ *                   (a, b) becomes (a cos - b sin, b cos + a sin)
+ *  rope_base        > 0 when rope_dim > 0 (10000 is the usual value)
+ * For the main compressor (E = 2 D = [K | V]) the key's rotary channels are
+ * a slice of the first D channels; queries get the same rotation at their
+ * token positions from the caller.
+ */
+typedef struct {
+  const float* norm_weight;
+  float norm_eps;
+  int rope_dim;
+  int rope_offset;
+  float rope_base;
+  int rope_interleaved;
+} csa_compress_opts_t;
+
+/*
+ * csa_compress with the entry post-processing above (opts, or NULL for
+ * none) and an optional paged output (pages, or NULL for the [B, Nc_cap,
+ * ...] layout; see csa_page_table_t below).  Everything else, the workspace
+ * included, is as in csa_compress.  Errors: CSA_E_ARG for a rotary slice
+ * outside the entry, an odd rope_dim, rope_base <= 0 or norm_eps < 0.
+ */
+typedef struct csa_page_table_s csa_page_table_t;
+csa_status_t csa_compress_ex(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                             const int64_t* pos0, const void* x, const void* w_kv,
+                             const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                             const float* state_in, float* state_out, void* out,
+                             void* out_scale, csa_dtype_t out_dt, int Nc_cap,
+                             const csa_page_table_t* pages, const csa_compress_opts_t* opts,
+                             void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Lightning Indexer score and per-query top-k (DS-V4 analysis section 1.2;
  * article section 3.2: score each query against every compressed entry, keep
  * the top k).  Score, with sq = q_scale and sk = k_scale (1 unless fp8):
@@ -248,12 +296,12 @@ size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int
  * The struct is read on the host during the call; the caller owns it and the
  * table.  Errors: CSA_E_ARG for a missing table or a bad size.
  */
-typedef struct {
+struct csa_page_table_s {
   const int32_t* block_table;
   int page_size;
   int max_pages;
   int n_pages;
-} csa_page_table_t;
+};
 
 /*
  * csa_compress with a paged output: out (and out_scale) are pools of

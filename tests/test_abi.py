@@ -159,3 +159,16 @@ def test_page_table_checks_reject_bad_tables_before_any_call():
         pt.check(2, pool)                       # a host table with the caches
     with pytest.raises(ValueError, match="int32"):
         csa.PageTable(table.long(), 16, 8)
+
+
+def test_compress_ex_rejects_bad_rotary_slices(L):
+    import compressed_sparse_attention_overlapped_amd as csa
+    vp = C.c_void_p
+    p = vp(256)
+    for dim, off, base, ok in ((3, 0, 1e4, False), (16, 60, 1e4, False), (16, 0, 0.0, False),
+                               (-2, 0, 1e4, False)):
+        o = csa._COpts(None, 1e-6, dim, off, base, 0)
+        rc = L.csa_compress_ex(1, 4, 64, 64, 4, 1, 0, p, p, p, p, 0, None, None, None, p, None, 0,
+                               8, None, C.byref(o), None, 0, None)
+        assert rc == 1, (dim, off, base)
+        assert b"rope" in L.csa_last_error()

@@ -353,3 +353,86 @@ def test_compress_bf16_ragged_tiles_and_split_k():
         assert np.isnan(g[b, ~wr]).all()
         assert_rows_rel(g[b, wr], ref[b, wr], 1e-5, "compress bf16 ragged tiles")
     np.testing.assert_allclose(st.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=2e-5, atol=2e-5)
+
+
+def _run_opts(x, w_kv, w_gate, pos0, m, o, Nc_cap, out_dtype, state_in=None, **opts):
+    B, E = x.shape[0], w_kv.shape[0]
+    out = torch.full((B, Nc_cap, E), float("nan"), device=DEV).to(out_dtype)
+    out_scale = torch.zeros(B, Nc_cap, device=DEV) if out_dtype == torch.float8_e4m3fn else None
+    ns = (1 + o) * m - 1
+    state_out = torch.zeros(B, ns, 2, E, device=DEV)
+    csa.csa_compress(x, w_kv, w_gate, dev_i64(pos0), m, o, out, out_scale=out_scale,
+                     state_in=state_in, state_out=state_out, **opts)
+    torch.cuda.synchronize()
+    return out, out_scale, state_out
+
+
+@pytest.mark.parametrize("out_kind,interleaved,rotate", [("f32", False, False), ("f32", True, False),
+                                                          ("bf16", False, True), ("fp8", False, False)])
+def test_compress_norm_and_rope_chunks(out_kind, interleaved, rotate):
+    # RMS norm + rotary embedding of a slice of the K half (E = 2 D, D = 64:
+    # channels 32..63), ragged starts, a carried state between two chunks;
+    # positions reach past 2^18 tokens
+    d = gen.Draw(90 + interleaved + 2 * rotate)
+    B, L, dm, E, m, o = 3, 45, 256, 128, 4, 1
+    x = gen.store(d.normal(B, 2 * L, dm), gen.BF16)
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    g = 1.0 + 0.2 * d.normal(E)
+    pos0 = [0, 13, (1 << 18) + 3]
+    Nc = ((1 << 18) + 3 + 2 * L) // m + 1
+    opts = dict(norm_weight=g, norm_eps=1e-6, rope_dim=32, rope_offset=32, rope_base=10000.0,
+                rope_interleaved=interleaved)
+    odt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "f32": torch.float32}[out_kind]
+    xg, wk, wg = x.to(DEV), w_kv.to(DEV), w_gate.to(DEV)
+    gopts = dict(opts, norm_weight=g.to(DEV))
+    # two chunks: the second starts where the first ended and takes its state
+    out1, sc1, st1 = _run_opts(xg[:, :L].contiguous(), wk, wg, pos0, m, o, Nc, odt, rotate=rotate,
+                               **gopts)
+    out2, sc2, _ = _run_opts(xg[:, L:].contiguous(), wk, wg, [p + L for p in pos0], m, o, Nc, odt,
+                             state_in=st1, rotate=rotate, **gopts)
+    oo = dict(opts, norm_weight=g.numpy())
+    r1, w1, s1 = orc.compress(gen.host_bits(x[:, :L]), gen.host_bits(w_kv), gen.host_bits(w_gate),
+                              m, o, np.asarray(pos0), Nc, rotate=rotate, **oo)
+    r2, w2, _ = orc.compress(gen.host_bits(x[:, L:]), gen.host_bits(w_kv), gen.host_bits(w_gate),
+                             m, o, np.asarray(pos0) + L, Nc, state_in=s1, rotate=rotate, **oo)
+    for out, sc, ref, wr in ((out1, sc1, r1, w1), (out2, sc2, r2, w2)):
+        for b in range(B):
+            rows = np.nonzero(wr[b])[0]
+            assert rows.size > 0
+            if out_kind == "f32":
+                assert_rows_rel(out[b, rows].cpu().numpy(), ref[b, rows], 1e-5, "norm+rope f32")
+            elif out_kind == "bf16":
+                assert_bf16_close(out[b, rows].float().cpu().numpy(), ref[b, rows], "norm+rope bf16")
+            else:
+                codes, scales = orc.quant_rows_e4m3(ref[b, rows])
+                np.testing.assert_allclose(sc[b, rows].cpu().numpy(), scales, rtol=1e-5)
+                gv = (gen.host_bits(out[b, rows]).astype(np.int64))
+                gvv = np.vectorize(orc.e4m3_decode)(gv)
+                rv = np.vectorize(orc.e4m3_decode)(codes)
+                step = np.maximum(np.abs(rv), 2.0 ** -6) * 2.0 ** -3
+                assert (np.abs(gvv - rv) <= step + 1e-12).all()
+
+
+def test_compress_rope_decode_step_at_1m():
+    # the one-token decode step (few-row projection with split partials)
+    # emitting entry 262143 at position 2^20 - 4, RMS norm + RoPE, fp32 store
+    d = gen.Draw(95)
+    B, dm, E, m, o = 8, 4096, 256, 4, 1
+    wk, wg = gen.compressor_weights(d, dm, E, gen.BF16)
+    x_tail = gen.store(d.normal(B, 7, dm), gen.BF16)
+    x_new = gen.store(d.normal(B, 1, dm), gen.BF16)
+    g = 1.0 + 0.1 * d.normal(E)
+    T = 1 << 20
+    Nc = T // m
+    opts = dict(norm_weight=g.to(DEV), norm_eps=1e-6, rope_dim=64, rope_offset=64)
+    _, _, st = _run_opts(x_tail.to(DEV), wk.to(DEV), wg.to(DEV), [T - 8] * B, m, o, Nc,
+                         torch.float32, **opts)
+    out, _, _ = _run_opts(x_new.to(DEV), wk.to(DEV), wg.to(DEV), [T - 1] * B, m, o, Nc,
+                          torch.float32, state_in=st, **opts)
+    oo = dict(norm_weight=g.numpy(), norm_eps=1e-6, rope_dim=64, rope_offset=64)
+    _, _, s_ref = orc.compress(gen.host_bits(x_tail), gen.host_bits(wk), gen.host_bits(wg), m, o,
+                               np.full(B, T - 8), Nc, **oo)
+    ref, wr, _ = orc.compress(gen.host_bits(x_new), gen.host_bits(wk), gen.host_bits(wg), m, o,
+                              np.full(B, T - 1), Nc, state_in=s_ref, **oo)
+    assert wr[:, Nc - 1].all()
+    assert_rows_rel(out[:, Nc - 1].cpu().numpy(), ref[:, Nc - 1], 1e-5, "decode rope at 1M")
