@@ -17,7 +17,8 @@ from typing import Optional
 import torch
 
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
-           "csa_sparse_attn_noalloc",
+           "csa_sparse_attn_noalloc", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
+           "csa_indexer_topk_varlen", "csa_sparse_attn_varlen",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
            "CsaError", "PageTable", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
@@ -108,6 +109,21 @@ def lib():
         L.csa_compress_ex.argtypes = ([i32] * 7 + [vp] * 4 + [i32, vp, vp, vp, vp, vp, i32, i32,
                                       pt, C.POINTER(_COpts), vp, sz, vp])
         L.csa_compress_ex.restype = C.c_int
+        L.csa_build_cmp_cu_seqlens.argtypes = [i32, vp, i32, vp, vp]
+        L.csa_compress_varlen.argtypes = ([i32] * 8 + [vp] * 5 + [i32, vp, vp, vp, vp, i32,
+                                          C.POINTER(_COpts), vp, sz, vp])
+        L.csa_compress_varlen_workspace_size.argtypes = [i32] * 6
+        L.csa_indexer_topk_varlen.argtypes = ([i32] * 8 + [vp] * 5 + [i32, vp, vp, vp, sz, vp])
+        L.csa_indexer_topk_varlen_workspace_size.argtypes = [i32] * 4
+        L.csa_sparse_attn_varlen.argtypes = ([i32] * 7 + [f32] + [vp] * 5 + [i32, vp, vp, i32,
+                                             vp, vp, vp, sz, vp])
+        L.csa_sparse_attn_varlen_workspace_size.argtypes = [i32] * 5
+        for f in (L.csa_build_cmp_cu_seqlens, L.csa_compress_varlen, L.csa_indexer_topk_varlen,
+                  L.csa_sparse_attn_varlen):
+            f.restype = C.c_int
+        for f in (L.csa_compress_varlen_workspace_size, L.csa_indexer_topk_varlen_workspace_size,
+                  L.csa_sparse_attn_varlen_workspace_size):
+            f.restype = C.c_size_t
         L.csa_sparse_attn_paged.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, pt, vp, vp, i32,
                                             vp, i32, vp, vp, vp, sz, vp])
         L.csa_sparse_attn_noalloc.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32,
@@ -339,4 +355,104 @@ def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=N
                               _p(kv_cmp), kv_cmp.shape[1], _p(kv_raw), kv_raw.shape[1],
                               _p(raw_base), _DT[q.dtype], _p(out), _p(lse), _p(ws), nb, _stream(q))
     _check("hca_dense_attn", rc)
+    return out, lse
+
+
+# ---------------------------------------------------------------- packed sequences
+
+def _cu(t, n1):
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != n1 or not t.is_cuda:
+        raise ValueError("sequence offsets must be device int32 tensors of n + 1 elements")
+    return t
+
+
+def csa_build_cmp_cu_seqlens(cu_seqlens, m):
+    """Entry offsets of packed sequences: [0, floor(len_0 / m), ...] cumulated (device int32)."""
+    n = cu_seqlens.numel() - 1
+    out = torch.empty(n + 1, dtype=torch.int32, device=cu_seqlens.device)
+    rc = lib().csa_build_cmp_cu_seqlens(n, _p(_cu(cu_seqlens, n + 1)), m, _p(out),
+                                        _stream(cu_seqlens))
+    _check("csa_build_cmp_cu_seqlens", rc)
+    return out
+
+
+def _opts(norm_weight, norm_eps, rope_dim, rope_offset, rope_base, rope_interleaved, E):
+    if norm_weight is None and not rope_dim:
+        return None
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or
+                                    norm_weight.shape != (E,)):
+        raise ValueError("norm_weight must be a float32 tensor of shape [E]")
+    return C.byref(_COpts(None if norm_weight is None else norm_weight.data_ptr(),
+                          float(norm_eps), int(rope_dim), int(rope_offset), float(rope_base),
+                          int(bool(rope_interleaved))))
+
+
+def csa_compress_varlen(x, w_kv, w_gate, cu_seqlens, cmp_cu_seqlens, max_len, m, overlap, out,
+                        out_scale=None, ape=None, state_out=None, rotate=False, workspace=None,
+                        norm_weight=None, norm_eps=1e-6, rope_dim=0, rope_offset=0,
+                        rope_base=10000.0, rope_interleaved=False):
+    """Compressor over packed sequences (csa_compress_varlen in include/csa.h):
+    x [total, d_model]; out [total entries, E] (rows from cmp_cu_seqlens)."""
+    _dense(x, w_kv, w_gate, out, out_scale, ape, state_out, norm_weight)
+    total, d_model = x.shape
+    E = w_kv.shape[0]
+    n = cu_seqlens.numel() - 1
+    ws, nb = _workspace(lib().csa_compress_varlen_workspace_size(total, d_model, E, m, overlap,
+                                                                 _DT[x.dtype]), x, workspace)
+    rc = lib().csa_compress_varlen(n, total, int(max_len), d_model, E, m, overlap,
+                                   int(bool(rotate)), _p(_cu(cu_seqlens, n + 1)),
+                                   _p(_cu(cmp_cu_seqlens, n + 1)), _p(x), _p(w_kv), _p(w_gate),
+                                   _DT[x.dtype], _p(ape), _p(state_out), _p(out), _p(out_scale),
+                                   _DT[out.dtype],
+                                   _opts(norm_weight, norm_eps, rope_dim, rope_offset, rope_base,
+                                         rope_interleaved, E), _p(ws), nb, _stream(x))
+    _check("csa_compress_varlen", rc)
+    return out
+
+
+def csa_indexer_topk_varlen(q_idx, w_idx, k_idx, cu_seqlens, cmp_cu_seqlens, max_len, max_cmp,
+                            m, topk, idx_out=None, score_out=None, want_scores=False,
+                            workspace=None):
+    """Indexer top-k over packed sequences: q_idx [total, H_I, d_I], w_idx [total, H_I],
+    k_idx [total entries, d_I]; returns (idx [total, topk] local to each sequence, scores)."""
+    _dense(q_idx, w_idx, k_idx)
+    total, H_I, d_I = q_idx.shape
+    n = cu_seqlens.numel() - 1
+    if idx_out is None:
+        idx_out = torch.empty(total, topk, dtype=torch.int32, device=q_idx.device)
+    if want_scores and score_out is None:
+        score_out = torch.empty(total, topk, dtype=torch.float32, device=q_idx.device)
+    ws, nb = _workspace(lib().csa_indexer_topk_varlen_workspace_size(total, max(1, max_cmp), topk,
+                                                                     _DT[q_idx.dtype]),
+                        q_idx, workspace)
+    rc = lib().csa_indexer_topk_varlen(n, total, int(max_len), H_I, d_I, int(max_cmp), m, topk,
+                                       _p(_cu(cu_seqlens, n + 1)), _p(_cu(cmp_cu_seqlens, n + 1)),
+                                       _p(q_idx), _p(w_idx), _p(k_idx), _DT[q_idx.dtype],
+                                       _p(idx_out), _p(score_out), _p(ws), nb, _stream(q_idx))
+    _check("csa_indexer_topk_varlen", rc)
+    return idx_out, score_out
+
+
+def csa_sparse_attn_varlen(q, kv_cmp, idx, kv_raw, cu_seqlens, cmp_cu_seqlens, max_len, max_cmp,
+                           window, scale=None, out=None, lse=None, want_lse=False, sink=None,
+                           workspace=None):
+    """CSA attention over packed sequences: q [total, H, D], kv_cmp [total entries, 2D],
+    idx [total, topk] local indices, kv_raw [total, 2D]; returns (out, lse)."""
+    _dense(q, kv_cmp, idx, kv_raw, sink)
+    total, H, D = q.shape
+    n = cu_seqlens.numel() - 1
+    topk = idx.shape[1] if idx is not None else 0
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(total, H, dtype=torch.float32, device=q.device)
+    ws, nb = _workspace(lib().csa_sparse_attn_varlen_workspace_size(total, H, D, topk, window), q,
+                        workspace)
+    rc = lib().csa_sparse_attn_varlen(n, total, int(max_len), H, D, topk, window, scale,
+                                      _p(_sink(sink, H)), _p(_cu(cu_seqlens, n + 1)),
+                                      _p(_cu(cmp_cu_seqlens, n + 1)), _p(q), _p(kv_cmp),
+                                      int(max_cmp), _p(idx), _p(kv_raw), _DT[q.dtype], _p(out),
+                                      _p(lse), _p(ws), nb, _stream(q))
+    _check("csa_sparse_attn_varlen", rc)
     return out, lse

@@ -393,4 +393,171 @@ csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float
   return hip_status(csa_host::launch_attn(a, stream), "hca_dense_attn launch");
 }
 
+/* ---- packed variable-length sequences --------------------------------- */
+
+csa_status_t csa_build_cmp_cu_seqlens(int n, const int32_t* cu_seqlens, int m,
+                                      int32_t* cmp_cu_seqlens, hipStream_t stream) {
+  if (n < 1 || m < 1 || !cu_seqlens || !cmp_cu_seqlens)
+    return fail(CSA_E_ARG, "csa_build_cmp_cu_seqlens: n, m >= 1 and both arrays are required");
+  return hip_status(csa_host::launch_cmp_cu(n, cu_seqlens, m, cmp_cu_seqlens, stream),
+                    "csa_build_cmp_cu_seqlens launch");
+}
+
+static csa_status_t check_varlen(const char* fn, int n, int total, int max_len,
+                                 const int32_t* cu, const int32_t* cmp_cu) {
+  if (n < 1 || total < 1 || max_len < 1)
+    return fail(CSA_E_ARG, "%s: n, total and max_len must be >= 1", fn);
+  if (!cu || !cmp_cu) return fail(CSA_E_ARG, "%s: cu_seqlens and cmp_cu_seqlens are required", fn);
+  return CSA_OK;
+}
+
+size_t csa_compress_varlen_workspace_size(int total, int d_model, int E, int m, int overlap,
+                                          csa_dtype_t in_dt) {
+  if (total <= 0 || d_model <= 0 || E <= 0) return 0;
+  return csa_host::compress_ws_bytes(1, total, d_model, E, m, overlap, in_dt);
+}
+
+csa_status_t csa_compress_varlen(int n, int total, int max_len, int d_model, int E, int m,
+                                 int overlap, int rotate, const int32_t* cu_seqlens,
+                                 const int32_t* cmp_cu_seqlens, const void* x, const void* w_kv,
+                                 const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                                 float* state_out, void* out, void* out_scale, csa_dtype_t out_dt,
+                                 const csa_compress_opts_t* opts, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream) {
+  csa_status_t st = check_varlen("csa_compress_varlen", n, total, max_len, cu_seqlens,
+                                 cmp_cu_seqlens);
+  if (st != CSA_OK) return st;
+  static const int64_t zero = 0;  // a stand-in pos0 (packed sequences start at 0)
+  const size_t need = csa_host::compress_ws_bytes(1, total, d_model, E, m, overlap, in_dt);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "csa_compress_varlen: workspace %zu < %zu bytes", ws_bytes, need);
+  if (m < 1) return fail(CSA_E_ARG, "csa_compress_varlen: m must be >= 1");
+  if (overlap != 0 && overlap != 1)
+    return fail(CSA_E_ARG, "csa_compress_varlen: overlap must be 0 or 1");
+  if (rotate != 0 && rotate != 1) return fail(CSA_E_ARG, "csa_compress_varlen: rotate must be 0 or 1");
+  if (rotate && (E & (E - 1)))
+    return fail(CSA_E_ARG, "csa_compress_varlen: rotate needs E a power of two (got %d)", E);
+  if (!x || !w_kv || !w_gate || !out)
+    return fail(CSA_E_ARG, "csa_compress_varlen: x, w_kv, w_gate and out are required");
+  if (in_dt != CSA_DT_F32 && in_dt != CSA_DT_BF16)
+    return fail(CSA_E_UNSUPPORTED, "csa_compress_varlen: in_dt must be F32 or BF16");
+  if (out_dt != CSA_DT_F32 && out_dt != CSA_DT_BF16 && out_dt != CSA_DT_FP8E4M3 &&
+      out_dt != CSA_DT_MXFP4)
+    return fail(CSA_E_ARG, "csa_compress_varlen: bad out_dt %d", (int)out_dt);
+  if ((out_dt == CSA_DT_FP8E4M3 || out_dt == CSA_DT_MXFP4) && !out_scale)
+    return fail(CSA_E_ARG, "csa_compress_varlen: fp8 and mxfp4 outputs need out_scale");
+  if (out_dt == CSA_DT_MXFP4 && E % 32 != 0)
+    return fail(CSA_E_UNSUPPORTED, "csa_compress_varlen: mxfp4 output needs E %% 32 == 0");
+  if (E > 1024) return fail(CSA_E_UNSUPPORTED, "csa_compress_varlen: E > 1024");
+  if (in_dt == CSA_DT_BF16 && (d_model % 64 != 0 || !aligned16(x) || !aligned16(w_kv) ||
+                               !aligned16(w_gate)))
+    return fail(CSA_E_UNSUPPORTED,
+                "csa_compress_varlen: bf16 needs d_model %% 64 == 0 and 16-byte aligned x and "
+                "weights");
+  csa_host::EntryOpts eo{nullptr, 0.0f, 0, 0, 0, 10000.0f};
+  if (opts) {
+    const int R = opts->rope_dim;
+    if (R < 0 || (R & 1) || opts->rope_offset < 0 || (int64_t)opts->rope_offset + R > E ||
+        (R > 0 && !(opts->rope_base > 0.0f)) ||
+        (opts->rope_interleaved != 0 && opts->rope_interleaved != 1) ||
+        (opts->norm_weight && !(opts->norm_eps >= 0.0f)))
+      return fail(CSA_E_ARG, "csa_compress_varlen: bad rope / norm options");
+    eo = csa_host::EntryOpts{opts->norm_weight, opts->norm_eps, R, opts->rope_offset,
+                             opts->rope_interleaved, opts->rope_base};
+  }
+  csa_host::CompressArgs a{n, max_len, d_model, E, m, overlap, rotate, 0, &zero, x, w_kv,
+                           w_gate, in_dt, out_dt, ape, nullptr, state_out, out, out_scale,
+                           workspace};
+  a.opt = eo;
+  a.vl = csa::Varlen{cu_seqlens, cmp_cu_seqlens, n};
+  a.total_rows = total;
+  return hip_status(csa_host::launch_compress(a, stream), "csa_compress_varlen launch");
+}
+
+size_t csa_indexer_topk_varlen_workspace_size(int total, int max_cmp, int topk,
+                                              csa_dtype_t qk_dt) {
+  if (total <= 0 || max_cmp <= 0) return 0;
+  return csa_host::indexer_ws_bytes(1, total, 16, 64, max_cmp, topk, qk_dt);
+}
+
+csa_status_t csa_indexer_topk_varlen(int n, int total, int max_len, int H_I, int d_I,
+                                     int max_cmp, int m, int topk, const int32_t* cu_seqlens,
+                                     const int32_t* cmp_cu_seqlens, const void* q_idx,
+                                     const float* w_idx, const void* k_idx, csa_dtype_t qk_dt,
+                                     int32_t* idx_out, float* score_out, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream) {
+  csa_status_t st = check_varlen("csa_indexer_topk_varlen", n, total, max_len, cu_seqlens,
+                                 cmp_cu_seqlens);
+  if (st != CSA_OK) return st;
+  if (H_I <= 0 || d_I <= 0 || max_cmp < 0 || topk < 0 || m < 1)
+    return fail(CSA_E_ARG, "csa_indexer_topk_varlen: H_I, d_I, m >= 1; max_cmp, topk >= 0");
+  if (topk == 0) return ok();
+  if (!q_idx || !w_idx || !idx_out || (max_cmp > 0 && !k_idx))
+    return fail(CSA_E_ARG, "csa_indexer_topk_varlen: missing required pointer");
+  if (topk > 8192) return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_varlen: topk > 8192");
+  if (max_cmp > 8192)
+    return fail(CSA_E_UNSUPPORTED,
+                "csa_indexer_topk_varlen: sequences of more than 8192 entries are not supported");
+  if (qk_dt == CSA_DT_F32) {
+    if (!((H_I == 4 && d_I == 32) || (H_I == 16 && d_I == 64)))
+      return fail(CSA_E_UNSUPPORTED,
+                  "csa_indexer_topk_varlen: f32 needs (H_I, d_I) in {(4,32),(16,64)}");
+  } else if (qk_dt == CSA_DT_BF16) {
+    if (H_I != 16 || d_I != 64)
+      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_varlen: bf16 needs H_I = 16, d_I = 64");
+    if (!aligned16(q_idx) || (max_cmp > 0 && !aligned16(k_idx)))
+      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_varlen: q_idx, k_idx 16-byte aligned");
+  } else {
+    return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_varlen: qk_dt must be F32 or BF16");
+  }
+  const size_t need = csa_host::indexer_ws_bytes(1, total, H_I, d_I, max_cmp, topk, qk_dt);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "csa_indexer_topk_varlen: workspace %zu < %zu bytes", ws_bytes,
+                need);
+  // (max_cmp 0: no sequence has an entry and every row is padding; the
+  // kernels run with a one-entry cap and read no key)
+  csa_host::IndexerArgs a{n, max_len, H_I, d_I, max_cmp > 0 ? max_cmp : 1, m, topk, nullptr,
+                          nullptr, q_idx, nullptr, w_idx, k_idx, nullptr, qk_dt, idx_out,
+                          score_out, workspace};
+  a.vl = csa::Varlen{cu_seqlens, cmp_cu_seqlens, n};
+  a.total_rows = total;
+  return hip_status(csa_host::launch_indexer_topk(a, stream), "csa_indexer_topk_varlen launch");
+}
+
+size_t csa_sparse_attn_varlen_workspace_size(int total, int H, int D, int topk, int window) {
+  if (total <= 0 || H <= 0 || D <= 0) return 0;
+  return csa_host::attn_ws_bytes(1, total, H, D, topk + window, true);
+}
+
+csa_status_t csa_sparse_attn_varlen(int n, int total, int max_len, int H, int D, int topk,
+                                    int window, float scale, const float* sink,
+                                    const int32_t* cu_seqlens, const int32_t* cmp_cu_seqlens,
+                                    const void* q, const void* kv_cmp, int max_cmp,
+                                    const int32_t* idx, const void* kv_raw, csa_dtype_t dt,
+                                    void* out, float* lse, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  csa_status_t st = check_varlen("csa_sparse_attn_varlen", n, total, max_len, cu_seqlens,
+                                 cmp_cu_seqlens);
+  if (st != CSA_OK) return st;
+  static const int64_t zero = 0;
+  st = check_attn("csa_sparse_attn_varlen", 1, total, H, D, window, &zero, q, kv_cmp, max_cmp,
+                  kv_raw, max_len, &zero, dt, out);
+  if (st != CSA_OK) return st;
+  if (topk < 0) return fail(CSA_E_ARG, "csa_sparse_attn_varlen: topk must be >= 0");
+  if (topk > 0 && !idx) return fail(CSA_E_ARG, "csa_sparse_attn_varlen: idx is required");
+  if (!kv_raw) return fail(CSA_E_ARG, "csa_sparse_attn_varlen: kv_raw is required");
+  if (dt == CSA_DT_BF16 && !csa_host::attn_supported(1, total, H, topk + window, true))
+    return fail(CSA_E_UNSUPPORTED, "csa_sparse_attn_varlen: topk + window too large");
+  const size_t need =
+      dt == CSA_DT_F32 ? 0 : csa_host::attn_ws_bytes(1, total, H, D, topk + window, true);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "csa_sparse_attn_varlen: workspace %zu < %zu bytes", ws_bytes,
+                need);
+  csa_host::AttnArgs a{n, max_len, H, D, topk, window, 1, max_cmp, max_len, false, scale, sink,
+                       nullptr, nullptr, q, kv_cmp, idx, kv_raw, nullptr, dt, out, lse, workspace};
+  a.vl = csa::Varlen{cu_seqlens, cmp_cu_seqlens, n};
+  a.total_rows = total;
+  return hip_status(csa_host::launch_attn(a, stream), "csa_sparse_attn_varlen launch");
+}
+
 }  // extern "C"

@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, float scale_log2, const float* __restrict__ sink, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int64_t cmp_rows_b) {
+    float* __restrict__ lse, int64_t cmp_rows_b, Varlen vl) {
   constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH;
   constexpr bool dense = !SPARSE;
   // phase A uses tiles 0..1 (double buffer); phase B tile r per row
@@ -150,16 +150,29 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   const int tiles_per_b = (T + PF_ROWS - 1) / PF_ROWS;
   const int b = blockIdx.x / tiles_per_b;
   const int t0 = (blockIdx.x % tiles_per_b) * PF_ROWS;
+  // the sequence's rows, compressed entries and raw rows (packed sequences:
+  // offsets into the packed tensors, the raw rows being the sequence's own
+  // tokens from position 0; T is then the longest sequence)
+  size_t qrow0 = (size_t)b * T;
+  const uint16_t* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
+  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  if (vl.cu_q) {
+    qrow0 = (size_t)vl.cu_q[b];
+    T = vl.cu_q[b + 1] - vl.cu_q[b];
+    R_cap = T;
+    kvc_b = kv_cmp + (size_t)vl.cu_k[b] * 2 * D;
+    kvr_b = kv_raw + qrow0 * 2 * D;
+    Nc_cap = vl.cu_k[b + 1] - vl.cu_k[b];
+    if (t0 >= T) return;  // uniform, before any barrier
+  }
   const int t = t0 + row_w;
   const bool active = t < T;
   const int t_last = min(T - 1, t0 + PF_ROWS - 1);
-  const int64_t qp = q_pos[b];
+  const int64_t qp = vl.cu_q ? 0 : q_pos[b];
   const int64_t pos = qp + t, pos_first = qp + t0, pos_last = qp + t_last;
-  const int32_t ncb = n_cmp ? n_cmp[b] : 0;
-  const int64_t rbase = raw_base[b];
-  const uint16_t* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
-  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
-  const size_t rowi = (size_t)b * T + (active ? t : t_last);
+  const int32_t ncb = vl.cu_q ? Nc_cap : (n_cmp ? n_cmp[b] : 0);
+  const int64_t rbase = vl.cu_q ? 0 : raw_base[b];
+  const size_t rowi = qrow0 + (active ? t : t_last);
 
   // this row's visibility
   const int nv_me = dense ? n_visible(pos, ncb, m, Nc_cap) : 0;
@@ -318,7 +331,7 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   // that a tile's loads need one LDS read per four rows and never wait on a
   // global index load.
   if (SPARSE && topk > 0 && Nc_cap > 0) {
-    const int32_t* idx_rows = idx + ((size_t)b * T + t0) * topk;
+    const int32_t* idx_rows = idx + (qrow0 + t0) * topk;
     const int nrows = t_last - t0 + 1;
     const int* idx_s = idx_all[row_w];
     // the row's NH waves load its tile: lane group gB (32 lanes, one 512-byte
@@ -428,7 +441,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, bool dense, float scale_log2, const float* __restrict__ sink, int n_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int64_t cmp_rows_b, PageTable pt, int nc_logical) {
+    float* __restrict__ part_ml, int64_t cmp_rows_b, PageTable pt, int nc_logical, Varlen vl) {
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
   constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
@@ -442,9 +455,22 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   const int g = lane >> 4, hl = lane & 15;
   const int item = blockIdx.x;
   const int rowi = item / n_split, split = item % n_split;
-  const int b = rowi / T, t = rowi % T;
-  const int64_t pos = q_pos[b] + t;
-  const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
+  const int b = vl.cu_q ? varlen_seq(vl, rowi) : rowi / T;
+  const int t = vl.cu_q ? rowi - vl.cu_q[b] : rowi % T;
+  // packed sequences: the sequence's entries and its own tokens as the raw
+  // rows, positions from 0
+  const uint16_t* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
+  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  if (vl.cu_q) {
+    kvc_b = kv_cmp + (size_t)vl.cu_k[b] * 2 * D;
+    kvr_b = kv_raw + (size_t)vl.cu_q[b] * 2 * D;
+    Nc_cap = vl.cu_k[b + 1] - vl.cu_k[b];
+    R_cap = vl.cu_q[b + 1] - vl.cu_q[b];
+  }
+  const int64_t pos = vl.cu_q ? t : q_pos[b] + t;
+  // n_cmp exists only for the dense (HCA) form: csa_sparse_attn passes none
+  const int32_t ncmp_b = vl.cu_q ? Nc_cap : (dense ? n_cmp[b] : 0);
+  const KeyList L = key_list(dense, topk, window, pos, ncmp_b, m, Nc_cap);
   // Tile-aligned list: compressed slots [0, n_c) padded to a whole tile, then
   // the window, so that every tile reads from one of the two caches.  Splits
   // take whole tiles.
@@ -456,12 +482,10 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   const int kb = ta * DC_KT;
   const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
   const uint16_t* dummy = q + (size_t)rowi * H * D;  // a valid row for empty slots
-  const char* cbase = Nc_cap > 0 ? (const char*)(kv_cmp + (size_t)b * cmp_rows_b * 2 * D)
-                                 : (const char*)dummy;
-  const char* wbase = R_cap > 0 ? (const char*)(kv_raw + (size_t)b * R_cap * 2 * D)
-                                : (const char*)dummy;
+  const char* cbase = Nc_cap > 0 ? (const char*)kvc_b : (const char*)dummy;
+  const char* wbase = R_cap > 0 ? (const char*)kvr_b : (const char*)dummy;
   const int n_c = L.n_c, n_w = L.n_w;
-  const int64_t w_row0 = L.lo - raw_base[b];  // cache row of window slot 0
+  const int64_t w_row0 = L.lo - (vl.cu_q ? 0 : raw_base[b]);  // cache row of window slot 0
   // index slots of this item's compressed positions, staged once (loads
   // batched four per thread before their LDS stores); the host splits the
   // list so that an item holds at most DC_IDX_MAX of them
@@ -716,17 +740,26 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
     const int32_t* __restrict__ n_cmp, const int64_t* __restrict__ raw_base, int T, int H, int D,
     int topk, int window, int m, int Nc_cap, int R_cap, bool dense, float scale_log2,
     const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse,
-    int64_t cmp_rows_b) {
+    int64_t cmp_rows_b, Varlen vl) {
   const int lane = threadIdx.x;
   const int rowi = blockIdx.x / H, h = blockIdx.x % H;
-  const int b = rowi / T, t = rowi % T;
-  const int64_t pos = q_pos[b] + t;
-  const KeyList L = key_list(dense, topk, window, pos, n_cmp[b], m, Nc_cap);
-  const int nk = L.n_c + L.n_w;
-  const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
+  const int b = vl.cu_q ? varlen_seq(vl, rowi) : rowi / T;
+  const int t = vl.cu_q ? rowi - vl.cu_q[b] : rowi % T;
   const float* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
   const float* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
-  const int64_t rbase = raw_base[b];
+  if (vl.cu_q) {  // packed sequences (positions from 0, own tokens as raw rows)
+    kvc_b = kv_cmp + (size_t)vl.cu_k[b] * 2 * D;
+    kvr_b = kv_raw + (size_t)vl.cu_q[b] * 2 * D;
+    Nc_cap = vl.cu_k[b + 1] - vl.cu_k[b];
+    R_cap = vl.cu_q[b + 1] - vl.cu_q[b];
+  }
+  const int64_t pos = vl.cu_q ? t : q_pos[b] + t;
+  // n_cmp exists only for the dense (HCA) form: csa_sparse_attn passes none
+  const int32_t ncmp_b = vl.cu_q ? Nc_cap : (dense ? n_cmp[b] : 0);
+  const KeyList L = key_list(dense, topk, window, pos, ncmp_b, m, Nc_cap);
+  const int nk = L.n_c + L.n_w;
+  const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
+  const int64_t rbase = vl.cu_q ? 0 : raw_base[b];
   const float* qr = q + ((size_t)rowi * H + h) * D;
   const float q0 = lane < D ? qr[lane] : 0.0f;
   const float q1 = lane + 64 < D ? qr[lane + 64] : 0.0f;
@@ -845,7 +878,9 @@ size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse) 
 
 hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
   AttnArgs a = a_in;
-  const int rows = a.B * a.T;
+  // packed sequences: one row per query token of every sequence (a.T is the
+  // longest sequence)
+  const int rows = a.vl.cu_q ? a.total_rows : a.B * a.T;
   const float scale_log2 = a.scale * kLog2e;
   int64_t cmp_rows_b = a.Nc_cap;  // rows of one sequence's compressed cache
   const int nc_logical = a.Nc_cap;
@@ -872,7 +907,7 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
     attn_f32_kernel<<<rows * a.H, 64, 0, st>>>(
         (const float*)a.q, (const float*)a.kv_cmp, a.idx, (const float*)a.kv_raw, a.q_pos,
         a.n_cmp, a.raw_base, a.T, a.H, a.D, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-        scale_log2, a.sink, (float*)a.out, a.lse, cmp_rows_b);
+        scale_log2, a.sink, (float*)a.out, a.lse, cmp_rows_b, a.vl);
     return hipGetLastError();
   }
   const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
@@ -887,13 +922,13 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
-          dec_pages, nc_logical);
+          dec_pages, nc_logical, a.vl);
     else
       attn_dec_kernel<2><<<grid, 128, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
-          dec_pages, nc_logical);
+          dec_pages, nc_logical, a.vl);
   } else {
     // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
     // rows share only the window: 2 rows, so that two independent
@@ -903,7 +938,7 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
                                  st>>>(                                                             \
       (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,  \
       a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, scale_log2, a.sink,      \
-      (uint16_t*)a.out, a.lse, cmp_rows_b)
+      (uint16_t*)a.out, a.lse, cmp_rows_b, a.vl)
     if (a.H == 64) {
       if (a.dense) CSA_LAUNCH_PF(2, 4, false);
       else CSA_LAUNCH_PF(2, 2, true);

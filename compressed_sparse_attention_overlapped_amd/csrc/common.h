@@ -154,6 +154,28 @@ __device__ __forceinline__ int32_t page_or_absent(const PageTable& pt, int b, in
   return (unsigned)pg < (unsigned)pt.n_pages ? pg : -1;
 }
 
+// ---- packed variable-length sequences ------------------------------------
+// cu_q null: the fixed layout [B, T, ...] with per-sequence metadata arrays.
+// Otherwise the B sequences are packed: sequence b holds the rows
+// [cu_q[b], cu_q[b + 1]) of every per-token tensor and the compressed
+// entries [cu_k[b], cu_k[b + 1]) of every per-entry tensor; every sequence
+// starts at position 0.
+struct Varlen {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B;
+};
+// the sequence holding packed row r (binary search over cu_q; B >= 1)
+__device__ __forceinline__ int varlen_seq(const Varlen& v, int r) {
+  int lo = 0, hi = v.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (v.cu_q[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 }  // namespace csa
 
 // ---- host-side launch entry points (defined in the kernel sources) --------
@@ -184,8 +206,11 @@ struct CompressArgs {
   void* ws;
   csa::PageTable pages;  // block_table null: unpaged out
   EntryOpts opt;
+  csa::Varlen vl;        // cu_q null: fixed [B, L] layout
+  int total_rows;        // packed sequences: rows of x (L is then the longest)
 };
 size_t compress_ws_bytes(int B, int L, int d_model, int E, int m, int overlap, csa_dtype_t in_dt);
+hipError_t launch_cmp_cu(int n, const int32_t* cu, int m, int32_t* cmp_cu, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
 struct IndexerArgs {
@@ -202,6 +227,8 @@ struct IndexerArgs {
   float* score_out;
   void* ws;
   csa::PageTable pages;  // block_table null: unpaged k_idx / k_scale
+  csa::Varlen vl;        // cu_q null: fixed [B, T] layout
+  int total_rows;        // packed sequences: query rows (T is then the longest)
 };
 size_t indexer_ws_bytes(int B, int T, int H_I, int d_I, int Nc_cap, int topk, csa_dtype_t dt);
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t s);
@@ -223,6 +250,8 @@ struct AttnArgs {
   float* lse;
   void* ws;
   csa::PageTable pages;  // block_table null: unpaged kv_cmp (sparse only)
+  csa::Varlen vl;        // cu_q null: fixed [B, T] layout
+  int total_rows;        // packed sequences: query rows (T is then the longest)
 };
 size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse);
 // the static scratch of csa_sparse_attn_noalloc: its size and its device

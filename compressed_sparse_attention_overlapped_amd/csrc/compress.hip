@@ -259,10 +259,18 @@ __global__ void __launch_bounds__(256) pool_kernel(
     int E, int m, int overlap, const float* __restrict__ ape, const float* __restrict__ state_in,
     float* __restrict__ state_out, void* __restrict__ out, void* __restrict__ out_scale,
     int Nc_cap, int n_slots, int n_split, bool rotate, float rot_scale, PageTable pt,
-    csa_host::EntryOpts opt) {
+    csa_host::EntryOpts opt, Varlen vl) {
   const int b = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
   const int ns = (1 + overlap) * m - 1;
-  const int64_t p0 = pos0[b];
+  // this sequence's rows of the call: [rb, rb + L) of the projection output
+  // (packed sequences: the sequence's own length, from position 0)
+  const int M = vl.cu_q ? vl.cu_q[B] : B * L;
+  const size_t rb = vl.cu_q ? (size_t)vl.cu_q[b] : (size_t)b * L;
+  if (vl.cu_q) {
+    L = vl.cu_q[b + 1] - vl.cu_q[b];
+    Nc_cap = vl.cu_k[b + 1] - vl.cu_k[b];
+  }
+  const int64_t p0 = vl.cu_q ? 0 : pos0[b];
   const size_t N = 2 * (size_t)E;
 
   // P and G of the token at absolute position j, channel e; the caller
@@ -273,8 +281,8 @@ __global__ void __launch_bounds__(256) pool_kernel(
     if (j < 0) return;
     if (j >= p0) {
       // the projection's split-K partials are summed here, in split order
-      const float* r = pg + ((size_t)b * L + (size_t)(j - p0)) * N;
-      const size_t stride = (size_t)B * L * N;
+      const float* r = pg + (rb + (size_t)(j - p0)) * N;
+      const size_t stride = (size_t)M * N;
       pv = r[e];
       gv = r[E + e];
       for (int s0 = 1; s0 < n_split; s0 += 8) {  // eight splits' loads in flight
@@ -317,7 +325,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
           const bool in_call = j >= p0;
           const bool in_state = !in_call && state_in && j >= 0;
           const float* src =
-              in_call ? pg + ((size_t)b * L + (size_t)(j - p0)) * N
+              in_call ? pg + (rb + (size_t)(j - p0)) * N
                       : (in_state ? state_in + ((size_t)b * ns + (size_t)(j - (p0 - ns))) * 2 * E : pg);
           pv[u] = src[e];
           gv[u] = src[E + e];
@@ -354,7 +362,8 @@ __global__ void __launch_bounds__(256) pool_kernel(
   if (last >= p0 + L) return;
   const int64_t first = (int64_t)m * (i - overlap);
   // paged output: an entry whose page is absent is not stored (uniform)
-  const int64_t orow64 = pt.block_table ? paged_row(pt, b, (int)i) : (int64_t)b * Nc_cap + i;
+  const int64_t orow64 = pt.block_table ? paged_row(pt, b, (int)i)
+                         : (vl.cu_k ? (int64_t)vl.cu_k[b] : (int64_t)b * Nc_cap) + i;
   if (orow64 < 0) return;
 
   __shared__ float red[256];
@@ -376,7 +385,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
         const int64_t j = first + u;
         in_call[u] = j >= p0;
         if (j >= p0) {
-          src[u] = pg + ((size_t)b * L + (size_t)(j - p0)) * N;
+          src[u] = pg + (rb + (size_t)(j - p0)) * N;
           present[u] = true;
         } else if (state_in && j >= 0 && j >= p0 - ns) {
           src[u] = state_in + ((size_t)b * ns + (size_t)(j - (p0 - ns))) * 2 * E;
@@ -386,7 +395,7 @@ __global__ void __launch_bounds__(256) pool_kernel(
           present[u] = false;
         }
       }
-      const size_t sstride = (size_t)B * L * N;  // between split partials
+      const size_t sstride = (size_t)M * N;  // between split partials
       const float* ap = ape ? ape : pg;  // a readable stand-in when there is no ape
       for (int e = tid; e < E; e += blockDim.x, ++nv) {
         float pv[WIN], gv[WIN], av[WIN];
@@ -571,10 +580,48 @@ __global__ void __launch_bounds__(256) pool_kernel(
   }
 }
 
+// ------------------------------------------------ packed sequence offsets
+// cmp_cu[0] = 0, cmp_cu[b + 1] = cmp_cu[b] + floor((cu[b + 1] - cu[b]) / m):
+// the compressed entries of packed sequences.  One workgroup of 1024 threads,
+// an inclusive block scan per chunk of 1024 sequences.
+__global__ void __launch_bounds__(1024) cmp_cu_kernel(int n, const int32_t* __restrict__ cu, int m,
+                                                      int32_t* __restrict__ cmp_cu) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    carry = 0;
+    cmp_cu[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + tid;
+    const int v = i < n ? (cu[i + 1] - cu[i]) / m : 0;
+    int x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (i < n) cmp_cu[i + 1] = before + x;
+    __syncthreads();
+    if (tid == 1023) carry = before + x;
+    __syncthreads();
+  }
+}
+
 }  // namespace csa
 
 namespace csa_host {
 using namespace csa;
+
+hipError_t launch_cmp_cu(int n, const int32_t* cu, int m, int32_t* cmp_cu, hipStream_t st) {
+  cmp_cu_kernel<<<1, 1024, 0, st>>>(n, cu, m, cmp_cu);
+  return hipGetLastError();
+}
 
 static int proj_splits(int M, int E, int K, csa_dtype_t dt) {
   if (use_proj_small(M, K, dt)) return proj_small_splits(E, K);
@@ -603,7 +650,9 @@ size_t compress_ws_bytes(int B, int L, int d_model, int E, int m, int overlap,
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
-  const int M = a.B * a.L, K = a.d_model, E = a.E;
+  // rows of the projection: every token of the call (packed sequences:
+  // a.total_rows, the sum of their lengths)
+  const int M = a.vl.cu_q ? a.total_rows : a.B * a.L, K = a.d_model, E = a.E;
   const int splits = proj_splits(M, E, K, a.in_dt);
   float* pg = (float*)a.ws;
   if (use_proj_small(M, K, a.in_dt)) {
@@ -618,6 +667,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
     proj_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
         (const float*)a.x, (const float*)a.w_kv, (const float*)a.w_gate, pg, M, E, K);
   }
+  // packed sequences: a.L is the longest sequence (the grid covers its
+  // entries; shorter sequences' extra slots return at once)
   const int n_slots = (a.L + a.m - 1) / a.m + 1;
   dim3 pgrid(n_slots + 1, a.B);
   // the common gated window (m = 4 with overlap: 8 tokens) has a batched path
@@ -630,7 +681,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   pool_kernel<DT, W, NS><<<pgrid, pthreads, 0, st>>>(                                           \
       pg, a.pos0, a.B, a.L, E, a.m, a.overlap, a.ape, a.state_in, a.state_out, a.out,           \
       a.out_scale, a.Nc_cap, n_slots, splits, a.rotate != 0, (float)(1.0 / std::sqrt((double)E)), \
-      a.pages, a.opt)
+      a.pages, a.opt, a.vl)
 #define CSA_POOL_DT(DT)                            \
   if (w8 == 1) CSA_LAUNCH_POOL(DT, 8, 1);          \
   else if (w8 == 4) CSA_LAUNCH_POOL(DT, 8, 4);     \

@@ -95,18 +95,22 @@ __global__ void __launch_bounds__(256) score_f32_kernel(
     const float* __restrict__ q_idx, const float* __restrict__ w_idx,
     const float* __restrict__ k_idx, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int T, int H_I, int d_I, int Nc_cap, int m,
-    float* __restrict__ scores, uint32_t* __restrict__ ghist) {
+    float* __restrict__ scores, uint32_t* __restrict__ ghist, Varlen vl) {
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
-  const int row = blockIdx.y, b = row / T, t = row % T;
+  const int row = blockIdx.y;
+  const int b = vl.cu_q ? varlen_seq(vl, row) : row / T;
+  const int t = vl.cu_q ? row - vl.cu_q[b] : row % T;
+  const size_t kb0 = vl.cu_q ? (size_t)vl.cu_k[b] : (size_t)b * Nc_cap;
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  const int nv = vl.cu_q ? n_visible(t, vl.cu_k[b + 1] - vl.cu_k[b], m, Nc_cap)
+                         : n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   if (HIST) {
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lhist[i] = 0;
     __syncthreads();
   }
   if (j < nv) {
     const float* qr = q_idx + (size_t)row * H_I * d_I;
-    const float* kr = k_idx + ((size_t)b * Nc_cap + j) * d_I;
+    const float* kr = k_idx + (kb0 + j) * d_I;
     float s = 0.0f;
     for (int h = 0; h < H_I; ++h) {
       float dot = 0.0f;
@@ -140,7 +144,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int key_chunk,
-    float* __restrict__ scores, uint32_t* __restrict__ ghist, PageTable pt) {
+    float* __restrict__ scores, uint32_t* __restrict__ ghist, PageTable pt, Varlen vl) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][SB_KT * SB_KSTRIDE];
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
   // paged caches: the chunk's page ids (pages of at least 16 entries)
@@ -148,8 +152,14 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
   // later rows see more entries: they are dispatched first
   const int b = blockIdx.z, t0 = (gridDim.x - 1 - blockIdx.x) * SB_ROWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t p0 = q_pos[b];
-  const int ncb = n_cmp[b];
+  // this sequence's first query row and key row (packed sequences: their
+  // offsets, positions from 0; the grid covers the longest sequence)
+  const size_t qrow0 = vl.cu_q ? (size_t)vl.cu_q[b] : (size_t)b * T;
+  const size_t kb0 = vl.cu_q ? (size_t)vl.cu_k[b] : (size_t)b * Nc_cap;
+  if (vl.cu_q) T = vl.cu_q[b + 1] - vl.cu_q[b];
+  if (t0 >= T) return;  // uniform, before any barrier
+  const int64_t p0 = vl.cu_q ? 0 : q_pos[b];
+  const int ncb = vl.cu_q ? vl.cu_k[b + 1] - vl.cu_k[b] : n_cmp[b];
   const int jb = blockIdx.y * key_chunk;
   // entries this workgroup must score: up to the largest n_vis of its rows
   const int t_last = min(T - 1, t0 + SB_ROWS - 1);
@@ -177,7 +187,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     // waits in the key loop count loads exactly); their scores are not stored
     const int tq = min(tt, T - 1);
     for (int s = 0; s < 4; ++s)
-      a[mt][s] = *(const bf16x8*)(q_idx + (((size_t)b * T + tq) * 16 + h) * 64 + 16 * s +
+      a[mt][s] = *(const bf16x8*)(q_idx + ((qrow0 + tq) * 16 + h) * 64 + 16 * s +
                                   8 * (lane >> 5));
   }
   // head weights for the accumulator rows: tile mt, register r -> token
@@ -188,7 +198,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     for (int r = 0; r < 16; ++r) {
       int tt = t0 + wave * 4 + mt * 2 + (r >> 3);
       int h = 8 * ((r & 7) >> 2) + 4 * (lane >> 5) + (r & 3);
-      wv[mt][r] = w_idx[((size_t)b * T + min(tt, T - 1)) * 16 + h];
+      wv[mt][r] = w_idx[(qrow0 + min(tt, T - 1)) * 16 + h];
     }
     for (int u = 0; u < 2; ++u) {
       int tt = t0 + wave * 4 + mt * 2 + u;
@@ -206,7 +216,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     for (int i = 0; i < 2; ++i) {
       const int c = i * 256 + tid, r = c >> 3, q8 = c & 7;
       const int row = min(j0 + r, je - 1);
-      size_t at = (size_t)b * Nc_cap + row;
+      size_t at = kb0 + row;
       if constexpr (PAGED) {
         // an absent page reads pool row 0 (its scores are replaced below)
         const int pg = pg_s[(row >> pt.page_log2) - p_first];
@@ -256,7 +266,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
           // an entry of an absent page has no key: the lowest score
           if constexpr (PAGED)
             if (pg_s[(j >> pt.page_log2) - p_first] < 0) sc = -INFINITY;
-          scores[((size_t)b * T + tt) * Nc_cap + j] = sc;
+          scores[(qrow0 + tt) * Nc_cap + j] = sc;
           if (HIST) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
         }
       }
@@ -273,7 +283,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(
     // one histogram per query row: rows of this workgroup share the LDS
     // histogram, so long rows run with T == 1 (row = b)
     __syncthreads();
-    hist_flush(lhist, ghist + ((size_t)b * T + t0) * kHistBins);
+    hist_flush(lhist, ghist + (qrow0 + t0) * kHistBins);
   }
 }
 
@@ -494,7 +504,7 @@ template <int KMAX>
 __global__ void __launch_bounds__(256) select_short_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_cmp, int rows, int T, int Nc_cap, int m, int topk,
-    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out, Varlen vl) {
   // rows of up to 2048 keys keep them in registers (lane l: keys l, l + 64,
   // ...), longer ones in the wave's LDS slice
   constexpr bool REG = KMAX <= 2048;
@@ -505,10 +515,12 @@ __global__ void __launch_bounds__(256) select_short_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;
-  const int b = row / T, t = row % T;
+  const int b = vl.cu_q ? varlen_seq(vl, row) : row / T;
+  const int t = vl.cu_q ? row - vl.cu_q[b] : row % T;
   uint32_t* keys = keys_all[REG ? 0 : wave];
   uint32_t* hist = hist_all[wave];
-  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  const int nv = vl.cu_q ? n_visible(t, vl.cu_k[b + 1] - vl.cu_k[b], m, Nc_cap)
+                         : n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
   const float* srow = scores + (size_t)row * Nc_cap;
   int32_t* orow = idx_out + (size_t)row * topk;
   float* sorow = score_out ? score_out + (size_t)row * topk : nullptr;
@@ -1046,11 +1058,12 @@ size_t indexer_ws_bytes(int B, int T, int H_I, int d_I, int Nc_cap, int topk, cs
 }
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
-  const IdxLayout L = idx_layout(a.B, a.T, a.Nc_cap, a.topk);
+  // packed sequences: one row per query token of every sequence
+  const int rows = a.vl.cu_q ? a.total_rows : a.B * a.T;
+  const IdxLayout L = idx_layout(1, rows, a.Nc_cap, a.topk);
   char* ws = (char*)a.ws;
   float* scores = (float*)(ws + L.scores);
   uint32_t* hist = L.long_rows ? (uint32_t*)(ws + L.hist) : nullptr;
-  const int rows = a.B * a.T;
   if (L.long_rows) {
     size_t n = (size_t)rows * kHistBins;
     zero_u32_kernel<<<(unsigned)std::min<size_t>((n + 255) / 256, 1024), 256, 0, st>>>(hist, n);
@@ -1062,11 +1075,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     if (L.long_rows)
       score_f32_kernel<true><<<g, 256, 0, st>>>((const float*)a.q_idx, a.w_idx,
                                                 (const float*)a.k_idx, a.q_pos, a.n_cmp, a.T,
-                                                a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist);
+                                                a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist, a.vl);
     else
       score_f32_kernel<false><<<g, 256, 0, st>>>((const float*)a.q_idx, a.w_idx,
                                                  (const float*)a.k_idx, a.q_pos, a.n_cmp, a.T,
-                                                 a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist);
+                                                 a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist, a.vl);
   } else if (a.dt == CSA_DT_BF16) {
     // long rows need one histogram per row: one row per workgroup then;
     // short rows split their entries in chunks of 512 so that the causal
@@ -1077,11 +1090,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   if (a.pages.block_table)                                                                    \
     score_bf16_kernel<HS, true><<<g, 256, 0, st>>>(                                           \
         (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,   \
-        a.Nc_cap, a.m, key_chunk, scores, hist, a.pages);                                      \
+        a.Nc_cap, a.m, key_chunk, scores, hist, a.pages, a.vl);                                \
   else                                                                                        \
     score_bf16_kernel<HS, false><<<g, 256, 0, st>>>(                                          \
         (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,   \
-        a.Nc_cap, a.m, key_chunk, scores, hist, a.pages)
+        a.Nc_cap, a.m, key_chunk, scores, hist, a.pages, a.vl)
     if (L.long_rows) {
       // rows of a workgroup must share a histogram: only T == 1 qualifies
       if (a.T != 1) return hipErrorNotSupported;
@@ -1120,11 +1133,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     const unsigned g = (unsigned)((rows + 3) / 4);
     if (a.Nc_cap <= 2048)
       select_short_kernel<2048><<<g, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, rows, a.T, a.Nc_cap,
-                                                   a.m, a.topk, a.idx_out, a.score_out);
+                                                   a.m, a.topk, a.idx_out, a.score_out, a.vl);
     else
       select_short_kernel<kShortMax><<<g, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, rows, a.T,
                                                         a.Nc_cap, a.m, a.topk, a.idx_out,
-                                                        a.score_out);
+                                                        a.score_out, a.vl);
   } else {
     uint32_t* cnt = (uint32_t*)(ws + L.chunk_cnt);
     uint32_t* bm = (uint32_t*)(ws + L.def_bm);

@@ -348,6 +348,70 @@ csa_status_t csa_sparse_attn_paged(int B, int T, int H, int D, int topk, int win
                                    void* workspace, size_t ws_bytes, hipStream_t stream);
 size_t csa_sparse_attn_paged_workspace_size(int B, int T, int H, int D, int topk, int window);
 
+/*
+ * Packed variable-length prefill (the CSA migration analysis, section 4.2:
+ * the attention entry point takes actual_seq_len; its phase 3 builds
+ * cmp_cu_seqlens for packed sequences).  n sequences of lengths
+ * len_b = cu_seqlens[b + 1] - cu_seqlens[b] are packed along the token
+ * axis (total = cu_seqlens[n] tokens), every one starting at position 0:
+ * token j of sequence b is row cu_seqlens[b] + j of every per-token tensor,
+ * and its compressed entry i is row cmp_cu_seqlens[b] + i of every per-entry
+ * tensor.  A sequence never sees another sequence's tokens or entries.  The
+ * raw window rows of a sequence are its own packed tokens (kv_raw row
+ * cu_seqlens[b] + j is token j).  Offsets are device int32 arrays of n + 1
+ * elements; max_len (host) is at least every len_b, and max_cmp the largest
+ * entry count floor(len_b / m).
+ */
+
+/* cmp_cu_seqlens[0] = 0, cmp_cu_seqlens[b + 1] = cmp_cu_seqlens[b] +
+ * floor(len_b / m): the entry offsets of the packed sequences (device). */
+csa_status_t csa_build_cmp_cu_seqlens(int n, const int32_t* cu_seqlens, int m,
+                                      int32_t* cmp_cu_seqlens, hipStream_t stream);
+
+/* csa_compress over packed sequences, each from position 0 (no carried state
+ * in): x [total, d_model]; out [cmp_cu_seqlens[n], E] (and out_scale) in the
+ * layouts of csa_compress; state_out [n, (1 + overlap) m - 1, 2, E] or NULL
+ * receives each sequence's tail for a later decode step.  opts as for
+ * csa_compress_ex.  Workspace: csa_compress_varlen_workspace_size(). */
+csa_status_t csa_compress_varlen(int n, int total, int max_len, int d_model, int E, int m,
+                                 int overlap, int rotate, const int32_t* cu_seqlens,
+                                 const int32_t* cmp_cu_seqlens, const void* x, const void* w_kv,
+                                 const void* w_gate, csa_dtype_t in_dt, const float* ape,
+                                 float* state_out, void* out, void* out_scale, csa_dtype_t out_dt,
+                                 const csa_compress_opts_t* opts, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream);
+size_t csa_compress_varlen_workspace_size(int total, int d_model, int E, int m, int overlap,
+                                          csa_dtype_t in_dt);
+
+/* csa_indexer_topk over packed sequences: q_idx [total, H_I, d_I], w_idx
+ * [total, H_I], k_idx [cmp_cu_seqlens[n], d_I]; idx_out [total, topk] holds
+ * indices local to the row's sequence (entry i of sequence b is i).
+ * Supported: F32 and BF16 as for csa_indexer_topk, max_cmp <= 8192.
+ * Workspace: csa_indexer_topk_varlen_workspace_size(). */
+csa_status_t csa_indexer_topk_varlen(int n, int total, int max_len, int H_I, int d_I,
+                                     int max_cmp, int m, int topk, const int32_t* cu_seqlens,
+                                     const int32_t* cmp_cu_seqlens, const void* q_idx,
+                                     const float* w_idx, const void* k_idx, csa_dtype_t qk_dt,
+                                     int32_t* idx_out, float* score_out, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream);
+size_t csa_indexer_topk_varlen_workspace_size(int total, int max_cmp, int topk,
+                                              csa_dtype_t qk_dt);
+
+/* csa_sparse_attn over packed sequences: q and out [total, H, D], kv_cmp
+ * [cmp_cu_seqlens[n], 2 D], idx [total, topk] local to each sequence (as
+ * csa_indexer_topk_varlen writes it; slots outside [0, floor(len_b / m))
+ * are skipped), kv_raw [total, 2 D] the packed tokens' own KV rows.  Other
+ * arguments and the supported set as for csa_sparse_attn.  Workspace:
+ * csa_sparse_attn_varlen_workspace_size(). */
+csa_status_t csa_sparse_attn_varlen(int n, int total, int max_len, int H, int D, int topk,
+                                    int window, float scale, const float* sink,
+                                    const int32_t* cu_seqlens, const int32_t* cmp_cu_seqlens,
+                                    const void* q, const void* kv_cmp, int max_cmp,
+                                    const int32_t* idx, const void* kv_raw, csa_dtype_t dt,
+                                    void* out, float* lse, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+size_t csa_sparse_attn_varlen_workspace_size(int total, int H, int D, int topk, int window);
+
 /* Static text of a status code. */
 const char* csa_status_string(csa_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */
