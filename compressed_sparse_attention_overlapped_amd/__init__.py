@@ -125,7 +125,10 @@ def lib():
                   L.csa_sparse_attn_varlen_workspace_size):
             f.restype = C.c_size_t
         L.csa_sparse_attn_paged.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, pt, vp, vp, i32,
-                                            vp, i32, vp, vp, vp, sz, vp])
+                                            vp, pt, i32, vp, vp, vp, sz, vp])
+        L.hca_dense_attn_paged.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, vp, i32, pt, vp, i32,
+                                           vp, pt, i32, vp, vp, vp, sz, vp])
+        L.hca_dense_attn_paged.restype = C.c_int
         L.csa_sparse_attn_noalloc.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32,
                                               vp, i32, vp, vp, vp])
         L.csa_sparse_attn_noalloc.restype = C.c_int
@@ -288,10 +291,13 @@ def _sink(sink, H):
 
 
 def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None, out=None,
-                    lse=None, want_lse=False, workspace=None, sink=None, pages=None):
+                    lse=None, want_lse=False, workspace=None, sink=None, pages=None,
+                    raw_pages=None):
     """CSA attention; returns (out [B, T, H, D], lse f32 [B, T, H] or None).
     sink: f32 [H] per-head sink logits or None.  pages: a PageTable; kv_cmp is then
-    the pool [n_pages * page_size, 2 D] and idx holds logical indices."""
+    the pool [n_pages * page_size, 2 D] and idx holds logical indices.  raw_pages: a
+    PageTable for the window cache; kv_raw is then a pool and raw_pages.nc_cap the
+    logical rows per sequence."""
     _dense(q, kv_cmp, idx, kv_raw, q_pos, raw_base, sink)
     B, T, H, D = q.shape
     topk = idx.shape[2] if idx is not None else 0
@@ -300,14 +306,22 @@ def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None,
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
-    if pages is not None:
-        pages.check(B, kv_cmp)
-        ws, nb = _workspace(lib().csa_sparse_attn_paged_workspace_size(B, T, H, D, topk, window),
-                            q, workspace)
-        rc = lib().csa_sparse_attn_paged(B, T, H, D, topk, window, scale, _p(_sink(sink, H)),
-                                         _p(q_pos), _p(q), _p(kv_cmp), pages.nc_cap, pages.c(),
-                                         _p(idx), _p(kv_raw), kv_raw.shape[1], _p(raw_base),
-                                         _DT[q.dtype], _p(out), _p(lse), _p(ws), nb, _stream(q))
+    if pages is not None or raw_pages is not None:
+        if pages is not None:
+            pages.check(B, kv_cmp)
+            nb_ws = lib().csa_sparse_attn_paged_workspace_size(B, T, H, D, topk, window)
+        else:
+            nb_ws = csa_sparse_attn_workspace_size(B, T, H, D, topk, window)
+        if raw_pages is not None:
+            raw_pages.check(B, kv_raw)
+        ws, nb = _workspace(nb_ws, q, workspace)
+        rc = lib().csa_sparse_attn_paged(
+            B, T, H, D, topk, window, scale, _p(_sink(sink, H)), _p(q_pos), _p(q), _p(kv_cmp),
+            pages.nc_cap if pages is not None else kv_cmp.shape[1],
+            pages.c() if pages is not None else None, _p(idx), _p(kv_raw),
+            raw_pages.nc_cap if raw_pages is not None else kv_raw.shape[1], _p(raw_base),
+            raw_pages.c() if raw_pages is not None else None, _DT[q.dtype], _p(out), _p(lse),
+            _p(ws), nb, _stream(q))
         _check("csa_sparse_attn_paged", rc)
         return out, lse
     ws, nb = _workspace(csa_sparse_attn_workspace_size(B, T, H, D, topk, window), q, workspace)
@@ -338,9 +352,11 @@ def csa_sparse_attn_noalloc(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, out
 
 
 def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=None, out=None,
-                   lse=None, want_lse=False, workspace=None, sink=None):
+                   lse=None, want_lse=False, workspace=None, sink=None, pages=None,
+                   raw_pages=None):
     """HCA attention; returns (out [B, T, H, D], lse or None).
-    sink: f32 [H] per-head sink logits or None."""
+    sink: f32 [H] per-head sink logits or None.  pages / raw_pages: PageTables of the
+    compressed and window caches (each then a pool; nc_cap the logical rows)."""
     _dense(q, kv_cmp, kv_raw, q_pos, n_cmp, raw_base, sink)
     B, T, H, D = q.shape
     scale = D ** -0.5 if scale is None else float(scale)
@@ -348,6 +364,21 @@ def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=N
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    if pages is not None or raw_pages is not None:
+        nc = pages.nc_cap if pages is not None else kv_cmp.shape[1]
+        rcap = raw_pages.nc_cap if raw_pages is not None else kv_raw.shape[1]
+        if pages is not None:
+            pages.check(B, kv_cmp)
+        if raw_pages is not None:
+            raw_pages.check(B, kv_raw)
+        ws, nb = _workspace(hca_dense_attn_workspace_size(B, T, H, D, nc, window), q, workspace)
+        rc = lib().hca_dense_attn_paged(
+            B, T, H, D, m, window, scale, _p(_sink(sink, H)), _p(q_pos), _p(n_cmp), _p(q),
+            _p(kv_cmp), nc, pages.c() if pages is not None else None, _p(kv_raw), rcap,
+            _p(raw_base), raw_pages.c() if raw_pages is not None else None, _DT[q.dtype], _p(out),
+            _p(lse), _p(ws), nb, _stream(q))
+        _check("hca_dense_attn_paged", rc)
+        return out, lse
     ws, nb = _workspace(hca_dense_attn_workspace_size(B, T, H, D, kv_cmp.shape[1], window), q,
                         workspace)
     rc = lib().hca_dense_attn(B, T, H, D, m, window, scale, _p(_sink(sink, H)), _p(q_pos),

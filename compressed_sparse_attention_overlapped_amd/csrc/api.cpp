@@ -289,16 +289,23 @@ static csa_status_t sparse_attn_impl(int B, int T, int H, int D, int topk, int w
                                      const int32_t* idx, const void* kv_raw, int R_cap,
                                      const int64_t* raw_base, csa_dtype_t dt, void* out,
                                      float* lse, void* workspace, size_t ws_bytes,
-                                     hipStream_t stream, const csa_page_table_t* pages) {
-  csa::PageTable pt;
+                                     hipStream_t stream, const csa_page_table_t* pages,
+                                     const csa_page_table_t* raw_pages) {
+  csa::PageTable pt, rpt;
   csa_status_t st = check_pages("csa_sparse_attn", pages, Nc_cap, pt);
   if (st != CSA_OK) return st;
-  // a paged kv_cmp is the pool: its row count is what the kernels bound
+  st = check_pages("csa_sparse_attn (window)", raw_pages, R_cap, rpt);
+  if (st != CSA_OK) return st;
+  // a paged cache is its pool: its row count is what the kernels bound
   const int cmp_rows =
       pages ? (int)std::min<int64_t>((int64_t)pages->n_pages * pages->page_size, INT32_MAX)
             : Nc_cap;
+  const int raw_rows =
+      raw_pages
+          ? (int)std::min<int64_t>((int64_t)raw_pages->n_pages * raw_pages->page_size, INT32_MAX)
+          : R_cap;
   st = check_attn("csa_sparse_attn", B, T, H, D, window, q_pos, q, kv_cmp, cmp_rows, kv_raw,
-                  R_cap, raw_base, dt, out);
+                  raw_rows, raw_base, dt, out);
   if (st != CSA_OK) return st;
   if (topk < 0) return fail(CSA_E_ARG, "csa_sparse_attn: topk must be >= 0");
   if (topk > 0 && !idx) return fail(CSA_E_ARG, "csa_sparse_attn: idx is required when topk > 0");
@@ -312,6 +319,7 @@ static csa_status_t sparse_attn_impl(int B, int T, int H, int D, int topk, int w
   csa_host::AttnArgs a{B, T, H, D, topk, window, 1, Nc_cap, R_cap, false, scale, sink, q_pos,
                        nullptr, q, kv_cmp, idx, kv_raw, raw_base, dt, out, lse, workspace};
   a.pages = pt;
+  a.raw_pages = rpt;
   return hip_status(csa_host::launch_attn(a, stream), "csa_sparse_attn launch");
 }
 
@@ -323,19 +331,21 @@ csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, f
                              void* workspace, size_t ws_bytes, hipStream_t stream) {
   return sparse_attn_impl(B, T, H, D, topk, window, scale, sink, q_pos, q, kv_cmp, Nc_cap, idx,
                           kv_raw, R_cap, raw_base, dt, out, lse, workspace, ws_bytes, stream,
-                          nullptr);
+                          nullptr, nullptr);
 }
 
 csa_status_t csa_sparse_attn_paged(int B, int T, int H, int D, int topk, int window, float scale,
                                    const float* sink, const int64_t* q_pos, const void* q,
                                    const void* kv_cmp, int Nc_cap, const csa_page_table_t* pages,
                                    const int32_t* idx, const void* kv_raw, int R_cap,
-                                   const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
-                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (!pages) return fail(CSA_E_ARG, "csa_sparse_attn_paged: pages is required");
+                                   const int64_t* raw_base, const csa_page_table_t* raw_pages,
+                                   csa_dtype_t dt, void* out, float* lse, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (!pages && !raw_pages)
+    return fail(CSA_E_ARG, "csa_sparse_attn_paged: pages or raw_pages is required");
   return sparse_attn_impl(B, T, H, D, topk, window, scale, sink, q_pos, q, kv_cmp, Nc_cap, idx,
                           kv_raw, R_cap, raw_base, dt, out, lse, workspace, ws_bytes, stream,
-                          pages);
+                          pages, raw_pages);
 }
 
 csa_status_t csa_sparse_attn_noalloc(int B, int T, int H, int D, int topk, int window,
@@ -365,7 +375,7 @@ csa_status_t csa_sparse_attn_noalloc(int B, int T, int H, int D, int topk, int w
   }
   return sparse_attn_impl(B, T, H, D, topk, window, scale, sink, q_pos, q, kv_cmp, Nc_cap, idx,
                           kv_raw, R_cap, raw_base, dt, out, lse, ws, need > 0 ? cap : 0, stream,
-                          nullptr);
+                          nullptr, nullptr);
 }
 
 size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window) {
@@ -373,14 +383,26 @@ size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int
   return csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window, false);
 }
 
-csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float scale,
-                            const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
-                            const void* q,
-                            const void* kv_cmp, int Nc_cap, const void* kv_raw, int R_cap,
-                            const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
-                            void* workspace, size_t ws_bytes, hipStream_t stream) {
-  csa_status_t st = check_attn("hca_dense_attn", B, T, H, D, window, q_pos, q, kv_cmp, Nc_cap,
-                               kv_raw, R_cap, raw_base, dt, out);
+static csa_status_t hca_impl(int B, int T, int H, int D, int m, int window, float scale,
+                             const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                             const void* q, const void* kv_cmp, int Nc_cap, const void* kv_raw,
+                             int R_cap, const int64_t* raw_base, csa_dtype_t dt, void* out,
+                             float* lse, void* workspace, size_t ws_bytes, hipStream_t stream,
+                             const csa_page_table_t* pages, const csa_page_table_t* raw_pages) {
+  csa::PageTable pt, rpt;
+  csa_status_t st = check_pages("hca_dense_attn", pages, Nc_cap, pt);
+  if (st != CSA_OK) return st;
+  st = check_pages("hca_dense_attn (window)", raw_pages, R_cap, rpt);
+  if (st != CSA_OK) return st;
+  const int cmp_rows =
+      pages ? (int)std::min<int64_t>((int64_t)pages->n_pages * pages->page_size, INT32_MAX)
+            : Nc_cap;
+  const int raw_rows =
+      raw_pages
+          ? (int)std::min<int64_t>((int64_t)raw_pages->n_pages * raw_pages->page_size, INT32_MAX)
+          : R_cap;
+  st = check_attn("hca_dense_attn", B, T, H, D, window, q_pos, q, kv_cmp, cmp_rows, kv_raw,
+                  raw_rows, raw_base, dt, out);
   if (st != CSA_OK) return st;
   if (m < 1) return fail(CSA_E_ARG, "hca_dense_attn: m must be >= 1");
   if (!n_cmp) return fail(CSA_E_ARG, "hca_dense_attn: n_cmp is required");
@@ -390,7 +412,32 @@ csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float
     return fail(CSA_E_WORKSPACE, "hca_dense_attn: workspace %zu < %zu bytes", ws_bytes, need);
   csa_host::AttnArgs a{B, T, H, D, 0, window, m, Nc_cap, R_cap, true, scale, sink, q_pos,
                        n_cmp, q, kv_cmp, nullptr, kv_raw, raw_base, dt, out, lse, workspace};
+  a.pages = pt;
+  a.raw_pages = rpt;
   return hip_status(csa_host::launch_attn(a, stream), "hca_dense_attn launch");
+}
+
+csa_status_t hca_dense_attn(int B, int T, int H, int D, int m, int window, float scale,
+                            const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                            const void* q,
+                            const void* kv_cmp, int Nc_cap, const void* kv_raw, int R_cap,
+                            const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return hca_impl(B, T, H, D, m, window, scale, sink, q_pos, n_cmp, q, kv_cmp, Nc_cap, kv_raw,
+                  R_cap, raw_base, dt, out, lse, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+csa_status_t hca_dense_attn_paged(int B, int T, int H, int D, int m, int window, float scale,
+                                  const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                                  const void* q, const void* kv_cmp, int Nc_cap,
+                                  const csa_page_table_t* pages, const void* kv_raw, int R_cap,
+                                  const int64_t* raw_base, const csa_page_table_t* raw_pages,
+                                  csa_dtype_t dt, void* out, float* lse, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (!pages && !raw_pages)
+    return fail(CSA_E_ARG, "hca_dense_attn_paged: pages or raw_pages is required");
+  return hca_impl(B, T, H, D, m, window, scale, sink, q_pos, n_cmp, q, kv_cmp, Nc_cap, kv_raw,
+                  R_cap, raw_base, dt, out, lse, workspace, ws_bytes, stream, pages, raw_pages);
 }
 
 /* ---- packed variable-length sequences --------------------------------- */

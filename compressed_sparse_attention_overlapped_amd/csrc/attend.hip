@@ -49,19 +49,26 @@ __device__ __forceinline__ KeyList key_list(bool dense, int topk, int window, in
   return L;
 }
 
-// Source row of list position p (nullptr if the slot is empty).
+// Source row of list position p (nullptr if the slot is empty).  With a
+// block table (cmp_pt for the dense form's entries, raw_pt for the window),
+// the row is found in the pool, and a row of an absent page is empty.
 template <typename Tp>
 __device__ __forceinline__ const Tp* key_row(int p, const KeyList& L, bool dense,
                                              const int32_t* idx_row, const Tp* kv_cmp_b,
                                              int Nc_cap, const Tp* kv_raw_b, int R_cap,
-                                             int64_t raw_base, int row_elems) {
+                                             int64_t raw_base, int row_elems, int b,
+                                             const PageTable& cmp_pt, const PageTable& raw_pt) {
   if (p < L.n_c) {
-    int j = dense ? p : idx_row[p];
+    int64_t j = dense ? p : idx_row[p];
     if (j < 0 || j >= Nc_cap) return nullptr;
+    if (dense && cmp_pt.block_table) j = paged_row(cmp_pt, b, (int)j);
+    if (j < 0) return nullptr;
     return kv_cmp_b + (size_t)j * row_elems;
   }
   int64_t r = L.lo + (p - L.n_c) - raw_base;
   if (r < 0 || r >= R_cap) return nullptr;
+  if (raw_pt.block_table) r = paged_row(raw_pt, b, (int)r);
+  if (r < 0) return nullptr;
   return kv_raw_b + (size_t)r * row_elems;
 }
 
@@ -126,20 +133,25 @@ constexpr float PF_RESCALE = 8.0f;   // log2 headroom before the maximum is rais
 // (top-k entries + window) rather than HCA (every visible entry + window).
 // Two waves per SIMD: the register budget is held to 256 so that a second
 // workgroup hides the first one's load and barrier latency.
-template <int NH, int PF_ROWS, bool SPARSE>
+// PG: paged window rows (raw_pt) and, for HCA, paged compressed entries
+// (cmp_pt): a shared-segment row is found through its sequence's block
+// table, and rows of absent pages are masked.
+template <int NH, int PF_ROWS, bool SPARSE, bool PG>
 __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv_cmp,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp,
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, float scale_log2, const float* __restrict__ sink, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int64_t cmp_rows_b, Varlen vl) {
+    float* __restrict__ lse, int64_t cmp_rows_b, Varlen vl, PageTable cmp_pt, PageTable raw_pt) {
   constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH;
   constexpr bool dense = !SPARSE;
   // phase A uses tiles 0..1 (double buffer); phase B tile r per row
   constexpr int NTILES = SPARSE && PF_ROWS > 2 ? PF_ROWS : 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NTILES * PF_TILE];
   __shared__ __attribute__((aligned(16))) int idx_all[SPARSE ? PF_ROWS : 1][SPARSE ? PF_IDX_MAX : 1];
+  // paged shared segments: whether each row of the two tile buffers exists
+  __shared__ int rowok[PG ? 2 : 1][PG ? PF_KT : 1];
   // the wave index is a scalar so that every per-wave decision below is a
   // uniform branch
   const int tid = threadIdx.x, lane = tid & 63;
@@ -154,8 +166,10 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   // offsets into the packed tensors, the raw rows being the sequence's own
   // tokens from position 0; T is then the longest sequence)
   size_t qrow0 = (size_t)b * T;
+  // (a paged segment addresses its shared pool: no per-sequence offset; the
+  // host passes cmp_rows_b = 0 for a paged compressed cache)
   const uint16_t* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
-  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  const uint16_t* kvr_b = kv_raw + (PG && raw_pt.block_table ? 0 : (size_t)b * R_cap * 2 * D);
   if (vl.cu_q) {
     qrow0 = (size_t)vl.cu_q[b];
     T = vl.cu_q[b + 1] - vl.cu_q[b];
@@ -276,10 +290,12 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   constexpr int CHA = PF_KT * 32 / NT;  // 16-byte chunks per thread per shared tile
   const int colA = tid & 31;
   u32x4 pfa[CHA];
+  bool pva[CHA];  // paged: the row's page exists
   // Key kk of a segment is cache row row0 + kk; it is loaded when kk < kk_lim
   // and the row is below row_lim, else row 0 of the same cache stands in (a
   // segment has tiles only when its cache has rows).  Byte offsets fit in 32
-  // bits: caches hold at most 2^23 rows of 512 bytes.
+  // bits: caches hold at most 2^23 rows of 512 bytes.  Paged: the row's pool
+  // row, pool row 0 standing in for an absent page.
   auto issueA = [&](int ti) {
     const bool seg0 = ti < tiles0;  // uniform
     const char* base = (const char*)(seg0 ? kvc_b : kvr_b);
@@ -291,14 +307,32 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     for (int i = 0; i < CHA; ++i) {
       const int rr = i * (NT / 32) + (tid >> 5);
       const int row = row0 + rr;
-      const bool ok = (kk0 + rr < kk_lim) & ((uint32_t)row < row_lim);
-      const uint32_t off = (uint32_t)(ok ? row : 0) * (uint32_t)(4 * D) + 16u * (uint32_t)colA;
+      bool ok = (kk0 + rr < kk_lim) & ((uint32_t)row < row_lim);
+      int prow = row;
+      if constexpr (PG) {
+        const PageTable& spt = seg0 ? cmp_pt : raw_pt;
+        if (spt.block_table) {  // uniform: this segment's cache is paged
+          const int64_t pr = ok ? paged_row(spt, b, row) : -1;
+          ok = pr >= 0;
+          prow = (int)pr;
+        }
+        pva[i] = ok;
+      }
+      const uint32_t off = (uint32_t)(ok ? prow : 0) * (uint32_t)(4 * D) + 16u * (uint32_t)colA;
       pfa[i] = *(const u32x4*)(base + off);
+    }
+  };
+  auto putA = [&](uint16_t* tile, int buf) {
+    for (int i = 0; i < CHA; ++i) {
+      const int rr = i * (NT / 32) + (tid >> 5);
+      put(tile, rr, colA, pfa[i]);
+      if constexpr (PG)
+        if (colA == 0) rowok[buf][rr] = pva[i];
     }
   };
   if (ntA > 0) {
     issueA(0);
-    for (int i = 0; i < CHA; ++i) put(smem, i * (NT / 32) + (tid >> 5), colA, pfa[i]);
+    putA(smem, 0);
     if (ntA > 1) issueA(1);
     __syncthreads();
   }
@@ -313,13 +347,14 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
       const int64_t r = tok - rbase;
       ok = tok >= w_lo && tok <= w_hi && r >= 0 && r < R_cap;
     }
+    if constexpr (PG) ok = ok && rowok[ti & 1][l32];
     const uint32_t vmask = (uint32_t)__ballot(ok);
     if (active && vmask) compute(cur, cur + PF_KT * PF_KS, vmask);
     if (ti + 1 < ntA) {
       // tile ti+1 goes into the other buffer, last read for tile ti-1 before
       // the previous barrier
       uint16_t* nxt = smem + ((ti + 1) & 1) * PF_TILE;
-      for (int i = 0; i < CHA; ++i) put(nxt, i * (NT / 32) + (tid >> 5), colA, pfa[i]);
+      putA(nxt, (ti + 1) & 1);
       if (ti + 2 < ntA) issueA(ti + 2);
     }
     __syncthreads();
@@ -441,7 +476,8 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, bool dense, float scale_log2, const float* __restrict__ sink, int n_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int64_t cmp_rows_b, PageTable pt, int nc_logical, Varlen vl) {
+    float* __restrict__ part_ml, int64_t cmp_rows_b, PageTable pt, int nc_logical, Varlen vl,
+    PageTable raw_pt) {
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
   constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
@@ -459,8 +495,11 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   const int t = vl.cu_q ? rowi - vl.cu_q[b] : rowi % T;
   // packed sequences: the sequence's entries and its own tokens as the raw
   // rows, positions from 0
-  const uint16_t* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
-  const uint16_t* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  // (pt with the dense form and raw_pt: rows found in the shared pools on
+  // load; pt with the sparse form: the staged indices are pool rows)
+  const bool cmp_paged = dense && pt.block_table;
+  const uint16_t* kvc_b = kv_cmp + (cmp_paged ? 0 : (size_t)b * cmp_rows_b * 2 * D);
+  const uint16_t* kvr_b = kv_raw + (raw_pt.block_table ? 0 : (size_t)b * R_cap * 2 * D);
   if (vl.cu_q) {
     kvc_b = kv_cmp + (size_t)vl.cu_k[b] * 2 * D;
     kvr_b = kv_raw + (size_t)vl.cu_q[b] * 2 * D;
@@ -497,7 +536,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
         const int i = i0 + u * NT + tid;
         v[u] = i < c_hi - c_lo ? idx_row[c_lo + i] : 0;
       }
-      if (pt.block_table) {  // paged: logical entries to pool rows
+      if (pt.block_table && !dense) {  // paged: logical entries to pool rows
         for (int u = 0; u < 4; ++u)
           v[u] = (v[u] >= 0 && v[u] < nc_logical) ? (int)paged_row(pt, b, v[u]) : -1;
       }
@@ -540,8 +579,12 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
       #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int p = p0 + i * (NT / 32) + (tid >> 5);
-        const int j = dense ? p : idx_s[min(max(0, p - c_lo), DC_IDX_MAX - 1)];
-        const bool ok = (p < n_c) & (j >= 0) & (j < Nc_cap);
+        int j = dense ? p : idx_s[min(max(0, p - c_lo), DC_IDX_MAX - 1)];
+        bool ok = (p < n_c) & (j >= 0) & (j < Nc_cap);
+        if (cmp_paged && ok) {
+          j = (int)paged_row(pt, b, j);
+          ok = j >= 0;
+        }
         pv[i] = ok;
         off[i] = ok ? (uint32_t)j * kRowBytes : 0u;
       }
@@ -549,8 +592,12 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
       #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int w = p0 - nc_pad + i * (NT / 32) + (tid >> 5);
-        const int64_t r = w_row0 + w;
-        const bool ok = (ti < ntiles) & (w < n_w) & (r >= 0) & (r < R_cap);
+        int64_t r = w_row0 + w;
+        bool ok = (ti < ntiles) & (w < n_w) & (r >= 0) & (r < R_cap);
+        if (raw_pt.block_table && ok) {
+          r = paged_row(raw_pt, b, (int)r);
+          ok = r >= 0;
+        }
         pv[i] = ok;
         off[i] = ok ? (uint32_t)r * kRowBytes : 0u;
       }
@@ -740,13 +787,13 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
     const int32_t* __restrict__ n_cmp, const int64_t* __restrict__ raw_base, int T, int H, int D,
     int topk, int window, int m, int Nc_cap, int R_cap, bool dense, float scale_log2,
     const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse,
-    int64_t cmp_rows_b, Varlen vl) {
+    int64_t cmp_rows_b, Varlen vl, PageTable cmp_pt, PageTable raw_pt) {
   const int lane = threadIdx.x;
   const int rowi = blockIdx.x / H, h = blockIdx.x % H;
   const int b = vl.cu_q ? varlen_seq(vl, rowi) : rowi / T;
   const int t = vl.cu_q ? rowi - vl.cu_q[b] : rowi % T;
-  const float* kvc_b = kv_cmp + (size_t)b * cmp_rows_b * 2 * D;
-  const float* kvr_b = kv_raw + (size_t)b * R_cap * 2 * D;
+  const float* kvc_b = kv_cmp + (cmp_pt.block_table ? 0 : (size_t)b * cmp_rows_b * 2 * D);
+  const float* kvr_b = kv_raw + (raw_pt.block_table ? 0 : (size_t)b * R_cap * 2 * D);
   if (vl.cu_q) {  // packed sequences (positions from 0, own tokens as raw rows)
     kvc_b = kv_cmp + (size_t)vl.cu_k[b] * 2 * D;
     kvr_b = kv_raw + (size_t)vl.cu_q[b] * 2 * D;
@@ -765,7 +812,8 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
   const float q1 = lane + 64 < D ? qr[lane + 64] : 0.0f;
   float mrun = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
   for (int p = 0; p < nk; ++p) {
-    const float* src = key_row(p, L, dense, idx_row, kvc_b, Nc_cap, kvr_b, R_cap, rbase, 2 * D);
+    const float* src = key_row(p, L, dense, idx_row, kvc_b, Nc_cap, kvr_b, R_cap, rbase, 2 * D,
+                               b, cmp_pt, raw_pt);
     if (!src) continue;
     float part = (lane < D ? q0 * src[lane] : 0.0f) + (lane + 64 < D ? q1 * src[lane + 64] : 0.0f);
     const float s = wave_sum(part) * scale_log2;
@@ -884,8 +932,14 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
   const float scale_log2 = a.scale * kLog2e;
   int64_t cmp_rows_b = a.Nc_cap;  // rows of one sequence's compressed cache
   const int nc_logical = a.Nc_cap;
-  PageTable dec_pages{nullptr, 0, 0, 0};
-  if (a.pages.block_table && a.dt != CSA_DT_F32 && use_decode_kernel(rows, a.H)) {
+  PageTable dec_pages{nullptr, 0, 0, 0}, cmp_pt{nullptr, 0, 0, 0};
+  const PageTable raw_pt = a.raw_pages;
+  if (a.pages.block_table && a.dense) {
+    // paged entries of the dense form: every kernel finds each visible entry
+    // through the table when it loads it
+    cmp_pt = a.pages;
+    cmp_rows_b = 0;
+  } else if (a.pages.block_table && a.dt != CSA_DT_F32 && use_decode_kernel(rows, a.H)) {
     // paged decode rows: the kernel maps each staged index to its pool row
     dec_pages = a.pages;
     a.Nc_cap = a.pages.n_pages << a.pages.page_log2;
@@ -907,7 +961,7 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
     attn_f32_kernel<<<rows * a.H, 64, 0, st>>>(
         (const float*)a.q, (const float*)a.kv_cmp, a.idx, (const float*)a.kv_raw, a.q_pos,
         a.n_cmp, a.raw_base, a.T, a.H, a.D, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
-        scale_log2, a.sink, (float*)a.out, a.lse, cmp_rows_b, a.vl);
+        scale_log2, a.sink, (float*)a.out, a.lse, cmp_rows_b, a.vl, cmp_pt, raw_pt);
     return hipGetLastError();
   }
   const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
@@ -922,29 +976,42 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
-          dec_pages, nc_logical, a.vl);
+          a.dense ? cmp_pt : dec_pages, nc_logical, a.vl, raw_pt);
     else
       attn_dec_kernel<2><<<grid, 128, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
-          dec_pages, nc_logical, a.vl);
+          a.dense ? cmp_pt : dec_pages, nc_logical, a.vl, raw_pt);
   } else {
     // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
     // rows share only the window: 2 rows, so that two independent
     // workgroups fill each CU.
-#define CSA_LAUNCH_PF(NH, ROWS, SP)                                                               \
-  attn_pf_kernel<NH, ROWS, SP><<<(unsigned)(a.B * ((a.T + ROWS - 1) / ROWS)), 64 * ROWS * NH, 0,   \
-                                 st>>>(                                                             \
+#define CSA_LAUNCH_PF(NH, ROWS, SP, PG)                                                           \
+  attn_pf_kernel<NH, ROWS, SP, PG><<<(unsigned)(a.B * ((a.T + ROWS - 1) / ROWS)), 64 * ROWS * NH, \
+                                     0, st>>>(                                                     \
       (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw, a.q_pos,  \
       a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, scale_log2, a.sink,      \
-      (uint16_t*)a.out, a.lse, cmp_rows_b, a.vl)
+      (uint16_t*)a.out, a.lse, cmp_rows_b, a.vl, cmp_pt, raw_pt)
+    // paged window rows or paged dense entries: the variant that looks rows
+    // up in the block tables
+    const bool pg = cmp_pt.block_table || raw_pt.block_table;
     if (a.H == 64) {
-      if (a.dense) CSA_LAUNCH_PF(2, 4, false);
-      else CSA_LAUNCH_PF(2, 2, true);
+      if (a.dense) {
+        if (pg) CSA_LAUNCH_PF(2, 4, false, true);
+        else CSA_LAUNCH_PF(2, 4, false, false);
+      } else {
+        if (pg) CSA_LAUNCH_PF(2, 2, true, true);
+        else CSA_LAUNCH_PF(2, 2, true, false);
+      }
     } else {
-      if (a.dense) CSA_LAUNCH_PF(1, 4, false);
-      else CSA_LAUNCH_PF(1, 2, true);
+      if (a.dense) {
+        if (pg) CSA_LAUNCH_PF(1, 4, false, true);
+        else CSA_LAUNCH_PF(1, 4, false, false);
+      } else {
+        if (pg) CSA_LAUNCH_PF(1, 2, true, true);
+        else CSA_LAUNCH_PF(1, 2, true, false);
+      }
     }
 #undef CSA_LAUNCH_PF
   }

@@ -249,9 +249,10 @@ struct AttnArgs {
   void* out;
   float* lse;
   void* ws;
-  csa::PageTable pages;  // block_table null: unpaged kv_cmp (sparse only)
+  csa::PageTable pages;  // block_table null: unpaged kv_cmp
   csa::Varlen vl;        // cu_q null: fixed [B, T] layout
   int total_rows;        // packed sequences: query rows (T is then the longest)
+  csa::PageTable raw_pages;  // block_table null: unpaged kv_raw
 };
 size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse);
 // the static scratch of csa_sparse_attn_noalloc: its size and its device

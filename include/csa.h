@@ -335,17 +335,38 @@ csa_status_t csa_indexer_topk_paged(int B, int T, int H_I, int d_I, int Nc_cap, 
                                     hipStream_t stream);
 
 /*
- * csa_sparse_attn over a paged kv_cmp pool ([rows, 2 D]); idx holds logical
- * indices as csa_indexer_topk writes them.  The workspace is
- * csa_sparse_attn_paged_workspace_size() bytes (it also holds the selected
- * entries' pool rows).  BF16 pools hold at most 2^23 rows.
+ * csa_sparse_attn over a paged kv_cmp pool ([rows, 2 D]; pages), a paged raw
+ * window cache (raw_pages: raw row r of sequence b, the token raw_base[b] +
+ * r, is pool row block_table[b, r / page_size] * page_size + r % page_size
+ * of a kv_raw pool [rows, 2 D]; R_cap logical rows per sequence), or both;
+ * either may be NULL, not both.  idx holds logical indices as
+ * csa_indexer_topk writes them.  Rows of absent pages are skipped.  The
+ * workspace is csa_sparse_attn_paged_workspace_size() bytes with pages (it
+ * also holds the selected entries' pool rows), csa_sparse_attn_workspace_size()
+ * without.  BF16 pools hold at most 2^23 rows.
  */
 csa_status_t csa_sparse_attn_paged(int B, int T, int H, int D, int topk, int window, float scale,
                                    const float* sink, const int64_t* q_pos, const void* q,
                                    const void* kv_cmp, int Nc_cap, const csa_page_table_t* pages,
                                    const int32_t* idx, const void* kv_raw, int R_cap,
-                                   const int64_t* raw_base, csa_dtype_t dt, void* out, float* lse,
-                                   void* workspace, size_t ws_bytes, hipStream_t stream);
+                                   const int64_t* raw_base, const csa_page_table_t* raw_pages,
+                                   csa_dtype_t dt, void* out, float* lse, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hca_dense_attn over a paged compressed cache (pages: entry j of sequence b
+ * at its pool row of kv_cmp [rows, 2 D]), a paged raw window cache
+ * (raw_pages, as for csa_sparse_attn_paged), or both; either may be NULL,
+ * not both.  Entries and window rows of absent pages are skipped.  Everything
+ * else, the workspace included, is as in hca_dense_attn.
+ */
+csa_status_t hca_dense_attn_paged(int B, int T, int H, int D, int m, int window, float scale,
+                                  const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                                  const void* q, const void* kv_cmp, int Nc_cap,
+                                  const csa_page_table_t* pages, const void* kv_raw, int R_cap,
+                                  const int64_t* raw_base, const csa_page_table_t* raw_pages,
+                                  csa_dtype_t dt, void* out, float* lse, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream);
 size_t csa_sparse_attn_paged_workspace_size(int B, int T, int H, int D, int topk, int window);
 
 /*

@@ -138,9 +138,18 @@ def test_paged_entry_points_validate_the_page_table(L):
     b = L.csa_sparse_attn_workspace_size(2, 1, 64, 128, 512, 128)
     assert a == b + 2 * 512 * 4
     rc = L.csa_sparse_attn_paged(1, 1, 64, 128, 4, 4, C.c_float(1.0), None, dummy, dummy, dummy, 64,
-                                 None, dummy, dummy, 4, dummy, 1, dummy, None, dummy, 1 << 30,
+                                 None, dummy, dummy, 4, dummy, None, 1, dummy, None, dummy, 1 << 30,
                                  None)
-    assert rc == 1 and b"pages is required" in L.csa_last_error()
+    assert rc == 1 and b"pages or raw_pages is required" in L.csa_last_error()
+    # a window table shorter than R_cap
+    rc = L.csa_sparse_attn_paged(1, 1, 64, 128, 4, 4, C.c_float(1.0), None, dummy, dummy, dummy, 64,
+                                 None, dummy, dummy, 100, dummy, C.byref(_PT(16, 16, 4, 8)), 1,
+                                 dummy, None, dummy, 1 << 30, None)
+    assert rc == 1 and b"exceeds" in L.csa_last_error()
+    rc = L.hca_dense_attn_paged(1, 1, 64, 128, 128, 4, C.c_float(1.0), None, dummy, dummy, dummy,
+                                dummy, 64, None, dummy, 4, dummy, None, 1, dummy, None, dummy,
+                                1 << 30, None)
+    assert rc == 1 and b"pages or raw_pages is required" in L.csa_last_error()
 
 
 def test_page_table_checks_reject_bad_tables_before_any_call():

@@ -301,3 +301,107 @@ def test_paged_compress_absent_page_is_not_stored():
     keep[rows[0, :16]] = False
     keep[rows[1, 16:]] = False
     assert torch.equal(pb[keep], sb[keep])
+
+
+@pytest.mark.parametrize("dt,B,T", [(gen.BF16, 4, 1), (gen.BF16, 1, 1100), (gen.F32, 2, 30)])
+@pytest.mark.parametrize("both", [False, True])
+def test_paged_window_matches_unpaged_and_oracle(dt, B, T, both):
+    # the raw window cache in a pool of 32-row pages (alone, or with the
+    # compressed cache paged too): bit-exact with the unpaged call
+    d = gen.Draw(80 + T + both)
+    H, D = (64, 128) if dt == gen.BF16 else (8, 64)
+    Nc, R, W, m, P, Pr, topk = 900, T + 200, 128, 4, 64, 32, 64
+    q = gen.store(d.normal(B, T, H, D), dt)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), dt)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), dt)
+    q_pos = [4 * Nc - T - 3 - 5 * b for b in range(B)]
+    raw_base = [p + T - R for p in q_pos]
+    idx = _rand_idx(d, B, T, topk, lambda b, t: _n_vis(q_pos[b] + t, Nc, m, Nc), 0.1)
+    common = (W, dev_i64(q_pos), dev_i64(raw_base))
+    ou, lu = csa.csa_sparse_attn(q.to(DEV), kv_cmp.to(DEV), idx.to(DEV), kv_raw.to(DEV), *common,
+                                 want_lse=True)
+    rpt, rtable = _pages(B, R, Pr, seed=11 + T)
+    raw_pool = _to_pool(kv_raw, _rows(rtable, Pr, R), rpt.n_pages * Pr)
+    kw = dict(raw_pages=rpt)
+    cmp_in = kv_cmp.to(DEV)
+    if both:
+        cpt, ctable = _pages(B, Nc, P, seed=12 + T)
+        cmp_in = _to_pool(kv_cmp, _rows(ctable, P, Nc), cpt.n_pages * P)
+        kw["pages"] = cpt
+    op, lp = csa.csa_sparse_attn(q.to(DEV), cmp_in, idx.to(DEV), raw_pool, *common, want_lse=True,
+                                 **kw)
+    torch.cuda.synchronize()
+    _same_bits(op, ou, "paged window out")
+    _same_bits(lp, lu, "paged window lse")
+    rows = range(0, T, max(1, T // 12))
+    for t in rows:
+        r, l = orc.sparse_attn(gen.host_bits(q)[:, t:t + 1], gen.host_bits(kv_cmp),
+                               idx.numpy()[:, t:t + 1], gen.host_bits(kv_raw), W,
+                               [p + t for p in q_pos], raw_base)
+        attn_check(op[:, t:t + 1], lp[:, t:t + 1], r, l, q.dtype, "paged window row %d" % t)
+
+
+@pytest.mark.parametrize("T", [1, 1030])
+def test_paged_hca_matches_unpaged(T):
+    # HCA with its compressed cache and its window cache both paged: the
+    # prefill kernel's shared segments and the decode kernel find every row
+    # through the tables; bit-exact with the unpaged call
+    d = gen.Draw(85 + T)
+    B, H, D, m, W, Nc, P, Pr = 2, 64, 128, 16, 64, 300, 16, 32
+    R = T + W
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    q_pos = [m * Nc - T - 1, m * 200]
+    n_cmp = [Nc, 250]
+    raw_base = [p - W + 1 for p in q_pos]
+    args = (m, W, dev_i64(q_pos), dev_i32(n_cmp), dev_i64(raw_base))
+    ou, lu = csa.hca_dense_attn(q.to(DEV), kv_cmp.to(DEV), kv_raw.to(DEV), *args, want_lse=True)
+    cpt, ctable = _pages(B, Nc, P, seed=T)
+    rpt, rtable = _pages(B, R, Pr, seed=T + 1)
+    op, lp = csa.hca_dense_attn(q.to(DEV), _to_pool(kv_cmp, _rows(ctable, P, Nc), cpt.n_pages * P),
+                                _to_pool(kv_raw, _rows(rtable, Pr, R), rpt.n_pages * Pr), *args,
+                                want_lse=True, pages=cpt, raw_pages=rpt)
+    torch.cuda.synchronize()
+    _same_bits(op, ou, "paged hca out")
+    _same_bits(lp, lu, "paged hca lse")
+    for t in (0, T // 2, T - 1):
+        r, l = orc.hca_dense_attn(gen.host_bits(q)[:, t:t + 1], gen.host_bits(kv_cmp),
+                                  gen.host_bits(kv_raw), m, W, [p + t for p in q_pos], n_cmp,
+                                  raw_base)
+        attn_check(op[:, t:t + 1], lp[:, t:t + 1], r, l, q.dtype, "paged hca row %d" % t)
+
+
+def test_paged_window_absent_page_rows_are_skipped():
+    # a window page marked absent: its rows leave the softmax, checked
+    # against the library attention with those keys masked out
+    from tests import brute
+    d = gen.Draw(88)
+    B, T, H, D, W, Pr = 1, 3, 64, 128, 100, 16
+    R = T + W
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    q_pos = [5000]
+    raw_base = [q_pos[0] + T - R]
+    rpt, rtable = _pages(B, R, Pr, seed=88)
+    bad = rtable.clone()
+    bad[0, 2] = -1                     # raw rows 32..47 absent
+    raw_pool = _to_pool(kv_raw, _rows(rtable, Pr, R), rpt.n_pages * Pr)
+    pt_bad = csa.PageTable(bad.to(DEV), Pr, rpt.n_pages, nc_cap=R)
+    op, _ = csa.csa_sparse_attn(q.to(DEV), torch.zeros(1, 1, 2 * D, dtype=torch.bfloat16,
+                                                         device=DEV), None, raw_pool, W,
+                                dev_i64(q_pos), dev_i64(raw_base), raw_pages=pt_bad)
+    torch.cuda.synchronize()
+    kr = gen.host_bits(kv_raw)[0]
+    keys = brute.decode_bits(kr[:, :D])
+    vals = brute.decode_bits(kr[:, D:])
+    mask = np.zeros((T, R), bool)
+    for t in range(T):
+        pos = q_pos[0] + t
+        for tok in range(pos - W + 1, pos + 1):
+            r = tok - raw_base[0]
+            if 0 <= r < R and not (32 <= r < 48):
+                mask[t, r] = True
+    ref, _ = brute.sdpa_masked(brute.decode_bits(gen.host_bits(q)[0]), keys, vals, mask, D ** -0.5)
+    from tests.helpers import assert_bf16_close
+    assert_bf16_close(op[0].float().cpu().numpy(), ref, "absent window page")
