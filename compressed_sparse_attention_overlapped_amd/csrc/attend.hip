@@ -109,30 +109,39 @@ __device__ __forceinline__ void finish_softmax(float m, float l, const float* si
 //    workgroup (double-buffered, one barrier per tile); each wave masks keys
 //    outside its own row's visibility;
 //  * phase B - CSA only: each row's selected compressed rows are gathered into
-//    that row's LDS tile by the row's waves (the index row is staged first).
+//    that row's own pair of LDS tiles by the row's waves (the index row is
+//    staged first).
+// Tiles move from global memory straight into LDS (global_load_lds_dwordx4:
+// lane l of one instruction writes the 16 bytes at instruction base + 16 l),
+// two 512-byte [K | V] rows per instruction, with no register staging and no
+// LDS store instructions; one barrier per tile publishes a tile and frees the
+// other buffer.  Rows are 512 bytes apart in a tile and the 16-byte chunk c
+// of row r sits at slot c ^ pf_swz(r): 16 consecutive rows read at one chunk
+// by the K fragment loads, and 4 rows read by the V transpose loads, fall in
+// distinct bank groups.  The loader places a chunk by choosing, per lane, the
+// global chunk that belongs in that lane's slot.
 // Per wave and 32-key tile: S^T (32 keys x 32 heads) = K Q^T in 8 MFMA
 // 32x32x16 and O^T (128 dims x 32 heads) += V^T P^T in 8 more; the S^T
 // accumulator is the P^T operand once the second product's k order is
 // permuted to match, and V^T fragments come from the LDS transpose read.
-// K and V halves of a row sit in separate LDS arrays whose strides suit their
-// readers: 272 B (68 dwords) for the 16-byte K reads, so that 16 rows hit 16
-// distinct 4-bank groups; 320 B (80 dwords, 16 mod 64) for the 8-byte
-// transpose reads of V, whose 32-lane halves cover 4 rows x 16 dwords each.
 // Every tile load is issued unconditionally (empty slots read a valid dummy
-// row and are masked), so that the waits count the loads exactly.  The running maximum is
-// only raised when a tile exceeds it by more than 2^8 (the final
-// normalisation makes the result independent of the maximum used).
+// row and are masked).  The running maximum is only raised when a tile
+// exceeds it by more than 2^8 (the final normalisation makes the result
+// independent of the maximum used).
 constexpr int PF_KT = 32;
-constexpr int PF_KS = 128 + 8;       // bf16 per K row in LDS (272 B)
-constexpr int PF_VS = 128 + 32;      // bf16 per V row in LDS (320 B)
-constexpr int PF_TILE = PF_KT * (PF_KS + PF_VS);
-constexpr int PF_IDX_MAX = 2048;     // index slots per row staged in LDS
-constexpr float PF_RESCALE = 8.0f;   // log2 headroom before the maximum is raised
+constexpr int PF_ROWB = 512;                // bytes of one [K | V] row
+constexpr int PF_TILEB = PF_KT * PF_ROWB;   // 16 KB per tile
+constexpr int PF_IDX_MAX = 1024;            // index slots per row staged in LDS
+constexpr float PF_RESCALE = 8.0f;          // log2 headroom before the maximum is raised
 
-// H = 32 NH: waves per row; PF_ROWS query rows per workgroup; SPARSE: CSA
-// (top-k entries + window) rather than HCA (every visible entry + window).
-// Two waves per SIMD: the register budget is held to 256 so that a second
-// workgroup hides the first one's load and barrier latency.
+// chunk slot permutation of tile row r (an involution on the 16 chunks of
+// either half of the row)
+__device__ __forceinline__ int pf_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// H = 32 NH; PF_ROWS query rows per workgroup; SPARSE: CSA (top-k entries +
+// window) rather than HCA (every visible entry + window).  Two waves per
+// SIMD: the register budget is held to 256 so that a second workgroup hides
+// the first one's load and barrier latency.
 // PG: paged window rows (raw_pt) and, for HCA, paged compressed entries
 // (cmp_pt): a shared-segment row is found through its sequence's block
 // table, and rows of absent pages are masked.
@@ -144,11 +153,16 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const int64_t* __restrict__ raw_base, int T, int topk, int window, int m, int Nc_cap,
     int R_cap, float scale_log2, const float* __restrict__ sink, uint16_t* __restrict__ out,
     float* __restrict__ lse, int64_t cmp_rows_b, Varlen vl, PageTable cmp_pt, PageTable raw_pt) {
-  constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH;
+  constexpr int H = 32 * NH, D = 128, NT = 64 * PF_ROWS * NH, NW = NT / 64;
   constexpr bool dense = !SPARSE;
-  // phase A uses tiles 0..1 (double buffer); phase B tile r per row
-  constexpr int NTILES = SPARSE && PF_ROWS > 2 ? PF_ROWS : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NTILES * PF_TILE];
+  // phase A: tiles tile0[0] and tile1[0] (shared); phase B: row r's tiles
+  // tile0[r] and tile1[r].  The two buffers are distinct variables so that the
+  // compiler can tell reads of one from the loads in flight into the other
+  // (otherwise it waits for every load before any read of the tile memory).
+  constexpr int NROWBUF = SPARSE ? PF_ROWS : 1;
+  static_assert(16 % NW == 0 && 16 % NH == 0, "a tile is 16 two-row load instructions");
+  __shared__ __attribute__((aligned(16))) uint8_t tile0[NROWBUF][PF_TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1[NROWBUF][PF_TILEB];
   __shared__ __attribute__((aligned(16))) int idx_all[SPARSE ? PF_ROWS : 1][SPARSE ? PF_IDX_MAX : 1];
   // paged shared segments: whether each row of the two tile buffers exists
   __shared__ int rowok[PG ? 2 : 1][PG ? PF_KT : 1];
@@ -204,22 +218,48 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
   float mrun = -INFINITY, lrun = 0.0f;
 
-  // transpose-read offset inside a V tile: lane j of a 16-lane group supplies
-  // key row 16 ks + 4 h' + j/4 (+ 8 for the second read), dims
-  // 32 dt + 16 (group & 1) + 4 (j & 3)
+  // byte offsets of this lane's fragments inside a tile: K fragment s is key
+  // row l32, chunk 2 s + h2 (dims 16 s + 8 h2 ..); the transpose reads of V
+  // take key row 4 (g / 2) + j / 4 (+ 8 for the second read, + 16 per k
+  // step), dims 32 dt + 16 (g & 1) + 4 (j & 3), for lane j of 16-lane group g
   const int gg = lane >> 4, jj = lane & 15;
-  const int tr_off = (4 * (gg >> 1) + (jj >> 2)) * PF_VS + 16 * (gg & 1) + 4 * (jj & 3);
+  uint32_t kofs[8], vofs[4][2];
+  {
+    const int fk = pf_swz(l32);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kofs[s] = (uint32_t)(l32 * PF_ROWB + 16 * ((2 * s + h2) ^ fk));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 4 * (gg >> 1) + (jj >> 2) + 8 * e;
+      const int fr = pf_swz(r);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int c = 16 + 4 * dt + 2 * (gg & 1) + ((jj & 3) >> 1);
+        vofs[dt][e] = (uint32_t)(r * PF_ROWB + 16 * (c ^ fr) + 8 * (jj & 1));
+      }
+    }
+  }
+  // phase base: the fragment offsets then point into buffer 0 of the phase
+  auto rebase = [&](uint32_t base) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kofs[s] += base;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      vofs[dt][0] += base;
+      vofs[dt][1] += base;
+    }
+  };
 
-  // One tile (K rows at ks_t, V rows at vs_t); vmask bit k: key k attended.
-  auto compute = [&](const uint16_t* ks_t, const uint16_t* vs_t, uint32_t vmask) {
+  // One tile in the phase's buffer BUF; vmask bit k: key k attended.
+  auto compute = [&](auto buf_tag, uint32_t vmask) {
+    const uint8_t* const tb = decltype(buf_tag)::value ? &tile1[0][0] : &tile0[0][0];
     f32x16 sacc;
     for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-    const uint16_t* krow = ks_t + l32 * PF_KS + 8 * h2;
     // all eight K fragments are read before the products start, so that one
     // LDS latency is exposed per tile instead of one per pair
     bf16x8 kf[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kf[s] = *(const bf16x8*)(krow + 16 * s);
+    for (int s = 0; s < 8; ++s) kf[s] = *(const bf16x8*)(tb + kofs[s]);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
@@ -259,17 +299,24 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
       for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)sacc[8 * ks + e];
     for (int ks = 0; ks < 2; ++ks)
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* tp = vs_t + tr_off + 16 * ks * PF_VS + 32 * dt;
-        const u32x2 v1 = __builtin_bit_cast(u32x2, lds_read_tr16(tp));
-        const u32x2 v2 = __builtin_bit_cast(u32x2, lds_read_tr16(tp + 8 * PF_VS));
+        const uint32_t ko = (uint32_t)ks * 16 * PF_ROWB;
+        const u32x2 v1 = __builtin_bit_cast(u32x2, lds_read_tr16((const uint16_t*)(tb + vofs[dt][0] + ko)));
+        const u32x2 v2 = __builtin_bit_cast(u32x2, lds_read_tr16((const uint16_t*)(tb + vofs[dt][1] + ko)));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{v1[0], v1[1], v2[0], v2[1]});
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
       }
   };
-  // LDS stores of one 16-byte chunk of row rr: chunks 0..15 are K, 16..31 V
-  auto put = [&](uint16_t* tile, int rr, int col, const u32x4& v) {
-    const int off = col < 16 ? rr * PF_KS + 8 * col : PF_KT * PF_KS + rr * PF_VS + 8 * (col - 16);
-    *(u32x4*)(tile + off) = v;
+  // the loads of a tile (global_load_lds) complete before the barrier that
+  // publishes it
+  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // one two-row load instruction: tile rows 2 i, 2 i + 1 (lane halves) into
+  // the LDS tile at `dst`; the lane's global row byte offset is `roff`
+  auto dma = [&](uint8_t* dst, int i, const char* base, uint32_t roff) {
+    const int r = 2 * i + h2;
+    const uint32_t c = (uint32_t)(l32 ^ pf_swz(r));  // the chunk that belongs in this slot
+    __builtin_amdgcn_global_load_lds((const void*)(base + roff + 16u * c),
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * i),
+                                     16, 0, 0);
   };
 
   // ---------------- phase A: shared contiguous segments
@@ -287,16 +334,15 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   // [0, R_cap) are skipped either way)
   const int64_t rw0_64 = win_first - rbase;
   const int rw0 = (int)(rw0_64 < -(1 << 30) ? -(1 << 30) : (rw0_64 > (1 << 30) ? (1 << 30) : rw0_64));
-  constexpr int CHA = PF_KT * 32 / NT;  // 16-byte chunks per thread per shared tile
-  const int colA = tid & 31;
-  u32x4 pfa[CHA];
-  bool pva[CHA];  // paged: the row's page exists
   // Key kk of a segment is cache row row0 + kk; it is loaded when kk < kk_lim
   // and the row is below row_lim, else row 0 of the same cache stands in (a
   // segment has tiles only when its cache has rows).  Byte offsets fit in 32
   // bits: caches hold at most 2^23 rows of 512 bytes.  Paged: the row's pool
-  // row, pool row 0 standing in for an absent page.
-  auto issueA = [&](int ti) {
+  // row, pool row 0 standing in for an absent page.  Wave w issues the
+  // instructions w, w + NW, ... of the tile.
+  auto issueA = [&](int ti, auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
+    uint8_t* const dst = buf ? &tile1[0][0] : &tile0[0][0];
     const bool seg0 = ti < tiles0;  // uniform
     const char* base = (const char*)(seg0 ? kvc_b : kvr_b);
     const int kk0 = (seg0 ? ti : ti - tiles0) * PF_KT;
@@ -304,8 +350,9 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const int row0 = seg0 ? kk0 : rw0 + kk0;
     const uint32_t row_lim = (uint32_t)(seg0 ? Nc_cap : R_cap);
 #pragma unroll
-    for (int i = 0; i < CHA; ++i) {
-      const int rr = i * (NT / 32) + (tid >> 5);
+    for (int k = 0; k < 16 / NW; ++k) {
+      const int i = wave + NW * k;
+      const int rr = 2 * i + h2;
       const int row = row0 + rr;
       bool ok = (kk0 + rr < kk_lim) & ((uint32_t)row < row_lim);
       int prow = row;
@@ -316,29 +363,13 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
           ok = pr >= 0;
           prow = (int)pr;
         }
-        pva[i] = ok;
+        if (l32 == 0) rowok[buf][rr] = ok;
       }
-      const uint32_t off = (uint32_t)(ok ? prow : 0) * (uint32_t)(4 * D) + 16u * (uint32_t)colA;
-      pfa[i] = *(const u32x4*)(base + off);
+      dma(dst, i, base, (uint32_t)(ok ? prow : 0) * (uint32_t)PF_ROWB);
     }
   };
-  auto putA = [&](uint16_t* tile, int buf) {
-    for (int i = 0; i < CHA; ++i) {
-      const int rr = i * (NT / 32) + (tid >> 5);
-      put(tile, rr, colA, pfa[i]);
-      if constexpr (PG)
-        if (colA == 0) rowok[buf][rr] = pva[i];
-    }
-  };
-  if (ntA > 0) {
-    issueA(0);
-    putA(smem, 0);
-    if (ntA > 1) issueA(1);
-    __syncthreads();
-  }
-  for (int ti = 0; ti < ntA; ++ti) {
-    uint16_t* cur = smem + (ti & 1) * PF_TILE;
-    // this wave's mask over the tile's 32 keys (key = lane & 31)
+  // this wave's mask over tile ti's 32 keys (key = lane & 31)
+  auto maskA = [&](int ti, int buf) -> uint32_t {
     bool ok;
     if (ti < tiles0) {
       ok = ti * PF_KT + l32 < nv_me;
@@ -347,41 +378,44 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
       const int64_t r = tok - rbase;
       ok = tok >= w_lo && tok <= w_hi && r >= 0 && r < R_cap;
     }
-    if constexpr (PG) ok = ok && rowok[ti & 1][l32];
-    const uint32_t vmask = (uint32_t)__ballot(ok);
-    if (active && vmask) compute(cur, cur + PF_KT * PF_KS, vmask);
-    if (ti + 1 < ntA) {
-      // tile ti+1 goes into the other buffer, last read for tile ti-1 before
-      // the previous barrier
-      uint16_t* nxt = smem + ((ti + 1) & 1) * PF_TILE;
-      putA(nxt, (ti + 1) & 1);
-      if (ti + 2 < ntA) issueA(ti + 2);
-    }
+    if constexpr (PG) ok = ok && rowok[buf][l32];
+    return (uint32_t)__ballot(ok);
+  };
+  // step of tile ti in buffer BUF: publish it, start tile ti + 1 in the
+  // other buffer (free: every wave finished tile ti - 1 before the barrier)
+  auto stepA = [&](auto buf_tag, int ti) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    wait_loads();
     __syncthreads();
+    if (ti + 1 < ntA) issueA(ti + 1, std::integral_constant<int, BUF ^ 1>{});
+    const uint32_t vmask = maskA(ti, BUF);
+    if (active && vmask) compute(buf_tag, vmask);
+  };
+  if (ntA > 0) {
+    issueA(0, std::integral_constant<int, 0>{});
+    for (int ti = 0; ti < ntA; ti += 2) {
+      stepA(std::integral_constant<int, 0>{}, ti);
+      if (ti + 1 < ntA) stepA(std::integral_constant<int, 1>{}, ti + 1);
+    }
   }
 
   // ---------------- phase B: each row's selected compressed entries
   // The index rows are staged in LDS, PF_IDX_MAX slots at a time, as entry
   // numbers or -1 (padding, out of range, past the list, a row past T), so
-  // that a tile's loads need one LDS read per four rows and never wait on a
-  // global index load.
+  // that a tile's loads need one LDS read per instruction and never wait on a
+  // global index load.  Row r's tiles are tile0[r] and tile1[r].
   if (SPARSE && topk > 0 && Nc_cap > 0) {
     const int32_t* idx_rows = idx + (qrow0 + t0) * topk;
     const int nrows = t_last - t0 + 1;
     const int* idx_s = idx_all[row_w];
-    // the row's NH waves load its tile: lane group gB (32 lanes, one 512-byte
-    // row per load) takes rows CHB gB .. CHB gB + CHB - 1
-    constexpr int CHB = PF_KT * 32 / (64 * NH);
-    static_assert(CHB % 4 == 0, "index slots are read four at a time");
-    const int rt = (wave % NH) * 64 + lane;     // thread index within the row
-    const int colB = rt & 31, gB = rt >> 5;
-    uint16_t* mine = smem + row_w * PF_TILE;
+    rebase((uint32_t)row_w * PF_TILEB);
     for (int c0 = 0; c0 < topk; c0 += PF_IDX_MAX) {
       const int cn = min(PF_IDX_MAX, topk - c0);
       const int cw = (cn + PF_KT - 1) / PF_KT * PF_KT;  // whole tiles
-      // every thread takes part: the barrier below, and the last one of the
-      // previous chunk's tile loop, order these stores against the reads
-      // (loads batched four per thread, from clamped addresses)
+      // every thread takes part: the barrier below orders these stores
+      // after every read of the previous chunk's slots and tiles (loads
+      // batched four per thread, from clamped addresses)
+      __syncthreads();
       const int n_st = PF_ROWS * cw;
       for (int i0 = 0; i0 < n_st; i0 += 4 * NT) {
         int v[4];
@@ -400,31 +434,31 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
         }
       }
       __syncthreads();
-      u32x4 pfb[CHB];
-      auto issueB = [&](int ti) {
-        const int* sp = idx_s + ti * PF_KT + CHB * gB;
-        int jv[CHB];
+      // the row's NH waves issue the 16 instructions of its tile: wave hh
+      // takes hh, hh + NH, ...
+      auto issueB = [&](int ti, auto buf_tag) {
+        uint8_t* const dst = decltype(buf_tag)::value ? &tile1[row_w][0] : &tile0[row_w][0];
 #pragma unroll
-        for (int q4 = 0; q4 < CHB / 4; ++q4) {
-          const i32x4 x = *(const i32x4*)(sp + 4 * q4);
-          for (int e = 0; e < 4; ++e) jv[4 * q4 + e] = x[e];
-        }
-#pragma unroll
-        for (int i = 0; i < CHB; ++i) {
-          const uint32_t off = (uint32_t)max(jv[i], 0) * (uint32_t)(4 * D) + 16u * (uint32_t)colB;
-          pfb[i] = *(const u32x4*)((const char*)kvc_b + off);
+        for (int k = 0; k < 16 / NH; ++k) {
+          const int i = hh + NH * k;
+          const int j = idx_s[ti * PF_KT + 2 * i + h2];
+          dma(dst, i, (const char*)kvc_b,
+              (uint32_t)max(j, 0) * (uint32_t)PF_ROWB);
         }
       };
       const int ntB = cw / PF_KT;
-      issueB(0);
-      for (int ti = 0; ti < ntB; ++ti) {
-#pragma unroll
-        for (int i = 0; i < CHB; ++i) put(mine, CHB * gB + i, colB, pfb[i]);
+      auto stepB = [&](auto buf_tag, int ti) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        wait_loads();
         __syncthreads();
-        if (ti + 1 < ntB) issueB(ti + 1);
+        if (ti + 1 < ntB) issueB(ti + 1, std::integral_constant<int, BUF ^ 1>{});
         const uint32_t vmask = (uint32_t)__ballot(idx_s[ti * PF_KT + l32] >= 0);
-        if (vmask) compute(mine, mine + PF_KT * PF_KS, vmask);
-        __syncthreads();
+        if (vmask) compute(buf_tag, vmask);
+      };
+      issueB(0, std::integral_constant<int, 0>{});
+      for (int ti = 0; ti < ntB; ti += 2) {
+        stepB(std::integral_constant<int, 0>{}, ti);
+        if (ti + 1 < ntB) stepB(std::integral_constant<int, 1>{}, ti + 1);
       }
     }
   }
