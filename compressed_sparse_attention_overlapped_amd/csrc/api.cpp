@@ -207,8 +207,6 @@ static csa_status_t indexer_impl(int B, int T, int H_I, int d_I, int Nc_cap, int
       return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: bf16/fp8/mxfp4 need H_I = 16, d_I = 64");
     if (!aligned16(q_idx) || (Nc_cap > 0 && !aligned16(k_idx)))
       return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: q_idx and k_idx must be 16-byte aligned");
-    if (qk_dt == CSA_DT_BF16 && Nc_cap > 8192 && T != 1)
-      return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk: bf16 rows longer than 8192 need T == 1");
   } else {
     return fail(CSA_E_ARG, "csa_indexer_topk: bad qk_dt %d", (int)qk_dt);
   }
@@ -542,9 +540,8 @@ csa_status_t csa_indexer_topk_varlen(int n, int total, int max_len, int H_I, int
   if (!q_idx || !w_idx || !idx_out || (max_cmp > 0 && !k_idx))
     return fail(CSA_E_ARG, "csa_indexer_topk_varlen: missing required pointer");
   if (topk > 8192) return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_varlen: topk > 8192");
-  if (max_cmp > 8192)
-    return fail(CSA_E_UNSUPPORTED,
-                "csa_indexer_topk_varlen: sequences of more than 8192 entries are not supported");
+  if (max_cmp > 1024 * 2048)
+    return fail(CSA_E_UNSUPPORTED, "csa_indexer_topk_varlen: max_cmp > 2^21");
   if (qk_dt == CSA_DT_F32) {
     if (!((H_I == 4 && d_I == 32) || (H_I == 16 && d_I == 64)))
       return fail(CSA_E_UNSUPPORTED,

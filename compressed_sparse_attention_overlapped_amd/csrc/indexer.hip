@@ -19,7 +19,11 @@
 //    into the chunk's segment; "finalize" (one workgroup per row) picks the
 //    missing entries among the candidates by an exact radix select on (key,
 //    then index), adds them to the bitmap and writes the selection in
-//    ascending order from it.
+//    ascending order from it.  The score workgroup must own one query row
+//    (a histogram per row), and the histogram starts at zero.
+//  * long rows the histogram path cannot take (bf16 prefill rows, packed
+//    sequences): exact selection over 8192-entry segments and merge levels
+//    of their candidates, with no workspace that must start at zero.
 #include <algorithm>
 
 #include <type_traits>
@@ -600,7 +604,9 @@ __global__ void __launch_bounds__(256) select_short_kernel(
   // first nsel entries.)
   const uint32_t diff = kmin ^ kmax;
   int hi = diff ? 31 - __clz((int)diff) : -1;  // highest bit where keys differ
-  uint32_t mask = hi < 0 ? 0xffffffffu : (hi >= 31 ? 0u : ~((2u << hi) - 1u));
+  // the bits above hi (all of them when every key is equal, hi = -1), as one
+  // 64-bit shift rather than nested selects
+  uint32_t mask = (uint32_t)(0xffffffffull << (hi + 1));
   uint32_t prefix = kmax & mask, remaining = (uint32_t)nsel;
   bool all_eq = false;
   auto radix_pass = [&](auto bpl_tag) {
@@ -1008,6 +1014,303 @@ __global__ void zero_u32_kernel(uint32_t* __restrict__ p, size_t n) {
     p[i] = 0u;
 }
 
+// ---------------------------------------------------------------- long rows: segments
+// The long rows that the histogram path cannot take (bf16 prefill rows,
+// whose score workgroups span 16 query rows, and packed sequences) are
+// selected in segments: a workgroup of NT
+// threads keeps the exact best min(topk, n) of up to 32 NT items.  Level 0
+// takes segments of 8192 entries (256 threads, so that a row spreads over
+// many compute units); merge levels select again among the candidates of
+// several segments, P (a power of two >= topk) being the slot stride of a
+// segment's candidates, until one group per row remains (the best topk of a
+// row lie among the best topk of its segments); a merge workgroup has 256,
+// 512 or 1024 threads, as its candidates need.  Thread t owns the 32 consecutive items [32 t, 32 t + 32):
+// they are loaded coalesced into LDS and read back per thread, so that index
+// order is thread order, then bit order.
+// The k-th key is found by narrowing a key range [lo, lo + span]: each pass
+// histograms (key - lo) >> shift over 2048 bins, shift chosen so that the
+// range fits, for the items still in range (the first pass from registers,
+// later ones through a per-thread bit mask), and keeps the bin holding the
+// k-th key.  A final packed scan of the per-thread counts above and inside
+// the range places the selection in ascending index order; keys inside the
+// range (all equal once it is one key wide) are taken lowest index first.
+// Every workgroup writes all it produces and nothing accumulates across
+// workgroups, so no workspace starts at zero.
+constexpr int LS_KPT = 32, LS_SEG = 256 * LS_KPT;  // level 0: 8192 entries
+constexpr int LS_BINS = 2048;
+constexpr int LS_GROUP_MAX = 64;  // input segments per merge workgroup
+
+// visible entries of a query row
+__device__ __forceinline__ int row_visible(int row, const int64_t* q_pos, const int32_t* n_cmp,
+                                           int T, int Nc_cap, int m, Varlen vl) {
+  if (vl.cu_q) {
+    const int b = varlen_seq(vl, row);
+    return n_visible(row - vl.cu_q[b], vl.cu_k[b + 1] - vl.cu_k[b], m, Nc_cap);
+  }
+  const int b = row / T;
+  return n_visible(q_pos[b] + row % T, n_cmp[b], m, Nc_cap);
+}
+
+// LDS position of item q: the 16-byte chunk c of thread t's 32 items sits at
+// chunk c ^ ((t >> 1) & 7), so that both the coalesced stores (64 consecutive
+// items) and the per-thread 16-byte reads (16 threads) hit distinct banks
+__device__ __forceinline__ int ls_phys(int q) {
+  return (q & ~31) | ((((q >> 2) & 7) ^ ((q >> 6) & 7)) << 2) | (q & 3);
+}
+
+// inclusive prefix sum over the wave's lanes
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// FROM_SCORES: level 0, grid (rows, segments); the items are the segment's
+// visible entries.  Otherwise a merge level, grid (rows, ceil(n_in /
+// group)); the items are the slots s P + i (i below the count of input
+// segment s) of the workgroup's `group` input segments, in index order.  The
+// last level (one workgroup per row) writes idx_out and score_out, -1 / NaN
+// padded; the others write the candidates (key, entry) and their count.
+template <int NT, bool FROM_SCORES>
+__global__ void __launch_bounds__(NT) select_seg_kernel(
+    const float* __restrict__ scores, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, int topk, int p_log2, int n_in,
+    int group, const uint32_t* __restrict__ in_key, const int32_t* __restrict__ in_idx,
+    const int32_t* __restrict__ in_cnt, uint32_t* __restrict__ out_key,
+    int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out, Varlen vl) {
+  constexpr int NW = NT / 64, ITEMS = NT * LS_KPT, BPT = LS_BINS / NT;  // bins per thread
+  __shared__ __attribute__((aligned(16))) uint32_t keys_s[ITEMS];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][LS_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[2][NW];
+  __shared__ uint32_t res[4];
+  __shared__ int32_t scnt[LS_GROUP_MAX];
+  const int row = blockIdx.x, grp = blockIdx.y, n_out = gridDim.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float* srow = scores + (size_t)row * Nc_cap;
+  const int P = 1 << p_log2;
+  // level 0: entries seg0 + q, q < n_items; merge: slots q of the
+  // candidates starting at in_base
+  int n_items = 0, seg0 = 0;
+  const size_t in_base = ((size_t)row * n_in + (size_t)grp * group) << p_log2;
+  if constexpr (FROM_SCORES) {
+    const int nv = row_visible(row, q_pos, n_cmp, T, Nc_cap, m, vl);
+    seg0 = grp * ITEMS;
+    n_items = min(max(nv - seg0, 0), ITEMS);
+  } else {
+    if (tid < group) {
+      const int sg = grp * group + tid;
+      scnt[tid] = sg < n_in ? in_cnt[(size_t)row * n_in + sg] : 0;
+    }
+    __syncthreads();
+    for (int sg = 0; sg < group; ++sg) n_items += scnt[sg];
+  }
+  const int nsel = min(topk, n_items);
+  const bool last = n_out == 1;
+  int32_t* orow = idx_out + (size_t)row * topk;
+  float* sorow = score_out ? score_out + (size_t)row * topk : nullptr;
+  const size_t out_base = ((size_t)row * n_out + grp) << p_log2;
+  if (last) {
+    for (int k = nsel + tid; k < topk; k += NT) {
+      orow[k] = -1;
+      if (sorow) sorow[k] = __uint_as_float(0x7fc00000u);
+    }
+  } else if (tid == 0) {
+    out_cnt[(size_t)row * n_out + grp] = nsel;
+  }
+  if (nsel == 0) return;  // uniform
+
+  // whether item q exists
+  auto item_ok = [&](int q) -> bool {
+    if constexpr (FROM_SCORES) return q < n_items;
+    const int sg = q >> p_log2;
+    return sg < group && (q & (P - 1)) < scnt[min(sg, group - 1)];
+  };
+  // coalesced loads (all issued before the first is used; clamped
+  // addresses) into LDS; both histogram buffers cleared meanwhile
+  {
+    uint32_t x[LS_KPT];
+#pragma unroll
+    for (int r = 0; r < LS_KPT; ++r) {
+      const int q = r * NT + tid;
+      if constexpr (FROM_SCORES) x[r] = score_key(srow[seg0 + min(q, n_items - 1)]);
+      else x[r] = in_key[in_base + (item_ok(q) ? q : 0)];
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; i += 2) *(u32x2*)&hist[0][BPT * tid + i] = u32x2{0u, 0u};
+#pragma unroll
+    for (int r = 0; r < LS_KPT; ++r) keys_s[ls_phys(r * NT + tid)] = x[r];
+  }
+  __syncthreads();
+  // this thread's items; invalid ones count as absent everywhere below
+  uint32_t kr[LS_KPT];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const u32x4 v = *(const u32x4*)&keys_s[ls_phys(32 * tid + 4 * c)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kr[4 * c + e] = v[e];
+  }
+  uint32_t vb;  // bit u: item 32 tid + u exists
+  if constexpr (FROM_SCORES) {
+    const int nmine = min(max(n_items - 32 * tid, 0), 32);
+    vb = nmine >= 32 ? 0xffffffffu : ((1u << nmine) - 1u);
+  } else {
+    vb = 0u;
+#pragma unroll
+    for (int u = 0; u < LS_KPT; ++u) vb |= item_ok(32 * tid + u) ? 1u << u : 0u;
+  }
+
+  // the selected set: keys above lo + span, plus the `remaining` lowest-index
+  // keys in [lo, lo + span] (all of them with all_in)
+  uint32_t lo = 0u, span = 0xffffffffu, remaining = (uint32_t)nsel;
+  bool all_in = nsel == n_items;  // every item: the full range holds them all
+  if (!all_in) {
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < LS_KPT; ++u) {
+      const bool ok = (vb >> u) & 1u;
+      kmin = min(kmin, ok ? kr[u] : 0xffffffffu);
+      kmax = max(kmax, ok ? kr[u] : 0u);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    }
+    if (lane == 0) {
+      wsum[0][wave] = kmin;
+      wsum[1][wave] = kmax;
+    }
+    __syncthreads();
+    kmin = wsum[0][0];
+    kmax = wsum[1][0];
+    for (int w = 1; w < NW; ++w) {
+      kmin = min(kmin, wsum[0][w]);
+      kmax = max(kmax, wsum[1][w]);
+    }
+    lo = kmin;
+    span = kmax - kmin;
+    uint32_t mb = vb;  // items still in [lo, lo + span]
+    for (int pass = 0; !all_in && span != 0u; ++pass) {
+      uint32_t* h = hist[pass & 1];
+      const int shift = max(0, (32 - __clz((int)span)) - 11);
+      // (wsum and the other buffer: their last readers passed the barrier
+      // that ended the previous pass)
+      __syncthreads();
+      if (pass == 0) {
+#pragma unroll
+        for (int u = 0; u < LS_KPT; ++u)
+          if ((vb >> u) & 1u) atomicAdd(&h[(kr[u] - lo) >> shift], 1u);
+      } else {
+        for (uint32_t bits = mb; bits; bits &= bits - 1u) {
+          const int u = __builtin_ctz(bits);
+          atomicAdd(&h[(keys_s[ls_phys(32 * tid + u)] - lo) >> shift], 1u);
+        }
+      }
+      __syncthreads();
+      // thread t owns the BPT bins below 2048 - BPT t (top bins first);
+      // clear the other buffer for the next pass
+      uint32_t cb[BPT], csum = 0u;
+#pragma unroll
+      for (int i = 0; i < BPT; i += 2) {
+        const u32x2 v = *(const u32x2*)&h[LS_BINS - BPT * (tid + 1) + i];
+        cb[i] = v[0];
+        cb[i + 1] = v[1];
+        csum += v[0] + v[1];
+        *(u32x2*)&hist[(pass + 1) & 1][BPT * tid + i] = u32x2{0u, 0u};
+      }
+      const uint32_t incl = wave_incl_scan(csum);
+      if (lane == 63) wsum[0][wave] = incl;
+      __syncthreads();
+      uint32_t above_w = 0u;
+      for (int w = 0; w < wave; ++w) above_w += wsum[0][w];
+      const uint32_t above = above_w + incl - csum;
+      if (above < remaining && above + csum >= remaining) {
+        // cb[BPT - 1] is this thread's top bin
+        uint32_t acc = above;
+        for (int i = BPT - 1; i >= 0; --i) {
+          if (acc + cb[i] >= remaining) {
+            res[0] = (uint32_t)(LS_BINS - BPT * (tid + 1) + i);
+            res[1] = acc;
+            res[2] = cb[i];
+            break;
+          }
+          acc += cb[i];
+        }
+      }
+      __syncthreads();
+      const uint32_t d = res[0], cum = res[1], cnt = res[2];
+      remaining -= cum;
+      const uint32_t d_lo = d << shift;
+      lo += d_lo;
+      span = min(span - d_lo, (1u << shift) - 1u);
+      if (cnt == remaining) all_in = true;
+      // keep the items of the bin
+      if (pass == 0) {
+        uint32_t nm = 0u;
+#pragma unroll
+        for (int u = 0; u < LS_KPT; ++u)
+          nm |= (((vb >> u) & 1u) && ((kr[u] - (lo - d_lo)) >> shift) == d) ? 1u << u : 0u;
+        mb = nm;
+      } else {
+        for (uint32_t bits = mb; bits; bits &= bits - 1u) {
+          const int u = __builtin_ctz(bits);
+          if (keys_s[ls_phys(32 * tid + u)] - lo > span) mb &= ~(1u << u);
+        }
+      }
+    }
+  }
+
+  // this thread's keys above and inside the range; one packed scan gives
+  // the counts before it (ties are taken in index order, so the taken ones
+  // before a thread number min(remaining, ties before it))
+  uint32_t gtb = 0u, inb = 0u;
+  const uint32_t hi_key = lo + span;
+#pragma unroll
+  for (int u = 0; u < LS_KPT; ++u) {
+    const bool ok = (vb >> u) & 1u;
+    gtb |= (ok && kr[u] > hi_key) ? 1u << u : 0u;
+    inb |= (ok && kr[u] >= lo && kr[u] <= hi_key) ? 1u << u : 0u;
+  }
+  const uint32_t packed = ((uint32_t)__popc(gtb) << 16) | (uint32_t)__popc(inb);
+  const uint32_t incl = wave_incl_scan(packed);
+  __syncthreads();  // the last pass's readers of wsum are done
+  if (lane == 63) wsum[1][wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - packed;
+  for (int w = 0; w < wave; ++w) before += wsum[1][w];
+  const uint32_t gt_before = before >> 16, in_before = before & 0xffffu;
+  // one branch-free form for both cases: with all_in every key in range is
+  // taken (an unbounded limit), else the first `remaining` of them
+  const uint32_t lim = all_in ? 0xffffffffu : remaining;
+  // (the headroom as max - in_before: a guarded lim - in_before has let the
+  // optimizer assume lim >= in_before and drop the min below)
+  uint32_t take = min((uint32_t)__popc(inb), max(lim, in_before) - in_before);
+  uint32_t selb = gtb;
+  for (uint32_t bits = inb; take; --take) {
+    const uint32_t low = bits & (0u - bits);
+    selb |= low;
+    bits ^= low;
+  }
+  uint32_t at = gt_before + min(in_before, lim);
+  for (uint32_t bits = selb; bits; bits &= bits - 1u, ++at) {
+    // (the selection holds exactly nsel items; the bound is a guard)
+    if (at >= (uint32_t)nsel) break;
+    const int q = 32 * tid + __builtin_ctz(bits);
+    const int j = FROM_SCORES ? seg0 + q : in_idx[in_base + q];
+    if (last) {
+      orow[at] = j;
+      if (sorow && (uint32_t)j < (uint32_t)Nc_cap) sorow[at] = srow[j];
+    } else {
+      out_key[out_base + at] = keys_s[ls_phys(q)];
+      out_idx[out_base + at] = j;
+    }
+  }
+}
+
 }  // namespace csa
 
 namespace csa_host {
@@ -1019,20 +1322,28 @@ struct IdxLayout {
   bool long_rows, bm_lds;
   int n_chunks, bm_words;
   size_t scores, hist, chunk_cnt, def_bm, cand_idx, cand_key, cand_flat, total;
+  // segment path: segments of LS_SEG entries, candidate slot stride
+  // 2^p_log2, two candidate buffers (keys, entries, counts)
+  int n_seg, p_log2;
+  size_t seg_cand[2];
 };
 
+// The two long-row paths use the space after the scores in turn: its size
+// is the larger of theirs.
 static IdxLayout idx_layout(int B, int T, int Nc_cap, int topk) {
-  (void)topk;
   IdxLayout L{};
   const size_t rows = (size_t)B * T;
   L.long_rows = Nc_cap > kShortMax;
   L.bm_lds = Nc_cap <= kBitmapLds * 32;
   L.n_chunks = (Nc_cap + kChunk - 1) / kChunk;
   L.bm_words = 2 * ((Nc_cap + 63) / 64);  // even: collect stores word pairs
+  L.n_seg = (Nc_cap + LS_SEG - 1) / LS_SEG;
+  while ((1 << L.p_log2) < topk) ++L.p_log2;
   size_t off = 0;
   L.scores = off;
   off += align256(rows * (size_t)Nc_cap * 4);
   if (L.long_rows) {
+    const size_t base = off;
     L.hist = off;  // the only part that must start at zero
     off += align256(rows * kHistBins * 4);
     L.chunk_cnt = off;
@@ -1045,6 +1356,13 @@ static IdxLayout idx_layout(int B, int T, int Nc_cap, int topk) {
     off += align256(rows * (size_t)Nc_cap * 4);
     L.cand_flat = off;
     off += align256(rows * (size_t)Nc_cap * 8);
+    size_t off2 = base;
+    const size_t slots = rows * (size_t)L.n_seg << L.p_log2;
+    for (int k = 0; k < 2; ++k) {
+      L.seg_cand[k] = off2;
+      off2 += align256(slots * 8 + rows * (size_t)L.n_seg * 4);
+    }
+    off = std::max(off, off2);
   }
   L.total = off;
   return L;
@@ -1063,8 +1381,12 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   const IdxLayout L = idx_layout(1, rows, a.Nc_cap, a.topk);
   char* ws = (char*)a.ws;
   float* scores = (float*)(ws + L.scores);
-  uint32_t* hist = L.long_rows ? (uint32_t*)(ws + L.hist) : nullptr;
-  if (L.long_rows) {
+  // long rows: the histogram path when each score workgroup owns one query
+  // row of one sequence, else the segment path
+  const bool seg_path = L.long_rows && (a.vl.cu_q || (a.dt == CSA_DT_BF16 && a.T != 1));
+  const bool hist_path = L.long_rows && !seg_path;
+  uint32_t* hist = hist_path ? (uint32_t*)(ws + L.hist) : nullptr;
+  if (hist_path) {
     size_t n = (size_t)rows * kHistBins;
     zero_u32_kernel<<<(unsigned)std::min<size_t>((n + 255) / 256, 1024), 256, 0, st>>>(hist, n);
   }
@@ -1072,7 +1394,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     // no entry exists: every output row is padding
   } else if (a.dt == CSA_DT_F32) {
     dim3 g((a.Nc_cap + 255) / 256, rows);
-    if (L.long_rows)
+    if (hist_path)
       score_f32_kernel<true><<<g, 256, 0, st>>>((const float*)a.q_idx, a.w_idx,
                                                 (const float*)a.k_idx, a.q_pos, a.n_cmp, a.T,
                                                 a.H_I, a.d_I, a.Nc_cap, a.m, scores, hist, a.vl);
@@ -1084,7 +1406,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     // long rows need one histogram per row: one row per workgroup then;
     // short rows split their entries in chunks of 512 so that the causal
     // growth of the visible range spreads over more, smaller workgroups
-    const int key_chunk = L.long_rows ? kChunk : std::min(a.Nc_cap, 512);
+    const int key_chunk = hist_path ? kChunk : std::min(a.Nc_cap, 512);
     dim3 g((a.T + SB_ROWS - 1) / SB_ROWS, (a.Nc_cap + key_chunk - 1) / key_chunk, a.B);
 #define CSA_LAUNCH_SB(HS)                                                                     \
   if (a.pages.block_table)                                                                    \
@@ -1095,10 +1417,8 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     score_bf16_kernel<HS, false><<<g, 256, 0, st>>>(                                          \
         (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, a.q_pos, a.n_cmp, a.T,   \
         a.Nc_cap, a.m, key_chunk, scores, hist, a.pages, a.vl)
-    if (L.long_rows) {
-      // rows of a workgroup must share a histogram: only T == 1 qualifies
-      if (a.T != 1) return hipErrorNotSupported;
-      CSA_LAUNCH_SB(true);
+    if (hist_path) {
+      CSA_LAUNCH_SB(true);  // (T == 1: the workgroup's rows share the histogram)
     } else {
       CSA_LAUNCH_SB(false);
     }
@@ -1115,13 +1435,13 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
         (const uint8_t*)a.q_idx, a.q_scale, a.w_idx, (const uint8_t*)a.k_idx, a.k_scale,      \
         a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m, scores, hist, a.pages)
     if (a.dt == CSA_DT_MXFP4) {
-      if (L.long_rows) {
+      if (hist_path) {
         CSA_LAUNCH_SF(true, CSA_DT_MXFP4);
       } else {
         CSA_LAUNCH_SF(false, CSA_DT_MXFP4);
       }
     } else {
-      if (L.long_rows) {
+      if (hist_path) {
         CSA_LAUNCH_SF(true, CSA_DT_FP8E4M3);
       } else {
         CSA_LAUNCH_SF(false, CSA_DT_FP8E4M3);
@@ -1138,6 +1458,43 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
       select_short_kernel<kShortMax><<<g, 256, 0, st>>>(scores, a.q_pos, a.n_cmp, rows, a.T,
                                                         a.Nc_cap, a.m, a.topk, a.idx_out,
                                                         a.score_out, a.vl);
+  } else if (seg_path) {
+    // level 0 over segments of LS_SEG entries, then merge levels until one
+    // workgroup per row remains
+    const size_t slots = (size_t)rows * L.n_seg << L.p_log2;
+    uint32_t* ck[2];
+    int32_t *ci[2], *cc[2];
+    for (int k = 0; k < 2; ++k) {
+      ck[k] = (uint32_t*)(ws + L.seg_cand[k]);
+      ci[k] = (int32_t*)(ck[k] + slots);
+      cc[k] = ci[k] + slots;
+    }
+    select_seg_kernel<256, true><<<dim3(rows, L.n_seg), 256, 0, st>>>(
+        scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m, a.topk, L.p_log2, 1, 1, nullptr, nullptr,
+        nullptr, ck[0], ci[0], cc[0], a.idx_out, a.score_out, a.vl);
+    // each merge level: one workgroup per row when the candidates fit 32768
+    // slots (with the thread count they need), else groups of at least four
+    // segments
+    int n_in = L.n_seg, cur = 0;
+    while (n_in > 1) {
+      const long slots_in = (long)n_in << L.p_log2;
+      const int nt = slots_in <= 8192    ? 256
+                     : slots_in <= 16384 ? 512
+                     : slots_in <= 32768 ? 1024
+                                         : std::max(256, (4 << L.p_log2) / LS_KPT);
+      const int group = std::min(LS_GROUP_MAX, (nt * LS_KPT) >> L.p_log2);
+      const int n_out = (n_in + group - 1) / group;
+#define CSA_LAUNCH_MERGE(NT_)                                                                 \
+  select_seg_kernel<NT_, false><<<dim3(rows, n_out), NT_, 0, st>>>(                          \
+      scores, a.q_pos, a.n_cmp, a.T, a.Nc_cap, a.m, a.topk, L.p_log2, n_in, group, ck[cur],  \
+      ci[cur], cc[cur], ck[cur ^ 1], ci[cur ^ 1], cc[cur ^ 1], a.idx_out, a.score_out, a.vl)
+      if (nt == 256) CSA_LAUNCH_MERGE(256);
+      else if (nt == 512) CSA_LAUNCH_MERGE(512);
+      else CSA_LAUNCH_MERGE(1024);
+#undef CSA_LAUNCH_MERGE
+      n_in = n_out;
+      cur ^= 1;
+    }
   } else {
     uint32_t* cnt = (uint32_t*)(ws + L.chunk_cnt);
     uint32_t* bm = (uint32_t*)(ws + L.def_bm);

@@ -190,7 +190,9 @@ csa_status_t csa_compress_ex(int B, int L, int d_model, int E, int m, int overla
  *            (NaN in padded slots)
  *  workspace at least csa_indexer_topk_workspace_size() bytes
  * Supported: (H_I, d_I) in {(4, 32), (16, 64)} for F32; (16, 64) for BF16,
- * FP8E4M3 and MXFP4; topk <= 8192.  fp8 scales must be positive.
+ * FP8E4M3 and MXFP4; topk <= 8192; Nc_cap <= 2^21.  fp8 scales must be
+ * positive.  The workspace holds scores and selection candidates only; its
+ * contents on entry do not matter.
  */
 csa_status_t csa_indexer_topk(int B, int T, int H_I, int d_I, int Nc_cap, int m, int topk,
                               const int64_t* q_pos, const int32_t* n_cmp, const void* q_idx,
@@ -407,7 +409,7 @@ size_t csa_compress_varlen_workspace_size(int total, int d_model, int E, int m, 
 /* csa_indexer_topk over packed sequences: q_idx [total, H_I, d_I], w_idx
  * [total, H_I], k_idx [cmp_cu_seqlens[n], d_I]; idx_out [total, topk] holds
  * indices local to the row's sequence (entry i of sequence b is i).
- * Supported: F32 and BF16 as for csa_indexer_topk, max_cmp <= 8192.
+ * Supported: F32 and BF16 as for csa_indexer_topk, max_cmp <= 2^21.
  * Workspace: csa_indexer_topk_varlen_workspace_size(). */
 csa_status_t csa_indexer_topk_varlen(int n, int total, int max_len, int H_I, int d_I,
                                      int max_cmp, int m, int topk, const int32_t* cu_seqlens,

@@ -44,7 +44,8 @@ def test_status_strings(L):
 
 
 def test_workspace_sizes(L):
-    # long decode rows need the score row plus chunk lists; short rows only scores
+    # long rows need the score row plus chunk lists (or segment candidates);
+    # short rows only scores
     a = L.csa_indexer_topk_workspace_size(8, 1, 16, 64, 262144, 2048, 2)
     assert a >= 8 * 262144 * 4 * 3
     assert L.csa_indexer_topk_workspace_size(1, 8192, 16, 64, 2048, 512, 1) == 8192 * 2048 * 4

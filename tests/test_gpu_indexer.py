@@ -274,6 +274,34 @@ def test_indexer_fp8_long_rows_degenerate(kind):
         assert (g_idx[0, 0] == np.arange(topk)).all()
 
 
+@pytest.mark.parametrize("kind", ["all_equal", "two_values", "one_high"])
+def test_indexer_bf16_segment_path_degenerate(kind):
+    # the same degenerate rows through the segment path (bf16 keys, two query
+    # positions): one repeated key, two alternating keys, one key above a
+    # repeated one; ties resolve to the lowest indices across segments
+    d = gen.Draw(32, "cpu")
+    B, T, Nc, m, topk = 1, 2, 24000, 4, 2048
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    if kind == "all_equal":
+        k_idx[0] = k_idx[0, 9].clone()
+    elif kind == "two_values":
+        k_idx[0, 0::2] = k_idx[0, 5].clone()
+        k_idx[0, 1::2] = k_idx[0, 8].clone()
+    else:
+        k_idx[0] = k_idx[0, 9].clone()
+        k_idx[0, 12345] = k_idx[0, 12345] * 4.0
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    w_idx = w_idx.abs()  # positive weights: the scaled key scores higher
+    q_pos, n_cmp = [4 * Nc], [Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    for t in range(T):
+        assert sorted(g_idx[0, t].tolist()) == sorted(o[0][0, t].tolist()), (kind, t)
+        assert (np.diff(g_idx[0, t]) > 0).all()
+    if kind == "all_equal":
+        assert (g_idx[0, :] == np.arange(topk)).all()
+
+
 def test_indexer_edge_rows():
     d = gen.Draw(25)
     B, T, Nc, m, topk = 2, 9, 40, 4, 16
@@ -335,3 +363,43 @@ def test_indexer_fp8_rows_beyond_lds_bitmap():
     g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
     o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
     _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "fp8 bitmap in workspace")
+
+
+def test_indexer_bf16_long_rows_many_query_rows():
+    # prefill-shaped rows (T > 1) that see more than 8192 entries: the
+    # segment select over rows of one 16-row score group
+    d = gen.Draw(41)
+    B, T, Nc, m, topk = 2, 40, 9000, 4, 512
+    q_idx, _, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    k_idx, _ = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+    q_pos, n_cmp = [4 * 8990, 4 * 8100], [Nc, 8500]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "bf16 long prefill rows")
+
+
+@pytest.mark.parametrize("path", ["histogram", "segments"])
+@pytest.mark.parametrize("Nc,topk", [(163841, 8192), (100000, 7), (65537, 2048), (600000, 16),
+                                     (2097152, 16)])
+def test_indexer_long_rows_merge_levels(Nc, topk, path):
+    # the two long-row paths at row lengths with many selection segments:
+    # e4m3 decode rows take the histogram path; bf16 rows of two query
+    # positions take the segment path, where 163841 entries with topk 8192
+    # need three merge levels (21 -> 6 -> 2 -> 1) and end in a one-entry
+    # segment, as does 65537 (9 segments, two levels); 100000 with topk 7 one
+    # level; 600000 and the largest row (2^21 entries, 256 segments) with
+    # topk 16 two levels of 64-segment groups
+    d = gen.Draw(43 + topk % 5, "cpu")
+    B, m = 2, 4
+    if path == "histogram":
+        T = 1
+        k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.FP8)
+        q_idx, q_scale, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.FP8)
+    else:
+        T = 2
+        k_idx, k_scale = gen.indexer_keys(d, B, Nc, 64, gen.BF16)
+        q_idx, q_scale, w_idx = gen.indexer_query(d, B, T, 16, 64, gen.BF16)
+    q_pos, n_cmp = [4 * Nc + 3, 4 * 40000], [Nc, Nc]
+    g_idx, g_sc = _gpu(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    o = _oracle_rows(q_idx, w_idx, k_idx, m, topk, q_pos, n_cmp, q_scale, k_scale)
+    _compare(g_idx, g_sc, o[3], m, topk, q_pos, n_cmp, Nc, "%s merge %d/%d" % (path, Nc, topk))

@@ -98,3 +98,40 @@ def test_packed_prefill_matches_each_sequence_alone(lens, dt):
             assert_bf16_close(g_out[t0:t1], r[0], "attention " + what)
         fin = np.isfinite(rl[0])
         np.testing.assert_allclose(g_lse[t0:t1][fin], rl[0][fin], rtol=1e-4, atol=1e-4)
+
+
+def test_packed_indexer_long_sequence():
+    # a packed sequence of more than 8192 entries beside short ones: every
+    # row goes through the segment select with the packed offsets; sampled
+    # rows of the long sequence and every row of the short ones against the
+    # oracle on the sequence alone
+    d = gen.Draw(120)
+    m, topk = 4, 300
+    lens = [33000, 50, 700]
+    cu, ccu = _offsets(lens, m)
+    total, max_len, max_cmp = sum(lens), max(lens), max(lens) // m
+    n_ent = int(ccu[-1])
+    q_idx = gen.store(d.normal(total, 16, 64), gen.BF16)
+    w_idx = d.normal(total, 16)
+    k_idx = gen.store(d.normal(n_ent, 64), gen.BF16)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    ccu_d = torch.from_numpy(ccu).to(DEV)
+    idx, _ = csa.csa_indexer_topk_varlen(q_idx.to(DEV), w_idx.to(DEV), k_idx.to(DEV), cu_d, ccu_d,
+                                         max_len, max_cmp, m, topk)
+    torch.cuda.synchronize()
+    g_idx = idx.cpu().numpy()
+    hb = lambda t: gen.host_bits(t)
+    blocks = {0: [0, 4090, 32760, 32992], 1: [0, 8, 16, 24, 32, 40, 48], 2: list(range(0, 700, 8))}
+    for b, starts in blocks.items():
+        t0s, e0, e1 = cu[b], ccu[b], ccu[b + 1]
+        L, Nc = cu[b + 1] - t0s, e1 - e0
+        kb = hb(k_idx[e0:e1])[None]
+        for s in starts:
+            s1 = min(s + 8, L)
+            rows = slice(t0s + s, t0s + s1)
+            _, _, _, alls = orc.indexer_topk(hb(q_idx[None, rows]), w_idx[None, rows].numpy(), kb,
+                                             m, topk, s, Nc, want_all=True)
+            for t in range(s, s1):
+                nv = min(Nc, (t + 1) // m)
+                check_topk_row(g_idx[t0s + t], alls[0, t - s], topk, nv,
+                               "seq %d row %d" % (b, t))
