@@ -35,31 +35,16 @@ constexpr int PJ_BM = 128, PJ_BN = 128, PJ_BK = 64;
 constexpr int PJ_LDS_STRIDE = PJ_BK + 8;
 constexpr int PJ_TILE = PJ_BM * PJ_LDS_STRIDE;  // bf16 per operand tile
 
-__global__ void __launch_bounds__(512) proj_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
-    const uint16_t* __restrict__ w_gate, float* __restrict__ pg, int M, int E, int K,
-    int k_per_split) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][PJ_TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][PJ_TILE];
-  const int N = 2 * E;
+// The k loop of one 128 x 128 tile: arow[u] / brow[u] point at the k0 = 0
+// element of the A row / B row that thread chunk u (of two) stages; acc gets
+// the wave's 64 x 32 block (wave w: rows 64 (w / 4), columns 32 (w % 4)).
+__device__ __forceinline__ void pj_mainloop(uint16_t* As, uint16_t* Bs,
+                                            const uint16_t* const (&arow)[2],
+                                            const uint16_t* const (&brow)[2], int nk,
+                                            f32x16 (&acc)[2]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m0 = blockIdx.x * PJ_BM, n0 = blockIdx.y * PJ_BN;
-  const int split = blockIdx.z;
-  const int kb = split * k_per_split, ke = min(K, kb + k_per_split);
-  const int nk = (ke - kb) / PJ_BK;
   const int wm = (wave >> 2) * 64, wn = (wave & 3) * 32;
-
-  // global -> LDS: a tile row is 64 bf16 = 8 chunks of 16 B; 128 rows x 8 =
-  // 1024 chunks per operand, 2 per thread (rows r = c / 8, chunk q = c % 8)
-  const uint16_t* arow[2];
-  const uint16_t* brow[2];
-  for (int u = 0; u < 2; ++u) {
-    const int c = u * 512 + tid, r = c >> 3, q = c & 7;
-    const int gm = m0 + r < M ? m0 + r : 0, gn = n0 + r < N ? n0 + r : 0;
-    arow[u] = x + (size_t)gm * K + kb + q * 8;
-    brow[u] = (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(gn - E) * K) + kb + q * 8;
-  }
   u32x4 ra[2][2], rb[2][2];
   auto load = [&](int kt, u32x4(&a)[2], u32x4(&bq)[2]) {
     const int k0 = min(kt, nk - 1) * PJ_BK;
@@ -73,25 +58,23 @@ __global__ void __launch_bounds__(512) proj_bf16_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int c = u * 512 + tid, r = c >> 3, q = c & 7;
-      *(u32x4*)(&As[buf][r * PJ_LDS_STRIDE + q * 8]) = a[u];
-      *(u32x4*)(&Bs[buf][r * PJ_LDS_STRIDE + q * 8]) = bq[u];
+      *(u32x4*)(&As[buf * PJ_TILE + r * PJ_LDS_STRIDE + q * 8]) = a[u];
+      *(u32x4*)(&Bs[buf * PJ_TILE + r * PJ_LDS_STRIDE + q * 8]) = bq[u];
     }
   };
-
-  f32x16 acc[2];
   for (int i = 0; i < 2; ++i)
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-
   auto compute = [&](int buf) {
     // four k steps of 16; lane holds 8 consecutive k of one row (A) / column (B)
 #pragma unroll
     for (int ks = 0; ks < PJ_BK / 16; ++ks) {
       bf16x8 a[2];
       for (int i = 0; i < 2; ++i)
-        a[i] = *(const bf16x8*)(&As[buf][(wm + i * 32 + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 +
-                                         (lane >> 5) * 8]);
-      const bf16x8 b =
-          *(const bf16x8*)(&Bs[buf][(wn + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 + (lane >> 5) * 8]);
+        a[i] = *(const bf16x8*)(&As[buf * PJ_TILE +
+                                    (wm + i * 32 + (lane & 31)) * PJ_LDS_STRIDE + ks * 16 +
+                                    (lane >> 5) * 8]);
+      const bf16x8 b = *(const bf16x8*)(&Bs[buf * PJ_TILE + (wn + (lane & 31)) * PJ_LDS_STRIDE +
+                                            ks * 16 + (lane >> 5) * 8]);
       for (int i = 0; i < 2; ++i)
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i], 0, 0, 0);
     }
@@ -123,6 +106,35 @@ __global__ void __launch_bounds__(512) proj_bf16_kernel(
       __syncthreads();
     }
   }
+}
+
+__global__ void __launch_bounds__(512) proj_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
+    const uint16_t* __restrict__ w_gate, float* __restrict__ pg, int M, int E, int K,
+    int k_per_split) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * PJ_TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * PJ_TILE];
+  const int N = 2 * E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = blockIdx.x * PJ_BM, n0 = blockIdx.y * PJ_BN;
+  const int split = blockIdx.z;
+  const int kb = split * k_per_split, ke = min(K, kb + k_per_split);
+  const int nk = (ke - kb) / PJ_BK;
+  const int wm = (wave >> 2) * 64, wn = (wave & 3) * 32;
+
+  // global -> LDS: a tile row is 64 bf16 = 8 chunks of 16 B; 128 rows x 8 =
+  // 1024 chunks per operand, 2 per thread (rows r = c / 8, chunk q = c % 8)
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  for (int u = 0; u < 2; ++u) {
+    const int c = u * 512 + tid, r = c >> 3, q = c & 7;
+    const int gm = m0 + r < M ? m0 + r : 0, gn = n0 + r < N ? n0 + r : 0;
+    arow[u] = x + (size_t)gm * K + kb + q * 8;
+    brow[u] = (gn < E ? w_kv + (size_t)gn * K : w_gate + (size_t)(gn - E) * K) + kb + q * 8;
+  }
+  f32x16 acc[2];
+  pj_mainloop(As, Bs, arow, brow, nk, acc);
   // accumulator layout (32x32): lane holds column (lane & 31), rows
   // 8 (r / 4) + 4 (lane / 32) + (r % 4)
   float* out = pg + (size_t)split * M * N;
@@ -133,6 +145,202 @@ __global__ void __launch_bounds__(512) proj_bf16_kernel(
         const int row = m0 + wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row < M) out[(size_t)row * N + col] = acc[i][r];
       }
+}
+
+// ------------------------------------------- fused projection + pool (bf16)
+// The compressor of a prefill chunk (bf16 input, m = 4 with overlap, so that
+// an entry pools the 8 tokens of blocks i - 1 and i; fp32 or bf16 output; no
+// step that mixes channels) with the overlapping windows pooled out of LDS.
+// Workgroup (t, c, b): the 32 blocks i0 + 32 t .. i0 + 32 t + 31 of sequence
+// b (128 token positions from 4 (i0 + 32 t), i0 the call's first entry), and
+// channels [64 c, 64 c + 64) of P and the same of G as the tile's 128
+// columns; tiles of whole blocks, so that an 8K chunk with 256 channels is
+// 64 x 4 workgroups, one per compute unit.  After the k loop the fp32 P and
+// G tiles go to LDS (over the operand buffers) and each thread pools entries
+// of one channel: the tile's entries i0 + 32 t + k, k = 1 .. 31, have both
+// of their blocks in it.  The first block of every tile and the last block
+// of every tile go to the workspace, and the seam kernel pools the entries
+// i0 + 32 t from them (t = 0: the previous block from the carried state).
+// Tokens before the call come from the carried state (absent without it);
+// tile positions among the call's last 7 tokens go to the next call's state.
+// GEMM rows for positions outside the call read row 0 of the sequence and
+// are not used.
+constexpr int FU_BLK = 32, FU_CH = 64, FU_PS = FU_CH + 8;  // fp32 LDS row stride
+
+// One token of the workspace's seam buffer: [B][n_tiles][2 (first, last
+// block)][4 tokens][2 (P, G)][E] fp32.
+__device__ __forceinline__ size_t fu_seam_at(int b, int n_tiles, int t, int which, int u, int pg,
+                                            int E, int e) {
+  return ((((((size_t)b * n_tiles + t) * 2 + which) * 4 + u) * 2 + pg) * E) + e;
+}
+
+// P and G of one window token (absent: G = -inf; P = 0 wherever G = -inf)
+struct FuTok {
+  float p, g;
+};
+
+template <int OUT_DT>
+__device__ __forceinline__ void fu_store(void* out, int64_t orow, int E, int e, float v) {
+  if (OUT_DT == CSA_DT_F32) ((float*)out)[(size_t)orow * E + e] = v;
+  else ((uint16_t*)out)[(size_t)orow * E + e] = f32_to_bf16(v);
+}
+
+// the gated pool of one 8-token window (the same arithmetic as pool_kernel)
+__device__ __forceinline__ float fu_pool(const FuTok (&tk)[8], const float (&av)[8]) {
+  float gv[8], cm = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    gv[u] = tk[u].g == -INFINITY ? -INFINITY : tk[u].g + av[u];
+    cm = fmaxf(cm, gv[u]);
+  }
+  float den = 0.0f, num = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float w = __expf(gv[u] - cm);
+    den += w;
+    num = fmaf(w, tk[u].g == -INFINITY ? 0.0f : tk[u].p, num);
+  }
+  return num / den;
+}
+
+template <int OUT_DT>
+__global__ void __launch_bounds__(512) compress_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_kv,
+    const uint16_t* __restrict__ w_gate, const int64_t* __restrict__ pos0, int L, int E, int K,
+    const float* __restrict__ ape, const float* __restrict__ state_in,
+    float* __restrict__ state_out, void* __restrict__ out, int Nc_cap, PageTable pt,
+    float* __restrict__ seam, int n_tiles) {
+  constexpr int m = 4, NS = 7;  // window 2m, carried tokens 2m - 1
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * PJ_TILE];  // 73728 B
+  uint16_t* const As = smem;
+  uint16_t* const Bs = smem + 2 * PJ_TILE;
+  float* const Pl = (float*)smem;       // [128][FU_PS]
+  float* const Gl = Pl + PJ_BM * FU_PS;  // [128][FU_PS]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = blockIdx.x, c0 = blockIdx.y * FU_CH, b = blockIdx.z;
+  const int64_t p0 = pos0[b];
+  const int64_t i0 = p0 / m;  // first entry whose last token is >= p0
+  const int64_t tp0 = (int64_t)m * (i0 + (int64_t)FU_BLK * t);  // position of tile row 0
+  if (tp0 >= p0 + L) return;  // uniform: nothing of this call in the tile
+  const uint16_t* xb = x + (size_t)b * L * K;
+
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  for (int u = 0; u < 2; ++u) {
+    const int c = u * 512 + tid, r = c >> 3, q = c & 7;
+    const int64_t rr = tp0 + r - p0;  // row of the call
+    arow[u] = xb + (size_t)(rr >= 0 && rr < L ? rr : 0) * K + q * 8;
+    brow[u] = (r < FU_CH ? w_kv + (size_t)(c0 + r) * K : w_gate + (size_t)(c0 + r - FU_CH) * K) +
+              q * 8;
+  }
+  f32x16 acc[2];
+  pj_mainloop(As, Bs, arow, brow, K / PJ_BK, acc);
+  // (the main loop ends with a barrier: the operand buffers are free)
+  {
+    const int wm = (wave >> 2) * 64, wn = (wave & 3) * 32;
+    const int col = wn + (lane & 31);
+    float* const dst = col < FU_CH ? Pl + col : Gl + (col - FU_CH);
+    for (int i = 0; i < 2; ++i)
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        dst[row * FU_PS] = acc[i][r];
+      }
+  }
+  __syncthreads();
+  const int ch = lane, e = c0 + ch;
+  auto token = [&](int r) -> FuTok {
+    const int64_t pos = tp0 + r;
+    FuTok tk{0.0f, -INFINITY};
+    if (pos >= p0) {
+      tk.p = Pl[r * FU_PS + ch];
+      tk.g = Gl[r * FU_PS + ch];
+    } else if (state_in && pos >= 0 && pos >= p0 - NS) {
+      const float* sr = state_in + (((size_t)b * NS + (size_t)(pos - (p0 - NS))) * 2) * E;
+      tk.p = sr[e];
+      tk.g = sr[E + e];
+    }
+    if (tk.g == -INFINITY) tk.p = 0.0f;
+    return tk;
+  };
+  float av[2 * m];
+#pragma unroll
+  for (int u = 0; u < 2 * m; ++u) av[u] = ape ? ape[(size_t)u * E + e] : 0.0f;
+  // entries i0 + 32 t + k, k = 1 .. 31: blocks k - 1 and k of the tile
+  for (int k = 1 + wave; k < FU_BLK; k += 8) {
+    const int64_t i = i0 + (int64_t)FU_BLK * t + k;
+    if (i >= Nc_cap || (int64_t)m * (i + 1) - 1 >= p0 + L) continue;  // uniform per wave
+    const int64_t orow = pt.block_table ? paged_row(pt, b, (int)i) : (int64_t)b * Nc_cap + i;
+    if (orow < 0) continue;  // an absent page: not stored
+    FuTok tk[2 * m];
+#pragma unroll
+    for (int u = 0; u < 2 * m; ++u) tk[u] = token(m * (k - 1) + u);
+    fu_store<OUT_DT>(out, orow, E, e, fu_pool(tk, av));
+  }
+  // the tile's first and last blocks for the seam kernel (waves 0 and 1)
+  if (wave < 2) {
+    const int r0 = wave == 0 ? 0 : PJ_BM - m;
+#pragma unroll
+    for (int u = 0; u < m; ++u) {
+      const FuTok tk = token(r0 + u);
+      seam[fu_seam_at(b, n_tiles, t, wave, u, 0, E, e)] = tk.p;
+      seam[fu_seam_at(b, n_tiles, t, wave, u, 1, E, e)] = tk.g;
+    }
+  }
+  // the next call's state: positions p0 + L - 7 .. p0 + L - 1 in this tile
+  // (L >= 7: all of them are rows of this call)
+  if (state_out) {  // (uniform)
+    for (int s = wave; s < NS; s += 8) {
+      const int64_t r = p0 + L - NS + s - tp0;
+      if (r < 0 || r >= PJ_BM) continue;
+      const FuTok tk = token((int)r);
+      state_out[(((size_t)b * NS + s) * 2 + 0) * E + e] = tk.p;
+      state_out[(((size_t)b * NS + s) * 2 + 1) * E + e] = tk.g;
+    }
+  }
+}
+
+// The entries i0 + 32 t whose windows straddle two tiles: the last block of
+// tile t - 1 (for t = 0, the block before the call, from the carried state)
+// and the first block of tile t.  Grid (tiles, E / 64, B), 64 threads: one
+// channel each.  Reads state_in, never state_out, so that the two may not
+// alias as in every compressor call.
+template <int OUT_DT>
+__global__ void __launch_bounds__(64) compress_seam_kernel(
+    const int64_t* __restrict__ pos0, int L, int E, const float* __restrict__ ape,
+    const float* __restrict__ state_in, void* __restrict__ out, int Nc_cap, PageTable pt,
+    const float* __restrict__ seam, int n_tiles) {
+  constexpr int m = 4, NS = 7;
+  const int t = blockIdx.x, e = blockIdx.y * FU_CH + threadIdx.x, b = blockIdx.z;
+  const int64_t p0 = pos0[b];
+  const int64_t i0 = p0 / m;
+  const int64_t i = i0 + (int64_t)FU_BLK * t;
+  if (i >= Nc_cap || (int64_t)m * (i + 1) - 1 >= p0 + L) return;
+  const int64_t orow = pt.block_table ? paged_row(pt, b, (int)i) : (int64_t)b * Nc_cap + i;
+  if (orow < 0) return;
+  FuTok tk[2 * m];
+#pragma unroll
+  for (int u = 0; u < m; ++u) {
+    if (t > 0) {
+      tk[u].p = seam[fu_seam_at(b, n_tiles, t - 1, 1, u, 0, E, e)];
+      tk[u].g = seam[fu_seam_at(b, n_tiles, t - 1, 1, u, 1, E, e)];
+    } else {
+      const int64_t pos = (int64_t)m * (i - 1) + u;  // before the call
+      tk[u] = FuTok{0.0f, -INFINITY};
+      if (state_in && pos >= 0 && pos >= p0 - NS) {
+        const float* sr = state_in + (((size_t)b * NS + (size_t)(pos - (p0 - NS))) * 2) * E;
+        tk[u].p = sr[e];
+        tk[u].g = sr[E + e];
+      }
+      if (tk[u].g == -INFINITY) tk[u].p = 0.0f;
+    }
+    tk[m + u].p = seam[fu_seam_at(b, n_tiles, t, 0, u, 0, E, e)];
+    tk[m + u].g = seam[fu_seam_at(b, n_tiles, t, 0, u, 1, E, e)];
+  }
+  float av[2 * m];
+#pragma unroll
+  for (int u = 0; u < 2 * m; ++u) av[u] = ape ? ape[(size_t)u * E + e] : 0.0f;
+  fu_store<OUT_DT>(out, orow, E, e, fu_pool(tk, av));
 }
 
 // ------------------------------------------------------- proj (bf16, few rows)
@@ -649,7 +857,43 @@ size_t compress_ws_bytes(int B, int L, int d_model, int E, int m, int overlap,
   return (size_t)s * M * 2 * E * sizeof(float);
 }
 
+// The fused kernel takes prefill chunks of bf16 tokens with m = 4 and
+// overlap, stored as fp32 or bf16 with no step that mixes channels, and at
+// least 128 channels: it cannot split K, so narrower entries (the indexer's
+// 64: one channel block, a quarter of the 8K chunk's workgroups) keep the
+// split-K projection and the pool.
+static bool use_fused(const CompressArgs& a) {
+  return a.in_dt == CSA_DT_BF16 && (a.out_dt == CSA_DT_F32 || a.out_dt == CSA_DT_BF16) &&
+         !a.rotate && !a.opt.norm_w && !a.opt.rope_dim && a.m == 4 && a.overlap == 1 &&
+         a.E % FU_CH == 0 && a.E >= 128 && !a.vl.cu_q && a.L >= PJ_BM &&
+         a.d_model % PJ_BK == 0;
+}
+
+// Tiles of 32 blocks from block floor(pos0 / 4), whose first position is at
+// most 3 before pos0: enough for any pos0 (the tiles past the call return at
+// once).  Their seam buffer (2 blocks of P and G per tile and channel) fits
+// the projection workspace the call is given.
+static int fused_tiles(int L) { return (L + 3 + 4 * FU_BLK - 1) / (4 * FU_BLK); }
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
+  if (use_fused(a)) {
+    const int n_tiles = fused_tiles(a.L);
+    dim3 grid(n_tiles, a.E / FU_CH, a.B);
+    float* seam = (float*)a.ws;
+#define CSA_LAUNCH_FUSED(DT)                                                                   \
+  compress_fused_kernel<DT><<<grid, 512, 0, st>>>(                                             \
+      (const uint16_t*)a.x, (const uint16_t*)a.w_kv, (const uint16_t*)a.w_gate, a.pos0, a.L,   \
+      a.E, a.d_model, a.ape, a.state_in, a.state_out, a.out, a.Nc_cap, a.pages, seam, n_tiles); \
+  compress_seam_kernel<DT><<<grid, FU_CH, 0, st>>>(a.pos0, a.L, a.E, a.ape, a.state_in, a.out, \
+                                                   a.Nc_cap, a.pages, seam, n_tiles)
+    if (a.out_dt == CSA_DT_F32) {
+      CSA_LAUNCH_FUSED(CSA_DT_F32);
+    } else {
+      CSA_LAUNCH_FUSED(CSA_DT_BF16);
+    }
+#undef CSA_LAUNCH_FUSED
+    return hipGetLastError();
+  }
   // rows of the projection: every token of the call (packed sequences:
   // a.total_rows, the sum of their lengths)
   const int M = a.vl.cu_q ? a.total_rows : a.B * a.L, K = a.d_model, E = a.E;

@@ -334,6 +334,48 @@ def test_compress_prefill_8k_sampled_entries():
     assert checked >= 128
 
 
+@pytest.mark.parametrize("E,out_kind", [(128, "f32"), (128, "bf16"), (256, "f32"), (64, "bf16")])
+def test_compress_fused_prefill_chunks_with_state(E, out_kind):
+    # chunks of at least 128 tokens with E >= 128 take the fused projection +
+    # pool (the windows pooled out of LDS, 31 entries per 128-token tile, 4
+    # halo tokens); the short chunk in between, and E = 64, take the
+    # two-kernel path; chunk
+    # starts off the block boundary (307, 507), two sequences, ape, and the
+    # carried state across the calls, against the oracle run in one shot
+    d = gen.Draw(140 + E)
+    B, dm, m, o = 2, 256, 4, 1
+    S = 700
+    x = gen.store(d.normal(B, S, dm), gen.BF16)
+    w_kv, w_gate = gen.compressor_weights(d, dm, E, gen.BF16)
+    ape = d.normal((1 + o) * m, E)
+    Nc = S // m + 1
+    ref, written, st_ref = _oracle(x, w_kv, w_gate, [0] * B, m, o, Nc, ape=ape)
+    xg, wk, wg, ag = x.to(DEV), w_kv.to(DEV), w_gate.to(DEV), ape.to(DEV)
+    ns = (1 + o) * m - 1
+    odt = torch.float32 if out_kind == "f32" else torch.bfloat16
+    out = torch.full((B, Nc, E), float("nan"), device=DEV).to(odt)
+    st = [torch.zeros(B, ns, 2, E, device=DEV), torch.zeros(B, ns, 2, E, device=DEV)]
+    st_in, p, k = None, 0, 0
+    for L in (301, 6, 200, 193):
+        csa.csa_compress(xg[:, p:p + L].contiguous(), wk, wg, dev_i64([p] * B), m, o, out,
+                         ape=ag, state_in=st_in, state_out=st[k])
+        st_in = st[k]
+        k ^= 1
+        p += L
+    assert p == S
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    for b in range(B):
+        wr = written[b]
+        assert wr.all() or np.isnan(g[b, ~wr]).all()
+        if out_kind == "f32":
+            assert_rows_rel(g[b, wr], ref[b, wr], 1e-5, "fused chunks")
+        else:
+            assert_bf16_close(g[b, wr], ref[b, wr], "fused chunks")
+    np.testing.assert_allclose(st_in.cpu().numpy()[:, :, 0], st_ref[:, :, 0], rtol=2e-5, atol=2e-5)
+    assert np.array_equal(np.isneginf(st_in.cpu().numpy()[:, :, 1]), np.isneginf(st_ref[:, :, 1]))
+
+
 def test_compress_bf16_ragged_tiles_and_split_k():
     # output width 2E = 80 (a partial 128-column tile), 300 rows (a partial
     # 128-row tile) and d_model 1024 so that the projection splits K and the

@@ -162,6 +162,39 @@ def test_paged_compress_matches_unpaged(out_fmt, L):
     assert not pb[~used].any()
 
 
+def test_paged_compress_fused_chunk_matches_unpaged():
+    # a 260-token chunk through the fused projection + pool, storing each
+    # entry at its pool row, bit-exact against the unpaged call
+    d = gen.Draw(66)
+    B, d_model, E, m, o, P = 2, 512, 128, 4, 1, 16
+    L, Nc = 260, 160
+    wk, wg = (w.to(DEV) for w in gen.compressor_weights(d, d_model, E, gen.BF16))
+    x = gen.store(d.normal(B, L, d_model), gen.BF16).to(DEV)
+    pos0 = dev_i64([3, 300])
+    ns = (1 + o) * m - 1
+    state_in = d.normal(B, ns, 2, E).to(DEV)
+    pt, table = _pages(B, Nc, P, seed=9)
+    n_rows = pt.n_pages * P
+    out_u = torch.zeros(B, Nc, E, dtype=torch.bfloat16, device=DEV)
+    su = torch.zeros(B, ns, 2, E, device=DEV)
+    csa.csa_compress(x, wk, wg, pos0, m, o, out_u, state_in=state_in, state_out=su)
+    out_p = torch.zeros(n_rows, E, dtype=torch.bfloat16, device=DEV)
+    sp = torch.zeros(B, ns, 2, E, device=DEV)
+    csa.csa_compress(x, wk, wg, pos0, m, o, out_p, state_in=state_in, state_out=sp, pages=pt)
+    torch.cuda.synchronize()
+    rows = _rows(table, P, Nc).reshape(-1)
+    pb = out_p.cpu().contiguous().view(torch.uint8)
+    ub = out_u.cpu().contiguous().view(torch.uint8)
+    assert torch.equal(pb[rows].view(ub.shape), ub), "paged fused store"
+    # the entries of each call were written (positions 3 .. 262 and 300 .. 559)
+    ue = ub.view(B, Nc, E * 2)
+    assert ue[0, 1:65].any(dim=1).all() and ue[1, 75:140].any(dim=1).all()
+    _same_bits(sp, su, "carried state")
+    used = torch.zeros(n_rows, dtype=torch.bool)
+    used[rows] = True
+    assert not pb[~used].any()
+
+
 def _absent(table, n_pages, P, nc_cap):
     """Marks one page of sequence 0 with -1 and one of the last sequence with
     an id past the pool; returns the table, and the logical entries that the
