@@ -340,6 +340,14 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   // bits: caches hold at most 2^23 rows of 512 bytes.  Paged: the row's pool
   // row, pool row 0 standing in for an absent page.  Wave w issues the
   // instructions w, w + NW, ... of the tile.
+  // the lane's byte offset inside a tile's rows for each of the wave's load
+  // instructions (instruction i: rows 2 i, 2 i + 1; the lane's chunk)
+  uint32_t doff[16 / NW];
+#pragma unroll
+  for (int k = 0; k < 16 / NW; ++k) {
+    const int r = 2 * (wave + NW * k) + h2;
+    doff[k] = (uint32_t)(r * PF_ROWB + 16 * (l32 ^ pf_swz(r)));
+  }
   auto issueA = [&](int ti, auto buf_tag) {
     constexpr int buf = decltype(buf_tag)::value;
     uint8_t* const dst = buf ? &tile1[0][0] : &tile0[0][0];
@@ -349,6 +357,18 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
     const int kk_lim = seg0 ? nv_max : n_win;
     const int row0 = seg0 ? kk0 : rw0 + kk0;
     const uint32_t row_lim = (uint32_t)(seg0 ? Nc_cap : R_cap);
+    if (!PG && kk0 + PF_KT <= kk_lim && row0 >= 0 && (uint32_t)row0 + PF_KT <= row_lim) {
+      // (uniform) every row of the tile exists: one scalar base per tile
+      const char* tb = base + (size_t)(uint32_t)row0 * PF_ROWB;
+#pragma unroll
+      for (int k = 0; k < 16 / NW; ++k) {
+        const int i = wave + NW * k;
+        __builtin_amdgcn_global_load_lds((const void*)(tb + doff[k]),
+                                         (__attribute__((address_space(3))) void*)(dst + 1024 * i),
+                                         16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < 16 / NW; ++k) {
       const int i = wave + NW * k;
@@ -372,8 +392,13 @@ __global__ void __launch_bounds__(64 * PF_ROWS * NH, 2) attn_pf_kernel(
   auto maskA = [&](int ti, int buf) -> uint32_t {
     bool ok;
     if (ti < tiles0) {
+      if (!PG && (ti + 1) * PF_KT <= nv_me) return 0xffffffffu;  // (uniform)
       ok = ti * PF_KT + l32 < nv_me;
     } else {
+      const int64_t tok0 = win_first + (int64_t)(ti - tiles0) * PF_KT;
+      if (!PG && tok0 >= w_lo && tok0 + PF_KT - 1 <= w_hi && tok0 - rbase >= 0 &&
+          tok0 - rbase + PF_KT <= R_cap)
+        return 0xffffffffu;  // (uniform) every key of the tile is in the row's window
       const int64_t tok = win_first + (int64_t)(ti - tiles0) * PF_KT + l32;
       const int64_t r = tok - rbase;
       ok = tok >= w_lo && tok <= w_hi && r >= 0 && r < R_cap;
