@@ -57,6 +57,17 @@
  *    CompressedSparseAttention; read as one more softmax term with logit
  *    sink[h] and no value) is pinned to the same attention with one extra
  *    key whose logit equals the sink and whose value is zero.
+ *  - orc_attn_bwd (both attention forms, sink and per-slot attention mass):
+ *    pinned to torch autograd through the library attention with an explicit
+ *    mask, to central differences of orc_sparse_attn, and to the identities
+ *    sum dV = sum dO, sum dK = 0, sum q.dq = sum K.dK.
+ *  - orc_indexer_kl_bwd: the loss form is a reading (the pages name the
+ *    loss, not its formula; see the function); given that reading it is
+ *    pinned to torch autograd through torch's kl_div and log_softmax, and to
+ *    its closed forms (zero at the indexer's own distribution, linearity in
+ *    the gradient scale).
+ *  - orc_compress_bwd: pinned to central differences of orc_compress and to
+ *    the mean-pool closed form.
  */
 #include <math.h>
 #include <stdint.h>
@@ -644,6 +655,347 @@ int orc_hca_dense_attn(int B, int T, int H, int D, int m, int window, double sca
     }
     free(src);
     free(off);
+  }
+  return 0;
+}
+
+/* ---- attention backward ---------------------------------------------------
+ * Gradients of the attention above (either form) for an upstream gradient dO
+ * of out, by the chain rule through its definition.  Per query token and head,
+ * over the same key set J and softmax:
+ *     P_j = e^{l_j - lse},  P_z = e^{z - lse} (the sink, no value),
+ *     dP_j = dO . V_j,      delta = sum_j P_j dP_j = dO . out,
+ *     dl_j = P_j (dP_j - delta),  dz = -P_z delta,
+ *     dq += scale sum_j dl_j K_j,  dK_j += scale dl_j q,  dV_j += P_j dO.
+ * dK_j and dV_j sum over every (token, head) whose key set holds row j (the
+ * compressed entry or the raw row), so they land in dkv_cmp [B, Nc_cap, 2D] /
+ * dkv_raw [B, R_cap, 2D] as [dK | dV]; dsink [H] sums dz over all tokens.
+ * idx == NULL selects the HCA form (every visible entry, m and n_cmp as for
+ * the indexer), otherwise the CSA form over idx.  attn_mass (CSA form,
+ * optional) receives, per selected slot, sum_h P_j: the main attention's
+ * probability mass on that entry over all heads (0 in skipped slots).
+ * The caller zeroes nothing: every output is written in full. */
+int orc_attn_bwd(int B, int T, int H, int D, int topk, int window, double scale,
+                 const double* sink, const int64_t* q_pos, const void* q, const void* kv_cmp,
+                 int Nc_cap, const int32_t* idx, int m, const int32_t* n_cmp,
+                 const void* kv_raw, int R_cap, const int64_t* raw_base, int dt,
+                 const double* dout, double* dq, double* dkv_cmp, double* dkv_raw,
+                 double* dsink, double* attn_mass) {
+  if (B < 0 || T < 0 || H < 1 || D < 1 || topk < 0 || window < 0) return 1;
+  if (!idx && (m < 1 || !n_cmp)) return 1;
+  memset(dkv_cmp, 0, sizeof(double) * (size_t)B * Nc_cap * 2 * D);
+  memset(dkv_raw, 0, sizeof(double) * (size_t)B * R_cap * 2 * D);
+  if (dsink) memset(dsink, 0, sizeof(double) * H);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+    const int b = (int)(bt / T), t = (int)(bt % T);
+    const int64_t pos = q_pos[b] + t;
+    const int64_t nv = idx ? 0 : n_visible(pos, n_cmp[b], m, Nc_cap);
+    const int64_t cap = (idx ? topk : nv) + window;
+    /* key list: source flag (0 compressed, 1 raw), row, and the slot of a
+     * selected entry (-1 otherwise) */
+    int* src = (int*)malloc(sizeof(int) * (cap > 0 ? cap : 1));
+    int64_t* row = (int64_t*)malloc(sizeof(int64_t) * (cap > 0 ? cap : 1));
+    int* slot = (int*)malloc(sizeof(int) * (cap > 0 ? cap : 1));
+    double* l = (double*)malloc(sizeof(double) * (cap > 0 ? cap : 1));
+    double* P = (double*)malloc(sizeof(double) * (cap > 0 ? cap : 1));
+    double* o = (double*)malloc(sizeof(double) * D);
+    int n = 0;
+    if (idx) {
+      for (int k = 0; k < topk; ++k) {
+        const int32_t j = idx[((size_t)b * T + t) * topk + k];
+        if (attn_mass) attn_mass[((size_t)b * T + t) * topk + k] = 0;
+        if (j < 0 || j >= Nc_cap) continue;
+        src[n] = 0, row[n] = j, slot[n++] = k;
+      }
+    } else {
+      for (int64_t j = 0; j < nv; ++j) src[n] = 0, row[n] = j, slot[n++] = -1;
+    }
+    if (window > 0) {
+      int64_t lo = pos - window + 1;
+      if (lo < 0) lo = 0;
+      for (int64_t j = lo; j <= pos; ++j) {
+        const int64_t r = j - raw_base[b];
+        if (r < 0 || r >= R_cap) continue;
+        src[n] = 1, row[n] = r, slot[n++] = -1;
+      }
+    }
+    for (int h = 0; h < H; ++h) {
+      const size_t qr = ((size_t)b * T + t) * H + h;
+      const double z = sink ? sink[h] : -INFINITY;
+      const double* dO = dout + qr * D;
+      /* forward quantities */
+      double mx = z, den = 0;
+      for (int r = 0; r < n; ++r) {
+        const void* kv = src[r] ? kv_raw : kv_cmp;
+        const size_t ko = ((size_t)b * (src[r] ? R_cap : Nc_cap) + row[r]) * 2 * D;
+        double dot = 0;
+        for (int d = 0; d < D; ++d) dot += ld(q, qr * D + d, dt) * ld(kv, ko + d, dt);
+        l[r] = scale * dot;
+        if (l[r] > mx) mx = l[r];
+      }
+      for (int r = 0; r < n; ++r) den += exp(l[r] - mx);
+      if (z > -INFINITY) den += exp(z - mx);
+      for (int d = 0; d < D; ++d) dq[qr * D + d] = 0;
+      if (den == 0) continue; /* empty key set: out = 0, no gradient */
+      const double lse = mx + log(den);
+      for (int d = 0; d < D; ++d) o[d] = 0;
+      for (int r = 0; r < n; ++r) {
+        const void* kv = src[r] ? kv_raw : kv_cmp;
+        const size_t ko = ((size_t)b * (src[r] ? R_cap : Nc_cap) + row[r]) * 2 * D;
+        P[r] = exp(l[r] - lse);
+        for (int d = 0; d < D; ++d) o[d] += P[r] * ld(kv, ko + D + d, dt);
+      }
+      double delta = 0;
+      for (int d = 0; d < D; ++d) delta += dO[d] * o[d];
+      if (dsink && z > -INFINITY) {
+        const double dz = -exp(z - lse) * delta;
+#pragma omp atomic
+        dsink[h] += dz;
+      }
+      /* backward through the softmax and both products */
+      for (int r = 0; r < n; ++r) {
+        const void* kv = src[r] ? kv_raw : kv_cmp;
+        double* g = (src[r] ? dkv_raw : dkv_cmp) +
+                    ((size_t)b * (src[r] ? R_cap : Nc_cap) + row[r]) * 2 * D;
+        const size_t ko = ((size_t)b * (src[r] ? R_cap : Nc_cap) + row[r]) * 2 * D;
+        double dP = 0;
+        for (int d = 0; d < D; ++d) dP += dO[d] * ld(kv, ko + D + d, dt);
+        const double dl = P[r] * (dP - delta);
+        for (int d = 0; d < D; ++d) {
+          const double gk = scale * dl * ld(q, qr * D + d, dt);
+          const double gv = P[r] * dO[d];
+          dq[qr * D + d] += scale * dl * ld(kv, ko + d, dt);
+#pragma omp atomic
+          g[d] += gk;
+#pragma omp atomic
+          g[D + d] += gv;
+        }
+        if (attn_mass && slot[r] >= 0) attn_mass[((size_t)b * T + t) * topk + slot[r]] += P[r];
+      }
+    }
+    free(src);
+    free(row);
+    free(slot);
+    free(l);
+    free(P);
+    free(o);
+  }
+  return 0;
+}
+
+/* ---- indexer KL loss and its gradient --------------------------------------
+ * The migration page (sections 1 and 3.2) names an indexer loss for training,
+ * a fused sparse "lightning indexer grad + KL loss" operator, a loss
+ * coefficient and a sparse-loss switch (config, section 4.3), but not the
+ * formula.  Reading (sparse form): per query token, over its selected entries
+ * S (the slots of idx with 0 <= idx < Nc_cap), the target is the main
+ * attention's probability mass on each entry summed over heads (attn_mass,
+ * from orc_attn_bwd), normalised over S:  p_k = mass_k / sum_S mass; the
+ * indexer's distribution is the softmax over S of its scores I_k (as in
+ * orc_indexer_topk):  q_k = e^{I_k} / sum_S e^{I}.  The row's loss is
+ * KL(p || q) = sum_S p_k (log p_k - log q_k), with 0 log 0 = 0.  The target
+ * carries no gradient; with g = grad_scale[row] (the caller's loss
+ * coefficient and averaging), dI_k = g (q_k - p_k), and through the score
+ * (v_hk = q_h . k_j, I_k = sum_h w_h ReLU(v_hk), ReLU'(0) = 0):
+ *     dw[t,h] = sum_k dI_k ReLU(v_hk),
+ *     dq[t,h] = sum_k dI_k w_h [v_hk > 0] k_j,
+ *     dk[j]  += sum_h dI_k w_h [v_hk > 0] q_h     (j = idx_k).
+ * Inputs fp32 or bf16 (the training formats).  A row with no selected entry
+ * or zero total mass has loss 0 and no gradient. */
+int orc_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int topk, const void* q_idx,
+                       const float* w_idx, const void* k_idx, int qk_dt, const int32_t* idx,
+                       const double* mass, const double* grad_scale, double* loss,
+                       double* dq_idx, double* dw_idx, double* dk_idx) {
+  if (B < 0 || T < 0 || H_I < 1 || d_I < 1 || topk < 0) return 1;
+  if (qk_dt != ODT_F32 && qk_dt != ODT_BF16) return 1;
+  memset(dk_idx, 0, sizeof(double) * (size_t)B * Nc_cap * d_I);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+    const int b = (int)(bt / T);
+    double* I = (double*)malloc(sizeof(double) * (topk > 0 ? topk : 1));
+    double* dI = (double*)malloc(sizeof(double) * (topk > 0 ? topk : 1));
+    const int32_t* irow = idx + (size_t)bt * topk;
+    const double* mrow = mass + (size_t)bt * topk;
+    double msum = 0, imax = -INFINITY;
+    int any = 0;
+    for (int h = 0; h < H_I; ++h) {
+      dw_idx[(size_t)bt * H_I + h] = 0;
+      for (int e = 0; e < d_I; ++e) dq_idx[((size_t)bt * H_I + h) * d_I + e] = 0;
+    }
+    loss[bt] = 0;
+    for (int k = 0; k < topk; ++k) {
+      const int32_t j = irow[k];
+      dI[k] = 0;
+      if (j < 0 || j >= Nc_cap) continue;
+      double s = 0;
+      for (int h = 0; h < H_I; ++h) {
+        const size_t qr = (size_t)bt * H_I + h;
+        double v = 0;
+        for (int e = 0; e < d_I; ++e)
+          v += ld(q_idx, qr * d_I + e, qk_dt) * ld(k_idx, ((size_t)b * Nc_cap + j) * d_I + e, qk_dt);
+        s += (double)w_idx[qr] * (v > 0 ? v : 0.0);
+      }
+      I[k] = s;
+      if (s > imax) imax = s;
+      msum += mrow[k];
+      any = 1;
+    }
+    if (!any || !(msum > 0)) {
+      free(I);
+      free(dI);
+      continue;
+    }
+    double zsum = 0;
+    for (int k = 0; k < topk; ++k)
+      if (irow[k] >= 0 && irow[k] < Nc_cap) zsum += exp(I[k] - imax);
+    const double logz = imax + log(zsum);
+    const double g = grad_scale ? grad_scale[bt] : 1.0;
+    double kl = 0;
+    for (int k = 0; k < topk; ++k) {
+      const int32_t j = irow[k];
+      if (j < 0 || j >= Nc_cap) continue;
+      const double p = mrow[k] / msum, lq = I[k] - logz;
+      if (p > 0) kl += p * (log(p) - lq);
+      dI[k] = g * (exp(lq) - p);
+    }
+    loss[bt] = kl;
+    for (int k = 0; k < topk; ++k) {
+      const int32_t j = irow[k];
+      if (j < 0 || j >= Nc_cap) continue;
+      const size_t kr = ((size_t)b * Nc_cap + j) * d_I;
+      for (int h = 0; h < H_I; ++h) {
+        const size_t qr = (size_t)bt * H_I + h;
+        double v = 0;
+        for (int e = 0; e < d_I; ++e) v += ld(q_idx, qr * d_I + e, qk_dt) * ld(k_idx, kr + e, qk_dt);
+        if (v > 0) {
+          const double c = dI[k] * (double)w_idx[qr];
+          dw_idx[qr] += dI[k] * v;
+          for (int e = 0; e < d_I; ++e) {
+            dq_idx[qr * d_I + e] += c * ld(k_idx, kr + e, qk_dt);
+            const double gk = c * ld(q_idx, qr * d_I + e, qk_dt);
+#pragma omp atomic
+            dk_idx[kr + e] += gk;
+          }
+        }
+      }
+    }
+    free(I);
+    free(dI);
+  }
+  return 0;
+}
+
+/* ---- compressor backward ----------------------------------------------------
+ * Gradients of a one-shot compressor call over tokens [0, L) (pos0 = 0, no
+ * carried state; entries post-processed by nothing or by the Hadamard
+ * rotation only) for an upstream gradient dC [B, Nc_cap, E] of the entries it
+ * writes (rows i < min(L / m, Nc_cap); other rows are ignored).  With the
+ * rotation, the gradient of the pooled entry is H dC / sqrt(E) (the matrix is
+ * symmetric and orthogonal).  Through the pool, for every entry i and token
+ * j of its window (slot s = j - m (i - o)):
+ *     dP_j += a_{i,j} dC_i,   dG_j += a_{i,j} (P_j - C_i) dC_i,
+ *     dape[s] += a_{i,j} (P_j - C_i) dC_i            (all per channel),
+ * and through the projections P = W_kv x, G = W_gate x:
+ *     dx_j = W_kv^T dP_j + W_gate^T dG_j,
+ *     dW_kv = sum_j dP_j x_j^T,  dW_gate = sum_j dG_j x_j^T  (over b and j).
+ * dape may be NULL (no ape). */
+int orc_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                     const void* x, const void* w_kv, const void* w_gate, int in_dt,
+                     const double* ape, int Nc_cap, const double* dC, double* dx,
+                     double* dw_kv, double* dw_gate, double* dape) {
+  const int Sw = (1 + overlap) * m;
+  if (B < 0 || L < 0 || m < 1 || E < 1 || d_model < 1) return 1;
+  if (rotate && (E & (E - 1))) return 1;
+  memset(dw_kv, 0, sizeof(double) * (size_t)E * d_model);
+  memset(dw_gate, 0, sizeof(double) * (size_t)E * d_model);
+  if (dape) memset(dape, 0, sizeof(double) * (size_t)Sw * E);
+  const int64_t n_ent = (int64_t)L / m < Nc_cap ? (int64_t)L / m : Nc_cap;
+  for (int b = 0; b < B; ++b) {
+    double* P = (double*)malloc(sizeof(double) * ((size_t)L * E + 1));
+    double* G = (double*)malloc(sizeof(double) * ((size_t)L * E + 1));
+    double* dP = (double*)calloc((size_t)L * E + 1, sizeof(double));
+    double* dG = (double*)calloc((size_t)L * E + 1, sizeof(double));
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < L; ++t)
+      for (int e = 0; e < E; ++e) {
+        double pk = 0, gk = 0;
+        for (int k = 0; k < d_model; ++k) {
+          const double xv = ld(x, ((size_t)b * L + t) * d_model + k, in_dt);
+          pk += xv * ld(w_kv, (size_t)e * d_model + k, in_dt);
+          gk += xv * ld(w_gate, (size_t)e * d_model + k, in_dt);
+        }
+        P[(size_t)t * E + e] = pk;
+        G[(size_t)t * E + e] = gk;
+      }
+    /* through the pool: entries are independent; the token rows they share
+     * are summed with atomics */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_ent; ++i) {
+      double* g = (double*)malloc(sizeof(double) * E);
+      for (int e = 0; e < E; ++e) g[e] = dC[((size_t)b * Nc_cap + i) * E + e];
+      if (rotate) hadamard_rows(g, E);
+      const int64_t first = (int64_t)m * (i - overlap), last = (int64_t)m * (i + 1) - 1;
+      for (int e = 0; e < E; ++e) {
+        double mx = -INFINITY, den = 0, C = 0;
+        for (int64_t j = first; j <= last; ++j) {
+          if (j < 0) continue;
+          const double z = G[(size_t)j * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+          if (z > mx) mx = z;
+        }
+        for (int64_t j = first; j <= last; ++j) {
+          if (j < 0) continue;
+          const double z = G[(size_t)j * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+          den += exp(z - mx);
+        }
+        for (int64_t j = first; j <= last; ++j) {
+          if (j < 0) continue;
+          const double z = G[(size_t)j * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+          C += exp(z - mx) / den * P[(size_t)j * E + e];
+        }
+        for (int64_t j = first; j <= last; ++j) {
+          if (j < 0) continue;
+          const double z = G[(size_t)j * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+          const double a = exp(z - mx) / den;
+          const double gp = a * g[e], gg = a * (P[(size_t)j * E + e] - C) * g[e];
+#pragma omp atomic
+          dP[(size_t)j * E + e] += gp;
+#pragma omp atomic
+          dG[(size_t)j * E + e] += gg;
+          if (dape) {
+#pragma omp atomic
+            dape[(size_t)(j - first) * E + e] += gg;
+          }
+        }
+      }
+      free(g);
+    }
+    /* through the projections */
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < L; ++t)
+      for (int k = 0; k < d_model; ++k) {
+        double s = 0;
+        for (int e = 0; e < E; ++e)
+          s += dP[(size_t)t * E + e] * ld(w_kv, (size_t)e * d_model + k, in_dt) +
+               dG[(size_t)t * E + e] * ld(w_gate, (size_t)e * d_model + k, in_dt);
+        dx[((size_t)b * L + t) * d_model + k] = s;
+      }
+#pragma omp parallel for schedule(static)
+    for (int e = 0; e < E; ++e)
+      for (int k = 0; k < d_model; ++k) {
+        double sk = 0, sg = 0;
+        for (int t = 0; t < L; ++t) {
+          const double xv = ld(x, ((size_t)b * L + t) * d_model + k, in_dt);
+          sk += dP[(size_t)t * E + e] * xv;
+          sg += dG[(size_t)t * E + e] * xv;
+        }
+        dw_kv[(size_t)e * d_model + k] += sk;
+        dw_gate[(size_t)e * d_model + k] += sg;
+      }
+    free(P);
+    free(G);
+    free(dP);
+    free(dG);
   }
   return 0;
 }

@@ -76,6 +76,13 @@ def lib():
         L.orc_e2m1_decode.restype = C.c_double
         L.orc_quant_rows_mxfp4.argtypes = [i32, i32, dp, vp, vp]
         L.orc_quant_rows_mxfp4.restype = None
+        L.orc_attn_bwd.argtypes = ([i32] * 6 + [C.c_double, dp, i64p, vp, vp, i32, vp, i32, vp, vp,
+                                    i32, i64p, i32, dp, dp, dp, dp, dp, dp])
+        L.orc_attn_bwd.restype = C.c_int
+        L.orc_indexer_kl_bwd.argtypes = [i32] * 6 + [vp, vp, vp, i32, vp, dp, dp, dp, dp, dp, dp]
+        L.orc_indexer_kl_bwd.restype = C.c_int
+        L.orc_compress_bwd.argtypes = [i32] * 7 + [vp, vp, vp, i32, dp, i32, dp, dp, dp, dp, dp]
+        L.orc_compress_bwd.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = C.c_int
         _lib = L
@@ -294,3 +301,92 @@ def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=N
                                   _p(raw_base), dt, _p(out), _p(lse))
     assert rc == 0
     return out, lse
+
+
+def attn_bwd(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, dout, scale=None, sink=None,
+             m=None, n_cmp=None, want_mass=False):
+    """Gradients of sparse_attn (idx given) or hca_dense_attn (idx None, with m
+    and n_cmp) for an upstream gradient dout [B, T, H, D] of out.
+    Returns (dq [B,T,H,D], dkv_cmp [B,Nc_cap,2D], dkv_raw [B,R_cap,2D],
+    dsink [H] or None, attn_mass [B,T,topk] or None) in float64; attn_mass is
+    the per-slot attention probability summed over heads (CSA form)."""
+    q, kv_cmp, kv_raw = _c(q), _c(kv_cmp), _c(kv_raw)
+    B, T, H, D = q.shape
+    dt = _dt(q)
+    assert _dt(kv_cmp) == dt and _dt(kv_raw) == dt
+    dout = _c(dout, np.float64)
+    assert dout.shape == (B, T, H, D)
+    if idx is not None:
+        idx = _c(idx, np.int32)
+        topk = idx.shape[2]
+        m_, ncp = 1, None
+    else:
+        topk = 0
+        m_ = int(m)
+        ncp = _c(np.broadcast_to(np.asarray(n_cmp, np.int32), (B,)), np.int32)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    q_pos = _c(np.broadcast_to(np.asarray(q_pos, np.int64), (B,)), np.int64)
+    raw_base = _c(np.broadcast_to(np.asarray(raw_base, np.int64), (B,)), np.int64)
+    Nc_cap, R_cap = kv_cmp.shape[1], kv_raw.shape[1]
+    dq = np.zeros((B, T, H, D), np.float64)
+    dkc = np.zeros((B, Nc_cap, 2 * D), np.float64)
+    dkr = np.zeros((B, R_cap, 2 * D), np.float64)
+    sk = _sink(sink, H)
+    dsink = np.zeros(H, np.float64) if sk is not None else None
+    mass = np.zeros((B, T, topk), np.float64) if (want_mass and idx is not None) else None
+    rc = lib().orc_attn_bwd(B, T, H, D, topk, window, scale, _p(sk), _p(q_pos), _p(q),
+                            _p(kv_cmp), Nc_cap, _p(idx), m_, _p(ncp), _p(kv_raw), R_cap,
+                            _p(raw_base), dt, _p(dout), _p(dq), _p(dkc), _p(dkr), _p(dsink),
+                            _p(mass))
+    assert rc == 0
+    return dq, dkc, dkr, dsink, mass
+
+
+def indexer_kl_bwd(q_idx, w_idx, k_idx, idx, mass, grad_scale=None):
+    """Sparse indexer KL loss per query row and its gradients (see the C
+    file): q_idx [B,T,H_I,d_I], w_idx [B,T,H_I] fp32, k_idx [B,Nc_cap,d_I]
+    (fp32 or bf16 bits), idx [B,T,topk], mass [B,T,topk] (attention mass per
+    slot), grad_scale [B,T] or None (1).  Returns (loss [B,T], dq_idx, dw_idx,
+    dk_idx) in float64."""
+    q_idx, k_idx = _c(q_idx), _c(k_idx)
+    w_idx = _c(w_idx, np.float32)
+    idx = _c(idx, np.int32)
+    mass = _c(mass, np.float64)
+    B, T, H_I, d_I = q_idx.shape
+    Nc_cap = k_idx.shape[1]
+    topk = idx.shape[2]
+    dt = _dt(q_idx)
+    assert _dt(k_idx) == dt and dt in (DT_F32, DT_BF16)
+    gs = None if grad_scale is None else _c(np.broadcast_to(np.asarray(grad_scale, np.float64),
+                                                            (B, T)), np.float64)
+    loss = np.zeros((B, T), np.float64)
+    dq = np.zeros((B, T, H_I, d_I), np.float64)
+    dw = np.zeros((B, T, H_I), np.float64)
+    dk = np.zeros((B, Nc_cap, d_I), np.float64)
+    rc = lib().orc_indexer_kl_bwd(B, T, H_I, d_I, Nc_cap, topk, _p(q_idx), _p(w_idx), _p(k_idx),
+                                  dt, _p(idx), _p(mass), _p(gs), _p(loss), _p(dq), _p(dw), _p(dk))
+    assert rc == 0
+    return loss, dq, dw, dk
+
+
+def compress_bwd(x, w_kv, w_gate, m, overlap, Nc_cap, dC, ape=None, rotate=False):
+    """Gradients of a one-shot compress call from position 0 (no state) for
+    an upstream gradient dC [B, Nc_cap, E] of its entries.  Returns (dx
+    [B,L,d_model], dw_kv [E,d_model], dw_gate [E,d_model], dape or None)."""
+    x, w_kv, w_gate = _c(x), _c(w_kv), _c(w_gate)
+    B, L, d_model = x.shape
+    E = w_kv.shape[0]
+    dt = _dt(x)
+    assert _dt(w_kv) == dt and _dt(w_gate) == dt
+    dC = _c(dC, np.float64)
+    assert dC.shape == (B, Nc_cap, E)
+    ape = _c(ape, np.float64)
+    dx = np.zeros((B, L, d_model), np.float64)
+    dwk = np.zeros((E, d_model), np.float64)
+    dwg = np.zeros((E, d_model), np.float64)
+    dape = np.zeros(((1 + overlap) * m, E), np.float64) if ape is not None else None
+    rc = lib().orc_compress_bwd(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(x), _p(w_kv),
+                                _p(w_gate), dt, _p(ape), Nc_cap, _p(dC), _p(dx), _p(dwk),
+                                _p(dwg), _p(dape))
+    assert rc == 0
+    return dx, dwk, dwg, dape
