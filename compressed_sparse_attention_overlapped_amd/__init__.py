@@ -18,7 +18,8 @@ import torch
 
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
-           "csa_indexer_topk_varlen", "csa_sparse_attn_varlen",
+           "csa_indexer_topk_varlen", "csa_sparse_attn_varlen", "csa_sparse_attn_bwd",
+           "hca_dense_attn_bwd",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
            "CsaError", "PageTable", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
@@ -140,6 +141,16 @@ def lib():
         for f in (L.csa_compress_workspace_size, L.csa_indexer_topk_workspace_size,
                   L.csa_sparse_attn_workspace_size, L.hca_dense_attn_workspace_size):
             f.restype = C.c_size_t
+        L.csa_sparse_attn_bwd.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32, vp,
+                                          i32] + [vp] * 8 + [sz, vp])
+        L.csa_sparse_attn_bwd.restype = C.c_int
+        L.csa_sparse_attn_bwd_workspace_size.argtypes = [i32] * 4
+        L.csa_sparse_attn_bwd_workspace_size.restype = C.c_size_t
+        L.hca_dense_attn_bwd.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, vp, i32, vp, i32, vp,
+                                         i32] + [vp] * 7 + [sz, vp])
+        L.hca_dense_attn_bwd.restype = C.c_int
+        L.hca_dense_attn_bwd_workspace_size.argtypes = [i32] * 3
+        L.hca_dense_attn_bwd_workspace_size.restype = C.c_size_t
         L.csa_status_string.argtypes = [i32]
         L.csa_status_string.restype = C.c_char_p
         L.csa_last_error.argtypes = []
@@ -387,6 +398,68 @@ def hca_dense_attn(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, scale=N
                               _p(raw_base), _DT[q.dtype], _p(out), _p(lse), _p(ws), nb, _stream(q))
     _check("hca_dense_attn", rc)
     return out, lse
+
+
+# ---------------------------------------------------------------- backward
+
+def _bwd_outputs(q, kv_cmp, kv_raw, sink, dq, dkv_cmp, dkv_raw, dsink):
+    B, T, H, D = q.shape
+    f32 = dict(dtype=torch.float32, device=q.device)
+    if dq is None:
+        dq = torch.empty(B, T, H, D, **f32)
+    if dkv_cmp is None:
+        dkv_cmp = torch.empty(B, kv_cmp.shape[1], 2 * D, **f32)
+    if dkv_raw is None:
+        dkv_raw = torch.empty(B, kv_raw.shape[1], 2 * D, **f32)
+    if dsink is None and sink is not None:
+        dsink = torch.empty(H, **f32)
+    return dq, dkv_cmp, dkv_raw, dsink
+
+
+def csa_sparse_attn_bwd(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, lse, dout,
+                        scale=None, sink=None, want_mass=False, dq=None, dkv_cmp=None,
+                        dkv_raw=None, dsink=None, attn_mass=None, workspace=None):
+    """Gradients of csa_sparse_attn for the upstream gradient dout (bf16, like
+    q); lse is the forward's.  Returns (dq, dkv_cmp, dkv_raw, dsink or
+    None, attn_mass or None), all float32; attn_mass [B, T, topk] is the
+    attention probability of each selected slot summed over heads."""
+    _dense(q, kv_cmp, idx, kv_raw, q_pos, raw_base, lse, dout, sink)
+    B, T, H, D = q.shape
+    topk = idx.shape[2] if idx is not None else 0
+    scale = D ** -0.5 if scale is None else float(scale)
+    sink = _sink(sink, H)
+    dq, dkv_cmp, dkv_raw, dsink = _bwd_outputs(q, kv_cmp, kv_raw, sink, dq, dkv_cmp, dkv_raw,
+                                               dsink)
+    if want_mass and attn_mass is None:
+        attn_mass = torch.empty(B, T, topk, dtype=torch.float32, device=q.device)
+    ws, nb = _workspace(lib().csa_sparse_attn_bwd_workspace_size(B, T, H, kv_cmp.shape[1]), q,
+                        workspace)
+    rc = lib().csa_sparse_attn_bwd(B, T, H, D, topk, window, scale, _p(sink), _p(q_pos), _p(q),
+                                   _p(kv_cmp), kv_cmp.shape[1], _p(idx), _p(kv_raw),
+                                   kv_raw.shape[1], _p(raw_base), _DT[q.dtype], _p(lse), _p(dout),
+                                   _p(dq), _p(dkv_cmp), _p(dkv_raw), _p(dsink), _p(attn_mass),
+                                   _p(ws), nb, _stream(q))
+    _check("csa_sparse_attn_bwd", rc)
+    return dq, dkv_cmp, dkv_raw, dsink, attn_mass
+
+
+def hca_dense_attn_bwd(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, lse, dout,
+                       scale=None, sink=None, dq=None, dkv_cmp=None, dkv_raw=None, dsink=None,
+                       workspace=None):
+    """Gradients of hca_dense_attn; returns (dq, dkv_cmp, dkv_raw, dsink or None)."""
+    _dense(q, kv_cmp, kv_raw, q_pos, n_cmp, raw_base, lse, dout, sink)
+    B, T, H, D = q.shape
+    scale = D ** -0.5 if scale is None else float(scale)
+    sink = _sink(sink, H)
+    dq, dkv_cmp, dkv_raw, dsink = _bwd_outputs(q, kv_cmp, kv_raw, sink, dq, dkv_cmp, dkv_raw,
+                                               dsink)
+    ws, nb = _workspace(lib().hca_dense_attn_bwd_workspace_size(B, T, H), q, workspace)
+    rc = lib().hca_dense_attn_bwd(B, T, H, D, m, window, scale, _p(sink), _p(q_pos), _p(n_cmp),
+                                  _p(q), _p(kv_cmp), kv_cmp.shape[1], _p(kv_raw), kv_raw.shape[1],
+                                  _p(raw_base), _DT[q.dtype], _p(lse), _p(dout), _p(dq),
+                                  _p(dkv_cmp), _p(dkv_raw), _p(dsink), _p(ws), nb, _stream(q))
+    _check("hca_dense_attn_bwd", rc)
+    return dq, dkv_cmp, dkv_raw, dsink
 
 
 # ---------------------------------------------------------------- packed sequences

@@ -605,3 +605,74 @@ csa_status_t csa_sparse_attn_varlen(int n, int total, int max_len, int H, int D,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- backward
+
+size_t csa_sparse_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap) {
+  if (B <= 0 || T <= 0 || H <= 0 || Nc_cap < 0) return 0;
+  return csa_host::attn_bwd_ws_bytes(B, T, H, Nc_cap, true);
+}
+
+size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H) {
+  if (B <= 0 || T <= 0 || H <= 0) return 0;
+  return csa_host::attn_bwd_ws_bytes(B, T, H, 0, false);
+}
+
+static csa_status_t attn_bwd_impl(const char* fn, csa_host::AttnBwdArgs& a, int D,
+                                  csa_dtype_t dt, size_t ws_bytes, hipStream_t stream) {
+  if (a.B <= 0 || a.T <= 0 || a.H <= 0 || D <= 0 || a.window < 0 || a.Nc_cap < 0 ||
+      a.R_cap < 0 || a.topk < 0)
+    return fail(CSA_E_ARG, "%s: B, T, H, D must be > 0; window, Nc_cap, R_cap, topk >= 0", fn);
+  if (!a.q_pos || !a.q || !a.raw_base || !a.lse || !a.dout || !a.dq)
+    return fail(CSA_E_ARG, "%s: q_pos, q, raw_base, lse, dout and dq are required", fn);
+  if ((a.Nc_cap > 0 && (!a.kv_cmp || !a.dkv_cmp)) || (a.R_cap > 0 && (!a.kv_raw || !a.dkv_raw)))
+    return fail(CSA_E_ARG, "%s: a cache with rows needs its tensor and its gradient", fn);
+  if (a.dsink && !a.sink) return fail(CSA_E_ARG, "%s: dsink needs sink", fn);
+  if (dt != CSA_DT_BF16) return fail(CSA_E_UNSUPPORTED, "%s: dt must be BF16", fn);
+  if (D != 128 || (a.H != 32 && a.H != 64))
+    return fail(CSA_E_UNSUPPORTED, "%s: needs D = 128 and H in {32, 64}", fn);
+  const void* al[] = {a.q, a.dout, a.kv_cmp, a.kv_raw, a.dq};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return fail(CSA_E_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+  if (a.Nc_cap > (1 << 23) || a.R_cap > (1 << 23))
+    return fail(CSA_E_UNSUPPORTED, "%s: caches hold at most 2^23 rows", fn);
+  if ((a.T + 63) / 64 > 65535 || a.B > 65535)
+    return fail(CSA_E_UNSUPPORTED, "%s: T <= 65535 * 64 and B <= 65535", fn);
+  const size_t need = csa_host::attn_bwd_ws_bytes(a.B, a.T, a.H, a.Nc_cap, !a.dense);
+  if (ws_bytes < need || !a.ws)
+    return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  return hip_status(csa_host::launch_attn_bwd(a, stream), fn);
+}
+
+csa_status_t csa_sparse_attn_bwd(int B, int T, int H, int D, int topk, int window, float scale,
+                                 const float* sink, const int64_t* q_pos, const void* q,
+                                 const void* kv_cmp, int Nc_cap, const int32_t* idx,
+                                 const void* kv_raw, int R_cap, const int64_t* raw_base,
+                                 csa_dtype_t dt, const float* lse, const void* dout, float* dq,
+                                 float* dkv_cmp, float* dkv_raw, float* dsink, float* attn_mass,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (topk > 4096) return fail(CSA_E_UNSUPPORTED, "csa_sparse_attn_bwd: topk > 4096");
+  if (Nc_cap > 65536) return fail(CSA_E_UNSUPPORTED, "csa_sparse_attn_bwd: Nc_cap > 65536");
+  if (topk > 0 && !idx) return fail(CSA_E_ARG, "csa_sparse_attn_bwd: idx is required when topk > 0");
+  csa_host::AttnBwdArgs a{B,      T,      H,       topk,    window,  1,       Nc_cap,
+                          R_cap,  false,  scale,   sink,    q_pos,   nullptr, q,
+                          kv_cmp, idx,    kv_raw,  raw_base, lse,    dout,    dq,
+                          dkv_cmp, dkv_raw, dsink, attn_mass, workspace};
+  return attn_bwd_impl("csa_sparse_attn_bwd", a, D, dt, ws_bytes, stream);
+}
+
+csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, float scale,
+                                const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                                const void* q, const void* kv_cmp, int Nc_cap, const void* kv_raw,
+                                int R_cap, const int64_t* raw_base, csa_dtype_t dt,
+                                const float* lse, const void* dout, float* dq, float* dkv_cmp,
+                                float* dkv_raw, float* dsink, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (m < 1) return fail(CSA_E_ARG, "hca_dense_attn_bwd: m must be >= 1");
+  if (!n_cmp) return fail(CSA_E_ARG, "hca_dense_attn_bwd: n_cmp is required");
+  csa_host::AttnBwdArgs a{B,      T,       H,       0,       window,  m,       Nc_cap,
+                          R_cap,  true,    scale,   sink,    q_pos,   n_cmp,   q,
+                          kv_cmp, nullptr, kv_raw,  raw_base, lse,    dout,    dq,
+                          dkv_cmp, dkv_raw, dsink,  nullptr, workspace};
+  return attn_bwd_impl("hca_dense_attn_bwd", a, D, dt, ws_bytes, stream);
+}

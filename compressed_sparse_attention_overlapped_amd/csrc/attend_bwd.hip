@@ -1,0 +1,700 @@
+// Attention backward for gfx950: gradients of the sparse (CSA) and dense
+// (HCA) MQA attention with respect to the queries, the compressed and raw KV
+// rows and the per-head sink, plus the main attention's probability mass per
+// selected entry (the indexer loss target).
+//
+// Math, per query token and head over the forward's key set J (DS-V4 analysis
+// section 1.2; Notion copy section 1.1: one shared KV head, 1/sqrt(D) scale):
+//   P_j = exp(l_j - lse) with the forward's lse,  dP_j = dO . V_j,
+//   delta = dO . out,  dS_j = P_j (dP_j - delta),
+//   dq = scale sum_j dS_j K_j,  dK_j += scale sum dS_j q,  dV_j += sum P_j dO,
+//   dsink = -sum exp(sink - lse) delta.
+//
+// Launches: a zero fill of the summed outputs; for CSA a bitmap kernel (the
+// selected entries of each row as bits, with the rank of each word); a
+// query-major dq kernel (the forward's tile walk: gathered or dense
+// compressed tiles, then the window, 32 keys per tile in LDS), which also
+// computes delta = sum_j P_j dP_j exactly (a first sweep over the row's tiles,
+// so delta does not inherit the rounding of a stored bf16 output) and hands
+// delta and lse to the next kernels; a reduction of the sink gradient; and a
+// key-major dK/dV kernel (a workgroup owns 128 keys and walks the query rows
+// that see them, each row's Q and dO staged in LDS), whose row-chunk
+// partials are summed with fp32 atomics into the zeroed outputs.  The per-key
+// sums need no atomics between query rows (MFMA reduces over heads and rows
+// inside the workgroup); an fp32 atomic costs about as much as eight plain
+// stores here, so the query-major form that scatters every (row, key)
+// contribution is avoided.
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+
+namespace csa {
+
+constexpr int BW_KT = 32;                   // keys per tile (dq kernel)
+constexpr int BW_ROWB = 512;                // bytes of one [K | V] row (D = 128, bf16)
+constexpr int BW_TILEB = BW_KT * BW_ROWB;   // 16 KB
+constexpr int BW_IDX_MAX = 4096;            // index slots per row staged in LDS
+constexpr int BW_KV_KEYS = 128;             // keys per workgroup (dK/dV kernel)
+constexpr int BW_RC = 64;                   // query rows per dK/dV workgroup
+
+// 16-byte chunk c of row r of an LDS tile sits at slot c ^ bw_swz(r): 16
+// consecutive rows read at one chunk (the MFMA operand reads) and the 4 x 4
+// row/chunk blocks of the transposing reads both spread over all banks.
+__device__ __forceinline__ int bw_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// LDS transpose read: lane i of each 16-lane group receives element i % 4 of
+// the 8-byte chunks whose addresses lanes i / 4 + 4 v (v = 0..3) supplied.
+typedef __attribute__((ext_vector_type(4))) short bw_s16x4;
+__device__ __forceinline__ bw_s16x4 bw_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bw_s16x4*)p);
+}
+
+// one 16-byte global -> LDS copy per lane: lane l fills dst + 16 l
+__device__ __forceinline__ void bw_dma(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void bw_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------- sink
+// dsink[h] = sum over rows of dz[row][h] (the dq kernel's per-row terms):
+// each workgroup sums a slice of rows per head, then one atomic per head.
+template <int H>
+__global__ void __launch_bounds__(256) bwd_sink_kernel(const float* __restrict__ dz, int rows,
+                                                       float* __restrict__ dsink) {
+  constexpr int RPS = 256 / H;  // rows per step
+  __shared__ float part[256];
+  const int tid = threadIdx.x, h = tid % H, r0 = tid / H;
+  float s = 0.0f;
+  for (int r = blockIdx.x * RPS + r0; r < rows; r += gridDim.x * RPS) s += dz[(size_t)r * H + h];
+  part[tid] = s;
+  __syncthreads();
+  if (tid < H) {
+    float t = 0.0f;
+    for (int k = 0; k < RPS; ++k) t += part[k * H + tid];
+    atomicAdd(dsink + tid, t);
+  }
+}
+
+// ---------------------------------------------------------------- bitmap
+// One workgroup (256 threads) per query row: bit j of words[row] is set when
+// entry j is selected (0 <= idx < Nc_cap); rank[row][w] = selected entries in
+// words < w, so an entry's slot in an ascending index row is its rank.
+__global__ void __launch_bounds__(256) bwd_bitmap_kernel(const int32_t* __restrict__ idx,
+                                                         int topk, int Nc_cap, int nw,
+                                                         uint32_t* __restrict__ bm,
+                                                         uint32_t* __restrict__ rank) {
+  __shared__ uint32_t words[2048];
+  __shared__ uint32_t sh[16];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  for (int w = tid; w < nw; w += 256) words[w] = 0;
+  __syncthreads();
+  const int32_t* ir = idx + (size_t)row * topk;
+  for (int k = tid; k < topk; k += 256) {
+    const int32_t j = ir[k];
+    if (j >= 0 && j < Nc_cap) atomicOr(&words[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  const int per = (nw + 255) / 256;
+  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+  uint32_t c = 0;
+  for (int w = w0; w < w1; ++w) c += __popc(words[w]);
+  uint32_t tot;
+  uint32_t r = block_excl_scan(c, sh, tot);
+  uint32_t* brow = bm + (size_t)row * nw;
+  uint32_t* rrow = rank + (size_t)row * nw;
+  for (int w = w0; w < w1; ++w) {
+    brow[w] = words[w];
+    rrow[w] = r;
+    r += __popc(words[w]);
+  }
+}
+
+// ---------------------------------------------------------------- zero fill
+__global__ void bwd_zero_kernel(float* __restrict__ p, size_t n) {
+  const size_t n4 = n / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * blockDim.x)
+    *(f32x4*)(p + 4 * i) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (size_t i = 4 * n4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------- dq
+// One workgroup per query row, NHH waves (wave w: heads 32 w .. 32 w + 31).
+// Tiles of 32 keys in the forward's order: the compressed segment (CSA: the
+// row's index slots; HCA: entries [0, n_vis)), then the window's raw rows.
+// Per tile and wave (keys on MFMA rows, heads on columns):
+//   S^T = K Q^T, dP^T = V dO^T (16 MFMAs), P and dS in registers,
+//   dq^T += K^T dS^T (8 MFMAs; K^T through transposing LDS reads).
+template <int NHH, bool DENSE>
+__global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ sink,
+    const uint16_t* __restrict__ kv_cmp,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw,
+    const int64_t* __restrict__ q_pos, const int64_t* __restrict__ raw_base,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int R_cap, int topk, int window, int m,
+    float scale, float* __restrict__ dq, float* __restrict__ ldw, float* __restrict__ dz) {
+  constexpr int H = 32 * NHH;
+  constexpr int NI = 16 / NHH;  // load instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t tile0[BW_TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile1[BW_TILEB];
+  __shared__ int32_t idx_s[DENSE ? 1 : BW_IDX_MAX];
+  __shared__ int32_t sh_last;
+  const int row = blockIdx.x, b = row / T, t = row - b * T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int head = 32 * wave + l32;
+  const int64_t pos = q_pos[b] + t;
+  const float lse_n = lse[(size_t)row * H + head];
+  const float lse2 = lse_n * kLog2e;
+  const float sc2 = scale * kLog2e;
+  float dlt = 0.0f;  // delta of this lane's head (first sweep)
+
+  // compressed segment: n_a tiles
+  int nv = 0, n_a;
+  if constexpr (DENSE) {
+    nv = n_visible(pos, n_cmp[b], m, Nc_cap);
+    n_a = (nv + BW_KT - 1) / BW_KT;
+  } else {
+    if (tid == 0) sh_last = -1;
+    __syncthreads();
+    int last = -1;
+    const int32_t* ir = idx + (size_t)row * topk;
+    for (int k = tid; k < topk; k += 64 * NHH) {
+      const int32_t v = ir[k];
+      const bool ok = v >= 0 && v < Nc_cap;
+      idx_s[k] = ok ? v : -1;
+      if (ok) last = k;
+    }
+    if (last >= 0) atomicMax(&sh_last, last);
+    __syncthreads();
+    n_a = (sh_last + 1 + BW_KT - 1) / BW_KT;
+  }
+  // window segment: raw rows [ra, rb]
+  int64_t ra = 0, rb = -1;
+  if (window > 0 && R_cap > 0) {
+    const int64_t rbase = raw_base[b];
+    int64_t wlo = pos - window + 1;
+    if (wlo < 0) wlo = 0;
+    ra = wlo - rbase;
+    rb = pos - rbase;
+    if (ra < 0) ra = 0;
+    if (rb > R_cap - 1) rb = R_cap - 1;
+  }
+  const int n_w = rb >= ra ? (int)((rb - ra + BW_KT) / BW_KT) : 0;
+  const int ntiles = n_a + n_w;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+
+  if (ntiles > 0) {
+    // B operands: Q^T and dO^T, head `head`, dims 16 s + 8 h2 ..
+    bf16x8 qf[8], of[8];
+    {
+      const uint16_t* qr = q + ((size_t)row * H + head) * 128 + 8 * h2;
+      const uint16_t* orr = dout + ((size_t)row * H + head) * 128 + 8 * h2;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        qf[s] = *(const bf16x8*)(qr + 16 * s);
+        of[s] = *(const bf16x8*)(orr + 16 * s);
+      }
+    }
+    // K^T transposing reads: key rows 4 h2 + jj / 4 + 8 e, dims 32 dt +
+    // 16 (gg & 1) + 4 (jj & 3), for lane jj of 16-lane group gg
+    uint32_t tofs[4][2];
+    const uint32_t krow = (uint32_t)(l32 * BW_ROWB), kx = (uint32_t)(h2 ^ bw_swz(l32));
+    {
+      const int gg = lane >> 4, jj = lane & 15;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 4 * (gg >> 1) + (jj >> 2) + 8 * e;
+        const int fr = bw_swz(r);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int c = 4 * dt + 2 * (gg & 1) + ((jj & 3) >> 1);
+          tofs[dt][e] = (uint32_t)(r * BW_ROWB + 16 * (c ^ fr) + 8 * (jj & 1));
+        }
+      }
+    }
+    const char* cmp_b = (const char*)(kv_cmp + (size_t)b * Nc_cap * 256);
+    const char* raw_b = (const char*)(kv_raw + (size_t)b * R_cap * 256);
+    // tile ti into dst: load instruction i covers tile rows 2 i, 2 i + 1
+    auto issue = [&](int ti, uint8_t* dst) {
+      const bool seg_a = ti < n_a;  // uniform
+      const char* base = seg_a ? cmp_b : raw_b;
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int i = wave + NHH * k;
+        const int r = 2 * i + h2;
+        uint32_t grow;
+        if (seg_a) {
+          const int kk = ti * BW_KT + r;
+          if constexpr (DENSE) {
+            grow = kk < nv ? (uint32_t)kk : 0u;
+          } else {
+            const int v = kk < topk ? idx_s[kk] : -1;
+            grow = v >= 0 ? (uint32_t)v : 0u;
+          }
+        } else {
+          const int64_t rr = ra + (int64_t)(ti - n_a) * BW_KT + r;
+          grow = rr <= rb ? (uint32_t)rr : 0u;
+        }
+        const uint32_t c = (uint32_t)(l32 ^ bw_swz(r));
+        bw_dma(base + (size_t)grow * BW_ROWB + 16u * c, dst + 1024 * i);
+      }
+    };
+    auto vmask = [&](int ti) -> uint32_t {
+      bool ok;
+      if (ti < n_a) {
+        const int kk = ti * BW_KT + l32;
+        if constexpr (DENSE) ok = kk < nv;
+        else ok = kk < topk && idx_s[kk] >= 0;
+      } else {
+        ok = ra + (int64_t)(ti - n_a) * BW_KT + l32 <= rb;
+      }
+      return (uint32_t)__ballot(ok);
+    };
+    // PASS 0: delta += sum_j P_j dP_j; PASS 1: dq^T += K^T dS^T
+    float dacc = 0.0f;
+    auto compute = [&](const uint8_t* tb, uint32_t vm, auto pass_tag) {
+      constexpr int PASS = decltype(pass_tag)::value;
+      f32x16 s_acc, p_acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_acc[r] = p_acc[r] = 0.0f;
+      // K / V rows: key l32, chunk 2 s + h2 (+ 16 for V) at slot chunk ^ bw_swz(l32);
+      // (2 s + h2) ^ f = 2 s ^ (h2 ^ f) since 2 s is even
+#pragma unroll
+      for (int s0 = 0; s0 < 8; s0 += 4) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          kf[u] = *(const bf16x8*)(tb + krow + 16 * ((uint32_t)(2 * (s0 + u)) ^ kx));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u], qf[s0 + u], s_acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int s0 = 0; s0 < 8; s0 += 4) {
+        bf16x8 vf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          vf[u] = *(const bf16x8*)(tb + krow + 16 * ((uint32_t)(16 + 2 * (s0 + u)) ^ kx));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], of[s0 + u], p_acc, 0, 0, 0);
+      }
+      // keys of register r: 8 (r / 4) + 4 h2 + r % 4
+      const uint32_t mv = vm >> (4 * h2);
+      if constexpr (PASS == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool on = (mv >> (8 * (r >> 2) + (r & 3))) & 1u;
+          const float p = on ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], sc2, -lse2)) : 0.0f;
+          dacc = __builtin_fmaf(p, p_acc[r], dacc);
+        }
+      } else {
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool on = (mv >> (8 * (r >> 2) + (r & 3))) & 1u;
+          const float p = on ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], sc2, -lse2)) : 0.0f;
+          dsb[r >> 3][r & 7] = (__bf16)(p * (p_acc[r] - dlt));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const uint32_t ko = (uint32_t)ks * 16 * BW_ROWB;
+            const u32x2 v1 = __builtin_bit_cast(u32x2, bw_read_tr16(tb + tofs[dt][0] + ko));
+            const u32x2 v2 = __builtin_bit_cast(u32x2, bw_read_tr16(tb + tofs[dt][1] + ko));
+            const bf16x8 kt = __builtin_bit_cast(bf16x8, u32x4{v1[0], v1[1], v2[0], v2[1]});
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb[ks], acc[dt], 0, 0, 0);
+          }
+      }
+    };
+    auto sweep = [&](auto pass_tag) {
+      issue(0, tile0);
+      for (int ti = 0; ti < ntiles; ti += 2) {
+        bw_wait_loads();
+        __syncthreads();
+        if (ti + 1 < ntiles) issue(ti + 1, tile1);
+        {
+          const uint32_t vm = vmask(ti);
+          if (vm) compute(tile0, vm, pass_tag);
+        }
+        if (ti + 1 >= ntiles) break;
+        bw_wait_loads();
+        __syncthreads();
+        if (ti + 2 < ntiles) issue(ti + 2, tile0);
+        {
+          const uint32_t vm = vmask(ti + 1);
+          if (vm) compute(tile1, vm, pass_tag);
+        }
+      }
+      __syncthreads();  // every wave is done with both buffers
+    };
+    sweep(std::integral_constant<int, 0>{});
+    dlt = dacc + lane_xor32(dacc);  // the other half of the keys
+    sweep(std::integral_constant<int, 1>{});
+  }
+  // delta and lse (log2 units) for the dK / dV kernel; the sink term
+  if (h2 == 0) {
+    ldw[(size_t)row * 2 * H + head] = lse2;
+    ldw[(size_t)row * 2 * H + H + head] = dlt;
+    if (dz) {
+      const float z = sink[head];
+      dz[(size_t)row * H + head] =
+          (z > -INFINITY && lse_n > -INFINITY) ? -__builtin_amdgcn_exp2f((z - lse_n) * kLog2e) * dlt
+                                               : 0.0f;
+    }
+  }
+  // dq^T: head `head` on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4
+  float* o = dq + ((size_t)row * H + head) * 128 + 4 * h2;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(o + 32 * dt + 8 * g) =
+          f32x4{scale * acc[dt][4 * g], scale * acc[dt][4 * g + 1], scale * acc[dt][4 * g + 2],
+                scale * acc[dt][4 * g + 3]};
+}
+
+// ---------------------------------------------------------------- dK / dV
+// KIND: 0 compressed entries of the CSA form (a row attends entry j when bit
+// j of its bitmap is set), 1 compressed entries of the HCA form (j < n_vis),
+// 2 raw window rows.  Workgroup (kt, chunk, b): keys [128 kt, 128 kt + 128)
+// of the cache, wave w the 32 keys from 128 kt + 32 w, and up to 64 query
+// rows from the first row that can see the tile.  Per row, all four waves read
+// its Q and dO (staged in LDS); per wave (heads on MFMA rows, keys on columns):
+//   S = Q K^T, dP = dO V^T (32 MFMAs), P and dS in registers,
+//   dV^T += dO^T P, dK^T += Q^T dS (32 MFMAs; dO^T and Q^T through
+//   transposing LDS reads).
+template <int NHH, int KIND>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
+    const float* __restrict__ ldw, const uint16_t* __restrict__ kv, int rows_cap,
+    const uint32_t* __restrict__ bm, const uint32_t* __restrict__ rank, int nw,
+    const int64_t* __restrict__ q_pos, const int64_t* __restrict__ raw_base,
+    const int32_t* __restrict__ n_cmp, int T, int topk, int window, int m, float scale,
+    float* __restrict__ dkv, float* __restrict__ attn_mass) {
+  constexpr int H = 32 * NHH;
+  constexpr int QB = H * 256;             // bytes of one row's Q (or dO)
+  constexpr int SB = 2 * QB + 8 * H;      // Q | dO | lse2 | delta
+  constexpr int NQI = QB / 1024;          // load instructions for Q (and for dO)
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[SB];
+  __shared__ int32_t rows_s[BW_RC];
+  __shared__ uint32_t sh[16];
+  const int kt = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int j0 = BW_KV_KEYS * kt;
+  const int jw = j0 + 32 * wave + l32;  // this lane's key (MFMA column)
+  const int64_t qp = q_pos[b];
+  const int64_t rbase = KIND == 2 ? raw_base[b] : 0;
+  const int ncb = KIND == 1 ? n_cmp[b] : 0;
+
+  // rows that can see the tile: [t_lo, t_hi]
+  int64_t t_lo = 0, t_hi = T - 1;
+  if (KIND == 2) {
+    const int64_t p0 = rbase + j0, p1 = rbase + min(j0 + BW_KV_KEYS, rows_cap) - 1;
+    t_lo = p0 - qp;
+    t_hi = p1 + window - 1 - qp;
+  } else if (KIND == 1) {
+    if (ncb <= j0) return;  // uniform
+    t_lo = (int64_t)m * (j0 + 1) - 1 - qp;
+  }
+  if (t_lo < 0) t_lo = 0;
+  if (t_hi > T - 1) t_hi = T - 1;
+  const int64_t c0 = t_lo + (int64_t)chunk * BW_RC;
+  if (c0 > t_hi) return;  // uniform, before any barrier
+  const int nc = (int)min((int64_t)BW_RC, t_hi - c0 + 1);
+
+  // the chunk's rows that see any key of the tile (CSA: a selected entry)
+  {
+    bool act = false;
+    if (tid < nc) {
+      act = true;
+      if (KIND == 0) {
+        const uint32_t* w = bm + ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
+        uint32_t any = 0;
+        for (int k = 0; k < 4; ++k)
+          if ((j0 >> 5) + k < nw) any |= w[k];
+        act = any != 0;
+      }
+    }
+    uint32_t tot;
+    const uint32_t at = block_excl_scan(act ? 1u : 0u, sh, tot);
+    if (act) rows_s[at] = (int)(c0 + tid);
+    sh[8] = tot;  // read after the next barrier
+  }
+  __syncthreads();
+  const int n_rows = (int)sh[8];
+  if (n_rows == 0) return;  // uniform
+
+  // B operands: K^T and V^T of this lane's key (dims 16 s + 8 h2 ..); keys
+  // past the cache read row 0 and are masked
+  const bool key_in = jw < rows_cap;
+  bf16x8 kf[8], vf[8];
+  {
+    const uint16_t* kr = kv + ((size_t)b * rows_cap + (key_in ? jw : 0)) * 256 + 8 * h2;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kf[s] = *(const bf16x8*)(kr + 16 * s);
+      vf[s] = *(const bf16x8*)(kr + 128 + 16 * s);
+    }
+  }
+  // LDS offsets: A operands Q / dO (head l32 of each 32-head half, chunk
+  // 2 s + h2); the transposing reads of Q^T / dO^T (head rows 4 (gg >> 1) +
+  // jj / 4 + 8 e, dims 32 dt + 16 (gg & 1) + 4 (jj & 3))
+  uint32_t aofs[8], tofs[4][2];
+  {
+    const int fa = bw_swz(l32);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) aofs[s] = (uint32_t)(l32 * 256 + 16 * ((2 * s + h2) ^ fa));
+    const int gg = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 4 * (gg >> 1) + (jj >> 2) + 8 * e;
+      const int fr = bw_swz(r);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int c = 4 * dt + 2 * (gg & 1) + ((jj & 3) >> 1);
+        tofs[dt][e] = (uint32_t)(r * 256 + 16 * (c ^ fr) + 8 * (jj & 1));
+      }
+    }
+  }
+  // stage row t into dst: Q and dO rows of 4 heads per load instruction
+  // (lane l: head 4 i + l / 16, chunk l % 16 at slot chunk ^ bw_swz(head)),
+  // then lse2 | delta (8 H bytes) by the lanes that cover it
+  auto stage = [&](int t, uint8_t* dst) {
+    const size_t rq = ((size_t)b * T + t) * H;
+    const int hh = lane >> 4, cc = lane & 15;
+    for (int i = wave; i < 2 * NQI + 1; i += 4) {
+      if (i < 2 * NQI) {
+        const int qi = i < NQI ? i : i - NQI;
+        const uint16_t* src = i < NQI ? q : dout;
+        const int hd = 4 * qi + hh;
+        const int c = cc ^ bw_swz(hd);
+        bw_dma(src + (rq + hd) * 128 + 8 * c, dst + (i < NQI ? 0 : QB) + 1024 * qi);
+      } else if (lane < H / 2) {
+        bw_dma(ldw + ((size_t)b * T + t) * 2 * H + 4 * lane, dst + 2 * QB);
+      }
+    }
+  };
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
+  bool touched = false;
+  const float sc2 = scale * kLog2e;
+  const int wsel = (j0 >> 5) + wave;  // the bitmap word of this wave's keys
+
+  auto compute = [&](const uint8_t* sb, int t) {
+    const int64_t pos = qp + t;
+    bool ok = key_in;
+    if (KIND == 0) {
+      ok = ok && wsel < nw && ((bm[((size_t)b * T + t) * nw + wsel] >> l32) & 1u);
+    } else if (KIND == 1) {
+      ok = ok && jw < n_visible(pos, ncb, m, rows_cap);
+    } else {
+      const int64_t p = rbase + jw;
+      ok = ok && p <= pos && p > pos - window;
+    }
+    if (!__ballot(ok)) return;
+    touched = true;
+    const float* lw = (const float*)(sb + 2 * QB);
+    f32x16 s_acc[NHH], p_acc[NHH];
+#pragma unroll
+    for (int hf = 0; hf < NHH; ++hf) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_acc[hf][r] = p_acc[hf][r] = 0.0f;
+      bf16x8 af[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) af[s] = *(const bf16x8*)(sb + hf * 32 * 256 + aofs[s]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        s_acc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], kf[s], s_acc[hf], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) af[s] = *(const bf16x8*)(sb + QB + hf * 32 * 256 + aofs[s]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        p_acc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], vf[s], p_acc[hf], 0, 0, 0);
+    }
+    // heads of register r: 32 hf + 8 (r / 4) + 4 h2 + r % 4
+    bf16x8 pb[NHH][2], db[NHH][2];
+    float msum = 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < NHH; ++hf)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *(const f32x4*)(lw + 32 * hf + 8 * g + 4 * h2);
+        const f32x4 d4 = *(const f32x4*)(lw + H + 32 * hf + 8 * g + 4 * h2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[hf][r], sc2, -l4[e]))
+                             : 0.0f;
+          msum += p;
+          pb[hf][r >> 3][r & 7] = (__bf16)p;
+          db[hf][r >> 3][r & 7] = (__bf16)(p * (p_acc[hf][r] - d4[e]));
+        }
+      }
+    if (KIND == 0 && attn_mass) {
+      msum += lane_xor32(msum);
+      if (ok && h2 == 0) {
+        const size_t wi = ((size_t)b * T + t) * nw + wsel;
+        const uint32_t below = bm[wi] & ((1u << l32) - 1u);
+        const uint32_t slot = rank[wi] + __popc(below);
+        if (slot < (uint32_t)topk) attn_mass[((size_t)b * T + t) * topk + slot] = msum;
+      }
+    }
+#pragma unroll
+    for (int hf = 0; hf < NHH; ++hf)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t ho = (uint32_t)(32 * hf + 16 * ks) * 256;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x2 o1 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + QB + ho + tofs[dt][0]));
+          const u32x2 o2 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + QB + ho + tofs[dt][1]));
+          const bf16x8 ot = __builtin_bit_cast(bf16x8, u32x4{o1[0], o1[1], o2[0], o2[1]});
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pb[hf][ks], dv[dt], 0, 0, 0);
+          const u32x2 q1 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + ho + tofs[dt][0]));
+          const u32x2 q2 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + ho + tofs[dt][1]));
+          const bf16x8 qt = __builtin_bit_cast(bf16x8, u32x4{q1[0], q1[1], q2[0], q2[1]});
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, db[hf][ks], dk[dt], 0, 0, 0);
+        }
+      }
+  };
+
+  stage(rows_s[0], st0);
+  for (int i = 0; i < n_rows; i += 2) {
+    bw_wait_loads();
+    __syncthreads();
+    if (i + 1 < n_rows) stage(rows_s[i + 1], st1);
+    compute(st0, rows_s[i]);
+    if (i + 1 >= n_rows) break;
+    bw_wait_loads();
+    __syncthreads();
+    if (i + 2 < n_rows) stage(rows_s[i + 2], st0);
+    compute(st1, rows_s[i + 1]);
+  }
+  if (!touched || !key_in) return;
+  // dK^T / dV^T: key jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4
+  float* gk = dkv + ((size_t)b * rows_cap + jw) * 256 + 4 * h2;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = 32 * dt + 8 * (r >> 2) + (r & 3);
+      atomicAdd(gk + d, scale * dk[dt][r]);
+      atomicAdd(gk + 128 + d, dv[dt][r]);
+    }
+}
+
+}  // namespace csa
+
+// ---------------------------------------------------------------- host side
+namespace csa_host {
+using namespace csa;
+
+// workspace: ldw [rows][2 H] (lse in log2 units | delta), dz [rows][H] (the
+// per-row sink terms), and for CSA the bitmap and word ranks [rows][nw]
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t attn_bwd_ws_bytes(int B, int T, int H, int Nc_cap, bool sparse) {
+  const size_t rows = (size_t)B * T;
+  size_t n = al256(rows * 2 * H * sizeof(float)) + al256(rows * H * sizeof(float));
+  if (sparse) n += 2 * al256(rows * (((size_t)Nc_cap + 31) / 32) * sizeof(uint32_t));
+  return n;
+}
+
+static int zero_grid(size_t n) {
+  const size_t g = (n / 4 + 255) / 256;
+  return (int)std::min<size_t>(std::max<size_t>(g, 1), 2048);
+}
+
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
+  const int rows = a.B * a.T;
+  const bool sparse = !a.dense;
+  const int nw = (a.Nc_cap + 31) / 32;
+  char* ws = (char*)a.ws;
+  float* ldw = (float*)ws;
+  ws += al256((size_t)rows * 2 * a.H * sizeof(float));
+  float* dz = (float*)ws;
+  ws += al256((size_t)rows * a.H * sizeof(float));
+  uint32_t* bm = nullptr;
+  uint32_t* rank = nullptr;
+  if (sparse) {
+    bm = (uint32_t*)ws;
+    rank = (uint32_t*)(ws + al256((size_t)rows * nw * sizeof(uint32_t)));
+  }
+  const size_t nc = (size_t)a.B * a.Nc_cap * 256, nr = (size_t)a.B * a.R_cap * 256;
+  if (nc) bwd_zero_kernel<<<zero_grid(nc), 256, 0, s>>>(a.dkv_cmp, nc);
+  if (nr) bwd_zero_kernel<<<zero_grid(nr), 256, 0, s>>>(a.dkv_raw, nr);
+  if (a.dsink) bwd_zero_kernel<<<1, 256, 0, s>>>(a.dsink, (size_t)a.H);
+  if (sparse && a.attn_mass && a.topk > 0)
+    bwd_zero_kernel<<<zero_grid((size_t)rows * a.topk), 256, 0, s>>>(a.attn_mass,
+                                                                     (size_t)rows * a.topk);
+  const uint16_t* q = (const uint16_t*)a.q;
+  const uint16_t* dout = (const uint16_t*)a.dout;
+  const uint16_t* kvc = (const uint16_t*)a.kv_cmp;
+  const uint16_t* kvr = (const uint16_t*)a.kv_raw;
+  float* dzp = a.dsink ? dz : nullptr;
+  if (sparse && a.topk > 0 && a.Nc_cap > 0)
+    bwd_bitmap_kernel<<<rows, 256, 0, s>>>(a.idx, a.topk, a.Nc_cap, nw, bm, rank);
+
+#define CSA_BWD_DQ(NHH_, DENSE_)                                                              \
+  attn_bwd_dq_kernel<NHH_, DENSE_><<<rows, 64 * NHH_, 0, s>>>(                                \
+      q, dout, a.lse, a.sink, kvc, a.idx, kvr, a.q_pos, a.raw_base, a.n_cmp, a.T, a.Nc_cap,   \
+      a.R_cap, sparse ? a.topk : 0, a.window, a.m, a.scale, a.dq, ldw, dzp)
+  if (a.H == 64) {
+    if (a.dense) CSA_BWD_DQ(2, true);
+    else CSA_BWD_DQ(2, false);
+  } else {
+    if (a.dense) CSA_BWD_DQ(1, true);
+    else CSA_BWD_DQ(1, false);
+  }
+#undef CSA_BWD_DQ
+  if (a.dsink) {
+    const int g = std::min(64, std::max(1, rows / 64));
+    if (a.H == 64) bwd_sink_kernel<64><<<g, 256, 0, s>>>(dz, rows, a.dsink);
+    else bwd_sink_kernel<32><<<g, 256, 0, s>>>(dz, rows, a.dsink);
+  }
+
+#define CSA_BWD_KV(NHH_, KIND_, KV_, CAP_, NCH_, DKV_)                                        \
+  attn_bwd_dkv_kernel<NHH_, KIND_><<<dim3((CAP_ + BW_KV_KEYS - 1) / BW_KV_KEYS, NCH_, a.B),  \
+                                     256, 0, s>>>(                                            \
+      q, dout, ldw, KV_, CAP_, bm, rank, nw, a.q_pos, a.raw_base, a.n_cmp, a.T, a.topk,       \
+      a.window, a.m, a.scale, DKV_, a.attn_mass)
+  const int ch_all = (a.T + BW_RC - 1) / BW_RC;
+  if (a.Nc_cap > 0 && (a.dense || (a.topk > 0))) {
+    if (a.H == 64) {
+      if (a.dense) CSA_BWD_KV(2, 1, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
+      else CSA_BWD_KV(2, 0, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
+    } else {
+      if (a.dense) CSA_BWD_KV(1, 1, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
+      else CSA_BWD_KV(1, 0, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
+    }
+  }
+  if (a.R_cap > 0 && a.window > 0) {
+    const int ch_w = std::min(ch_all, (BW_KV_KEYS + a.window - 1 + BW_RC - 1) / BW_RC);
+    if (a.H == 64) CSA_BWD_KV(2, 2, kvr, a.R_cap, ch_w, a.dkv_raw);
+    else CSA_BWD_KV(1, 2, kvr, a.R_cap, ch_w, a.dkv_raw);
+  }
+#undef CSA_BWD_KV
+  return hipGetLastError();
+}
+
+}  // namespace csa_host

@@ -133,6 +133,28 @@ __device__ __forceinline__ float sum_xor16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---------------------------------------------------------------- block scans
+// Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64);
+// returns the caller's offset and sets the block total.  sh: >= 16 words.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) base += sh[w];
+    tot += sh[w];
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
 // ---- paged compressed caches ---------------------------------------------
 // Logical entry j of sequence b lives in pool row
 //   (block_table[b * max_pages + j / 2^page_log2] * 2^page_log2) + j % 2^page_log2;
@@ -261,5 +283,30 @@ size_t noalloc_scratch_bytes();
 hipError_t noalloc_scratch(void** out);
 bool attn_supported(int B, int T, int H, int keys_per_row, bool sparse);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// Attention backward (bf16 inputs, D = 128, H in {32, 64}; fp32 gradients).
+struct AttnBwdArgs {
+  int B, T, H, topk, window, m, Nc_cap, R_cap;
+  bool dense;  // HCA: every visible entry instead of an index list
+  float scale;
+  const float* sink;
+  const int64_t* q_pos;
+  const int32_t* n_cmp;
+  const void* q;
+  const void* kv_cmp;
+  const int32_t* idx;
+  const void* kv_raw;
+  const int64_t* raw_base;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dkv_cmp;
+  float* dkv_raw;
+  float* dsink;
+  float* attn_mass;
+  void* ws;
+};
+size_t attn_bwd_ws_bytes(int B, int T, int H, int Nc_cap, bool sparse);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 
 }  // namespace csa_host

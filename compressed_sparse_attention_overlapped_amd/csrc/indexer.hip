@@ -44,28 +44,6 @@ __device__ __forceinline__ void hist_flush(const uint32_t* lhist, uint32_t* ghis
   }
 }
 
-// ---------------------------------------------------------------- block scans
-// Exclusive prefix sum over the block (blockDim.x <= 1024, a multiple of 64);
-// returns the caller's offset and sets the block total.  sh: >= 16 words.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) base += sh[w];
-    tot += sh[w];
-  }
-  __syncthreads();
-  total = tot;
-  return base + x - v;
-}
-
 // Threshold bin of a row from its histogram: the bin where the count from the
 // top first reaches `need` (1 <= need <= total).  256 threads; each owns 8
 // consecutive bins from the top.  Returns the bin in every thread.

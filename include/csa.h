@@ -435,6 +435,65 @@ csa_status_t csa_sparse_attn_varlen(int n, int total, int max_len, int H, int D,
                                     hipStream_t stream);
 size_t csa_sparse_attn_varlen_workspace_size(int total, int H, int D, int topk, int window);
 
+/*
+ * ---- training: backward passes ----------------------------------------------
+ * The migration page (sections 1 and 3.2) places the training path of
+ * CompressedSparseAttention in scope: its backward, the indexer loss and a
+ * fused "sparse lightning indexer grad + KL loss" operator.  The gradients
+ * below are those of the forward definitions above (chain rule); the call
+ * recomputes the attention probabilities from the forward's lse, and delta
+ * as sum_j P_j dP_j (equal to dout . out, without the rounding of a stored
+ * output).
+ *
+ * Gradients of csa_sparse_attn for an upstream gradient dout of out.  Per
+ * query token and head, over the forward's key set J:
+ *     P_j = exp(l_j - lse),  dP_j = dout . V_j,  delta = sum_j P_j dP_j,
+ *     dS_j = P_j (dP_j - delta),
+ *     dq = scale sum_j dS_j K_j,  dK_j += scale dS_j q,  dV_j += P_j dout,
+ *     dsink[h] = -sum over tokens of exp(sink[h] - lse) delta.
+ *  q, dout  bf16 [B, T, H, D];  lse fp32 [B, T, H] (the forward's)
+ *  kv_cmp, idx, kv_raw, raw_base, q_pos, sink, scale, window: as in the forward
+ *  dq        fp32 [B, T, H, D] (written)
+ *  dkv_cmp   fp32 [B, Nc_cap, 2 D] = [dK | dV] per compressed row (written in
+ *            full; rows no token attends get 0); dkv_raw fp32 [B, R_cap, 2 D]
+ *  dsink     fp32 [H] or NULL (needs sink)
+ *  attn_mass fp32 [B, T, topk] or NULL: per slot, the attention probability
+ *            of its entry summed over heads (0 in skipped slots), the target
+ *            of csa_indexer_kl_bwd
+ * Each row of idx must name an entry at most once (csa_indexer_topk's rows
+ * do; the forward attends a repeated entry twice, this call once), and
+ * attn_mass assumes the valid indices of a row ascend before its -1 pads, as
+ * csa_indexer_topk writes them.  Supported: dt BF16, D = 128, H in {32, 64},
+ * topk <= 4096, Nc_cap <= 65536, R_cap <= 2^23, 16-byte aligned tensors.
+ * Workspace: csa_sparse_attn_bwd_workspace_size() bytes (contents on entry do
+ * not matter).  The gradients of keys shared by many rows are summed with
+ * fp32 atomics, so their rounding order, and their last bits, vary from run
+ * to run.
+ */
+csa_status_t csa_sparse_attn_bwd(int B, int T, int H, int D, int topk, int window, float scale,
+                                 const float* sink, const int64_t* q_pos, const void* q,
+                                 const void* kv_cmp, int Nc_cap, const int32_t* idx,
+                                 const void* kv_raw, int R_cap, const int64_t* raw_base,
+                                 csa_dtype_t dt, const float* lse, const void* dout, float* dq,
+                                 float* dkv_cmp, float* dkv_raw, float* dsink, float* attn_mass,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t csa_sparse_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap);
+
+/*
+ * Gradients of hca_dense_attn (the compressed part of J is every visible
+ * entry j < n_vis(t)); arguments, outputs and limits as in
+ * csa_sparse_attn_bwd without idx and attn_mass (Nc_cap <= 2^23).
+ * Workspace: hca_dense_attn_bwd_workspace_size() bytes.
+ */
+csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, float scale,
+                                const float* sink, const int64_t* q_pos, const int32_t* n_cmp,
+                                const void* q, const void* kv_cmp, int Nc_cap, const void* kv_raw,
+                                int R_cap, const int64_t* raw_base, csa_dtype_t dt,
+                                const float* lse, const void* dout, float* dq, float* dkv_cmp,
+                                float* dkv_raw, float* dsink, void* workspace, size_t ws_bytes,
+                                hipStream_t stream);
+size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H);
+
 /* Static text of a status code. */
 const char* csa_status_string(csa_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -1,0 +1,208 @@
+"""GPU parity of the attention backward (csa_sparse_attn_bwd, hca_dense_attn_bwd)
+against the CPU oracle's gradients.
+
+The device gradients use bf16 operands for P and dS (as the forward uses
+bf16 for P) with fp32 accumulation; delta = sum_j P_j dP_j is summed in fp32.  Tolerance, per row of a gradient (one head of one query for dq,
+one cache row for dK / dV): max |gpu - oracle| <= GRAD_TOL * max |oracle row|
+(GRAD_TOL = 1e-2: the bf16 operands P and dS carry 2^-9 relative rounding
+each and their products 2^-8, while every row sums many such terms of either
+sign, so the row error stays near 2^-8 of the row's scale; the cases here
+measure at most 4.7e-3).  attn_mass (a sum of 64 fp32
+probabilities, no bf16 rounding on its path): |gpu - oracle| <= 1e-4 + 1e-4 r.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_attention_overlapped_amd as csa
+from compressed_sparse_attention_overlapped_amd import inputs as gen
+from oracle import oracle as orc
+from tests import brute
+from tests.helpers import dev_i32, dev_i64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GRAD_TOL = 1e-2
+
+
+def _n_vis(pos, ncmp, m, cap):
+    return max(0, min(ncmp, (pos + 1) // m, cap))
+
+
+def _rows_rel(gpu, ref, what, tol=GRAD_TOL):
+    """Row-relative check with a floor: a row whose exact gradient vanishes
+    (a token that sees one key: P = 1 and dP = delta) is compared against
+    1e-3 of the tensor's largest row, the size of the rounding noise that
+    the two fp32 sums dP and delta leave."""
+    g = np.asarray(gpu, np.float64).reshape(-1, np.asarray(gpu).shape[-1])
+    r = np.asarray(ref, np.float64).reshape(-1, g.shape[-1])
+    assert np.isfinite(g).all(), what + ": non-finite gradient"
+    err = np.abs(g - r).max(axis=1)
+    scale = np.maximum(np.abs(r).max(axis=1), 1e-3 * np.abs(r).max())
+    rel = err / np.maximum(scale, 1e-30)
+    worst = np.argsort(-rel)[:3]
+    print("%s: worst row-relative error %.3e over %d rows; worst rows %s (err %s, scale %s)"
+          % (what, rel.max(), rel.size, worst.tolist(), err[worst].tolist(),
+             np.abs(r).max(axis=1)[worst].tolist()))
+    bad = rel > tol
+    assert not bad.any(), "%s: %d rows over %.1e; worst %.3e (row %d)" % (
+        what, bad.sum(), tol, rel.max(), int(np.argmax(rel)))
+
+
+def _dec(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _sink_vec(d, H):
+    z = (d.normal(H) * 2.0).float()
+    z[0] = -math.inf          # no sink for head 0
+    z[1] = 12.0               # a sink above every logit
+    return z
+
+
+def _run_sparse(d, B, T, H, Nc, R, topk, W, q_pos, raw_base, sink=False, pad=0.2):
+    D = 128
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    dout = gen.store(d.normal(B, T, H, D), gen.BF16)
+    nv = torch.tensor([[_n_vis(q_pos[b] + t, Nc, 4, Nc) for t in range(T)] for b in range(B)])
+    idx = gen.random_index_sets(d, B, T, topk, nv, pad)
+    z = _sink_vec(d, H) if sink else None
+    zd = z.to(DEV) if sink else None
+    args = (q.to(DEV), kv_cmp.to(DEV), idx.to(DEV), kv_raw.to(DEV), W, dev_i64(q_pos),
+            dev_i64(raw_base))
+    out, lse = csa.csa_sparse_attn(*args, want_lse=True, sink=zd)
+    dq, dkc, dkr, ds, mass = csa.csa_sparse_attn_bwd(*args, lse, dout.to(DEV), sink=zd,
+                                                     want_mass=True)
+    torch.cuda.synchronize()
+    host = dict(q=gen.host_bits(q), kv_cmp=gen.host_bits(kv_cmp), kv_raw=gen.host_bits(kv_raw),
+                idx=idx.numpy(), dout=_dec(dout), sink=None if z is None else z.double().numpy())
+    return (dq, dkc, dkr, ds, mass), host
+
+
+@pytest.mark.parametrize("H,sink", [(64, False), (64, True), (32, False)])
+def test_csa_attn_bwd_ragged_matches_oracle(H, sink):
+    # ragged everywhere: 77 rows (two 64-row chunks), 150 entries and 260 raw
+    # rows (partial 128-key tiles), rows with no compressed entry, a sequence
+    # whose early window rows are absent, padded index rows
+    d = gen.Draw(500 + H + 7 * sink)
+    B, T, Nc, R, topk, W = 2, 77, 150, 260, 40, 45
+    q_pos, raw_base = [0, 480], [0, 470]
+    (dq, dkc, dkr, ds, mass), h = _run_sparse(d, B, T, H, Nc, R, topk, W, q_pos, raw_base, sink)
+    rq, rc, rr, rs, rm = orc.attn_bwd(h["q"], h["kv_cmp"], h["idx"], h["kv_raw"], W, q_pos,
+                                      raw_base, h["dout"], sink=h["sink"], want_mass=True)
+    _rows_rel(_dec(dq), rq, "dq H=%d" % H)
+    _rows_rel(_dec(dkc), rc, "dkv_cmp H=%d" % H)
+    _rows_rel(_dec(dkr), rr, "dkv_raw H=%d" % H)
+    m = _dec(mass)
+    assert np.all(np.abs(m - rm) <= 1e-4 + 1e-4 * np.abs(rm)), np.abs(m - rm).max()
+    # rows no token attends stay exactly zero
+    assert (_dec(dkc)[rc == 0] == 0).all() and (_dec(dkr)[rr == 0] == 0).all()
+    if sink:
+        g = _dec(ds)
+        np.testing.assert_allclose(g, rs, rtol=GRAD_TOL, atol=GRAD_TOL * np.abs(rs).max())
+        assert g[0] == 0  # head 0 has no sink
+
+
+def test_csa_attn_bwd_window_only_and_empty_rows():
+    # topk = 0 (the sliding-window layer) and a second call with every index
+    # slot padded: both reduce to the window's gradients
+    d = gen.Draw(520)
+    B, T, H, Nc, R, W = 1, 70, 64, 40, 70, 30
+    for topk, pad in ((0, 0.0), (16, 1.0)):
+        (dq, dkc, dkr, _, _), h = _run_sparse(d, B, T, H, Nc, R, topk, W, [0], [0], pad=pad)
+        rq, rc, rr, _, _ = orc.attn_bwd(h["q"], h["kv_cmp"], h["idx"], h["kv_raw"], W, 0, 0,
+                                        h["dout"])
+        _rows_rel(_dec(dq), rq, "dq topk=%d" % topk)
+        _rows_rel(_dec(dkr), rr, "dkv_raw topk=%d" % topk)
+        assert (_dec(dkc) == 0).all()
+
+
+@pytest.mark.parametrize("H", [64, 32])
+def test_hca_attn_bwd_matches_oracle(H):
+    d = gen.Draw(530 + H)
+    B, T, D, m, Nc, R, W = 2, 90, 128, 4, 300, 200, 37
+    q_pos, n_cmp, raw_base = [300, 0], [Nc, 17], [250, 0]
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    dout = gen.store(d.normal(B, T, H, D), gen.BF16)
+    z = _sink_vec(d, H).to(DEV)
+    args = (q.to(DEV), kv_cmp.to(DEV), kv_raw.to(DEV), m, W, dev_i64(q_pos), dev_i32(n_cmp),
+            dev_i64(raw_base))
+    out, lse = csa.hca_dense_attn(*args, want_lse=True, sink=z)
+    dq, dkc, dkr, ds = csa.hca_dense_attn_bwd(*args, lse, dout.to(DEV), sink=z)
+    torch.cuda.synchronize()
+    rq, rc, rr, rs, _ = orc.attn_bwd(gen.host_bits(q), gen.host_bits(kv_cmp), None,
+                                     gen.host_bits(kv_raw), W, q_pos, raw_base, _dec(dout),
+                                     sink=z.double().cpu().numpy(), m=m, n_cmp=n_cmp)
+    _rows_rel(_dec(dq), rq, "hca dq H=%d" % H)
+    _rows_rel(_dec(dkc), rc, "hca dkv_cmp H=%d" % H)
+    _rows_rel(_dec(dkr), rr, "hca dkv_raw H=%d" % H)
+    np.testing.assert_allclose(_dec(ds), rs, rtol=GRAD_TOL, atol=GRAD_TOL * np.abs(rs).max())
+
+
+def test_csa_attn_bwd_full_8k_prefill():
+    # the 8K prefill shape (T = 8192, H = 64, topk = 512, W = 512, 2048
+    # entries): dq and attention mass of sampled rows (every row index mod 64,
+    # the dK/dV row chunk, and both ends), dK/dV of the entries and raw rows
+    # that only the last 40 rows attend (exact from those rows), and for the
+    # whole call the identities sum dV = sum dout, sum dK = 0 (no sink) and
+    # sum q . dq = sum K . dK
+    w = gen.WORKLOADS["csa_prefill_8k_bf16"]
+    d = gen.Draw(540, DEV)
+    T, H, D, Nc, topk, W = w.T, w.H, w.D, w.n_cmp, w.topk, w.window
+    q = gen.store(d.normal(1, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(1, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(1, T, 2 * D), gen.BF16)
+    dout = gen.store(d.normal(1, T, H, D), gen.BF16)
+    t = torch.arange(T, device=DEV)
+    nv = torch.clamp((t + 1) // 4, max=Nc)
+    sc = torch.rand(T, Nc, device=DEV, generator=d.g)
+    sc[torch.arange(Nc, device=DEV)[None, :] >= nv[:, None]] = -1
+    top = sc.topk(topk, dim=1)
+    big = torch.full_like(top.indices, 1 << 30)
+    idx = torch.where(top.values >= 0, top.indices, big).sort(dim=1).values
+    idx = torch.where(idx == (1 << 30), torch.full_like(idx, -1), idx).to(torch.int32)
+    idx = idx.view(1, T, topk).contiguous()
+    zero = dev_i64([0])
+    out, lse = csa.csa_sparse_attn(q, kv_cmp, idx, kv_raw, W, zero, zero, want_lse=True)
+    dq, dkc, dkr, _, mass = csa.csa_sparse_attn_bwd(q, kv_cmp, idx, kv_raw, W, zero, zero, lse,
+                                                    dout, want_mass=True)
+    torch.cuda.synchronize()
+    hq, hc, hr = gen.host_bits(q), gen.host_bits(kv_cmp), gen.host_bits(kv_raw)
+    hi, hd = idx.cpu().numpy(), _dec(dout)
+    rows = sorted(set([0, 1, 63, 64, 4095, 4096] + list(range(5, T, 131)) + [T - 1]))
+    rows = sorted(set(rows + [64 * k + (k % 64) for k in range(T // 64)][::2]))
+    gq, gm = _dec(dq), _dec(mass)
+    for i in range(0, len(rows), 48):
+        part = rows[i:i + 48]
+        rq = np.zeros((1, len(part), H, D))
+        rm = np.zeros((1, len(part), topk))
+        for k, r in enumerate(part):
+            a, _, _, _, b = orc.attn_bwd(hq[:, r:r + 1], hc, hi[:, r:r + 1], hr, W, r, 0,
+                                         hd[:, r:r + 1], want_mass=True)
+            rq[:, k], rm[:, k] = a[:, 0], b[:, 0]
+        _rows_rel(gq[:, part], rq, "8k dq rows %d..%d" % (part[0], part[-1]))
+        assert np.all(np.abs(gm[:, part] - rm) <= 1e-4 + 1e-4 * np.abs(rm))
+    t0 = T - 40
+    _, rc, rr, _, _ = orc.attn_bwd(hq[:, t0:], hc, hi[:, t0:], hr, W, t0, 0, hd[:, t0:])
+    jc = (t0 + 1) // 4 + 1          # entries no row before t0 can see
+    _rows_rel(_dec(dkc)[0, jc:], rc[0, jc:], "8k dkv_cmp tail entries")
+    _rows_rel(_dec(dkr)[0, t0:], rr[0, t0:], "8k dkv_raw tail rows")
+    # identities over the whole call (fp32 sums of fp32 gradients)
+    gc, gr = _dec(dkc), _dec(dkr)
+    sdv = gc[0, :, D:].sum(0) + gr[0, :, D:].sum(0)
+    sdo = hd[0].sum((0, 1))
+    e_dv = np.abs(sdv - sdo).max() / np.abs(sdo).max()
+    sdk = gc[0, :, :D].sum(0) + gr[0, :, :D].sum(0)
+    e_dk = np.abs(sdk).max() / (np.abs(gc[0, :, :D]).sum(0) + np.abs(gr[0, :, :D]).sum(0)).max()
+    qv, kc, kr = brute.decode_bits(hq), brute.decode_bits(hc), brute.decode_bits(hr)
+    lhs = (qv * gq).sum()
+    rhs = (kc[0, :, :D] * gc[0, :, :D]).sum() + (kr[0, :, :D] * gr[0, :, :D]).sum()
+    e_bl = abs(lhs - rhs) / np.abs(qv * gq).sum()
+    print("8k identities: sum dV %.2e, sum dK %.2e, q.dq vs K.dK %.2e" % (e_dv, e_dk, e_bl))
+    assert e_dv <= 1e-2 and e_dk <= 1e-2 and e_bl <= 1e-2
