@@ -19,7 +19,7 @@ import torch
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
            "csa_indexer_topk_varlen", "csa_sparse_attn_varlen", "csa_sparse_attn_bwd",
-           "hca_dense_attn_bwd",
+           "hca_dense_attn_bwd", "csa_indexer_kl_bwd",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
            "CsaError", "PageTable", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
@@ -151,6 +151,10 @@ def lib():
         L.hca_dense_attn_bwd.restype = C.c_int
         L.hca_dense_attn_bwd_workspace_size.argtypes = [i32] * 3
         L.hca_dense_attn_bwd_workspace_size.restype = C.c_size_t
+        L.csa_indexer_kl_bwd.argtypes = [i32] * 6 + [vp, vp, vp, i32] + [vp] * 7 + [vp, sz, vp]
+        L.csa_indexer_kl_bwd.restype = C.c_int
+        L.csa_indexer_kl_bwd_workspace_size.argtypes = [i32] * 4
+        L.csa_indexer_kl_bwd_workspace_size.restype = C.c_size_t
         L.csa_status_string.argtypes = [i32]
         L.csa_status_string.restype = C.c_char_p
         L.csa_last_error.argtypes = []
@@ -460,6 +464,31 @@ def hca_dense_attn_bwd(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, lse
                                   _p(dkv_cmp), _p(dkv_raw), _p(dsink), _p(ws), nb, _stream(q))
     _check("hca_dense_attn_bwd", rc)
     return dq, dkv_cmp, dkv_raw, dsink
+
+
+def csa_indexer_kl_bwd(q_idx, w_idx, k_idx, idx, attn_mass, grad_scale=None, loss=None,
+                       dq_idx=None, dw_idx=None, dk_idx=None, workspace=None):
+    """Indexer KL loss per query row and its gradients (bf16 q_idx
+    [B, T, 16, 64], k_idx [B, Nc_cap, 64]; w_idx f32 [B, T, 16]; idx and
+    attn_mass [B, T, topk] from csa_indexer_topk and csa_sparse_attn_bwd;
+    grad_scale f32 [B, T] or None).  Returns (loss, dq_idx, dw_idx, dk_idx),
+    all float32."""
+    _dense(q_idx, w_idx, k_idx, idx, attn_mass, grad_scale)
+    B, T, H_I, d_I = q_idx.shape
+    Nc_cap, topk = k_idx.shape[1], idx.shape[2]
+    f32 = dict(dtype=torch.float32, device=q_idx.device)
+    loss = torch.empty(B, T, **f32) if loss is None else loss
+    dq_idx = torch.empty(B, T, H_I, d_I, **f32) if dq_idx is None else dq_idx
+    dw_idx = torch.empty(B, T, H_I, **f32) if dw_idx is None else dw_idx
+    dk_idx = torch.empty(B, Nc_cap, d_I, **f32) if dk_idx is None else dk_idx
+    ws, nb = _workspace(lib().csa_indexer_kl_bwd_workspace_size(B, T, Nc_cap, topk), q_idx,
+                        workspace)
+    rc = lib().csa_indexer_kl_bwd(B, T, H_I, d_I, Nc_cap, topk, _p(q_idx), _p(w_idx), _p(k_idx),
+                                  _DT[q_idx.dtype], _p(idx), _p(attn_mass), _p(grad_scale),
+                                  _p(loss), _p(dq_idx), _p(dw_idx), _p(dk_idx), _p(ws), nb,
+                                  _stream(q_idx))
+    _check("csa_indexer_kl_bwd", rc)
+    return loss, dq_idx, dw_idx, dk_idx
 
 
 # ---------------------------------------------------------------- packed sequences

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_bwd.hip"]
+SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_bwd.hip", "indexer_bwd.hip"]
 # Per-source extra flags.  attend.hip and indexer.hip keep their MFMA
 # accumulators in VGPRs: the attention loops rescale the output accumulator
 # conditionally and the score epilogues read every accumulator element, and

@@ -676,3 +676,37 @@ csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, f
                           dkv_cmp, dkv_raw, dsink,  nullptr, workspace};
   return attn_bwd_impl("hca_dense_attn_bwd", a, D, dt, ws_bytes, stream);
 }
+
+size_t csa_indexer_kl_bwd_workspace_size(int B, int T, int Nc_cap, int topk) {
+  if (B <= 0 || T <= 0 || Nc_cap < 0 || topk < 0) return 0;
+  return csa_host::indexer_kl_ws_bytes(B, T, Nc_cap, topk);
+}
+
+csa_status_t csa_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int topk,
+                                const void* q_idx, const float* w_idx, const void* k_idx,
+                                csa_dtype_t qk_dt, const int32_t* idx, const float* attn_mass,
+                                const float* grad_scale, float* loss, float* dq_idx,
+                                float* dw_idx, float* dk_idx, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  const char* fn = "csa_indexer_kl_bwd";
+  if (B <= 0 || T <= 0 || H_I <= 0 || d_I <= 0 || Nc_cap < 0 || topk < 0)
+    return fail(CSA_E_ARG, "%s: B, T, H_I, d_I must be > 0; Nc_cap, topk >= 0", fn);
+  if (!q_idx || !w_idx || !loss || !dq_idx || !dw_idx || (topk > 0 && (!idx || !attn_mass)) ||
+      (Nc_cap > 0 && (!k_idx || !dk_idx)))
+    return fail(CSA_E_ARG, "%s: missing required pointer", fn);
+  if (qk_dt != CSA_DT_BF16) return fail(CSA_E_UNSUPPORTED, "%s: qk_dt must be BF16", fn);
+  if (H_I != 16 || d_I != 64) return fail(CSA_E_UNSUPPORTED, "%s: needs H_I = 16, d_I = 64", fn);
+  if (topk > 1024) return fail(CSA_E_UNSUPPORTED, "%s: topk > 1024", fn);
+  if (Nc_cap > 65536) return fail(CSA_E_UNSUPPORTED, "%s: Nc_cap > 65536", fn);
+  if ((T + 63) / 64 > 65535 || B > 65535)
+    return fail(CSA_E_UNSUPPORTED, "%s: T <= 65535 * 64 and B <= 65535", fn);
+  if (!aligned16(q_idx) || (k_idx && !aligned16(k_idx)) || !aligned16(w_idx) ||
+      !aligned16(dq_idx))
+    return fail(CSA_E_UNSUPPORTED, "%s: q_idx, k_idx, w_idx and dq_idx must be 16-byte aligned", fn);
+  const size_t need = csa_host::indexer_kl_ws_bytes(B, T, Nc_cap, topk);
+  if (ws_bytes < need || !workspace)
+    return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  csa_host::IndexerKlArgs a{B,          T,    Nc_cap, topk,   q_idx,  w_idx, k_idx, idx,
+                            attn_mass,  grad_scale, loss, dq_idx, dw_idx, dk_idx, workspace};
+  return hip_status(csa_host::launch_indexer_kl_bwd(a, stream), fn);
+}

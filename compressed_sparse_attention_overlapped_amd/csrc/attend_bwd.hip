@@ -625,6 +625,17 @@ static int zero_grid(size_t n) {
   return (int)std::min<size_t>(std::max<size_t>(g, 1), 2048);
 }
 
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s) {
+  if (n) bwd_zero_kernel<<<zero_grid(n), 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_sel_bitmap(const int32_t* idx, int rows, int topk, int Nc_cap, uint32_t* bm,
+                             uint32_t* rank, hipStream_t s) {
+  bwd_bitmap_kernel<<<rows, 256, 0, s>>>(idx, topk, Nc_cap, (Nc_cap + 31) / 32, bm, rank);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   const int rows = a.B * a.T;
   const bool sparse = !a.dense;

@@ -308,5 +308,27 @@ struct AttnBwdArgs {
 };
 size_t attn_bwd_ws_bytes(int B, int T, int H, int Nc_cap, bool sparse);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
+// helpers shared by the backward passes
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
+hipError_t launch_sel_bitmap(const int32_t* idx, int rows, int topk, int Nc_cap, uint32_t* bm,
+                             uint32_t* rank, hipStream_t s);
+
+// Indexer KL loss and gradients (bf16, H_I = 16, d_I = 64).
+struct IndexerKlArgs {
+  int B, T, Nc_cap, topk;
+  const void* q_idx;
+  const float* w_idx;
+  const void* k_idx;
+  const int32_t* idx;
+  const float* mass;
+  const float* grad_scale;
+  float* loss;
+  float* dq_idx;
+  float* dw_idx;
+  float* dk_idx;
+  void* ws;
+};
+size_t indexer_kl_ws_bytes(int B, int T, int Nc_cap, int topk);
+hipError_t launch_indexer_kl_bwd(const IndexerKlArgs& a, hipStream_t s);
 
 }  // namespace csa_host

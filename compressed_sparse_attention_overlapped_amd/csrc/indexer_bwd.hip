@@ -1,0 +1,428 @@
+// Indexer KL loss and its gradients for gfx950 (bf16 queries and keys,
+// H_I = 16, d_I = 64).
+//
+// The migration page (sections 1 and 3.2) names an indexer loss for training
+// and a fused sparse "lightning indexer grad + KL loss" operator; section 4.3
+// gives a loss coefficient and a sparse-loss switch.  The loss's formula is
+// not on the pages; the reading used here (sparse form): per query token,
+// over its selected entries S, the target p is the main attention's
+// probability mass per entry summed over heads and normalised over S, the
+// indexer's distribution is the softmax over S of its scores
+// I_k = sum_h w_h ReLU(q_h . k_j), and the loss is KL(p || softmax(I)).
+// With g the row's gradient scale, dI_k = g (softmax(I)_k - p_k) and
+//   dw[h] = sum_k dI_k ReLU(v_hk),  dq[h] = sum_k dI_k w_h [v_hk > 0] k_j,
+//   dk[j] += sum_h dI_k w_h [v_hk > 0] q_h.
+//
+// Two kernels.  A row kernel (one workgroup per query token) computes the
+// selected entries' scores on the 16x16x32 MFMA (heads x entries, the keys
+// gathered straight from global memory), the loss, dI, dw and dq (dq^T =
+// K_sel^T C^T on the MFMA, the selected key rows staged in LDS 256 at a time).
+// A key-major kernel sums dk over the rows that select each entry (a
+// workgroup owns 128 entries, pairs of query rows are 32 MFMA rows of
+// heads), so no per-(row, entry) atomics are needed.
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+
+namespace csa {
+
+constexpr int KL_HI = 16, KL_DI = 64;
+constexpr int KL_TOPK_MAX = 1024;
+constexpr int KL_TILES_W = KL_TOPK_MAX / 16 / 4;  // 16-slot tiles per wave
+constexpr int KL_CH = 256;                        // slots per dq chunk
+constexpr int KL_RC = 64;                         // query rows per dk workgroup
+
+typedef __attribute__((ext_vector_type(4))) short kl_s16x4;
+__device__ __forceinline__ kl_s16x4 kl_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) kl_s16x4*)p);
+}
+__device__ __forceinline__ void kl_dma(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void kl_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// block reductions over 256 threads (sh: >= 8 floats; ends with a barrier)
+__device__ __forceinline__ float kl_block_max(float v, float* sh) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  __syncthreads();
+  return v;
+}
+__device__ __forceinline__ float kl_block_sum(float v, float* sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  __syncthreads();
+  return v;
+}
+
+// ---------------------------------------------------------------- row kernel
+// Slot tile u (16 slots) belongs to wave u % 4; lane l holds slot 16 u + l % 16
+// and, after the MFMA, v of heads 4 (l / 16) .. + 3 for it.
+__global__ void __launch_bounds__(256) idx_kl_row_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ idx,
+    const float* __restrict__ mass, const float* __restrict__ gscale, int T, int Nc_cap, int topk,
+    float* __restrict__ loss, float* __restrict__ dq_idx, float* __restrict__ dw_idx,
+    float* __restrict__ dIw) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[KL_CH * 128];  // key rows of a chunk
+  __shared__ __attribute__((aligned(16))) uint16_t cs[KL_HI][KL_CH];  // C^T of a chunk (bf16)
+  __shared__ float sh[8];
+  __shared__ float dws[4][KL_HI];
+  const int row = blockIdx.x, b = row / T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int ntile = (topk + 15) / 16;
+  const uint16_t* kb = k_idx + (size_t)b * Nc_cap * KL_DI;
+  // A operands: head l16, dims 32 s + 8 g4 .. + 8
+  bf16x8 qa[2];
+  {
+    const uint16_t* qr = q_idx + ((size_t)row * KL_HI + l16) * KL_DI + 8 * g4;
+    qa[0] = *(const bf16x8*)qr;
+    qa[1] = *(const bf16x8*)(qr + 32);
+  }
+  float wq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wq[i] = w_idx[(size_t)row * KL_HI + 4 * g4 + i];
+  const int32_t* ir = idx + (size_t)row * topk;
+
+  // scores of this wave's tiles
+  float v[KL_TILES_W][4];
+  float sc[KL_TILES_W];
+  int jv[KL_TILES_W];
+  float imax = -INFINITY, msum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KL_TILES_W; ++i) {
+    const int u = wave + 4 * i;
+    const int k = 16 * u + l16;
+    int j = -1;
+    if (u < ntile && k < topk) j = ir[k];
+    if (j >= Nc_cap) j = -1;
+    jv[i] = j;
+    sc[i] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[i][e] = 0.0f;
+    if (u < ntile) {  // uniform
+      const uint16_t* kr = kb + (size_t)(j >= 0 ? j : 0) * KL_DI + 8 * g4;
+      const bf16x8 k0 = *(const bf16x8*)kr, k1 = *(const bf16x8*)(kr + 32);
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], k0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], k1, acc, 0, 0, 0);
+      float p = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[i][e] = acc[e];
+        p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
+      }
+      p += lane_xor16(p);
+      p += lane_xor32(p);
+      if (j >= 0) {
+        sc[i] = p;
+        imax = fmaxf(imax, p);
+        if (g4 == 0) msum += mass[(size_t)row * topk + k];
+      }
+    }
+  }
+  imax = kl_block_max(imax, sh);
+  msum = kl_block_sum(msum, sh);
+  float zs = 0.0f;
+  if (imax > -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < KL_TILES_W; ++i)
+      if (jv[i] >= 0 && g4 == 0) zs += __expf(sc[i] - imax);
+  }
+  zs = kl_block_sum(zs, sh);
+  const bool live = imax > -INFINITY && msum > 0.0f;  // uniform
+  const float lz = live ? imax + __logf(zs) : 0.0f;
+  const float g = gscale ? gscale[row] : 1.0f;
+  // dI, the loss and dw
+  float dI[KL_TILES_W];
+  float kl = 0.0f, dwp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < KL_TILES_W; ++i) {
+    const int u = wave + 4 * i;
+    const int k = 16 * u + l16;
+    dI[i] = 0.0f;
+    if (live && jv[i] >= 0) {
+      const float p = mass[(size_t)row * topk + k] / msum;
+      const float lq = sc[i] - lz;
+      if (g4 == 0 && p > 0.0f) kl += p * (__logf(p) - lq);
+      dI[i] = g * (__expf(lq) - p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dwp[e] = fmaf(dI[i], fmaxf(v[i][e], 0.0f), dwp[e]);
+    }
+    if (u < ntile && g4 == 0 && k < topk) dIw[(size_t)row * topk + k] = dI[i];
+  }
+  kl = kl_block_sum(kl, sh);
+  if (tid == 0) loss[row] = live ? kl : 0.0f;
+  // dw: sum over the 16 slot lanes of each head group, then over the waves
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = dwp[e];
+    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+    dwp[e] = x;
+  }
+  if (l16 == 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dws[wave][4 * g4 + e] = dwp[e];
+  __syncthreads();
+  if (tid < KL_HI) dw_idx[(size_t)row * KL_HI + tid] = dws[0][tid] + dws[1][tid] + dws[2][tid] + dws[3][tid];
+
+  // dq^T (64 dims x 16 heads) = K_sel^T C^T over chunks of 256 slots; wave w
+  // owns dims 16 w .. 16 w + 15.  A: the transposing reads of the chunk's
+  // key rows (lane l16: dim 16 w + l16; slots 8 g4 + 32 step ..); B: C^T
+  // (lane l16: head, the same slots).
+  f32x4 dqa = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < ntile * 16; c0 += KL_CH) {
+    // stage the chunk's key rows (row r of the chunk at 128 r) and C^T
+    for (int r = tid; r < KL_CH; r += 256) {
+      const int k = c0 + r;
+      int j = k < topk ? ir[k] : -1;
+      if (j >= Nc_cap) j = -1;
+      const u32x4* src = (const u32x4*)(kb + (size_t)(j >= 0 ? j : 0) * KL_DI);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        ((u32x4*)(ks + 128 * r))[c] = j >= 0 ? src[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    // slots past the last tile: zero (their key rows are zero too)
+    if (c0 + tid >= ntile * 16)
+#pragma unroll
+      for (int h = 0; h < KL_HI; ++h) cs[h][tid] = 0;
+#pragma unroll
+    for (int i = 0; i < KL_TILES_W; ++i) {
+      const int u = wave + 4 * i;
+      const int k = 16 * u + l16;
+      if (k >= c0 && k < c0 + KL_CH) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float c = v[i][e] > 0.0f ? dI[i] * wq[e] : 0.0f;
+          cs[4 * g4 + e][k - c0] = f32_to_bf16(c);
+        }
+      }
+    }
+    __syncthreads();
+    const int nst = (min(KL_CH, ntile * 16 - c0) + 31) / 32;  // 32-slot steps in the chunk
+    for (int st = 0; st < nst; ++st) {
+      // lane jj of 16-lane group gg reads slot rows 32 st + 8 gg + 4 e + jj / 4,
+      // dims 16 w + 4 (jj & 3) .. + 4; after the transpose lane l holds dim
+      // 16 w + l16 of slots 32 st + 8 g4 + 4 e .. + 4
+      bf16x8 ka;
+      {
+        const int jj = lane & 15, gg = lane >> 4;
+        u32x2 t[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 32 * st + 8 * gg + 4 * e + (jj >> 2);
+          t[e] = __builtin_bit_cast(u32x2, kl_read_tr16(ks + 128 * r + 2 * (16 * wave + 4 * (jj & 3))));
+        }
+        ka = __builtin_bit_cast(bf16x8, u32x4{t[0][0], t[0][1], t[1][0], t[1][1]});
+      }
+      const bf16x8 cb = *(const bf16x8*)&cs[l16][32 * st + 8 * g4];
+      dqa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, cb, dqa, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // dqa[e]: dim 16 w + 4 g4 + e, head l16
+  float* o = dq_idx + ((size_t)row * KL_HI + l16) * KL_DI + 16 * wave + 4 * g4;
+  *(f32x4*)o = dqa;
+}
+
+// ---------------------------------------------------------------- dk kernel
+// Workgroup (kt, chunk, b): entries [128 kt, + 128) (wave w: 32 from 128 kt +
+// 32 w), up to 64 query rows from the chunk, taken two at a time: the pair's
+// 2 x 16 heads are the 32 MFMA rows.  Per wave and pair:
+//   V = Q2 K^T (4 MFMAs), C = dI w [V > 0], dk^T += Q2^T C (4 MFMAs).
+__global__ void __launch_bounds__(256) idx_kl_dk_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, const uint32_t* __restrict__ bm,
+    const uint32_t* __restrict__ rank, const float* __restrict__ dIw, int nw, int T, int Nc_cap,
+    int topk, float* __restrict__ dk_idx) {
+  constexpr int PB = 32 * 128;  // bytes of a pair's 32 head rows
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[PB + 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[PB + 128];
+  __shared__ int32_t rows_s[KL_RC + 1];
+  __shared__ uint32_t shc[16];
+  const int kt = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int j0 = 128 * kt;
+  const int jw = j0 + 32 * wave + l32;
+  const int c0 = chunk * KL_RC;
+  if (c0 >= T) return;  // uniform
+  const int nc = min(KL_RC, T - c0);
+  {
+    bool act = false;
+    if (tid < nc) {
+      const uint32_t* w = bm + ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
+      uint32_t any = 0;
+      for (int k = 0; k < 4; ++k)
+        if ((j0 >> 5) + k < nw) any |= w[k];
+      act = any != 0;
+    }
+    uint32_t tot;
+    const uint32_t at = block_excl_scan(act ? 1u : 0u, shc, tot);
+    if (act) rows_s[at] = c0 + tid;
+    shc[8] = tot;
+  }
+  __syncthreads();
+  const int n_rows = (int)shc[8];
+  if (n_rows == 0) return;  // uniform
+  if (tid == 0) rows_s[n_rows] = -1;  // the odd row's partner: none
+  __syncthreads();
+
+  const bool key_in = jw < Nc_cap;
+  bf16x8 kf[4];
+  {
+    const uint16_t* kr = k_idx + ((size_t)b * Nc_cap + (key_in ? jw : 0)) * KL_DI + 8 * h2;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf[s] = *(const bf16x8*)(kr + 16 * s);
+  }
+  // LDS rows: head row m (0..31) at 128 m, 16-byte chunk c at slot c ^ ((m >> 1) & 7)
+  uint32_t aofs[4], tofs[2][2];
+  {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) aofs[s] = (uint32_t)(128 * l32 + 16 * ((2 * s + h2) ^ ((l32 >> 1) & 7)));
+    const int gg = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 4 * (gg >> 1) + (jj >> 2) + 8 * e;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int d = 32 * dt + 16 * (gg & 1) + 4 * (jj & 3);
+        tofs[dt][e] = (uint32_t)(128 * r + 16 * (((d >> 3)) ^ ((r >> 1) & 7)) + 2 * (d & 7));
+      }
+    }
+  }
+  // stage pair (t0, t1): head rows of t0 then t1 (t1 < 0: zeros), then w
+  auto stage = [&](int t0, int t1, uint8_t* dst) {
+    const int i = wave;  // load instruction i: head rows 8 i .. 8 i + 7
+    const int m = 8 * i + (lane >> 3), c = lane & 7;
+    const int t = m < 16 ? t0 : t1;
+    const int hd = m & 15;
+    const int lc = c ^ ((m >> 1) & 7);
+    const size_t src_row = ((size_t)b * T + (t >= 0 ? t : t0)) * KL_HI + hd;
+    kl_dma(q_idx + src_row * KL_DI + 8 * lc, dst + 1024 * i);
+    if (wave == 0 && lane < 8) {
+      const int tt = lane < 4 ? t0 : (t1 >= 0 ? t1 : t0);
+      kl_dma(w_idx + ((size_t)b * T + tt) * KL_HI + 4 * (lane & 3), dst + PB);
+    }
+  };
+  f32x16 dk[2];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[dt][r] = 0.0f;
+  bool touched = false;
+  const int wsel = (j0 >> 5) + wave;
+
+  auto compute = [&](const uint8_t* sb, int t0, int t1) {
+    // dI of this lane's entry for each row of the pair (0: not selected)
+    float di[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int t = p ? t1 : t0;
+      if (t >= 0 && key_in && wsel < nw) {
+        const size_t wi = ((size_t)b * T + t) * nw + wsel;
+        const uint32_t word = bm[wi];
+        if ((word >> l32) & 1u) {
+          const uint32_t slot = rank[wi] + __popc(word & ((1u << l32) - 1u));
+          if (slot < (uint32_t)topk) di[p] = dIw[((size_t)b * T + t) * topk + slot];
+        }
+      }
+    }
+    if (!__ballot(di[0] != 0.0f || di[1] != 0.0f)) return;
+    touched = true;
+    f32x16 va;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) va[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      va = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sb + aofs[s]), kf[s], va, 0, 0, 0);
+    // register r: head row 8 (r / 4) + 4 h2 + r % 4 (row r >= 8 of the pair's second token)
+    const float* ws = (const float*)(sb + PB);
+    bf16x8 cb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * h2 + (r & 3);
+      const float c = va[r] > 0.0f ? di[r >> 3] * ws[m] : 0.0f;
+      cb[r >> 3][r & 7] = (__bf16)c;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint32_t ho = (uint32_t)(16 * ks) * 128;
+        const u32x2 a1 = __builtin_bit_cast(u32x2, kl_read_tr16(sb + ho + tofs[dt][0]));
+        const u32x2 a2 = __builtin_bit_cast(u32x2, kl_read_tr16(sb + ho + tofs[dt][1]));
+        const bf16x8 qt = __builtin_bit_cast(bf16x8, u32x4{a1[0], a1[1], a2[0], a2[1]});
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, cb[ks], dk[dt], 0, 0, 0);
+      }
+  };
+
+  const int npairs = (n_rows + 1) / 2;
+  stage(rows_s[0], rows_s[1], st0);
+  for (int pi = 0; pi < npairs; pi += 2) {
+    kl_wait_loads();
+    __syncthreads();
+    if (pi + 1 < npairs) stage(rows_s[2 * pi + 2], rows_s[2 * pi + 3], st1);
+    compute(st0, rows_s[2 * pi], rows_s[2 * pi + 1]);
+    if (pi + 1 >= npairs) break;
+    kl_wait_loads();
+    __syncthreads();
+    if (pi + 2 < npairs) stage(rows_s[2 * pi + 4], rows_s[2 * pi + 5], st0);
+    compute(st1, rows_s[2 * pi + 2], rows_s[2 * pi + 3]);
+  }
+  if (!touched || !key_in) return;
+  // dk^T: entry jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4
+  float* gk = dk_idx + ((size_t)b * Nc_cap + jw) * KL_DI + 4 * h2;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) atomicAdd(gk + 32 * dt + 8 * (r >> 2) + (r & 3), dk[dt][r]);
+}
+
+}  // namespace csa
+
+// ---------------------------------------------------------------- host side
+namespace csa_host {
+using namespace csa;
+
+static size_t kl_al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t indexer_kl_ws_bytes(int B, int T, int Nc_cap, int topk) {
+  const size_t rows = (size_t)B * T, nw = ((size_t)Nc_cap + 31) / 32;
+  return kl_al256(rows * topk * sizeof(float)) + 2 * kl_al256(rows * nw * sizeof(uint32_t));
+}
+
+hipError_t launch_indexer_kl_bwd(const IndexerKlArgs& a, hipStream_t s) {
+  const int rows = a.B * a.T;
+  const int nw = (a.Nc_cap + 31) / 32;
+  char* ws = (char*)a.ws;
+  float* dIw = (float*)ws;
+  ws += kl_al256((size_t)rows * a.topk * sizeof(float));
+  uint32_t* bm = (uint32_t*)ws;
+  uint32_t* rank = (uint32_t*)(ws + kl_al256((size_t)rows * nw * sizeof(uint32_t)));
+  const size_t nk = (size_t)a.B * a.Nc_cap * KL_DI;
+  hipError_t e = launch_zero_f32(a.dk_idx, nk, s);
+  if (e != hipSuccess) return e;
+  if (a.topk > 0 && a.Nc_cap > 0) {
+    e = launch_sel_bitmap(a.idx, rows, a.topk, a.Nc_cap, bm, rank, s);
+    if (e != hipSuccess) return e;
+  }
+  idx_kl_row_kernel<<<rows, 256, 0, s>>>((const uint16_t*)a.q_idx, a.w_idx,
+                                         (const uint16_t*)a.k_idx, a.idx, a.mass, a.grad_scale,
+                                         a.T, a.Nc_cap, a.topk, a.loss, a.dq_idx, a.dw_idx, dIw);
+  if (a.topk > 0 && a.Nc_cap > 0)
+    idx_kl_dk_kernel<<<dim3((a.Nc_cap + 127) / 128, (a.T + KL_RC - 1) / KL_RC, a.B), 256, 0, s>>>(
+        (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, bm, rank, dIw, nw, a.T,
+        a.Nc_cap, a.topk, a.dk_idx);
+  return hipGetLastError();
+}
+
+}  // namespace csa_host

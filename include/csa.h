@@ -494,6 +494,42 @@ csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, f
                                 hipStream_t stream);
 size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H);
 
+/*
+ * Indexer KL loss and its gradients, the training signal of the Lightning
+ * Indexer (migration page, sections 1 and 3.2: the indexer loss and the fused
+ * sparse "lightning indexer grad + KL loss" operator; section 4.3: the loss
+ * coefficient and the sparse-loss switch).  The pages do not print the loss;
+ * the reading implemented (sparse form): for query row t with selected slots
+ * S (0 <= idx < Nc_cap), the target is the main attention's mass per entry,
+ * p_k = attn_mass[k] / sum_S attn_mass, the indexer's distribution is the
+ * softmax over S of its scores I_k = sum_h w[h] ReLU(q[h] . k_idx[idx_k]),
+ * and
+ *     loss[t] = KL(p || softmax(I)) = sum_S p_k (ln p_k - ln softmax(I)_k).
+ * The target carries no gradient.  With g = grad_scale[t] (1 if NULL; the
+ * caller's loss coefficient and averaging), dI_k = g (softmax(I)_k - p_k) and
+ *     dw_idx[t, h] = sum_k dI_k ReLU(v_hk),
+ *     dq_idx[t, h] = sum_k dI_k w[h] [v_hk > 0] k_idx[idx_k],
+ *     dk_idx[j]   += sum over rows and heads of dI_k w[h] [v_hk > 0] q[h],
+ * v_hk = q[h] . k_idx[idx_k].  A row with no selected entry or zero total
+ * mass has loss 0 and no gradient.
+ *  q_idx  bf16 [B, T, 16, 64];  w_idx fp32 [B, T, 16];  k_idx bf16 [B, Nc_cap, 64]
+ *  idx    int32 [B, T, topk] (each row's valid indices distinct and ascending
+ *         before its -1 pads, as csa_indexer_topk writes them)
+ *  attn_mass fp32 [B, T, topk] (csa_sparse_attn_bwd's);  grad_scale fp32 [B, T] or NULL
+ *  loss fp32 [B, T]; dq_idx fp32 [B, T, 16, 64]; dw_idx fp32 [B, T, 16];
+ *  dk_idx fp32 [B, Nc_cap, 64] (written in full)
+ * Supported: qk_dt BF16, H_I = 16, d_I = 64, topk <= 1024, Nc_cap <= 65536.
+ * Workspace: csa_indexer_kl_bwd_workspace_size() bytes (contents on entry do
+ * not matter).  dk_idx sums rows with fp32 atomics (run-to-run last bits).
+ */
+csa_status_t csa_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int topk,
+                                const void* q_idx, const float* w_idx, const void* k_idx,
+                                csa_dtype_t qk_dt, const int32_t* idx, const float* attn_mass,
+                                const float* grad_scale, float* loss, float* dq_idx,
+                                float* dw_idx, float* dk_idx, void* workspace, size_t ws_bytes,
+                                hipStream_t stream);
+size_t csa_indexer_kl_bwd_workspace_size(int B, int T, int Nc_cap, int topk);
+
 /* Static text of a status code. */
 const char* csa_status_string(csa_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -206,3 +206,71 @@ def test_csa_attn_bwd_full_8k_prefill():
     e_bl = abs(lhs - rhs) / np.abs(qv * gq).sum()
     print("8k identities: sum dV %.2e, sum dK %.2e, q.dq vs K.dK %.2e" % (e_dv, e_dk, e_bl))
     assert e_dv <= 1e-2 and e_dk <= 1e-2 and e_bl <= 1e-2
+
+
+# ---------------------------------------------------------------- indexer KL loss
+# loss: fp32 scores (bf16 inputs, fp32 MFMA accumulation) and fp32 softmax:
+# |gpu - oracle| <= 1e-4 (1 + |oracle|); dw (fp32 sums): row-relative 1e-4;
+# dq and dk (the coefficients dI w [v > 0] rounded to bf16 for the MFMA):
+# row-relative GRAD_TOL as above.
+
+def _kl_inputs(d, B, T, Nc, topk, q_pos):
+    qi = gen.store(d.normal(B, T, 16, 64), gen.BF16)
+    wi = d.normal(B, T, 16).float().contiguous()
+    ki = gen.store(d.normal(B, Nc, 64), gen.BF16)
+    nv = torch.tensor([[_n_vis(q_pos[b] + t, Nc, 4, Nc) for t in range(T)] for b in range(B)])
+    idx = gen.random_index_sets(d, B, T, topk, nv, 0.15)
+    mass = (torch.rand(B, T, topk, generator=d.g) * (idx >= 0)).float()
+    return qi, wi, ki, idx, mass
+
+
+def _kl_check(res, ref, what, with_dk=True):
+    loss, dq, dw = (_dec(x) for x in res[:3])
+    rl, rq, rw = ref[:3]
+    assert np.all(np.abs(loss - rl) <= 1e-4 * (1 + np.abs(rl))), (what, np.abs(loss - rl).max())
+    _rows_rel(dw, rw, what + " dw", tol=1e-4)
+    _rows_rel(dq, rq, what + " dq")
+    if with_dk:
+        _rows_rel(_dec(res[3]), ref[3], what + " dk")
+
+
+def test_indexer_kl_bwd_ragged_matches_oracle():
+    # 100 slots (a partial 16-slot tile and a partial 32-slot step of the dq
+    # product), rows without a selected entry, a row whose mass is zero, a
+    # per-row gradient scale, 300 entries (a partial 128-entry dk tile)
+    d = gen.Draw(560)
+    B, T, Nc, topk = 2, 70, 300, 100
+    q_pos = [0, 900]
+    qi, wi, ki, idx, mass = _kl_inputs(d, B, T, Nc, topk, q_pos)
+    idx[1, 5] = -1
+    mass[1, 6] = 0.0
+    gs = (torch.rand(B, T, generator=d.g) + 0.5).float()
+    res = csa.csa_indexer_kl_bwd(qi.to(DEV), wi.to(DEV), ki.to(DEV), idx.to(DEV), mass.to(DEV),
+                                 gs.to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.indexer_kl_bwd(gen.host_bits(qi), wi.numpy(), gen.host_bits(ki), idx.numpy(),
+                             mass.double().numpy(), gs.double().numpy())
+    _kl_check(res, ref, "kl ragged")
+    assert float(res[0][1, 5]) == 0.0 and float(res[0][1, 6]) == 0.0
+    assert (_dec(res[1])[1, 5] == 0).all() and (_dec(res[2])[1, 6] == 0).all()
+
+
+def test_indexer_kl_bwd_8k_prefill_shape():
+    # T = 8192, 2048 entries, topk = 512: loss, dq, dw of sampled rows (both
+    # ends, every 131st row) and dk of the entries only the last 40 rows see
+    d = gen.Draw(570)
+    B, T, Nc, topk = 1, 8192, 2048, 512
+    qi, wi, ki, idx, mass = _kl_inputs(d, B, T, Nc, topk, [0])
+    res = csa.csa_indexer_kl_bwd(qi.to(DEV), wi.to(DEV), ki.to(DEV), idx.to(DEV), mass.to(DEV))
+    torch.cuda.synchronize()
+    hq, hk, hi, hm, hw = (gen.host_bits(qi), gen.host_bits(ki), idx.numpy(),
+                          mass.double().numpy(), wi.numpy())
+    rows = sorted(set([0, 1, 4095, 4096] + list(range(5, T, 131)) + [T - 1]))
+    loss, dq, dw, _ = (_dec(x) for x in res)
+    rl, rq, rw, _ = orc.indexer_kl_bwd(hq[:, rows], hw[:, rows], hk, hi[:, rows], hm[:, rows])
+    _kl_check((res[0][:, rows], res[1][:, rows], res[2][:, rows]), (rl, rq, rw), "kl 8k rows",
+              with_dk=False)
+    t0 = T - 40
+    _, _, _, rk = orc.indexer_kl_bwd(hq[:, t0:], hw[:, t0:], hk, hi[:, t0:], hm[:, t0:])
+    jc = (t0 + 1) // 4 + 1
+    _rows_rel(_dec(res[3])[0, jc:], rk[0, jc:], "kl 8k dk tail entries")
