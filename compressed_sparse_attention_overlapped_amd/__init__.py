@@ -19,7 +19,7 @@ import torch
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
            "csa_indexer_topk_varlen", "csa_sparse_attn_varlen", "csa_sparse_attn_bwd",
-           "hca_dense_attn_bwd", "csa_indexer_kl_bwd",
+           "hca_dense_attn_bwd", "csa_indexer_kl_bwd", "csa_compress_bwd",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
            "CsaError", "PageTable", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
@@ -155,6 +155,10 @@ def lib():
         L.csa_indexer_kl_bwd.restype = C.c_int
         L.csa_indexer_kl_bwd_workspace_size.argtypes = [i32] * 4
         L.csa_indexer_kl_bwd_workspace_size.restype = C.c_size_t
+        L.csa_compress_bwd.argtypes = [i32] * 7 + [vp, vp, vp, i32, vp, i32] + [vp] * 5 + [vp, sz, vp]
+        L.csa_compress_bwd.restype = C.c_int
+        L.csa_compress_bwd_workspace_size.argtypes = [i32] * 5
+        L.csa_compress_bwd_workspace_size.restype = C.c_size_t
         L.csa_status_string.argtypes = [i32]
         L.csa_status_string.restype = C.c_char_p
         L.csa_last_error.argtypes = []
@@ -464,6 +468,29 @@ def hca_dense_attn_bwd(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, lse
                                   _p(dkv_cmp), _p(dkv_raw), _p(dsink), _p(ws), nb, _stream(q))
     _check("hca_dense_attn_bwd", rc)
     return dq, dkv_cmp, dkv_raw, dsink
+
+
+def csa_compress_bwd(x, w_kv, w_gate, m, overlap, Nc_cap, d_out, ape=None, rotate=False,
+                     want_dape=True, dx=None, dw_kv=None, dw_gate=None, dape=None,
+                     workspace=None):
+    """Gradients of a one-shot csa_compress call from position 0 (bf16 x
+    [B, L, d_model] and weights [E, d_model]) for d_out f32 [B, Nc_cap, E].
+    Returns (dx, dw_kv, dw_gate, dape or None), all float32."""
+    _dense(x, w_kv, w_gate, d_out, ape)
+    B, L, d_model = x.shape
+    E = w_kv.shape[0]
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty(B, L, d_model, **f32) if dx is None else dx
+    dw_kv = torch.empty(E, d_model, **f32) if dw_kv is None else dw_kv
+    dw_gate = torch.empty(E, d_model, **f32) if dw_gate is None else dw_gate
+    if ape is not None and want_dape and dape is None:
+        dape = torch.empty((1 + overlap) * m, E, **f32)
+    ws, nb = _workspace(lib().csa_compress_bwd_workspace_size(B, L, E, m, Nc_cap), x, workspace)
+    rc = lib().csa_compress_bwd(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(x), _p(w_kv),
+                                _p(w_gate), _DT[x.dtype], _p(ape), Nc_cap, _p(d_out), _p(dx),
+                                _p(dw_kv), _p(dw_gate), _p(dape), _p(ws), nb, _stream(x))
+    _check("csa_compress_bwd", rc)
+    return dx, dw_kv, dw_gate, dape
 
 
 def csa_indexer_kl_bwd(q_idx, w_idx, k_idx, idx, attn_mass, grad_scale=None, loss=None,

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libcsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_bwd.hip", "indexer_bwd.hip"]
+SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_bwd.hip", "indexer_bwd.hip",
+           "compress_bwd.hip"]
 # Per-source extra flags.  attend.hip and indexer.hip keep their MFMA
 # accumulators in VGPRs: the attention loops rescale the output accumulator
 # conditionally and the score epilogues read every accumulator element, and
@@ -25,6 +26,7 @@ SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_bwd.h
 EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-Wall", "-Wno-unused-result"]
@@ -51,7 +53,10 @@ def build() -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
+    # rocBLAS serves the compressor backward's plain GEMMs (dx, dW)
+    subprocess.check_call(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs,
+                           "-L" + os.path.join(ROCM, "lib"), "-lrocblas",
+                           "-Wl,-rpath," + os.path.join(ROCM, "lib")])
     os.replace(tmp, LIB)
     return LIB
 

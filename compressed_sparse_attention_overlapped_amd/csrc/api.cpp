@@ -710,3 +710,40 @@ csa_status_t csa_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int 
                             attn_mass,  grad_scale, loss, dq_idx, dw_idx, dk_idx, workspace};
   return hip_status(csa_host::launch_indexer_kl_bwd(a, stream), fn);
 }
+
+size_t csa_compress_bwd_workspace_size(int B, int L, int E, int m, int Nc_cap) {
+  if (B <= 0 || L <= 0 || E <= 0 || m < 1 || Nc_cap < 0) return 0;
+  return csa_host::compress_bwd_ws_bytes(B, L, E, m, Nc_cap);
+}
+
+csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                              const void* x, const void* w_kv, const void* w_gate,
+                              csa_dtype_t in_dt, const float* ape, int Nc_cap, const float* d_out,
+                              float* dx, float* dw_kv, float* dw_gate, float* dape,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "csa_compress_bwd";
+  if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0 || Nc_cap < 0)
+    return fail(CSA_E_ARG, "%s: B, L, d_model, E must be > 0 and Nc_cap >= 0", fn);
+  if (m < 1) return fail(CSA_E_ARG, "%s: m must be >= 1", fn);
+  if (overlap != 0 && overlap != 1) return fail(CSA_E_ARG, "%s: overlap must be 0 or 1", fn);
+  if (rotate != 0 && rotate != 1) return fail(CSA_E_ARG, "%s: rotate must be 0 or 1", fn);
+  if (rotate && (E & (E - 1))) return fail(CSA_E_ARG, "%s: rotate needs E a power of two", fn);
+  if (!x || !w_kv || !w_gate || !dx || !dw_kv || !dw_gate || (Nc_cap > 0 && !d_out) ||
+      (dape && !ape))
+    return fail(CSA_E_ARG, "%s: missing required pointer (dape needs ape)", fn);
+  if (in_dt != CSA_DT_BF16) return fail(CSA_E_UNSUPPORTED, "%s: in_dt must be BF16", fn);
+  if (E > 1024 || d_model % 64 != 0)
+    return fail(CSA_E_UNSUPPORTED, "%s: needs E <= 1024 and d_model a multiple of 64", fn);
+  if ((1 + overlap) * m > 1024) return fail(CSA_E_UNSUPPORTED, "%s: (1 + overlap) m > 1024", fn);
+  if ((int64_t)B * L > INT32_MAX / 2 || (L + 127) / 128 > 65535 || B > 65535)
+    return fail(CSA_E_UNSUPPORTED, "%s: B * L too large", fn);
+  if (!aligned16(x) || !aligned16(w_kv) || !aligned16(w_gate))
+    return fail(CSA_E_UNSUPPORTED, "%s: x and the weights must be 16-byte aligned", fn);
+  const size_t need = csa_host::compress_bwd_ws_bytes(B, L, E, m, Nc_cap);
+  if (ws_bytes < need || !workspace)
+    return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  csa_host::CompressBwdArgs a{B,     L,     d_model, E,       m,       overlap, rotate, Nc_cap,
+                              x,     w_kv,  w_gate,  ape,     d_out,   dx,      dw_kv,  dw_gate,
+                              dape,  workspace};
+  return hip_status(csa_host::launch_compress_bwd(a, stream), fn);
+}

@@ -329,6 +329,28 @@ struct IndexerKlArgs {
   void* ws;
 };
 size_t indexer_kl_ws_bytes(int B, int T, int Nc_cap, int topk);
+
+// The bf16 projection P | G = x [W_kv; W_gate]^T into fp32 rows of 2 E
+// (K a multiple of 64).
+hipError_t launch_proj_pg(const void* x, const void* w_kv, const void* w_gate, int M, int E, int K,
+                          float* pg, hipStream_t st);
+
+// Compressor backward (bf16 tokens and weights, one-shot call from position 0).
+struct CompressBwdArgs {
+  int B, L, d_model, E, m, overlap, rotate, Nc_cap;
+  const void* x;
+  const void* w_kv;
+  const void* w_gate;
+  const float* ape;
+  const float* dC;
+  float* dx;
+  float* dw_kv;
+  float* dw_gate;
+  float* dape;
+  void* ws;
+};
+size_t compress_bwd_ws_bytes(int B, int L, int E, int m, int Nc_cap);
+hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s);
 hipError_t launch_indexer_kl_bwd(const IndexerKlArgs& a, hipStream_t s);
 
 }  // namespace csa_host

@@ -875,6 +875,14 @@ static bool use_fused(const CompressArgs& a) {
 // the projection workspace the call is given.
 static int fused_tiles(int L) { return (L + 3 + 4 * FU_BLK - 1) / (4 * FU_BLK); }
 
+hipError_t launch_proj_pg(const void* x, const void* w_kv, const void* w_gate, int M, int E, int K,
+                          float* pg, hipStream_t st) {
+  dim3 grid((M + PJ_BM - 1) / PJ_BM, (2 * E + PJ_BN - 1) / PJ_BN, 1);
+  proj_bf16_kernel<<<grid, 512, 0, st>>>((const uint16_t*)x, (const uint16_t*)w_kv,
+                                         (const uint16_t*)w_gate, pg, M, E, K, K);
+  return hipGetLastError();
+}
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   if (use_fused(a)) {
     const int n_tiles = fused_tiles(a.L);

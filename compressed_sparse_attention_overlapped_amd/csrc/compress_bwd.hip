@@ -1,0 +1,210 @@
+// Compressor backward for gfx950: gradients of a one-shot compressor call
+// over tokens [0, L) of each sequence (bf16 tokens and weights, no carried
+// state; entries optionally Hadamard-rotated) for an upstream gradient dC of
+// its entries (migration page, section 3.2: the compressor is two linear maps
+// and a softmax-gated pool over overlapping windows; its training path is
+// listed in sections 1 and 3.2).
+//
+// For entry i over its window tokens j (slot s = j - m (i - o)), per channel:
+//   a_j = softmax_j(G_j + ape_s),  C_i = sum_j a_j P_j,
+//   dP_j += a_j dC_i,  dG_j += a_j (P_j - C_i) dC_i,  dape_s += the same;
+// and through P = x W_kv^T, G = x W_gate^T:
+//   dx = dP W_kv + dG W_gate,  dW_kv = dP^T x,  dW_gate = dG^T x.
+//
+// Launches: the forward projection (recomputes P | G in fp32); an entry
+// kernel (each entry's softmax statistics lse and C per channel, and, with the
+// rotation, the gradient through it: H dC / sqrt(E), H symmetric); a token
+// kernel (owner computes: token j takes its share of the one or two entries
+// whose windows hold it, so no two threads write one element, and dape is
+// summed per workgroup in LDS, then one atomic per slot and channel); and
+// four plain GEMMs for dx and the weight gradients (rocBLAS, bf16 operands,
+// fp32 accumulation and output).
+#include <rocblas/rocblas.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+
+#include "common.h"
+
+namespace csa {
+
+constexpr int CB_TT = 128;  // tokens per workgroup of the token kernel
+
+// Per (b, entry i < n_ent, channel e): lse and C of the window softmax, and
+// the entry's gradient (rotated back through the Hadamard matrix when the
+// entries were rotated).  One workgroup per entry row, E threads (E <= 1024).
+__global__ void __launch_bounds__(1024) cmp_bwd_entry_kernel(
+    const float* __restrict__ pg, const float* __restrict__ ape, const float* __restrict__ dC,
+    int L, int E, int m, int overlap, int Nc_cap, int n_ent, int rotate, float rs,
+    float* __restrict__ stats, float* __restrict__ gent) {
+  __shared__ float hv[1024];
+  const int i = blockIdx.x, b = blockIdx.y, e = threadIdx.x;
+  const int N = 2 * E;
+  const size_t prow = (size_t)b * L;
+  float g = dC[((size_t)b * Nc_cap + i) * E + e];
+  if (rotate) {
+    // fast Walsh-Hadamard transform of the row (Sylvester order), / sqrt(E)
+    hv[e] = g;
+    __syncthreads();
+    for (int len = 1; len < E; len <<= 1) {
+      const int blk = e / (2 * len), off = e % (2 * len);
+      float val;
+      if (off < len) val = hv[blk * 2 * len + off] + hv[blk * 2 * len + off + len];
+      else val = hv[blk * 2 * len + off - len] - hv[blk * 2 * len + off];
+      __syncthreads();
+      hv[e] = val;
+      __syncthreads();
+    }
+    g = hv[e] * rs;
+  }
+  const int first = m * (i - overlap), last = m * (i + 1) - 1;
+  float mx = -INFINITY;
+  for (int j = max(first, 0); j <= last; ++j)
+    mx = fmaxf(mx, pg[(prow + j) * N + E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0f));
+  float den = 0.0f, num = 0.0f;
+  for (int j = max(first, 0); j <= last; ++j) {
+    const float w = __expf(pg[(prow + j) * N + E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0f) - mx);
+    den += w;
+    num = fmaf(w, pg[(prow + j) * N + e], num);
+  }
+  const size_t o = ((size_t)b * n_ent + i) * E + e;
+  stats[2 * o] = mx + __logf(den);
+  stats[2 * o + 1] = num / den;
+  gent[o] = g;
+}
+
+// Token j (workgroup: CB_TT tokens x 64 channels; thread: a channel and
+// every fourth token): dP_j, dG_j as bf16 [M, 2 E] rows, and dape.
+__global__ void __launch_bounds__(256) cmp_bwd_token_kernel(
+    const float* __restrict__ pg, const float* __restrict__ ape, const float* __restrict__ stats,
+    const float* __restrict__ gent, int L, int E, int m, int overlap, int n_ent,
+    uint16_t* __restrict__ dpg, float* __restrict__ dape) {
+  extern __shared__ float dsh[];  // [(1 + o) m][64]
+  const int Sw = (1 + overlap) * m;
+  const int c = threadIdx.x & 63, tq = threadIdx.x >> 6;
+  const int e = blockIdx.y * 64 + c, b = blockIdx.z;
+  const int j0 = blockIdx.x * CB_TT;
+  const int N = 2 * E;
+  const bool ch = e < E;
+  for (int k = threadIdx.x; k < Sw * 64; k += 256) dsh[k] = 0.0f;
+  __syncthreads();
+  for (int j = j0 + tq; j < min(j0 + CB_TT, L) && ch; j += 4) {
+    const size_t r = (size_t)b * L + j;
+    const float P = pg[r * N + e], G = pg[r * N + E + e];
+    float dP = 0.0f, dG = 0.0f;
+    const int q = j / m;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      if (w == 1 && !overlap) break;
+      const int i = q + w;  // own block's entry, then the next one (its previous block)
+      if (i >= n_ent) continue;
+      const int s = j - m * (i - overlap);
+      const size_t o = ((size_t)b * n_ent + i) * E + e;
+      const float a = __expf(G + (ape ? ape[(size_t)s * E + e] : 0.0f) - stats[2 * o]);
+      const float g = gent[o];
+      const float gg = a * (P - stats[2 * o + 1]) * g;
+      dP = fmaf(a, g, dP);
+      dG += gg;
+      if (dape) atomicAdd(&dsh[s * 64 + c], gg);
+    }
+    dpg[r * N + e] = f32_to_bf16(dP);
+    dpg[r * N + E + e] = f32_to_bf16(dG);
+  }
+  __syncthreads();
+  if (dape)
+    for (int k = threadIdx.x; k < Sw * 64; k += 256) {
+      const int ee = blockIdx.y * 64 + (k & 63);
+      if (ee < E && dsh[k] != 0.0f) atomicAdd(&dape[(size_t)(k >> 6) * E + ee], dsh[k]);
+    }
+}
+
+}  // namespace csa
+
+// ---------------------------------------------------------------- host side
+namespace csa_host {
+using namespace csa;
+
+static size_t cb_al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t compress_bwd_ws_bytes(int B, int L, int E, int m, int Nc_cap) {
+  const size_t M = (size_t)B * L;
+  const size_t n_ent = std::min<size_t>((size_t)L / m, (size_t)Nc_cap);
+  return cb_al256(M * 2 * E * sizeof(float)) + cb_al256(M * 2 * E * sizeof(uint16_t)) +
+         cb_al256((size_t)B * n_ent * E * 2 * sizeof(float)) +
+         cb_al256((size_t)B * n_ent * E * sizeof(float));
+}
+
+// one rocBLAS handle per device, created on first use
+static rocblas_handle blas_handle(hipError_t& err) {
+  static std::mutex mu;
+  static rocblas_handle h[64] = {};
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess || dev < 0 || dev >= 64) {
+    if (err == hipSuccess) err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (!h[dev] && rocblas_create_handle(&h[dev]) != rocblas_status_success) {
+    err = hipErrorUnknown;
+    return nullptr;
+  }
+  return h[dev];
+}
+
+// C (col-major rows x cols) = op(A) op(B) + beta C, bf16 operands, fp32 C
+static bool gemm_bf16_f32(rocblas_handle hb, rocblas_operation ta, rocblas_operation tb, int rows,
+                          int cols, int k, const void* A, int lda, const void* B, int ldb,
+                          float beta, float* C, int ldc) {
+  const float alpha = 1.0f;
+  return rocblas_gemm_ex(hb, ta, tb, rows, cols, k, &alpha, A, rocblas_datatype_bf16_r, lda, B,
+                         rocblas_datatype_bf16_r, ldb, &beta, C, rocblas_datatype_f32_r, ldc, C,
+                         rocblas_datatype_f32_r, ldc, rocblas_datatype_f32_r,
+                         rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
+}
+
+hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
+  const int M = a.B * a.L, E = a.E, K = a.d_model, N = 2 * E;
+  const int n_ent = std::min(a.L / a.m, a.Nc_cap);
+  char* ws = (char*)a.ws;
+  float* pg = (float*)ws;
+  ws += cb_al256((size_t)M * N * sizeof(float));
+  uint16_t* dpg = (uint16_t*)ws;
+  ws += cb_al256((size_t)M * N * sizeof(uint16_t));
+  float* stats = (float*)ws;
+  ws += cb_al256((size_t)a.B * std::max(n_ent, 0) * E * 2 * sizeof(float));
+  float* gent = (float*)ws;
+  hipError_t e = launch_proj_pg(a.x, a.w_kv, a.w_gate, M, E, K, pg, s);
+  if (e != hipSuccess) return e;
+  const int Sw = (1 + a.overlap) * a.m;
+  if (a.dape) {
+    e = launch_zero_f32(a.dape, (size_t)Sw * E, s);
+    if (e != hipSuccess) return e;
+  }
+  if (n_ent > 0)
+    cmp_bwd_entry_kernel<<<dim3(n_ent, a.B), E, 0, s>>>(
+        pg, a.ape, a.dC, a.L, E, a.m, a.overlap, a.Nc_cap, n_ent, a.rotate,
+        (float)(1.0 / std::sqrt((double)E)), stats, gent);
+  cmp_bwd_token_kernel<<<dim3((a.L + CB_TT - 1) / CB_TT, (E + 63) / 64, a.B), 256,
+                         (size_t)Sw * 64 * sizeof(float), s>>>(
+      pg, a.ape, stats, gent, a.L, E, a.m, a.overlap, n_ent, dpg, a.dape);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  rocblas_handle hb = blas_handle(e);
+  if (!hb) return e;
+  if (rocblas_set_stream(hb, s) != rocblas_status_success) return hipErrorUnknown;
+  // row-major views as column-major: dx^T (K x M) = W_kv^T dP^T + W_gate^T dG^T
+  bool ok = gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, E, a.w_kv, K,
+                          dpg, N, 0.0f, a.dx, K) &&
+            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, E, a.w_gate, K,
+                          dpg + E, N, 1.0f, a.dx, K) &&
+            // dW_kv^T (K x E) = x^T dP  (x: K x M column-major; dP^T viewed E x M)
+            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, E, M, a.x, K,
+                          dpg, N, 0.0f, a.dw_kv, K) &&
+            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, E, M, a.x, K,
+                          dpg + E, N, 0.0f, a.dw_gate, K);
+  return ok ? hipGetLastError() : hipErrorUnknown;
+}
+
+}  // namespace csa_host

@@ -530,6 +530,33 @@ csa_status_t csa_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int 
                                 hipStream_t stream);
 size_t csa_indexer_kl_bwd_workspace_size(int B, int T, int Nc_cap, int topk);
 
+/*
+ * Gradients of a one-shot compressor call (csa_compress from position 0 with
+ * no carried state, bf16 tokens and weights, entries post-processed by
+ * nothing or by the Hadamard rotation) for an upstream gradient d_out
+ * [B, Nc_cap, E] (fp32) of the entries it writes, rows i < min(L / m, Nc_cap)
+ * (other rows are ignored).  By the chain rule through the compressor's
+ * definition (migration page, section 3.2), for entry i and window token j
+ * (slot s = j - m (i - overlap)), per channel, with g the entry's gradient
+ * (H d_out / sqrt(E) under the rotation, H being symmetric):
+ *     a_j = softmax_j(G_j + ape[s]),  C_i = sum_j a_j P_j,
+ *     dP_j += a_j g,  dG_j += a_j (P_j - C_i) g,  dape[s] += a_j (P_j - C_i) g,
+ *     dx = dP W_kv + dG W_gate,  dw_kv = sum_j dP_j x_j^T,  dw_gate = sum_j dG_j x_j^T.
+ *  x bf16 [B, L, d_model];  w_kv, w_gate bf16 [E, d_model];  ape fp32 [(1+o) m, E] or NULL
+ *  dx fp32 [B, L, d_model];  dw_kv, dw_gate fp32 [E, d_model];  dape fp32 [(1+o) m, E]
+ *  or NULL (needs ape); every output is written in full.
+ * dP and dG enter the weight and input products as bf16 (fp32 accumulation);
+ * those products run on rocBLAS.  Supported: in_dt BF16, E <= 1024, d_model a
+ * multiple of 64, (1 + overlap) m <= 1024.  Workspace:
+ * csa_compress_bwd_workspace_size() bytes (contents on entry do not matter).
+ */
+csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                              const void* x, const void* w_kv, const void* w_gate,
+                              csa_dtype_t in_dt, const float* ape, int Nc_cap, const float* d_out,
+                              float* dx, float* dw_kv, float* dw_gate, float* dape,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t csa_compress_bwd_workspace_size(int B, int L, int E, int m, int Nc_cap);
+
 /* Static text of a status code. */
 const char* csa_status_string(csa_status_t status);
 /* Detail of the last failure on the calling thread ("" if none). */

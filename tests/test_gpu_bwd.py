@@ -274,3 +274,75 @@ def test_indexer_kl_bwd_8k_prefill_shape():
     _, _, _, rk = orc.indexer_kl_bwd(hq[:, t0:], hw[:, t0:], hk, hi[:, t0:], hm[:, t0:])
     jc = (t0 + 1) // 4 + 1
     _rows_rel(_dec(res[3])[0, jc:], rk[0, jc:], "kl 8k dk tail entries")
+
+
+# ---------------------------------------------------------------- compressor
+# dP and dG enter the two products as bf16 (fp32 accumulation): dx, dW row-
+# relative GRAD_TOL; dape (fp32 sums): row-relative 1e-4.
+
+def _cmp_inputs(d, B, L, dm, E, m, o, ape=True):
+    x = gen.store(d.normal(B, L, dm), gen.BF16)
+    wk = gen.store(d.normal(E, dm, std=dm ** -0.5), gen.BF16)
+    wg = gen.store(d.normal(E, dm, std=dm ** -0.5), gen.BF16)
+    ap = (d.normal((1 + o) * m, E) * 0.3).float().contiguous() if ape else None
+    return x, wk, wg, ap
+
+
+@pytest.mark.parametrize("m,o,rotate,E,Nc", [(4, 1, False, 128, 30), (4, 1, True, 64, 12),
+                                            (3, 0, False, 128, 40)])
+def test_compress_bwd_matches_oracle(m, o, rotate, E, Nc):
+    # L = 75 is no multiple of m (trailing tokens without an entry); Nc = 12
+    # keeps fewer entries than L / m (the rest get no gradient)
+    d = gen.Draw(580 + m + 3 * rotate)
+    B, L, dm = 2, 75, 128
+    x, wk, wg, ap = _cmp_inputs(d, B, L, dm, E, m, o)
+    dC = d.normal(B, Nc, E).float().contiguous()
+    dx, dwk, dwg, dape = csa.csa_compress_bwd(x.to(DEV), wk.to(DEV), wg.to(DEV), m, o, Nc,
+                                              dC.to(DEV), ape=ap.to(DEV), rotate=rotate)
+    torch.cuda.synchronize()
+    rx, rk, rg, ra = orc.compress_bwd(gen.host_bits(x), gen.host_bits(wk), gen.host_bits(wg), m,
+                                      o, Nc, dC.double().numpy(), ape=ap.double().numpy(),
+                                      rotate=rotate)
+    _rows_rel(_dec(dx), rx, "cmp dx")
+    _rows_rel(_dec(dwk), rk, "cmp dw_kv")
+    _rows_rel(_dec(dwg), rg, "cmp dw_gate")
+    _rows_rel(_dec(dape), ra, "cmp dape", tol=1e-4)
+    n_ent = min(L // m, Nc)
+    assert (_dec(dx)[:, n_ent * m:] == 0).all()  # tokens of no entry
+
+
+def test_compress_bwd_8k_main_compressor():
+    # the 8K prefill chunk's main compressor (L = 8192, d_model = 4096,
+    # E = 256, m = 4 with overlap): dW rows of sampled channels (the pool is
+    # per channel, so a one-channel oracle call gives them exactly), dx of
+    # sampled tokens from a local slice (a token's gradient depends on the
+    # two windows that hold it), and for everything the bilinear identity
+    # sum_j x_j . dx_j = sum W_kv . dW_kv + sum W_gate . dW_gate
+    d = gen.Draw(590, DEV)
+    B, L, dm, E, m, o = 1, 8192, 4096, 256, 4, 1
+    Nc = L // m
+    x, wk, wg, ap = _cmp_inputs(d, B, L, dm, E, m, o)
+    dC = d.normal(B, Nc, E).float().contiguous()
+    dx, dwk, dwg, dape = csa.csa_compress_bwd(x, wk, wg, m, o, Nc, dC, ape=ap)
+    torch.cuda.synchronize()
+    hx, hk, hg, ha, hd = (gen.host_bits(x), gen.host_bits(wk), gen.host_bits(wg),
+                          ap.double().cpu().numpy(), dC.double().cpu().numpy())
+    for e in (0, 1, 63, 64, 129, 255):
+        _, rk, rg, ra = orc.compress_bwd(hx, hk[e:e + 1], hg[e:e + 1], m, o, Nc,
+                                         hd[:, :, e:e + 1], ape=ha[:, e:e + 1])
+        _rows_rel(_dec(dwk[e:e + 1]), rk, "8k dw_kv channel %d" % e)
+        _rows_rel(_dec(dwg[e:e + 1]), rg, "8k dw_gate channel %d" % e)
+        np.testing.assert_allclose(_dec(dape)[:, e], ra[:, 0], rtol=1e-4,
+                                   atol=1e-4 * np.abs(ra).max())
+    for q0 in (0, 1000, 2047 - 16):
+        j0 = 4 * q0
+        sl = slice(j0, j0 + 64)
+        rx, _, _, _ = orc.compress_bwd(hx[:, sl], hk, hg, m, o, 16, hd[:, q0:q0 + 16],
+                                       ape=ha)
+        lo = 0 if q0 == 0 else 4   # a slice's first block lacks its previous block
+        _rows_rel(_dec(dx)[0, j0 + lo:j0 + 56], rx[0, lo:56], "8k dx tokens %d.." % j0)
+    xv, wkv, wgv = (brute.decode_bits(a) for a in (hx, hk, hg))
+    lhs = (xv * _dec(dx)).sum()
+    rhs = (wkv * _dec(dwk)).sum() + (wgv * _dec(dwg)).sum()
+    print("8k compressor identity: %.3e vs %.3e" % (lhs, rhs))
+    assert abs(lhs - rhs) <= 1e-3 * (np.abs(xv * _dec(dx)).sum())
