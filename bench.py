@@ -3,7 +3,10 @@
 A step is one pass of the whole path over one batch of synthetic input:
   * csa_prefill_8k_bf16 (the line's `value`): compress (main and indexer) ->
     indexer top-k -> sparse attention for 8192 tokens;
-  * reported in the same line: csa_decode_128k_b32 ("decode_128k": indexer
+  * reported in the same line: csa_train_bwd_8k_bf16 ("train_bwd_8k": the
+    backward of that step for training: attention gradients with the
+    per-entry attention mass, the indexer KL loss and its gradients, both
+    compressors' gradients), csa_decode_128k_b32 ("decode_128k": indexer
     top-k -> sparse attention for 32 sequences at 131072 tokens of context,
     caches resident in HBM), hca_prefill_1m_chunk4k ("hca_1m_chunk4k": dense
     compressed attention of a 4096-token chunk at 1M context) and
@@ -237,6 +240,65 @@ def step_prefill(w, st):
     return fn, ["indexer_compress", "indexer_topk_and_main_compress", "sparse_attn"]
 
 
+def setup_train_bwd(w):
+    """The forward of the 8K prefill step once (untimed), through the
+    library, then every buffer of its backward."""
+    st = setup_prefill(w)
+    B, S, dt = w.B, w.T, gen.torch_dtype(w.dt)
+    d = gen.Draw(w.seed + 7, DEV)
+    csa.csa_compress(st["x"], st["w_kv"], st["w_gate"], st["pos0"], w.m, w.overlap, st["kv_cmp"],
+                     workspace=st["ws_c1"])
+    csa.csa_compress(st["x"], st["w_ikv"], st["w_igate"], st["pos0"], w.m, w.overlap, st["k_idx"],
+                     workspace=st["ws_c2"])
+    csa.csa_indexer_topk(st["q_idx"], st["w_idx"], st["k_idx"], w.m, w.topk, st["pos0"],
+                         st["ncmp"], q_scale=st["q_scale"], idx_out=st["idx"], workspace=st["ws_i"])
+    _, st["lse"] = csa.csa_sparse_attn(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"], w.window,
+                                       st["pos0"], st["raw_base"], out=st["out"], want_lse=True,
+                                       workspace=st["ws_a"])
+    st["dout"] = gen.store(d.normal(B, S, w.H, w.D), w.dt)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    st["dq"] = torch.empty(B, S, w.H, w.D, **f32)
+    st["dkv_cmp"] = torch.empty(B, w.n_cmp, 2 * w.D, **f32)
+    st["dkv_raw"] = torch.empty(B, S, 2 * w.D, **f32)
+    st["mass"] = torch.empty(B, S, w.topk, **f32)
+    st["loss"] = torch.empty(B, S, **f32)
+    st["dq_idx"] = torch.empty(B, S, w.H_I, w.d_I, **f32)
+    st["dw_idx"] = torch.empty(B, S, w.H_I, **f32)
+    st["dk_idx"] = torch.empty(B, w.n_cmp, w.d_I, **f32)
+    for k, E in (("c1", 2 * w.D), ("c2", w.d_I)):
+        st["dx_" + k] = torch.empty(B, S, w.d_model, **f32)
+        st["dwk_" + k] = torch.empty(E, w.d_model, **f32)
+        st["dwg_" + k] = torch.empty(E, w.d_model, **f32)
+        st["wsb_" + k] = torch.empty(csa.lib().csa_compress_bwd_workspace_size(B, S, E, w.m, w.n_cmp),
+                                     dtype=torch.uint8, device=DEV)
+    st["wsb_a"] = torch.empty(csa.lib().csa_sparse_attn_bwd_workspace_size(
+        B, S, w.H, w.n_cmp, S, w.window), dtype=torch.uint8, device=DEV)
+    st["wsb_i"] = torch.empty(csa.lib().csa_indexer_kl_bwd_workspace_size(B, S, w.n_cmp, w.topk),
+                              dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    return st
+
+
+def step_train_bwd(w, st):
+    def fn(tm):
+        tm.mark(0)
+        csa.csa_sparse_attn_bwd(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"], w.window,
+                                st["pos0"], st["raw_base"], st["lse"], st["dout"], dq=st["dq"],
+                                dkv_cmp=st["dkv_cmp"], dkv_raw=st["dkv_raw"],
+                                attn_mass=st["mass"], workspace=st["wsb_a"])
+        tm.mark(1)
+        csa.csa_indexer_kl_bwd(st["q_idx"], st["w_idx"], st["k_idx"], st["idx"], st["mass"],
+                               loss=st["loss"], dq_idx=st["dq_idx"], dw_idx=st["dw_idx"],
+                               dk_idx=st["dk_idx"], workspace=st["wsb_i"])
+        tm.mark(2)
+        for k, wk, wg, dc in (("c1", "w_kv", "w_gate", "dkv_cmp"), ("c2", "w_ikv", "w_igate", "dk_idx")):
+            csa.csa_compress_bwd(st["x"], st[wk], st[wg], w.m, w.overlap, w.n_cmp, st[dc],
+                                 dx=st["dx_" + k], dw_kv=st["dwk_" + k], dw_gate=st["dwg_" + k],
+                                 workspace=st["wsb_" + k])
+        tm.mark(3)
+    return fn, ["attn_bwd", "indexer_kl_bwd", "compress_bwd"]
+
+
 def setup_decode(w):
     stream = w.d_model > 0
     # the streaming step emits the last entry itself
@@ -387,6 +449,43 @@ def cpu_baseline(w, budget_s=12.0):
                 "sample": "%d query tokens in blocks of %d consecutive positions drawn uniformly "
                           "from the %d-token prefill; per block both compressors over the block, "
                           "its indexer rows and its attention rows" % (n_tok, blk, S)}
+    if w.kind == "csa_train_bwd":
+        dm, S, blk = w.d_model, w.T, 16
+        wk, wg = (gen.host_bits(t) for t in gen.compressor_weights(d, dm, 2 * w.D, w.dt))
+        wik, wig = (gen.host_bits(t) for t in gen.compressor_weights(d, dm, w.d_I, w.dt))
+        kv_cmp = gen.host_bits(gen.store(d.normal(1, w.n_cmp, 2 * w.D), w.dt))
+        kv_raw = gen.host_bits(gen.store(d.normal(1, S, 2 * w.D), w.dt))
+        k_idx = gen.host_bits(gen.store(d.normal(1, w.n_cmp, w.d_I), w.idx_dt))
+        n_tok, tot = 0, 0.0
+        while tot < budget_s:
+            s0 = 4 * int(rng.integers(0, (S - blk) // 4 + 1))
+            x = gen.host_bits(gen.store(d.normal(1, blk, dm), w.dt))
+            q_idx = gen.host_bits(gen.store(d.normal(1, blk, w.H_I, w.d_I), w.idx_dt))
+            w_idx = d.normal(1, blk, w.H_I).numpy()
+            q = gen.host_bits(gen.store(d.normal(1, blk, w.H, w.D), w.dt))
+            dout = d.normal(1, blk, w.H, w.D).double().numpy()
+            nv = np.minimum((s0 + np.arange(blk) + 1) // w.m, w.n_cmp)
+            idx = np.full((1, blk, w.topk), -1, np.int32)
+            for r in range(blk):
+                k = min(w.topk, int(nv[r]))
+                idx[0, r, :k] = np.sort(rng.choice(int(nv[r]), k, replace=False))
+            dc1 = d.normal(1, blk // w.m, 2 * w.D).double().numpy()
+            dc2 = d.normal(1, blk // w.m, w.d_I).double().numpy()
+            a = time.perf_counter()
+            # the block's attention rows, their indexer loss rows, and both
+            # compressors over the block's tokens
+            _, _, _, _, mass = orc.attn_bwd(q, kv_cmp, idx, kv_raw, w.window, s0, 0, dout,
+                                            want_mass=True)
+            orc.indexer_kl_bwd(q_idx, w_idx, k_idx, idx, mass)
+            orc.compress_bwd(x, wk, wg, w.m, w.overlap, blk // w.m, dc1)
+            orc.compress_bwd(x, wik, wig, w.m, w.overlap, blk // w.m, dc2)
+            tot += time.perf_counter() - a
+            n_tok += blk
+        return {"value": n_tok / tot, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "sample": "%d tokens in blocks of %d consecutive positions drawn uniformly from "
+                          "the %d-token chunk; per block the attention backward of its rows, their "
+                          "indexer KL loss and gradients, and both compressors' backward over "
+                          "the block" % (n_tok, blk, S)}
     if w.kind == "csa_decode":
         Bs = 8
         Ns = min(w.n_cmp, 65536)
@@ -442,6 +541,18 @@ def measure(name, steps, warmup, with_cpu, graph=True):
         idx_flops = pairs * w.H_I * w.d_I * 2
         comp_flops = 2 * w.B * w.T * w.d_model * 2 * (2 * w.D + w.d_I)
         unit_items, unit = w.B * w.T, "tokens/s"
+    elif w.kind == "csa_train_bwd":
+        st = setup_train_bwd(w)
+        fn, names = step_train_bwd(w, st)
+        pairs, visits = csa_counts(w, 0, w.T, w.n_cmp)
+        sel = int(np.minimum(w.topk, np.minimum(w.n_cmp, (np.arange(w.T) + 1) // w.m)).sum())
+        # S (recomputed), dP, dQ, dK, dV per key visit; the indexer loss: the
+        # scores twice, dq and dk; each compressor: the projection recomputed,
+        # dx and dW
+        attn_flops = visits * w.H * w.D * 2 * 5
+        idx_flops = sel * w.H_I * w.d_I * 2 * 4
+        comp_flops = 3 * 2 * w.B * w.T * w.d_model * 2 * (2 * w.D + w.d_I)
+        unit_items, unit = w.B * w.T, "tokens/s"
     elif w.kind == "csa_decode":
         st = setup_decode(w)
         fn, names = step_decode(w, st)
@@ -476,6 +587,16 @@ def measure(name, steps, warmup, with_cpu, graph=True):
                                "frac": ach / FP32_VECTOR_PEAK_TFLOPS, "traffic": None}
         res["work"] = {"attn_gflop": attn_flops / 1e9, "indexer_gflop": idx_flops / 1e9,
                        "compress_gflop": comp_flops / 1e9,
+                       "step_mfma_frac": (attn_flops + idx_flops + comp_flops) / step_s / 1e12
+                       / MFMA_BF16_PEAK_TFLOPS}
+    elif w.kind == "csa_train_bwd":
+        ach = attn_flops / (sm["attn_bwd"] / 1e3) / 1e12
+        res["roofline"] = {"bound": "mfma", "kernel": "attention backward (attn_bwd_dq_kernel + "
+                           "attn_bwd_dkv_kernel)", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                           "traffic": measured_traffic("attn_bwd", name)}
+        res["work"] = {"attn_bwd_gflop": attn_flops / 1e9, "indexer_kl_gflop": idx_flops / 1e9,
+                       "compress_bwd_gflop": comp_flops / 1e9,
                        "step_mfma_frac": (attn_flops + idx_flops + comp_flops) / step_s / 1e12
                        / MFMA_BF16_PEAK_TFLOPS}
     elif w.kind == "csa_decode":
@@ -556,7 +677,8 @@ def main():
         return
     prim = measure("csa_prefill_8k_bf16", args.steps, args.warmup, not args.no_cpu)
     sub = {}
-    for key, wl, graph in (("decode_128k", "csa_decode_128k_b32", True),
+    for key, wl, graph in (("train_bwd_8k", "csa_train_bwd_8k_bf16", False),
+                           ("decode_128k", "csa_decode_128k_b32", True),
                            ("hca_1m_chunk4k", "hca_prefill_1m_chunk4k", False),
                            ("decode_1m_stream", "csa_decode_1m_b8_stream", False)):
         r = measure(wl, args.steps, args.warmup, not args.no_cpu, graph=graph)

@@ -144,12 +144,12 @@ def lib():
         L.csa_sparse_attn_bwd.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32, vp,
                                           i32] + [vp] * 8 + [sz, vp])
         L.csa_sparse_attn_bwd.restype = C.c_int
-        L.csa_sparse_attn_bwd_workspace_size.argtypes = [i32] * 4
+        L.csa_sparse_attn_bwd_workspace_size.argtypes = [i32] * 6
         L.csa_sparse_attn_bwd_workspace_size.restype = C.c_size_t
         L.hca_dense_attn_bwd.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, vp, i32, vp, i32, vp,
                                          i32] + [vp] * 7 + [sz, vp])
         L.hca_dense_attn_bwd.restype = C.c_int
-        L.hca_dense_attn_bwd_workspace_size.argtypes = [i32] * 3
+        L.hca_dense_attn_bwd_workspace_size.argtypes = [i32] * 6
         L.hca_dense_attn_bwd_workspace_size.restype = C.c_size_t
         L.csa_indexer_kl_bwd.argtypes = [i32] * 6 + [vp, vp, vp, i32] + [vp] * 7 + [vp, sz, vp]
         L.csa_indexer_kl_bwd.restype = C.c_int
@@ -440,8 +440,8 @@ def csa_sparse_attn_bwd(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, lse, do
                                                dsink)
     if want_mass and attn_mass is None:
         attn_mass = torch.empty(B, T, topk, dtype=torch.float32, device=q.device)
-    ws, nb = _workspace(lib().csa_sparse_attn_bwd_workspace_size(B, T, H, kv_cmp.shape[1]), q,
-                        workspace)
+    ws, nb = _workspace(lib().csa_sparse_attn_bwd_workspace_size(
+        B, T, H, kv_cmp.shape[1], kv_raw.shape[1], window), q, workspace)
     rc = lib().csa_sparse_attn_bwd(B, T, H, D, topk, window, scale, _p(sink), _p(q_pos), _p(q),
                                    _p(kv_cmp), kv_cmp.shape[1], _p(idx), _p(kv_raw),
                                    kv_raw.shape[1], _p(raw_base), _DT[q.dtype], _p(lse), _p(dout),
@@ -461,7 +461,8 @@ def hca_dense_attn_bwd(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, lse
     sink = _sink(sink, H)
     dq, dkv_cmp, dkv_raw, dsink = _bwd_outputs(q, kv_cmp, kv_raw, sink, dq, dkv_cmp, dkv_raw,
                                                dsink)
-    ws, nb = _workspace(lib().hca_dense_attn_bwd_workspace_size(B, T, H), q, workspace)
+    ws, nb = _workspace(lib().hca_dense_attn_bwd_workspace_size(
+        B, T, H, kv_cmp.shape[1], kv_raw.shape[1], window), q, workspace)
     rc = lib().hca_dense_attn_bwd(B, T, H, D, m, window, scale, _p(sink), _p(q_pos), _p(n_cmp),
                                   _p(q), _p(kv_cmp), kv_cmp.shape[1], _p(kv_raw), kv_raw.shape[1],
                                   _p(raw_base), _DT[q.dtype], _p(lse), _p(dout), _p(dq),

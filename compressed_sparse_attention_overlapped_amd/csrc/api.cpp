@@ -608,14 +608,15 @@ csa_status_t csa_sparse_attn_varlen(int n, int total, int max_len, int H, int D,
 
 // ---------------------------------------------------------------- backward
 
-size_t csa_sparse_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap) {
-  if (B <= 0 || T <= 0 || H <= 0 || Nc_cap < 0) return 0;
-  return csa_host::attn_bwd_ws_bytes(B, T, H, Nc_cap, true);
+size_t csa_sparse_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap, int R_cap,
+                                          int window) {
+  if (B <= 0 || T <= 0 || H <= 0 || Nc_cap < 0 || R_cap < 0 || window < 0) return 0;
+  return csa_host::attn_bwd_ws_bytes(B, T, H, Nc_cap, R_cap, window, true);
 }
 
-size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H) {
-  if (B <= 0 || T <= 0 || H <= 0) return 0;
-  return csa_host::attn_bwd_ws_bytes(B, T, H, 0, false);
+size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap, int R_cap, int window) {
+  if (B <= 0 || T <= 0 || H <= 0 || Nc_cap < 0 || R_cap < 0 || window < 0) return 0;
+  return csa_host::attn_bwd_ws_bytes(B, T, H, Nc_cap, R_cap, window, false);
 }
 
 static csa_status_t attn_bwd_impl(const char* fn, csa_host::AttnBwdArgs& a, int D,
@@ -638,7 +639,8 @@ static csa_status_t attn_bwd_impl(const char* fn, csa_host::AttnBwdArgs& a, int 
     return fail(CSA_E_UNSUPPORTED, "%s: caches hold at most 2^23 rows", fn);
   if ((a.T + 63) / 64 > 65535 || a.B > 65535)
     return fail(CSA_E_UNSUPPORTED, "%s: T <= 65535 * 64 and B <= 65535", fn);
-  const size_t need = csa_host::attn_bwd_ws_bytes(a.B, a.T, a.H, a.Nc_cap, !a.dense);
+  const size_t need =
+      csa_host::attn_bwd_ws_bytes(a.B, a.T, a.H, a.Nc_cap, a.R_cap, a.window, !a.dense);
   if (ws_bytes < need || !a.ws)
     return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   return hip_status(csa_host::launch_attn_bwd(a, stream), fn);

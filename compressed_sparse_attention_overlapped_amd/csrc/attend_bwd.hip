@@ -383,14 +383,18 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
     const uint32_t* __restrict__ bm, const uint32_t* __restrict__ rank, int nw,
     const int64_t* __restrict__ q_pos, const int64_t* __restrict__ raw_base,
     const int32_t* __restrict__ n_cmp, int T, int topk, int window, int m, float scale,
-    float* __restrict__ dkv, float* __restrict__ attn_mass) {
+    int nslot, float* __restrict__ part, uint32_t* __restrict__ pflag,
+    float* __restrict__ attn_mass) {
   constexpr int H = 32 * NHH;
   constexpr int QB = H * 256;             // bytes of one row's Q (or dO)
-  constexpr int SB = 2 * QB + 8 * H;      // Q | dO | lse2 | delta
+  constexpr int SB0 = 2 * QB + 8 * H;     // Q | dO | lse2 | delta
+  constexpr int SB = SB0 > 2 * 32 * 129 * 4 ? SB0 : 2 * 32 * 129 * 4;  // (the epilogue's rows)
   constexpr int NQI = QB / 1024;          // load instructions for Q (and for dO)
   __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[SB];
   __shared__ int32_t rows_s[BW_RC];
+  __shared__ uint32_t rows_w[KIND == 0 ? BW_RC : 1][4];   // the row's bitmap words of the tile
+  __shared__ uint32_t rows_r[KIND == 0 ? BW_RC : 1][4];   // and their ranks
   __shared__ uint32_t sh[16];
   const int kt = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -402,43 +406,26 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
   const int64_t rbase = KIND == 2 ? raw_base[b] : 0;
   const int ncb = KIND == 1 ? n_cmp[b] : 0;
 
-  // rows that can see the tile: [t_lo, t_hi]
+  // rows that can see the tile: [t_lo, t_hi]; this workgroup takes the
+  // 64-row chunks slot, slot + nslot, ... of them and leaves one partial
+  // [128 keys][2 D] (with a flag: 0 if it saw no row) for the reduction
+  const size_t slot = ((size_t)b * gridDim.x + kt) * nslot + chunk;
+  float* pdst = part + slot * (BW_KV_KEYS * 256);
   int64_t t_lo = 0, t_hi = T - 1;
   if (KIND == 2) {
     const int64_t p0 = rbase + j0, p1 = rbase + min(j0 + BW_KV_KEYS, rows_cap) - 1;
     t_lo = p0 - qp;
     t_hi = p1 + window - 1 - qp;
   } else if (KIND == 1) {
-    if (ncb <= j0) return;  // uniform
+    if (ncb <= j0) t_hi = -1;  // no visible entry in the tile
     t_lo = (int64_t)m * (j0 + 1) - 1 - qp;
   }
   if (t_lo < 0) t_lo = 0;
   if (t_hi > T - 1) t_hi = T - 1;
-  const int64_t c0 = t_lo + (int64_t)chunk * BW_RC;
-  if (c0 > t_hi) return;  // uniform, before any barrier
-  const int nc = (int)min((int64_t)BW_RC, t_hi - c0 + 1);
-
-  // the chunk's rows that see any key of the tile (CSA: a selected entry)
-  {
-    bool act = false;
-    if (tid < nc) {
-      act = true;
-      if (KIND == 0) {
-        const uint32_t* w = bm + ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
-        uint32_t any = 0;
-        for (int k = 0; k < 4; ++k)
-          if ((j0 >> 5) + k < nw) any |= w[k];
-        act = any != 0;
-      }
-    }
-    uint32_t tot;
-    const uint32_t at = block_excl_scan(act ? 1u : 0u, sh, tot);
-    if (act) rows_s[at] = (int)(c0 + tid);
-    sh[8] = tot;  // read after the next barrier
+  if (t_lo + (int64_t)chunk * BW_RC > t_hi) {  // uniform, before any barrier
+    if (tid == 0) pflag[slot] = 0u;
+    return;
   }
-  __syncthreads();
-  const int n_rows = (int)sh[8];
-  if (n_rows == 0) return;  // uniform
 
   // B operands: K^T and V^T of this lane's key (dims 16 s + 8 h2 ..); keys
   // past the cache read row 0 and are masked
@@ -498,13 +485,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
     for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
   bool touched = false;
   const float sc2 = scale * kLog2e;
-  const int wsel = (j0 >> 5) + wave;  // the bitmap word of this wave's keys
 
-  auto compute = [&](const uint8_t* sb, int t) {
+  auto compute = [&](const uint8_t* sb, int ri) {
+    const int t = rows_s[ri];
     const int64_t pos = qp + t;
     bool ok = key_in;
+    uint32_t word = 0u;
     if (KIND == 0) {
-      ok = ok && wsel < nw && ((bm[((size_t)b * T + t) * nw + wsel] >> l32) & 1u);
+      word = rows_w[ri][wave];  // zero past the cache's words
+      ok = ok && ((word >> l32) & 1u);
     } else if (KIND == 1) {
       ok = ok && jw < n_visible(pos, ncb, m, rows_cap);
     } else {
@@ -553,9 +542,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
     if (KIND == 0 && attn_mass) {
       msum += lane_xor32(msum);
       if (ok && h2 == 0) {
-        const size_t wi = ((size_t)b * T + t) * nw + wsel;
-        const uint32_t below = bm[wi] & ((1u << l32) - 1u);
-        const uint32_t slot = rank[wi] + __popc(below);
+        const uint32_t slot = rows_r[ri][wave] + __popc(word & ((1u << l32) - 1u));
         if (slot < (uint32_t)topk) attn_mass[((size_t)b * T + t) * topk + slot] = msum;
       }
     }
@@ -578,29 +565,107 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
       }
   };
 
-  stage(rows_s[0], st0);
-  for (int i = 0; i < n_rows; i += 2) {
-    bw_wait_loads();
-    __syncthreads();
-    if (i + 1 < n_rows) stage(rows_s[i + 1], st1);
-    compute(st0, rows_s[i]);
-    if (i + 1 >= n_rows) break;
-    bw_wait_loads();
-    __syncthreads();
-    if (i + 2 < n_rows) stage(rows_s[i + 2], st0);
-    compute(st1, rows_s[i + 1]);
-  }
-  if (!touched || !key_in) return;
-  // dK^T / dV^T: key jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4
-  float* gk = dkv + ((size_t)b * rows_cap + jw) * 256 + 4 * h2;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d = 32 * dt + 8 * (r >> 2) + (r & 3);
-      atomicAdd(gk + d, scale * dk[dt][r]);
-      atomicAdd(gk + 128 + d, dv[dt][r]);
+  for (int64_t c0 = t_lo + (int64_t)chunk * BW_RC; c0 <= t_hi; c0 += (int64_t)nslot * BW_RC) {
+    const int nc = (int)min((int64_t)BW_RC, t_hi - c0 + 1);
+    // the chunk's rows that see any key of the tile (CSA: a selected entry)
+    {
+      bool act = false;
+      uint32_t wv[4] = {0u, 0u, 0u, 0u}, rv[4] = {0u, 0u, 0u, 0u};
+      if (tid < nc) {
+        act = true;
+        if (KIND == 0) {
+          const size_t wi = ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
+          uint32_t any = 0;
+          for (int k = 0; k < 4; ++k)
+            if ((j0 >> 5) + k < nw) {
+              wv[k] = bm[wi + k];
+              rv[k] = rank[wi + k];
+              any |= wv[k];
+            }
+          act = any != 0;
+        }
+      }
+      uint32_t tot;
+      const uint32_t at = block_excl_scan(act ? 1u : 0u, sh, tot);
+      if (act) {
+        rows_s[at] = (int)(c0 + tid);
+        if (KIND == 0)
+          for (int k = 0; k < 4; ++k) {
+            rows_w[at][k] = wv[k];
+            rows_r[at][k] = rv[k];
+          }
+      }
+      sh[8] = tot;  // read after the next barrier
     }
+    __syncthreads();
+    const int n_rows = (int)sh[8];
+    if (n_rows > 0) {  // uniform
+      stage(rows_s[0], st0);
+      for (int i = 0; i < n_rows; i += 2) {
+        bw_wait_loads();
+        __syncthreads();
+        if (i + 1 < n_rows) stage(rows_s[i + 1], st1);
+        compute(st0, i);
+        if (i + 1 >= n_rows) break;
+        bw_wait_loads();
+        __syncthreads();
+        if (i + 2 < n_rows) stage(rows_s[i + 2], st0);
+        compute(st1, i + 1);
+      }
+    }
+    __syncthreads();  // the staging buffers and rows_s are free again
+  }
+  // dK^T / dV^T (key jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4)
+  // through LDS into key rows (stride 129 floats: the 32 keys of one store
+  // hit 32 banks), then stored as the workgroup's partial in whole rows
+  // (64 consecutive floats per store); waves 0-1 use st0, waves 2-3 st1.
+  // dK first, then dV.
+  float* red = (float*)((wave < 2 ? st0 : st1)) + (wave & 1) * 32 * 129;
+  float* prow = pdst + (size_t)(32 * wave) * 256;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * dt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        red[l32 * 129 + d] = half ? dv[dt][r] : scale * dk[dt][r];
+      }
+    __syncthreads();
+    for (int k = 0; k < 32; ++k) {
+      prow[(size_t)k * 256 + 128 * half + lane] = red[k * 129 + lane];
+      prow[(size_t)k * 256 + 128 * half + 64 + lane] = red[k * 129 + 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) pflag[slot] = 1u;
+  (void)touched;
+}
+
+// dkv[b, key] = the sum, in slot order, of the valid partials of the key's
+// tile.  Workgroup (8-key group g, b): keys 8 (g % 16) .. of tile g / 16;
+// thread d: element d of each row.
+__global__ void __launch_bounds__(256) bwd_dkv_reduce_kernel(const float* __restrict__ part,
+                                                             const uint32_t* __restrict__ pflag,
+                                                             int n_tiles, int nslot, int rows_cap,
+                                                             float* __restrict__ dkv) {
+  const int g = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int kt = g / 16, kl0 = 8 * (g % 16);
+  const size_t s0 = ((size_t)b * n_tiles + kt) * nslot;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+  for (int p = 0; p < nslot; ++p) {
+    if (!pflag[s0 + p]) continue;  // uniform
+    const float* ps = part + (s0 + p) * (BW_KV_KEYS * 256) + (size_t)kl0 * 256 + d;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += ps[(size_t)k * 256];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int key = BW_KV_KEYS * kt + kl0 + k;
+    if (key < rows_cap) dkv[((size_t)b * rows_cap + key) * 256 + d] = acc[k];
+  }
 }
 
 }  // namespace csa
@@ -613,10 +678,31 @@ using namespace csa;
 // per-row sink terms), and for CSA the bitmap and word ranks [rows][nw]
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t attn_bwd_ws_bytes(int B, int T, int H, int Nc_cap, bool sparse) {
+// row-chunk slots per key tile of the dK / dV kernel: compressed tiles take
+// enough workgroups to fill the chip about twice (each looping over several
+// 64-row chunks), window tiles one per chunk of the rows that can see them
+static int dkv_slots_cmp(int B, int T, int Nc_cap) {
+  const int tiles = (Nc_cap + BW_KV_KEYS - 1) / BW_KV_KEYS, ch = (T + BW_RC - 1) / BW_RC;
+  if (tiles == 0) return 0;
+  return std::max(1, std::min(ch, (512 + tiles * B - 1) / (tiles * B)));
+}
+static int dkv_slots_raw(int T, int window) {
+  const int ch = (T + BW_RC - 1) / BW_RC;
+  return std::max(1, std::min(ch, (BW_KV_KEYS + window - 1 + BW_RC - 1) / BW_RC));
+}
+static size_t dkv_part_floats(int B, int T, int Nc_cap, int R_cap, int window) {
+  const size_t tc = (Nc_cap + BW_KV_KEYS - 1) / BW_KV_KEYS, tr = (R_cap + BW_KV_KEYS - 1) / BW_KV_KEYS;
+  size_t slots = tc * dkv_slots_cmp(B, T, Nc_cap);
+  if (window > 0) slots += tr * dkv_slots_raw(T, window);
+  return (size_t)B * slots * BW_KV_KEYS * 256;
+}
+
+size_t attn_bwd_ws_bytes(int B, int T, int H, int Nc_cap, int R_cap, int window, bool sparse) {
   const size_t rows = (size_t)B * T;
   size_t n = al256(rows * 2 * H * sizeof(float)) + al256(rows * H * sizeof(float));
   if (sparse) n += 2 * al256(rows * (((size_t)Nc_cap + 31) / 32) * sizeof(uint32_t));
+  const size_t pf = dkv_part_floats(B, T, Nc_cap, R_cap, window);
+  n += al256(pf * sizeof(float)) + al256(pf / (BW_KV_KEYS * 256) * sizeof(uint32_t));
   return n;
 }
 
@@ -650,10 +736,19 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   if (sparse) {
     bm = (uint32_t*)ws;
     rank = (uint32_t*)(ws + al256((size_t)rows * nw * sizeof(uint32_t)));
+    ws += 2 * al256((size_t)rows * nw * sizeof(uint32_t));
   }
+  const size_t pfl = dkv_part_floats(a.B, a.T, a.Nc_cap, a.R_cap, a.window);
+  float* part = (float*)ws;
+  uint32_t* pflag = (uint32_t*)(ws + al256(pfl * sizeof(float)));
+  const int tc = (a.Nc_cap + BW_KV_KEYS - 1) / BW_KV_KEYS;
+  const int sc = dkv_slots_cmp(a.B, a.T, a.Nc_cap);
+  float* part_r = part + (size_t)a.B * tc * sc * BW_KV_KEYS * 256;
+  uint32_t* pflag_r = pflag + (size_t)a.B * tc * sc;
   const size_t nc = (size_t)a.B * a.Nc_cap * 256, nr = (size_t)a.B * a.R_cap * 256;
-  if (nc) bwd_zero_kernel<<<zero_grid(nc), 256, 0, s>>>(a.dkv_cmp, nc);
-  if (nr) bwd_zero_kernel<<<zero_grid(nr), 256, 0, s>>>(a.dkv_raw, nr);
+  // rows with no partial (no compressed tile attended, no window) are zero
+  if (nc && !(a.dense || a.topk > 0)) bwd_zero_kernel<<<zero_grid(nc), 256, 0, s>>>(a.dkv_cmp, nc);
+  if (nr && a.window <= 0) bwd_zero_kernel<<<zero_grid(nr), 256, 0, s>>>(a.dkv_raw, nr);
   if (a.dsink) bwd_zero_kernel<<<1, 256, 0, s>>>(a.dsink, (size_t)a.H);
   if (sparse && a.attn_mass && a.topk > 0)
     bwd_zero_kernel<<<zero_grid((size_t)rows * a.topk), 256, 0, s>>>(a.attn_mass,
@@ -684,25 +779,28 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     else bwd_sink_kernel<32><<<g, 256, 0, s>>>(dz, rows, a.dsink);
   }
 
-#define CSA_BWD_KV(NHH_, KIND_, KV_, CAP_, NCH_, DKV_)                                        \
-  attn_bwd_dkv_kernel<NHH_, KIND_><<<dim3((CAP_ + BW_KV_KEYS - 1) / BW_KV_KEYS, NCH_, a.B),  \
+#define CSA_BWD_KV(NHH_, KIND_, KV_, CAP_, NSL_, PART_, FLAG_)                                \
+  attn_bwd_dkv_kernel<NHH_, KIND_><<<dim3((CAP_ + BW_KV_KEYS - 1) / BW_KV_KEYS, NSL_, a.B),  \
                                      256, 0, s>>>(                                            \
       q, dout, ldw, KV_, CAP_, bm, rank, nw, a.q_pos, a.raw_base, a.n_cmp, a.T, a.topk,       \
-      a.window, a.m, a.scale, DKV_, a.attn_mass)
-  const int ch_all = (a.T + BW_RC - 1) / BW_RC;
+      a.window, a.m, a.scale, NSL_, PART_, FLAG_, a.attn_mass)
   if (a.Nc_cap > 0 && (a.dense || (a.topk > 0))) {
     if (a.H == 64) {
-      if (a.dense) CSA_BWD_KV(2, 1, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
-      else CSA_BWD_KV(2, 0, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
+      if (a.dense) CSA_BWD_KV(2, 1, kvc, a.Nc_cap, sc, part, pflag);
+      else CSA_BWD_KV(2, 0, kvc, a.Nc_cap, sc, part, pflag);
     } else {
-      if (a.dense) CSA_BWD_KV(1, 1, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
-      else CSA_BWD_KV(1, 0, kvc, a.Nc_cap, ch_all, a.dkv_cmp);
+      if (a.dense) CSA_BWD_KV(1, 1, kvc, a.Nc_cap, sc, part, pflag);
+      else CSA_BWD_KV(1, 0, kvc, a.Nc_cap, sc, part, pflag);
     }
+    bwd_dkv_reduce_kernel<<<dim3(tc * 16, a.B), 256, 0, s>>>(part, pflag, tc, sc, a.Nc_cap,
+                                                            a.dkv_cmp);
   }
   if (a.R_cap > 0 && a.window > 0) {
-    const int ch_w = std::min(ch_all, (BW_KV_KEYS + a.window - 1 + BW_RC - 1) / BW_RC);
-    if (a.H == 64) CSA_BWD_KV(2, 2, kvr, a.R_cap, ch_w, a.dkv_raw);
-    else CSA_BWD_KV(1, 2, kvr, a.R_cap, ch_w, a.dkv_raw);
+    const int sr = dkv_slots_raw(a.T, a.window), tr = (a.R_cap + BW_KV_KEYS - 1) / BW_KV_KEYS;
+    if (a.H == 64) CSA_BWD_KV(2, 2, kvr, a.R_cap, sr, part_r, pflag_r);
+    else CSA_BWD_KV(1, 2, kvr, a.R_cap, sr, part_r, pflag_r);
+    bwd_dkv_reduce_kernel<<<dim3(tr * 16, a.B), 256, 0, s>>>(part_r, pflag_r, tr, sr, a.R_cap,
+                                                            a.dkv_raw);
   }
 #undef CSA_BWD_KV
   return hipGetLastError();

@@ -306,7 +306,7 @@ struct AttnBwdArgs {
   float* attn_mass;
   void* ws;
 };
-size_t attn_bwd_ws_bytes(int B, int T, int H, int Nc_cap, bool sparse);
+size_t attn_bwd_ws_bytes(int B, int T, int H, int Nc_cap, int R_cap, int window, bool sparse);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 // helpers shared by the backward passes
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);

@@ -243,8 +243,9 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
     const uint32_t* __restrict__ rank, const float* __restrict__ dIw, int nw, int T, int Nc_cap,
     int topk, float* __restrict__ dk_idx) {
   constexpr int PB = 32 * 128;  // bytes of a pair's 32 head rows
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[PB + 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[PB + 128];
+  constexpr int SB = 2 * 32 * 65 * 4;   // >= PB + 128; the epilogue's rows
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[SB];
   __shared__ int32_t rows_s[KL_RC + 1];
   __shared__ uint32_t shc[16];
   const int kt = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
@@ -378,13 +379,21 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
     if (pi + 2 < npairs) stage(rows_s[2 * pi + 4], rows_s[2 * pi + 5], st0);
     compute(st1, rows_s[2 * pi + 2], rows_s[2 * pi + 3]);
   }
-  if (!touched || !key_in) return;
-  // dk^T: entry jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4
-  float* gk = dk_idx + ((size_t)b * Nc_cap + jw) * KL_DI + 4 * h2;
+  // dk^T (entry jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4)
+  // through LDS into entry rows (stride 65 floats), then atomics of 64
+  // consecutive floats (one entry row) per instruction
+  __syncthreads();  // every wave is done with the staging buffers
+  float* red = (float*)(wave < 2 ? st0 : st1) + (wave & 1) * 32 * 65;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) atomicAdd(gk + 32 * dt + 8 * (r >> 2) + (r & 3), dk[dt][r]);
+    for (int r = 0; r < 16; ++r) red[l32 * 65 + 32 * dt + 8 * (r >> 2) + 4 * h2 + (r & 3)] = dk[dt][r];
+  __syncthreads();
+  const int nkeys = min(32, Nc_cap - (j0 + 32 * wave));  // uniform
+  if (touched) {
+    float* gk0 = dk_idx + ((size_t)b * Nc_cap + j0 + 32 * wave) * KL_DI;
+    for (int k = 0; k < nkeys; ++k) atomicAdd(gk0 + (size_t)k * KL_DI + lane, red[k * 65 + lane]);
+  }
 }
 
 }  // namespace csa

@@ -31,7 +31,7 @@ F32, BF16, FP8, MXFP4 = "f32", "bf16", "fp8", "mxfp4"
 class Workload:
     """One synthetic workload (sizes as the pages' DeepSeek-V4 shapes)."""
     name: str
-    kind: str            # "csa_prefill" | "csa_decode" | "hca_prefill"
+    kind: str            # "csa_prefill" | "csa_train_bwd" | "csa_decode" | "hca_prefill"
     B: int
     ctx: int             # tokens of context per sequence
     T: int               # query tokens per sequence in the call
@@ -61,6 +61,13 @@ WORKLOADS = {
     "csa_prefill_8k_bf16": Workload("csa_prefill_8k_bf16", "csa_prefill", B=1, ctx=8192, T=8192,
                                     H=64, D=128, m=4, overlap=1, window=512, topk=512, H_I=16,
                                     d_I=64, d_model=4096, dt=BF16, idx_dt=BF16, n_cmp=2048, seed=1002),
+    # the backward of the 8K bf16 prefill step (training): attention
+    # gradients, the indexer KL loss and its gradients, both compressors'
+    # gradients; the forward shapes above
+    "csa_train_bwd_8k_bf16": Workload("csa_train_bwd_8k_bf16", "csa_train_bwd", B=1, ctx=8192,
+                                      T=8192, H=64, D=128, m=4, overlap=1, window=512, topk=512,
+                                      H_I=16, d_I=64, d_model=4096, dt=BF16, idx_dt=BF16,
+                                      n_cmp=2048, seed=1007),
     # CSA decode at 128K context, batch 32, fp8 indexer
     "csa_decode_128k_b32": Workload("csa_decode_128k_b32", "csa_decode", B=32, ctx=131072, T=1,
                                     H=64, D=128, m=4, overlap=1, window=512, topk=2048, H_I=16,

@@ -466,9 +466,11 @@ size_t csa_sparse_attn_varlen_workspace_size(int total, int H, int D, int topk, 
  * csa_indexer_topk writes them.  Supported: dt BF16, D = 128, H in {32, 64},
  * topk <= 4096, Nc_cap <= 65536, R_cap <= 2^23, 16-byte aligned tensors.
  * Workspace: csa_sparse_attn_bwd_workspace_size() bytes (contents on entry do
- * not matter).  The gradients of keys shared by many rows are summed with
- * fp32 atomics, so their rounding order, and their last bits, vary from run
- * to run.
+ * not matter; about 10 KB per window row plus 16 MB per 128 compressed rows
+ * of row-chunk partials, 2^26 bytes at most for the compressed part at
+ * B = 1).  The per-key sums over query rows are reduced in a fixed order:
+ * repeated calls give the same bits.  The sink gradient alone is summed with
+ * a few fp32 atomics per head.
  */
 csa_status_t csa_sparse_attn_bwd(int B, int T, int H, int D, int topk, int window, float scale,
                                  const float* sink, const int64_t* q_pos, const void* q,
@@ -477,7 +479,8 @@ csa_status_t csa_sparse_attn_bwd(int B, int T, int H, int D, int topk, int windo
                                  csa_dtype_t dt, const float* lse, const void* dout, float* dq,
                                  float* dkv_cmp, float* dkv_raw, float* dsink, float* attn_mass,
                                  void* workspace, size_t ws_bytes, hipStream_t stream);
-size_t csa_sparse_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap);
+size_t csa_sparse_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap, int R_cap,
+                                          int window);
 
 /*
  * Gradients of hca_dense_attn (the compressed part of J is every visible
@@ -492,7 +495,7 @@ csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, f
                                 const float* lse, const void* dout, float* dq, float* dkv_cmp,
                                 float* dkv_raw, float* dsink, void* workspace, size_t ws_bytes,
                                 hipStream_t stream);
-size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H);
+size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap, int R_cap, int window);
 
 /*
  * Indexer KL loss and its gradients, the training signal of the Lightning
