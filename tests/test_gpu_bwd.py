@@ -346,3 +346,60 @@ def test_compress_bwd_8k_main_compressor():
     rhs = (wkv * _dec(dwk)).sum() + (wgv * _dec(dwg)).sum()
     print("8k compressor identity: %.3e vs %.3e" % (lhs, rhs))
     assert abs(lhs - rhs) <= 1e-3 * (np.abs(xv * _dec(dx)).sum())
+
+
+def test_training_step_end_to_end_small():
+    # forward (both compressors, the indexer, the attention) and backward
+    # (attention, indexer KL loss, both compressors) on the device, against
+    # the oracle's own chain (its entries rounded to the bf16 the caches
+    # store): the index sets agree exactly, then the losses, and the input and
+    # weight gradients within the gradient tolerance (errors compound over
+    # the chain: 2 GRAD_TOL)
+    d = gen.Draw(600)
+    B, T, dm, H, D, HI, dI, m, o, topk, W = 1, 128, 128, 64, 128, 16, 64, 4, 1, 8, 16
+    Nc = T // m
+    x = gen.store(d.normal(B, T, dm), gen.BF16)
+    wk, wg = gen.compressor_weights(d, dm, 2 * D, gen.BF16)
+    wik, wig = gen.compressor_weights(d, dm, dI, gen.BF16)
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, T, 2 * D), gen.BF16)
+    qi = gen.store(d.normal(B, T, HI, dI), gen.BF16)
+    wi = d.normal(B, T, HI).float().contiguous()
+    dout = gen.store(d.normal(B, T, H, D), gen.BF16)
+    z = dev_i64([0])
+    dv = lambda t: t.to(DEV)
+    kv_cmp = torch.empty(B, Nc, 2 * D, dtype=torch.bfloat16, device=DEV)
+    k_idx = torch.empty(B, Nc, dI, dtype=torch.bfloat16, device=DEV)
+    csa.csa_compress(dv(x), dv(wk), dv(wg), z, m, o, kv_cmp)
+    csa.csa_compress(dv(x), dv(wik), dv(wig), z, m, o, k_idx)
+    idx, _ = csa.csa_indexer_topk(dv(qi), dv(wi), k_idx, m, topk, z, dev_i32([Nc]))
+    out, lse = csa.csa_sparse_attn(dv(q), kv_cmp, idx, dv(kv_raw), W, z, z, want_lse=True)
+    dq, dkc, dkr, _, mass = csa.csa_sparse_attn_bwd(dv(q), kv_cmp, idx, dv(kv_raw), W, z, z, lse,
+                                                    dv(dout), want_mass=True)
+    loss, dqi, dwi, dki = csa.csa_indexer_kl_bwd(dv(qi), dv(wi), k_idx, idx, mass)
+    dx1, dwk, dwg, _ = csa.csa_compress_bwd(dv(x), dv(wk), dv(wg), m, o, Nc, dkc)
+    dx2, dwik, dwig, _ = csa.csa_compress_bwd(dv(x), dv(wik), dv(wig), m, o, Nc, dki)
+    torch.cuda.synchronize()
+    # the oracle's chain
+    hx, hwk, hwg, hwik, hwig = (gen.host_bits(t) for t in (x, wk, wg, wik, wig))
+    c1, _, _ = orc.compress(hx, hwk, hwg, m, o, 0, Nc, want_state=False)
+    c2, _, _ = orc.compress(hx, hwik, hwig, m, o, 0, Nc, want_state=False)
+    enc = np.vectorize(orc.bf16_encode, otypes=[np.uint16])
+    r_kv, r_k = enc(c1), enc(c2)
+    r_idx = orc.indexer_topk(gen.host_bits(qi), wi.numpy(), r_k, m, topk, 0, Nc)[0]
+    assert np.array_equal(idx.cpu().numpy(), r_idx)
+    hdo = _dec(dout)
+    _, rkc, rkr, _, rmass = orc.attn_bwd(gen.host_bits(q), r_kv, r_idx, gen.host_bits(kv_raw), W,
+                                         0, 0, hdo, want_mass=True)
+    rl, rqi, rwi, rki = orc.indexer_kl_bwd(gen.host_bits(qi), wi.numpy(), r_k, r_idx, rmass)
+    rx1, rwk, rwg, _ = orc.compress_bwd(hx, hwk, hwg, m, o, Nc, rkc)
+    rx2, rwik, rwig, _ = orc.compress_bwd(hx, hwik, hwig, m, o, Nc, rki)
+    assert np.all(np.abs(_dec(loss) - rl) <= 1e-3 * (1 + np.abs(rl)))
+    tol = 2 * GRAD_TOL
+    _rows_rel(_dec(dqi), rqi, "e2e dq_idx", tol)
+    _rows_rel(_dec(dwi), rwi, "e2e dw_idx", tol)
+    _rows_rel(_dec(dx1) + _dec(dx2), rx1 + rx2, "e2e dx", tol)
+    _rows_rel(_dec(dwk), rwk, "e2e dw_kv", tol)
+    _rows_rel(_dec(dwg), rwg, "e2e dw_gate", tol)
+    _rows_rel(_dec(dwik), rwik, "e2e indexer dw_kv", tol)
+    _rows_rel(_dec(dwig), rwig, "e2e indexer dw_gate", tol)
