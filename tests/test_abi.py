@@ -182,3 +182,62 @@ def test_compress_ex_rejects_bad_rotary_slices(L):
                                8, None, C.byref(o), None, 0, None)
         assert rc == 1, (dim, off, base)
         assert b"rope" in L.csa_last_error()
+
+
+def test_backward_entry_points_validate_before_any_launch(L):
+    vp = C.c_void_p
+    d = vp(16)   # never dereferenced: validation fails first
+    f = C.c_float(0.088)
+    # attention backward: fp32 inputs are not supported; dsink without sink;
+    # a too small workspace; too many index slots
+    rc = L.csa_sparse_attn_bwd(1, 8, 64, 128, 4, 4, f, None, d, d, d, 16, d, d, 16, d, 0, d, d,
+                               d, d, d, None, None, d, 10 ** 9, None)
+    assert rc == 2 and b"BF16" in L.csa_last_error()
+    rc = L.csa_sparse_attn_bwd(1, 8, 64, 128, 4, 4, f, None, d, d, d, 16, d, d, 16, d, 1, d, d,
+                               d, d, d, d, None, d, 10 ** 9, None)
+    assert rc == 1 and b"dsink needs sink" in L.csa_last_error()
+    rc = L.csa_sparse_attn_bwd(1, 8, 64, 128, 4, 4, f, None, d, d, d, 16, d, d, 16, d, 1, d, d,
+                               d, d, d, None, None, d, 1, None)
+    assert rc == 3
+    rc = L.csa_sparse_attn_bwd(1, 8, 64, 128, 5000, 4, f, None, d, d, d, 16, d, d, 16, d, 1, d,
+                               d, d, d, d, None, None, d, 10 ** 9, None)
+    assert rc == 2 and b"topk" in L.csa_last_error()
+    rc = L.hca_dense_attn_bwd(1, 8, 48, 128, 4, 4, f, None, d, d, d, d, 16, d, 16, d, 1, d, d,
+                              d, d, d, None, d, 10 ** 9, None)
+    assert rc == 2 and b"H in {32, 64}" in L.csa_last_error()
+    # indexer KL loss: geometry, topk limit, a missing mass
+    rc = L.csa_indexer_kl_bwd(1, 8, 8, 64, 32, 4, d, d, d, 1, d, d, None, d, d, d, d, d,
+                              10 ** 9, None)
+    assert rc == 2 and b"H_I = 16" in L.csa_last_error()
+    rc = L.csa_indexer_kl_bwd(1, 8, 16, 64, 32, 2048, d, d, d, 1, d, d, None, d, d, d, d, d,
+                              10 ** 9, None)
+    assert rc == 2 and b"topk" in L.csa_last_error()
+    rc = L.csa_indexer_kl_bwd(1, 8, 16, 64, 32, 4, d, d, d, 1, d, None, None, d, d, d, d, d,
+                              10 ** 9, None)
+    assert rc == 1
+    # compressor backward: fp32 tokens, a rotation of a width that is not a
+    # power of two, dape without ape, d_model not a multiple of 64
+    rc = L.csa_compress_bwd(1, 64, 128, 32, 4, 1, 0, d, d, d, 0, None, 16, d, d, d, d, None, d,
+                            10 ** 9, None)
+    assert rc == 2 and b"BF16" in L.csa_last_error()
+    rc = L.csa_compress_bwd(1, 64, 128, 48, 4, 1, 1, d, d, d, 1, None, 16, d, d, d, d, None, d,
+                            10 ** 9, None)
+    assert rc == 1 and b"power of two" in L.csa_last_error()
+    rc = L.csa_compress_bwd(1, 64, 128, 32, 4, 1, 0, d, d, d, 1, None, 16, d, d, d, d, d, d,
+                            10 ** 9, None)
+    assert rc == 1 and b"dape needs ape" in L.csa_last_error()
+    rc = L.csa_compress_bwd(1, 64, 100, 32, 4, 1, 0, d, d, d, 1, None, 16, d, d, d, d, None, d,
+                            10 ** 9, None)
+    assert rc == 2 and b"multiple of 64" in L.csa_last_error()
+
+
+def test_backward_workspace_sizes(L):
+    # the attention backward's workspace grows with the window rows and the
+    # compressed entries, and covers the per-row terms at least
+    a = L.csa_sparse_attn_bwd_workspace_size(1, 8192, 64, 2048, 8192, 512)
+    assert a >= 8192 * (2 * 64 + 64) * 4 and a < 512 * 2 ** 20
+    assert L.csa_sparse_attn_bwd_workspace_size(1, 8192, 64, 2048, 8192, 0) < a
+    assert L.hca_dense_attn_bwd_workspace_size(1, 4096, 64, 8192, 4607, 512) > 0
+    assert L.csa_indexer_kl_bwd_workspace_size(1, 8192, 2048, 512) >= 8192 * 512 * 4
+    assert L.csa_compress_bwd_workspace_size(1, 8192, 256, 4, 2048) >= 8192 * 512 * 6
+    assert L.csa_sparse_attn_bwd_workspace_size(0, 8, 64, 16, 16, 4) == 0
