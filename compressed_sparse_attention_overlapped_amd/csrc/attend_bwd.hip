@@ -139,9 +139,9 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
     float scale, float* __restrict__ dq, float* __restrict__ ldw, float* __restrict__ dz) {
   constexpr int H = 32 * NHH;
   constexpr int NI = 16 / NHH;  // load instructions per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t tile0[BW_TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t tile1[BW_TILEB];
-  __shared__ int32_t idx_s[DENSE ? 1 : BW_IDX_MAX];
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * BW_TILEB];
+  extern __shared__ int32_t idx_s[];  // [topk] (CSA form; sized at launch, so that four
+                                      // workgroups fit one CU's LDS at topk 512)
   __shared__ int32_t sh_last;
   const int row = blockIdx.x, b = row / T, t = row - b * T;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -320,25 +320,17 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
       }
     };
     auto sweep = [&](auto pass_tag) {
-      issue(0, tile0);
-      for (int ti = 0; ti < ntiles; ti += 2) {
+      issue(0, tiles);
+      int cur = 0;
+      for (int ti = 0; ti < ntiles; ++ti) {
         bw_wait_loads();
         __syncthreads();
-        if (ti + 1 < ntiles) issue(ti + 1, tile1);
-        {
-          const uint32_t vm = vmask(ti);
-          if (vm) compute(tile0, vm, pass_tag);
-        }
-        if (ti + 1 >= ntiles) break;
-        bw_wait_loads();
-        __syncthreads();
-        if (ti + 2 < ntiles) issue(ti + 2, tile0);
-        {
-          const uint32_t vm = vmask(ti + 1);
-          if (vm) compute(tile1, vm, pass_tag);
-        }
+        if (ti + 1 < ntiles) issue(ti + 1, tiles + (cur ^ 1) * BW_TILEB);
+        const uint32_t vm = vmask(ti);
+        if (vm) compute(tiles + cur * BW_TILEB, vm, pass_tag);
+        cur ^= 1;
       }
-      __syncthreads();  // every wave is done with both buffers
+      __syncthreads();  // every wave is done with the buffers
     };
     sweep(std::integral_constant<int, 0>{});
     dlt = dacc + lane_xor32(dacc);  // the other half of the keys
@@ -396,7 +388,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
   __shared__ uint32_t rows_w[KIND == 0 ? BW_RC : 1][4];   // the row's bitmap words of the tile
   __shared__ uint32_t rows_r[KIND == 0 ? BW_RC : 1][4];   // and their ranks
   __shared__ uint32_t sh[16];
-  const int kt = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+  // Workgroup order: consecutive workgroups go to the 8 XCDs in turn, so each
+  // XCD takes a contiguous range of the logical order (key tile fastest for
+  // compressed entries, whose tiles all read the same query rows; row chunk
+  // fastest for window tiles, whose neighbours share rows), and workgroups
+  // reading the same Q / dO rows share one L2.
+  const int ntl = gridDim.x, nwg = ntl * nslot * gridDim.z;
+  const int lin = blockIdx.x + ntl * (blockIdx.y + nslot * blockIdx.z);
+  const int xcd = lin & 7, xq = nwg >> 3, xr = nwg & 7;
+  const int lg = xcd * xq + min(xcd, xr) + (lin >> 3);
+  int kt, chunk, b;
+  if (KIND == 2) {
+    chunk = lg % nslot;
+    kt = (lg / nslot) % ntl;
+  } else {
+    kt = lg % ntl;
+    chunk = (lg / ntl) % nslot;
+  }
+  b = lg / (ntl * nslot);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
@@ -762,7 +771,8 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
     bwd_bitmap_kernel<<<rows, 256, 0, s>>>(a.idx, a.topk, a.Nc_cap, nw, bm, rank);
 
 #define CSA_BWD_DQ(NHH_, DENSE_)                                                              \
-  attn_bwd_dq_kernel<NHH_, DENSE_><<<rows, 64 * NHH_, 0, s>>>(                                \
+  attn_bwd_dq_kernel<NHH_, DENSE_><<<rows, 64 * NHH_, DENSE_ ? 0 : sizeof(int32_t) * a.topk,  \
+                                     s>>>(                                                    \
       q, dout, a.lse, a.sink, kvc, a.idx, kvr, a.q_pos, a.raw_base, a.n_cmp, a.T, a.Nc_cap,   \
       a.R_cap, sparse ? a.topk : 0, a.window, a.m, a.scale, a.dq, ldw, dzp)
   if (a.H == 64) {
