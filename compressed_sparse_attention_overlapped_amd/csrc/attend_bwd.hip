@@ -139,7 +139,10 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
     float scale, float* __restrict__ dq, float* __restrict__ ldw, float* __restrict__ dz) {
   constexpr int H = 32 * NHH;
   constexpr int NI = 16 / NHH;  // load instructions per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * BW_TILEB];
+  // two distinct buffers, each named at compile time in the loop below, so the
+  // compiler sees that a tile's reads do not touch the buffer being loaded
+  __shared__ __attribute__((aligned(1024))) uint8_t tile0[BW_TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile1[BW_TILEB];
   extern __shared__ int32_t idx_s[];  // [topk] (CSA form; sized at launch, so that four
                                       // workgroups fit one CU's LDS at topk 512)
   __shared__ int32_t sh_last;
@@ -186,6 +189,8 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
     if (rb > R_cap - 1) rb = R_cap - 1;
   }
   const int n_w = rb >= ra ? (int)((rb - ra + BW_KT) / BW_KT) : 0;
+  // (window rows are cache rows, below 2^23: 32-bit from here on)
+  const int ra32 = (int)ra, rb32 = (int)rb;
   const int ntiles = n_a + n_w;
 
   f32x16 acc[4];
@@ -243,8 +248,8 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
             grow = v >= 0 ? (uint32_t)v : 0u;
           }
         } else {
-          const int64_t rr = ra + (int64_t)(ti - n_a) * BW_KT + r;
-          grow = rr <= rb ? (uint32_t)rr : 0u;
+          const int rr = ra32 + (ti - n_a) * BW_KT + r;
+          grow = rr <= rb32 ? (uint32_t)rr : 0u;
         }
         const uint32_t c = (uint32_t)(l32 ^ bw_swz(r));
         bw_dma(base + (size_t)grow * BW_ROWB + 16u * c, dst + 1024 * i);
@@ -257,7 +262,7 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
         if constexpr (DENSE) ok = kk < nv;
         else ok = kk < topk && idx_s[kk] >= 0;
       } else {
-        ok = ra + (int64_t)(ti - n_a) * BW_KT + l32 <= rb;
+        ok = ra32 + (ti - n_a) * BW_KT + l32 <= rb32;
       }
       return (uint32_t)__ballot(ok);
     };
@@ -319,18 +324,23 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
           }
       }
     };
+    // step of tile ti in buffer BUF: publish it, start tile ti + 1 in the
+    // other buffer (every wave finished tile ti - 1 before the barrier)
+    auto step = [&](auto buf_tag, int ti, auto pass_tag) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      bw_wait_loads();
+      __syncthreads();
+      if (ti + 1 < ntiles) issue(ti + 1, BUF ? tile0 : tile1);
+      const uint32_t vm = vmask(ti);
+      if (vm) compute(BUF ? tile1 : tile0, vm, pass_tag);
+    };
     auto sweep = [&](auto pass_tag) {
-      issue(0, tiles);
-      int cur = 0;
-      for (int ti = 0; ti < ntiles; ++ti) {
-        bw_wait_loads();
-        __syncthreads();
-        if (ti + 1 < ntiles) issue(ti + 1, tiles + (cur ^ 1) * BW_TILEB);
-        const uint32_t vm = vmask(ti);
-        if (vm) compute(tiles + cur * BW_TILEB, vm, pass_tag);
-        cur ^= 1;
+      issue(0, tile0);
+      for (int ti = 0; ti < ntiles; ti += 2) {
+        step(std::integral_constant<int, 0>{}, ti, pass_tag);
+        if (ti + 1 < ntiles) step(std::integral_constant<int, 1>{}, ti + 1, pass_tag);
       }
-      __syncthreads();  // every wave is done with the buffers
+      __syncthreads();  // every wave is done with both buffers
     };
     sweep(std::integral_constant<int, 0>{});
     dlt = dacc + lane_xor32(dacc);  // the other half of the keys
@@ -734,6 +744,8 @@ hipError_t launch_sel_bitmap(const int32_t* idx, int rows, int topk, int Nc_cap,
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   const int rows = a.B * a.T;
   const bool sparse = !a.dense;
+  // the dq kernel stages a row's index slots in LDS (4 bytes each)
+  if (sparse && a.topk > BW_IDX_MAX) return hipErrorInvalidValue;
   const int nw = (a.Nc_cap + 31) / 32;
   char* ws = (char*)a.ws;
   float* ldw = (float*)ws;
