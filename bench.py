@@ -269,7 +269,7 @@ def setup_train_bwd(w):
         st["dx_" + k] = torch.empty(B, S, w.d_model, **f32)
         st["dwk_" + k] = torch.empty(E, w.d_model, **f32)
         st["dwg_" + k] = torch.empty(E, w.d_model, **f32)
-        st["wsb_" + k] = torch.empty(csa.lib().csa_compress_bwd_workspace_size(B, S, E, w.m, w.n_cmp),
+        st["wsb_" + k] = torch.empty(csa.lib().csa_compress_bwd_workspace_size(B, S, w.d_model, E, w.m, w.n_cmp),
                                      dtype=torch.uint8, device=DEV)
     st["wsb_a"] = torch.empty(csa.lib().csa_sparse_attn_bwd_workspace_size(
         B, S, w.H, w.n_cmp, S, w.window), dtype=torch.uint8, device=DEV)

@@ -157,7 +157,7 @@ def lib():
         L.csa_indexer_kl_bwd_workspace_size.restype = C.c_size_t
         L.csa_compress_bwd.argtypes = [i32] * 7 + [vp, vp, vp, i32, vp, i32] + [vp] * 5 + [vp, sz, vp]
         L.csa_compress_bwd.restype = C.c_int
-        L.csa_compress_bwd_workspace_size.argtypes = [i32] * 5
+        L.csa_compress_bwd_workspace_size.argtypes = [i32] * 6
         L.csa_compress_bwd_workspace_size.restype = C.c_size_t
         L.csa_status_string.argtypes = [i32]
         L.csa_status_string.restype = C.c_char_p
@@ -486,7 +486,7 @@ def csa_compress_bwd(x, w_kv, w_gate, m, overlap, Nc_cap, d_out, ape=None, rotat
     dw_gate = torch.empty(E, d_model, **f32) if dw_gate is None else dw_gate
     if ape is not None and want_dape and dape is None:
         dape = torch.empty((1 + overlap) * m, E, **f32)
-    ws, nb = _workspace(lib().csa_compress_bwd_workspace_size(B, L, E, m, Nc_cap), x, workspace)
+    ws, nb = _workspace(lib().csa_compress_bwd_workspace_size(B, L, d_model, E, m, Nc_cap), x, workspace)
     rc = lib().csa_compress_bwd(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(x), _p(w_kv),
                                 _p(w_gate), _DT[x.dtype], _p(ape), Nc_cap, _p(d_out), _p(dx),
                                 _p(dw_kv), _p(dw_gate), _p(dape), _p(ws), nb, _stream(x))

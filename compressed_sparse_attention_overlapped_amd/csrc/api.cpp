@@ -713,9 +713,9 @@ csa_status_t csa_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int 
   return hip_status(csa_host::launch_indexer_kl_bwd(a, stream), fn);
 }
 
-size_t csa_compress_bwd_workspace_size(int B, int L, int E, int m, int Nc_cap) {
-  if (B <= 0 || L <= 0 || E <= 0 || m < 1 || Nc_cap < 0) return 0;
-  return csa_host::compress_bwd_ws_bytes(B, L, E, m, Nc_cap);
+size_t csa_compress_bwd_workspace_size(int B, int L, int d_model, int E, int m, int Nc_cap) {
+  if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0 || m < 1 || Nc_cap < 0) return 0;
+  return csa_host::compress_bwd_ws_bytes(B, L, d_model, E, m, Nc_cap);
 }
 
 csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
@@ -741,7 +741,7 @@ csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overl
     return fail(CSA_E_UNSUPPORTED, "%s: B * L too large", fn);
   if (!aligned16(x) || !aligned16(w_kv) || !aligned16(w_gate))
     return fail(CSA_E_UNSUPPORTED, "%s: x and the weights must be 16-byte aligned", fn);
-  const size_t need = csa_host::compress_bwd_ws_bytes(B, L, E, m, Nc_cap);
+  const size_t need = csa_host::compress_bwd_ws_bytes(B, L, d_model, E, m, Nc_cap);
   if (ws_bytes < need || !workspace)
     return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   csa_host::CompressBwdArgs a{B,     L,     d_model, E,       m,       overlap, rotate, Nc_cap,

@@ -349,7 +349,7 @@ struct CompressBwdArgs {
   float* dape;
   void* ws;
 };
-size_t compress_bwd_ws_bytes(int B, int L, int E, int m, int Nc_cap);
+size_t compress_bwd_ws_bytes(int B, int L, int d_model, int E, int m, int Nc_cap);
 hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s);
 hipError_t launch_indexer_kl_bwd(const IndexerKlArgs& a, hipStream_t s);
 

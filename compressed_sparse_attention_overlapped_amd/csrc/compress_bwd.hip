@@ -16,9 +16,11 @@
 // rotation, the gradient through it: H dC / sqrt(E), H symmetric); a token
 // kernel (owner computes: token j takes its share of the one or two entries
 // whose windows hold it, so no two threads write one element, and dape is
-// summed per workgroup in LDS, then one atomic per slot and channel); and
-// four plain GEMMs for dx and the weight gradients (rocBLAS, bf16 operands,
-// fp32 accumulation and output).
+// summed per workgroup in LDS, then one atomic per slot and channel); and two
+// plain GEMMs (rocBLAS, bf16 operands, fp32 accumulation and output) over the
+// [dP | dG] rows: dx against the two weights stacked as one [2E, d_model]
+// matrix (one pass over the fp32 dx instead of a write and an accumulate),
+// and both weight gradients as one [2E, d_model] product, split afterwards.
 #include <rocblas/rocblas.h>
 
 #include <algorithm>
@@ -127,12 +129,17 @@ using namespace csa;
 
 static size_t cb_al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t compress_bwd_ws_bytes(int B, int L, int E, int m, int Nc_cap) {
+// workspace: P | G fp32 [M, 2E], dP | dG bf16 [M, 2E], the entries' stats and
+// gradients, the stacked weights bf16 [2E, d_model] and the stacked weight
+// gradients fp32 [2E, d_model]
+size_t compress_bwd_ws_bytes(int B, int L, int d_model, int E, int m, int Nc_cap) {
   const size_t M = (size_t)B * L;
   const size_t n_ent = std::min<size_t>((size_t)L / m, (size_t)Nc_cap);
+  const size_t WK = (size_t)2 * E * d_model;
   return cb_al256(M * 2 * E * sizeof(float)) + cb_al256(M * 2 * E * sizeof(uint16_t)) +
          cb_al256((size_t)B * n_ent * E * 2 * sizeof(float)) +
-         cb_al256((size_t)B * n_ent * E * sizeof(float));
+         cb_al256((size_t)B * n_ent * E * sizeof(float)) + cb_al256(WK * sizeof(uint16_t)) +
+         cb_al256(WK * sizeof(float));
 }
 
 // one rocBLAS handle per device, created on first use
@@ -175,7 +182,16 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   float* stats = (float*)ws;
   ws += cb_al256((size_t)a.B * std::max(n_ent, 0) * E * 2 * sizeof(float));
   float* gent = (float*)ws;
-  hipError_t e = launch_proj_pg(a.x, a.w_kv, a.w_gate, M, E, K, pg, s);
+  ws += cb_al256((size_t)a.B * std::max(n_ent, 0) * E * sizeof(float));
+  uint16_t* wcat = (uint16_t*)ws;
+  ws += cb_al256((size_t)2 * E * K * sizeof(uint16_t));
+  float* dwcat = (float*)ws;
+  const size_t wb = (size_t)E * K * sizeof(uint16_t), dwb = (size_t)E * K * sizeof(float);
+  hipError_t e = hipMemcpyAsync(wcat, a.w_kv, wb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(wcat + (size_t)E * K, a.w_gate, wb, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  e = launch_proj_pg(a.x, a.w_kv, a.w_gate, M, E, K, pg, s);
   if (e != hipSuccess) return e;
   const int Sw = (1 + a.overlap) * a.m;
   if (a.dape) {
@@ -194,17 +210,18 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   rocblas_handle hb = blas_handle(e);
   if (!hb) return e;
   if (rocblas_set_stream(hb, s) != rocblas_status_success) return hipErrorUnknown;
-  // row-major views as column-major: dx^T (K x M) = W_kv^T dP^T + W_gate^T dG^T
-  bool ok = gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, E, a.w_kv, K,
+  // row-major views as column-major: dx^T (K x M) = [W_kv; W_gate]^T [dP | dG]^T,
+  // [dW_kv; dW_gate]^T (K x 2E) = x^T [dP | dG]  (x: K x M column-major)
+  bool ok = gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, N, wcat, K,
                           dpg, N, 0.0f, a.dx, K) &&
-            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, E, a.w_gate, K,
-                          dpg + E, N, 1.0f, a.dx, K) &&
-            // dW_kv^T (K x E) = x^T dP  (x: K x M column-major; dP^T viewed E x M)
-            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, E, M, a.x, K,
-                          dpg, N, 0.0f, a.dw_kv, K) &&
-            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, E, M, a.x, K,
-                          dpg + E, N, 0.0f, a.dw_gate, K);
-  return ok ? hipGetLastError() : hipErrorUnknown;
+            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, N, M, a.x,
+                          K, dpg, N, 0.0f, dwcat, K);
+  if (!ok) return hipErrorUnknown;
+  e = hipMemcpyAsync(a.dw_kv, dwcat, dwb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(a.dw_gate, dwcat + (size_t)E * K, dwb, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
 }
 
 }  // namespace csa_host

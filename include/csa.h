@@ -551,14 +551,16 @@ size_t csa_indexer_kl_bwd_workspace_size(int B, int T, int Nc_cap, int topk);
  * dP and dG enter the weight and input products as bf16 (fp32 accumulation);
  * those products run on rocBLAS.  Supported: in_dt BF16, E <= 1024, d_model a
  * multiple of 64, (1 + overlap) m <= 1024.  Workspace:
- * csa_compress_bwd_workspace_size() bytes (contents on entry do not matter).
+ * csa_compress_bwd_workspace_size() bytes (contents on entry do not matter;
+ * it holds P | G, dP | dG, the two weights stacked and their gradients
+ * stacked).
  */
 csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                               const void* x, const void* w_kv, const void* w_gate,
                               csa_dtype_t in_dt, const float* ape, int Nc_cap, const float* d_out,
                               float* dx, float* dw_kv, float* dw_gate, float* dape,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
-size_t csa_compress_bwd_workspace_size(int B, int L, int E, int m, int Nc_cap);
+size_t csa_compress_bwd_workspace_size(int B, int L, int d_model, int E, int m, int Nc_cap);
 
 /* Static text of a status code. */
 const char* csa_status_string(csa_status_t status);

@@ -239,5 +239,6 @@ def test_backward_workspace_sizes(L):
     assert L.csa_sparse_attn_bwd_workspace_size(1, 8192, 64, 2048, 8192, 0) < a
     assert L.hca_dense_attn_bwd_workspace_size(1, 4096, 64, 8192, 4607, 512) > 0
     assert L.csa_indexer_kl_bwd_workspace_size(1, 8192, 2048, 512) >= 8192 * 512 * 4
-    assert L.csa_compress_bwd_workspace_size(1, 8192, 256, 4, 2048) >= 8192 * 512 * 6
+    assert L.csa_compress_bwd_workspace_size(1, 8192, 4096, 256, 4, 2048) >= 8192 * 512 * 6 + 512 * 4096 * 6
+    assert L.csa_compress_bwd_workspace_size(1, 8192, 0, 256, 4, 2048) == 0
     assert L.csa_sparse_attn_bwd_workspace_size(0, 8, 64, 16, 16, 4) == 0
