@@ -69,8 +69,12 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
     const float* __restrict__ mass, const float* __restrict__ gscale, int T, int Nc_cap, int topk,
     float* __restrict__ loss, float* __restrict__ dq_idx, float* __restrict__ dw_idx,
     float* __restrict__ dIw) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[KL_CH * 128];  // key rows of a chunk
-  __shared__ __attribute__((aligned(16))) uint16_t cs[KL_HI][KL_CH];  // C^T of a chunk (bf16)
+  // key rows of a chunk: 16-byte chunk c of row r at slot c ^ (r & 7), so the
+  // row-per-lane staging stores and the transposing reads spread over the banks
+  __shared__ __attribute__((aligned(16))) uint8_t ks[KL_CH * 128];
+  // C^T of a chunk (bf16), rows padded by 16 bytes: the 16 head rows read at
+  // one slot fall in distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t cs[KL_HI][KL_CH + 8];
   __shared__ float sh[8];
   __shared__ float dws[4][KL_HI];
   const int row = blockIdx.x, b = row / T;
@@ -187,7 +191,7 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
       const u32x4* src = (const u32x4*)(kb + (size_t)(j >= 0 ? j : 0) * KL_DI);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        ((u32x4*)(ks + 128 * r))[c] = j >= 0 ? src[c] : u32x4{0u, 0u, 0u, 0u};
+        ((u32x4*)(ks + 128 * r))[c ^ (r & 7)] = j >= 0 ? src[c] : u32x4{0u, 0u, 0u, 0u};
     }
     // slots past the last tile: zero (their key rows are zero too)
     if (c0 + tid >= ntile * 16)
@@ -218,7 +222,9 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 32 * st + 8 * gg + 4 * e + (jj >> 2);
-          t[e] = __builtin_bit_cast(u32x2, kl_read_tr16(ks + 128 * r + 2 * (16 * wave + 4 * (jj & 3))));
+          const int d0 = 16 * wave + 4 * (jj & 3);  // first dim: chunk d0 / 8, byte 2 (d0 % 8)
+          t[e] = __builtin_bit_cast(
+              u32x2, kl_read_tr16(ks + 128 * r + 16 * ((d0 >> 3) ^ (r & 7)) + 2 * (d0 & 7)));
         }
         ka = __builtin_bit_cast(bf16x8, u32x4{t[0][0], t[0][1], t[1][0], t[1][1]});
       }
