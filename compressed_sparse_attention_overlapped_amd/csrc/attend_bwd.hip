@@ -230,29 +230,43 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
     }
     const char* cmp_b = (const char*)(kv_cmp + (size_t)b * Nc_cap * 256);
     const char* raw_b = (const char*)(kv_raw + (size_t)b * R_cap * 256);
-    // tile ti into dst: load instruction i covers tile rows 2 i, 2 i + 1
+    // tile ti into dst: load instruction i = wave + NHH k covers tile rows
+    // 2 i, 2 i + 1 (lane half h2); the lane's source is a 32-bit byte offset
+    // from the segment's uniform base (cache rows are below 2^23), and the
+    // index slots of a gathered tile are read before the first load
     auto issue = [&](int ti, uint8_t* dst) {
-      const bool seg_a = ti < n_a;  // uniform
-      const char* base = seg_a ? cmp_b : raw_b;
+      const char* base = ti < n_a ? cmp_b : raw_b;
+      // groups of (at most) eight instructions: offsets, then the loads
 #pragma unroll
-      for (int k = 0; k < NI; ++k) {
-        const int i = wave + NHH * k;
-        const int r = 2 * i + h2;
-        uint32_t grow;
-        if (seg_a) {
-          const int kk = ti * BW_KT + r;
-          if constexpr (DENSE) {
-            grow = kk < nv ? (uint32_t)kk : 0u;
-          } else {
-            const int v = kk < topk ? idx_s[kk] : -1;
-            grow = v >= 0 ? (uint32_t)v : 0u;
+      for (int k0 = 0; k0 < NI; k0 += 8) {
+        constexpr int NG = NI < 8 ? NI : 8;
+        uint32_t off[NG];
+        if (ti < n_a) {  // uniform: compressed entries
+#pragma unroll
+          for (int u = 0; u < NG; ++u) {
+            const int r = 2 * (wave + NHH * (k0 + u)) + h2;
+            const int kk = ti * BW_KT + r;
+            uint32_t grow;
+            if constexpr (DENSE) {
+              grow = kk < nv ? (uint32_t)kk : 0u;
+            } else {
+              // (n_a > 0: some slot is valid, so topk >= 1)
+              const int v = idx_s[min(kk, topk - 1)];
+              grow = kk < topk && v >= 0 ? (uint32_t)v : 0u;
+            }
+            off[u] = grow * (uint32_t)BW_ROWB + 16u * (uint32_t)(l32 ^ bw_swz(r));
           }
-        } else {
-          const int rr = ra32 + (ti - n_a) * BW_KT + r;
-          grow = rr <= rb32 ? (uint32_t)rr : 0u;
+        } else {  // window rows
+#pragma unroll
+          for (int u = 0; u < NG; ++u) {
+            const int r = 2 * (wave + NHH * (k0 + u)) + h2;
+            const int rr = ra32 + (ti - n_a) * BW_KT + r;
+            const uint32_t grow = rr <= rb32 ? (uint32_t)rr : 0u;
+            off[u] = grow * (uint32_t)BW_ROWB + 16u * (uint32_t)(l32 ^ bw_swz(r));
+          }
         }
-        const uint32_t c = (uint32_t)(l32 ^ bw_swz(r));
-        bw_dma(base + (size_t)grow * BW_ROWB + 16u * c, dst + 1024 * i);
+#pragma unroll
+        for (int u = 0; u < NG; ++u) bw_dma(base + off[u], dst + 1024 * (wave + NHH * (k0 + u)));
       }
     };
     auto vmask = [&](int ti) -> uint32_t {
@@ -296,22 +310,24 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
           p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], of[s0 + u], p_acc, 0, 0, 0);
       }
       // keys of register r: 8 (r / 4) + 4 h2 + r % 4
+      // partial tiles zero the probabilities of absent keys; full tiles
+      // (uniform test) skip the per-key selects
       const uint32_t mv = vm >> (4 * h2);
+      const bool full = vm == 0xffffffffu;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], sc2, -lse2));
+      if (!full)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((mv >> (8 * (r >> 2) + (r & 3))) & 1u)) p[r] = 0.0f;
       if constexpr (PASS == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool on = (mv >> (8 * (r >> 2) + (r & 3))) & 1u;
-          const float p = on ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], sc2, -lse2)) : 0.0f;
-          dacc = __builtin_fmaf(p, p_acc[r], dacc);
-        }
+        for (int r = 0; r < 16; ++r) dacc = __builtin_fmaf(p[r], p_acc[r], dacc);
       } else {
         bf16x8 dsb[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool on = (mv >> (8 * (r >> 2) + (r & 3))) & 1u;
-          const float p = on ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], sc2, -lse2)) : 0.0f;
-          dsb[r >> 3][r & 7] = (__bf16)(p * (p_acc[r] - dlt));
-        }
+        for (int r = 0; r < 16; ++r) dsb[r >> 3][r & 7] = (__bf16)(p[r] * (p_acc[r] - dlt));
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -480,21 +496,26 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
   }
   // stage row t into dst: Q and dO rows of 4 heads per load instruction
   // (lane l: head 4 i + l / 16, chunk l % 16 at slot chunk ^ bw_swz(head)),
-  // then lse2 | delta (8 H bytes) by the lanes that cover it
-  auto stage = [&](int t, uint8_t* dst) {
+  // instructions i = wave, wave + 4, ... of each; then lse2 | delta (8 H
+  // bytes) by the lanes of wave 0 that cover it.  Sources are 32-bit byte
+  // offsets from the row's uniform base.
+  static_assert(NQI % 4 == 0, "Q load instructions split evenly over 4 waves");
+  auto stage = [&](int t_row, uint8_t* dst) {
+    const int t = __builtin_amdgcn_readfirstlane(t_row);  // (one row per workgroup step)
     const size_t rq = ((size_t)b * T + t) * H;
+    const char* qrow = (const char*)(q + rq * 128);
+    const char* orow = (const char*)(dout + rq * 128);
     const int hh = lane >> 4, cc = lane & 15;
-    for (int i = wave; i < 2 * NQI + 1; i += 4) {
-      if (i < 2 * NQI) {
-        const int qi = i < NQI ? i : i - NQI;
-        const uint16_t* src = i < NQI ? q : dout;
-        const int hd = 4 * qi + hh;
-        const int c = cc ^ bw_swz(hd);
-        bw_dma(src + (rq + hd) * 128 + 8 * c, dst + (i < NQI ? 0 : QB) + 1024 * qi);
-      } else if (lane < H / 2) {
-        bw_dma(ldw + ((size_t)b * T + t) * 2 * H + 4 * lane, dst + 2 * QB);
-      }
+#pragma unroll
+    for (int u = 0; u < NQI / 4; ++u) {
+      const int qi = wave + 4 * u;
+      const int hd = 4 * qi + hh;
+      const uint32_t off = (uint32_t)(hd * 256 + 16 * (cc ^ bw_swz(hd)));
+      bw_dma(qrow + off, dst + 1024 * qi);
+      bw_dma(orow + off, dst + QB + 1024 * qi);
     }
+    if (wave == 0 && lane < H / 2)
+      bw_dma((const char*)(ldw + ((size_t)b * T + t) * 2 * H) + 16u * (uint32_t)lane, dst + 2 * QB);
   };
 
   f32x16 dk[4], dv[4];
