@@ -253,6 +253,9 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[SB];
   __shared__ int32_t rows_s[KL_RC + 1];
+  // the active rows' bitmap words over the tile's 128 entries and their ranks
+  // (row n_rows: the odd row's absent partner, all zero)
+  __shared__ uint32_t rows_w[KL_RC + 1][4], rows_r[KL_RC + 1][4];
   __shared__ uint32_t shc[16];
   const int kt = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -265,22 +268,36 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
   const int nc = min(KL_RC, T - c0);
   {
     bool act = false;
+    uint32_t wv[4] = {0u, 0u, 0u, 0u}, rv[4] = {0u, 0u, 0u, 0u};
     if (tid < nc) {
-      const uint32_t* w = bm + ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
+      const size_t wi = ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
       uint32_t any = 0;
       for (int k = 0; k < 4; ++k)
-        if ((j0 >> 5) + k < nw) any |= w[k];
+        if ((j0 >> 5) + k < nw) {
+          wv[k] = bm[wi + k];
+          rv[k] = rank[wi + k];
+          any |= wv[k];
+        }
       act = any != 0;
     }
     uint32_t tot;
     const uint32_t at = block_excl_scan(act ? 1u : 0u, shc, tot);
-    if (act) rows_s[at] = c0 + tid;
+    if (act) {
+      rows_s[at] = c0 + tid;
+      for (int k = 0; k < 4; ++k) {
+        rows_w[at][k] = wv[k];
+        rows_r[at][k] = rv[k];
+      }
+    }
     shc[8] = tot;
   }
   __syncthreads();
   const int n_rows = (int)shc[8];
   if (n_rows == 0) return;  // uniform
-  if (tid == 0) rows_s[n_rows] = -1;  // the odd row's partner: none
+  if (tid == 0) {
+    rows_s[n_rows] = -1;  // the odd row's partner: none
+    for (int k = 0; k < 4; ++k) rows_w[n_rows][k] = rows_r[n_rows][k] = 0u;
+  }
   __syncthreads();
 
   const bool key_in = jw < Nc_cap;
@@ -326,23 +343,20 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[dt][r] = 0.0f;
   bool touched = false;
-  const int wsel = (j0 >> 5) + wave;
 
-  auto compute = [&](const uint8_t* sb, int t0, int t1) {
-    // dI of this lane's entry for each row of the pair (0: not selected)
-    float di[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int t = p ? t1 : t0;
-      if (t >= 0 && key_in && wsel < nw) {
-        const size_t wi = ((size_t)b * T + t) * nw + wsel;
-        const uint32_t word = bm[wi];
-        if ((word >> l32) & 1u) {
-          const uint32_t slot = rank[wi] + __popc(word & ((1u << l32) - 1u));
-          if (slot < (uint32_t)topk) di[p] = dIw[((size_t)b * T + t) * topk + slot];
-        }
-      }
+  // dI of this lane's entry for active row ri (0: not selected); the word
+  // and rank come from LDS, so one global load remains
+  auto fetch_di = [&](int ri) -> float {
+    const int t = rows_s[ri];
+    const uint32_t word = rows_w[ri][wave];  // zero past the bitmap's words
+    float v = 0.0f;
+    if (t >= 0 && key_in && ((word >> l32) & 1u)) {
+      const uint32_t slot = rows_r[ri][wave] + __popc(word & ((1u << l32) - 1u));
+      if (slot < (uint32_t)topk) v = dIw[((size_t)b * T + t) * topk + slot];
     }
+    return v;
+  };
+  auto compute = [&](const uint8_t* sb, const float (&di)[2]) {
     if (!__ballot(di[0] != 0.0f || di[1] != 0.0f)) return;
     touched = true;
     f32x16 va;
@@ -372,18 +386,31 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
       }
   };
 
+  // pair pi = active rows 2 pi, 2 pi + 1; its dI values are fetched while the
+  // previous pair computes
   const int npairs = (n_rows + 1) / 2;
   stage(rows_s[0], rows_s[1], st0);
+  float di_cur[2] = {fetch_di(0), fetch_di(1)};
   for (int pi = 0; pi < npairs; pi += 2) {
     kl_wait_loads();
     __syncthreads();
-    if (pi + 1 < npairs) stage(rows_s[2 * pi + 2], rows_s[2 * pi + 3], st1);
-    compute(st0, rows_s[2 * pi], rows_s[2 * pi + 1]);
+    float di_nxt[2] = {0.0f, 0.0f};
+    if (pi + 1 < npairs) {
+      stage(rows_s[2 * pi + 2], rows_s[2 * pi + 3], st1);
+      di_nxt[0] = fetch_di(2 * pi + 2);
+      di_nxt[1] = fetch_di(2 * pi + 3);
+    }
+    compute(st0, di_cur);
     if (pi + 1 >= npairs) break;
     kl_wait_loads();
     __syncthreads();
-    if (pi + 2 < npairs) stage(rows_s[2 * pi + 4], rows_s[2 * pi + 5], st0);
-    compute(st1, rows_s[2 * pi + 2], rows_s[2 * pi + 3]);
+    di_cur[0] = di_cur[1] = 0.0f;
+    if (pi + 2 < npairs) {
+      stage(rows_s[2 * pi + 4], rows_s[2 * pi + 5], st0);
+      di_cur[0] = fetch_di(2 * pi + 4);
+      di_cur[1] = fetch_di(2 * pi + 5);
+    }
+    compute(st1, di_nxt);
   }
   // dk^T (entry jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4)
   // through LDS into entry rows (stride 65 floats), then atomics of 64
