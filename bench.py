@@ -246,6 +246,12 @@ def setup_train_bwd(w):
     st = setup_prefill(w)
     B, S, dt = w.B, w.T, gen.torch_dtype(w.dt)
     d = gen.Draw(w.seed + 7, DEV)
+    # each compressor's two weights (and their gradients below) in one
+    # [2E, d_model] buffer, as a fused projection keeps them
+    for wk, wg in (("w_kv", "w_gate"), ("w_ikv", "w_igate")):
+        E = st[wk].shape[0]
+        cat = torch.cat([st[wk], st[wg]]).contiguous()
+        st[wk], st[wg] = cat[:E], cat[E:]
     csa.csa_compress(st["x"], st["w_kv"], st["w_gate"], st["pos0"], w.m, w.overlap, st["kv_cmp"],
                      workspace=st["ws_c1"])
     csa.csa_compress(st["x"], st["w_ikv"], st["w_igate"], st["pos0"], w.m, w.overlap, st["k_idx"],
@@ -267,8 +273,8 @@ def setup_train_bwd(w):
     st["dk_idx"] = torch.empty(B, w.n_cmp, w.d_I, **f32)
     for k, E in (("c1", 2 * w.D), ("c2", w.d_I)):
         st["dx_" + k] = torch.empty(B, S, w.d_model, **f32)
-        st["dwk_" + k] = torch.empty(E, w.d_model, **f32)
-        st["dwg_" + k] = torch.empty(E, w.d_model, **f32)
+        dwcat = torch.empty(2 * E, w.d_model, **f32)
+        st["dwk_" + k], st["dwg_" + k] = dwcat[:E], dwcat[E:]
         st["wsb_" + k] = torch.empty(csa.lib().csa_compress_bwd_workspace_size(B, S, w.d_model, E, w.m, w.n_cmp),
                                      dtype=torch.uint8, device=DEV)
     st["wsb_a"] = torch.empty(csa.lib().csa_sparse_attn_bwd_workspace_size(

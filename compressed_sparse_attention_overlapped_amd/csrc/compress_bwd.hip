@@ -187,10 +187,19 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   ws += cb_al256((size_t)2 * E * K * sizeof(uint16_t));
   float* dwcat = (float*)ws;
   const size_t wb = (size_t)E * K * sizeof(uint16_t), dwb = (size_t)E * K * sizeof(float);
-  hipError_t e = hipMemcpyAsync(wcat, a.w_kv, wb, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(wcat + (size_t)E * K, a.w_gate, wb, hipMemcpyDeviceToDevice, s);
-  if (e != hipSuccess) return e;
+  // weights (and weight gradients) the caller already keeps stacked - w_gate
+  // right after w_kv - are used in place
+  const bool w_stacked = (const char*)a.w_gate == (const char*)a.w_kv + wb;
+  const bool dw_stacked = (char*)a.dw_gate == (char*)a.dw_kv + dwb;
+  const uint16_t* wsrc = w_stacked ? (const uint16_t*)a.w_kv : wcat;
+  float* dwdst = dw_stacked ? a.dw_kv : dwcat;
+  hipError_t e = hipSuccess;
+  if (!w_stacked) {
+    e = hipMemcpyAsync(wcat, a.w_kv, wb, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(wcat + (size_t)E * K, a.w_gate, wb, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
   e = launch_proj_pg(a.x, a.w_kv, a.w_gate, M, E, K, pg, s);
   if (e != hipSuccess) return e;
   const int Sw = (1 + a.overlap) * a.m;
@@ -212,15 +221,17 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   if (rocblas_set_stream(hb, s) != rocblas_status_success) return hipErrorUnknown;
   // row-major views as column-major: dx^T (K x M) = [W_kv; W_gate]^T [dP | dG]^T,
   // [dW_kv; dW_gate]^T (K x 2E) = x^T [dP | dG]  (x: K x M column-major)
-  bool ok = gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, N, wcat, K,
+  bool ok = gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, N, wsrc, K,
                           dpg, N, 0.0f, a.dx, K) &&
             gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, N, M, a.x,
-                          K, dpg, N, 0.0f, dwcat, K);
+                          K, dpg, N, 0.0f, dwdst, K);
   if (!ok) return hipErrorUnknown;
-  e = hipMemcpyAsync(a.dw_kv, dwcat, dwb, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(a.dw_gate, dwcat + (size_t)E * K, dwb, hipMemcpyDeviceToDevice, s);
-  if (e != hipSuccess) return e;
+  if (!dw_stacked) {
+    e = hipMemcpyAsync(a.dw_kv, dwcat, dwb, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(a.dw_gate, dwcat + (size_t)E * K, dwb, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 

@@ -553,7 +553,9 @@ size_t csa_indexer_kl_bwd_workspace_size(int B, int T, int Nc_cap, int topk);
  * multiple of 64, (1 + overlap) m <= 1024.  Workspace:
  * csa_compress_bwd_workspace_size() bytes (contents on entry do not matter;
  * it holds P | G, dP | dG, the two weights stacked and their gradients
- * stacked).
+ * stacked).  When w_gate starts right where w_kv ends (one [2E, d_model]
+ * buffer), the weights are read in place, and likewise dw_gate right after
+ * dw_kv receives the weight gradients directly: no stacking copies.
  */
 csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
                               const void* x, const void* w_kv, const void* w_gate,

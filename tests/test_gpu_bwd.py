@@ -311,6 +311,26 @@ def test_compress_bwd_matches_oracle(m, o, rotate, E, Nc):
     assert (_dec(dx)[:, n_ent * m:] == 0).all()  # tokens of no entry
 
 
+def test_compress_bwd_stacked_weights_in_place():
+    # weights kept as one [2E, d_model] buffer (w_gate right after w_kv) and
+    # weight gradients likewise are used in place: the same products as the
+    # stacking copies of separate buffers, so the results are bit-identical
+    d = gen.Draw(585)
+    B, L, dm, E, m, o, Nc = 2, 75, 128, 64, 4, 1, 18
+    x, wk, wg, ap = _cmp_inputs(d, B, L, dm, E, m, o)
+    dC = d.normal(B, Nc, E).float().contiguous().to(DEV)
+    x, wk, wg, ap = x.to(DEV), wk.to(DEV), wg.to(DEV), ap.to(DEV)
+    sep = csa.csa_compress_bwd(x, wk.clone(), wg.clone(), m, o, Nc, dC, ape=ap)
+    wcat = torch.cat([wk, wg]).contiguous()
+    dwcat = torch.full((2 * E, dm), float("nan"), device=DEV)
+    st = csa.csa_compress_bwd(x, wcat[:E], wcat[E:], m, o, Nc, dC, ape=ap,
+                              dw_kv=dwcat[:E], dw_gate=dwcat[E:])
+    torch.cuda.synchronize()
+    for a, b_, name in zip(sep, st, ("dx", "dw_kv", "dw_gate", "dape")):
+        assert torch.equal(a, b_), name
+    assert torch.equal(dwcat, torch.cat([sep[1], sep[2]]))
+
+
 def test_compress_bwd_8k_main_compressor():
     # the 8K prefill chunk's main compressor (L = 8192, d_model = 4096,
     # E = 256, m = 4 with overlap): dW rows of sampled channels (the pool is
