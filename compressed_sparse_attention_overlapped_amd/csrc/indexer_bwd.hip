@@ -29,7 +29,6 @@ namespace csa {
 
 constexpr int KL_HI = 16, KL_DI = 64;
 constexpr int KL_TOPK_MAX = 1024;
-constexpr int KL_TILES_W = KL_TOPK_MAX / 16 / 4;  // 16-slot tiles per wave
 constexpr int KL_CH = 256;                        // slots per dq chunk
 constexpr int KL_RC = 64;                         // query rows per dk workgroup
 
@@ -63,6 +62,9 @@ __device__ __forceinline__ float kl_block_sum(float v, float* sh) {
 // ---------------------------------------------------------------- row kernel
 // Slot tile u (16 slots) belongs to wave u % 4; lane l holds slot 16 u + l % 16
 // and, after the MFMA, v of heads 4 (l / 16) .. + 3 for it.
+// TW: 16-slot tiles per wave (topk <= 64 TW); fewer tiles keep fewer
+// registers, so that three workgroups share a CU at topk 512
+template <int TW>
 __global__ void __launch_bounds__(256) idx_kl_row_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ idx,
@@ -75,6 +77,10 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
   // C^T of a chunk (bf16), rows padded by 16 bytes: the 16 head rows read at
   // one slot fall in distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t cs[KL_HI][KL_CH + 8];
+  // the row's index slots (entry, or -1 for padding and entries past the
+  // cache) and attention mass, staged once with coalesced loads
+  __shared__ int32_t idx_l[KL_TOPK_MAX];
+  __shared__ float mass_l[KL_TOPK_MAX];
   __shared__ float sh[8];
   __shared__ float dws[4][KL_HI];
   const int row = blockIdx.x, b = row / T;
@@ -93,42 +99,65 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
   float wq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) wq[i] = w_idx[(size_t)row * KL_HI + 4 * g4 + i];
-  const int32_t* ir = idx + (size_t)row * topk;
+  {
+    const int32_t* ir = idx + (size_t)row * topk;
+    const float* mr = mass + (size_t)row * topk;
+    for (int k = tid; k < topk; k += 256) {
+      const int32_t j = ir[k];
+      idx_l[k] = j >= 0 && j < Nc_cap ? j : -1;
+      mass_l[k] = mr[k];
+    }
+  }
+  __syncthreads();
 
-  // scores of this wave's tiles
-  float v[KL_TILES_W][4];
-  float sc[KL_TILES_W];
-  int jv[KL_TILES_W];
+  // scores of this wave's tiles, four tiles' key rows in flight at a time
+  // (empty slots read row 0 and are ignored)
+  float v[TW][4];
+  float sc[TW];
+  int jv[TW];
   float imax = -INFINITY, msum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < KL_TILES_W; ++i) {
-    const int u = wave + 4 * i;
-    const int k = 16 * u + l16;
-    int j = -1;
-    if (u < ntile && k < topk) j = ir[k];
-    if (j >= Nc_cap) j = -1;
-    jv[i] = j;
+  for (int i = 0; i < TW; ++i) {
+    jv[i] = -1;
     sc[i] = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[i][e] = 0.0f;
-    if (u < ntile) {  // uniform
-      const uint16_t* kr = kb + (size_t)(j >= 0 ? j : 0) * KL_DI + 8 * g4;
-      const bf16x8 k0 = *(const bf16x8*)kr, k1 = *(const bf16x8*)(kr + 32);
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], k0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], k1, acc, 0, 0, 0);
-      float p = 0.0f;
+  }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[i][e] = acc[e];
-        p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
-      }
-      p += lane_xor16(p);
-      p += lane_xor32(p);
-      if (j >= 0) {
-        sc[i] = p;
-        imax = fmaxf(imax, p);
-        if (g4 == 0) msum += mass[(size_t)row * topk + k];
+  for (int i0 = 0; i0 < TW; i0 += 4) {
+    if (wave + 4 * i0 >= ntile) break;  // uniform: no tile of this wave left
+    bf16x8 k0[4], k1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = wave + 4 * (i0 + q);
+      const int k = 16 * u + l16;
+      const int j = u < ntile && k < topk ? idx_l[k] : -1;
+      jv[i0 + q] = j;
+      const uint16_t* kr = kb + (size_t)(j >= 0 ? j : 0) * KL_DI + 8 * g4;
+      k0[q] = *(const bf16x8*)kr;
+      k1[q] = *(const bf16x8*)(kr + 32);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q;
+      const int u = wave + 4 * i;
+      if (u < ntile) {  // uniform
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], k0[q], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], k1[q], acc, 0, 0, 0);
+        float p = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[i][e] = acc[e];
+          p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
+        }
+        p += lane_xor16(p);
+        p += lane_xor32(p);
+        if (jv[i] >= 0) {
+          sc[i] = p;
+          imax = fmaxf(imax, p);
+          if (g4 == 0) msum += mass_l[16 * u + l16];
+        }
       }
     }
   }
@@ -137,7 +166,7 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
   float zs = 0.0f;
   if (imax > -INFINITY) {
 #pragma unroll
-    for (int i = 0; i < KL_TILES_W; ++i)
+    for (int i = 0; i < TW; ++i)
       if (jv[i] >= 0 && g4 == 0) zs += __expf(sc[i] - imax);
   }
   zs = kl_block_sum(zs, sh);
@@ -145,15 +174,15 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
   const float lz = live ? imax + __logf(zs) : 0.0f;
   const float g = gscale ? gscale[row] : 1.0f;
   // dI, the loss and dw
-  float dI[KL_TILES_W];
+  float dI[TW];
   float kl = 0.0f, dwp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < KL_TILES_W; ++i) {
+  for (int i = 0; i < TW; ++i) {
     const int u = wave + 4 * i;
     const int k = 16 * u + l16;
     dI[i] = 0.0f;
     if (live && jv[i] >= 0) {
-      const float p = mass[(size_t)row * topk + k] / msum;
+      const float p = mass_l[k] / msum;
       const float lq = sc[i] - lz;
       if (g4 == 0 && p > 0.0f) kl += p * (__logf(p) - lq);
       dI[i] = g * (__expf(lq) - p);
@@ -186,8 +215,7 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
     // stage the chunk's key rows (row r of the chunk at 128 r) and C^T
     for (int r = tid; r < KL_CH; r += 256) {
       const int k = c0 + r;
-      int j = k < topk ? ir[k] : -1;
-      if (j >= Nc_cap) j = -1;
+      const int j = k < topk ? idx_l[k] : -1;
       const u32x4* src = (const u32x4*)(kb + (size_t)(j >= 0 ? j : 0) * KL_DI);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
@@ -198,7 +226,7 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
 #pragma unroll
       for (int h = 0; h < KL_HI; ++h) cs[h][tid] = 0;
 #pragma unroll
-    for (int i = 0; i < KL_TILES_W; ++i) {
+    for (int i = 0; i < TW; ++i) {
       const int u = wave + 4 * i;
       const int k = 16 * u + l16;
       if (k >= c0 && k < c0 + KL_CH) {
@@ -457,9 +485,14 @@ hipError_t launch_indexer_kl_bwd(const IndexerKlArgs& a, hipStream_t s) {
     e = launch_sel_bitmap(a.idx, rows, a.topk, a.Nc_cap, bm, rank, s);
     if (e != hipSuccess) return e;
   }
-  idx_kl_row_kernel<<<rows, 256, 0, s>>>((const uint16_t*)a.q_idx, a.w_idx,
-                                         (const uint16_t*)a.k_idx, a.idx, a.mass, a.grad_scale,
-                                         a.T, a.Nc_cap, a.topk, a.loss, a.dq_idx, a.dw_idx, dIw);
+#define CSA_KL_ROW(TW_)                                                                      \
+  idx_kl_row_kernel<TW_><<<rows, 256, 0, s>>>((const uint16_t*)a.q_idx, a.w_idx,           \
+                                              (const uint16_t*)a.k_idx, a.idx, a.mass,     \
+                                              a.grad_scale, a.T, a.Nc_cap, a.topk, a.loss, \
+                                              a.dq_idx, a.dw_idx, dIw)
+  if (a.topk <= 512) CSA_KL_ROW(8);
+  else CSA_KL_ROW(KL_TOPK_MAX / 64);
+#undef CSA_KL_ROW
   if (a.topk > 0 && a.Nc_cap > 0)
     idx_kl_dk_kernel<<<dim3((a.Nc_cap + 127) / 128, (a.T + KL_RC - 1) / KL_RC, a.B), 256, 0, s>>>(
         (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, bm, rank, dIw, nw, a.T,

@@ -234,13 +234,16 @@ def _kl_check(res, ref, what, with_dk=True):
         _rows_rel(_dec(res[3]), ref[3], what + " dk")
 
 
-def test_indexer_kl_bwd_ragged_matches_oracle():
+@pytest.mark.parametrize("Nc,topk,pos1", [(300, 100, 900), (700, 600, 2800)])
+def test_indexer_kl_bwd_ragged_matches_oracle(Nc, topk, pos1):
     # 100 slots (a partial 16-slot tile and a partial 32-slot step of the dq
     # product), rows without a selected entry, a row whose mass is zero, a
-    # per-row gradient scale, 300 entries (a partial 128-entry dk tile)
-    d = gen.Draw(560)
-    B, T, Nc, topk = 2, 70, 300, 100
-    q_pos = [0, 900]
+    # per-row gradient scale, 300 entries (a partial 128-entry dk tile); 600
+    # slots take the row kernel's variant for more than 512 slots (three
+    # 256-slot dq chunks, the last partial)
+    d = gen.Draw(560 + topk)
+    B, T = 2, 70
+    q_pos = [0, pos1]  # (the second sequence sees every entry at pos1 = 2800)
     qi, wi, ki, idx, mass = _kl_inputs(d, B, T, Nc, topk, q_pos)
     idx[1, 5] = -1
     mass[1, 6] = 0.0
