@@ -121,6 +121,27 @@ __global__ void __launch_bounds__(256) cmp_bwd_token_kernel(
     }
 }
 
+// out[i] = sum over s < S of part[s n + i] (the token-split weight gradient)
+__global__ void __launch_bounds__(256) cmp_bwd_sum_kernel(const float* __restrict__ part, int S,
+                                                          size_t n, float* __restrict__ out) {
+  const size_t n4 = n / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * blockDim.x) {
+    f32x4 acc = *(const f32x4*)(part + 4 * i);
+    for (int k = 1; k < S; ++k) {
+      const f32x4 v = *(const f32x4*)(part + (size_t)k * n + 4 * i);
+      acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+    }
+    *(f32x4*)(out + 4 * i) = acc;
+  }
+  for (size_t i = 4 * n4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    float acc = part[i];
+    for (int k = 1; k < S; ++k) acc += part[(size_t)k * n + i];
+    out[i] = acc;
+  }
+}
+
 }  // namespace csa
 
 // ---------------------------------------------------------------- host side
@@ -129,17 +150,26 @@ using namespace csa;
 
 static size_t cb_al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Token splits of the weight-gradient product: a [d_model, 2E] output too
+// small to fill the chip on its own (below about 256 tiles of 64 x 128) is
+// computed as S partial products over token ranges, then summed.
+static int dw_splits(size_t M, int d_model, int E) {
+  if ((size_t)d_model * 2 * E >= (size_t)256 * 64 * 128) return 1;
+  return (M % 4 == 0 && M >= 4096) ? 4 : 1;
+}
+
 // workspace: P | G fp32 [M, 2E], dP | dG bf16 [M, 2E], the entries' stats and
-// gradients, the stacked weights bf16 [2E, d_model] and the stacked weight
-// gradients fp32 [2E, d_model]
+// gradients, the stacked weights bf16 [2E, d_model], the stacked weight
+// gradients fp32 [2E, d_model] and, with token splits, their partials
 size_t compress_bwd_ws_bytes(int B, int L, int d_model, int E, int m, int Nc_cap) {
   const size_t M = (size_t)B * L;
   const size_t n_ent = std::min<size_t>((size_t)L / m, (size_t)Nc_cap);
   const size_t WK = (size_t)2 * E * d_model;
+  const int S = dw_splits(M, d_model, E);
   return cb_al256(M * 2 * E * sizeof(float)) + cb_al256(M * 2 * E * sizeof(uint16_t)) +
          cb_al256((size_t)B * n_ent * E * 2 * sizeof(float)) +
          cb_al256((size_t)B * n_ent * E * sizeof(float)) + cb_al256(WK * sizeof(uint16_t)) +
-         cb_al256(WK * sizeof(float));
+         cb_al256(WK * sizeof(float)) + (S > 1 ? cb_al256(S * WK * sizeof(float)) : 0);
 }
 
 // one rocBLAS handle per device, created on first use
@@ -186,6 +216,9 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   uint16_t* wcat = (uint16_t*)ws;
   ws += cb_al256((size_t)2 * E * K * sizeof(uint16_t));
   float* dwcat = (float*)ws;
+  ws += cb_al256((size_t)2 * E * K * sizeof(float));
+  float* dwpart = (float*)ws;  // S partials [2E, K] when the tokens are split
+  const int S = dw_splits((size_t)M, K, E);
   const size_t wb = (size_t)E * K * sizeof(uint16_t), dwb = (size_t)E * K * sizeof(float);
   // weights (and weight gradients) the caller already keeps stacked - w_gate
   // right after w_kv - are used in place
@@ -222,9 +255,26 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   // row-major views as column-major: dx^T (K x M) = [W_kv; W_gate]^T [dP | dG]^T,
   // [dW_kv; dW_gate]^T (K x 2E) = x^T [dP | dG]  (x: K x M column-major)
   bool ok = gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_none, K, M, N, wsrc, K,
-                          dpg, N, 0.0f, a.dx, K) &&
-            gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, N, M, a.x,
-                          K, dpg, N, 0.0f, dwdst, K);
+                          dpg, N, 0.0f, a.dx, K);
+  if (ok && S == 1) {
+    ok = gemm_bf16_f32(hb, rocblas_operation_none, rocblas_operation_transpose, K, N, M, a.x, K,
+                       dpg, N, 0.0f, dwdst, K);
+  } else if (ok) {
+    // partial s over tokens [s M / S, (s + 1) M / S), then their sum
+    const int Ms = M / S;
+    const float alpha = 1.0f, beta = 0.0f;
+    ok = rocblas_gemm_strided_batched_ex(
+             hb, rocblas_operation_none, rocblas_operation_transpose, K, N, Ms, &alpha, a.x,
+             rocblas_datatype_bf16_r, K, (rocblas_stride)Ms * K, dpg, rocblas_datatype_bf16_r, N,
+             (rocblas_stride)Ms * N, &beta, dwpart, rocblas_datatype_f32_r, K,
+             (rocblas_stride)K * N, dwpart, rocblas_datatype_f32_r, K, (rocblas_stride)K * N, S,
+             rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
+    if (ok) {
+      const size_t n = (size_t)K * N;
+      cmp_bwd_sum_kernel<<<(unsigned)std::min<size_t>((n / 4 + 255) / 256, 1024), 256, 0, s>>>(
+          dwpart, S, n, dwdst);
+    }
+  }
   if (!ok) return hipErrorUnknown;
   if (!dw_stacked) {
     e = hipMemcpyAsync(a.dw_kv, dwcat, dwb, hipMemcpyDeviceToDevice, s);
