@@ -388,14 +388,18 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
 // KIND: 0 compressed entries of the CSA form (a row attends entry j when bit
 // j of its bitmap is set), 1 compressed entries of the HCA form (j < n_vis),
 // 2 raw window rows.  Workgroup (kt, chunk, b): keys [128 kt, 128 kt + 128)
-// of the cache, wave w the 32 keys from 128 kt + 32 w, and up to 64 query
-// rows from the first row that can see the tile.  Per row, all four waves read
-// its Q and dO (staged in LDS); per wave (heads on MFMA rows, keys on columns):
-//   S = Q K^T, dP = dO V^T (32 MFMAs), P and dS in registers,
-//   dV^T += dO^T P, dK^T += Q^T dS (32 MFMAs; dO^T and Q^T through
-//   transposing LDS reads).
+// of the cache and up to 64 query rows from the first row that can see the
+// tile.  Eight waves: key group g = wave % 4 (the 32 keys from 128 kt + 32 g)
+// is shared by two waves of different roles, so that each holds one set of
+// key fragments and one set of accumulators (two waves per SIMD):
+//   role 0: S = Q K^T (16 MFMAs), P = exp(S - lse) into LDS and registers,
+//           the per-slot mass, dV^T += dO^T P (16 MFMAs);
+//   role 1: dP = dO V^T (16 MFMAs), after a barrier P from LDS,
+//           dS = P (dP - delta), dK^T += Q^T dS (16 MFMAs)
+// (heads on MFMA rows, keys on columns; dO^T and Q^T through transposing LDS
+// reads).  Per row, every wave reads its Q and dO staged in LDS.
 template <int NHH, int KIND>
-__global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
+__global__ void __launch_bounds__(512, 1) attn_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout,
     const float* __restrict__ ldw, const uint16_t* __restrict__ kv, int rows_cap,
     const uint32_t* __restrict__ bm, const uint32_t* __restrict__ rank, int nw,
@@ -410,10 +414,12 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
   constexpr int NQI = QB / 1024;          // load instructions for Q (and for dO)
   __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[SB];
+  // P of the current row for each key group: [group][head half][register][lane]
+  __shared__ __attribute__((aligned(16))) float pex[4 * NHH * 16 * 64];
   __shared__ int32_t rows_s[BW_RC];
   __shared__ uint32_t rows_w[KIND == 0 ? BW_RC : 1][4];   // the row's bitmap words of the tile
   __shared__ uint32_t rows_r[KIND == 0 ? BW_RC : 1][4];   // and their ranks
-  __shared__ uint32_t sh[16];
+  __shared__ uint32_t sh[32];
   // Workgroup order: consecutive workgroups go to the 8 XCDs in turn, so each
   // XCD takes a contiguous range of the logical order (key tile fastest for
   // compressed entries, whose tiles all read the same query rows; row chunk
@@ -434,9 +440,10 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
   b = lg / (ntl * nslot);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave & 3, role = wave >> 2;
   const int h2 = lane >> 5, l32 = lane & 31;
   const int j0 = BW_KV_KEYS * kt;
-  const int jw = j0 + 32 * wave + l32;  // this lane's key (MFMA column)
+  const int jw = j0 + 32 * grp + l32;  // this lane's key (MFMA column)
   const int64_t qp = q_pos[b];
   const int64_t rbase = KIND == 2 ? raw_base[b] : 0;
   const int ncb = KIND == 1 ? n_cmp[b] : 0;
@@ -462,17 +469,14 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
     return;
   }
 
-  // B operands: K^T and V^T of this lane's key (dims 16 s + 8 h2 ..); keys
-  // past the cache read row 0 and are masked
+  // B operands: role 0 K^T, role 1 V^T of this lane's key (dims 16 s + 8 h2
+  // ..); keys past the cache read row 0 and are masked
   const bool key_in = jw < rows_cap;
-  bf16x8 kf[8], vf[8];
+  bf16x8 kvf[8];
   {
-    const uint16_t* kr = kv + ((size_t)b * rows_cap + (key_in ? jw : 0)) * 256 + 8 * h2;
+    const uint16_t* kr = kv + ((size_t)b * rows_cap + (key_in ? jw : 0)) * 256 + 128 * role + 8 * h2;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kf[s] = *(const bf16x8*)(kr + 16 * s);
-      vf[s] = *(const bf16x8*)(kr + 128 + 16 * s);
-    }
+    for (int s = 0; s < 8; ++s) kvf[s] = *(const bf16x8*)(kr + 16 * s);
   }
   // LDS offsets: A operands Q / dO (head l32 of each 32-head half, chunk
   // 2 s + h2); the transposing reads of Q^T / dO^T (head rows 4 (gg >> 1) +
@@ -494,12 +498,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
       }
     }
   }
+  // role 0 reads Q (A of S) then dO^T (A of dV); role 1 dO (A of dP) then
+  // Q^T (A of dK)
+  const uint32_t a_base = role ? (uint32_t)QB : 0u, t_base = role ? 0u : (uint32_t)QB;
   // stage row t into dst: Q and dO rows of 4 heads per load instruction
   // (lane l: head 4 i + l / 16, chunk l % 16 at slot chunk ^ bw_swz(head)),
-  // instructions i = wave, wave + 4, ... of each; then lse2 | delta (8 H
+  // instructions i = wave, wave + 8, ... of each; then lse2 | delta (8 H
   // bytes) by the lanes of wave 0 that cover it.  Sources are 32-bit byte
   // offsets from the row's uniform base.
-  static_assert(NQI % 4 == 0, "Q load instructions split evenly over 4 waves");
+  static_assert(NQI % 8 == 0, "Q load instructions split evenly over 8 waves");
   auto stage = [&](int t_row, uint8_t* dst) {
     const int t = __builtin_amdgcn_readfirstlane(t_row);  // (one row per workgroup step)
     const size_t rq = ((size_t)b * T + t) * H;
@@ -507,8 +514,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
     const char* orow = (const char*)(dout + rq * 128);
     const int hh = lane >> 4, cc = lane & 15;
 #pragma unroll
-    for (int u = 0; u < NQI / 4; ++u) {
-      const int qi = wave + 4 * u;
+    for (int u = 0; u < NQI / 8; ++u) {
+      const int qi = wave + 8 * u;
       const int hd = 4 * qi + hh;
       const uint32_t off = (uint32_t)(hd * 256 + 16 * (cc ^ bw_swz(hd)));
       bw_dma(qrow + off, dst + 1024 * qi);
@@ -518,21 +525,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
       bw_dma((const char*)(ldw + ((size_t)b * T + t) * 2 * H) + 16u * (uint32_t)lane, dst + 2 * QB);
   };
 
-  f32x16 dk[4], dv[4];
+  // role 0: dV^T, role 1: dK^T (key jw on columns, dims 32 dt + 8 (r / 4) +
+  // 4 h2 + r % 4)
+  f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
-  bool touched = false;
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
   const float sc2 = scale * kLog2e;
+  float* pexw = pex + grp * (NHH * 16 * 64) + lane;
 
+  // one row: the waves of both roles meet at the barrier between the halves
   auto compute = [&](const uint8_t* sb, int ri) {
     const int t = rows_s[ri];
     const int64_t pos = qp + t;
     bool ok = key_in;
     uint32_t word = 0u;
     if (KIND == 0) {
-      word = rows_w[ri][wave];  // zero past the cache's words
+      word = rows_w[ri][grp];  // zero past the cache's words
       ok = ok && ((word >> l32) & 1u);
     } else if (KIND == 1) {
       ok = ok && jw < n_visible(pos, ncb, m, rows_cap);
@@ -540,69 +550,79 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
       const int64_t p = rbase + jw;
       ok = ok && p <= pos && p > pos - window;
     }
-    if (!__ballot(ok)) return;
-    touched = true;
+    const bool any = __ballot(ok) != 0;  // uniform; the same in both roles of the group
     const float* lw = (const float*)(sb + 2 * QB);
-    f32x16 s_acc[NHH], p_acc[NHH];
+    f32x16 x_acc[NHH];  // role 0: S, role 1: dP
+    if (any) {
 #pragma unroll
-    for (int hf = 0; hf < NHH; ++hf) {
+      for (int hf = 0; hf < NHH; ++hf) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_acc[hf][r] = p_acc[hf][r] = 0.0f;
-      bf16x8 af[8];
+        for (int r = 0; r < 16; ++r) x_acc[hf][r] = 0.0f;
+        bf16x8 af[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) af[s] = *(const bf16x8*)(sb + hf * 32 * 256 + aofs[s]);
+        for (int s = 0; s < 8; ++s) af[s] = *(const bf16x8*)(sb + a_base + hf * 32 * 256 + aofs[s]);
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        s_acc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], kf[s], s_acc[hf], 0, 0, 0);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) af[s] = *(const bf16x8*)(sb + QB + hf * 32 * 256 + aofs[s]);
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        p_acc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], vf[s], p_acc[hf], 0, 0, 0);
+        for (int s = 0; s < 8; ++s)
+          x_acc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s], kvf[s], x_acc[hf], 0, 0, 0);
+      }
     }
     // heads of register r: 32 hf + 8 (r / 4) + 4 h2 + r % 4
-    bf16x8 pb[NHH][2], db[NHH][2];
-    float msum = 0.0f;
+    bf16x8 bop[NHH][2];
+    if (any && role == 0) {
+      float msum = 0.0f;
 #pragma unroll
-    for (int hf = 0; hf < NHH; ++hf)
+      for (int hf = 0; hf < NHH; ++hf)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const f32x4*)(lw + 32 * hf + 8 * g + 4 * h2);
-        const f32x4 d4 = *(const f32x4*)(lw + H + 32 * hf + 8 * g + 4 * h2);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *(const f32x4*)(lw + 32 * hf + 8 * g + 4 * h2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[hf][r], sc2, -l4[e]))
-                             : 0.0f;
-          msum += p;
-          pb[hf][r >> 3][r & 7] = (__bf16)p;
-          db[hf][r >> 3][r & 7] = (__bf16)(p * (p_acc[hf][r] - d4[e]));
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(x_acc[hf][r], sc2, -l4[e]))
+                               : 0.0f;
+            msum += p;
+            pexw[(hf * 16 + r) * 64] = p;
+            bop[hf][r >> 3][r & 7] = (__bf16)p;
+          }
         }
-      }
-    if (KIND == 0 && attn_mass) {
-      msum += lane_xor32(msum);
-      if (ok && h2 == 0) {
-        const uint32_t slot = rows_r[ri][wave] + __popc(word & ((1u << l32) - 1u));
-        if (slot < (uint32_t)topk) attn_mass[((size_t)b * T + t) * topk + slot] = msum;
+      if (KIND == 0 && attn_mass) {
+        msum += lane_xor32(msum);
+        if (ok && h2 == 0) {
+          const uint32_t sl = rows_r[ri][grp] + __popc(word & ((1u << l32) - 1u));
+          if (sl < (uint32_t)topk) attn_mass[((size_t)b * T + t) * topk + sl] = msum;
+        }
       }
     }
+    __syncthreads();  // P of every group is in LDS
+    if (any) {
+      if (role == 1) {
 #pragma unroll
-    for (int hf = 0; hf < NHH; ++hf)
+        for (int hf = 0; hf < NHH; ++hf)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t ho = (uint32_t)(32 * hf + 16 * ks) * 256;
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *(const f32x4*)(lw + H + 32 * hf + 8 * g + 4 * h2);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const u32x2 o1 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + QB + ho + tofs[dt][0]));
-          const u32x2 o2 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + QB + ho + tofs[dt][1]));
-          const bf16x8 ot = __builtin_bit_cast(bf16x8, u32x4{o1[0], o1[1], o2[0], o2[1]});
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pb[hf][ks], dv[dt], 0, 0, 0);
-          const u32x2 q1 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + ho + tofs[dt][0]));
-          const u32x2 q2 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + ho + tofs[dt][1]));
-          const bf16x8 qt = __builtin_bit_cast(bf16x8, u32x4{q1[0], q1[1], q2[0], q2[1]});
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, db[hf][ks], dk[dt], 0, 0, 0);
-        }
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              const float p = pexw[(hf * 16 + r) * 64];
+              bop[hf][r >> 3][r & 7] = (__bf16)(p * (x_acc[hf][r] - d4[e]));
+            }
+          }
       }
+#pragma unroll
+      for (int hf = 0; hf < NHH; ++hf)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint32_t ho = (uint32_t)(32 * hf + 16 * ks) * 256;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const u32x2 o1 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + t_base + ho + tofs[dt][0]));
+            const u32x2 o2 = __builtin_bit_cast(u32x2, bw_read_tr16(sb + t_base + ho + tofs[dt][1]));
+            const bf16x8 at = __builtin_bit_cast(bf16x8, u32x4{o1[0], o1[1], o2[0], o2[1]});
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, bop[hf][ks], acc[dt], 0, 0, 0);
+          }
+        }
+    }
   };
 
   for (int64_t c0 = t_lo + (int64_t)chunk * BW_RC; c0 <= t_hi; c0 += (int64_t)nslot * BW_RC) {
@@ -615,14 +635,14 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
         act = true;
         if (KIND == 0) {
           const size_t wi = ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
-          uint32_t any = 0;
+          uint32_t anyw = 0;
           for (int k = 0; k < 4; ++k)
             if ((j0 >> 5) + k < nw) {
               wv[k] = bm[wi + k];
               rv[k] = rank[wi + k];
-              any |= wv[k];
+              anyw |= wv[k];
             }
-          act = any != 0;
+          act = anyw != 0;
         }
       }
       uint32_t tot;
@@ -635,10 +655,10 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
             rows_r[at][k] = rv[k];
           }
       }
-      sh[8] = tot;  // read after the next barrier
+      sh[24] = tot;  // read after the next barrier
     }
     __syncthreads();
-    const int n_rows = (int)sh[8];
+    const int n_rows = (int)sh[24];
     if (n_rows > 0) {  // uniform
       stage(rows_s[0], st0);
       for (int i = 0; i < n_rows; i += 2) {
@@ -653,33 +673,34 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkv_kernel(
         compute(st1, i + 1);
       }
     }
-    __syncthreads();  // the staging buffers and rows_s are free again
+    __syncthreads();  // the staging buffers, P and rows_s are free again
   }
-  // dK^T / dV^T (key jw on columns, dims 32 dt + 8 (r / 4) + 4 h2 + r % 4)
-  // through LDS into key rows (stride 129 floats: the 32 keys of one store
-  // hit 32 banks), then stored as the workgroup's partial in whole rows
-  // (64 consecutive floats per store); waves 0-1 use st0, waves 2-3 st1.
-  // dK first, then dV.
-  float* red = (float*)((wave < 2 ? st0 : st1)) + (wave & 1) * 32 * 129;
-  float* prow = pdst + (size_t)(32 * wave) * 256;
+  // dK^T (role 1) then dV^T (role 0) through LDS into key rows (stride 129
+  // floats: the 32 keys of one store hit 32 banks), then stored as the
+  // workgroup's partial in whole rows (64 consecutive floats per store);
+  // groups 0-1 use st0, groups 2-3 st1.
+  float* red = (float*)((grp < 2 ? st0 : st1)) + (grp & 1) * 32 * 129;
+  float* prow = pdst + (size_t)(32 * grp) * 256;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    const bool mine = role == (half ? 0 : 1);  // uniform
+    if (mine)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * dt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        red[l32 * 129 + d] = half ? dv[dt][r] : scale * dk[dt][r];
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int d = 32 * dt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          red[l32 * 129 + d] = half ? acc[dt][r] : scale * acc[dt][r];
+        }
     __syncthreads();
-    for (int k = 0; k < 32; ++k) {
-      prow[(size_t)k * 256 + 128 * half + lane] = red[k * 129 + lane];
-      prow[(size_t)k * 256 + 128 * half + 64 + lane] = red[k * 129 + 64 + lane];
-    }
+    if (mine)
+      for (int k = 0; k < 32; ++k) {
+        prow[(size_t)k * 256 + 128 * half + lane] = red[k * 129 + lane];
+        prow[(size_t)k * 256 + 128 * half + 64 + lane] = red[k * 129 + 64 + lane];
+      }
     __syncthreads();
   }
   if (tid == 0) pflag[slot] = 1u;
-  (void)touched;
 }
 
 // dkv[b, key] = the sum, in slot order, of the valid partials of the key's
@@ -824,7 +845,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
 
 #define CSA_BWD_KV(NHH_, KIND_, KV_, CAP_, NSL_, PART_, FLAG_)                                \
   attn_bwd_dkv_kernel<NHH_, KIND_><<<dim3((CAP_ + BW_KV_KEYS - 1) / BW_KV_KEYS, NSL_, a.B),  \
-                                     256, 0, s>>>(                                            \
+                                     512, 0, s>>>(                                            \
       q, dout, ldw, KV_, CAP_, bm, rank, nw, a.q_pos, a.raw_base, a.n_cmp, a.T, a.topk,       \
       a.window, a.m, a.scale, NSL_, PART_, FLAG_, a.attn_mass)
   if (a.Nc_cap > 0 && (a.dense || (a.topk > 0))) {
