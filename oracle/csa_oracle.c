@@ -66,8 +66,10 @@
  *    pinned to torch autograd through torch's kl_div and log_softmax, and to
  *    its closed forms (zero at the indexer's own distribution, linearity in
  *    the gradient scale).
- *  - orc_compress_bwd: pinned to central differences of orc_compress and to
- *    the mean-pool closed form.
+ *  - orc_compress_bwd / orc_compress_bwd_ex: pinned to central differences
+ *    of orc_compress_ex (with and without the norm, the rotary embedding and
+ *    the Hadamard step, the norm weight's gradient included) and to the
+ *    mean-pool closed form.
  */
 #include <math.h>
 #include <stdint.h>
@@ -888,28 +890,42 @@ int orc_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int topk, con
 
 /* ---- compressor backward ----------------------------------------------------
  * Gradients of a one-shot compressor call over tokens [0, L) (pos0 = 0, no
- * carried state; entries post-processed by nothing or by the Hadamard
- * rotation only) for an upstream gradient dC [B, Nc_cap, E] of the entries it
- * writes (rows i < min(L / m, Nc_cap); other rows are ignored).  With the
- * rotation, the gradient of the pooled entry is H dC / sqrt(E) (the matrix is
- * symmetric and orthogonal).  Through the pool, for every entry i and token
- * j of its window (slot s = j - m (i - o)):
+ * carried state; entries post-processed as orc_compress_ex does with opts,
+ * or not at all with opts NULL) for an upstream gradient dC [B, Nc_cap, E]
+ * of the entries it writes (rows i < min(L / m, Nc_cap); other rows are
+ * ignored).  The entry's gradient goes back through the post-processing in
+ * reverse order (the chain rule through the definitions above):
+ *  - the Hadamard rotation: g <- H g / sqrt(E) (H symmetric and orthogonal);
+ *  - the rotary embedding: the pair rotation's transpose, i.e. the same
+ *    rotation at position -m i;
+ *  - the RMS norm y = C r w, r = (mean C^2 + eps)^(-1/2): with u = g w,
+ *    g_C = r u - C r^3 (sum_e u_e C_e) / E, and dnorm_w += g C r.
+ * Through the pool, for every entry i and token j of its window (slot
+ * s = j - m (i - o)), with dC_i now that gradient of the pooled entry:
  *     dP_j += a_{i,j} dC_i,   dG_j += a_{i,j} (P_j - C_i) dC_i,
  *     dape[s] += a_{i,j} (P_j - C_i) dC_i            (all per channel),
  * and through the projections P = W_kv x, G = W_gate x:
  *     dx_j = W_kv^T dP_j + W_gate^T dG_j,
  *     dW_kv = sum_j dP_j x_j^T,  dW_gate = sum_j dG_j x_j^T  (over b and j).
- * dape may be NULL (no ape). */
-int orc_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
-                     const void* x, const void* w_kv, const void* w_gate, int in_dt,
-                     const double* ape, int Nc_cap, const double* dC, double* dx,
-                     double* dw_kv, double* dw_gate, double* dape) {
+ * dape may be NULL (no ape); dnorm_w [E] is written when opts has a norm. */
+int orc_compress_bwd_ex(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                        const void* x, const void* w_kv, const void* w_gate, int in_dt,
+                        const double* ape, int Nc_cap, const double* dC,
+                        const orc_compress_opts* opts, double* dx, double* dw_kv,
+                        double* dw_gate, double* dape, double* dnorm_w) {
   const int Sw = (1 + overlap) * m;
   if (B < 0 || L < 0 || m < 1 || E < 1 || d_model < 1) return 1;
   if (rotate && (E & (E - 1))) return 1;
+  if (opts && opts->rope_dim &&
+      (opts->rope_dim < 0 || opts->rope_dim % 2 || opts->rope_off < 0 ||
+       opts->rope_off + opts->rope_dim > E))
+    return 1;
+  const double* nw = opts ? opts->norm_w : NULL;
+  if (nw && !dnorm_w) return 1;
   memset(dw_kv, 0, sizeof(double) * (size_t)E * d_model);
   memset(dw_gate, 0, sizeof(double) * (size_t)E * d_model);
   if (dape) memset(dape, 0, sizeof(double) * (size_t)Sw * E);
+  if (nw) memset(dnorm_w, 0, sizeof(double) * (size_t)E);
   const int64_t n_ent = (int64_t)L / m < Nc_cap ? (int64_t)L / m : Nc_cap;
   for (int b = 0; b < B; ++b) {
     double* P = (double*)malloc(sizeof(double) * ((size_t)L * E + 1));
@@ -933,9 +949,46 @@ int orc_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int r
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n_ent; ++i) {
       double* g = (double*)malloc(sizeof(double) * E);
+      double* Cv = (double*)malloc(sizeof(double) * E);
       for (int e = 0; e < E; ++e) g[e] = dC[((size_t)b * Nc_cap + i) * E + e];
       if (rotate) hadamard_rows(g, E);
       const int64_t first = (int64_t)m * (i - overlap), last = (int64_t)m * (i + 1) - 1;
+      if (opts && opts->rope_dim)
+        rope_row(g + opts->rope_off, opts->rope_dim, opts->rope_interleaved, opts->rope_base,
+                 -((int64_t)m * i));
+      if (nw) {
+        /* the pooled entry, then the norm's backward */
+        for (int e = 0; e < E; ++e) {
+          double mx = -INFINITY, den = 0, C = 0;
+          for (int64_t j = first; j <= last; ++j) {
+            if (j < 0) continue;
+            const double z = G[(size_t)j * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+            if (z > mx) mx = z;
+          }
+          for (int64_t j = first; j <= last; ++j) {
+            if (j < 0) continue;
+            const double z = G[(size_t)j * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+            den += exp(z - mx);
+          }
+          for (int64_t j = first; j <= last; ++j) {
+            if (j < 0) continue;
+            const double z = G[(size_t)j * E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0);
+            C += exp(z - mx) / den * P[(size_t)j * E + e];
+          }
+          Cv[e] = C;
+        }
+        double ss = 0, dot = 0;
+        for (int e = 0; e < E; ++e) {
+          ss += Cv[e] * Cv[e];
+          dot += g[e] * nw[e] * Cv[e];
+        }
+        const double r = 1.0 / sqrt(ss / E + opts->norm_eps);
+        for (int e = 0; e < E; ++e) {
+#pragma omp atomic
+          dnorm_w[e] += g[e] * Cv[e] * r;
+          g[e] = r * g[e] * nw[e] - Cv[e] * r * r * r * dot / E;
+        }
+      }
       for (int e = 0; e < E; ++e) {
         double mx = -INFINITY, den = 0, C = 0;
         for (int64_t j = first; j <= last; ++j) {
@@ -969,6 +1022,7 @@ int orc_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int r
         }
       }
       free(g);
+      free(Cv);
     }
     /* through the projections */
 #pragma omp parallel for schedule(static)
@@ -998,6 +1052,14 @@ int orc_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int r
     free(dG);
   }
   return 0;
+}
+
+int orc_compress_bwd(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                     const void* x, const void* w_kv, const void* w_gate, int in_dt,
+                     const double* ape, int Nc_cap, const double* dC, double* dx,
+                     double* dw_kv, double* dw_gate, double* dape) {
+  return orc_compress_bwd_ex(B, L, d_model, E, m, overlap, rotate, x, w_kv, w_gate, in_dt, ape,
+                             Nc_cap, dC, NULL, dx, dw_kv, dw_gate, dape, NULL);
 }
 
 /* Number of threads an OpenMP parallel region will use (for reporting). */

@@ -83,6 +83,9 @@ def lib():
         L.orc_indexer_kl_bwd.restype = C.c_int
         L.orc_compress_bwd.argtypes = [i32] * 7 + [vp, vp, vp, i32, dp, i32, dp, dp, dp, dp, dp]
         L.orc_compress_bwd.restype = C.c_int
+        L.orc_compress_bwd_ex.argtypes = ([i32] * 7 + [vp, vp, vp, i32, dp, i32, dp,
+                                                       C.POINTER(_Opts), dp, dp, dp, dp, dp])
+        L.orc_compress_bwd_ex.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = C.c_int
         _lib = L
@@ -390,3 +393,32 @@ def compress_bwd(x, w_kv, w_gate, m, overlap, Nc_cap, dC, ape=None, rotate=False
                                 _p(dwg), _p(dape))
     assert rc == 0
     return dx, dwk, dwg, dape
+
+
+def compress_bwd_ex(x, w_kv, w_gate, m, overlap, Nc_cap, dC, ape=None, rotate=False,
+                    norm_weight=None, norm_eps=1e-6, rope_dim=0, rope_offset=0,
+                    rope_base=10000.0, rope_interleaved=False):
+    """compress_bwd for entries post-processed as compress does with the same
+    norm / rotary options.  Returns (dx, dw_kv, dw_gate, dape or None,
+    dnorm_weight [E] or None)."""
+    x, w_kv, w_gate = _c(x), _c(w_kv), _c(w_gate)
+    B, L, d_model = x.shape
+    E = w_kv.shape[0]
+    dt = _dt(x)
+    assert _dt(w_kv) == dt and _dt(w_gate) == dt
+    dC = _c(dC, np.float64)
+    assert dC.shape == (B, Nc_cap, E)
+    ape = _c(ape, np.float64)
+    dx = np.zeros((B, L, d_model), np.float64)
+    dwk = np.zeros((E, d_model), np.float64)
+    dwg = np.zeros((E, d_model), np.float64)
+    dape = np.zeros(((1 + overlap) * m, E), np.float64) if ape is not None else None
+    nw = _c(norm_weight, np.float64)
+    dnw = np.zeros(E, np.float64) if nw is not None else None
+    opts = _Opts(None if nw is None else nw.ctypes.data, float(norm_eps), int(rope_dim),
+                 int(rope_offset), int(bool(rope_interleaved)), float(rope_base))
+    rc = lib().orc_compress_bwd_ex(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(x),
+                                   _p(w_kv), _p(w_gate), dt, _p(ape), Nc_cap, _p(dC),
+                                   C.byref(opts), _p(dx), _p(dwk), _p(dwg), _p(dape), _p(dnw))
+    assert rc == 0
+    return dx, dwk, dwg, dape, dnw

@@ -295,6 +295,66 @@ def test_compress_bwd_finite_differences_of_the_forward(m, overlap, rotate):
         assert abs(fd - dape[i]) <= 1e-6 * max(1.0, abs(dape[i]))
 
 
+@pytest.mark.parametrize("rotate,interleaved", [(False, False), (True, False), (False, True)])
+def test_compress_bwd_with_norm_and_rope_finite_differences(rotate, interleaved):
+    # entries RMS-normed, rotated on channels [2, 6) at their positions m i
+    # (base 10: angles well away from 0) and optionally Hadamard-rotated: the
+    # gradients of x, both weights, ape and the norm weight against central
+    # differences of the oracle's own forward with the same options
+    r = rng(80 + 2 * rotate + interleaved)
+    m, overlap = 4, 1
+    B, L, dm, E = 2, 4 * m + 3, 6, 8
+    Nc = L // m + 1
+    x = r.normal(0, 1, (B, L, dm)).astype(np.float32)
+    wk = r.normal(0, 0.5, (E, dm)).astype(np.float32)
+    wg = r.normal(0, 0.5, (E, dm)).astype(np.float32)
+    ape = r.normal(0, 0.3, ((1 + overlap) * m, E))
+    nw = r.normal(1, 0.3, E)
+    dC = r.normal(0, 1, (B, Nc, E))
+    opt = dict(norm_eps=1e-3, rope_dim=4, rope_offset=2, rope_base=10.0,
+               rope_interleaved=interleaved)
+    dx, dwk, dwg, dape, dnw = orc.compress_bwd_ex(x, wk, wg, m, overlap, Nc, dC, ape=ape,
+                                                  rotate=rotate, norm_weight=nw, **opt)
+
+    def f(x_, wk_, wg_, ape_, nw_):
+        out, written, _ = orc.compress(x_, wk_, wg_, m, overlap, 0, Nc, ape=ape_,
+                                       want_state=False, rotate=rotate, norm_weight=nw_, **opt)
+        return float(np.where(written[..., None], out * dC, 0.0).sum())
+
+    h = 1e-3
+    args = {"x": x, "wk": wk, "wg": wg}
+    for name, grad in (("x", dx), ("wk", dwk), ("wg", dwg)):
+        arr = args[name]
+        for _ in range(8):
+            i = tuple(r.integers(0, s_) for s_ in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[i] += h
+            am[i] -= h
+            step = float(ap[i]) - float(am[i])
+            kp = dict(args, **{name: ap})
+            km = dict(args, **{name: am})
+            fd = (f(kp["x"], kp["wk"], kp["wg"], ape, nw) - f(km["x"], km["wk"], km["wg"], ape, nw)) / step
+            assert abs(fd - grad[i]) <= 1e-4 * max(1.0, abs(grad[i])), (name, i, fd, grad[i])
+    for arr, grad, which in ((ape, dape, "ape"), (nw, dnw, "nw")):
+        for _ in range(6):
+            i = tuple(r.integers(0, s_) for s_ in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[i] += 1e-5
+            am[i] -= 1e-5
+            if which == "ape":
+                fd = (f(x, wk, wg, ap, nw) - f(x, wk, wg, am, nw)) / 2e-5
+            else:
+                fd = (f(x, wk, wg, ape, ap) - f(x, wk, wg, ape, am)) / 2e-5
+            assert abs(fd - grad[i]) <= 1e-6 * max(1.0, abs(grad[i])), (which, i, fd, grad[i])
+    # no options: the plain entry point (to rounding: the oracle sums token rows
+    # shared by two entries with atomics, in thread order)
+    a = orc.compress_bwd(x, wk, wg, m, overlap, Nc, dC, ape=ape, rotate=rotate)
+    b_ = orc.compress_bwd_ex(x, wk, wg, m, overlap, Nc, dC, ape=ape, rotate=rotate)
+    for u, v in zip(a, b_[:4]):
+        np.testing.assert_allclose(u, v, rtol=1e-12, atol=1e-14)
+    assert b_[4] is None
+
+
 def test_compress_bwd_mean_pool_closed_form():
     # uniform gates (zero gate weights, no ape) and no overlap: each entry is
     # the mean of its m projected tokens, so dP_j = dC_i / m for the entry i
