@@ -19,7 +19,7 @@ import torch
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
            "csa_indexer_topk_varlen", "csa_sparse_attn_varlen", "csa_sparse_attn_bwd",
-           "hca_dense_attn_bwd", "csa_indexer_kl_bwd", "csa_compress_bwd",
+           "hca_dense_attn_bwd", "csa_indexer_kl_bwd", "csa_compress_bwd", "csa_compress_bwd_ex",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
            "CsaError", "PageTable", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
@@ -159,6 +159,9 @@ def lib():
         L.csa_compress_bwd.restype = C.c_int
         L.csa_compress_bwd_workspace_size.argtypes = [i32] * 6
         L.csa_compress_bwd_workspace_size.restype = C.c_size_t
+        L.csa_compress_bwd_ex.argtypes = ([i32] * 7 + [vp, vp, vp, i32, vp, i32, vp,
+                                                       C.POINTER(_COpts)] + [vp] * 5 + [vp, sz, vp])
+        L.csa_compress_bwd_ex.restype = C.c_int
         L.csa_status_string.argtypes = [i32]
         L.csa_status_string.restype = C.c_char_p
         L.csa_last_error.argtypes = []
@@ -492,6 +495,39 @@ def csa_compress_bwd(x, w_kv, w_gate, m, overlap, Nc_cap, d_out, ape=None, rotat
                                 _p(dw_kv), _p(dw_gate), _p(dape), _p(ws), nb, _stream(x))
     _check("csa_compress_bwd", rc)
     return dx, dw_kv, dw_gate, dape
+
+
+def csa_compress_bwd_ex(x, w_kv, w_gate, m, overlap, Nc_cap, d_out, ape=None, rotate=False,
+                        norm_weight=None, norm_eps=1e-6, rope_dim=0, rope_offset=0,
+                        rope_base=10000.0, rope_interleaved=False, want_dape=True, dx=None,
+                        dw_kv=None, dw_gate=None, dape=None, d_norm_weight=None,
+                        workspace=None):
+    """csa_compress_bwd for entries post-processed as csa_compress does with
+    the same norm_weight / norm_eps / rope_* options.  Returns (dx, dw_kv,
+    dw_gate, dape or None, d_norm_weight or None), all float32."""
+    _dense(x, w_kv, w_gate, d_out, ape, norm_weight)
+    B, L, d_model = x.shape
+    E = w_kv.shape[0]
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or
+                                    norm_weight.shape != (E,)):
+        raise ValueError("norm_weight must be a float32 tensor of shape [E]")
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty(B, L, d_model, **f32) if dx is None else dx
+    dw_kv = torch.empty(E, d_model, **f32) if dw_kv is None else dw_kv
+    dw_gate = torch.empty(E, d_model, **f32) if dw_gate is None else dw_gate
+    if ape is not None and want_dape and dape is None:
+        dape = torch.empty((1 + overlap) * m, E, **f32)
+    if norm_weight is not None and d_norm_weight is None:
+        d_norm_weight = torch.empty(E, **f32)
+    opts = _COpts(None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps),
+                  int(rope_dim), int(rope_offset), float(rope_base), int(bool(rope_interleaved)))
+    ws, nb = _workspace(lib().csa_compress_bwd_workspace_size(B, L, d_model, E, m, Nc_cap), x, workspace)
+    rc = lib().csa_compress_bwd_ex(B, L, d_model, E, m, overlap, int(bool(rotate)), _p(x),
+                                   _p(w_kv), _p(w_gate), _DT[x.dtype], _p(ape), Nc_cap,
+                                   _p(d_out), C.byref(opts), _p(dx), _p(dw_kv), _p(dw_gate),
+                                   _p(dape), _p(d_norm_weight), _p(ws), nb, _stream(x))
+    _check("csa_compress_bwd_ex", rc)
+    return dx, dw_kv, dw_gate, dape, (d_norm_weight if norm_weight is not None else None)
 
 
 def csa_indexer_kl_bwd(q_idx, w_idx, k_idx, idx, attn_mass, grad_scale=None, loss=None,

@@ -723,7 +723,33 @@ csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overl
                               csa_dtype_t in_dt, const float* ape, int Nc_cap, const float* d_out,
                               float* dx, float* dw_kv, float* dw_gate, float* dape,
                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return csa_compress_bwd_ex(B, L, d_model, E, m, overlap, rotate, x, w_kv, w_gate, in_dt, ape,
+                             Nc_cap, d_out, nullptr, dx, dw_kv, dw_gate, dape, nullptr, workspace,
+                             ws_bytes, stream);
+}
+
+csa_status_t csa_compress_bwd_ex(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                                 const void* x, const void* w_kv, const void* w_gate,
+                                 csa_dtype_t in_dt, const float* ape, int Nc_cap,
+                                 const float* d_out, const csa_compress_opts_t* opts, float* dx,
+                                 float* dw_kv, float* dw_gate, float* dape, float* d_norm_weight,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream) {
   const char* fn = "csa_compress_bwd";
+  csa_host::EntryOpts eo{nullptr, 0.0f, 0, 0, 0, 10000.0f};
+  if (opts) {
+    const int R = opts->rope_dim;
+    if (R < 0 || (R & 1) || opts->rope_offset < 0 || (int64_t)opts->rope_offset + R > E ||
+        (R > 0 && !(opts->rope_base > 0.0f)) ||
+        (opts->rope_interleaved != 0 && opts->rope_interleaved != 1) ||
+        (opts->norm_weight && !(opts->norm_eps >= 0.0f)))
+      return fail(CSA_E_ARG,
+                  "%s: rope_dim must be even with [rope_offset, rope_offset + rope_dim) inside "
+                  "[0, E), rope_base > 0, rope_interleaved 0 or 1, norm_eps >= 0", fn);
+    if (opts->norm_weight && !d_norm_weight)
+      return fail(CSA_E_ARG, "%s: a norm weight needs d_norm_weight", fn);
+    eo = csa_host::EntryOpts{opts->norm_weight, opts->norm_eps, R, opts->rope_offset,
+                             opts->rope_interleaved, opts->rope_base};
+  }
   if (B <= 0 || L <= 0 || d_model <= 0 || E <= 0 || Nc_cap < 0)
     return fail(CSA_E_ARG, "%s: B, L, d_model, E must be > 0 and Nc_cap >= 0", fn);
   if (m < 1) return fail(CSA_E_ARG, "%s: m must be >= 1", fn);
@@ -746,6 +772,6 @@ csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overl
     return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   csa_host::CompressBwdArgs a{B,     L,     d_model, E,       m,       overlap, rotate, Nc_cap,
                               x,     w_kv,  w_gate,  ape,     d_out,   dx,      dw_kv,  dw_gate,
-                              dape,  workspace};
+                              dape,  workspace, eo, d_norm_weight};
   return hip_status(csa_host::launch_compress_bwd(a, stream), fn);
 }

@@ -348,6 +348,8 @@ struct CompressBwdArgs {
   float* dw_gate;
   float* dape;
   void* ws;
+  EntryOpts opt;   // the forward's entry post-processing (norm, rotary)
+  float* dnorm_w;  // [E], written when opt.norm_w
 };
 size_t compress_bwd_ws_bytes(int B, int L, int d_model, int E, int m, int Nc_cap);
 hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s);

@@ -12,8 +12,13 @@
 //   dx = dP W_kv + dG W_gate,  dW_kv = dP^T x,  dW_gate = dG^T x.
 //
 // Launches: the forward projection (recomputes P | G in fp32); an entry
-// kernel (each entry's softmax statistics lse and C per channel, and, with the
-// rotation, the gradient through it: H dC / sqrt(E), H symmetric); a token
+// kernel (each entry's softmax statistics lse and C per channel, and the
+// entry's gradient back through the post-processing the forward applied, in
+// reverse order: the Hadamard rotation (H dC / sqrt(E), H symmetric), the
+// rotary embedding (its transpose: the pair rotation at -m i) and the RMS
+// norm y = C r w, r = (mean C^2 + eps)^(-1/2), whose gradient is
+// r u - C r^3 (sum u C) / E with u = g w, and whose weight gradient sums
+// g C r over the entries - per-entry rows, then a fixed-order column sum); a token
 // kernel (owner computes: token j takes its share of the one or two entries
 // whose windows hold it, so no two threads write one element, and dape is
 // summed per workgroup in LDS, then one atomic per slot and channel); and two
@@ -33,17 +38,48 @@ namespace csa {
 
 constexpr int CB_TT = 128;  // tokens per workgroup of the token kernel
 
+// Sum over the block (any blockDim.x <= 1024; red: 1024 floats); every
+// thread gets the total.  Ends with a barrier.
+__device__ float cb_block_sum(float v, float* red) {
+  const int tid = threadIdx.x, n = blockDim.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (tid < o && tid + o < n) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float t = red[0];
+  __syncthreads();
+  return t;
+}
+
 // Per (b, entry i < n_ent, channel e): lse and C of the window softmax, and
-// the entry's gradient (rotated back through the Hadamard matrix when the
-// entries were rotated).  One workgroup per entry row, E threads (E <= 1024).
+// the entry's gradient back through the Hadamard rotation, the rotary
+// embedding and the RMS norm (each when the forward applied it).  One
+// workgroup per entry row, E threads (E <= 1024).  dnw_part [B n_ent, E]:
+// the entry's terms of the norm weight's gradient (when opt.norm_w).
 __global__ void __launch_bounds__(1024) cmp_bwd_entry_kernel(
     const float* __restrict__ pg, const float* __restrict__ ape, const float* __restrict__ dC,
     int L, int E, int m, int overlap, int Nc_cap, int n_ent, int rotate, float rs,
-    float* __restrict__ stats, float* __restrict__ gent) {
+    csa_host::EntryOpts opt, float* __restrict__ stats, float* __restrict__ gent,
+    float* __restrict__ dnw_part) {
   __shared__ float hv[1024];
+  __shared__ float red[1024];
   const int i = blockIdx.x, b = blockIdx.y, e = threadIdx.x;
   const int N = 2 * E;
   const size_t prow = (size_t)b * L;
+  // the pooled entry's statistics for this channel
+  const int first = m * (i - overlap), last = m * (i + 1) - 1;
+  float mx = -INFINITY;
+  for (int j = max(first, 0); j <= last; ++j)
+    mx = fmaxf(mx, pg[(prow + j) * N + E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0f));
+  float den = 0.0f, num = 0.0f;
+  for (int j = max(first, 0); j <= last; ++j) {
+    const float w = __expf(pg[(prow + j) * N + E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0f) - mx);
+    den += w;
+    num = fmaf(w, pg[(prow + j) * N + e], num);
+  }
+  const float C = num / den;
   float g = dC[((size_t)b * Nc_cap + i) * E + e];
   if (rotate) {
     // fast Walsh-Hadamard transform of the row (Sylvester order), / sqrt(E)
@@ -60,20 +96,50 @@ __global__ void __launch_bounds__(1024) cmp_bwd_entry_kernel(
     }
     g = hv[e] * rs;
   }
-  const int first = m * (i - overlap), last = m * (i + 1) - 1;
-  float mx = -INFINITY;
-  for (int j = max(first, 0); j <= last; ++j)
-    mx = fmaxf(mx, pg[(prow + j) * N + E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0f));
-  float den = 0.0f, num = 0.0f;
-  for (int j = max(first, 0); j <= last; ++j) {
-    const float w = __expf(pg[(prow + j) * N + E + e] + (ape ? ape[(size_t)(j - first) * E + e] : 0.0f) - mx);
-    den += w;
-    num = fmaf(w, pg[(prow + j) * N + e], num);
+  if (opt.rope_dim) {
+    // the forward turned pair (a, b) into (a cos - b sin, b cos + a sin); its
+    // transpose takes (g_a, g_b) to (g_a cos + g_b sin, g_b cos - g_a sin)
+    __syncthreads();  // (hv's last reads above)
+    hv[e] = g;
+    __syncthreads();
+    const int R = opt.rope_dim, half = R / 2, c = e - opt.rope_off;
+    if (c >= 0 && c < R) {
+      const int k = opt.rope_interleaved ? c >> 1 : (c < half ? c : c - half);
+      const bool lo = opt.rope_interleaved ? (c & 1) == 0 : c < half;
+      const int partner = opt.rope_interleaved ? (lo ? e + 1 : e - 1) : (lo ? e + half : e - half);
+      const double ang = (double)m * (double)i * pow((double)opt.rope_base, -2.0 * k / R);
+      const float cs = (float)cos(ang), sn = (float)sin(ang);
+      g = fmaf(g, cs, (lo ? hv[partner] : -hv[partner]) * sn);
+    }
+  }
+  if (opt.norm_w) {
+    const float w = opt.norm_w[e];
+    const float ss = cb_block_sum(C * C, red);
+    const float dot = cb_block_sum(g * w * C, red);
+    const float r = 1.0f / sqrtf(ss / (float)E + opt.norm_eps);
+    dnw_part[((size_t)b * n_ent + i) * E + e] = g * C * r;
+    g = r * g * w - C * (r * r * r) * dot / (float)E;
   }
   const size_t o = ((size_t)b * n_ent + i) * E + e;
   stats[2 * o] = mx + __logf(den);
-  stats[2 * o + 1] = num / den;
+  stats[2 * o + 1] = C;
   gent[o] = g;
+}
+
+// dnw[e] = sum over rows of part[row][e], rows in a fixed order per thread
+// then a fixed tree: workgroup of 256 threads per 64 channels
+__global__ void __launch_bounds__(256) cmp_bwd_colsum_kernel(const float* __restrict__ part,
+                                                             int rows, int E,
+                                                             float* __restrict__ out) {
+  __shared__ float sh[4][64];
+  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + c;
+  float acc = 0.0f;
+  if (e < E)
+    for (int r = rg; r < rows; r += 4) acc += part[(size_t)r * E + e];
+  sh[rg][c] = acc;
+  __syncthreads();
+  if (rg == 0 && e < E) out[e] = (sh[0][c] + sh[1][c]) + (sh[2][c] + sh[3][c]);
 }
 
 // Token j (workgroup: CB_TT tokens x 64 channels; thread: a channel and
@@ -158,9 +224,10 @@ static int dw_splits(size_t M, int d_model, int E) {
   return (M % 4 == 0 && M >= 4096) ? 4 : 1;
 }
 
-// workspace: P | G fp32 [M, 2E], dP | dG bf16 [M, 2E], the entries' stats and
-// gradients, the stacked weights bf16 [2E, d_model], the stacked weight
-// gradients fp32 [2E, d_model] and, with token splits, their partials
+// workspace: P | G fp32 [M, 2E], dP | dG bf16 [M, 2E], the entries' stats,
+// gradients and norm-weight terms, the stacked weights bf16 [2E, d_model],
+// the stacked weight gradients fp32 [2E, d_model] and, with token splits,
+// their partials
 size_t compress_bwd_ws_bytes(int B, int L, int d_model, int E, int m, int Nc_cap) {
   const size_t M = (size_t)B * L;
   const size_t n_ent = std::min<size_t>((size_t)L / m, (size_t)Nc_cap);
@@ -168,7 +235,7 @@ size_t compress_bwd_ws_bytes(int B, int L, int d_model, int E, int m, int Nc_cap
   const int S = dw_splits(M, d_model, E);
   return cb_al256(M * 2 * E * sizeof(float)) + cb_al256(M * 2 * E * sizeof(uint16_t)) +
          cb_al256((size_t)B * n_ent * E * 2 * sizeof(float)) +
-         cb_al256((size_t)B * n_ent * E * sizeof(float)) + cb_al256(WK * sizeof(uint16_t)) +
+         2 * cb_al256((size_t)B * n_ent * E * sizeof(float)) + cb_al256(WK * sizeof(uint16_t)) +
          cb_al256(WK * sizeof(float)) + (S > 1 ? cb_al256(S * WK * sizeof(float)) : 0);
 }
 
@@ -213,6 +280,8 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   ws += cb_al256((size_t)a.B * std::max(n_ent, 0) * E * 2 * sizeof(float));
   float* gent = (float*)ws;
   ws += cb_al256((size_t)a.B * std::max(n_ent, 0) * E * sizeof(float));
+  float* dnw_part = (float*)ws;
+  ws += cb_al256((size_t)a.B * std::max(n_ent, 0) * E * sizeof(float));
   uint16_t* wcat = (uint16_t*)ws;
   ws += cb_al256((size_t)2 * E * K * sizeof(uint16_t));
   float* dwcat = (float*)ws;
@@ -243,7 +312,14 @@ hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s) {
   if (n_ent > 0)
     cmp_bwd_entry_kernel<<<dim3(n_ent, a.B), E, 0, s>>>(
         pg, a.ape, a.dC, a.L, E, a.m, a.overlap, a.Nc_cap, n_ent, a.rotate,
-        (float)(1.0 / std::sqrt((double)E)), stats, gent);
+        (float)(1.0 / std::sqrt((double)E)), a.opt, stats, gent, dnw_part);
+  if (a.opt.norm_w) {
+    if (n_ent > 0)
+      cmp_bwd_colsum_kernel<<<(E + 63) / 64, 256, 0, s>>>(dnw_part, a.B * n_ent, E, a.dnorm_w);
+    else
+      e = launch_zero_f32(a.dnorm_w, (size_t)E, s);
+    if (e != hipSuccess) return e;
+  }
   cmp_bwd_token_kernel<<<dim3((a.L + CB_TT - 1) / CB_TT, (E + 63) / 64, a.B), 256,
                          (size_t)Sw * 64 * sizeof(float), s>>>(
       pg, a.ape, stats, gent, a.L, E, a.m, a.overlap, n_ent, dpg, a.dape);

@@ -536,7 +536,8 @@ size_t csa_indexer_kl_bwd_workspace_size(int B, int T, int Nc_cap, int topk);
 /*
  * Gradients of a one-shot compressor call (csa_compress from position 0 with
  * no carried state, bf16 tokens and weights, entries post-processed by
- * nothing or by the Hadamard rotation) for an upstream gradient d_out
+ * nothing or by the Hadamard rotation; csa_compress_bwd_ex below adds the
+ * RMS norm and the rotary embedding) for an upstream gradient d_out
  * [B, Nc_cap, E] (fp32) of the entries it writes, rows i < min(L / m, Nc_cap)
  * (other rows are ignored).  By the chain rule through the compressor's
  * definition (migration page, section 3.2), for entry i and window token j
@@ -563,6 +564,31 @@ csa_status_t csa_compress_bwd(int B, int L, int d_model, int E, int m, int overl
                               float* dx, float* dw_kv, float* dw_gate, float* dape,
                               void* workspace, size_t ws_bytes, hipStream_t stream);
 size_t csa_compress_bwd_workspace_size(int B, int L, int d_model, int E, int m, int Nc_cap);
+
+/*
+ * csa_compress_bwd for a compressor whose entries were post-processed by
+ * csa_compress_ex with opts (RMS norm, rotary embedding; NULL: none, which
+ * is csa_compress_bwd).  The entry's gradient goes back through the
+ * post-processing in reverse order (migration page, section 3.2: the
+ * compressor's norm and its rotary embedding of the key positions; chain
+ * rule through the definitions at csa_compress_opts_t): the Hadamard
+ * rotation, the rotary embedding (the pair rotation at position -m i), and
+ * the RMS norm y = C r w with r = (mean_e C_e^2 + norm_eps)^(-1/2):
+ *     dC = r u - C r^3 (sum_e u_e C_e) / E,   u = g w,
+ *     d_norm_weight[e] = sum over entries of g_e C_e r
+ * (g the gradient reaching the norm's output).  d_norm_weight fp32 [E] is
+ * required when opts has a norm weight (written in full; a fixed-order sum,
+ * so repeated calls agree bit for bit) and ignored otherwise.  Errors: as
+ * csa_compress_bwd, and CSA_E_ARG for opts that csa_compress_ex rejects or a
+ * norm weight without d_norm_weight.  The workspace is
+ * csa_compress_bwd_workspace_size() bytes, as for csa_compress_bwd.
+ */
+csa_status_t csa_compress_bwd_ex(int B, int L, int d_model, int E, int m, int overlap, int rotate,
+                                 const void* x, const void* w_kv, const void* w_gate,
+                                 csa_dtype_t in_dt, const float* ape, int Nc_cap,
+                                 const float* d_out, const csa_compress_opts_t* opts, float* dx,
+                                 float* dw_kv, float* dw_gate, float* dape, float* d_norm_weight,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Static text of a status code. */
 const char* csa_status_string(csa_status_t status);

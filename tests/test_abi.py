@@ -229,6 +229,18 @@ def test_backward_entry_points_validate_before_any_launch(L):
     rc = L.csa_compress_bwd(1, 64, 100, 32, 4, 1, 0, d, d, d, 1, None, 16, d, d, d, d, None, d,
                             10 ** 9, None)
     assert rc == 2 and b"multiple of 64" in L.csa_last_error()
+    # with entry post-processing: a norm weight without its gradient's
+    # output, an odd rotary slice, a slice past the entry
+    import compressed_sparse_attention_overlapped_amd as csa
+    o = csa._COpts(d.value, 1e-6, 0, 0, 10000.0, 0)
+    rc = L.csa_compress_bwd_ex(1, 64, 128, 32, 4, 1, 0, d, d, d, 1, None, 16, d, C.byref(o), d,
+                               d, d, None, None, d, 10 ** 9, None)
+    assert rc == 1 and b"d_norm_weight" in L.csa_last_error()
+    for dim, off in ((3, 0), (8, 28)):
+        o = csa._COpts(None, 1e-6, dim, off, 10000.0, 0)
+        rc = L.csa_compress_bwd_ex(1, 64, 128, 32, 4, 1, 0, d, d, d, 1, None, 16, d, C.byref(o),
+                                   d, d, d, None, None, d, 10 ** 9, None)
+        assert rc == 1 and b"rope" in L.csa_last_error(), (dim, off)
 
 
 def test_backward_workspace_sizes(L):

@@ -314,6 +314,69 @@ def test_compress_bwd_matches_oracle(m, o, rotate, E, Nc):
     assert (_dec(dx)[:, n_ent * m:] == 0).all()  # tokens of no entry
 
 
+@pytest.mark.parametrize("rotate,interleaved,E", [(False, False, 128), (True, False, 64),
+                                                   (False, True, 96)])
+def test_compress_bwd_with_norm_and_rope_matches_oracle(rotate, interleaved, E):
+    # entries RMS-normed and rotated on a channel slice at their positions
+    # m i (base 100: sizeable angles), optionally Hadamard-rotated; L = 75 is
+    # no multiple of m; E = 96 is no power of two (the entry kernel's block
+    # sums over any width); the norm weight's gradient to fp32 accuracy
+    d = gen.Draw(600 + E + rotate)
+    m, o, Nc = 4, 1, 16
+    B, L, dm = 2, 75, 128
+    x, wk, wg, ap = _cmp_inputs(d, B, L, dm, E, m, o)
+    nw = (1.0 + 0.3 * d.normal(E)).float().contiguous()
+    dC = d.normal(B, Nc, E).float().contiguous()
+    opt = dict(norm_eps=1e-5, rope_dim=32, rope_offset=8, rope_base=100.0,
+               rope_interleaved=interleaved)
+    dx, dwk, dwg, dape, dnw = csa.csa_compress_bwd_ex(
+        x.to(DEV), wk.to(DEV), wg.to(DEV), m, o, Nc, dC.to(DEV), ape=ap.to(DEV), rotate=rotate,
+        norm_weight=nw.to(DEV), **opt)
+    torch.cuda.synchronize()
+    rx, rk, rg, ra, rn = orc.compress_bwd_ex(
+        gen.host_bits(x), gen.host_bits(wk), gen.host_bits(wg), m, o, Nc, dC.double().numpy(),
+        ape=ap.double().numpy(), rotate=rotate, norm_weight=nw.double().numpy(), **opt)
+    _rows_rel(_dec(dx), rx, "cmp+norm dx")
+    _rows_rel(_dec(dwk), rk, "cmp+norm dw_kv")
+    _rows_rel(_dec(dwg), rg, "cmp+norm dw_gate")
+    _rows_rel(_dec(dape), ra, "cmp+norm dape", tol=1e-4)
+    _rows_rel(_dec(dnw)[None], rn[None], "cmp+norm dnorm_w", tol=1e-4)
+    # the same call without options is csa_compress_bwd's
+    a = csa.csa_compress_bwd(x.to(DEV), wk.to(DEV), wg.to(DEV), m, o, Nc, dC.to(DEV),
+                             ape=ap.to(DEV), rotate=rotate)
+    b_ = csa.csa_compress_bwd_ex(x.to(DEV), wk.to(DEV), wg.to(DEV), m, o, Nc, dC.to(DEV),
+                                 ape=ap.to(DEV), rotate=rotate)
+    torch.cuda.synchronize()
+    for u, v, name in zip(a, b_[:4], ("dx", "dw_kv", "dw_gate", "dape")):
+        assert torch.equal(u, v), name
+    assert b_[4] is None
+
+
+def test_compress_bwd_with_norm_and_rope_main_width():
+    # the main compressor's width (E = 256: [K | V], the rotary slice the
+    # key's first 64 channels, the usual base) on 1024 tokens of a 1024-wide
+    # model: every output against the oracle
+    d = gen.Draw(610, DEV)
+    B, L, dm, E, m, o = 1, 1024, 1024, 256, 4, 1
+    Nc = L // m
+    x, wk, wg, ap = _cmp_inputs(d, B, L, dm, E, m, o)
+    nw = (1.0 + 0.3 * d.normal(E)).float().contiguous()
+    dC = d.normal(B, Nc, E).float().contiguous()
+    opt = dict(norm_eps=1e-6, rope_dim=64, rope_offset=0, rope_base=10000.0)
+    dx, dwk, dwg, dape, dnw = csa.csa_compress_bwd_ex(x, wk, wg, m, o, Nc, dC, ape=ap,
+                                                      norm_weight=nw, **opt)
+    torch.cuda.synchronize()
+    rx, rk, rg, ra, rn = orc.compress_bwd_ex(
+        gen.host_bits(x), gen.host_bits(wk), gen.host_bits(wg), m, o, Nc,
+        dC.double().cpu().numpy(), ape=ap.double().cpu().numpy(),
+        norm_weight=nw.double().cpu().numpy(), **opt)
+    _rows_rel(_dec(dx), rx, "main-width dx")
+    _rows_rel(_dec(dwk), rk, "main-width dw_kv")
+    _rows_rel(_dec(dwg), rg, "main-width dw_gate")
+    _rows_rel(_dec(dape), ra, "main-width dape", tol=1e-4)
+    _rows_rel(_dec(dnw)[None], rn[None], "main-width dnorm_w", tol=1e-4)
+
+
 def test_compress_bwd_stacked_weights_in_place():
     # weights kept as one [2E, d_model] buffer (w_gate right after w_kv) and
     # weight gradients likewise are used in place: the same products as the
