@@ -10,20 +10,20 @@
 //   dq = scale sum_j dS_j K_j,  dK_j += scale sum dS_j q,  dV_j += sum P_j dO,
 //   dsink = -sum exp(sink - lse) delta.
 //
-// Launches: a zero fill of the summed outputs; for CSA a bitmap kernel (the
+// Launches: zero fills of the summed outputs; for CSA a bitmap kernel (the
 // selected entries of each row as bits, with the rank of each word); a
 // query-major dq kernel (the forward's tile walk: gathered or dense
 // compressed tiles, then the window, 32 keys per tile in LDS), which also
 // computes delta = sum_j P_j dP_j exactly (a first sweep over the row's tiles,
-// so delta does not inherit the rounding of a stored bf16 output) and hands
-// delta and lse to the next kernels; a reduction of the sink gradient; and a
+// so delta does not inherit the rounding of a stored output) and hands delta
+// and lse to the next kernels; a reduction of the sink gradient; and a
 // key-major dK/dV kernel (a workgroup owns 128 keys and walks the query rows
-// that see them, each row's Q and dO staged in LDS), whose row-chunk
-// partials are summed with fp32 atomics into the zeroed outputs.  The per-key
-// sums need no atomics between query rows (MFMA reduces over heads and rows
-// inside the workgroup); an fp32 atomic costs about as much as eight plain
-// stores here, so the query-major form that scatters every (row, key)
-// contribution is avoided.
+// that see them, each row's Q and dO staged in LDS) that leaves one partial
+// per row chunk, summed in slot order by a reduction kernel (deterministic).
+// The per-key sums need no atomics between query rows (MFMA reduces over
+// heads and rows inside the workgroup); an fp32 atomic costs about as much as
+// eight plain stores here, so the query-major form that scatters every
+// (row, key) contribution is avoided.
 #include <algorithm>
 #include <type_traits>
 
