@@ -63,9 +63,10 @@
  *    sum dV = sum dO, sum dK = 0, sum q.dq = sum K.dK.
  *  - orc_indexer_kl_bwd: the loss form is a reading (the pages name the
  *    loss, not its formula; see the function); given that reading it is
- *    pinned to torch autograd through torch's kl_div and log_softmax, and to
- *    its closed forms (zero at the indexer's own distribution, linearity in
- *    the gradient scale).
+ *    pinned to torch autograd through torch's kl_div and log_softmax (sparse
+ *    and dense forms), and to its closed forms (zero at the indexer's own
+ *    distribution, linearity in the gradient scale); the HCA form's
+ *    per-entry mass to the library softmax summed over heads.
  *  - orc_compress_bwd / orc_compress_bwd_ex: pinned to central differences
  *    of orc_compress_ex (with and without the norm, the rotary embedding and
  *    the Hadamard step, the norm weight's gradient included) and to the
@@ -673,9 +674,11 @@ int orc_hca_dense_attn(int B, int T, int H, int D, int m, int window, double sca
  * compressed entry or the raw row), so they land in dkv_cmp [B, Nc_cap, 2D] /
  * dkv_raw [B, R_cap, 2D] as [dK | dV]; dsink [H] sums dz over all tokens.
  * idx == NULL selects the HCA form (every visible entry, m and n_cmp as for
- * the indexer), otherwise the CSA form over idx.  attn_mass (CSA form,
- * optional) receives, per selected slot, sum_h P_j: the main attention's
- * probability mass on that entry over all heads (0 in skipped slots).
+ * the indexer), otherwise the CSA form over idx.  attn_mass (optional)
+ * receives sum_h P_j, the attention's probability mass on an entry over all
+ * heads: per selected slot in the CSA form ([B, T, topk], 0 in skipped
+ * slots), per entry in the HCA form ([B, T, Nc_cap], 0 past the visible
+ * entries) - the dense indexer loss's target.
  * The caller zeroes nothing: every output is written in full. */
 int orc_attn_bwd(int B, int T, int H, int D, int topk, int window, double scale,
                  const double* sink, const int64_t* q_pos, const void* q, const void* kv_cmp,
@@ -711,7 +714,9 @@ int orc_attn_bwd(int B, int T, int H, int D, int topk, int window, double scale,
         src[n] = 0, row[n] = j, slot[n++] = k;
       }
     } else {
-      for (int64_t j = 0; j < nv; ++j) src[n] = 0, row[n] = j, slot[n++] = -1;
+      if (attn_mass)
+        for (int64_t j = 0; j < Nc_cap; ++j) attn_mass[((size_t)b * T + t) * Nc_cap + j] = 0;
+      for (int64_t j = 0; j < nv; ++j) src[n] = 0, row[n] = j, slot[n++] = (int)j;
     }
     if (window > 0) {
       int64_t lo = pos - window + 1;
@@ -773,7 +778,8 @@ int orc_attn_bwd(int B, int T, int H, int D, int topk, int window, double scale,
 #pragma omp atomic
           g[D + d] += gv;
         }
-        if (attn_mass && slot[r] >= 0) attn_mass[((size_t)b * T + t) * topk + slot[r]] += P[r];
+        if (attn_mass && slot[r] >= 0)
+          attn_mass[((size_t)b * T + t) * (idx ? topk : Nc_cap) + slot[r]] += P[r];
       }
     }
     free(src);
@@ -804,7 +810,10 @@ int orc_attn_bwd(int B, int T, int H, int D, int topk, int window, double scale,
  *     dq[t,h] = sum_k dI_k w_h [v_hk > 0] k_j,
  *     dk[j]  += sum_h dI_k w_h [v_hk > 0] q_h     (j = idx_k).
  * Inputs fp32 or bf16 (the training formats).  A row with no selected entry
- * or zero total mass has loss 0 and no gradient. */
+ * or zero total mass has loss 0 and no gradient.  The dense form (the
+ * config's sparse-loss switch off) is this function over every visible entry:
+ * slots 0 .. n_vis - 1 in order, with the HCA form's per-entry mass of
+ * orc_attn_bwd as the target (oracle.py builds that index list). */
 int orc_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int topk, const void* q_idx,
                        const float* w_idx, const void* k_idx, int qk_dt, const int32_t* idx,
                        const double* mass, const double* grad_scale, double* loss,

@@ -311,8 +311,9 @@ def attn_bwd(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, dout, scale=None, 
     """Gradients of sparse_attn (idx given) or hca_dense_attn (idx None, with m
     and n_cmp) for an upstream gradient dout [B, T, H, D] of out.
     Returns (dq [B,T,H,D], dkv_cmp [B,Nc_cap,2D], dkv_raw [B,R_cap,2D],
-    dsink [H] or None, attn_mass [B,T,topk] or None) in float64; attn_mass is
-    the per-slot attention probability summed over heads (CSA form)."""
+    dsink [H] or None, attn_mass or None) in float64; attn_mass is the
+    attention probability summed over heads per slot ([B,T,topk], CSA form)
+    or per entry ([B,T,Nc_cap], HCA form: the dense indexer loss's target)."""
     q, kv_cmp, kv_raw = _c(q), _c(kv_cmp), _c(kv_raw)
     B, T, H, D = q.shape
     dt = _dt(q)
@@ -336,13 +337,33 @@ def attn_bwd(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, dout, scale=None, 
     dkr = np.zeros((B, R_cap, 2 * D), np.float64)
     sk = _sink(sink, H)
     dsink = np.zeros(H, np.float64) if sk is not None else None
-    mass = np.zeros((B, T, topk), np.float64) if (want_mass and idx is not None) else None
+    mass = None
+    if want_mass:
+        mass = np.zeros((B, T, topk if idx is not None else Nc_cap), np.float64)
     rc = lib().orc_attn_bwd(B, T, H, D, topk, window, scale, _p(sk), _p(q_pos), _p(q),
                             _p(kv_cmp), Nc_cap, _p(idx), m_, _p(ncp), _p(kv_raw), R_cap,
                             _p(raw_base), dt, _p(dout), _p(dq), _p(dkc), _p(dkr), _p(dsink),
                             _p(mass))
     assert rc == 0
     return dq, dkc, dkr, dsink, mass
+
+
+def indexer_kl_dense_bwd(q_idx, w_idx, k_idx, m, q_pos, n_cmp, mass, grad_scale=None):
+    """Dense indexer KL loss: the sparse form (indexer_kl_bwd) over every
+    visible entry of each row - slots 0 .. n_vis - 1 in order, n_vis as for
+    the indexer (m, q_pos, n_cmp) - with mass [B,T,Nc_cap] the dense
+    attention's per-entry mass (attn_bwd's HCA form).  Returns (loss, dq_idx,
+    dw_idx, dk_idx) in float64."""
+    B, T = np.asarray(mass).shape[:2]
+    Nc_cap = np.asarray(k_idx).shape[1]
+    q_pos = np.broadcast_to(np.asarray(q_pos, np.int64), (B,))
+    n_cmp = np.broadcast_to(np.asarray(n_cmp, np.int64), (B,))
+    idx = np.full((B, T, Nc_cap), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            nv = min(int(q_pos[b] + t + 1) // int(m), int(n_cmp[b]), Nc_cap)
+            idx[b, t, :nv] = np.arange(nv, dtype=np.int32)
+    return indexer_kl_bwd(q_idx, w_idx, k_idx, idx, mass, grad_scale)
 
 
 def indexer_kl_bwd(q_idx, w_idx, k_idx, idx, mass, grad_scale=None):

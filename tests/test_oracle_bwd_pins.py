@@ -187,6 +187,73 @@ def test_attn_bwd_identities_and_mass():
                 assert abs(mass[b, t, k] - want) <= 1e-12
 
 
+def test_hca_attn_mass_per_entry_is_the_library_softmax():
+    # the HCA form's mass per compressed entry (the dense indexer loss's
+    # target): the library softmax over the row's keys (visible entries and
+    # window) summed over heads, zero past the visible entries
+    r = rng(45)
+    B, T, H, D, m, Nc, R, W = 2, 10, 3, 8, 4, 6, 24, 4
+    q = r.normal(0, 1, (B, T, H, D)).astype(np.float32)
+    kv_cmp = r.normal(0, 1, (B, Nc, 2 * D)).astype(np.float32)
+    kv_raw = r.normal(0, 1, (B, R, 2 * D)).astype(np.float32)
+    dout = r.normal(0, 1, (B, T, H, D))
+    q_pos, n_cmp, raw_base = np.array([13, 1]), np.array([Nc, 2]), np.array([2, 0])
+    *_, mass = orc.attn_bwd(q, kv_cmp, None, kv_raw, W, q_pos, raw_base, dout, m=m, n_cmp=n_cmp,
+                            want_mass=True)
+    assert mass.shape == (B, T, Nc)
+    for b in range(B):
+        vis = [list(range(max(0, min((q_pos[b] + t + 1) // m, n_cmp[b], Nc)))) for t in range(T)]
+        mask = torch.as_tensor(brute.csa_mask(T, q_pos[b], vis, Nc, R, raw_base[b], W))
+        rows = torch.as_tensor(np.concatenate([kv_cmp[b], kv_raw[b]]).astype(np.float64))
+        logits = torch.einsum("thd,nd->thn", torch.as_tensor(q[b].astype(np.float64)),
+                              rows[:, :D]) / math.sqrt(D)
+        p = torch.softmax(logits.masked_fill(~mask[:, None, :], float("-inf")), -1)
+        p = torch.nan_to_num(p).sum(1).numpy()          # [T, Nc + R]
+        for t in range(T):
+            nv = len(vis[t])
+            np.testing.assert_allclose(mass[b, t, :nv], p[t, :nv], rtol=1e-12, atol=1e-14)
+            assert (mass[b, t, nv:] == 0).all()
+
+
+def test_indexer_kl_dense_matches_autograd_over_every_visible_entry():
+    # the dense form: KL of the normalised per-entry mass against the softmax
+    # of the indexer scores over every visible entry, through torch's kl_div
+    r = rng(52)
+    B, T, HI, dI, Nc, m = 2, 9, 3, 8, 7, 4
+    qi = r.normal(0, 1, (B, T, HI, dI)).astype(np.float32)
+    wi = r.normal(0, 1, (B, T, HI)).astype(np.float32)
+    ki = r.normal(0, 1, (B, Nc, dI)).astype(np.float32)
+    q_pos, n_cmp = np.array([3, 20]), np.array([Nc, 5])
+    nvis = [[min((q_pos[b] + t + 1) // m, n_cmp[b], Nc) for t in range(T)] for b in range(B)]
+    mass = r.uniform(0.0, 2.0, (B, T, Nc))
+    for b in range(B):
+        for t in range(T):
+            mass[b, t, nvis[b][t]:] = 0.0
+    gs = r.uniform(0.5, 2.0, (B, T))
+    loss, dq, dw, dk = orc.indexer_kl_dense_bwd(qi, wi, ki, m, q_pos, n_cmp, mass, gs)
+    qt = torch.tensor(qi.astype(np.float64), requires_grad=True)
+    wt = torch.tensor(wi.astype(np.float64), requires_grad=True)
+    kt = torch.tensor(ki.astype(np.float64), requires_grad=True)
+    total = 0
+    for b in range(B):
+        for t in range(T):
+            nv = nvis[b][t]
+            if nv == 0:
+                assert loss[b, t] == 0 and (dq[b, t] == 0).all()
+                continue
+            v = torch.relu(torch.matmul(kt[b, :nv], qt[b, t].T))        # [nv, HI]
+            scores = (v * wt[b, t]).sum(-1)
+            p = torch.as_tensor(mass[b, t, :nv])
+            p = p / p.sum()
+            kl = F.kl_div(torch.log_softmax(scores, 0), p, reduction="sum")
+            assert abs(kl.item() - loss[b, t]) <= 1e-12 * max(1.0, kl.item())
+            total = total + gs[b, t] * kl
+    total.backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
 def _kl_case(seed, B=2, T=6, HI=3, dI=8, Nc=9, topk=4):
     r = rng(seed)
     qi = r.normal(0, 1, (B, T, HI, dI)).astype(np.float32)
