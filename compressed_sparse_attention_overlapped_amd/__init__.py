@@ -19,7 +19,7 @@ import torch
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
            "csa_indexer_topk_varlen", "csa_sparse_attn_varlen", "csa_sparse_attn_bwd",
-           "hca_dense_attn_bwd", "csa_indexer_kl_bwd", "csa_compress_bwd", "csa_compress_bwd_ex",
+           "hca_dense_attn_bwd", "csa_indexer_kl_bwd", "csa_indexer_kl_dense_bwd", "csa_compress_bwd", "csa_compress_bwd_ex",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
            "csa_sparse_attn_workspace_size", "hca_dense_attn_workspace_size",
            "CsaError", "PageTable", "lib", "LIB_PATH", "DT_F32", "DT_BF16", "DT_FP8", "DT_MXFP4"]
@@ -147,7 +147,7 @@ def lib():
         L.csa_sparse_attn_bwd_workspace_size.argtypes = [i32] * 6
         L.csa_sparse_attn_bwd_workspace_size.restype = C.c_size_t
         L.hca_dense_attn_bwd.argtypes = ([i32] * 6 + [f32, vp, vp, vp, vp, vp, i32, vp, i32, vp,
-                                         i32] + [vp] * 7 + [sz, vp])
+                                         i32] + [vp] * 8 + [sz, vp])
         L.hca_dense_attn_bwd.restype = C.c_int
         L.hca_dense_attn_bwd_workspace_size.argtypes = [i32] * 6
         L.hca_dense_attn_bwd_workspace_size.restype = C.c_size_t
@@ -155,6 +155,10 @@ def lib():
         L.csa_indexer_kl_bwd.restype = C.c_int
         L.csa_indexer_kl_bwd_workspace_size.argtypes = [i32] * 4
         L.csa_indexer_kl_bwd_workspace_size.restype = C.c_size_t
+        L.csa_indexer_kl_dense_bwd.argtypes = [i32] * 6 + [vp] * 5 + [i32] + [vp] * 7 + [sz, vp]
+        L.csa_indexer_kl_dense_bwd.restype = C.c_int
+        L.csa_indexer_kl_dense_bwd_workspace_size.argtypes = [i32] * 3
+        L.csa_indexer_kl_dense_bwd_workspace_size.restype = C.c_size_t
         L.csa_compress_bwd.argtypes = [i32] * 7 + [vp, vp, vp, i32, vp, i32] + [vp] * 5 + [vp, sz, vp]
         L.csa_compress_bwd.restype = C.c_int
         L.csa_compress_bwd_workspace_size.argtypes = [i32] * 6
@@ -455,23 +459,28 @@ def csa_sparse_attn_bwd(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, lse, do
 
 
 def hca_dense_attn_bwd(q, kv_cmp, kv_raw, m, window, q_pos, n_cmp, raw_base, lse, dout,
-                       scale=None, sink=None, dq=None, dkv_cmp=None, dkv_raw=None, dsink=None,
-                       workspace=None):
-    """Gradients of hca_dense_attn; returns (dq, dkv_cmp, dkv_raw, dsink or None)."""
+                       scale=None, sink=None, want_mass=False, dq=None, dkv_cmp=None,
+                       dkv_raw=None, dsink=None, attn_mass=None, workspace=None):
+    """Gradients of hca_dense_attn; returns (dq, dkv_cmp, dkv_raw, dsink or
+    None, attn_mass or None); attn_mass [B, T, Nc_cap] is the attention
+    probability of each compressed entry summed over heads (0 where unseen)."""
     _dense(q, kv_cmp, kv_raw, q_pos, n_cmp, raw_base, lse, dout, sink)
     B, T, H, D = q.shape
     scale = D ** -0.5 if scale is None else float(scale)
     sink = _sink(sink, H)
     dq, dkv_cmp, dkv_raw, dsink = _bwd_outputs(q, kv_cmp, kv_raw, sink, dq, dkv_cmp, dkv_raw,
                                                dsink)
+    if want_mass and attn_mass is None:
+        attn_mass = torch.empty(B, T, kv_cmp.shape[1], dtype=torch.float32, device=q.device)
     ws, nb = _workspace(lib().hca_dense_attn_bwd_workspace_size(
         B, T, H, kv_cmp.shape[1], kv_raw.shape[1], window), q, workspace)
     rc = lib().hca_dense_attn_bwd(B, T, H, D, m, window, scale, _p(sink), _p(q_pos), _p(n_cmp),
                                   _p(q), _p(kv_cmp), kv_cmp.shape[1], _p(kv_raw), kv_raw.shape[1],
                                   _p(raw_base), _DT[q.dtype], _p(lse), _p(dout), _p(dq),
-                                  _p(dkv_cmp), _p(dkv_raw), _p(dsink), _p(ws), nb, _stream(q))
+                                  _p(dkv_cmp), _p(dkv_raw), _p(dsink), _p(attn_mass), _p(ws), nb,
+                                  _stream(q))
     _check("hca_dense_attn_bwd", rc)
-    return dq, dkv_cmp, dkv_raw, dsink
+    return dq, dkv_cmp, dkv_raw, dsink, attn_mass
 
 
 def csa_compress_bwd(x, w_kv, w_gate, m, overlap, Nc_cap, d_out, ape=None, rotate=False,
@@ -552,6 +561,31 @@ def csa_indexer_kl_bwd(q_idx, w_idx, k_idx, idx, attn_mass, grad_scale=None, los
                                   _p(loss), _p(dq_idx), _p(dw_idx), _p(dk_idx), _p(ws), nb,
                                   _stream(q_idx))
     _check("csa_indexer_kl_bwd", rc)
+    return loss, dq_idx, dw_idx, dk_idx
+
+
+def csa_indexer_kl_dense_bwd(q_idx, w_idx, k_idx, m, q_pos, n_cmp, attn_mass, grad_scale=None,
+                             loss=None, dq_idx=None, dw_idx=None, dk_idx=None, workspace=None):
+    """Dense indexer KL loss (every visible entry j < n_vis of each row) and
+    its gradients: q_idx [B, T, 16, 64] and k_idx [B, Nc_cap, 64] bf16, w_idx
+    f32 [B, T, 16], q_pos int64 [B], n_cmp int32 [B], attn_mass f32
+    [B, T, Nc_cap] from hca_dense_attn_bwd, grad_scale f32 [B, T] or None.
+    Returns (loss, dq_idx, dw_idx, dk_idx), all float32."""
+    _dense(q_idx, w_idx, k_idx, q_pos, n_cmp, attn_mass, grad_scale)
+    B, T, H_I, d_I = q_idx.shape
+    Nc_cap = k_idx.shape[1]
+    f32 = dict(dtype=torch.float32, device=q_idx.device)
+    loss = torch.empty(B, T, **f32) if loss is None else loss
+    dq_idx = torch.empty(B, T, H_I, d_I, **f32) if dq_idx is None else dq_idx
+    dw_idx = torch.empty(B, T, H_I, **f32) if dw_idx is None else dw_idx
+    dk_idx = torch.empty(B, Nc_cap, d_I, **f32) if dk_idx is None else dk_idx
+    ws, nb = _workspace(lib().csa_indexer_kl_dense_bwd_workspace_size(B, T, Nc_cap), q_idx,
+                        workspace)
+    rc = lib().csa_indexer_kl_dense_bwd(B, T, H_I, d_I, Nc_cap, m, _p(q_pos), _p(n_cmp),
+                                        _p(q_idx), _p(w_idx), _p(k_idx), _DT[q_idx.dtype],
+                                        _p(attn_mass), _p(grad_scale), _p(loss), _p(dq_idx),
+                                        _p(dw_idx), _p(dk_idx), _p(ws), nb, _stream(q_idx))
+    _check("csa_indexer_kl_dense_bwd", rc)
     return loss, dq_idx, dw_idx, dk_idx
 
 

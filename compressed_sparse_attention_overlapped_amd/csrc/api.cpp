@@ -668,14 +668,14 @@ csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, f
                                 const void* q, const void* kv_cmp, int Nc_cap, const void* kv_raw,
                                 int R_cap, const int64_t* raw_base, csa_dtype_t dt,
                                 const float* lse, const void* dout, float* dq, float* dkv_cmp,
-                                float* dkv_raw, float* dsink, void* workspace, size_t ws_bytes,
-                                hipStream_t stream) {
+                                float* dkv_raw, float* dsink, float* attn_mass, void* workspace,
+                                size_t ws_bytes, hipStream_t stream) {
   if (m < 1) return fail(CSA_E_ARG, "hca_dense_attn_bwd: m must be >= 1");
   if (!n_cmp) return fail(CSA_E_ARG, "hca_dense_attn_bwd: n_cmp is required");
   csa_host::AttnBwdArgs a{B,      T,       H,       0,       window,  m,       Nc_cap,
                           R_cap,  true,    scale,   sink,    q_pos,   n_cmp,   q,
                           kv_cmp, nullptr, kv_raw,  raw_base, lse,    dout,    dq,
-                          dkv_cmp, dkv_raw, dsink,  nullptr, workspace};
+                          dkv_cmp, dkv_raw, dsink,  attn_mass, workspace};
   return attn_bwd_impl("hca_dense_attn_bwd", a, D, dt, ws_bytes, stream);
 }
 
@@ -711,6 +711,44 @@ csa_status_t csa_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int 
   csa_host::IndexerKlArgs a{B,          T,    Nc_cap, topk,   q_idx,  w_idx, k_idx, idx,
                             attn_mass,  grad_scale, loss, dq_idx, dw_idx, dk_idx, workspace};
   return hip_status(csa_host::launch_indexer_kl_bwd(a, stream), fn);
+}
+
+size_t csa_indexer_kl_dense_bwd_workspace_size(int B, int T, int Nc_cap) {
+  if (B <= 0 || T <= 0 || Nc_cap < 0) return 0;
+  return csa_host::indexer_kl_dense_ws_bytes(B, T, Nc_cap);
+}
+
+csa_status_t csa_indexer_kl_dense_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int m,
+                                      const int64_t* q_pos, const int32_t* n_cmp,
+                                      const void* q_idx, const float* w_idx, const void* k_idx,
+                                      csa_dtype_t qk_dt, const float* attn_mass,
+                                      const float* grad_scale, float* loss, float* dq_idx,
+                                      float* dw_idx, float* dk_idx, void* workspace,
+                                      size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "csa_indexer_kl_dense_bwd";
+  if (B <= 0 || T <= 0 || H_I <= 0 || d_I <= 0 || Nc_cap < 0 || m < 1)
+    return fail(CSA_E_ARG, "%s: B, T, H_I, d_I, m must be > 0; Nc_cap >= 0", fn);
+  if (!q_pos || !n_cmp || !q_idx || !w_idx || !loss || !dq_idx || !dw_idx ||
+      (Nc_cap > 0 && (!k_idx || !dk_idx || !attn_mass)))
+    return fail(CSA_E_ARG, "%s: missing required pointer", fn);
+  if (qk_dt != CSA_DT_BF16) return fail(CSA_E_UNSUPPORTED, "%s: qk_dt must be BF16", fn);
+  if (H_I != 16 || d_I != 64) return fail(CSA_E_UNSUPPORTED, "%s: needs H_I = 16, d_I = 64", fn);
+  if (Nc_cap > 65536) return fail(CSA_E_UNSUPPORTED, "%s: Nc_cap > 65536", fn);
+  if ((T + 63) / 64 > 65535 || B > 65535)
+    return fail(CSA_E_UNSUPPORTED, "%s: T <= 65535 * 64 and B <= 65535", fn);
+  if (!aligned16(q_idx) || (k_idx && !aligned16(k_idx)) || !aligned16(w_idx) ||
+      !aligned16(dq_idx))
+    return fail(CSA_E_UNSUPPORTED, "%s: q_idx, k_idx, w_idx and dq_idx must be 16-byte aligned", fn);
+  const size_t need = csa_host::indexer_kl_dense_ws_bytes(B, T, Nc_cap);
+  if (ws_bytes < need || (need && !workspace))
+    return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  csa_host::IndexerKlArgs a{B,         T,          0,    0,      q_idx,  w_idx, k_idx, nullptr,
+                            attn_mass, grad_scale, loss, dq_idx, dw_idx, dk_idx, workspace};
+  a.Nc_cap = Nc_cap;
+  a.m = m;
+  a.q_pos = q_pos;
+  a.n_cmp = n_cmp;
+  return hip_status(csa_host::launch_indexer_kl_dense_bwd(a, stream), fn);
 }
 
 size_t csa_compress_bwd_workspace_size(int B, int L, int d_model, int E, int m, int Nc_cap) {

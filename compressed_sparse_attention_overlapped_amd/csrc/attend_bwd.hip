@@ -1,7 +1,8 @@
 // Attention backward for gfx950: gradients of the sparse (CSA) and dense
 // (HCA) MQA attention with respect to the queries, the compressed and raw KV
 // rows and the per-head sink, plus the main attention's probability mass per
-// selected entry (the indexer loss target).
+// selected slot (CSA) or per visible entry (HCA form), the indexer loss's
+// target in its sparse and dense forms.
 //
 // Math, per query token and head over the forward's key set J (DS-V4 analysis
 // section 1.2; Notion copy section 1.1: one shared KV head, 1/sqrt(D) scale):
@@ -393,7 +394,8 @@ __global__ void __launch_bounds__(64 * NHH, 2) attn_bwd_dq_kernel(
 // is shared by two waves of different roles, so that each holds one set of
 // key fragments and one set of accumulators (two waves per SIMD):
 //   role 0: S = Q K^T (16 MFMAs), P = exp(S - lse) into LDS and registers,
-//           the per-slot mass, dV^T += dO^T P (16 MFMAs);
+//           the mass per slot (CSA) or per entry (HCA), dV^T += dO^T P
+//           (16 MFMAs);
 //   role 1: dP = dO V^T (16 MFMAs), after a barrier P from LDS,
 //           dS = P (dP - delta), dK^T += Q^T dS (16 MFMAs)
 // (heads on MFMA rows, keys on columns; dO^T and Q^T through transposing LDS
@@ -585,12 +587,13 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkv_kernel(
             bop[hf][r >> 3][r & 7] = (__bf16)p;
           }
         }
-      if (KIND == 0 && attn_mass) {
+      if (KIND != 2 && attn_mass) {
         msum += lane_xor32(msum);
-        if (ok && h2 == 0) {
+        if (KIND == 0 && ok && h2 == 0) {
           const uint32_t sl = rows_r[ri][grp] + __popc(word & ((1u << l32) - 1u));
           if (sl < (uint32_t)topk) attn_mass[((size_t)b * T + t) * topk + sl] = msum;
         }
+        if (KIND == 1 && ok && h2 == 0) attn_mass[((size_t)b * T + t) * rows_cap + jw] = msum;
       }
     }
     __syncthreads();  // P of every group is in LDS
@@ -813,9 +816,10 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   if (nc && !(a.dense || a.topk > 0)) bwd_zero_kernel<<<zero_grid(nc), 256, 0, s>>>(a.dkv_cmp, nc);
   if (nr && a.window <= 0) bwd_zero_kernel<<<zero_grid(nr), 256, 0, s>>>(a.dkv_raw, nr);
   if (a.dsink) bwd_zero_kernel<<<1, 256, 0, s>>>(a.dsink, (size_t)a.H);
-  if (sparse && a.attn_mass && a.topk > 0)
-    bwd_zero_kernel<<<zero_grid((size_t)rows * a.topk), 256, 0, s>>>(a.attn_mass,
-                                                                     (size_t)rows * a.topk);
+  // mass of the slots (CSA) or entries (HCA) no row attends stays zero
+  const size_t nmass = (size_t)rows * (sparse ? a.topk : a.Nc_cap);
+  if (a.attn_mass && nmass)
+    bwd_zero_kernel<<<zero_grid(nmass), 256, 0, s>>>(a.attn_mass, nmass);
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* dout = (const uint16_t*)a.dout;
   const uint16_t* kvc = (const uint16_t*)a.kv_cmp;

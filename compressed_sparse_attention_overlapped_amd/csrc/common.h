@@ -327,8 +327,13 @@ struct IndexerKlArgs {
   float* dw_idx;
   float* dk_idx;
   void* ws;
+  // dense form: the visible entries of each row (n_visible of q_pos + t)
+  int m = 1;
+  const int64_t* q_pos = nullptr;
+  const int32_t* n_cmp = nullptr;
 };
 size_t indexer_kl_ws_bytes(int B, int T, int Nc_cap, int topk);
+size_t indexer_kl_dense_ws_bytes(int B, int T, int Nc_cap);
 
 // The bf16 projection P | G = x [W_kv; W_gate]^T into fp32 rows of 2 E
 // (K a multiple of 64).
@@ -354,5 +359,6 @@ struct CompressBwdArgs {
 size_t compress_bwd_ws_bytes(int B, int L, int d_model, int E, int m, int Nc_cap);
 hipError_t launch_compress_bwd(const CompressBwdArgs& a, hipStream_t s);
 hipError_t launch_indexer_kl_bwd(const IndexerKlArgs& a, hipStream_t s);
+hipError_t launch_indexer_kl_dense_bwd(const IndexerKlArgs& a, hipStream_t s);
 
 }  // namespace csa_host

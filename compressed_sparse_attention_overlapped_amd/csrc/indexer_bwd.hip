@@ -20,6 +20,11 @@
 // A key-major kernel sums dk over the rows that select each entry (a
 // workgroup owns 128 entries, pairs of query rows are 32 MFMA rows of
 // heads), so no per-(row, entry) atomics are needed.
+//
+// The dense form (the switch off) is the same loss over every visible entry
+// of a row, with the dense attention's per-entry mass as the target: a row
+// kernel that streams the entries in two passes (statistics, then gradients)
+// and the same key-major kernel with visibility in place of the bitmap.
 #include <algorithm>
 #include <type_traits>
 
@@ -266,23 +271,212 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
   *(f32x4*)o = dqa;
 }
 
+// ---------------------------------------------------------------- dense row kernel
+// The dense form (the sparse-loss switch off): the selected set of row t is
+// every visible entry j < n_vis(t), the target the dense attention's mass per
+// entry ([B, T, Nc_cap]).  Entries go in chunks of KL_CH (wave w: 16-entry
+// tiles w, w + 4, w + 8, w + 12 of the chunk; lane l: entry 16 u + l % 16,
+// heads 4 (l / 16) .. + 3 after the MFMA).  Pass 1 streams the chunks for the
+// softmax statistics (a running max and sum per lane) and the mass sum; pass 2
+// stages each chunk's key rows in LDS once, recomputes the scores from them,
+// forms dI, the loss and dw, and adds the chunk's dq^T = K^T C^T from the same
+// rows.  Entries past n_vis read row n_vis - 1 (a row of the cache that is
+// set) and are masked.
+__global__ void __launch_bounds__(256) idx_kl_dense_row_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, const float* __restrict__ mass,
+    const float* __restrict__ gscale, const int64_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, float* __restrict__ loss,
+    float* __restrict__ dq_idx, float* __restrict__ dw_idx, float* __restrict__ dIw) {
+  // key rows of a chunk: 16-byte chunk c of row r at slot c ^ (r & 7)
+  __shared__ __attribute__((aligned(1024))) uint8_t ks[KL_CH * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t cs[KL_HI][KL_CH + 8];
+  __shared__ float sh[8];
+  __shared__ float dws[4][KL_HI];
+  const int row = blockIdx.x, b = row / T, t = row - b * T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int nv = n_visible(q_pos[b] + t, n_cmp[b], m, Nc_cap);
+  const uint16_t* kb = k_idx + (size_t)b * Nc_cap * KL_DI;
+  const float* mr = mass + (size_t)row * Nc_cap;
+  float* dIr = dIw + (size_t)row * Nc_cap;
+  bf16x8 qa[2];
+  {
+    const uint16_t* qr = q_idx + ((size_t)row * KL_HI + l16) * KL_DI + 8 * g4;
+    qa[0] = *(const bf16x8*)qr;
+    qa[1] = *(const bf16x8*)(qr + 32);
+  }
+  float wq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wq[i] = w_idx[(size_t)row * KL_HI + 4 * g4 + i];
+
+  // pass 1: max and sum of exp of the scores, and the mass sum
+  float mx = -INFINITY, zs = 0.0f, msum = 0.0f;
+  for (int c0 = 0; c0 < nv; c0 += KL_CH) {
+    bf16x8 k0[4], k1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = c0 + 16 * (wave + 4 * q) + l16;
+      const uint16_t* kr = kb + (size_t)min(k, nv - 1) * KL_DI + 8 * g4;
+      k0[q] = *(const bf16x8*)kr;
+      k1[q] = *(const bf16x8*)(kr + 32);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k0t = c0 + 16 * (wave + 4 * q);
+      if (k0t < nv) {  // uniform
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], k0[q], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], k1[q], acc, 0, 0, 0);
+        float p = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
+        p += lane_xor16(p);
+        p += lane_xor32(p);
+        const int k = k0t + l16;
+        if (k < nv && g4 == 0) {
+          if (p > mx) {
+            zs = zs * __expf(mx - p) + 1.0f;
+            mx = p;
+          } else {
+            zs += __expf(p - mx);
+          }
+          msum += mr[k];
+        }
+      }
+    }
+  }
+  const float imax = kl_block_max(mx, sh);
+  zs = kl_block_sum(mx > -INFINITY ? zs * __expf(mx - imax) : 0.0f, sh);
+  msum = kl_block_sum(msum, sh);
+  const bool live = nv > 0 && msum > 0.0f;  // uniform
+  if (!live) {  // loss 0, no gradient
+    for (int k = tid; k < nv; k += 256) dIr[k] = 0.0f;
+    if (tid == 0) loss[row] = 0.0f;
+    if (tid < KL_HI) dw_idx[(size_t)row * KL_HI + tid] = 0.0f;
+    float* o = dq_idx + (size_t)row * KL_HI * KL_DI;
+    for (int k = tid; k < KL_HI * KL_DI; k += 256) o[k] = 0.0f;
+    return;
+  }
+  const float lz = imax + __logf(zs);
+  const float g = gscale ? gscale[row] : 1.0f;
+  const float rms = 1.0f / msum;
+
+  // pass 2
+  float kl = 0.0f, dwp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 dqa = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < nv; c0 += KL_CH) {
+    // load instruction i (wave, wave + 4, ...): chunk rows 8 i .. 8 i + 7,
+    // lane l writing slot l % 8 of row 8 i + l / 8
+#pragma unroll
+    for (int u = 0; u < KL_CH / 32; ++u) {
+      const int i = wave + 4 * u;
+      const int r = 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      kl_dma(kb + (size_t)min(c0 + r, nv - 1) * KL_DI + 8 * c, ks + 1024 * i);
+    }
+    kl_wait_loads();
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rl = 16 * (wave + 4 * q) + l16;  // entry c0 + rl
+      if (c0 + 16 * (wave + 4 * q) < nv) {       // uniform
+        const bf16x8 b0 = *(const bf16x8*)(ks + 128 * rl + 16 * (g4 ^ (rl & 7)));
+        const bf16x8 b1 = *(const bf16x8*)(ks + 128 * rl + 16 * ((4 + g4) ^ (rl & 7)));
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], b1, acc, 0, 0, 0);
+        float p = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
+        p += lane_xor16(p);
+        p += lane_xor32(p);
+        const int k = c0 + rl;
+        float dI = 0.0f;
+        if (k < nv) {
+          const float pt = mr[k] * rms;
+          const float lq = p - lz;
+          if (g4 == 0) {
+            if (pt > 0.0f) kl += pt * (__logf(pt) - lq);
+            dIr[k] = g * (__expf(lq) - pt);
+          }
+          dI = g * (__expf(lq) - pt);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dwp[e] = fmaf(dI, fmaxf(acc[e], 0.0f), dwp[e]);
+          cs[4 * g4 + e][rl] = f32_to_bf16(acc[e] > 0.0f ? dI * wq[e] : 0.0f);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[4 * g4 + e][rl] = 0;
+      }
+    }
+    __syncthreads();
+    // dq^T (64 dims x 16 heads) += K^T C^T over the chunk's 32-entry steps;
+    // wave w owns dims 16 w .. 16 w + 15 (lane layout as in the sparse form)
+    const int nst = (min(KL_CH, nv - c0) + 31) / 32;
+    for (int st = 0; st < nst; ++st) {
+      bf16x8 ka;
+      {
+        const int jj = lane & 15, gg = lane >> 4;
+        u32x2 tr[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 32 * st + 8 * gg + 4 * e + (jj >> 2);
+          const int d0 = 16 * wave + 4 * (jj & 3);
+          tr[e] = __builtin_bit_cast(
+              u32x2, kl_read_tr16(ks + 128 * r + 16 * ((d0 >> 3) ^ (r & 7)) + 2 * (d0 & 7)));
+        }
+        ka = __builtin_bit_cast(bf16x8, u32x4{tr[0][0], tr[0][1], tr[1][0], tr[1][1]});
+      }
+      const bf16x8 cb = *(const bf16x8*)&cs[l16][32 * st + 8 * g4];
+      dqa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, cb, dqa, 0, 0, 0);
+    }
+    __syncthreads();  // ks and cs are free for the next chunk
+  }
+  kl = kl_block_sum(kl, sh);
+  if (tid == 0) loss[row] = kl;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = dwp[e];
+    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+    dwp[e] = x;
+  }
+  if (l16 == 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dws[wave][4 * g4 + e] = dwp[e];
+  __syncthreads();
+  if (tid < KL_HI)
+    dw_idx[(size_t)row * KL_HI + tid] = dws[0][tid] + dws[1][tid] + dws[2][tid] + dws[3][tid];
+  float* o = dq_idx + ((size_t)row * KL_HI + l16) * KL_DI + 16 * wave + 4 * g4;
+  *(f32x4*)o = dqa;
+}
+
 // ---------------------------------------------------------------- dk kernel
 // Workgroup (kt, chunk, b): entries [128 kt, + 128) (wave w: 32 from 128 kt +
 // 32 w), up to 64 query rows from the chunk, taken two at a time: the pair's
 // 2 x 16 heads are the 32 MFMA rows.  Per wave and pair:
 //   V = Q2 K^T (4 MFMAs), C = dI w [V > 0], dk^T += Q2^T C (4 MFMAs).
+// Sparse form: a row takes part when it selects an entry of the tile (its
+// bitmap), dI of the slot from the rank; dense form (DENSE): when it sees
+// one (n_vis > 128 kt), dI at [row, entry].
+template <bool DENSE>
 __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const uint32_t* __restrict__ bm,
     const uint32_t* __restrict__ rank, const float* __restrict__ dIw, int nw, int T, int Nc_cap,
-    int topk, float* __restrict__ dk_idx) {
+    int topk, const int64_t* __restrict__ q_pos, const int32_t* __restrict__ n_cmp, int m,
+    float* __restrict__ dk_idx) {
   constexpr int PB = 32 * 128;  // bytes of a pair's 32 head rows
   constexpr int SB = 2 * 32 * 65 * 4;   // >= PB + 128; the epilogue's rows
   __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[SB];
   __shared__ int32_t rows_s[KL_RC + 1];
   // the active rows' bitmap words over the tile's 128 entries and their ranks
-  // (row n_rows: the odd row's absent partner, all zero)
+  // (dense form: n_vis in word 0; row n_rows: the odd row's absent partner,
+  // all zero)
   __shared__ uint32_t rows_w[KL_RC + 1][4], rows_r[KL_RC + 1][4];
   __shared__ uint32_t shc[16];
   const int kt = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
@@ -298,15 +492,21 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
     bool act = false;
     uint32_t wv[4] = {0u, 0u, 0u, 0u}, rv[4] = {0u, 0u, 0u, 0u};
     if (tid < nc) {
-      const size_t wi = ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
-      uint32_t any = 0;
-      for (int k = 0; k < 4; ++k)
-        if ((j0 >> 5) + k < nw) {
-          wv[k] = bm[wi + k];
-          rv[k] = rank[wi + k];
-          any |= wv[k];
-        }
-      act = any != 0;
+      if (DENSE) {
+        const int nvr = n_visible(q_pos[b] + c0 + tid, n_cmp[b], m, Nc_cap);
+        wv[0] = (uint32_t)nvr;
+        act = nvr > j0;
+      } else {
+        const size_t wi = ((size_t)b * T + c0 + tid) * nw + (j0 >> 5);
+        uint32_t any = 0;
+        for (int k = 0; k < 4; ++k)
+          if ((j0 >> 5) + k < nw) {
+            wv[k] = bm[wi + k];
+            rv[k] = rank[wi + k];
+            any |= wv[k];
+          }
+        act = any != 0;
+      }
     }
     uint32_t tot;
     const uint32_t at = block_excl_scan(act ? 1u : 0u, shc, tot);
@@ -376,8 +576,12 @@ __global__ void __launch_bounds__(256) idx_kl_dk_kernel(
   // and rank come from LDS, so one global load remains
   auto fetch_di = [&](int ri) -> float {
     const int t = rows_s[ri];
-    const uint32_t word = rows_w[ri][wave];  // zero past the bitmap's words
     float v = 0.0f;
+    if (DENSE) {
+      if (t >= 0 && key_in && jw < (int)rows_w[ri][0]) v = dIw[((size_t)b * T + t) * Nc_cap + jw];
+      return v;
+    }
+    const uint32_t word = rows_w[ri][wave];  // zero past the bitmap's words
     if (t >= 0 && key_in && ((word >> l32) & 1u)) {
       const uint32_t slot = rows_r[ri][wave] + __popc(word & ((1u << l32) - 1u));
       if (slot < (uint32_t)topk) v = dIw[((size_t)b * T + t) * topk + slot];
@@ -494,9 +698,30 @@ hipError_t launch_indexer_kl_bwd(const IndexerKlArgs& a, hipStream_t s) {
   else CSA_KL_ROW(KL_TOPK_MAX / 64);
 #undef CSA_KL_ROW
   if (a.topk > 0 && a.Nc_cap > 0)
-    idx_kl_dk_kernel<<<dim3((a.Nc_cap + 127) / 128, (a.T + KL_RC - 1) / KL_RC, a.B), 256, 0, s>>>(
-        (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, bm, rank, dIw, nw, a.T,
-        a.Nc_cap, a.topk, a.dk_idx);
+    idx_kl_dk_kernel<false><<<dim3((a.Nc_cap + 127) / 128, (a.T + KL_RC - 1) / KL_RC, a.B), 256,
+                              0, s>>>((const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx,
+                                      bm, rank, dIw, nw, a.T, a.Nc_cap, a.topk, nullptr, nullptr,
+                                      1, a.dk_idx);
+  return hipGetLastError();
+}
+
+size_t indexer_kl_dense_ws_bytes(int B, int T, int Nc_cap) {
+  return kl_al256((size_t)B * T * Nc_cap * sizeof(float));
+}
+
+hipError_t launch_indexer_kl_dense_bwd(const IndexerKlArgs& a, hipStream_t s) {
+  const int rows = a.B * a.T;
+  float* dIw = (float*)a.ws;
+  hipError_t e = launch_zero_f32(a.dk_idx, (size_t)a.B * a.Nc_cap * KL_DI, s);
+  if (e != hipSuccess) return e;
+  idx_kl_dense_row_kernel<<<rows, 256, 0, s>>>(
+      (const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx, a.mass, a.grad_scale, a.q_pos,
+      a.n_cmp, a.T, a.Nc_cap, a.m, a.loss, a.dq_idx, a.dw_idx, dIw);
+  if (a.Nc_cap > 0)
+    idx_kl_dk_kernel<true><<<dim3((a.Nc_cap + 127) / 128, (a.T + KL_RC - 1) / KL_RC, a.B), 256,
+                             0, s>>>((const uint16_t*)a.q_idx, a.w_idx, (const uint16_t*)a.k_idx,
+                                     nullptr, nullptr, dIw, 0, a.T, a.Nc_cap, 0, a.q_pos, a.n_cmp,
+                                     a.m, a.dk_idx);
   return hipGetLastError();
 }
 

@@ -485,7 +485,10 @@ size_t csa_sparse_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap, int R
 /*
  * Gradients of hca_dense_attn (the compressed part of J is every visible
  * entry j < n_vis(t)); arguments, outputs and limits as in
- * csa_sparse_attn_bwd without idx and attn_mass (Nc_cap <= 2^23).
+ * csa_sparse_attn_bwd without idx (Nc_cap <= 2^23), except:
+ *  attn_mass fp32 [B, T, Nc_cap] or NULL: per compressed entry, the attention
+ *            probability summed over heads (0 for entries the row does not
+ *            see), the target of csa_indexer_kl_dense_bwd
  * Workspace: hca_dense_attn_bwd_workspace_size() bytes.
  */
 csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, float scale,
@@ -493,8 +496,8 @@ csa_status_t hca_dense_attn_bwd(int B, int T, int H, int D, int m, int window, f
                                 const void* q, const void* kv_cmp, int Nc_cap, const void* kv_raw,
                                 int R_cap, const int64_t* raw_base, csa_dtype_t dt,
                                 const float* lse, const void* dout, float* dq, float* dkv_cmp,
-                                float* dkv_raw, float* dsink, void* workspace, size_t ws_bytes,
-                                hipStream_t stream);
+                                float* dkv_raw, float* dsink, float* attn_mass, void* workspace,
+                                size_t ws_bytes, hipStream_t stream);
 size_t hca_dense_attn_bwd_workspace_size(int B, int T, int H, int Nc_cap, int R_cap, int window);
 
 /*
@@ -532,6 +535,31 @@ csa_status_t csa_indexer_kl_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int 
                                 float* dw_idx, float* dk_idx, void* workspace, size_t ws_bytes,
                                 hipStream_t stream);
 size_t csa_indexer_kl_bwd_workspace_size(int B, int T, int Nc_cap, int topk);
+
+/*
+ * The dense form of the indexer KL loss (migration page, section 4.3: the
+ * sparse-loss switch off): the loss and gradients of csa_indexer_kl_bwd with
+ * the selected set of row t being every visible entry j < n_vis(t) =
+ * min((q_pos + t + 1) / m, n_cmp, Nc_cap), and the target the dense
+ * attention's mass per entry.  Reading: the dense form is the sparse form
+ * over that set (the pages give no separate formula).
+ *  q_pos int64 [B];  n_cmp int32 [B];  m: the compression ratio of the cache
+ *  q_idx, w_idx, k_idx, grad_scale, loss, dq_idx, dw_idx, dk_idx: as in
+ *  csa_indexer_kl_bwd
+ *  attn_mass fp32 [B, T, Nc_cap] (hca_dense_attn_bwd's; entries past n_vis
+ *  are not read)
+ * Supported: qk_dt BF16, H_I = 16, d_I = 64, Nc_cap <= 65536.  Workspace:
+ * csa_indexer_kl_dense_bwd_workspace_size() bytes (B T Nc_cap floats of dI;
+ * contents on entry do not matter).  dk_idx sums rows with fp32 atomics.
+ */
+csa_status_t csa_indexer_kl_dense_bwd(int B, int T, int H_I, int d_I, int Nc_cap, int m,
+                                      const int64_t* q_pos, const int32_t* n_cmp,
+                                      const void* q_idx, const float* w_idx, const void* k_idx,
+                                      csa_dtype_t qk_dt, const float* attn_mass,
+                                      const float* grad_scale, float* loss, float* dq_idx,
+                                      float* dw_idx, float* dk_idx, void* workspace,
+                                      size_t ws_bytes, hipStream_t stream);
+size_t csa_indexer_kl_dense_bwd_workspace_size(int B, int T, int Nc_cap);
 
 /*
  * Gradients of a one-shot compressor call (csa_compress from position 0 with

@@ -203,7 +203,7 @@ def test_backward_entry_points_validate_before_any_launch(L):
                                d, d, d, d, None, None, d, 10 ** 9, None)
     assert rc == 2 and b"topk" in L.csa_last_error()
     rc = L.hca_dense_attn_bwd(1, 8, 48, 128, 4, 4, f, None, d, d, d, d, 16, d, 16, d, 1, d, d,
-                              d, d, d, None, d, 10 ** 9, None)
+                              d, d, d, None, None, d, 10 ** 9, None)
     assert rc == 2 and b"H in {32, 64}" in L.csa_last_error()
     # indexer KL loss: geometry, topk limit, a missing mass
     rc = L.csa_indexer_kl_bwd(1, 8, 8, 64, 32, 4, d, d, d, 1, d, d, None, d, d, d, d, d,
@@ -215,6 +215,22 @@ def test_backward_entry_points_validate_before_any_launch(L):
     rc = L.csa_indexer_kl_bwd(1, 8, 16, 64, 32, 4, d, d, d, 1, d, None, None, d, d, d, d, d,
                               10 ** 9, None)
     assert rc == 1
+    # dense indexer KL loss: geometry, m, a missing mass, the cache limit
+    rc = L.csa_indexer_kl_dense_bwd(1, 8, 8, 64, 32, 4, d, d, d, d, d, 1, d, None, d, d, d, d,
+                                    d, 10 ** 9, None)
+    assert rc == 2 and b"H_I = 16" in L.csa_last_error()
+    rc = L.csa_indexer_kl_dense_bwd(1, 8, 16, 64, 32, 0, d, d, d, d, d, 1, d, None, d, d, d, d,
+                                    d, 10 ** 9, None)
+    assert rc == 1
+    rc = L.csa_indexer_kl_dense_bwd(1, 8, 16, 64, 32, 4, d, d, d, d, d, 1, None, None, d, d, d,
+                                    d, d, 10 ** 9, None)
+    assert rc == 1 and b"missing" in L.csa_last_error()
+    rc = L.csa_indexer_kl_dense_bwd(1, 8, 16, 64, 70000, 4, d, d, d, d, d, 1, d, None, d, d, d,
+                                    d, d, 10 ** 9, None)
+    assert rc == 2 and b"Nc_cap" in L.csa_last_error()
+    rc = L.csa_indexer_kl_dense_bwd(1, 8, 16, 64, 32, 4, d, d, d, d, d, 1, d, None, d, d, d, d,
+                                    d, 16, None)
+    assert rc == 3
     # compressor backward: fp32 tokens, a rotation of a width that is not a
     # power of two, dape without ape, d_model not a multiple of 64
     rc = L.csa_compress_bwd(1, 64, 128, 32, 4, 1, 0, d, d, d, 0, None, 16, d, d, d, d, None, d,
@@ -251,6 +267,8 @@ def test_backward_workspace_sizes(L):
     assert L.csa_sparse_attn_bwd_workspace_size(1, 8192, 64, 2048, 8192, 0) < a
     assert L.hca_dense_attn_bwd_workspace_size(1, 4096, 64, 8192, 4607, 512) > 0
     assert L.csa_indexer_kl_bwd_workspace_size(1, 8192, 2048, 512) >= 8192 * 512 * 4
+    assert L.csa_indexer_kl_dense_bwd_workspace_size(1, 8192, 2048) >= 8192 * 2048 * 4
+    assert L.csa_indexer_kl_dense_bwd_workspace_size(0, 8192, 2048) == 0
     assert L.csa_compress_bwd_workspace_size(1, 8192, 4096, 256, 4, 2048) >= 8192 * 512 * 6 + 512 * 4096 * 6
     assert L.csa_compress_bwd_workspace_size(1, 8192, 0, 256, 4, 2048) == 0
     assert L.csa_sparse_attn_bwd_workspace_size(0, 8, 64, 16, 16, 4) == 0

@@ -134,11 +134,17 @@ def test_hca_attn_bwd_matches_oracle(H):
     args = (q.to(DEV), kv_cmp.to(DEV), kv_raw.to(DEV), m, W, dev_i64(q_pos), dev_i32(n_cmp),
             dev_i64(raw_base))
     out, lse = csa.hca_dense_attn(*args, want_lse=True, sink=z)
-    dq, dkc, dkr, ds = csa.hca_dense_attn_bwd(*args, lse, dout.to(DEV), sink=z)
+    dq, dkc, dkr, ds, mass = csa.hca_dense_attn_bwd(*args, lse, dout.to(DEV), sink=z,
+                                                    want_mass=True)
     torch.cuda.synchronize()
-    rq, rc, rr, rs, _ = orc.attn_bwd(gen.host_bits(q), gen.host_bits(kv_cmp), None,
-                                     gen.host_bits(kv_raw), W, q_pos, raw_base, _dec(dout),
-                                     sink=z.double().cpu().numpy(), m=m, n_cmp=n_cmp)
+    rq, rc, rr, rs, rm = orc.attn_bwd(gen.host_bits(q), gen.host_bits(kv_cmp), None,
+                                      gen.host_bits(kv_raw), W, q_pos, raw_base, _dec(dout),
+                                      sink=z.double().cpu().numpy(), m=m, n_cmp=n_cmp,
+                                      want_mass=True)
+    # per-entry mass, exactly zero for entries a row does not see
+    mg = _dec(mass)
+    assert np.all(np.abs(mg - rm) <= 1e-4 + 1e-4 * np.abs(rm)), np.abs(mg - rm).max()
+    assert (mg[rm == 0] == 0).all()
     _rows_rel(_dec(dq), rq, "hca dq H=%d" % H)
     _rows_rel(_dec(dkc), rc, "hca dkv_cmp H=%d" % H)
     _rows_rel(_dec(dkr), rr, "hca dkv_raw H=%d" % H)
@@ -277,6 +283,113 @@ def test_indexer_kl_bwd_8k_prefill_shape():
     _, _, _, rk = orc.indexer_kl_bwd(hq[:, t0:], hw[:, t0:], hk, hi[:, t0:], hm[:, t0:])
     jc = (t0 + 1) // 4 + 1
     _rows_rel(_dec(res[3])[0, jc:], rk[0, jc:], "kl 8k dk tail entries")
+
+
+# dense form: the same tolerances; the selected set of a row is every visible
+# entry, the target the dense attention's mass per entry [B, T, Nc_cap]
+
+def _dense_kl_inputs(d, B, T, Nc, m, q_pos, n_cmp):
+    qi = gen.store(d.normal(B, T, 16, 64), gen.BF16)
+    wi = d.normal(B, T, 16).float().contiguous()
+    ki = gen.store(d.normal(B, Nc, 64), gen.BF16)
+    nv = torch.tensor([[_n_vis(q_pos[b] + t, n_cmp[b], m, Nc) for t in range(T)]
+                       for b in range(B)])
+    seen = torch.arange(Nc)[None, None, :] < nv[:, :, None]
+    mass = (torch.rand(B, T, Nc, generator=d.g) * seen).float()
+    return qi, wi, ki, mass, seen
+
+
+def _dense_rows_ref(hq, hw, hk, hm_rows, rows, nv):
+    """The oracle's dense loss for chosen rows of batch 0 (hm_rows: their
+    mass): the sparse form over each row's visible entries, as the dense
+    form is defined."""
+    Nc = hk.shape[1]
+    idx = np.full((1, len(rows), Nc), -1, np.int32)
+    for i, t in enumerate(rows):
+        idx[0, i, :nv[t]] = np.arange(nv[t], dtype=np.int32)
+    return orc.indexer_kl_bwd(hq[:, rows], hw[:, rows], hk, idx, hm_rows)
+
+
+def test_indexer_kl_dense_bwd_ragged_matches_oracle():
+    # 300 entries (a partial 128-entry dk tile), the second sequence seeing
+    # 275 .. 290 entries (two 256-entry chunks, the second partial, and a
+    # partial 16-entry tile), rows of the first that see no entry, a row
+    # whose mass is zero, a per-row gradient scale; the mass past n_vis and
+    # the key rows past n_cmp hold NaN, which must not be read
+    d = gen.Draw(600)
+    B, T, Nc, m = 2, 70, 300, 4
+    q_pos, n_cmp = [0, 1100], [300, 290]
+    qi, wi, ki, mass, seen = _dense_kl_inputs(d, B, T, Nc, m, q_pos, n_cmp)
+    mass[1, 6] = 0.0
+    gs = (torch.rand(B, T, generator=d.g) + 0.5).float()
+    mg = torch.where(seen, mass, torch.full_like(mass, float("nan")))
+    kg = ki.clone()
+    kg[1, n_cmp[1]:] = float("nan")
+    res = csa.csa_indexer_kl_dense_bwd(qi.to(DEV), wi.to(DEV), kg.to(DEV), m, dev_i64(q_pos),
+                                       dev_i32(n_cmp), mg.to(DEV), gs.to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.indexer_kl_dense_bwd(gen.host_bits(qi), wi.numpy(), gen.host_bits(ki), m, q_pos,
+                                   n_cmp, mass.double().numpy(), gs.double().numpy())
+    _kl_check(res, ref, "kl dense ragged")
+    for t in (0, 1, 2):  # no visible entry
+        assert float(res[0][0, t]) == 0.0 and (_dec(res[1])[0, t] == 0).all()
+    assert float(res[0][1, 6]) == 0.0 and (_dec(res[2])[1, 6] == 0).all()
+    assert (_dec(res[3])[1, n_cmp[1]:] == 0).all()
+
+
+def test_indexer_kl_dense_bwd_8k_shape():
+    # T = 8192 and 2048 entries of the m = 4 cache: loss, dq, dw of sampled
+    # rows (both ends, every 131st row) and dk of the entries only the last
+    # 40 rows see
+    d = gen.Draw(610, DEV)
+    B, T, Nc, m = 1, 8192, 2048, 4
+    qi = gen.store(d.normal(B, T, 16, 64), gen.BF16)
+    wi = d.normal(B, T, 16).float().contiguous()
+    ki = gen.store(d.normal(B, Nc, 64), gen.BF16)
+    nv = [_n_vis(t, Nc, m, Nc) for t in range(T)]
+    seen = torch.arange(Nc, device=DEV)[None, :] < torch.tensor(nv, device=DEV)[:, None]
+    mass = (torch.rand(B, T, Nc, device=DEV, generator=d.g) * seen).float()
+    zero = dev_i64([0])
+    res = csa.csa_indexer_kl_dense_bwd(qi, wi, ki, m, zero, dev_i32([Nc]), mass)
+    torch.cuda.synchronize()
+    hq, hk, hw = gen.host_bits(qi), gen.host_bits(ki), wi.cpu().numpy()
+    rows = sorted(set([0, 1, 3, 4, 1023, 1024, 4095, 4096] + list(range(5, T, 131)) + [T - 1]))
+    rl, rq, rw, _ = _dense_rows_ref(hq, hw, hk, mass[:, rows].double().cpu().numpy(), rows, nv)
+    _kl_check((res[0][:, rows], res[1][:, rows], res[2][:, rows]), (rl, rq, rw),
+              "kl dense 8k rows", with_dk=False)
+    t0 = T - 40
+    _, _, _, rk = orc.indexer_kl_dense_bwd(hq[:, t0:], hw[:, t0:], hk, m, [t0], [Nc],
+                                           mass[:, t0:].double().cpu().numpy())
+    jc = (t0 + 1) // m + 1
+    _rows_rel(_dec(res[3])[0, jc:], rk[0, jc:], "kl dense 8k dk tail entries")
+
+
+def test_dense_indexer_loss_on_the_dense_attention_mass():
+    # the chain of the dense form: the HCA-form attention backward's per-entry
+    # mass as the target of the dense indexer loss, on the device and in the
+    # oracle (each side from its own mass)
+    d = gen.Draw(620)
+    B, T, H, D, m, Nc, R, W = 1, 96, 64, 128, 4, 40, 96, 16
+    q_pos, n_cmp, raw_base = [60], [Nc], [0]
+    q = gen.store(d.normal(B, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(B, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(B, R, 2 * D), gen.BF16)
+    dout = gen.store(d.normal(B, T, H, D), gen.BF16)
+    qi = gen.store(d.normal(B, T, 16, 64), gen.BF16)
+    wi = d.normal(B, T, 16).float().contiguous()
+    ki = gen.store(d.normal(B, Nc, 64), gen.BF16)
+    args = (q.to(DEV), kv_cmp.to(DEV), kv_raw.to(DEV), m, W, dev_i64(q_pos), dev_i32(n_cmp),
+            dev_i64(raw_base))
+    out, lse = csa.hca_dense_attn(*args, want_lse=True)
+    mass = csa.hca_dense_attn_bwd(*args, lse, dout.to(DEV), want_mass=True)[4]
+    res = csa.csa_indexer_kl_dense_bwd(qi.to(DEV), wi.to(DEV), ki.to(DEV), m, dev_i64(q_pos),
+                                       dev_i32(n_cmp), mass)
+    torch.cuda.synchronize()
+    rm = orc.attn_bwd(gen.host_bits(q), gen.host_bits(kv_cmp), None, gen.host_bits(kv_raw), W,
+                      q_pos, raw_base, _dec(dout), m=m, n_cmp=n_cmp, want_mass=True)[4]
+    ref = orc.indexer_kl_dense_bwd(gen.host_bits(qi), wi.numpy(), gen.host_bits(ki), m, q_pos,
+                                   n_cmp, rm)
+    _kl_check(res, ref, "kl dense on hca mass")
 
 
 # ---------------------------------------------------------------- compressor
