@@ -86,6 +86,14 @@ __device__ __forceinline__ int n_visible(int64_t t, int32_t n_cmp, int m, int ca
 
 // ---- wave helpers ---------------------------------------------------------
 
+// Workgroup barrier that orders LDS only: the wave waits for its own LDS
+// reads and writes (lgkmcnt), not for its global loads, so direct-to-LDS
+// loads into another buffer stay in flight across it; the asm is also a
+// compiler barrier for memory.  Only for exchanges through LDS.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;

@@ -274,14 +274,19 @@ __global__ void __launch_bounds__(256) idx_kl_row_kernel(
 // ---------------------------------------------------------------- dense row kernel
 // The dense form (the sparse-loss switch off): the selected set of row t is
 // every visible entry j < n_vis(t), the target the dense attention's mass per
-// entry ([B, T, Nc_cap]).  Entries go in chunks of KL_CH (wave w: 16-entry
-// tiles w, w + 4, w + 8, w + 12 of the chunk; lane l: entry 16 u + l % 16,
-// heads 4 (l / 16) .. + 3 after the MFMA).  Pass 1 streams the chunks for the
-// softmax statistics (a running max and sum per lane) and the mass sum; pass 2
-// stages each chunk's key rows in LDS once, recomputes the scores from them,
-// forms dI, the loss and dw, and adds the chunk's dq^T = K^T C^T from the same
-// rows.  Entries past n_vis read row n_vis - 1 (a row of the cache that is
-// set) and are masked.
+// entry ([B, T, Nc_cap]).  A wave's 16-entry tiles are w, w + 4, ... of a
+// chunk (lane l: entry 16 u + l % 16, heads 4 (l / 16) .. + 3 after the
+// MFMA).  Pass 1 streams 256-entry chunks straight into registers, the next
+// chunk's keys and mass in flight while the current one is reduced, for the
+// softmax statistics (a running max and sum per lane) and the mass sum.
+// Pass 2 stages 128-entry chunks of key rows in LDS by direct loads, one
+// chunk ahead in the other of two buffers, recomputes the scores from them,
+// forms dI, the loss and dw, and adds the chunk's dq^T = K^T C^T from the
+// same rows.  Entries past n_vis read row n_vis - 1 (a row of the cache that
+// is set) and are masked.  Workgroups take the rows from the last (the
+// longest) down.
+constexpr int KL_DC = 128;  // entries per pass-2 chunk
+
 __global__ void __launch_bounds__(256) idx_kl_dense_row_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const float* __restrict__ mass,
@@ -289,11 +294,12 @@ __global__ void __launch_bounds__(256) idx_kl_dense_row_kernel(
     const int32_t* __restrict__ n_cmp, int T, int Nc_cap, int m, float* __restrict__ loss,
     float* __restrict__ dq_idx, float* __restrict__ dw_idx, float* __restrict__ dIw) {
   // key rows of a chunk: 16-byte chunk c of row r at slot c ^ (r & 7)
-  __shared__ __attribute__((aligned(1024))) uint8_t ks[KL_CH * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t cs[KL_HI][KL_CH + 8];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[KL_DC * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[KL_DC * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t cs[KL_HI][KL_DC + 8];
   __shared__ float sh[8];
   __shared__ float dws[4][KL_HI];
-  const int row = blockIdx.x, b = row / T, t = row - b * T;
+  const int row = gridDim.x - 1 - blockIdx.x, b = row / T, t = row - b * T;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -310,41 +316,63 @@ __global__ void __launch_bounds__(256) idx_kl_dense_row_kernel(
   float wq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) wq[i] = w_idx[(size_t)row * KL_HI + 4 * g4 + i];
+  // the row's score of this lane's entry (all four 16-lane groups end with it)
+  auto score = [&](const bf16x8& x0, const bf16x8& x1, f32x4& acc) -> float {
+    acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], x0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], x1, acc, 0, 0, 0);
+    float p = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
+    p += lane_xor16(p);
+    p += lane_xor32(p);
+    return p;
+  };
 
   // pass 1: max and sum of exp of the scores, and the mass sum
   float mx = -INFINITY, zs = 0.0f, msum = 0.0f;
-  for (int c0 = 0; c0 < nv; c0 += KL_CH) {
-    bf16x8 k0[4], k1[4];
+  auto load1 = [&](int c0, bf16x8 (&x0)[4], bf16x8 (&x1)[4], float (&mm)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int k = c0 + 16 * (wave + 4 * q) + l16;
-      const uint16_t* kr = kb + (size_t)min(k, nv - 1) * KL_DI + 8 * g4;
-      k0[q] = *(const bf16x8*)kr;
-      k1[q] = *(const bf16x8*)(kr + 32);
+      const int kc = min(c0 + 16 * (wave + 4 * q) + l16, nv - 1);
+      const uint16_t* kr = kb + (size_t)kc * KL_DI + 8 * g4;
+      x0[q] = *(const bf16x8*)kr;
+      x1[q] = *(const bf16x8*)(kr + 32);
+      mm[q] = mr[kc];
     }
+  };
+  auto stats = [&](int c0, const bf16x8 (&x0)[4], const bf16x8 (&x1)[4], const float (&mm)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int k0t = c0 + 16 * (wave + 4 * q);
       if (k0t < nv) {  // uniform
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], k0[q], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], k1[q], acc, 0, 0, 0);
-        float p = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
-        p += lane_xor16(p);
-        p += lane_xor32(p);
-        const int k = k0t + l16;
-        if (k < nv && g4 == 0) {
+        f32x4 acc;
+        const float p = score(x0[q], x1[q], acc);
+        if (k0t + l16 < nv && g4 == 0) {
           if (p > mx) {
             zs = zs * __expf(mx - p) + 1.0f;
             mx = p;
           } else {
             zs += __expf(p - mx);
           }
-          msum += mr[k];
+          msum += mm[q];
         }
       }
+    }
+  };
+  // (the next chunk's loads are issued unconditionally, clamped into the
+  // row: the same count in flight on every path, so each wait leaves them
+  // in flight)
+  if (nv > 0) {
+    bf16x8 a0[4], a1[4], b0[4], b1[4];
+    float ma[4], mb[4];
+    load1(0, a0, a1, ma);
+    for (int c0 = 0; c0 < nv; c0 += 2 * KL_CH) {
+      load1(c0 + KL_CH, b0, b1, mb);
+      stats(c0, a0, a1, ma);
+      if (c0 + KL_CH >= nv) break;
+      load1(c0 + 2 * KL_CH, a0, a1, ma);
+      stats(c0 + KL_CH, b0, b1, mb);
     }
   }
   const float imax = kl_block_max(mx, sh);
@@ -366,42 +394,39 @@ __global__ void __launch_bounds__(256) idx_kl_dense_row_kernel(
   // pass 2
   float kl = 0.0f, dwp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   f32x4 dqa = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c0 = 0; c0 < nv; c0 += KL_CH) {
-    // load instruction i (wave, wave + 4, ...): chunk rows 8 i .. 8 i + 7,
-    // lane l writing slot l % 8 of row 8 i + l / 8
+  // load instruction i (wave, wave + 4, ...): chunk rows 8 i .. 8 i + 7, lane
+  // l writing slot l % 8 of row 8 i + l / 8; and the mass of this lane's
+  // entries
+  auto stage2 = [&](int c0, uint8_t* dst, float (&mm)[2]) {
 #pragma unroll
-    for (int u = 0; u < KL_CH / 32; ++u) {
+    for (int u = 0; u < KL_DC / 32; ++u) {
       const int i = wave + 4 * u;
       const int r = 8 * i + (lane >> 3);
       const int c = (lane & 7) ^ (r & 7);
-      kl_dma(kb + (size_t)min(c0 + r, nv - 1) * KL_DI + 8 * c, ks + 1024 * i);
+      kl_dma(kb + (size_t)min(c0 + r, nv - 1) * KL_DI + 8 * c, dst + 1024 * i);
     }
-    kl_wait_loads();
-    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) mm[q] = mr[min(c0 + 16 * (wave + 4 * q) + l16, nv - 1)];
+  };
+  auto grad = [&](int c0, const uint8_t* kbuf, const float (&mm)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
       const int rl = 16 * (wave + 4 * q) + l16;  // entry c0 + rl
       if (c0 + 16 * (wave + 4 * q) < nv) {       // uniform
-        const bf16x8 b0 = *(const bf16x8*)(ks + 128 * rl + 16 * (g4 ^ (rl & 7)));
-        const bf16x8 b1 = *(const bf16x8*)(ks + 128 * rl + 16 * ((4 + g4) ^ (rl & 7)));
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], b0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], b1, acc, 0, 0, 0);
-        float p = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p = fmaf(wq[e], fmaxf(acc[e], 0.0f), p);
-        p += lane_xor16(p);
-        p += lane_xor32(p);
+        const bf16x8 x0 = *(const bf16x8*)(kbuf + 128 * rl + 16 * (g4 ^ (rl & 7)));
+        const bf16x8 x1 = *(const bf16x8*)(kbuf + 128 * rl + 16 * ((4 + g4) ^ (rl & 7)));
+        f32x4 acc;
+        const float p = score(x0, x1, acc);
         const int k = c0 + rl;
         float dI = 0.0f;
         if (k < nv) {
-          const float pt = mr[k] * rms;
+          const float pt = mm[q] * rms;
           const float lq = p - lz;
+          dI = g * (__expf(lq) - pt);
           if (g4 == 0) {
             if (pt > 0.0f) kl += pt * (__logf(pt) - lq);
-            dIr[k] = g * (__expf(lq) - pt);
+            dIr[k] = dI;
           }
-          dI = g * (__expf(lq) - pt);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -413,10 +438,10 @@ __global__ void __launch_bounds__(256) idx_kl_dense_row_kernel(
         for (int e = 0; e < 4; ++e) cs[4 * g4 + e][rl] = 0;
       }
     }
-    __syncthreads();
+    lds_barrier();  // cs is complete (the other buffer's loads stay in flight)
     // dq^T (64 dims x 16 heads) += K^T C^T over the chunk's 32-entry steps;
     // wave w owns dims 16 w .. 16 w + 15 (lane layout as in the sparse form)
-    const int nst = (min(KL_CH, nv - c0) + 31) / 32;
+    const int nst = (min(KL_DC, nv - c0) + 31) / 32;
     for (int st = 0; st < nst; ++st) {
       bf16x8 ka;
       {
@@ -427,14 +452,34 @@ __global__ void __launch_bounds__(256) idx_kl_dense_row_kernel(
           const int r = 32 * st + 8 * gg + 4 * e + (jj >> 2);
           const int d0 = 16 * wave + 4 * (jj & 3);
           tr[e] = __builtin_bit_cast(
-              u32x2, kl_read_tr16(ks + 128 * r + 16 * ((d0 >> 3) ^ (r & 7)) + 2 * (d0 & 7)));
+              u32x2, kl_read_tr16(kbuf + 128 * r + 16 * ((d0 >> 3) ^ (r & 7)) + 2 * (d0 & 7)));
         }
         ka = __builtin_bit_cast(bf16x8, u32x4{tr[0][0], tr[0][1], tr[1][0], tr[1][1]});
       }
       const bf16x8 cb = *(const bf16x8*)&cs[l16][32 * st + 8 * g4];
       dqa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, cb, dqa, 0, 0, 0);
     }
-    __syncthreads();  // ks and cs are free for the next chunk
+  };
+  // the barrier at the top of each half: the staged chunk is in, and every
+  // wave is done with the other buffer and with cs.  The next chunk is staged
+  // unconditionally (clamped into the row; one spare chunk at the end), so
+  // the loads in flight are the same on every path and nothing inside a
+  // chunk waits for them.
+  {
+    float ma[2], mb[2];
+    stage2(0, ks0, ma);
+    for (int c0 = 0; c0 < nv; c0 += 2 * KL_DC) {
+      kl_wait_loads();
+      __syncthreads();
+      stage2(c0 + KL_DC, ks1, mb);
+      grad(c0, ks0, ma);
+      if (c0 + KL_DC >= nv) break;
+      kl_wait_loads();
+      __syncthreads();
+      stage2(c0 + 2 * KL_DC, ks0, ma);
+      grad(c0 + KL_DC, ks1, mb);
+    }
+    kl_wait_loads();  // the spare chunk is in before the buffers go
   }
   kl = kl_block_sum(kl, sh);
   if (tid == 0) loss[row] = kl;
