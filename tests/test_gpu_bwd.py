@@ -214,6 +214,54 @@ def test_csa_attn_bwd_full_8k_prefill():
     assert e_dv <= 1e-2 and e_dk <= 1e-2 and e_bl <= 1e-2
 
 
+def test_hca_attn_bwd_1m_chunk_shape():
+    # the 1M-context HCA chunk (T = 4096 at position 1M - 4096, 8192 entries of
+    # m = 128, W = 512): dq and the per-entry mass of three runs of rows (the
+    # first 16, 16 in the middle, the last 40), dK/dV of the entry and the raw
+    # rows only the last 40 rows see (exact from those rows), and the identities
+    # sum dV = sum dout, sum dK = 0 and sum q . dq = sum K . dK over the call
+    w = gen.WORKLOADS["hca_prefill_1m_chunk4k"]
+    d = gen.Draw(630, DEV)
+    T, H, D, Nc, W, m = w.T, w.H, w.D, w.n_cmp, w.window, w.m
+    qp, R = w.ctx - T, w.T + w.window - 1
+    rbase = qp - (W - 1)
+    q = gen.store(d.normal(1, T, H, D), gen.BF16)
+    kv_cmp = gen.store(d.normal(1, Nc, 2 * D), gen.BF16)
+    kv_raw = gen.store(d.normal(1, R, 2 * D), gen.BF16)
+    dout = gen.store(d.normal(1, T, H, D), gen.BF16)
+    args = (q, kv_cmp, kv_raw, m, W, dev_i64([qp]), dev_i32([Nc]), dev_i64([rbase]))
+    out, lse = csa.hca_dense_attn(*args, want_lse=True)
+    dq, dkc, dkr, _, mass = csa.hca_dense_attn_bwd(*args, lse, dout, want_mass=True)
+    torch.cuda.synchronize()
+    hq, hc, hr, hd = gen.host_bits(q), gen.host_bits(kv_cmp), gen.host_bits(kv_raw), _dec(dout)
+    gq, gm, gc, gr = _dec(dq), _dec(mass), _dec(dkc), _dec(dkr)
+    t0 = T - 40
+    for a, n in ((0, 16), (T // 2 - 8, 16), (t0, 40)):
+        rq, rc, rr, _, rm = orc.attn_bwd(hq[:, a:a + n], hc, None, hr, W, qp + a, rbase,
+                                         hd[:, a:a + n], m=m, n_cmp=Nc, want_mass=True)
+        _rows_rel(gq[:, a:a + n], rq, "1m hca dq rows %d.." % a)
+        assert np.all(np.abs(gm[:, a:a + n] - rm) <= 1e-4 + 1e-4 * np.abs(rm))
+    # rc, rr: from the last 40 rows; an entry first seen at row m (j + 1) - 1 - qp
+    jc = -(-(t0 + 1 + qp) // m) - 1
+    ic = t0 + qp - rbase            # raw rows no row before t0 sees
+    _rows_rel(gc[0, jc:], rc[0, jc:], "1m hca dkv_cmp tail entries")
+    _rows_rel(gr[0, ic:], rr[0, ic:], "1m hca dkv_raw tail rows")
+    sdv = gc[0, :, D:].sum(0) + gr[0, :, D:].sum(0)
+    sdo = hd[0].sum((0, 1))
+    e_dv = np.abs(sdv - sdo).max() / np.abs(sdo).max()
+    sdk = gc[0, :, :D].sum(0) + gr[0, :, :D].sum(0)
+    e_dk = np.abs(sdk).max() / (np.abs(gc[0, :, :D]).sum(0) + np.abs(gr[0, :, :D]).sum(0)).max()
+    qv, kc, kr = brute.decode_bits(hq), brute.decode_bits(hc), brute.decode_bits(hr)
+    lhs = (qv * gq).sum()
+    rhs = (kc[0, :, :D] * gc[0, :, :D]).sum() + (kr[0, :, :D] * gr[0, :, :D]).sum()
+    e_bl = abs(lhs - rhs) / np.abs(qv * gq).sum()
+    print("1m hca identities: sum dV %.2e, sum dK %.2e, q.dq vs K.dK %.2e" % (e_dv, e_dk, e_bl))
+    assert e_dv <= 1e-2 and e_dk <= 1e-2 and e_bl <= 1e-2
+    # every row sees at least 8160 entries: the mass of a row sums to its
+    # non-window probability, at most the head count
+    assert (gm.sum(-1) <= H * (1 + 1e-5)).all()
+
+
 # ---------------------------------------------------------------- indexer KL loss
 # loss: fp32 scores (bf16 inputs, fp32 MFMA accumulation) and fp32 softmax:
 # |gpu - oracle| <= 1e-4 (1 + |oracle|); dw (fp32 sums): row-relative 1e-4;
