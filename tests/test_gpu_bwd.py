@@ -385,6 +385,22 @@ def test_indexer_kl_dense_bwd_ragged_matches_oracle():
     assert (_dec(res[3])[1, n_cmp[1]:] == 0).all()
 
 
+def test_indexer_kl_dense_bwd_without_entries():
+    # an empty cache (Nc_cap = 0): every row has loss 0 and no gradient, and
+    # neither the mass nor the keys are read
+    d = gen.Draw(605)
+    B, T = 2, 9
+    qi = gen.store(d.normal(B, T, 16, 64), gen.BF16).to(DEV)
+    wi = d.normal(B, T, 16).float().contiguous().to(DEV)
+    ki = torch.empty(B, 0, 64, dtype=torch.bfloat16, device=DEV)
+    mass = torch.empty(B, T, 0, dtype=torch.float32, device=DEV)
+    loss, dq, dw, dk = csa.csa_indexer_kl_dense_bwd(qi, wi, ki, 4, dev_i64([0, 100]),
+                                                    dev_i32([0, 0]), mass)
+    torch.cuda.synchronize()
+    assert (_dec(loss) == 0).all() and (_dec(dq) == 0).all() and (_dec(dw) == 0).all()
+    assert dk.shape == (B, 0, 64)
+
+
 def test_indexer_kl_dense_bwd_8k_shape():
     # T = 8192 and 2048 entries of the m = 4 cache: loss, dq, dw of sampled
     # rows (both ends, every 131st row) and dk of the entries only the last
