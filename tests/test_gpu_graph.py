@@ -1,5 +1,7 @@
 """The decode step (indexer top-k on long rows, split-key sparse attention)
-captured as a HIP graph and replayed gives the eager result on every replay.
+and a backward slice (attention backward of both forms with the mass, the
+sparse and dense indexer losses) captured as HIP graphs and replayed give the
+eager result on every replay.
 
 bench.py times decode steps as graph replays; this checks that capture adds
 nothing and drops nothing: all library launches are kernels (no memset), and
@@ -93,3 +95,88 @@ def test_decode_step_graph_replays_match_eager(paged):
         step()                           # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(idx, ref_idx) and torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+
+
+def test_backward_graph_replays_match_eager():
+    # one training-step backward slice captured as a graph: the CSA attention
+    # backward with the per-slot mass and the sparse indexer loss on it, the
+    # HCA-form backward with the per-entry mass and the dense indexer loss on
+    # it.  Everything is compared bit for bit except dk_idx, whose rows are
+    # summed with fp32 atomics (order-dependent last bits).
+    d = gen.Draw(33)
+    B, T, H, D, Nc, R, W, m, topk = 1, 200, 64, 128, 300, 300, 64, 4, 64
+    qp, rb = 100, 0
+    q = gen.store(d.normal(B, T, H, D), gen.BF16).to(DEV)
+    kv = gen.store(d.normal(B, Nc, 2 * D), gen.BF16).to(DEV)
+    kvr = gen.store(d.normal(B, R, 2 * D), gen.BF16).to(DEV)
+    dout = gen.store(d.normal(B, T, H, D), gen.BF16).to(DEV)
+    qi = gen.store(d.normal(B, T, 16, 64), gen.BF16).to(DEV)
+    wi = d.normal(B, T, 16).float().contiguous().to(DEV)
+    ki = gen.store(d.normal(B, Nc, 64), gen.BF16).to(DEV)
+    nv = torch.tensor([[min(Nc, (qp + t + 1) // m) for t in range(T)]])
+    idx = gen.random_index_sets(d, B, T, topk, nv).to(DEV)
+    q_pos = torch.tensor([qp], dtype=torch.int64, device=DEV)
+    n_cmp = torch.tensor([Nc], dtype=torch.int32, device=DEV)
+    raw_base = torch.tensor([rb], dtype=torch.int64, device=DEV)
+    _, lse = csa.csa_sparse_attn(q, kv, idx, kvr, W, q_pos, raw_base, want_lse=True)
+    _, lse_h = csa.hca_dense_attn(q, kv, kvr, m, W, q_pos, n_cmp, raw_base, want_lse=True)
+    L = csa.lib()
+    wsz = [L.csa_sparse_attn_bwd_workspace_size(B, T, H, Nc, R, W),
+           L.csa_indexer_kl_bwd_workspace_size(B, T, Nc, topk),
+           L.hca_dense_attn_bwd_workspace_size(B, T, H, Nc, R, W),
+           L.csa_indexer_kl_dense_bwd_workspace_size(B, T, Nc)]
+    ws = [torch.empty(n, dtype=torch.uint8, device=DEV) for n in wsz]
+    # outputs allocated by one eager call, then reused
+    a = csa.csa_sparse_attn_bwd(q, kv, idx, kvr, W, q_pos, raw_base, lse, dout, want_mass=True,
+                                workspace=ws[0])
+    k1 = csa.csa_indexer_kl_bwd(qi, wi, ki, idx, a[4], workspace=ws[1])
+    h = csa.hca_dense_attn_bwd(q, kv, kvr, m, W, q_pos, n_cmp, raw_base, lse_h, dout,
+                               want_mass=True, workspace=ws[2])
+    k2 = csa.csa_indexer_kl_dense_bwd(qi, wi, ki, m, q_pos, n_cmp, h[4], workspace=ws[3])
+
+    def step():
+        csa.csa_sparse_attn_bwd(q, kv, idx, kvr, W, q_pos, raw_base, lse, dout, dq=a[0],
+                                dkv_cmp=a[1], dkv_raw=a[2], attn_mass=a[4], workspace=ws[0])
+        csa.csa_indexer_kl_bwd(qi, wi, ki, idx, a[4], loss=k1[0], dq_idx=k1[1], dw_idx=k1[2],
+                               dk_idx=k1[3], workspace=ws[1])
+        csa.hca_dense_attn_bwd(q, kv, kvr, m, W, q_pos, n_cmp, raw_base, lse_h, dout, dq=h[0],
+                               dkv_cmp=h[1], dkv_raw=h[2], attn_mass=h[4], workspace=ws[2])
+        csa.csa_indexer_kl_dense_bwd(qi, wi, ki, m, q_pos, n_cmp, h[4], loss=k2[0],
+                                     dq_idx=k2[1], dw_idx=k2[2], dk_idx=k2[3], workspace=ws[3])
+
+    exact = [a[0], a[1], a[2], a[4], k1[0], k1[1], k1[2], h[0], h[1], h[2], h[4], k2[0], k2[1],
+             k2[2]]
+    summed = [k1[3], k2[3]]
+    step()
+    torch.cuda.synchronize()
+    ref_x = [t.clone() for t in exact]
+    ref_s = [t.clone() for t in summed]
+
+    def check(what):
+        for i, (t, r) in enumerate(zip(exact, ref_x)):
+            assert torch.equal(t.view(torch.int32), r.view(torch.int32)), "%s: output %d" % (what, i)
+        for t, r in zip(summed, ref_s):
+            err = (t - r).abs().amax(-1)
+            assert (err <= 1e-5 * r.abs().amax(-1) + 1e-30).all(), what + ": dk_idx"
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in exact + summed:
+            t.fill_(float("nan"))
+        for w in ws:
+            w.fill_(0xA5)                # stale workspace contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check("replay %d" % rep)
+        step()                           # eager work between replays
+        torch.cuda.synchronize()
+        check("eager after replay %d" % rep)
