@@ -78,36 +78,53 @@ __global__ void __launch_bounds__(256) bwd_sink_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------- bitmap
-// One workgroup (256 threads) per query row: bit j of words[row] is set when
-// entry j is selected (0 <= idx < Nc_cap); rank[row][w] = selected entries in
-// words < w, so an entry's slot in an ascending index row is its rank.
-__global__ void __launch_bounds__(256) bwd_bitmap_kernel(const int32_t* __restrict__ idx,
-                                                         int topk, int Nc_cap, int nw,
-                                                         uint32_t* __restrict__ bm,
-                                                         uint32_t* __restrict__ rank) {
-  __shared__ uint32_t words[2048];
-  __shared__ uint32_t sh[16];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  for (int w = tid; w < nw; w += 256) words[w] = 0;
-  __syncthreads();
+// One wave per query row, BM_ROWS rows per workgroup: bit j of words[row] is
+// set when entry j is selected (0 <= idx < Nc_cap); rank[row][w] = selected
+// entries in words < w, so an entry's slot in an ascending index row is its
+// rank.  Every step is the wave's own, with no workgroup barrier: a wave's LDS
+// operations complete in issue order.  nw <= 2048 (Nc_cap <= 65536).
+constexpr int BM_ROWS = 4;
+__global__ void __launch_bounds__(64 * BM_ROWS) bwd_bitmap_kernel(const int32_t* __restrict__ idx,
+                                                                  int rows, int topk, int Nc_cap,
+                                                                  int nw, uint32_t* __restrict__ bm,
+                                                                  uint32_t* __restrict__ rank) {
+  __shared__ uint32_t words[BM_ROWS][2048];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * BM_ROWS + wave;
+  if (row >= rows) return;  // the whole wave (no barrier follows)
+  uint32_t* wd = words[wave];
+  for (int w = lane; w < nw; w += 64) wd[w] = 0;
+  // the row's index slots, eight loads per lane in flight at a time
   const int32_t* ir = idx + (size_t)row * topk;
-  for (int k = tid; k < topk; k += 256) {
-    const int32_t j = ir[k];
-    if (j >= 0 && j < Nc_cap) atomicOr(&words[j >> 5], 1u << (j & 31));
+  for (int k0 = 0; k0 < topk; k0 += 8 * 64) {
+    int32_t jv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + 64 * u + lane;
+      jv[u] = k < topk ? ir[k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (jv[u] >= 0 && jv[u] < Nc_cap) atomicOr(&wd[jv[u] >> 5], 1u << (jv[u] & 31));
   }
-  __syncthreads();
-  const int per = (nw + 255) / 256;
-  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+  // lane l owns words [l per, l per + per); exclusive prefix of their counts
+  const int per = (nw + 63) / 64;
+  const int w0 = min(nw, lane * per), w1 = min(nw, w0 + per);
   uint32_t c = 0;
-  for (int w = w0; w < w1; ++w) c += __popc(words[w]);
-  uint32_t tot;
-  uint32_t r = block_excl_scan(c, sh, tot);
+  for (int w = w0; w < w1; ++w) c += __popc(wd[w]);
+  uint32_t x = c;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  uint32_t r = x - c;
   uint32_t* brow = bm + (size_t)row * nw;
   uint32_t* rrow = rank + (size_t)row * nw;
   for (int w = w0; w < w1; ++w) {
-    brow[w] = words[w];
+    const uint32_t v = wd[w];
+    brow[w] = v;
     rrow[w] = r;
-    r += __popc(words[w]);
+    r += __popc(v);
   }
 }
 
@@ -782,7 +799,8 @@ hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s) {
 
 hipError_t launch_sel_bitmap(const int32_t* idx, int rows, int topk, int Nc_cap, uint32_t* bm,
                              uint32_t* rank, hipStream_t s) {
-  bwd_bitmap_kernel<<<rows, 256, 0, s>>>(idx, topk, Nc_cap, (Nc_cap + 31) / 32, bm, rank);
+  bwd_bitmap_kernel<<<(rows + BM_ROWS - 1) / BM_ROWS, 64 * BM_ROWS, 0, s>>>(
+      idx, rows, topk, Nc_cap, (Nc_cap + 31) / 32, bm, rank);
   return hipGetLastError();
 }
 
@@ -826,7 +844,8 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
   const uint16_t* kvr = (const uint16_t*)a.kv_raw;
   float* dzp = a.dsink ? dz : nullptr;
   if (sparse && a.topk > 0 && a.Nc_cap > 0)
-    bwd_bitmap_kernel<<<rows, 256, 0, s>>>(a.idx, a.topk, a.Nc_cap, nw, bm, rank);
+    bwd_bitmap_kernel<<<(rows + BM_ROWS - 1) / BM_ROWS, 64 * BM_ROWS, 0, s>>>(
+        a.idx, rows, a.topk, a.Nc_cap, nw, bm, rank);
 
 #define CSA_BWD_DQ(NHH_, DENSE_)                                                              \
   attn_bwd_dq_kernel<NHH_, DENSE_><<<rows, 64 * NHH_, DENSE_ ? 0 : sizeof(int32_t) * a.topk,  \
