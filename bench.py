@@ -320,6 +320,14 @@ def setup_decode(w):
     st["ws_i"] = torch.empty(max(1, csa.csa_indexer_topk_workspace_size(B, 1, w.H_I, w.d_I, w.n_cmp, w.topk, torch.float8_e4m3fn)), dtype=torch.uint8, device=DEV)
     st["ws_a"] = torch.empty(max(1, csa.csa_sparse_attn_workspace_size(B, 1, w.H, w.D, w.topk, w.window)), dtype=torch.uint8, device=DEV)
     st["pages"] = None
+    # the attention in two halves: the window half on a side stream beside
+    # the compressors and the indexer, the selected half after top-k
+    nb = csa.csa_sparse_attn_split_workspace_size(B, 1, w.H, w.D, w.topk, w.window)
+    st["split"] = False
+    st["can_split"] = nb > 0 and not w.page
+    if st["can_split"]:
+        st["ws_s"] = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        st["side"] = torch.cuda.Stream()
     if w.page:
         # paged compressed caches: every sequence's pages shuffled over one
         # pool (untimed setup); the step reads them through the block table
@@ -362,6 +370,12 @@ def step_decode(w, st):
     def fn(tm):
         tm.mark(0)
         i = 0
+        main = torch.cuda.current_stream()
+        if st["split"]:
+            st["side"].wait_stream(main)
+            with torch.cuda.stream(st["side"]):
+                csa.csa_sparse_attn_window_half(st["q"], st["kv_raw"], w.window, st["q_pos"],
+                                                st["raw_base"], w.topk, st["ws_s"])
         if stream:
             csa.csa_compress(st["x_new"], st["w_kv"], st["w_gate"], st["q_pos"], w.m, w.overlap,
                              st["kv_cmp"], state_in=st["s0_main"], state_out=st["s1_main"],
@@ -376,9 +390,15 @@ def step_decode(w, st):
                              idx_out=st["idx"], workspace=st["ws_i"], pages=st["pages"])
         i += 1
         tm.mark(i)
-        csa.csa_sparse_attn(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"], w.window, st["q_pos"],
-                            st["raw_base"], out=st["out"], workspace=st["ws_a"],
-                            pages=st["pages"])
+        if st["split"]:
+            main.wait_stream(st["side"])
+            csa.csa_sparse_attn_selected_half(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"],
+                                              w.window, st["q_pos"], st["raw_base"], st["ws_s"],
+                                              out=st["out"])
+        else:
+            csa.csa_sparse_attn(st["q"], st["kv_cmp"], st["idx"], st["kv_raw"], w.window,
+                                st["q_pos"], st["raw_base"], out=st["out"], workspace=st["ws_a"],
+                                pages=st["pages"])
         i += 1
         tm.mark(i)
     names = (["compress"] if stream else []) + ["indexer_topk", "sparse_attn"]
@@ -573,6 +593,13 @@ def measure(name, steps, warmup, with_cpu, graph=True):
            "ms_per_step": r["step_ms_mean"], "ms_median": r["step_ms_median"],
            "ms_p90": r["step_ms_p90"], "stage_ms": r["stage_ms"],
            "cache": "L2 + last-level cache flushed before every step (outside the timed events)"}
+    if w.kind == "csa_decode" and st["can_split"]:
+        # the attention in two halves, the window half on a side stream beside
+        # the indexer, timed for comparison (on this stack the join of the two
+        # streams costs more than the overlap saves)
+        st["split"] = True
+        res["ms_per_step_split"] = run_steps(fn, names, steps, warmup, flush)["step_ms_mean"]
+        st["split"] = False
     if w.kind == "csa_decode" and graph:
         # the same step captured as a HIP graph and replayed, for comparison
         # (on this stack the replay is not faster than the eager launches)

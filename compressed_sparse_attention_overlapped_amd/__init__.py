@@ -17,7 +17,8 @@ from typing import Optional
 import torch
 
 __all__ = ["csa_compress", "csa_indexer_topk", "csa_sparse_attn", "hca_dense_attn",
-           "csa_sparse_attn_noalloc", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
+           "csa_sparse_attn_noalloc", "csa_sparse_attn_window_half",
+           "csa_sparse_attn_selected_half", "csa_sparse_attn_split_workspace_size", "csa_build_cmp_cu_seqlens", "csa_compress_varlen",
            "csa_indexer_topk_varlen", "csa_sparse_attn_varlen", "csa_sparse_attn_bwd",
            "hca_dense_attn_bwd", "csa_indexer_kl_bwd", "csa_indexer_kl_dense_bwd", "csa_compress_bwd", "csa_compress_bwd_ex",
            "csa_compress_workspace_size", "csa_indexer_topk_workspace_size",
@@ -101,6 +102,12 @@ def lib():
         L.csa_indexer_topk_workspace_size.argtypes = [i32] * 7
         L.csa_sparse_attn.argtypes = [i32] * 6 + [f32, vp, vp, vp, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, sz, vp]
         L.csa_sparse_attn_workspace_size.argtypes = [i32] * 6
+        L.csa_sparse_attn_window_half.argtypes = [i32] * 6 + [f32, vp, vp, vp, i32, vp, i32, vp, sz, vp]
+        L.csa_sparse_attn_selected_half.argtypes = L.csa_sparse_attn.argtypes
+        L.csa_sparse_attn_split_workspace_size.argtypes = [i32] * 6
+        L.csa_sparse_attn_window_half.restype = C.c_int
+        L.csa_sparse_attn_selected_half.restype = C.c_int
+        L.csa_sparse_attn_split_workspace_size.restype = C.c_size_t
         L.hca_dense_attn.argtypes = [i32] * 6 + [f32, vp, vp, vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
         L.hca_dense_attn_workspace_size.argtypes = [i32] * 6
         pt = C.POINTER(_CPageTable)
@@ -357,6 +364,49 @@ def csa_sparse_attn(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, scale=None,
                                _p(raw_base), _DT[q.dtype], _p(out), _p(lse), _p(ws), nb,
                                _stream(q))
     _check("csa_sparse_attn", rc)
+    return out, lse
+
+
+def csa_sparse_attn_split_workspace_size(B, T, H, D, topk, window) -> int:
+    """Bytes of the workspace both halves of a split csa_sparse_attn share (0: unsupported)."""
+    return lib().csa_sparse_attn_split_workspace_size(B, T, H, D, topk, window)
+
+
+def csa_sparse_attn_window_half(q, kv_raw, window, q_pos, raw_base, topk, workspace, scale=None):
+    """First half of csa_sparse_attn (decode rows, bf16): attends each row to its window
+    tokens only and leaves the partial results in workspace (a uint8 tensor of
+    csa_sparse_attn_split_workspace_size bytes) on q's current stream; it reads no
+    index, so it may run while the indexer chooses them."""
+    _dense(q, kv_raw, q_pos, raw_base)
+    B, T, H, D = q.shape
+    scale = D ** -0.5 if scale is None else float(scale)
+    rc = lib().csa_sparse_attn_window_half(B, T, H, D, topk, window, scale, _p(q_pos), _p(q),
+                                           _p(kv_raw), kv_raw.shape[1], _p(raw_base),
+                                           _DT[q.dtype], _p(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(q))
+    _check("csa_sparse_attn_window_half", rc)
+
+
+def csa_sparse_attn_selected_half(q, kv_cmp, idx, kv_raw, window, q_pos, raw_base, workspace,
+                                  scale=None, out=None, lse=None, want_lse=False, sink=None):
+    """Second half of csa_sparse_attn: attends the rows to their selected entries and merges
+    them with the window half's partials in workspace (which must have run first, on this
+    stream or ordered before it by an event); returns (out, lse) as csa_sparse_attn does."""
+    _dense(q, kv_cmp, idx, kv_raw, q_pos, raw_base, sink)
+    B, T, H, D = q.shape
+    topk = idx.shape[2] if idx is not None else 0
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    rc = lib().csa_sparse_attn_selected_half(
+        B, T, H, D, topk, window, scale, _p(_sink(sink, H)), _p(q_pos), _p(q), _p(kv_cmp),
+        kv_cmp.shape[1], _p(idx), _p(kv_raw), kv_raw.shape[1], _p(raw_base), _DT[q.dtype],
+        _p(out), _p(lse), _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q))
+    _check("csa_sparse_attn_selected_half", rc)
     return out, lse
 
 

@@ -376,6 +376,65 @@ csa_status_t csa_sparse_attn_noalloc(int B, int T, int H, int D, int topk, int w
                           nullptr, nullptr);
 }
 
+size_t csa_sparse_attn_split_workspace_size(int B, int T, int H, int D, int topk, int window) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || topk < 0 || window < 0) return 0;
+  if (!csa_host::attn_half_supported(B, T, H, topk, window)) return 0;
+  return csa_host::attn_half_ws_bytes(B, T, H, D, topk, window);
+}
+
+// One half of csa_sparse_attn taken in two calls (phase 1: the window,
+// phase 2: the selected entries and the merge).
+static csa_status_t sparse_attn_half(const char* fn, int phase, int B, int T, int H, int D,
+                                     int topk, int window, float scale, const float* sink,
+                                     const int64_t* q_pos, const void* q, const void* kv_cmp,
+                                     int Nc_cap, const int32_t* idx, const void* kv_raw,
+                                     int R_cap, const int64_t* raw_base, csa_dtype_t dt,
+                                     void* out, float* lse, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream) {
+  // the window half writes no output: q stands in for out in the checks
+  csa_status_t st = check_attn(fn, B, T, H, D, window, q_pos, q, phase == 2 ? kv_cmp : nullptr,
+                               phase == 2 ? Nc_cap : 0, kv_raw, R_cap, raw_base, dt,
+                               phase == 2 ? out : const_cast<void*>(q));
+  if (st != CSA_OK) return st;
+  if (topk < 0) return fail(CSA_E_ARG, "%s: topk must be >= 0", fn);
+  if (phase == 2 && topk > 0 && !idx) return fail(CSA_E_ARG, "%s: idx is required when topk > 0", fn);
+  if (dt != CSA_DT_BF16 || !csa_host::attn_half_supported(B, T, H, topk, window))
+    return fail(CSA_E_UNSUPPORTED,
+                "%s: needs bf16 with fewer than 1024 query rows and at most 64 splits "
+                "(%d rows, topk %d, window %d)", fn, B * T, topk, window);
+  const size_t need = csa_host::attn_half_ws_bytes(B, T, H, D, topk, window);
+  if (ws_bytes < need || !workspace)
+    return fail(CSA_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  csa_host::AttnArgs a{B, T, H, D, topk, window, 1, phase == 2 ? Nc_cap : 0, R_cap, false,
+                       scale, sink, q_pos, nullptr, q, phase == 2 ? kv_cmp : nullptr,
+                       phase == 2 ? idx : nullptr, kv_raw, raw_base, dt,
+                       phase == 2 ? out : nullptr, phase == 2 ? lse : nullptr, workspace};
+  a.phase = phase;
+  return hip_status(csa_host::launch_attn(a, stream), fn);
+}
+
+csa_status_t csa_sparse_attn_window_half(int B, int T, int H, int D, int topk, int window,
+                                         float scale, const int64_t* q_pos, const void* q,
+                                         const void* kv_raw, int R_cap, const int64_t* raw_base,
+                                         csa_dtype_t dt, void* workspace, size_t ws_bytes,
+                                         hipStream_t stream) {
+  return sparse_attn_half("csa_sparse_attn_window_half", 1, B, T, H, D, topk, window, scale,
+                          nullptr, q_pos, q, nullptr, 0, nullptr, kv_raw, R_cap, raw_base, dt,
+                          nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+csa_status_t csa_sparse_attn_selected_half(int B, int T, int H, int D, int topk, int window,
+                                           float scale, const float* sink, const int64_t* q_pos,
+                                           const void* q, const void* kv_cmp, int Nc_cap,
+                                           const int32_t* idx, const void* kv_raw, int R_cap,
+                                           const int64_t* raw_base, csa_dtype_t dt, void* out,
+                                           float* lse, void* workspace, size_t ws_bytes,
+                                           hipStream_t stream) {
+  return sparse_attn_half("csa_sparse_attn_selected_half", 2, B, T, H, D, topk, window, scale,
+                          sink, q_pos, q, kv_cmp, Nc_cap, idx, kv_raw, R_cap, raw_base, dt, out,
+                          lse, workspace, ws_bytes, stream);
+}
+
 size_t hca_dense_attn_workspace_size(int B, int T, int H, int D, int Nc_cap, int window) {
   if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
   return csa_host::attn_ws_bytes(B, T, H, D, Nc_cap + window, false);

@@ -536,7 +536,7 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
     int R_cap, bool dense, float scale_log2, const float* __restrict__ sink, int n_split,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml, int64_t cmp_rows_b, PageTable pt, int nc_logical, Varlen vl,
-    PageTable raw_pt) {
+    PageTable raw_pt, int phase, int n_split_c) {
   constexpr int H = 16 * WAVES, D = 128, NT = 64 * WAVES;
   constexpr int CH = DC_KT * 32 / NT;       // 16-byte chunks per thread per tile
   constexpr uint32_t kRowBytes = 2 * D * 2;  // one [K | V] row
@@ -548,8 +548,15 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, hl = lane & 15;
-  const int item = blockIdx.x;
-  const int rowi = item / n_split, split = item % n_split;
+  // phase 0: the n_split splits of each row share its tile list evenly.
+  // Phases 1 and 2 (the two halves of a split call): splits [0, n_split_c)
+  // take the selected entries' tiles, splits [n_split_c, n_split) the
+  // window's; phase 1 launches only the window splits, phase 2 only the
+  // others.  item is the partial slot (row, split).
+  const int n_launch = phase == 0 ? n_split : (phase == 1 ? n_split - n_split_c : n_split_c);
+  const int rowi = blockIdx.x / n_launch;
+  const int split = (phase == 1 ? n_split_c : 0) + blockIdx.x % n_launch;
+  const int item = rowi * n_split + split;
   const int b = vl.cu_q ? varlen_seq(vl, rowi) : rowi / T;
   const int t = vl.cu_q ? rowi - vl.cu_q[b] : rowi % T;
   // packed sequences: the sequence's entries and its own tokens as the raw
@@ -574,8 +581,22 @@ __global__ void __launch_bounds__(64 * WAVES) attn_dec_kernel(
   // take whole tiles.
   const int nc_pad = (L.n_c + DC_KT - 1) / DC_KT * DC_KT;
   const int n_tiles_row = (nc_pad + L.n_w + DC_KT - 1) / DC_KT;
-  const int tiles_per = (n_tiles_row + n_split - 1) / n_split;
-  const int ta = min(n_tiles_row, split * tiles_per), tb = min(n_tiles_row, ta + tiles_per);
+  int ta, tb;
+  if (phase == 0) {
+    const int tiles_per = (n_tiles_row + n_split - 1) / n_split;
+    ta = min(n_tiles_row, split * tiles_per);
+    tb = min(n_tiles_row, ta + tiles_per);
+  } else {
+    // the selected part's tiles [0, nc_pad / DC_KT) over n_split_c splits,
+    // the window's [nc_pad / DC_KT, n_tiles_row) over the rest
+    const int c_tiles = nc_pad / DC_KT;
+    const bool wpart = split >= n_split_c;
+    const int t0 = wpart ? c_tiles : 0, nt = wpart ? n_tiles_row - c_tiles : c_tiles;
+    const int ns = wpart ? n_split - n_split_c : n_split_c, s = wpart ? split - n_split_c : split;
+    const int per = (nt + ns - 1) / ns;
+    ta = t0 + min(nt, s * per);
+    tb = t0 + min(nt, s * per + per);
+  }
   const int ntiles = tb - ta;
   const int kb = ta * DC_KT;
   const int32_t* idx_row = dense ? nullptr : idx + (size_t)rowi * topk;
@@ -972,6 +993,33 @@ static int attn_splits(int rows, int keys_per_row, bool sparse, int H) {
   return 1;  // the prefill kernel has enough rows to fill the chip
 }
 
+// Splits of a call taken in two halves (decode rows, sparse form): the
+// window's tiles over about 128 workgroups, so that they fit beside the
+// indexer that runs at the same time, and the selected entries' tiles over
+// about one workgroup per CU, each split holding at most DC_IDX_MAX slots.
+// Both counts are fixed by (rows, topk, window) alone.  {0, 0}: unsupported.
+struct HalfSplits {
+  int s_c, s_w;
+};
+static HalfSplits half_splits(int rows, int H, int topk, int window) {
+  if (!use_decode_kernel(rows, H) || rows < 1) return {0, 0};
+  const int c_tiles = (topk + DC_KT - 1) / DC_KT, w_tiles = (window + DC_KT - 1) / DC_KT;
+  int s_w = std::min(std::max(w_tiles, 1), std::max(1, (128 + rows - 1) / rows));
+  int s_c = std::min(std::max(c_tiles, 1), std::max(1, (256 + rows - 1) / rows));
+  s_c = std::max(s_c, (c_tiles + DC_IDX_MAX / DC_KT - 1) / (DC_IDX_MAX / DC_KT));
+  if (s_c + s_w > CB_MAX_SPLIT) return {0, 0};
+  return {s_c, s_w};
+}
+
+bool attn_half_supported(int B, int T, int H, int topk, int window) {
+  return half_splits(B * T, H, topk, window).s_c > 0;
+}
+
+size_t attn_half_ws_bytes(int B, int T, int H, int D, int topk, int window) {
+  const HalfSplits hs = half_splits(B * T, H, topk, window);
+  return (size_t)B * T * (hs.s_c + hs.s_w) * H * (D + 2) * sizeof(float);
+}
+
 bool attn_supported(int B, int T, int H, int keys_per_row, bool sparse) {
   return attn_splits(B * T, keys_per_row, sparse, H) > 0;
 }
@@ -1024,24 +1072,31 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
     return hipGetLastError();
   }
   const int keys = (a.dense ? a.Nc_cap : a.topk) + a.window;
-  const int n_split = attn_splits(rows, keys, !a.dense, a.H);
+  int n_split = attn_splits(rows, keys, !a.dense, a.H), n_split_c = 0;
+  unsigned grid = (unsigned)(rows * n_split);
+  if (a.phase != 0) {
+    // one half of a split call: its own split layout (see half_splits)
+    const HalfSplits hs = half_splits(rows, a.H, a.topk, a.window);
+    n_split = hs.s_c + hs.s_w;
+    n_split_c = hs.s_c;
+    grid = (unsigned)(rows * (a.phase == 1 ? hs.s_w : hs.s_c));
+  }
   if (n_split == 0) return hipErrorNotSupported;
   float* part_o = (float*)a.ws;
   float* part_ml = part_o ? part_o + (size_t)rows * n_split * a.H * a.D : nullptr;
-  const unsigned grid = (unsigned)(rows * n_split);
   if (use_decode_kernel(rows, a.H)) {
     if (a.H == 64)
       attn_dec_kernel<4><<<grid, 256, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
-          a.dense ? cmp_pt : dec_pages, nc_logical, a.vl, raw_pt);
+          a.dense ? cmp_pt : dec_pages, nc_logical, a.vl, raw_pt, a.phase, n_split_c);
     else
       attn_dec_kernel<2><<<grid, 128, 0, st>>>(
           (const uint16_t*)a.q, (const uint16_t*)a.kv_cmp, a.idx, (const uint16_t*)a.kv_raw,
           a.q_pos, a.n_cmp, a.raw_base, a.T, a.topk, a.window, a.m, a.Nc_cap, a.R_cap, a.dense,
           scale_log2, a.sink, n_split, (uint16_t*)a.out, a.lse, part_o, part_ml, cmp_rows_b,
-          a.dense ? cmp_pt : dec_pages, nc_logical, a.vl, raw_pt);
+          a.dense ? cmp_pt : dec_pages, nc_logical, a.vl, raw_pt, a.phase, n_split_c);
   } else {
     // HCA rows share the whole compressed range: 4 rows per workgroup; CSA
     // rows share only the window: 2 rows, so that two independent
@@ -1074,7 +1129,8 @@ hipError_t launch_attn(const AttnArgs& a_in, hipStream_t st) {
     }
 #undef CSA_LAUNCH_PF
   }
-  if (n_split > 1)
+  // the window half leaves its partials for the selected half's combine
+  if (n_split > 1 && a.phase != 1)
     combine_kernel<CSA_DT_BF16><<<dim3(rows, a.H / 2), 256, 0, st>>>(part_o, part_ml, n_split,
                                                                       a.H, a.sink, a.out, a.lse);
   return hipGetLastError();

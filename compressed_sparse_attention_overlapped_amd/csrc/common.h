@@ -283,8 +283,11 @@ struct AttnArgs {
   csa::Varlen vl;        // cu_q null: fixed [B, T] layout
   int total_rows;        // packed sequences: query rows (T is then the longest)
   csa::PageTable raw_pages;  // block_table null: unpaged kv_raw
+  int phase;                 // 0: whole call; 1: window half; 2: selected half + combine
 };
 size_t attn_ws_bytes(int B, int T, int H, int D, int keys_per_row, bool sparse);
+bool attn_half_supported(int B, int T, int H, int topk, int window);
+size_t attn_half_ws_bytes(int B, int T, int H, int D, int topk, int window);
 // the static scratch of csa_sparse_attn_noalloc: its size and its device
 // address on the current device
 size_t noalloc_scratch_bytes();

@@ -238,6 +238,43 @@ csa_status_t csa_sparse_attn(int B, int T, int H, int D, int topk, int window, f
 size_t csa_sparse_attn_workspace_size(int B, int T, int H, int D, int topk, int window);
 
 /*
+ * csa_sparse_attn in two halves, so that the sliding-window half of a decode
+ * step can run while the indexer is still choosing the entries.  The
+ * attention of a query is one softmax over the selected compressed entries
+ * and the raw window tokens (DS-V4 analysis section 1.2); the window half
+ * does not depend on the top-k indices, and
+ * the softmax over the union of two key sets is the log-sum-exp merge of the
+ * softmaxes over each (the partials and merge of the split-key decode form).
+ *
+ * csa_sparse_attn_window_half attends each row to its window tokens only and
+ * leaves fp32 partial results (unnormalised output, running maximum and sum
+ * per head) in the workspace.  csa_sparse_attn_selected_half then attends the
+ * rows to their selected entries, merges both halves (and the sink) and writes
+ * out and lse exactly as csa_sparse_attn defines them (equal up to fp32
+ * summation order).  Both calls take the same B, T, H, D, topk, window, scale,
+ * q_pos, q, kv_raw, R_cap, raw_base, dt and workspace; the caller orders the
+ * selected half after the window half (same stream, or an event between the
+ * two streams); nothing else may use the workspace in between.  The window
+ * half reads no index, compressed row, sink or output.
+ * Supported: dt BF16, D = 128, H in {32, 64}, fewer than 1024 query rows
+ * (decode), unpaged caches and the [B, T] layout; CSA_E_UNSUPPORTED otherwise.
+ * Workspace: csa_sparse_attn_split_workspace_size() bytes (0: unsupported).
+ */
+size_t csa_sparse_attn_split_workspace_size(int B, int T, int H, int D, int topk, int window);
+csa_status_t csa_sparse_attn_window_half(int B, int T, int H, int D, int topk, int window,
+                                         float scale, const int64_t* q_pos, const void* q,
+                                         const void* kv_raw, int R_cap, const int64_t* raw_base,
+                                         csa_dtype_t dt, void* workspace, size_t ws_bytes,
+                                         hipStream_t stream);
+csa_status_t csa_sparse_attn_selected_half(int B, int T, int H, int D, int topk, int window,
+                                           float scale, const float* sink, const int64_t* q_pos,
+                                           const void* q, const void* kv_cmp, int Nc_cap,
+                                           const int32_t* idx, const void* kv_raw, int R_cap,
+                                           const int64_t* raw_base, csa_dtype_t dt, void* out,
+                                           float* lse, void* workspace, size_t ws_bytes,
+                                           hipStream_t stream);
+
+/*
  * csa_sparse_attn without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid hipMalloc).  Arguments, results and errors are those of
