@@ -718,8 +718,9 @@ def main():
         sub[key] = {k: r[k] for k in ("workload", "value", "unit", "ms_per_step", "ms_median",
                                       "ms_p90", "stage_ms", "roofline", "work", "cache")
                     if k in r}
-        if "ms_per_step_graph" in r:
-            sub[key]["ms_per_step_graph"] = r["ms_per_step_graph"]
+        for k in ("ms_per_step_graph", "ms_per_step_split"):
+            if k in r:
+                sub[key][k] = r[k]
         sub[key]["cpu_baseline"] = r.get("cpu_baseline")
     line = {
         "metric": "CSA prefill tokens/s + decode queries/s at 128K ctx; % of HBM/MFMA peak",
